@@ -1,0 +1,194 @@
+"""CPU fp64 oracle for the DeepSeek Sparse Attention forward hot path.
+
+TEST INFRASTRUCTURE ONLY. This module is the reference the HIP kernels are
+checked against. Only the test suite, the smoke check and the bench's CPU
+baseline leg may import it; the product path never calls it and shares no code
+with it (no kernels, headers, helpers, tables or constants).
+
+Every function is written from the definitions on the pages:
+
+* "DeepSeek Sparse Attention (DSA)", cuDNN Frontend OSS API docs
+  (docs.nvidia.com/cudnn/fe-oss-apis/dsa): section 1 "Sparse Attention
+  Forward" (slot semantics, sink, LSE, empty rows, topk_length clamp, D_qk=576
+  with V = first 512 dims), section 3 "Indexer Forward (score-only)" (score
+  formula and ratio-causal mask), section 4 "Combined Indexer Forward + Top-K"
+  (deterministic tie-break toward the smallest index) and section 5
+  "Indexer Top-K" (per-row effective length, top_k <= 2048).
+* "nemo_automodel...glm_moe_dsa.kernels.cudnn_dsa" API page:
+  prepare_cudnn_dsa_packed_metadata (per-query starts and causal lengths of
+  packed THD sequences), _topk_wrapper_chunked (scores [T, S_max] with causal
+  lengths [T]), cudnn_indexer_topk / cudnn_sparse_attention (global indices,
+  ascending valid prefix, -1 suffix).
+
+Arithmetic is float64 throughout; bf16 inputs are widened exactly from their
+bit patterns. Plain loops over rows, with a library matmul as the only
+primitive, so each step can be read against the definition.
+
+Readings where the pages are silent (each is listed with its reason in the
+repository's design notes): indexer scores carry no internal scaling (the
+caller pre-scales W); K has a single head shared by all indexer heads; masked
+score columns are -inf; -0.0 and +0.0 are equal values and tie; selected
+indices are emitted in ascending order; the sink is a per-head logit in scaled
+units that enters only the output denominator; LSE is the natural log over
+key slots only; empty rows give out=0, lse=+inf, max_logits=-inf.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# ---------------------------------------------------------------------------
+# Input widening
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Exact bf16 -> float64: a bf16 value is the top 16 bits of an fp32."""
+    u = np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Step a0: packed-THD metadata
+# ---------------------------------------------------------------------------
+
+def packed_metadata(cu_seqlens, T: int):
+    """Per-token document start and causal length for compact packed THD.
+
+    cudnn_dsa page, prepare_cudnn_dsa_packed_metadata: cu_seqlens are the
+    cumulative real-token lengths [n_seq+1]; each query gets the start of its
+    sequence and its real causal length (causality restarts per document).
+    Returns (row_starts, seq_lens) as int64 arrays of length T.
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    starts = np.zeros(T, dtype=np.int64)
+    seq_lens = np.zeros(T, dtype=np.int64)
+    for d in range(len(cu) - 1):
+        for t in range(int(cu[d]), int(cu[d + 1])):
+            starts[t] = cu[d]
+            seq_lens[t] = t - cu[d] + 1
+    return starts, seq_lens
+
+
+# ---------------------------------------------------------------------------
+# Step a1: lightning-indexer scores
+# ---------------------------------------------------------------------------
+
+def indexer_scores(q_idx, k_idx, w, row_starts, seq_lens, rows, width=None):
+    """Dense indexer scores for the given query rows, local key columns.
+
+    DSA page section 3: S[q, k] = sum_h ReLU(Q_h . K^T) * W_h with a
+    ratio-causal mask; with ratio 1 and no causal offsets the valid columns of
+    local row q are k < q + 1 within its segment. The indexer K has one head
+    (H_kv = 1), so every head h uses the same key row. Column j of row t is key
+    start(t) + j (cudnn_dsa page, _topk_wrapper_chunked: scores [T, S_max] with
+    causal lengths [T]); columns j >= seq_len(t) are -inf.
+
+    q_idx [T, H, D], k_idx [T, D], w [T, H] are float64. Returns float64
+    [len(rows), width].
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    if width is None:
+        width = int(max(seq_lens[rows].max(), 1)) if len(rows) else 1
+    out = np.full((len(rows), width), NEG_INF)
+    for r, t in enumerate(rows):
+        s = int(row_starts[t])
+        n = int(seq_lens[t])
+        keys = k_idx[s:s + n]                       # [n, D]
+        logits = q_idx[t] @ keys.T                  # [H, n]   Q_h . K^T
+        out[r, :n] = w[t] @ np.maximum(logits, 0.0)  # sum_h W_h * ReLU(.)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Steps a2 + a3: per-row top-K select, compaction, local -> global
+# ---------------------------------------------------------------------------
+
+def topk_row(x, n: int, k: int) -> np.ndarray:
+    """Selected local columns of one row, ascending.
+
+    DSA page section 5: top-K over the first n = seq_len columns of the row.
+    Section 4 (deterministic=True): exact-value ties at the K-th boundary go to
+    the smallest local index. Rows with n <= K keep all n columns.
+    """
+    x = np.asarray(x, dtype=np.float64)[:n]
+    if n <= k:
+        return np.arange(n, dtype=np.int64)
+    theta = np.partition(x, n - k)[n - k]          # K-th largest value
+    above = np.nonzero(x > theta)[0]
+    equal = np.nonzero(x == theta)[0]              # ascending column order
+    chosen = np.concatenate([above, equal[: k - len(above)]])
+    return np.sort(chosen)
+
+
+def topk(scores, seq_lens, k: int, row_starts=None, n_cols=None):
+    """Top-K indices in canonical compact form.
+
+    cudnn_dsa page (cudnn_indexer_topk, _compact_and_sort_indices): int32
+    indices in global packed coordinates (row start + local column), an
+    ascending valid prefix and a -1 suffix, plus valid lengths
+    min(seq_len, K). seq_lens are clamped to [0, n_cols]. With row_starts None
+    the local column ids are returned.
+    """
+    scores = np.asarray(scores)
+    n_rows = scores.shape[0]
+    n_cols = scores.shape[1] if n_cols is None else n_cols
+    idx = np.full((n_rows, k), -1, dtype=np.int64)
+    length = np.zeros(n_rows, dtype=np.int64)
+    for r in range(n_rows):
+        n = int(min(max(int(seq_lens[r]), 0), n_cols))
+        sel = topk_row(scores[r], n, k)
+        base = 0 if row_starts is None else int(row_starts[r])
+        idx[r, : len(sel)] = sel + base
+        length[r] = len(sel)
+    return idx.astype(np.int32), length.astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# Steps a4 / a5: sparse attention forward
+# ---------------------------------------------------------------------------
+
+def sparse_attention(q, k, v, indices, topk_length, sink, scale, d_v=None, rows=None):
+    """Sparse MQA attention forward over selected key rows.
+
+    DSA page section 1: for query row t, head h and valid slot j the score is
+    scale * dot(q[t, h, :], kv[idx[t, j], :]); invalid (-1) and out-of-bounds
+    ids have score -inf and duplicates stay distinct slots; topk_length is
+    clamped to [0, K] and slots at or beyond it are invalid. The sink adds
+    exp(sink_h) to the output denominator only; lse is KV-only (natural log,
+    excludes the sink); empty rows give out = 0, max_logits = -inf, lse = +inf.
+    For D_qk = 576 the values are the first 512 dims of the shared KV row
+    (v is None, d_v = 512); the block-routed GQA page passes a separate V.
+
+    q [Tq, H, Dqk], k [Tkv, Dqk], v [Tkv, Dv] or None, all float64.
+    Returns (out [n, H, Dv], lse [n, H], max_logits [n, H]) for the rows.
+    """
+    Tq, H, _ = q.shape
+    Tkv = k.shape[0]
+    if v is None:
+        v = k[:, :d_v]
+    Dv = v.shape[1]
+    kw = indices.shape[1]
+    rows = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((len(rows), H, Dv))
+    lse = np.full((len(rows), H), np.inf)
+    mx = np.full((len(rows), H), NEG_INF)
+    for r, t in enumerate(rows):
+        L = kw if topk_length is None else min(max(int(topk_length[t]), 0), kw)
+        ids = np.asarray(indices[t, :L], dtype=np.int64)
+        ids = ids[(ids >= 0) & (ids < Tkv)]
+        if len(ids) == 0:
+            continue
+        s = scale * (q[t] @ k[ids].T)               # [H, n] scaled logits
+        m = s.max(axis=1)
+        e = np.exp(s - m[:, None])
+        l = e.sum(axis=1)
+        denom = l.copy()
+        if sink is not None:
+            denom = denom + np.exp(np.asarray(sink, dtype=np.float64) - m)
+        out[r] = (e @ v[ids]) / denom[:, None]
+        lse[r] = m + np.log(l)
+        mx[r] = m
+    return out, lse, mx

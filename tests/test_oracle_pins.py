@@ -1,0 +1,419 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each pin checks the oracle against a hand-derived fixture (tests/golden), a
+brute-force evaluation, a textbook/library routine it must reduce to in a
+special case, or a closed form. Together they are meant to catch a dropped
+term, a wrong sign or index, or a transposed operand anywhere in the oracle.
+These run on the CPU only.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import dsa_oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _num(x):
+    if isinstance(x, str):
+        return float(x)
+    return x
+
+
+def _docs_meta(doc_lens):
+    cu = np.concatenate([[0], np.cumsum(doc_lens)]).astype(np.int64)
+    return cu, O.packed_metadata(cu, int(cu[-1]))
+
+
+# ---------------------------------------------------------------- metadata --
+
+def test_metadata_golden():
+    g = _load("metadata_cu_0_3_7.json")
+    st, sl = O.packed_metadata(g["cu_seqlens"], g["cu_seqlens"][-1])
+    assert st.tolist() == g["row_starts"]
+    assert sl.tolist() == g["seq_lens"]
+
+
+def test_metadata_matches_searchsorted():
+    rng = np.random.default_rng(0)
+    doc_lens = rng.integers(1, 40, size=9)
+    cu, (st, sl) = _docs_meta(doc_lens)
+    t = np.arange(cu[-1])
+    d = np.searchsorted(cu, t, side="right") - 1
+    assert np.array_equal(st, cu[d])
+    assert np.array_equal(sl, t - cu[d] + 1)
+
+
+def test_metadata_empty_documents():
+    # zero-length documents contribute no rows and do not shift the others
+    st, sl = O.packed_metadata([0, 2, 2, 5], 5)
+    assert st.tolist() == [0, 0, 2, 2, 2]
+    assert sl.tolist() == [1, 2, 1, 2, 3]
+
+
+# ----------------------------------------------------------------- indexer --
+
+def test_indexer_golden():
+    g = _load("indexer_small.json")
+    q = np.array(g["q_idx"], dtype=np.float64)
+    k = np.array(g["k_idx"], dtype=np.float64)
+    w = np.array(g["w"], dtype=np.float64)
+    for case in g["cases"]:
+        st, sl = O.packed_metadata(case["cu_seqlens"], q.shape[0])
+        exp = np.array([[_num(x) for x in row] for row in case["scores"]])
+        got = O.indexer_scores(q, k, w, st, sl, np.arange(q.shape[0]), width=exp.shape[1])
+        assert np.array_equal(np.isinf(got), np.isinf(exp))
+        np.testing.assert_allclose(got[np.isfinite(exp)], exp[np.isfinite(exp)], rtol=0, atol=1e-15)
+
+
+def _indexer_brute(q, k, w, cu):
+    T, H, D = q.shape
+    S = np.full((T, T), -np.inf)
+    for d in range(len(cu) - 1):
+        a, b = int(cu[d]), int(cu[d + 1])
+        for t in range(a, b):
+            for key in range(a, t + 1):
+                tot = 0.0
+                for h in range(H):
+                    dot = 0.0
+                    for e in range(D):
+                        dot += q[t, h, e] * k[key, e]
+                    tot += w[t, h] * max(dot, 0.0)
+                S[t, key - a] = tot
+    return S
+
+
+def test_indexer_bruteforce_multidoc():
+    rng = np.random.default_rng(1)
+    doc_lens = [5, 1, 17, 9]
+    cu, (st, sl) = _docs_meta(doc_lens)
+    T, H, D = int(cu[-1]), 4, 6
+    q = rng.standard_normal((T, H, D))
+    k = rng.standard_normal((T, D))
+    w = rng.standard_normal((T, H))
+    got = O.indexer_scores(q, k, w, st, sl, np.arange(T), width=T)
+    exp = _indexer_brute(q, k, w, cu)
+    assert np.array_equal(np.isinf(got), np.isinf(exp))
+    fin = np.isfinite(exp)
+    np.testing.assert_allclose(got[fin], exp[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_indexer_single_head_is_masked_relu_matmul():
+    # H = 1, W = 1: the score is ReLU(q k^T) on the causal lower triangle.
+    rng = np.random.default_rng(2)
+    T, D = 37, 8
+    q = rng.standard_normal((T, 1, D))
+    k = rng.standard_normal((T, D))
+    w = np.ones((T, 1))
+    st, sl = O.packed_metadata([0, T], T)
+    got = O.indexer_scores(q, k, w, st, sl, np.arange(T), width=T)
+    full = np.maximum(q[:, 0, :] @ k.T, 0.0)
+    exp = np.where(np.tril(np.ones((T, T), dtype=bool)), full, -np.inf)
+    np.testing.assert_array_equal(np.isinf(got), np.isinf(exp))
+    np.testing.assert_allclose(got[np.isfinite(exp)], exp[np.isfinite(exp)], rtol=1e-13, atol=1e-13)
+
+
+def test_indexer_nonnegative_inputs_reduce_to_gemv():
+    # q, k >= 0 elementwise: ReLU is inactive, so S = (sum_h W_h q_h) . k^T.
+    rng = np.random.default_rng(3)
+    T, H, D = 29, 5, 7
+    q = np.abs(rng.standard_normal((T, H, D)))
+    k = np.abs(rng.standard_normal((T, D)))
+    w = rng.standard_normal((T, H))
+    st, sl = O.packed_metadata([0, T], T)
+    got = O.indexer_scores(q, k, w, st, sl, np.arange(T), width=T)
+    qw = np.einsum("th,thd->td", w, q)
+    for t in range(T):
+        np.testing.assert_allclose(got[t, : t + 1], k[: t + 1] @ qw[t], rtol=1e-12, atol=1e-12)
+
+
+def test_indexer_mask_invariant():
+    rng = np.random.default_rng(4)
+    doc_lens = [3, 11, 1, 6]
+    cu, (st, sl) = _docs_meta(doc_lens)
+    T = int(cu[-1])
+    q = rng.standard_normal((T, 3, 4))
+    k = rng.standard_normal((T, 4))
+    w = rng.standard_normal((T, 3))
+    got = O.indexer_scores(q, k, w, st, sl, np.arange(T), width=T)
+    for t in range(T):
+        assert np.isfinite(got[t]).sum() == sl[t]
+        assert np.all(np.isfinite(got[t, : sl[t]]))
+    # no score depends on a key of another document: perturbing other docs' keys
+    k2 = k.copy()
+    k2[: cu[1]] += 10.0
+    got2 = O.indexer_scores(q, k2, w, st, sl, np.arange(T), width=T)
+    assert np.array_equal(got[cu[1]:], got2[cu[1]:])
+
+
+# ------------------------------------------------------------------- top-K --
+
+def test_topk_golden_ties_and_signed_zero():
+    g = _load("topk_ties.json")
+    row = np.array(g["row"], dtype=np.float64)
+    assert math.copysign(1.0, row[3]) < 0  # the fixture really holds -0.0
+    for c in g["cases"]:
+        idx, ln = O.topk(row[None, :], [c["seq_len"]], c["k"])
+        assert idx[0].tolist() == c["indices"], c
+        assert ln[0] == min(c["seq_len"], c["k"])
+
+
+def _topk_brute(x, n, k):
+    # full stable sort by (value descending, index ascending)
+    order = sorted(range(n), key=lambda j: (-float(x[j]), j))
+    return sorted(order[: min(n, k)])
+
+
+@pytest.mark.parametrize("levels", [None, 2, 3, 5])
+def test_topk_bruteforce_sort(levels):
+    rng = np.random.default_rng(10 + (levels or 0))
+    for trial in range(300):
+        n_cols = int(rng.integers(1, 40))
+        x = rng.standard_normal(n_cols)
+        if levels is not None:
+            x = np.round(x * levels / 2) / levels  # many exact ties, incl. 0
+            zeros = x == 0
+            x[zeros & (rng.random(n_cols) < 0.5)] = -0.0
+        n = int(rng.integers(0, n_cols + 1))
+        k = int(rng.integers(1, 12))
+        idx, ln = O.topk(x[None, :], [n], k)
+        exp = _topk_brute(x, n, k)
+        assert idx[0, : len(exp)].tolist() == exp
+        assert np.all(idx[0, len(exp):] == -1)
+        assert ln[0] == len(exp)
+
+
+def test_topk_closed_forms():
+    n, k = 50, 16
+    # all-equal row: the first K columns
+    idx, _ = O.topk(np.full((1, n), 0.25), [n], k)
+    assert idx[0].tolist() == list(range(k))
+    # strictly increasing row: the last K columns
+    idx, _ = O.topk(np.arange(n, dtype=np.float64)[None, :], [n], k)
+    assert idx[0].tolist() == list(range(n - k, n))
+    # strictly decreasing row: the first K columns
+    idx, _ = O.topk(-np.arange(n, dtype=np.float64)[None, :], [n], k)
+    assert idx[0].tolist() == list(range(k))
+    # seq_len <= K: every causal column, then -1
+    idx, ln = O.topk(np.random.default_rng(0).standard_normal((1, n)), [9], k)
+    assert idx[0].tolist() == list(range(9)) + [-1] * (k - 9) and ln[0] == 9
+    # global coordinates: row start added, padding stays -1
+    idx, _ = O.topk(np.full((1, n), 1.0), [3], 4, row_starts=[100])
+    assert idx[0].tolist() == [100, 101, 102, -1]
+    # seq_len beyond the row width is clamped to the width
+    idx, ln = O.topk(np.arange(6, dtype=np.float64)[None, :], [99], 8)
+    assert idx[0].tolist() == [0, 1, 2, 3, 4, 5, -1, -1] and ln[0] == 6
+
+
+def test_topk_invariants_random():
+    rng = np.random.default_rng(5)
+    n_rows, n_cols, k = 40, 300, 37
+    x = np.round(rng.standard_normal((n_rows, n_cols)) * 8) / 8
+    sl = rng.integers(0, n_cols + 1, size=n_rows)
+    idx, ln = O.topk(x, sl, k)
+    for r in range(n_rows):
+        n = sl[r]
+        sel = idx[r, : ln[r]]
+        assert ln[r] == min(n, k)
+        assert np.all(np.diff(sel) > 0) and np.all(sel >= 0) and np.all(sel < max(n, 1))
+        if n > k:
+            mask = np.zeros(n, dtype=bool)
+            mask[sel] = True
+            lo, hi = x[r, :n][mask].min(), x[r, :n][~mask].max()
+            assert lo >= hi
+            # tie rule: unselected columns equal to the threshold lie after
+            # every selected column of that value
+            tie_sel = np.nonzero(mask & (x[r, :n] == lo))[0]
+            tie_uns = np.nonzero(~mask & (x[r, :n] == lo))[0]
+            if len(tie_uns):
+                assert tie_sel.max() < tie_uns.min()
+
+
+# --------------------------------------------------------------- attention --
+
+def test_attention_golden():
+    g = _load("attention_two_keys.json")
+    q = np.array(g["q"], dtype=np.float64)
+    k = np.array(g["k"], dtype=np.float64)
+    v = np.array(g["v"], dtype=np.float64)
+    for c in g["cases"]:
+        idx = np.array([c["indices"]], dtype=np.int64)
+        tl = None if c["topk_length"] is None else np.array([c["topk_length"]])
+        sink = None if c["sink"] is None else np.array([c["sink"]])
+        out, lse, mx = O.sparse_attention(q, k, v, idx, tl, sink, g["scale"])
+        np.testing.assert_allclose(out[0, 0], c["out"], rtol=0, atol=1e-14)
+        assert lse[0, 0] == pytest.approx(_num(c["lse"]), abs=1e-14) or (
+            np.isinf(_num(c["lse"])) and lse[0, 0] == _num(c["lse"]))
+        assert mx[0, 0] == pytest.approx(_num(c["max_logits"]), abs=1e-14) or (
+            np.isinf(_num(c["max_logits"])) and mx[0, 0] == _num(c["max_logits"]))
+
+
+def _sdpa(q, k, v, scale, mask):
+    """torch's scaled_dot_product_attention in float64 on the CPU."""
+    tq = torch.from_numpy(np.ascontiguousarray(q))
+    tk = torch.from_numpy(np.ascontiguousarray(k))
+    tv = torch.from_numpy(np.ascontiguousarray(v))
+    tm = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask))
+    return torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=tm, scale=scale).numpy()
+
+
+def _causal_full_indices(T, width):
+    idx = np.full((T, width), -1, dtype=np.int64)
+    for t in range(T):
+        idx[t, : t + 1] = np.arange(t + 1)
+    return idx
+
+
+@pytest.mark.parametrize("shared", [True, False])
+def test_attention_dense_identity_sdpa(shared):
+    # Top-K covering every causal key and no sink == dense causal attention.
+    rng = np.random.default_rng(20)
+    T, H, Dqk, Dv = 23, 3, 12, 8
+    q = rng.standard_normal((T, H, Dqk))
+    kv = rng.standard_normal((T, Dqk))
+    v = None if shared else rng.standard_normal((T, Dv))
+    scale = 0.37
+    idx = _causal_full_indices(T, T + 5)
+    out, lse, _ = O.sparse_attention(q, kv, v, idx, None, None, scale, d_v=Dv)
+    vv = kv[:, :Dv] if shared else v
+    causal = np.where(np.tril(np.ones((T, T), dtype=bool)), 0.0, -np.inf)
+    ref = _sdpa(q.transpose(1, 0, 2), np.broadcast_to(kv, (H, T, Dqk)),
+                np.broadcast_to(vv, (H, T, Dv)), scale, causal)
+    np.testing.assert_allclose(out, ref.transpose(1, 0, 2), rtol=1e-12, atol=1e-13)
+    # LSE through a probe key: logit 0, value = one-hot in an extra value dim.
+    # Its attention weight is 1 / (1 + exp(lse)).
+    kp = np.concatenate([kv, np.zeros((1, Dqk))])
+    vp = np.zeros((T + 1, Dv + 1))
+    vp[:T, :Dv] = vv
+    vp[T, Dv] = 1.0
+    maskp = np.concatenate([causal, np.zeros((T, 1))], axis=1)
+    refp = _sdpa(q.transpose(1, 0, 2), np.broadcast_to(kp, (H, T + 1, Dqk)),
+                 np.broadcast_to(vp, (H, T + 1, Dv + 1)), scale, maskp)
+    wprobe = refp[:, :, Dv].T
+    np.testing.assert_allclose(lse, np.log(1.0 / wprobe - 1.0), rtol=1e-10, atol=1e-10)
+
+
+def test_attention_sink_as_extra_key_sdpa():
+    # The sink equals one more key with per-head logit sink_h and a zero value.
+    rng = np.random.default_rng(21)
+    T, H, D = 17, 4, 10
+    q = rng.standard_normal((T, H, D))
+    kv = rng.standard_normal((T, D))
+    sink = rng.standard_normal(H) * 2
+    scale = 0.5
+    idx = _causal_full_indices(T, T)
+    out, lse, mx = O.sparse_attention(q, kv, None, idx, None, sink, scale, d_v=D)
+    causal = np.where(np.tril(np.ones((T, T), dtype=bool)), 0.0, -np.inf)
+    kp = np.concatenate([kv, np.zeros((1, D))])
+    vp = np.concatenate([kv, np.zeros((1, D))])
+    mask = np.zeros((H, T, T + 1))
+    mask[:, :, :T] = causal
+    mask[:, :, T] = sink[:, None]
+    ref = _sdpa(q.transpose(1, 0, 2), np.broadcast_to(kp, (H, T + 1, D)),
+                np.broadcast_to(vp, (H, T + 1, D)), scale, mask)
+    np.testing.assert_allclose(out, ref.transpose(1, 0, 2), rtol=1e-12, atol=1e-13)
+    # the sink does not enter lse or max_logits
+    _, lse0, mx0 = O.sparse_attention(q, kv, None, idx, None, None, scale, d_v=D)
+    np.testing.assert_array_equal(lse, lse0)
+    np.testing.assert_array_equal(mx, mx0)
+
+
+def test_attention_duplicate_slot_is_log2_bias_sdpa():
+    rng = np.random.default_rng(22)
+    Tkv, H, D = 9, 2, 6
+    q = rng.standard_normal((1, H, D))
+    kv = rng.standard_normal((Tkv, D))
+    idx = np.array([[0, 3, 3, 7, 8]])
+    out, _, _ = O.sparse_attention(q, kv, None, idx, None, None, 0.8, d_v=D)
+    keys = np.array([0, 3, 7, 8])
+    mask = np.zeros((1, len(keys)))
+    mask[0, 1] = math.log(2.0)
+    ref = _sdpa(q.transpose(1, 0, 2), np.broadcast_to(kv[keys], (H, 4, D)),
+                np.broadcast_to(kv[keys], (H, 4, D)), 0.8, mask)
+    np.testing.assert_allclose(out[0], ref[:, 0, :], rtol=1e-12, atol=1e-13)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(23)
+    Tkv, H, Dqk, Dv, W = 30, 3, 16, 12, 11
+    kv = rng.standard_normal((Tkv, Dqk))
+    idx = rng.integers(0, Tkv, size=(1, W))
+    # V all ones: every output is 1 without a sink
+    v1 = np.ones((Tkv, Dv))
+    q = rng.standard_normal((1, H, Dqk))
+    out, _, _ = O.sparse_attention(q, kv, v1, idx, None, None, 0.3)
+    np.testing.assert_allclose(out, 1.0, rtol=0, atol=1e-14)
+    # q = 0: lse = ln(n), out = mean of the selected V rows
+    v = rng.standard_normal((Tkv, Dv))
+    out, lse, mx = O.sparse_attention(np.zeros((1, H, Dqk)), kv, v, idx, None, None, 0.3)
+    np.testing.assert_allclose(lse, math.log(W), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(out[0], np.broadcast_to(v[idx[0]].mean(0), (H, Dv)), atol=1e-14)
+    np.testing.assert_array_equal(mx, 0.0)
+    # a single valid slot: out = that V row, lse = max = its scaled logit
+    one = np.array([[-1, 5, -1, 99]])
+    out, lse, mx = O.sparse_attention(q, kv, v, one, None, None, 0.3)
+    np.testing.assert_allclose(out[0], np.broadcast_to(v[5], (H, Dv)), atol=1e-14)
+    s = 0.3 * np.array([sum(q[0, h, d] * kv[5, d] for d in range(Dqk)) for h in range(H)])
+    np.testing.assert_allclose(lse[0], s, atol=1e-13)
+    np.testing.assert_allclose(mx[0], s, atol=1e-13)
+    # sink closed form: out_sink = out / (1 + exp(sink - lse))
+    sink = rng.standard_normal(H)
+    o0, l0, _ = O.sparse_attention(q, kv, v, idx, None, None, 0.3)
+    o1, l1, _ = O.sparse_attention(q, kv, v, idx, None, sink, 0.3)
+    np.testing.assert_allclose(o1, o0 / (1.0 + np.exp(sink[None, :] - l0))[:, :, None], rtol=1e-12)
+    np.testing.assert_array_equal(l0, l1)
+
+
+def test_attention_permutation_and_invalid_slots():
+    rng = np.random.default_rng(24)
+    Tkv, H, D = 40, 2, 9
+    q = rng.standard_normal((1, H, D))
+    kv = rng.standard_normal((Tkv, D))
+    base = np.array([[3, 17, 5, 39, 0]])
+    o0, l0, m0 = O.sparse_attention(q, kv, None, base, None, None, 0.6, d_v=D)
+    perm = np.array([[39, 0, 5, 3, 17]])
+    o1, l1, m1 = O.sparse_attention(q, kv, None, perm, None, None, 0.6, d_v=D)
+    np.testing.assert_allclose(o1, o0, rtol=1e-13)
+    np.testing.assert_allclose(l1, l0, rtol=1e-13)
+    # -1, negative and out-of-range ids, and slots past topk_length are removed
+    noisy = np.array([[3, -1, 17, 40, 5, -7, 39, 1000, 0, 22, 11]])
+    o2, l2, m2 = O.sparse_attention(q, kv, None, noisy, np.array([9]), None, 0.6, d_v=D)
+    np.testing.assert_allclose(o2, o0, rtol=1e-13)
+    np.testing.assert_allclose(l2, l0, rtol=1e-13)
+    np.testing.assert_array_equal(m2, m0)
+
+
+def test_oracle_detects_planted_mistakes():
+    """The pins above must fail for typical slips; plant a few on the CPU."""
+    rng = np.random.default_rng(30)
+    T, H, D = 12, 3, 5
+    q = rng.standard_normal((T, H, D))
+    k = rng.standard_normal((T, D))
+    w = rng.standard_normal((T, H))
+    cu = np.array([0, 5, 12])
+    st, sl = O.packed_metadata(cu, T)
+    good = O.indexer_scores(q, k, w, st, sl, np.arange(T), width=T)
+    brute = _indexer_brute(q, k, w, cu)
+    fin = np.isfinite(brute)
+    # dropped ReLU, sign flip of W and transposed head/dim use all differ
+    no_relu = np.full_like(good, -np.inf)
+    flip = np.full_like(good, -np.inf)
+    for t in range(T):
+        n, s0 = sl[t], st[t]
+        no_relu[t, :n] = w[t] @ (q[t] @ k[s0:s0 + n].T)
+        flip[t, :n] = -(w[t] @ np.maximum(q[t] @ k[s0:s0 + n].T, 0))
+    assert np.allclose(good[fin], brute[fin])
+    assert not np.allclose(no_relu[fin], brute[fin])
+    assert not np.allclose(flip[fin], brute[fin])

@@ -1,0 +1,180 @@
+"""Seeded synthetic workloads for the DSA forward path.
+
+Shapes and value distributions follow the five workloads the pages' kernels are
+sized for: GLM-style sparse MLA (576-dim latent+rope queries over one shared
+576-dim KV row, 512-dim values) with a 64-head x 128-dim lightning indexer and
+K = 2048, and the 12-head x 256-dim block-routed sparse GQA of the Qwen3 QSA
+page. Every tensor is N(0, 1)/sqrt(last dim) in fp32, rounded to bf16 (RNE),
+except the sink (N(0, 1) fp32) and the QSA tensors (N(0, 1)/16).
+
+Tensors are drawn with a torch Generator on the requested device in a fixed
+order: q, kv (or k, v), q_idx, k_idx, w, sink. Document lengths and QSA routes
+come from a numpy Generator seeded from the same seed (drawn first, since the
+token count depends on them). Nothing here evaluates the method.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+# Workloads, in the order the bench and parity tests refer to them.
+CONFIGS = {
+    1: dict(name="tiny_T256", doc_lens=[256], H=16, D_qk=576, D_v=512, shared_kv=True,
+            H_idx=4, D_idx=64, topk=64, scale=1.0 / math.sqrt(576), sink=True),
+    2: dict(name="single_T4096", doc_lens=[4096], H=64, D_qk=576, D_v=512, shared_kv=True,
+            H_idx=64, D_idx=128, topk=2048, scale=1.0 / math.sqrt(576), sink=True),
+    3: dict(name="packed8_U512_4096_H128", doc_lens=None, n_docs=8, doc_len_range=(512, 4096),
+            H=128, D_qk=576, D_v=512, shared_kv=True,
+            H_idx=64, D_idx=128, topk=2048, scale=1.0 / math.sqrt(576), sink=True),
+    4: dict(name="long_T65536", doc_lens=[65536], H=64, D_qk=576, D_v=512, shared_kv=True,
+            H_idx=64, D_idx=128, topk=2048, scale=1.0 / math.sqrt(576), sink=True),
+    5: dict(name="qsa_B4x8192_H12_D256", doc_lens=[8192] * 4, H=12, D_qk=256, D_v=256,
+            shared_kv=False, H_idx=0, D_idx=0, topk=512, scale=1.0 / 16.0, sink=False,
+            qsa=True, value_std=1.0 / 16.0),
+}
+
+
+@dataclass
+class Workload:
+    name: str
+    T: int
+    doc_lens: List[int]
+    cu_seqlens: torch.Tensor          # int32 [n_docs+1]
+    H: int
+    D_qk: int
+    D_v: int
+    shared_kv: bool
+    q: torch.Tensor                   # bf16 [T, H, D_qk]
+    kv: torch.Tensor                  # bf16 [T, D_qk]  (K rows; V = kv[:, :D_v] when shared)
+    v: Optional[torch.Tensor]         # bf16 [T, D_v] when K/V are separate
+    H_idx: int
+    D_idx: int
+    q_idx: Optional[torch.Tensor]     # bf16 [T, H_idx, D_idx]
+    k_idx: Optional[torch.Tensor]     # bf16 [T, D_idx]
+    w: Optional[torch.Tensor]         # bf16 [T, H_idx]
+    sink: Optional[torch.Tensor]      # fp32 [H]
+    topk: int
+    scale: float
+    routes: Optional[torch.Tensor] = None   # int32 [T, W] (block-routed GQA only)
+    seed: int = 0
+    stress: bool = False
+    extra: dict = field(default_factory=dict)
+
+
+def bf16_to_numpy_bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bf16 bit patterns as a numpy uint16 array (host copy)."""
+    assert t.dtype == torch.bfloat16
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _randn(gen, shape, std, device):
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    return (x * std).to(torch.bfloat16)
+
+
+def qsa_routes(doc_lens: List[int], width: int, rng: np.random.Generator,
+               max_blocks: Optional[int] = None) -> np.ndarray:
+    """Four-token block routes for block-routed sparse GQA.
+
+    For the token at position p of a document, the row holds up to
+    (width/4 - 1) distinct complete causal blocks chosen uniformly without
+    replacement from blocks 0..p//4-1 (ascending, four ids each), then the
+    causal tail group [4*(p//4) .. p] padded with -1 to four slots, then -1
+    groups up to `width`. Ids are packed coordinates (document origin + local).
+    """
+    assert width % 4 == 0 and width >= 4
+    groups = width // 4
+    max_blocks = groups - 1 if max_blocks is None else max_blocks
+    T = int(sum(doc_lens))
+    out = np.full((T, width), -1, dtype=np.int32)
+    origin = 0
+    for L in doc_lens:
+        for c0 in range(0, L, 1024):
+            p = np.arange(c0, min(L, c0 + 1024))
+            nb = p // 4
+            m = np.minimum(nb, max_blocks)
+            nmax = int(nb.max()) if len(nb) else 0
+            if nmax > 0:
+                keys = rng.random((len(p), nmax))
+                keys[np.arange(nmax)[None, :] >= nb[:, None]] = np.inf
+                order = np.argsort(keys, axis=1, kind="stable")
+            for r, pos in enumerate(p):
+                row = out[origin + pos]
+                mm = int(m[r])
+                if mm > 0:
+                    blocks = np.sort(order[r, :mm])
+                    ids = (blocks[:, None] * 4 + np.arange(4)[None, :]).reshape(-1)
+                    row[: 4 * mm] = origin + ids
+                tail = np.arange(4 * nb[r], pos + 1)
+                row[4 * mm: 4 * mm + len(tail)] = origin + tail
+        origin += L
+    return out
+
+
+def make_custom(doc_lens, H, D_qk, D_v, shared_kv=True, H_idx=4, D_idx=64, topk=64,
+                scale=None, sink=True, seed=0, device="cpu", routes_width=None,
+                stress=False, value_std=None, name="custom"):
+    """Build a workload of any shape with the same recipe as the named configs."""
+    doc_lens = [int(x) for x in doc_lens]
+    T = int(sum(doc_lens))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(doc_lens)]).astype(np.int32))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    std_qk = value_std if value_std is not None else 1.0 / math.sqrt(D_qk)
+    std_v = value_std if value_std is not None else 1.0 / math.sqrt(D_v)
+    scale = (1.0 / math.sqrt(D_qk)) if scale is None else float(scale)
+    q = _randn(gen, (T, H, D_qk), std_qk, device)
+    kv = _randn(gen, (T, D_qk), std_qk, device)
+    v = None if shared_kv else _randn(gen, (T, D_v), std_v, device)
+    q_idx = k_idx = w = None
+    if H_idx > 0:
+        q_idx = _randn(gen, (T, H_idx, D_idx), 1.0 / math.sqrt(D_idx), device)
+        k_idx = _randn(gen, (T, D_idx), 1.0 / math.sqrt(D_idx), device)
+        w = _randn(gen, (T, H_idx), 1.0 / math.sqrt(H_idx), device)
+    sk = None
+    if sink:
+        sk = torch.randn((H,), generator=gen, device=device, dtype=torch.float32)
+    if stress:
+        # Scaled attention logits with std ~4 instead of ~1/D (softmax far from
+        # uniform), and sinks of the same order as the log-sum-exp.
+        fac = 4.0 / (scale * math.sqrt(D_qk) * std_qk * std_qk)
+        q = (q.float() * fac).to(torch.bfloat16)
+        if sk is not None:
+            sk = sk * 2.0 + 4.0 * math.sqrt(2.0 * math.log(max(topk, 2)))
+    routes = None
+    if routes_width is not None:
+        rng = np.random.default_rng(int(seed) + 7)
+        routes = torch.from_numpy(qsa_routes(doc_lens, routes_width, rng)).to(device)
+    return Workload(name=name, T=T, doc_lens=doc_lens, cu_seqlens=cu.to(device), H=H,
+                    D_qk=D_qk, D_v=D_v, shared_kv=shared_kv, q=q, kv=kv, v=v, H_idx=H_idx,
+                    D_idx=D_idx, q_idx=q_idx, k_idx=k_idx, w=w, sink=sk, topk=topk,
+                    scale=scale, routes=routes, seed=int(seed), stress=stress)
+
+
+def config_doc_lens(i: int, seed=None) -> List[int]:
+    """Document lengths of a named workload (drawn before any tensor)."""
+    c = CONFIGS[i]
+    seed = 1000 + i if seed is None else int(seed)
+    if c.get("doc_lens") is None:
+        lo, hi = c["doc_len_range"]
+        rng = np.random.default_rng(seed)
+        return [int(x) for x in rng.integers(lo, hi, size=c["n_docs"], endpoint=True)]
+    return list(c["doc_lens"])
+
+
+def make_config(i: int, device="cpu", seed=None, stress=False) -> Workload:
+    """One of the five named workloads; seed defaults to 1000 + i."""
+    c = dict(CONFIGS[i])
+    seed = 1000 + i if seed is None else int(seed)
+    doc_lens = config_doc_lens(i, seed)
+    wl = make_custom(doc_lens, c["H"], c["D_qk"], c["D_v"], shared_kv=c["shared_kv"],
+                     H_idx=c["H_idx"], D_idx=c["D_idx"], topk=c["topk"], scale=c["scale"],
+                     sink=c["sink"], seed=seed, device=device,
+                     routes_width=c["topk"] if c.get("qsa") else None, stress=stress,
+                     value_std=c.get("value_std"), name=c["name"] + ("_stress" if stress else ""))
+    return wl
