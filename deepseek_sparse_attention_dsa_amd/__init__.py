@@ -1,0 +1,333 @@
+"""MI355X (gfx950) DeepSeek Sparse Attention forward path.
+
+Python binding of libdsa.so. The functions carry the C ABI's names and only
+marshal arguments: they check torch dtypes, devices and shapes, allocate
+outputs the caller did not pass (torch is used for device memory and streams),
+and enqueue the HIP kernels on the current torch stream. Every step of the
+path runs in the library's kernels; there is no fallback.
+
+Status codes map to the exception classes of the NeMo cudnn_dsa API pages:
+DSA_ERR_TYPE -> TypeError, DSA_ERR_VALUE -> ValueError,
+DSA_ERR_RUNTIME -> RuntimeError.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "DSA_BF16", "DSA_F32", "DSA_MAX_TOPK", "DSA_TOPK_MAX_COLS", "DSA_MAX_HEADS",
+    "load_library", "library_path", "dsa_abi_version", "dsa_last_error",
+    "dsa_packed_metadata", "dsa_indexer_fwd", "dsa_topk", "dsa_sparse_attn_fwd",
+    "indexer_topk", "chunk_rows",
+]
+
+DSA_OK, DSA_ERR_TYPE, DSA_ERR_VALUE, DSA_ERR_RUNTIME = 0, 1, 2, 3
+DSA_BF16, DSA_F32 = 0, 1
+DSA_MAX_TOPK = 2048
+DSA_TOPK_MAX_COLS = 65536
+DSA_MAX_HEADS = 128
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F32 = ctypes.c_float
+
+_SIGNATURES = {
+    "dsa_last_error": ([], ctypes.c_char_p),
+    "dsa_abi_version": ([], ctypes.c_int),
+    "dsa_packed_metadata": ([_P, _I32, _I64, _P, _P, _P], ctypes.c_int),
+    "dsa_indexer_fwd": ([_P, _P, _P, _I32, _P, _P, _I64, _I32, _I32, _I64, _I64, _P, _I64, _P],
+                        ctypes.c_int),
+    "dsa_topk": ([_P, _I64, _I64, _I64, _P, _P, _I32, _P, _I64, _P, _P, _P], ctypes.c_int),
+    "dsa_sparse_attn_fwd": ([_P, _I64, _I32, _I32, _P, _I64, _I64, _P, _I64, _I32, _P, _I64,
+                             _I32, _P, _P, _F32, _P, _P, _P, _P], ctypes.c_int),
+}
+
+
+def library_path() -> str:
+    return os.environ.get("DSA_LIBRARY", os.path.join(_HERE, "libdsa.so"))
+
+
+def load_library(path: Optional[str] = None):
+    """Load libdsa.so (built in-tree by build.py). Raises if it is missing."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or library_path()
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"libdsa.so not found at {p}; build it with "
+            "`python -m deepseek_sparse_attention_dsa_amd.build`")
+    lib = ctypes.CDLL(p)
+    for name, (args, res) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def dsa_abi_version() -> int:
+    return load_library().dsa_abi_version()
+
+
+def dsa_last_error() -> str:
+    return load_library().dsa_last_error().decode()
+
+
+def _check(rc: int):
+    if rc == DSA_OK:
+        return
+    msg = dsa_last_error()
+    if rc == DSA_ERR_TYPE:
+        raise TypeError(msg)
+    if rc == DSA_ERR_VALUE:
+        raise ValueError(msg)
+    raise RuntimeError(msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _need(t, name, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t if t.is_contiguous() else t.contiguous()
+
+
+def _out(t, name, dtype, device):
+    """Validate a caller-provided output buffer (never copied)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name} must have a unit innermost stride")
+    return t
+
+
+def dsa_packed_metadata(cu_seqlens: torch.Tensor, T: int, row_starts=None, seq_lens=None,
+                        stream=None):
+    """Per-token document start and causal length of packed THD sequences."""
+    cu = _need(cu_seqlens, "cu_seqlens", torch.int32)
+    dev = cu.device
+    row_starts = (torch.empty(T, dtype=torch.int32, device=dev) if row_starts is None
+                  else _out(row_starts, "row_starts", torch.int32, dev))
+    seq_lens = (torch.empty(T, dtype=torch.int32, device=dev) if seq_lens is None
+                else _out(seq_lens, "seq_lens", torch.int32, dev))
+    if row_starts.numel() < T or seq_lens.numel() < T:
+        raise ValueError("row_starts and seq_lens need T entries")
+    lib = load_library()
+    _check(lib.dsa_packed_metadata(_ptr(cu), cu.numel() - 1, T, _ptr(row_starts), _ptr(seq_lens),
+                                   _stream(stream)))
+    return row_starts, seq_lens
+
+
+def dsa_indexer_fwd(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
+                    row_starts: torch.Tensor, seq_lens: torch.Tensor, row_begin: int = 0,
+                    n_rows: Optional[int] = None, scores: Optional[torch.Tensor] = None,
+                    width: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Indexer scores [n_rows, ld] fp32 for rows [row_begin, row_begin + n_rows).
+
+    `width` (>= the longest causal length of the rows) sizes a new score
+    buffer; its row stride is rounded up to a multiple of 4.
+    """
+    if not isinstance(w, torch.Tensor) or w.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"w must be a bfloat16 or float32 tensor (got {getattr(w, 'dtype', w)})")
+    q_idx = _need(q_idx, "q_idx", torch.bfloat16)
+    dev = q_idx.device
+    k_idx = _need(k_idx, "k_idx", torch.bfloat16, dev)
+    w = _need(w, "w", w.dtype, dev)
+    row_starts = _need(row_starts, "row_starts", torch.int32, dev)
+    seq_lens = _need(seq_lens, "seq_lens", torch.int32, dev)
+    if q_idx.dim() != 3 or k_idx.dim() != 2 or w.dim() != 2:
+        raise ValueError("expected q_idx [T,H,D], k_idx [T,D], w [T,H]")
+    T, H, D = q_idx.shape
+    if k_idx.shape != (T, D) or w.shape != (T, H):
+        raise ValueError(f"shape mismatch: q_idx {tuple(q_idx.shape)}, k_idx "
+                         f"{tuple(k_idx.shape)}, w {tuple(w.shape)}")
+    if n_rows is None:
+        n_rows = T - row_begin
+    if scores is None:
+        if width is None:
+            width = T
+        ld = max(4, (int(width) + 3) // 4 * 4)
+        scores = torch.empty((n_rows, ld), dtype=torch.float32, device=dev)
+    else:
+        scores = _out(scores, "scores", torch.float32, dev)
+        if scores.dim() != 2 or scores.shape[0] < n_rows:
+            raise ValueError("scores must be 2-D with at least n_rows rows")
+    lib = load_library()
+    _check(lib.dsa_indexer_fwd(_ptr(q_idx), _ptr(k_idx), _ptr(w),
+                               DSA_BF16 if w.dtype == torch.bfloat16 else DSA_F32,
+                               _ptr(row_starts), _ptr(seq_lens), T, H, D, row_begin, n_rows,
+                               _ptr(scores), scores.stride(0), _stream(stream)))
+    return scores
+
+
+def dsa_topk(scores: torch.Tensor, seq_lens: torch.Tensor, k: int,
+             row_starts: Optional[torch.Tensor] = None, n_cols: Optional[int] = None,
+             indices: Optional[torch.Tensor] = None, topk_length: Optional[torch.Tensor] = None,
+             return_values: bool = False, stream=None):
+    """Top-k per row -> (indices int32 [n_rows, k], topk_length int32 [n_rows], values|None)."""
+    if not isinstance(scores, torch.Tensor) or scores.dtype != torch.float32:
+        raise TypeError("scores must be a float32 tensor")
+    if scores.dim() != 2 or scores.stride(1) != 1:
+        raise ValueError("scores must be 2-D with unit column stride")
+    dev = scores.device
+    n_rows = scores.shape[0]
+    n_cols = scores.shape[1] if n_cols is None else int(n_cols)
+    seq_lens = _need(seq_lens, "seq_lens", torch.int32, dev)
+    if seq_lens.numel() != n_rows:
+        raise ValueError("seq_lens must have one entry per score row")
+    if row_starts is not None:
+        row_starts = _need(row_starts, "row_starts", torch.int32, dev)
+        if row_starts.numel() != n_rows:
+            raise ValueError("row_starts must have one entry per score row")
+    indices = (torch.empty((n_rows, k), dtype=torch.int32, device=dev) if indices is None
+               else _out(indices, "indices", torch.int32, dev))
+    topk_length = (torch.empty((n_rows,), dtype=torch.int32, device=dev) if topk_length is None
+                   else _out(topk_length, "topk_length", torch.int32, dev))
+    values = torch.empty((n_rows, indices.stride(0)), dtype=torch.float32,
+                         device=dev)[:, :k] if return_values else None
+    lib = load_library()
+    _check(lib.dsa_topk(_ptr(scores), scores.stride(0), n_rows, n_cols, _ptr(seq_lens),
+                        _ptr(row_starts), k, _ptr(indices), indices.stride(0), _ptr(topk_length),
+                        _ptr(values), _stream(stream)))
+    return indices, topk_length, values
+
+
+def dsa_sparse_attn_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,
+                        topk_length: Optional[torch.Tensor] = None,
+                        attn_sink: Optional[torch.Tensor] = None,
+                        softmax_scale: Optional[float] = None, v: Optional[torch.Tensor] = None,
+                        d_v: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None,
+                        max_logits: Optional[torch.Tensor] = None,
+                        return_max_logits: bool = True, stream=None):
+    """Sparse attention forward -> (out bf16 [T_q,H,D_v], lse fp32 [T_q,H], max_logits|None).
+
+    kv: [T_kv, D_qk] (or [T_kv, 1, D_qk]) key rows; V = kv[:, :d_v] unless a
+    separate v [T_kv, D_v] is given. d_v defaults to 512 for D_qk = 576 and to
+    D_qk otherwise. softmax_scale defaults to 1/sqrt(D_qk).
+    """
+    q = _need(q, "q", torch.bfloat16)
+    dev = q.device
+    if kv.dim() == 3 and kv.shape[1] == 1:
+        kv = kv[:, 0, :]
+    kv = _need(kv, "kv", torch.bfloat16, dev)
+    if v is not None:
+        if v.dim() == 3 and v.shape[1] == 1:
+            v = v[:, 0, :]
+        v = _need(v, "v", torch.bfloat16, dev)
+    if indices.dim() == 3 and indices.shape[1] == 1:
+        indices = indices[:, 0, :]
+    indices = _need(indices, "indices", torch.int32, dev)
+    if topk_length is not None:
+        topk_length = _need(topk_length, "topk_length", torch.int32, dev)
+    if attn_sink is not None:
+        attn_sink = _need(attn_sink, "attn_sink", torch.float32, dev)
+    if q.dim() != 3 or kv.dim() != 2 or indices.dim() != 2:
+        raise ValueError("expected q [T_q,H,D_qk], kv [T_kv,D_qk], indices [T_q,K]")
+    T_q, H, D_qk = q.shape
+    if kv.shape[1] != D_qk or indices.shape[0] != T_q:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, kv {tuple(kv.shape)}, "
+                         f"indices {tuple(indices.shape)}")
+    if v is not None:
+        d_v = v.shape[1]
+        if v.shape[0] != kv.shape[0]:
+            raise ValueError("v and kv must have the same number of rows")
+    elif d_v is None:
+        d_v = 512 if D_qk == 576 else D_qk
+    if attn_sink is not None and attn_sink.numel() != H:
+        raise ValueError("attn_sink must have one entry per head")
+    if topk_length is not None and topk_length.numel() != T_q:
+        raise ValueError("topk_length must have one entry per query row")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D_qk)
+    out = (torch.empty((T_q, H, d_v), dtype=torch.bfloat16, device=dev) if out is None
+           else _out(out, "out", torch.bfloat16, dev))
+    if not out.is_contiguous() or out.shape != (T_q, H, d_v):
+        raise ValueError("out must be a contiguous [T_q, H, D_v] tensor")
+    lse = (torch.empty((T_q, H), dtype=torch.float32, device=dev) if lse is None
+           else _out(lse, "lse", torch.float32, dev))
+    if max_logits is None and return_max_logits:
+        max_logits = torch.empty((T_q, H), dtype=torch.float32, device=dev)
+    elif max_logits is not None:
+        max_logits = _out(max_logits, "max_logits", torch.float32, dev)
+    for name, t in (("lse", lse), ("max_logits", max_logits)):
+        if t is not None and (not t.is_contiguous() or t.shape != (T_q, H)):
+            raise ValueError(f"{name} must be a contiguous [T_q, H] tensor")
+    lib = load_library()
+    _check(lib.dsa_sparse_attn_fwd(
+        _ptr(q), T_q, H, D_qk, _ptr(kv), kv.shape[0], kv.stride(0), _ptr(v),
+        0 if v is None else v.stride(0), d_v, _ptr(indices), indices.stride(0), indices.shape[1],
+        _ptr(topk_length), _ptr(attn_sink), float(softmax_scale), _ptr(out), _ptr(lse),
+        _ptr(max_logits), _stream(stream)))
+    return out, lse, max_logits
+
+
+# Score-buffer cap per chunk of rows (2 GiB, the cap the NeMo cudnn_dsa page
+# applies to its score / top-K scratch).
+SCORE_CHUNK_BYTES = 2 * 1024 * 1024 * 1024
+
+
+def chunk_rows(T: int, width: int, cap_bytes: int = SCORE_CHUNK_BYTES) -> int:
+    """Rows per score chunk so that [rows, width] fp32 stays under the cap."""
+    ld = max(4, (int(width) + 3) // 4 * 4)
+    return max(1, min(T, cap_bytes // (4 * ld)))
+
+
+def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
+                 cu_seqlens: torch.Tensor, k: int, max_seqlen: Optional[int] = None,
+                 rows_per_chunk: Optional[int] = None, stream=None):
+    """Metadata + indexer scores + top-K over all rows, in score chunks.
+
+    Returns (indices int32 [T, k] global ascending with -1 suffix,
+    topk_length int32 [T]). max_seqlen (the longest document) sizes each
+    chunk's score buffer; it defaults to T.
+    """
+    T = q_idx.shape[0]
+    dev = q_idx.device
+    width = T if max_seqlen is None else int(max_seqlen)
+    rows = chunk_rows(T, width) if rows_per_chunk is None else int(rows_per_chunk)
+    row_starts, seq_lens = dsa_packed_metadata(cu_seqlens, T, stream=stream)
+    indices = torch.empty((T, k), dtype=torch.int32, device=dev)
+    topk_length = torch.empty((T,), dtype=torch.int32, device=dev)
+    ld = max(4, (width + 3) // 4 * 4)
+    scores = torch.empty((min(rows, T), ld), dtype=torch.float32, device=dev)
+    for r0 in range(0, T, rows):
+        n = min(rows, T - r0)
+        dsa_indexer_fwd(q_idx, k_idx, w, row_starts, seq_lens, row_begin=r0, n_rows=n,
+                        scores=scores, stream=stream)
+        dsa_topk(scores[:n], seq_lens[r0:r0 + n], k, row_starts=row_starts[r0:r0 + n],
+                 n_cols=width, indices=indices[r0:r0 + n], topk_length=topk_length[r0:r0 + n],
+                 stream=stream)
+    return indices, topk_length
+

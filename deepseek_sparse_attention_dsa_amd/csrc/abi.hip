@@ -1,0 +1,190 @@
+// C ABI of the DSA forward path: host-side validation, device check, launch.
+// Every argument check runs before any HIP call, so a bad call returns its
+// status without touching the runtime. Nothing here allocates or synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/dsa.h"
+#include "dsa_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// 1 = gfx950, 0 = other arch, cached per device ordinal.
+constexpr int kMaxDev = 64;
+int g_arch_ok[kMaxDev];
+std::once_flag g_arch_once[kMaxDev];
+
+int check_device(const char* fn) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDev)
+    return fail(DSA_ERR_RUNTIME, "%s: no HIP device is current (%s)", fn, hipGetErrorString(e));
+  std::call_once(g_arch_once[dev], [dev]() {
+    hipDeviceProp_t prop;
+    g_arch_ok[dev] = 0;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess)
+      g_arch_ok[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+  });
+  if (!g_arch_ok[dev])
+    return fail(DSA_ERR_RUNTIME, "%s: device %d is not a gfx950 (MI355X) GPU", fn, dev);
+  return DSA_OK;
+}
+
+int launched(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(DSA_ERR_RUNTIME, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_last_error(void) { return g_err; }
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+int dsa_packed_metadata(const int32_t* cu_seqlens, int32_t n_seq, int64_t T, int32_t* row_starts,
+                        int32_t* seq_lens, void* stream) {
+  const char* fn = "dsa_packed_metadata";
+  REQUIRE(n_seq >= 1, DSA_ERR_VALUE, "%s: n_seq must be >= 1 (got %d)", fn, n_seq);
+  REQUIRE(T >= 0 && T <= INT32_MAX, DSA_ERR_VALUE, "%s: T must be in [0, 2^31-1] (got %lld)", fn,
+          (long long)T);
+  if (T == 0) return DSA_OK;
+  REQUIRE(cu_seqlens && row_starts && seq_lens, DSA_ERR_VALUE, "%s: NULL pointer argument", fn);
+  if (int rc = check_device(fn)) return rc;
+  return launched(fn, dsa::launch_packed_metadata(cu_seqlens, n_seq, T, row_starts, seq_lens,
+                                                  (hipStream_t)stream));
+}
+
+int dsa_indexer_fwd(const void* q_idx, const void* k_idx, const void* w, int32_t w_dtype,
+                    const int32_t* row_starts, const int32_t* seq_lens, int64_t T, int32_t H_idx,
+                    int32_t D_idx, int64_t row_begin, int64_t n_rows, float* scores,
+                    int64_t ld_scores, void* stream) {
+  const char* fn = "dsa_indexer_fwd";
+  REQUIRE(w_dtype == DSA_BF16 || w_dtype == DSA_F32, DSA_ERR_TYPE,
+          "%s: w_dtype must be DSA_BF16 or DSA_F32 (got %d)", fn, w_dtype);
+  REQUIRE(H_idx >= 1 && H_idx <= 64, DSA_ERR_VALUE, "%s: H_idx must be in [1, 64] (got %d)", fn,
+          H_idx);
+  REQUIRE(D_idx == 64 || D_idx == 128, DSA_ERR_VALUE, "%s: D_idx must be 64 or 128 (got %d)", fn,
+          D_idx);
+  REQUIRE(T >= 0 && T <= INT32_MAX, DSA_ERR_VALUE, "%s: T must be in [0, 2^31-1]", fn);
+  REQUIRE(row_begin >= 0 && n_rows >= 0 && row_begin + n_rows <= T, DSA_ERR_VALUE,
+          "%s: rows [%lld, %lld) outside [0, T=%lld)", fn, (long long)row_begin,
+          (long long)(row_begin + n_rows), (long long)T);
+  REQUIRE(ld_scores >= 4 && ld_scores % 4 == 0, DSA_ERR_VALUE,
+          "%s: ld_scores must be a positive multiple of 4 (got %lld)", fn, (long long)ld_scores);
+  if (n_rows == 0) return DSA_OK;
+  REQUIRE(q_idx && k_idx && w && row_starts && seq_lens && scores, DSA_ERR_VALUE,
+          "%s: NULL pointer argument", fn);
+  REQUIRE(aligned(q_idx, 16) && aligned(k_idx, 16) && aligned(scores, 16), DSA_ERR_VALUE,
+          "%s: q_idx, k_idx and scores must be 16-byte aligned", fn);
+  REQUIRE(aligned(w, w_dtype == DSA_F32 ? 4 : 2), DSA_ERR_VALUE, "%s: w misaligned", fn);
+  REQUIRE(n_rows <= (int64_t)8 * INT32_MAX, DSA_ERR_VALUE, "%s: too many rows", fn);
+  if (int rc = check_device(fn)) return rc;
+  return launched(fn, dsa::launch_indexer(q_idx, k_idx, w, w_dtype, row_starts, seq_lens, T, H_idx,
+                                          D_idx, row_begin, n_rows, scores, ld_scores,
+                                          (hipStream_t)stream));
+}
+
+int dsa_topk(const float* scores, int64_t ld_scores, int64_t n_rows, int64_t n_cols,
+             const int32_t* seq_lens, const int32_t* row_starts, int32_t k, int32_t* indices,
+             int64_t ld_indices, int32_t* topk_length, float* values, void* stream) {
+  const char* fn = "dsa_topk";
+  REQUIRE(k >= 1 && k <= DSA_MAX_TOPK, DSA_ERR_VALUE, "%s: k must be in [1, %d] (got %d)", fn,
+          DSA_MAX_TOPK, k);
+  REQUIRE(n_cols >= 1 && n_cols <= DSA_TOPK_MAX_COLS, DSA_ERR_VALUE,
+          "%s: n_cols must be in [1, %d] (got %lld)", fn, DSA_TOPK_MAX_COLS, (long long)n_cols);
+  REQUIRE(ld_scores >= n_cols && ld_scores % 4 == 0, DSA_ERR_VALUE,
+          "%s: ld_scores must be >= n_cols and a multiple of 4 (got %lld)", fn,
+          (long long)ld_scores);
+  REQUIRE(ld_indices >= k, DSA_ERR_VALUE, "%s: ld_indices (%lld) < k (%d)", fn,
+          (long long)ld_indices, k);
+  REQUIRE(n_rows >= 0 && n_rows <= INT32_MAX, DSA_ERR_VALUE, "%s: n_rows out of range", fn);
+  if (n_rows == 0) return DSA_OK;
+  REQUIRE(scores && seq_lens && indices, DSA_ERR_VALUE, "%s: NULL pointer argument", fn);
+  REQUIRE(aligned(scores, 16), DSA_ERR_VALUE, "%s: scores must be 16-byte aligned", fn);
+  if (int rc = check_device(fn)) return rc;
+  return launched(fn, dsa::launch_topk(scores, ld_scores, n_rows, n_cols, seq_lens, row_starts, k,
+                                       indices, ld_indices, topk_length, values,
+                                       (hipStream_t)stream));
+}
+
+int dsa_sparse_attn_fwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk, const void* k,
+                        int64_t T_kv, int64_t ld_k, const void* v, int64_t ld_v, int32_t D_v,
+                        const int32_t* indices, int64_t ld_indices, int32_t k_width,
+                        const int32_t* topk_length, const float* attn_sink, float softmax_scale,
+                        void* out, float* lse, float* max_logits, void* stream) {
+  const char* fn = "dsa_sparse_attn_fwd";
+  REQUIRE(H >= 1 && H <= DSA_MAX_HEADS, DSA_ERR_VALUE, "%s: H must be in [1, %d] (got %d)", fn,
+          DSA_MAX_HEADS, H);
+  const bool dims_ok = (D_qk == 576 && D_v == 512) || (D_qk == 512 && D_v == 512) ||
+                       (D_qk == 256 && D_v == 256);
+  REQUIRE(dims_ok, DSA_ERR_VALUE,
+          "%s: (D_qk, D_v) must be (576, 512), (512, 512) or (256, 256) (got (%d, %d))", fn, D_qk,
+          D_v);
+  REQUIRE(!(D_qk == 576 && v != nullptr), DSA_ERR_VALUE,
+          "%s: D_qk = 576 is shared latent KV; pass v = NULL (V = kv[:, :512])", fn);
+  REQUIRE(v == nullptr || v == k || D_qk == 256, DSA_ERR_VALUE,
+          "%s: a separate V tensor is supported for D_qk = D_v = 256 only", fn);
+  REQUIRE(T_q >= 0 && T_q <= INT32_MAX, DSA_ERR_VALUE, "%s: T_q out of range", fn);
+  REQUIRE(T_kv >= 0 && T_kv <= INT32_MAX, DSA_ERR_VALUE, "%s: T_kv out of range", fn);
+  REQUIRE(ld_k >= D_qk && ld_k % 8 == 0, DSA_ERR_VALUE,
+          "%s: ld_k must be >= D_qk and a multiple of 8 (got %lld)", fn, (long long)ld_k);
+  if (v) {
+    REQUIRE(ld_v >= D_v && ld_v % 8 == 0, DSA_ERR_VALUE,
+            "%s: ld_v must be >= D_v and a multiple of 8 (got %lld)", fn, (long long)ld_v);
+  }
+  REQUIRE(ld_indices >= 1 && k_width >= 0 && k_width <= ld_indices, DSA_ERR_VALUE,
+          "%s: need 0 <= k_width <= ld_indices (got %d, %lld)", fn, k_width,
+          (long long)ld_indices);
+  REQUIRE(isfinite(softmax_scale) && softmax_scale > 0.0f, DSA_ERR_VALUE,
+          "%s: softmax_scale must be finite and > 0", fn);
+  if (T_q == 0) return DSA_OK;
+  REQUIRE(q && (indices || k_width == 0) && out && lse && (k || T_kv == 0), DSA_ERR_VALUE,
+          "%s: NULL pointer argument", fn);
+  REQUIRE(aligned(q, 16) && aligned(out, 16) && aligned(k, 16) && aligned(v, 16), DSA_ERR_VALUE,
+          "%s: q, k, v and out must be 16-byte aligned", fn);
+  if (int rc = check_device(fn)) return rc;
+  dsa::AttnArgs a;
+  a.q = (const uint16_t*)q;
+  a.T_q = T_q;
+  a.H = H;
+  a.k = (const uint16_t*)k;
+  a.T_kv = k ? T_kv : 0;
+  a.ld_k = ld_k;
+  a.v = v ? (const uint16_t*)v : (const uint16_t*)k;
+  a.ld_v = v ? ld_v : ld_k;
+  a.indices = indices;
+  a.ld_idx = ld_indices;
+  a.k_width = k_width;
+  a.topk_length = topk_length;
+  a.sink = attn_sink;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.out = (uint16_t*)out;
+  a.lse = lse;
+  a.max_logits = max_logits;
+  return launched(fn, dsa::launch_sparse_attn(a, D_qk, D_v, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Internal host-side launchers behind the C ABI (one per kernel family).
+// Arguments are assumed validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+hipError_t launch_packed_metadata(const int32_t* cu, int32_t n_seq, int64_t T, int32_t* row_starts,
+                                  int32_t* seq_lens, hipStream_t st);
+
+hipError_t launch_indexer(const void* q, const void* k, const void* w, int w_dtype,
+                          const int32_t* row_starts, const int32_t* seq_lens, int64_t T, int H,
+                          int D, int64_t row_begin, int64_t n_rows, float* scores, int64_t ld,
+                          hipStream_t st);
+
+hipError_t launch_topk(const float* scores, int64_t ld, int64_t n_rows, int64_t n_cols,
+                       const int32_t* seq_lens, const int32_t* row_starts, int k, int32_t* indices,
+                       int64_t ld_idx, int32_t* topk_length, float* values, hipStream_t st);
+
+struct AttnArgs {
+  const uint16_t* q;
+  int64_t T_q;
+  int H;
+  const uint16_t* k;
+  int64_t T_kv;
+  int64_t ld_k;
+  const uint16_t* v;  // never null here: the ABI layer substitutes k for shared KV
+  int64_t ld_v;
+  const int32_t* indices;
+  int64_t ld_idx;
+  int k_width;
+  const int32_t* topk_length;
+  const float* sink;
+  float scale_log2;  // softmax_scale * log2(e)
+  uint16_t* out;
+  float* lse;
+  float* max_logits;
+};
+
+hipError_t launch_sparse_attn(const AttnArgs& a, int D_qk, int D_v, hipStream_t st);
+
+}  // namespace dsa

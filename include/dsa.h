@@ -1,0 +1,180 @@
+/*
+ * dsa.h - C ABI of the MI355X (gfx950) DeepSeek Sparse Attention forward path.
+ *
+ * Four stream-ordered calls cover the forward hot path of DSA:
+ *   dsa_packed_metadata  per-token document start and causal length (THD)
+ *   dsa_indexer_fwd      lightning-indexer scores  sum_h W_h * ReLU(q_h . k)
+ *   dsa_topk             per-row top-K select, ascending global indices, -1 pad
+ *   dsa_sparse_attn_fwd  sparse MQA/GQA attention over the selected KV rows
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pointers marked "device" are device pointers on the current HIP device.
+ *   The caller owns every buffer (inputs and outputs). The library never
+ *   allocates, frees or synchronises inside these calls; work is enqueued on
+ *   `stream` (a hipStream_t passed as void*; NULL = the legacy default stream)
+ *   and the call returns before it runs.
+ * - Arguments are validated on the host before anything is launched. On a bad
+ *   argument the call returns a non-OK status, launches nothing, and
+ *   dsa_last_error() describes the problem. Values that live in device memory
+ *   (cu_seqlens monotonicity, index ranges) are not checked on the host; the
+ *   kernels treat out-of-range indices as invalid slots instead.
+ * - Status codes: DSA_ERR_TYPE for an unknown dtype enum, DSA_ERR_VALUE for a
+ *   shape, size, pointer, alignment or scale that is out of contract,
+ *   DSA_ERR_RUNTIME when no gfx950 device is current or a launch fails.
+ * - bf16 means IEEE-754 binary32 truncated to its upper 16 bits (bfloat16).
+ *
+ * Source of the semantics: the cuDNN Frontend page "DeepSeek Sparse Attention
+ * (DSA)" (sections 1, 3, 4 and 5) and the NeMo AutoModel API pages for
+ * nemo_automodel...glm_moe_dsa.kernels.cudnn_dsa (cudnn_indexer_topk,
+ * cudnn_sparse_attention, prepare_cudnn_dsa_packed_metadata) and
+ * nemo_automodel...qwen3_8_flash_next.cudnn_qsa (cudnn_sparse_gqa_attention).
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_TYPE = 1,    /* bad dtype enum                                  */
+  DSA_ERR_VALUE = 2,   /* bad shape / size / pointer / alignment / scale  */
+  DSA_ERR_RUNTIME = 3  /* no gfx950 device current, or a launch failed    */
+} dsa_status;
+
+typedef enum { DSA_BF16 = 0, DSA_F32 = 1 } dsa_dtype;
+
+/* Message for the last non-OK status returned on the calling thread
+ * (thread-local, valid until the next call on that thread). Never NULL. */
+const char* dsa_last_error(void);
+
+/* ABI version of this header (bumped on any signature change). */
+#define DSA_ABI_VERSION 1
+int dsa_abi_version(void);
+
+/* Limits enforced by the host checks. */
+#define DSA_MAX_TOPK 2048           /* top_k <= 2048 (DSA page, section 5)  */
+#define DSA_TOPK_MAX_COLS 65536     /* longest score row dsa_topk selects on */
+#define DSA_MAX_HEADS 128           /* attention query heads per call        */
+
+/*
+ * dsa_packed_metadata - step a0.
+ * For compact packed THD sequences (cudnn_dsa page,
+ * prepare_cudnn_dsa_packed_metadata: per-query starts and real causal
+ * lengths; causality restarts at each document):
+ *   row_starts[t] = cu_seqlens[d], seq_lens[t] = t - cu_seqlens[d] + 1
+ * where d is the document holding token t (cu_seqlens[d] <= t < cu_seqlens[d+1]).
+ *   cu_seqlens  device int32 [n_seq + 1], cu_seqlens[0] = 0, non-decreasing,
+ *               cu_seqlens[n_seq] = T (not checked on the host)
+ *   row_starts, seq_lens  device int32 [T] outputs
+ * Errors: n_seq < 1, T < 0 or T > INT32_MAX, a NULL pointer with T > 0.
+ * T = 0 is a no-op.
+ */
+int dsa_packed_metadata(const int32_t* cu_seqlens, int32_t n_seq, int64_t T,
+                        int32_t* row_starts, int32_t* seq_lens, void* stream);
+
+/*
+ * dsa_indexer_fwd - step a1, lightning-indexer scores.
+ * DSA page section 3 with ratio 1 and no causal offsets: for query row t and
+ * local key column j < seq_lens[t],
+ *   scores[t - row_begin, j] = sum_h W[t, h] * max(0, sum_d q_idx[t, h, d] * k_idx[row_starts[t] + j, d])
+ * The indexer key has a single head shared by all H_idx query heads. No
+ * scaling is applied inside: W already carries any 1/sqrt(H) and 1/sqrt(D)
+ * factors (cudnn_dsa page, cudnn_indexer_topk, head_weights).
+ *   q_idx       device bf16 [T, H_idx, D_idx], contiguous
+ *   k_idx       device bf16 [T, D_idx], contiguous
+ *   w           device [T, H_idx], dtype w_dtype (DSA_BF16 or DSA_F32)
+ *   row_starts, seq_lens  device int32 [T] (from dsa_packed_metadata)
+ *   T, H_idx, D_idx       H_idx in [1, 64], D_idx in {64, 128}
+ *   row_begin, n_rows     rows [row_begin, row_begin + n_rows) of T; the
+ *                         caller chunks rows to bound the score buffer
+ *   scores      device fp32 [n_rows, ld_scores] output, 16-byte aligned,
+ *               ld_scores % 4 == 0. Only columns j < min(seq_lens[t],
+ *               ld_scores) are written; later columns are left untouched, so
+ *               ld_scores must be at least the longest causal length of the
+ *               chunk for every key to be scored.
+ * fp32 accumulation of bf16 products (MFMA), fp32 epilogue.
+ */
+int dsa_indexer_fwd(const void* q_idx, const void* k_idx, const void* w, int32_t w_dtype,
+                    const int32_t* row_starts, const int32_t* seq_lens, int64_t T,
+                    int32_t H_idx, int32_t D_idx, int64_t row_begin, int64_t n_rows,
+                    float* scores, int64_t ld_scores, void* stream);
+
+/*
+ * dsa_topk - steps a2 + a3, radix top-K with per-row length, compaction and
+ * local -> global conversion.
+ * DSA page section 5 (radix top-K over input_values (n_rows, num_cols) with a
+ * per-row effective length) and section 4 (deterministic tie-break: exact
+ * ties at the K-th boundary go to the smallest column); cudnn_dsa page
+ * (global coordinates, ascending valid prefix, -1 suffix).
+ * For row r with n = clamp(seq_lens[r], 0, n_cols):
+ *   n <= k : the selection is every column 0..n-1;
+ *   n >  k : the k largest of scores[r, 0..n-1], ties to the lower column;
+ *            -0.0 and +0.0 are equal values.
+ *   indices[r, 0..m-1] = row_starts[r] + selected columns in ascending order
+ *   (plain column ids when row_starts is NULL), indices[r, m..k-1] = -1,
+ *   m = min(n, k); topk_length[r] = m; values[r, i] = the selected score
+ *   (-inf in padded slots).
+ *   scores      device fp32 [n_rows, ld_scores], 16-byte aligned, ld % 4 == 0
+ *   n_cols      1..DSA_TOPK_MAX_COLS, n_cols <= ld_scores
+ *   seq_lens    device int32 [n_rows]
+ *   row_starts  device int32 [n_rows] or NULL
+ *   k           1..DSA_MAX_TOPK
+ *   indices     device int32 [n_rows, ld_indices] output, ld_indices >= k
+ *   topk_length device int32 [n_rows] output or NULL
+ *   values      device fp32 [n_rows, ld_indices] output or NULL
+ * Scores must not be NaN (NaN order is unspecified).
+ */
+int dsa_topk(const float* scores, int64_t ld_scores, int64_t n_rows, int64_t n_cols,
+             const int32_t* seq_lens, const int32_t* row_starts, int32_t k,
+             int32_t* indices, int64_t ld_indices, int32_t* topk_length, float* values,
+             void* stream);
+
+/*
+ * dsa_sparse_attn_fwd - steps a4 / a5, sparse attention forward.
+ * DSA page section 1: for query row t, head h and slot j < L_t, where
+ * L_t = clamp(topk_length[t], 0, k_width) (k_width when topk_length is NULL),
+ * slot j is valid iff 0 <= indices[t, j] < T_kv; invalid slots have score
+ * -inf, duplicates stay distinct slots. With s_j = scale * q[t,h,:D_qk] . K[idx_j,:D_qk]:
+ *   max_logits[t,h] = max_j s_j
+ *   lse[t,h]        = ln sum_j exp(s_j)          (KV-only, excludes the sink)
+ *   out[t,h,:]      = sum_j exp(s_j) V[idx_j,:D_v] / (sum_j exp(s_j) + exp(sink_h))
+ * The sink is a per-head fp32 logit in scaled units that enters only the
+ * output denominator (attn_sink NULL == -inf). A row with no valid slot gets
+ * out = 0, max_logits = -inf, lse = +inf.
+ *   q          device bf16 [T_q, H, D_qk], contiguous; H in [1, DSA_MAX_HEADS]
+ *   k          device bf16 [T_kv, ld_k] key rows (shared latent KV for MLA)
+ *   v          device bf16 [T_kv, ld_v] value rows, or NULL: V = k[:, :D_v]
+ *              (D_qk = 576 uses the first 512 KV dims as V; section 1)
+ *   (D_qk, D_v) in {(576, 512), (512, 512), (256, 256)}
+ *   indices    device int32 [T_q, ld_indices], global KV row ids, -1 invalid
+ *              (may be NULL when k_width = 0)
+ *   k_width    0..ld_indices slots per row (0: every row is empty)
+ *   topk_length device int32 [T_q] or NULL (compact prefix lengths)
+ *   attn_sink  device fp32 [H] or NULL
+ *   softmax_scale finite, > 0 (callers default it to 1/sqrt(D_qk))
+ *   out        device bf16 [T_q, H, D_v] output
+ *   lse        device fp32 [T_q, H] output (natural log)
+ *   max_logits device fp32 [T_q, H] output or NULL
+ * k, v, q, out need 16-byte alignment; ld_k, ld_v multiples of 8 elements.
+ * Softmax in fp32 (exp2 domain), bf16 MFMA for q.k and p.v, fp32 accumulation,
+ * output rounded to bf16 (round to nearest even).
+ */
+int dsa_sparse_attn_fwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk,
+                        const void* k, int64_t T_kv, int64_t ld_k,
+                        const void* v, int64_t ld_v, int32_t D_v,
+                        const int32_t* indices, int64_t ld_indices, int32_t k_width,
+                        const int32_t* topk_length, const float* attn_sink,
+                        float softmax_scale, void* out, float* lse, float* max_logits,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

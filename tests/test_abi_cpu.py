@@ -1,0 +1,175 @@
+"""C ABI checks that need no GPU: exports, version, host-side validation.
+
+Argument validation runs before any HIP call, so bad calls return their status
+without a device. Every call here passes fake (never dereferenced) pointers, so
+all of them run in a child process with every GPU hidden: even a missing check
+can then only reach the device lookup and report DSA_ERR_RUNTIME.
+"""
+
+import json
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+import deepseek_sparse_attention_dsa_amd as dsa  # noqa: E402
+
+OK, ETYPE, EVALUE, ERUNTIME = 0, 1, 2, 3
+FAKE = 1 << 20      # 16-byte aligned
+FAKE2 = 3 << 20     # a second, distinct fake buffer
+
+TOPK_BASE = dict(scores=FAKE, ld=4096, n_rows=8, n_cols=4096, seq_lens=FAKE, row_starts=None,
+                 k=64, indices=FAKE, ld_idx=64, tl=None, vals=None, stream=None)
+IDX_BASE = dict(q=FAKE, k=FAKE, w=FAKE, wd=0, rs=FAKE, sl=FAKE, T=256, H=4, D=64, rb=0, nr=256,
+                scores=FAKE, ld=256, stream=None)
+ATTN_BASE = dict(q=FAKE, Tq=16, H=16, Dqk=576, k=FAKE, Tkv=16, ldk=576, v=None, ldv=0, Dv=512,
+                 idx=FAKE, ldi=64, kw=64, tl=None, sink=None, scale=0.04, out=FAKE, lse=FAKE,
+                 mx=None, stream=None)
+META_BASE = dict(cu=FAKE, n_seq=1, T=4, rs=FAKE, sl=FAKE, stream=None)
+
+ORDER = {
+    "topk": ["scores", "ld", "n_rows", "n_cols", "seq_lens", "row_starts", "k", "indices",
+             "ld_idx", "tl", "vals", "stream"],
+    "idx": ["q", "k", "w", "wd", "rs", "sl", "T", "H", "D", "rb", "nr", "scores", "ld", "stream"],
+    "attn": ["q", "Tq", "H", "Dqk", "k", "Tkv", "ldk", "v", "ldv", "Dv", "idx", "ldi", "kw", "tl",
+             "sink", "scale", "out", "lse", "mx", "stream"],
+    "meta": ["cu", "n_seq", "T", "rs", "sl", "stream"],
+}
+BASE = {"topk": TOPK_BASE, "idx": IDX_BASE, "attn": ATTN_BASE, "meta": META_BASE}
+FN = {"topk": "dsa_topk", "idx": "dsa_indexer_fwd", "attn": "dsa_sparse_attn_fwd",
+      "meta": "dsa_packed_metadata"}
+
+CASES = [
+    # top-K
+    ("topk", dict(k=0), EVALUE), ("topk", dict(k=2049), EVALUE), ("topk", dict(n_cols=0), EVALUE),
+    ("topk", dict(n_cols=65537, ld=65540), EVALUE), ("topk", dict(ld=4095), EVALUE),
+    ("topk", dict(ld=4094, n_cols=4094), EVALUE), ("topk", dict(ld_idx=63), EVALUE),
+    ("topk", dict(n_rows=-1), EVALUE), ("topk", dict(scores=None), EVALUE),
+    ("topk", dict(seq_lens=None), EVALUE), ("topk", dict(indices=None), EVALUE),
+    ("topk", dict(scores=FAKE + 4), EVALUE),
+    ("topk", dict(n_rows=0, scores=None, seq_lens=None, indices=None), OK),
+    ("topk", dict(), ERUNTIME),
+    # indexer
+    ("idx", dict(wd=5), ETYPE), ("idx", dict(H=0), EVALUE), ("idx", dict(H=65), EVALUE),
+    ("idx", dict(D=96), EVALUE), ("idx", dict(rb=200, nr=100), EVALUE),
+    ("idx", dict(ld=254), EVALUE), ("idx", dict(q=None), EVALUE), ("idx", dict(k=FAKE + 2), EVALUE),
+    ("idx", dict(scores=FAKE + 8), EVALUE), ("idx", dict(wd=1, w=FAKE + 2), EVALUE),
+    ("idx", dict(T=-1), EVALUE), ("idx", dict(nr=0, q=None, k=None, w=None), OK),
+    ("idx", dict(), ERUNTIME), ("idx", dict(wd=1, D=128, H=64), ERUNTIME),
+    # attention
+    ("attn", dict(H=0), EVALUE), ("attn", dict(H=129), EVALUE),
+    ("attn", dict(Dqk=128, Dv=128, ldk=128), EVALUE), ("attn", dict(Dqk=576, Dv=576), EVALUE),
+    ("attn", dict(v=FAKE2, ldv=512), EVALUE),
+    ("attn", dict(Dqk=512, Dv=512, ldk=512, v=FAKE2, ldv=512), EVALUE),
+    ("attn", dict(ldk=570), EVALUE), ("attn", dict(ldk=580), EVALUE),
+    ("attn", dict(scale=0.0), EVALUE), ("attn", dict(scale=-1.0), EVALUE),
+    ("attn", dict(scale="nan"), EVALUE), ("attn", dict(scale="inf"), EVALUE),
+    ("attn", dict(kw=65), EVALUE), ("attn", dict(kw=-1), EVALUE), ("attn", dict(q=None), EVALUE),
+    ("attn", dict(out=None), EVALUE), ("attn", dict(lse=None), EVALUE),
+    ("attn", dict(idx=None), EVALUE), ("attn", dict(q=FAKE + 2), EVALUE),
+    ("attn", dict(out=FAKE + 8), EVALUE),
+    ("attn", dict(Dqk=256, Dv=256, ldk=256, v=FAKE2, ldv=250), EVALUE),
+    ("attn", dict(Dqk=256, Dv=256, ldk=256, v=FAKE2 + 2, ldv=256), EVALUE),
+    ("attn", dict(Tq=0, q=None, out=None, lse=None, idx=None), OK),
+    ("attn", dict(), ERUNTIME), ("attn", dict(Dqk=256, Dv=256, ldk=256, v=FAKE2, ldv=256), ERUNTIME),
+    ("attn", dict(kw=0), ERUNTIME), ("attn", dict(kw=0, idx=None), ERUNTIME),
+    # metadata
+    ("meta", dict(n_seq=0), EVALUE), ("meta", dict(T=-1), EVALUE), ("meta", dict(cu=None), EVALUE),
+    ("meta", dict(T=0, cu=None, rs=None, sl=None), OK), ("meta", dict(), ERUNTIME),
+]
+
+_CHILD = r"""
+import json, math, sys
+sys.path.insert(0, {root!r})
+import deepseek_sparse_attention_dsa_amd as dsa
+lib = dsa.load_library()
+calls = json.loads(sys.stdin.read())
+res = []
+for fn, args in calls:
+    args = [float(a) if isinstance(a, str) else a for a in args]
+    rc = getattr(lib, fn)(*args)
+    res.append([rc, lib.dsa_last_error().decode()])
+print(json.dumps(res))
+"""
+
+
+def _hidden_env():
+    return dict(os.environ, HIP_VISIBLE_DEVICES="", ROCR_VISIBLE_DEVICES="",
+                CUDA_VISIBLE_DEVICES="")
+
+
+@pytest.fixture(scope="module")
+def results():
+    calls = []
+    for kind, kw, _ in CASES:
+        a = dict(BASE[kind])
+        a.update(kw)
+        calls.append([FN[kind], [a[n] for n in ORDER[kind]]])
+    r = subprocess.run([sys.executable, "-c", _CHILD.format(root=ROOT)], input=json.dumps(calls),
+                       capture_output=True, text=True, env=_hidden_env(), timeout=300)
+    assert r.returncode == 0, r.stderr
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(dsa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_path():
+    names = _declared_functions()
+    for fn in ["dsa_packed_metadata", "dsa_indexer_fwd", "dsa_topk", "dsa_sparse_attn_fwd",
+               "dsa_last_error", "dsa_abi_version"]:
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dsa.load_library()
+    for fn in _declared_functions():
+        assert hasattr(lib, fn), fn
+    out = subprocess.run(["nm", "-D", "--defined-only", dsa.library_path()], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r"\bT\s+(dsa_\w+)", out))
+    assert set(_declared_functions()) <= exported
+
+
+def test_abi_version():
+    text = open(HEADER).read()
+    v = int(re.search(r"#define DSA_ABI_VERSION (\d+)", text).group(1))
+    assert dsa.load_library().dsa_abi_version() == v
+
+
+@pytest.mark.parametrize("case", range(len(CASES)),
+                         ids=[f"{c[0]}-{'-'.join(f'{k}={v}' for k, v in c[1].items()) or 'valid'}"
+                              for c in CASES])
+def test_validation_status(results, case):
+    kind, kw, code = CASES[case]
+    rc, msg = results[case]
+    assert rc == code, (kind, kw, rc, msg)
+    if code != OK:
+        assert msg.startswith(FN[kind]), msg
+
+
+def test_python_binding_type_and_shape_errors():
+    import torch
+    # dtype and device checks happen in the binding, before the library
+    with pytest.raises(TypeError):
+        dsa.dsa_topk(torch.zeros(2, 4, dtype=torch.float64), torch.zeros(2, dtype=torch.int32), 1)
+    with pytest.raises(TypeError):
+        dsa.dsa_sparse_attn_fwd(torch.zeros(1, 1, 576), torch.zeros(1, 576),
+                                torch.zeros(1, 1, dtype=torch.int32))
+    with pytest.raises(ValueError):  # host tensors are rejected
+        dsa.dsa_sparse_attn_fwd(torch.zeros(1, 1, 576, dtype=torch.bfloat16),
+                                torch.zeros(1, 576, dtype=torch.bfloat16),
+                                torch.zeros(1, 1, dtype=torch.int32))
+    with pytest.raises(TypeError):
+        dsa.dsa_indexer_fwd(torch.zeros(4, 2, 64, dtype=torch.bfloat16),
+                            torch.zeros(4, 64, dtype=torch.bfloat16),
+                            torch.zeros(4, 2, dtype=torch.float16),
+                            torch.zeros(4, dtype=torch.int32), torch.zeros(4, dtype=torch.int32))

@@ -1,0 +1,418 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Small shapes are compared element by element; the named workloads at full
+size are compared on sampled rows (every row the oracle can afford) plus
+whole-tensor properties. Top-K is bit-exact against the oracle run on the
+GPU's own fp32 scores; indexer scores are within 1e-2 * ||row||_inf (and a
+tighter 1e-4 internal gate); attention out within 1e-2 max-abs plus a per-row
+2e-2 relative gate, lse within 1e-3.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import deepseek_sparse_attention_dsa_amd as dsa
+from gpu_helpers import DEV, check_attention, check_indexer, f64, i64, say
+from oracle import dsa_oracle as O
+from workloads import make_config, make_custom
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    dsa.load_library()
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _meta(wl):
+    rs, sl = dsa.dsa_packed_metadata(wl.cu_seqlens, wl.T)
+    return rs, sl
+
+
+# ------------------------------------------------------------------ metadata
+
+@pytest.mark.parametrize("doc_lens", [[256], [3, 4], [1, 0, 7, 0, 0, 300, 2], [4096] * 3])
+def test_metadata(doc_lens):
+    cu = np.concatenate([[0], np.cumsum(doc_lens)]).astype(np.int32)
+    T = int(cu[-1])
+    say("metadata", doc_lens)
+    rs, sl = dsa.dsa_packed_metadata(torch.from_numpy(cu).to(DEV), T)
+    st_ref, sl_ref = O.packed_metadata(cu, T)
+    assert np.array_equal(i64(rs), st_ref) and np.array_equal(i64(sl), sl_ref)
+
+
+# ------------------------------------------------------------------- indexer
+
+@pytest.mark.parametrize("doc_lens,H,D,wdt", [
+    ([256], 4, 64, torch.bfloat16),
+    ([1, 70, 5, 130, 64], 64, 128, torch.bfloat16),
+    ([200, 9], 3, 128, torch.float32),
+    ([77, 300], 17, 64, torch.float32),
+    ([513], 64, 128, torch.float32),
+])
+def test_indexer_small(doc_lens, H, D, wdt):
+    say("indexer", doc_lens, H, D, wdt)
+    wl = make_custom(doc_lens, H=1, D_qk=256, D_v=256, H_idx=H, D_idx=D, seed=11, device=DEV)
+    if wdt == torch.float32:
+        wl.w = wl.w.float()  # exact widening; the oracle reads the same values
+    rs, sl = _meta(wl)
+    sc = dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, wl.w, rs, sl, width=max(doc_lens))
+    torch.cuda.synchronize()
+    err = check_indexer(sc, wl, np.arange(wl.T), i64(rs), i64(sl))
+    say("  worst rel err", err)
+
+
+def test_indexer_chunk_offsets_and_untouched_columns():
+    say("indexer chunk offsets")
+    wl = make_custom([150, 333], H=1, D_qk=256, D_v=256, H_idx=64, D_idx=128, seed=5, device=DEV)
+    rs, sl = _meta(wl)
+    ld = 400
+    r0, n = 97, 190
+    buf = torch.full((n, ld), float("nan"), device=DEV)
+    dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, wl.w, rs, sl, row_begin=r0, n_rows=n, scores=buf)
+    torch.cuda.synchronize()
+    rows = np.arange(r0, r0 + n)
+    check_indexer(buf, wl, rows, i64(rs), i64(sl))
+    g = buf.cpu().numpy()
+    sln = i64(sl)[rows]
+    for i in range(n):
+        assert np.all(np.isfinite(g[i, :sln[i]]))
+        assert np.all(np.isnan(g[i, sln[i]:])), "columns past seq_len must stay untouched"
+
+
+# --------------------------------------------------------------------- top-K
+
+def _topk_check(scores: torch.Tensor, seq_lens: torch.Tensor, k: int, row_starts=None,
+                n_cols=None):
+    idx, tl, vals = dsa.dsa_topk(scores, seq_lens, k, row_starts=row_starts, n_cols=n_cols,
+                                 return_values=True)
+    torch.cuda.synchronize()
+    sc = scores.detach().cpu().numpy()
+    st = None if row_starts is None else i64(row_starts)
+    ref_idx, ref_len = O.topk(sc.astype(np.float64), i64(seq_lens), k, row_starts=st,
+                              n_cols=n_cols)
+    gi, gl = i64(idx), i64(tl)
+    bad = np.nonzero(np.any(gi != ref_idx, axis=1))[0]
+    assert len(bad) == 0, (bad[:5], gi[bad[:1]], ref_idx[bad[:1]])
+    assert np.array_equal(gl, ref_len)
+    # values: the selected scores (-0.0 may come back as +0.0), -inf padding
+    gv = vals.cpu().numpy().astype(np.float64)
+    for r in range(sc.shape[0]):
+        m = ref_len[r]
+        loc = ref_idx[r, :m] - (0 if st is None else st[r])
+        assert np.array_equal(gv[r, :m], sc[r, loc].astype(np.float64))
+        assert np.all(gv[r, m:] == -np.inf)
+    return idx, tl
+
+
+@pytest.mark.parametrize("n_cols", [100, 256, 1000, 4096, 5000, 16384, 20000, 40000, 65536])
+@pytest.mark.parametrize("kind", ["gauss", "ties"])
+def test_topk_synthetic(n_cols, kind):
+    say("topk", n_cols, kind)
+    g = torch.Generator().manual_seed(n_cols + (7 if kind == "ties" else 0))
+    n_rows = 24 if n_cols > 16384 else 64
+    x = torch.randn((n_rows, n_cols), generator=g)
+    if kind == "ties":
+        x = torch.round(x * 4) / 4          # heavy exact ties, incl. 0.0
+        neg = torch.rand((n_rows, n_cols), generator=g) < 0.5
+        x = torch.where((x == 0) & neg, torch.full_like(x, -0.0), x)
+    ld = (n_cols + 3) // 4 * 4 + (4 if n_cols % 3 == 0 else 0)
+    buf = torch.zeros((n_rows, ld))
+    buf[:, :n_cols] = x
+    for k in ([1, 7, 64, 2048] if n_cols >= 2048 else [1, 7, 64]):
+        lens = torch.randint(0, n_cols + 1, (n_rows,), generator=g)
+        lens[0] = n_cols
+        lens[1] = min(k, n_cols)
+        lens[2] = min(k + 1, n_cols)
+        lens[3] = max(k - 1, 0)
+        lens[4] = 0
+        lens[5] = n_cols + 100          # clamped to n_cols
+        starts = torch.randint(0, 1 << 20, (n_rows,), generator=g).to(torch.int32)
+        _topk_check(buf.to(DEV), lens.to(torch.int32).to(DEV), k,
+                    row_starts=starts.to(DEV) if k != 7 else None, n_cols=n_cols)
+
+
+def test_topk_special_rows():
+    say("topk special rows")
+    n_cols, k = 3000, 64
+    rows = []
+    rows.append(np.full(n_cols, 0.25))                       # all equal -> first K
+    rows.append(np.arange(n_cols, dtype=np.float64))         # increasing -> last K
+    rows.append(-np.arange(n_cols, dtype=np.float64))        # decreasing -> first K
+    r = np.zeros(n_cols)
+    r[::2] = -0.0
+    rows.append(r)                                           # +-0 ties -> first K
+    r = np.full(n_cols, -np.inf)
+    r[100:110] = 1.0
+    rows.append(r)                                           # -inf is a value
+    r = np.random.default_rng(0).standard_normal(n_cols)
+    r[r < 1.5] = 1.5                                         # huge tie at the boundary
+    rows.append(r)
+    x = torch.tensor(np.stack(rows), dtype=torch.float32)
+    lens = torch.full((len(rows),), n_cols, dtype=torch.int32)
+    idx, _ = _topk_check(x.to(DEV), lens.to(DEV), k)
+    gi = i64(idx)
+    assert gi[0].tolist() == list(range(k))
+    assert gi[1].tolist() == list(range(n_cols - k, n_cols))
+    assert gi[2].tolist() == list(range(k))
+    assert gi[3].tolist() == list(range(k))
+
+
+# ----------------------------------------------------------------- attention
+
+def _attn_case(T_kv, T_q, H, Dqk, Dv, shared, kw, seed, tl_mode="none", sink=True,
+               stress=False, dup=False):
+    g = np.random.default_rng(seed)
+    wl = make_custom([max(T_q, T_kv)], H=H, D_qk=Dqk, D_v=Dv, shared_kv=shared, H_idx=0,
+                     sink=sink, seed=seed, device=DEV, stress=stress, topk=kw,
+                     value_std=(1 / 16 if Dqk == 256 else None))
+    q = wl.q[:T_q].contiguous()
+    kv = wl.kv[:T_kv].contiguous()
+    v = None if shared else wl.v[:T_kv].contiguous()
+    idx = g.integers(0, T_kv, size=(T_q, kw)).astype(np.int32)
+    if not dup:
+        for t in range(T_q):
+            idx[t] = g.permutation(T_kv)[:kw] if kw <= T_kv else idx[t]
+    # sprinkle invalid slots: -1, negative and out-of-range ids
+    m = g.random((T_q, kw))
+    idx[m < 0.05] = -1
+    idx[(m >= 0.05) & (m < 0.07)] = T_kv + 3
+    idx[(m >= 0.07) & (m < 0.08)] = -5
+    tl = None
+    if tl_mode == "prefix":
+        tl = g.integers(-3, kw + 5, size=T_q).astype(np.int32)
+        tl[0] = 0
+        tl[1] = kw
+    return wl, q, kv, v, torch.from_numpy(idx).to(DEV), \
+        (None if tl is None else torch.from_numpy(tl).to(DEV))
+
+
+@pytest.mark.parametrize("Dqk,Dv,shared,H,kw,tl_mode,sink,stress", [
+    (576, 512, True, 16, 64, "none", True, False),
+    (576, 512, True, 64, 100, "prefix", True, False),
+    (576, 512, True, 64, 37, "none", False, True),
+    (576, 512, True, 128, 96, "prefix", True, True),
+    (576, 512, True, 20, 33, "none", True, True),
+    (576, 512, True, 1, 5, "none", True, False),
+    (512, 512, True, 64, 70, "prefix", True, True),
+    (256, 256, False, 12, 64, "none", False, False),
+    (256, 256, False, 12, 129, "prefix", False, True),
+    (256, 256, True, 24, 40, "none", True, True),
+    (256, 256, False, 128, 32, "none", True, False),
+])
+def test_attention_small(Dqk, Dv, shared, H, kw, tl_mode, sink, stress):
+    say("attention", Dqk, Dv, shared, H, kw, tl_mode, sink, stress)
+    T_kv, T_q = 300, 41
+    wl, q, kv, v, idx, tl = _attn_case(T_kv, T_q, H, Dqk, Dv, shared, kw, seed=H * 7 + kw,
+                                       tl_mode=tl_mode, sink=sink, stress=stress,
+                                       dup=(kw == 37))
+    sk = wl.sink
+    out, lse, mx = dsa.dsa_sparse_attn_fwd(q, kv, idx, topk_length=tl, attn_sink=sk,
+                                           softmax_scale=wl.scale, v=v, d_v=Dv)
+    torch.cuda.synchronize()
+    e_out, e_rel = check_attention(out, lse, mx, q, kv, v, idx, tl, sk, wl.scale, Dv,
+                                   np.arange(T_q))
+    say("  max|dout|", e_out, "row rel", e_rel)
+
+
+def test_attention_edge_rows():
+    say("attention edge rows")
+    H, Dqk, Dv, kw, T_kv = 64, 576, 512, 48, 80
+    wl = make_custom([T_kv], H=H, D_qk=Dqk, D_v=Dv, H_idx=0, seed=3, device=DEV, stress=True)
+    q = wl.q[:8].contiguous()
+    kv = wl.kv
+    idx = np.full((8, kw), -1, dtype=np.int32)
+    idx[1, :3] = [5, 5, 5]                       # one key three times
+    idx[2, :] = np.arange(kw)                    # all valid, compact
+    idx[3, 10] = 7                               # a single valid slot deep in the row
+    idx[4, :] = T_kv + np.arange(kw)             # all out of range -> empty
+    idx[5, ::2] = np.arange(kw // 2)             # interleaved -1
+    idx[6, :] = np.arange(kw)                    # topk_length clamps below
+    idx[7, :] = np.arange(kw)                    # topk_length 0 -> empty
+    tl = np.array([kw, kw, kw, kw, kw, kw, 5, 0], dtype=np.int32)
+    idx_t = torch.from_numpy(idx).to(DEV)
+    tl_t = torch.from_numpy(tl).to(DEV)
+    for sink in (None, wl.sink):
+        out, lse, mx = dsa.dsa_sparse_attn_fwd(q, kv, idx_t, topk_length=tl_t, attn_sink=sink,
+                                               softmax_scale=wl.scale)
+        torch.cuda.synchronize()
+        check_attention(out, lse, mx, q, kv, None, idx_t, tl_t, sink, wl.scale, Dv,
+                        np.arange(8))
+        l = lse.cpu().numpy()
+        assert np.all(np.isposinf(l[[0, 4, 7]]))
+        assert np.all(out[[0, 4, 7]].float().cpu().numpy() == 0)
+    # k_width = 0: every row is empty
+    out, lse, mx = dsa.dsa_sparse_attn_fwd(q, kv, idx_t[:, :0].contiguous(), softmax_scale=0.1)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isposinf(lse)) and torch.all(out == 0)
+    assert torch.all(torch.isneginf(mx))
+
+
+def test_attention_dense_identity_on_gpu():
+    """Top-K covering every causal key and no sink == dense causal attention."""
+    say("attention dense identity")
+    T, H = 96, 16
+    wl = make_custom([T], H=H, D_qk=576, D_v=512, H_idx=0, sink=False, seed=9, device=DEV,
+                     stress=True)
+    idx = np.full((T, T), -1, dtype=np.int32)
+    for t in range(T):
+        idx[t, : t + 1] = np.arange(t + 1)
+    out, lse, _ = dsa.dsa_sparse_attn_fwd(wl.q, wl.kv, torch.from_numpy(idx).to(DEV),
+                                          softmax_scale=wl.scale)
+    torch.cuda.synchronize()
+    qf = wl.q.float().cpu().double().permute(1, 0, 2)
+    kf = wl.kv.float().cpu().double()
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qf, kf.expand(H, T, 576), kf[:, :512].expand(H, T, 512), is_causal=True,
+        scale=wl.scale).permute(1, 0, 2).numpy()
+    got = out.float().cpu().double().numpy()
+    assert np.abs(got - ref).max() <= 2e-2 * np.abs(ref).max()
+
+
+# ------------------------------------------------------- named workloads
+
+def _pipeline(wl, max_seqlen=None):
+    idx, tl = dsa.indexer_topk(wl.q_idx, wl.k_idx, wl.w, wl.cu_seqlens, wl.topk,
+                               max_seqlen=max_seqlen)
+    out, lse, mx = dsa.dsa_sparse_attn_fwd(wl.q, wl.kv, idx, topk_length=tl, attn_sink=wl.sink,
+                                           softmax_scale=wl.scale)
+    return idx, tl, out, lse, mx
+
+
+def test_config1_full():
+    say("config 1 full")
+    wl = make_config(1, device=DEV)
+    rs, sl = _meta(wl)
+    sc = dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, wl.w, rs, sl, width=wl.T)
+    idx, tl, vals = dsa.dsa_topk(sc, sl, wl.topk, row_starts=rs)
+    out, lse, mx = dsa.dsa_sparse_attn_fwd(wl.q, wl.kv, idx, topk_length=tl, attn_sink=wl.sink,
+                                           softmax_scale=wl.scale)
+    torch.cuda.synchronize()
+    check_indexer(sc, wl, np.arange(wl.T), i64(rs), i64(sl))
+    _topk_check(sc, sl, wl.topk, row_starts=rs)
+    check_attention(out, lse, mx, wl.q, wl.kv, None, idx, tl, wl.sink, wl.scale, 512,
+                    np.arange(wl.T))
+    # end to end against the oracle's own scores: overlap ratio (reported)
+    q = f64(wl.q_idx)
+    ref_sc = O.indexer_scores(q, f64(wl.k_idx), f64(wl.w), i64(rs), i64(sl), np.arange(wl.T),
+                              width=wl.T)
+    ref_idx, _ = O.topk(ref_sc, i64(sl), wl.topk, row_starts=i64(rs))
+    gi = i64(idx)
+    inter = sum(len(set(gi[t][gi[t] >= 0]) & set(ref_idx[t][ref_idx[t] >= 0]))
+                for t in range(wl.T))
+    total = int((ref_idx >= 0).sum())
+    say("  end-to-end top-K overlap", inter / total)
+    assert inter / total > 0.99
+
+
+@pytest.mark.parametrize("stress", [False, True])
+def test_config2(stress):
+    say("config 2", "stress" if stress else "")
+    wl = make_config(2, device=DEV, stress=stress)
+    rs, sl = _meta(wl)
+    sc = dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, wl.w, rs, sl, width=wl.T)
+    idx, tl, _ = dsa.dsa_topk(sc, sl, wl.topk, row_starts=rs)
+    out, lse, mx = dsa.dsa_sparse_attn_fwd(wl.q, wl.kv, idx, topk_length=tl, attn_sink=wl.sink,
+                                           softmax_scale=wl.scale)
+    torch.cuda.synchronize()
+    if not stress:
+        check_indexer(sc, wl, np.arange(wl.T), i64(rs), i64(sl))
+        _topk_check(sc, sl, wl.topk, row_starts=rs)
+    rows = np.unique(np.concatenate([[0, 1, 2047, 2048, 2049, 4095],
+                                     np.random.default_rng(2).integers(0, wl.T, 18)]))
+    check_attention(out, lse, mx, wl.q, wl.kv, None, idx, tl, wl.sink, wl.scale, 512, rows)
+    # rows t < 2048 keep every causal key, -1 after
+    gi = i64(idx)
+    for t in (0, 5, 2047):
+        assert gi[t, : t + 1].tolist() == list(range(t + 1))
+        assert np.all(gi[t, t + 1:] == -1)
+
+
+def test_config3_sampled():
+    say("config 3")
+    wl = make_config(3, device=DEV)
+    mx_len = max(wl.doc_lens)
+    idx, tl, out, lse, mx = _pipeline(wl, max_seqlen=mx_len)
+    torch.cuda.synchronize()
+    rs, sl = _meta(wl)
+    cu = np.cumsum([0] + wl.doc_lens)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([cu[:-1], cu[1:] - 1, cu[:-1] + 2048, cu[:-1] + 2047,
+                                     rng.integers(0, wl.T, 24)]))
+    rows = rows[rows < wl.T]
+    # indexer + top-K on the sampled rows (scores recomputed row by row)
+    for r in rows:
+        sc = dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, wl.w, rs, sl, row_begin=int(r), n_rows=1,
+                                 width=mx_len)
+        torch.cuda.synchronize()
+        check_indexer(sc, wl, [r], i64(rs), i64(sl))
+        ref_idx, ref_len = O.topk(sc.cpu().numpy().astype(np.float64), i64(sl)[[r]], wl.topk,
+                                  row_starts=i64(rs)[[r]], n_cols=mx_len)
+        assert np.array_equal(i64(idx)[r], ref_idx[0]) and i64(tl)[r] == ref_len[0]
+    check_attention(out, lse, mx, wl.q, wl.kv, None, idx, tl, wl.sink, wl.scale, 512,
+                    rows[:: max(1, len(rows) // 16)])
+
+
+def test_config4_sampled():
+    say("config 4")
+    wl = make_config(4, device=DEV)
+    idx, tl, out, lse, mx = _pipeline(wl)
+    torch.cuda.synchronize()
+    rs, sl = _meta(wl)
+    rows = np.array([0, 2047, 2048, 30000, 65535])
+    for r in rows:
+        sc = dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, wl.w, rs, sl, row_begin=int(r), n_rows=1,
+                                 width=wl.T)
+        torch.cuda.synchronize()
+        check_indexer(sc, wl, [r], i64(rs), i64(sl))
+        ref_idx, ref_len = O.topk(sc.cpu().numpy().astype(np.float64), i64(sl)[[r]], wl.topk,
+                                  row_starts=i64(rs)[[r]], n_cols=wl.T)
+        assert np.array_equal(i64(idx)[r], ref_idx[0]) and i64(tl)[r] == ref_len[0]
+    check_attention(out, lse, mx, wl.q, wl.kv, None, idx, tl, wl.sink, wl.scale, 512, rows)
+    # whole-tensor properties at full size
+    gi = idx.cpu().numpy()
+    tln = tl.cpu().numpy()
+    t = np.arange(wl.T)
+    assert np.array_equal(tln, np.minimum(t + 1, wl.topk))
+    valid = gi >= 0
+    assert np.array_equal(valid.sum(1), tln)
+    assert np.all(np.where(valid, gi <= t[:, None], True))
+    assert np.all(np.diff(np.where(valid, gi, np.iinfo(np.int32).max), axis=1)[:, :] >= 0)
+    assert torch.isfinite(lse).all() and torch.isfinite(out.float()).all()
+
+
+def test_config5_sampled():
+    say("config 5")
+    wl = make_config(5, device=DEV)
+    out, lse, mx = dsa.dsa_sparse_attn_fwd(wl.q, wl.kv, wl.routes, attn_sink=None,
+                                           softmax_scale=wl.scale, v=wl.v)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 3, 4, 8191, 8192, 8195, 32767],
+                                     np.random.default_rng(5).integers(0, wl.T, 40)]))
+    check_attention(out, lse, mx, wl.q, wl.kv, wl.v, wl.routes, None, None, wl.scale, 256, rows)
+    wls = make_config(5, device=DEV, stress=True)
+    out, lse, mx = dsa.dsa_sparse_attn_fwd(wls.q, wls.kv, wls.routes, softmax_scale=wls.scale,
+                                           v=wls.v)
+    torch.cuda.synchronize()
+    check_attention(out, lse, mx, wls.q, wls.kv, wls.v, wls.routes, None, None, wls.scale, 256,
+                    rows)
+
+
+# -------------------------------------------------------------- determinism
+
+def test_bitwise_determinism():
+    say("determinism")
+    wl = make_config(2, device=DEV)
+    a = _pipeline(wl)
+    b = _pipeline(wl)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y)
