@@ -1,0 +1,261 @@
+#!/usr/bin/env python
+"""Benchmark of the DSA forward hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+packed metadata -> lightning-indexer scores (row chunks under a 2 GiB score
+cap) -> radix top-K -> sparse attention forward. Inputs are generated on the
+GPU before the timed region and stay resident in HBM.
+
+Prints one JSON line. `value` is the sparse-attention forward throughput in
+TFLOP/s (algorithmic FLOP: 2*(D_qk+D_v) per valid slot per head, over the
+attention kernel's time measured with HIP events inside the timed steps);
+`indexer_topk_rows_per_s` is the second half of the metric; `ms_per_step` is
+the whole path. `roofline` describes the dominant kernel; `cpu_baseline` is
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn fwd TFLOP/s + indexer+topK rows/s at 1 MI355X; % of roofline"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+ATTN_SRC = os.path.join(ROOT, "deepseek_sparse_attention_dsa_amd", "csrc", "sparse_attn.hip")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--config", type=int, default=2, help="workload 1..5 (default: 2)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="approximate CPU time budget of the oracle baseline")
+    return p.parse_args()
+
+
+def workload_counts(wl, seq_lens_np):
+    """Algorithmic work of one step (what the method must do)."""
+    c = {}
+    K = wl.topk
+    if wl.q_idx is not None:
+        pairs = int(sum(L * (L + 1) // 2 for L in wl.doc_lens))
+        c["indexer_flop"] = 2.0 * wl.H_idx * wl.D_idx * pairs
+        sl = seq_lens_np.astype(np.int64)
+        rd = 4.0 * float(sl[sl > K].sum()) + 8.0 * len(sl)
+        wr = (4.0 * K + 4.0) * len(sl)
+        c["topk_bytes"] = rd + wr
+        c["valid_slots"] = float(np.minimum(sl, K).sum())
+    else:
+        c["valid_slots"] = float((wl.routes >= 0).sum().item())
+    c["attn_flop"] = 2.0 * (wl.D_qk + wl.D_v) * wl.H * c["valid_slots"]
+    return c
+
+
+def traffic_from_profile(workload_name: str):
+    """HBM bytes per attention launch from committed rocprofv3 counters.
+
+    Returns None unless profiles/traffic_<workload>.json exists and was taken
+    from the current attention kernel source (sha256 match).
+    """
+    path = os.path.join(PROFILES, f"traffic_attention_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, rs, sl, budget_s):
+    """Time the fp64 oracle on a bounded, seeded sample of the workload's rows."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import dsa_oracle as O
+    from workloads import bf16_to_numpy_bits
+
+    import torch
+
+    f64 = lambda t: O.bf16_bits_to_f64(bf16_to_numpy_bits(t))  # noqa: E731
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
+    rng = np.random.default_rng(1234)
+    T = wl.T
+    rs_np, sl_np = rs.cpu().numpy(), sl.cpu().numpy()
+    res = {"kind": "oracle", "cores": int(threads), "cpu": platform.processor() or platform.machine()}
+    # attention: the oracle on sampled rows with the GPU path's own indices
+    kv = f64(wl.kv)
+    v = None if wl.v is None else f64(wl.v)
+    sink = None if wl.sink is None else wl.sink.cpu().numpy().astype(np.float64)
+    idx_all, tl_all = wl.extra["indices"], wl.extra["topk_length"]
+    n_att, t_att, flop_att = 0, 0.0, 0.0
+    rows_order = rng.permutation(T)
+    while t_att < budget_s * 0.5 and n_att < T:
+        rows = rows_order[n_att:n_att + 8]
+        sel = torch.as_tensor(rows, device=wl.q.device)
+        q = f64(wl.q[sel])
+        idx = idx_all[sel].cpu().numpy().astype(np.int64)
+        tl = None if tl_all is None else tl_all[sel].cpu().numpy()
+        t0 = time.perf_counter()
+        O.sparse_attention(q, kv, v, idx, tl, sink, wl.scale, d_v=wl.D_v)
+        t_att += time.perf_counter() - t0
+        valid = (idx >= 0) if tl is None else (np.arange(idx.shape[1])[None, :] < tl[:, None])
+        flop_att += 2.0 * (wl.D_qk + wl.D_v) * wl.H * float(valid.sum())
+        n_att += len(rows)
+    res["value"] = flop_att / t_att / 1e12
+    res["unit"] = "TFLOP/s"
+    sample = f"attention on {n_att} random rows ({t_att:.1f} s)"
+    # indexer + top-K on sampled rows
+    if wl.q_idx is not None:
+        k_idx = f64(wl.k_idx)
+        n_idx, t_idx = 0, 0.0
+        while t_idx < budget_s * 0.5 and n_idx < T:
+            rows = rows_order[n_idx:n_idx + 16]
+            sel = torch.as_tensor(rows, device=wl.q_idx.device)
+            q = f64(wl.q_idx[sel])
+            w = f64(wl.w[sel])
+            st, ln = rs_np[rows].astype(np.int64), sl_np[rows].astype(np.int64)
+            t0 = time.perf_counter()
+            sc = O.indexer_scores(q, k_idx, w, st, ln, np.arange(len(rows)))
+            O.topk(sc, ln, wl.topk, row_starts=st)
+            t_idx += time.perf_counter() - t0
+            n_idx += len(rows)
+        res["indexer_topk_rows_per_s"] = n_idx / t_idx
+        sample += f"; indexer+top-K on {n_idx} random rows ({t_idx:.1f} s)"
+    res["sample"] = sample
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the DSA forward path here is a single-GPU build "
+              "(no collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import deepseek_sparse_attention_dsa_amd as dsa
+    from workloads import CONFIGS, make_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    dsa.load_library()
+    wl = make_config(args.config, device=dev)
+    T, K = wl.T, wl.topk
+    max_len = max(wl.doc_lens)
+    has_indexer = wl.q_idx is not None
+
+    rs, sl = dsa.dsa_packed_metadata(wl.cu_seqlens, T)
+    rows_per_chunk = dsa.chunk_rows(T, max_len)
+    ld = max(4, (max_len + 3) // 4 * 4)
+    scores = torch.empty((min(rows_per_chunk, T), ld), dtype=torch.float32, device=dev)
+    indices = torch.empty((T, K), dtype=torch.int32, device=dev) if has_indexer else wl.routes
+    topk_length = torch.empty((T,), dtype=torch.int32, device=dev) if has_indexer else None
+    out = torch.empty((T, wl.H, wl.D_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
+    max_logits = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    ev = {}
+
+    def step(timed: bool):
+        e0 = torch.cuda.Event(enable_timing=True) if timed else None
+        e1 = torch.cuda.Event(enable_timing=True) if timed else None
+        e2 = torch.cuda.Event(enable_timing=True) if timed else None
+        if timed:
+            e0.record(stream)
+        dsa.dsa_packed_metadata(wl.cu_seqlens, T, row_starts=rs, seq_lens=sl)
+        if has_indexer:
+            for r0 in range(0, T, rows_per_chunk):
+                n = min(rows_per_chunk, T - r0)
+                dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, wl.w, rs, sl, row_begin=r0, n_rows=n,
+                                    scores=scores)
+                dsa.dsa_topk(scores[:n], sl[r0:r0 + n], K, row_starts=rs[r0:r0 + n],
+                             n_cols=max_len, indices=indices[r0:r0 + n],
+                             topk_length=topk_length[r0:r0 + n])
+        if timed:
+            e1.record(stream)
+        dsa.dsa_sparse_attn_fwd(wl.q, wl.kv, indices, topk_length=topk_length,
+                                attn_sink=wl.sink, softmax_scale=wl.scale, v=wl.v, out=out,
+                                lse=lse, max_logits=max_logits)
+        if timed:
+            e2.record(stream)
+            ev.setdefault("steps", []).append((e0, e1, e2))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    idx_ms = [a.elapsed_time(b) for a, b, _ in ev["steps"]]
+    att_ms = [b.elapsed_time(c) for _, b, c in ev["steps"]]
+    sl_np = sl.cpu().numpy()
+    cnt = workload_counts(wl, sl_np)
+    att_s = float(np.mean(att_ms)) / 1e3
+    attn_tflops = cnt["attn_flop"] / att_s / 1e12
+    ms_per_step = wall / args.steps * 1e3
+
+    stages = {"attention": {"ms": float(np.mean(att_ms)), "tflops": attn_tflops,
+                            "frac_bf16_peak": attn_tflops / PEAK_BF16_TFLOPS,
+                            "algorithmic_flop": cnt["attn_flop"]}}
+    rows_per_s = None
+    if has_indexer:
+        idx_s = float(np.mean(idx_ms)) / 1e3
+        rows_per_s = T / idx_s
+        stages["metadata+indexer+topk"] = {"ms": float(np.mean(idx_ms)), "rows_per_s": rows_per_s,
+                                           "indexer_algorithmic_flop": cnt["indexer_flop"],
+                                           "topk_algorithmic_bytes": cnt["topk_bytes"],
+                                           "chunks": math.ceil(T / rows_per_chunk)}
+
+    roofline = {"kernel": "sparse_attn_kernel", "bound": "mfma", "achieved": attn_tflops,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                "algorithmic_per_launch": cnt["attn_flop"],
+                "avg_launch_ms": float(np.mean(att_ms)), "traffic": None}
+    tb = traffic_from_profile(CONFIGS[args.config]["name"])
+    if tb is not None:
+        roofline["traffic"] = tb
+
+    rec = {
+        "metric": METRIC, "value": attn_tflops, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": CONFIGS[args.config]["name"], "T": T, "heads": wl.H,
+                   "D_qk": wl.D_qk, "D_v": wl.D_v, "topk": K, "indexer_heads": wl.H_idx,
+                   "indexer_dim": wl.D_idx, "docs": len(wl.doc_lens), "parallelism": "none"},
+        "indexer_topk_rows_per_s": rows_per_s,
+        "stages": stages,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        wl.extra["indices"] = indices
+        wl.extra["topk_length"] = topk_length
+        rec["cpu_baseline"] = cpu_baseline(wl, rs, sl, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()
