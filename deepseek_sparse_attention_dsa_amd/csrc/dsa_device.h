@@ -38,6 +38,62 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, co
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// One v_mfma_f32_32x32x16_bf16: D[32x32] = A[32x16] * B[16x32] + C.
+// Lane l supplies A row (l % 32) and B column (l % 32), each over the eight
+// k values 8*(l/32) .. 8*(l/32)+7, and receives D column (l % 32), rows
+// 8*(i/4) + 4*(l/32) + (i%4) for its 16 values i.
+__device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives 16-bit
+// element (i % 4) of the 8-byte reads of source lanes i/4, 4 + i/4, 8 + i/4
+// and 12 + i/4. With source lane j pointing at row r0 + j/4, column
+// c0 + 4*(j%4) of a row-major bf16 matrix, lane i gets column c0 + i of rows
+// r0 .. r0+3: a 4 x 16 block read transposed.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_ptr) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(lds_ptr));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Asynchronous 16-byte global -> LDS copy (global_load_lds_dwordx4): lane l's
+// 16 bytes land at LDS byte address lds_base + 16 * l, lds_base being
+// wave-uniform. Issued through inline asm so that the compiler does not
+// insert its own (blanket) waits for it: the caller waits with
+// wait_vmcnt0() before reading the data.
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_base)
+               : "memory");
+}
+
+// Same copy with an immediate byte offset IMM (0 <= IMM < 4096). The offset
+// applies to both addresses: global gptr + IMM -> LDS lds_base + IMM + 16*l.
+template <int IMM>
+__device__ __forceinline__ void dma16_imm(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
+               :
+               : "v"(gptr), "s"(lds_base), "i"(IMM)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(0) through the builtin, so that the compiler's own wait
+// tracking also knows that every earlier vector-memory load has completed.
+__device__ __forceinline__ void wait_vmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt = 0, expcnt and lgkmcnt unconstrained
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }

@@ -255,6 +255,35 @@ def test_attention_edge_rows():
     assert torch.all(torch.isneginf(mx))
 
 
+def test_attention_reference_paths():
+    """First valid key late in the row, and logits far above the first tile's max."""
+    say("attention reference paths")
+    H, T_kv, kw = 64, 200, 160
+    wl = make_custom([T_kv], H=H, D_qk=576, D_v=512, H_idx=0, seed=17, device=DEV)
+    kv = wl.kv.clone()
+    q = wl.q[:4].clone()
+    # keys 100..199 get a large component along dim 0; q rows 2, 3 point at it
+    kv[100:, 0] = 32.0
+    q[2:, :, 0] = 64.0  # logit gap ~ 2048 * scale = 85 nats = 123 log2 units
+    idx = np.full((4, kw), -1, dtype=np.int32)
+    idx[0, 50] = 3                               # first valid key in the 2nd tile
+    idx[0, 120:125] = [7, 8, 9, 10, 11]
+    idx[1, 40:] = np.arange(kw - 40)             # leading invalid tile
+    idx[2, :] = np.arange(kw)                    # keys 0..99 small, 100..159 huge
+    idx[3, :100] = np.arange(100)                # huge key appears only in the last tile
+    idx[3, 150] = 150
+    idx_t = torch.from_numpy(idx).to(DEV)
+    for sink in (None, wl.sink):
+        out, lse, mx = dsa.dsa_sparse_attn_fwd(q, kv, idx_t, attn_sink=sink,
+                                               softmax_scale=wl.scale)
+        torch.cuda.synchronize()
+        # V dim 0 is 32 for keys >= 100, so outputs reach ~32 where one bf16 ulp
+        # is 0.25: the absolute bound scales with that, the per-row relative
+        # gate stays at 2e-2.
+        check_attention(out, lse, mx, q, kv, None, idx_t, None, sink, wl.scale, 512,
+                        np.arange(4), atol_out=0.1)
+
+
 def test_attention_dense_identity_on_gpu():
     """Top-K covering every causal key and no sink == dense causal attention."""
     say("attention dense identity")
