@@ -11,11 +11,12 @@ LIB = os.path.join(HERE, "libdsa.so")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 SOURCES = ["abi.hip", "indexer.hip", "topk.hip", "sparse_attn.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU ops stay disabled for every gfx950 build
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-Wno-unused-command-line-argument",
+    "-Wno-unused-command-line-argument", "-I" + INCLUDE,
 ]
 
 

@@ -8,7 +8,7 @@
 
 #include <mutex>
 
-#include "../../include/dsa.h"
+#include "dsa.h"
 #include "dsa_launch.h"
 
 namespace {

@@ -18,14 +18,15 @@
 //    registers (1 wave per SIMD: 144 + 256 registers for D_qk = 576).
 //  * Tiles of 32 selected KV rows are gathered with asynchronous
 //    global -> LDS copies (global_load_lds_dwordx4) into a 2-stage ring: the
-//    copy of tile i+1 runs while tile i is computed. A tile is stored as
-//    16-byte slots, slot 64*u + 2*r + h holding row r, dims 16*u + 8*h .. +7:
-//    one copy instruction moves dims [16u, 16u+16) of all 32 rows, lane l
-//    always copies row l/2 (so no lane ever looks up another row's id), the
-//    q.k operand read of a k-step is one contiguous 1 KiB block and the
-//    transposed v reads touch 4 rows x 32 contiguous bytes: no bank
-//    conflicts. Invalid rows copy from a zero constant, so masked rows hold
-//    zeros (0 * V never meets a non-finite value).
+//    copy of tile i+1 runs while tile i is computed. Dims [16u, 16u+16) of
+//    the 32 rows form 1 KiB block u of 16-byte slots; row r, half h (dims
+//    16u + 8h .. +7) sits in slot 32*h + ((r + 4h + 8*(u%2)) mod 32). One
+//    copy instruction fills one block, lane l always copying the same row
+//    (one per block parity, so no lane looks up another lane's id). With
+//    this rotation the q.k operand read of a k-step is 1 KiB in lane order,
+//    and the two 16-lane groups of each half-wave of a transposed v read hit
+//    disjoint LDS banks. Invalid rows copy from a zero constant, so masked
+//    rows hold zeros (0 * V never meets a non-finite value).
 //  * p.v reads V straight from the same row-major tile with
 //    ds_read_b64_tr_b16 (4 keys x 16 dims per 16-lane group, transposed), so
 //    no transposed copy of V is ever written.
@@ -90,17 +91,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl<0, N>(f);
 }
 
-// Bits 0, 2, 4, ... of x packed into bits 0, 1, 2, ...
-__device__ __forceinline__ uint32_t even_bits(uint64_t x) {
-  x &= 0x5555555555555555ull;
-  x = (x | (x >> 1)) & 0x3333333333333333ull;
-  x = (x | (x >> 2)) & 0x0F0F0F0F0F0F0F0Full;
-  x = (x | (x >> 4)) & 0x00FF00FF00FF00FFull;
-  x = (x | (x >> 8)) & 0x0000FFFF0000FFFFull;
-  x = (x | (x >> 16)) & 0x00000000FFFFFFFFull;
-  return (uint32_t)x;
-}
-
 template <int DQK, int DV, bool SHARED, int NW>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
   using C = Cfg<DQK, DV, SHARED, NW>;
@@ -125,12 +115,19 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
   if (a.T_kv <= 0) L = 0;
   const int n_tiles = (L + kBN - 1) / kBN;
 
-  // Raw index of tile row (lane / 2) for the tile starting at slot j0 (-1
-  // past the valid prefix). It is validated only when used, one iteration
-  // later: a compare right after the load would make the compiler wait for
-  // every outstanding vector-memory operation, the tile copies included.
-  auto load_id = [&](int j0) -> int32_t {
-    const int j = j0 + (lane >> 1);
+  // Copy lanes: lane l fills slot l of every block, i.e. half h = l/32 of
+  // row (l%32 - 4h - 8*(u%2)) mod 32. rowE / rowO are its rows in even / odd
+  // blocks.
+  const int hcp = lane >> 5;
+  const int rowE = ((lane & 31) - 4 * hcp) & 31;
+  const int rowO = ((lane & 31) - 4 * hcp - 8) & 31;
+
+  // Raw index of row `row` of the tile starting at slot j0 (-1 past the
+  // valid prefix). It is validated only when used, one iteration later: a
+  // compare right after the load would make the compiler wait for every
+  // outstanding vector-memory operation, the tile copies included.
+  auto load_id = [&](int j0, int row) -> int32_t {
+    const int j = j0 + row;
     int32_t raw = -1;
     if (j < L) raw = idx_row[j];
     return raw;
@@ -139,33 +136,59 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
     return (raw >= 0 && (int64_t)raw < a.T_kv) ? raw : -1;
   };
 
-  // Issue this wave's share of the asynchronous copies of one tile: copy c
-  // moves dims [16c, 16c + 16) of the 32 rows, lane l taking row l/2, dims
-  // 16c + 8*(l%2) .. +7. Wave w issues copies [w*PER_WAVE, (w+1)*PER_WAVE);
-  // each copy's offset within the row goes into the instruction's immediate
-  // (which shifts the LDS address as well, hence M0 = slot base - offset).
+  // This wave's share of the asynchronous copies of one tile: wave w fills
+  // K blocks [w*K_PER_WAVE, (w+1)*K_PER_WAVE) (and the same range of V
+  // blocks). Copy j of the share moves one block; its offset within the row
+  // goes into the instruction's immediate, which shifts the LDS address as
+  // well, hence M0 = block base - offset. The copies of tile i+1 are spread
+  // over the q.k MFMAs of tile i so that their issue (back-pressured by the
+  // L2 -> LDS path) overlaps matrix work instead of stalling in front of it.
   const uint32_t smem_base = lds_addr(smem);
-  auto issue_tile = [&](uint32_t stage, int32_t id) {
-    const int hsel = 8 * (lane & 1);
+  struct CopySrc {
+    const uint16_t* k0;  // even-parity block source
+    const uint16_t* k1;  // odd-parity block source
+    const uint16_t* v0;
+    const uint16_t* v1;
+    uint32_t km0, vm0;
+  };
+  auto prep_copy = [&](uint32_t stage, int32_t idE, int32_t idO) -> CopySrc {
+    CopySrc cs;
+    const int hsel = 8 * hcp;
     const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_zero_row) + hsel;
     {
-      const uint16_t* src = (id >= 0 ? a.k + (int64_t)id * a.ld_k + hsel : zero) +
-                            16 * C::K_PER_WAVE * wave;
-      const uint32_t m0 =
-          __builtin_amdgcn_readfirstlane(stage + 1024u * (uint32_t)(C::K_PER_WAVE * wave));
-      static_for<C::K_PER_WAVE>([&](auto u) {
-        dma16_imm<32 * decltype(u)::value>(src, m0 + 992u * decltype(u)::value);
-      });
+      const int c0 = C::K_PER_WAVE * wave;
+      const uint16_t* sE = (idE >= 0 ? a.k + (int64_t)idE * a.ld_k + hsel : zero) + 16 * c0;
+      const uint16_t* sO = (idO >= 0 ? a.k + (int64_t)idO * a.ld_k + hsel : zero) + 16 * c0;
+      const bool flip = (c0 & 1) != 0;  // block c0 + j has parity (c0 + j) % 2
+      cs.k0 = flip ? sO : sE;
+      cs.k1 = flip ? sE : sO;
+      cs.km0 = __builtin_amdgcn_readfirstlane(stage + 1024u * (uint32_t)c0);
     }
+    cs.v0 = cs.v1 = nullptr;
+    cs.vm0 = 0;
     if constexpr (!SHARED) {
-      const uint16_t* src = (id >= 0 ? a.v + (int64_t)id * a.ld_v + hsel : zero) +
-                            16 * C::V_PER_WAVE * wave;
-      const uint32_t m0 = __builtin_amdgcn_readfirstlane(
-          stage + C::V_BASE + 1024u * (uint32_t)(C::V_PER_WAVE * wave));
-      static_for<C::V_PER_WAVE>([&](auto u) {
-        dma16_imm<32 * decltype(u)::value>(src, m0 + 992u * decltype(u)::value);
-      });
+      const int c0 = C::V_PER_WAVE * wave;
+      const uint16_t* sE = (idE >= 0 ? a.v + (int64_t)idE * a.ld_v + hsel : zero) + 16 * c0;
+      const uint16_t* sO = (idO >= 0 ? a.v + (int64_t)idO * a.ld_v + hsel : zero) + 16 * c0;
+      const bool flip = (c0 & 1) != 0;
+      cs.v0 = flip ? sO : sE;
+      cs.v1 = flip ? sE : sO;
+      cs.vm0 = __builtin_amdgcn_readfirstlane(stage + C::V_BASE + 1024u * (uint32_t)c0);
     }
+    return cs;
+  };
+  constexpr int NCOPY = C::K_PER_WAVE + C::V_PER_WAVE;
+  auto copy_one = [&](const CopySrc& cs, auto jc) {
+    constexpr int J = decltype(jc)::value;
+    if constexpr (J < C::K_PER_WAVE) {
+      dma16_imm<32 * J>((J & 1) ? cs.k1 : cs.k0, cs.km0 + 992u * J);
+    } else {
+      constexpr int U = J - C::K_PER_WAVE;
+      dma16_imm<32 * U>((U & 1) ? cs.v1 : cs.v0, cs.vm0 + 992u * U);
+    }
+  };
+  auto copy_all = [&](const CopySrc& cs) {
+    static_for<NCOPY>([&](auto jc) { copy_one(cs, jc); });
   };
 
   // Q fragments (B operand): lane -> head h0 + r32, dims 16*ks + 8*half .. +7.
@@ -200,41 +223,75 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
     l_run = 0.f;
     bool overflow = false;
 
-    int32_t id_next = -1;
+    int32_t idE_next = -1, idO_next = -1;
     uint32_t mask_cur = 0;
     if (n_tiles > 0) {
-      const int32_t id0 = valid_id(load_id(0));
-      mask_cur = even_bits(ballot(id0 >= 0));
+      const int32_t idE = valid_id(load_id(0, rowE));
+      const int32_t idO = valid_id(load_id(0, rowO));
+      mask_cur = (uint32_t)ballot(idE >= 0);  // lanes 0..31 hold rows 0..31
       if (pass == 1) __syncthreads();  // pass 0's last tile is consumed by every wave
-      issue_tile(smem_base, id0);
-      if (n_tiles > 1) id_next = load_id(kBN);
+      copy_all(prep_copy(smem_base, idE, idO));
+      if (n_tiles > 1) {
+        idE_next = load_id(kBN, rowE);
+        idO_next = load_id(kBN, rowO);
+      }
     }
 
     for (int it = 0; it < n_tiles; ++it) {
       wait_vmcnt0();
       __syncthreads();  // every wave's copies of tile it have landed; tile it-1 is consumed
       uint32_t mask_next = 0;
-      if (it + 1 < n_tiles) {
-        const int32_t idn = valid_id(id_next);
-        mask_next = even_bits(ballot(idn >= 0));
-        issue_tile(smem_base + ((it + 1) & 1) * C::STAGE_BYTES, idn);
-        id_next = (it + 2 < n_tiles) ? load_id((it + 2) * kBN) : -1;
+      const bool copy_next = it + 1 < n_tiles;  // uniform over the workgroup
+      CopySrc cs{};
+      if (copy_next) {
+        const int32_t idE = valid_id(idE_next);
+        const int32_t idO = valid_id(idO_next);
+        mask_next = (uint32_t)ballot(idE >= 0);
+        cs = prep_copy(smem_base + ((it + 1) & 1) * C::STAGE_BYTES, idE, idO);
       }
       const unsigned char* tile = smem + (it & 1) * C::STAGE_BYTES;
 
       // ---- S^T = K_tile . Q^T: lane holds head r32, keys 8*(i/4)+4*half+(i%4) ----
-      f32x16 sc;
+      // Two accumulators (even / odd k-steps) keep consecutive MFMAs independent.
+      f32x16 sc, sc1;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+      for (int i = 0; i < 16; ++i) sc[i] = sc1[i] = 0.f;
       {
-        const unsigned char* krow = tile + (2 * r32 + half) * 16;
+        // Operand reads run PF k-steps ahead of the MFMAs that use them.
+        // lane reads row r32, half `half` of block ks: slot
+        // 32*half + ((r32 + 4*half + 8*(ks%2)) mod 32)
+        const unsigned char* kE = tile + (32 * half + ((r32 + 4 * half) & 31)) * 16;
+        const unsigned char* kO = tile + (32 * half + ((r32 + 4 * half + 8) & 31)) * 16;
+        auto kread = [&](int ks) -> u32x4 {
+          return *reinterpret_cast<const u32x4*>(((ks & 1) ? kO : kE) + ks * 1024);
+        };
+        constexpr int PF = 4;
+        u32x4 af[PF];
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-          const u32x4 af = *reinterpret_cast<const u32x4*>(krow + ks * 1024);
-          sc = mfma32x32x16(af, qf[ks], sc);
-          // keep the operand reads a few steps ahead, not all hoisted
-          if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int i = 0; i < PF; ++i) af[i] = kread(i);
+        static_for<C::KS>([&](auto kc) {
+          constexpr int ks = decltype(kc)::value;
+          const u32x4 cur = af[ks % PF];
+          if constexpr (ks + PF < C::KS) af[ks % PF] = kread(ks + PF);
+          if constexpr (ks & 1)
+            sc1 = mfma32x32x16(cur, qf[ks], sc1);
+          else
+            sc = mfma32x32x16(cur, qf[ks], sc);
+          // copies j with floor(j * KS / NCOPY) == ks go out at this k-step
+          constexpr int j0 = (ks * NCOPY + C::KS - 1) / C::KS;
+          constexpr int j1 = ((ks + 1) * NCOPY + C::KS - 1) / C::KS;
+          if (copy_next) {
+            static_for<j1 - j0>([&](auto dj) {
+              copy_one(cs, std::integral_constant<int, j0 + decltype(dj)::value>{});
+            });
+          }
+        });
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[i] += sc1[i];
+      }
+      if (copy_next) {
+        idE_next = (it + 2 < n_tiles) ? load_id((it + 2) * kBN, rowE) : -1;
+        idO_next = (it + 2 < n_tiles) ? load_id((it + 2) * kBN, rowO) : -1;
       }
 
       // ---- softmax weights against the fixed reference, exp2 domain ----
@@ -256,7 +313,8 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
       float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        p[i] = live ? fast_exp2(x[i] - m_ref) : 0.f;
+        p[i] = fast_exp2(x[i] - m_ref);  // masked keys: exp2(-inf) = 0
+        p[i] = live ? p[i] : 0.f;
         psum += p[i];
       }
       l_run += psum;
@@ -274,22 +332,49 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
         // Transposed reads: 16-lane group g reads keys 16*st + 4*(g/2) (+8),
         // dims 32*nb + 16*(g%2); lane i of the group points at key + i/4,
         // dim + 4*(i%4).
-        // In slot terms: row key, dim d lives at slot 64*(d/16) + 2*key +
-        // (d%16)/8, byte 2*(d%8).
+        // Row key, dim d lives in block u = d/16 at slot
+        // 32*h + ((key + 4h + 8*(u%2)) mod 32), h = (d%16)/8, byte 2*(d%8).
+        // Group g reads block 2*nb + g%2, so u%2 = g%2; its lane li reads
+        // key + li/4 with dims + 4*(li%4), i.e. h = (li%4)/2, byte 8*(li%2).
         const int g = lane >> 4, li = lane & 15;
-        const unsigned char* vbase = tile + C::V_BASE + (g & 1) * 1024 +
-                                     (2 * (4 * (g >> 1) + (li >> 2)) + ((li & 3) >> 1)) * 16 +
-                                     8 * (li & 1);
+        const int vh = (li & 3) >> 1;
+        auto vslot = [&](int key) -> int {
+          return 32 * vh + ((key + (li >> 2) + 4 * vh + 8 * (g & 1)) & 31);
+        };
+        // The four transposed reads of column block nb+1 are issued before
+        // the two MFMAs of block nb.
+        // slot offsets of the 4 key groups used by a column block (st, lo/hi)
+        const unsigned char* vb0 = tile + C::V_BASE + (g & 1) * 1024 + 8 * (li & 1);
+        const int s00 = vslot(4 * (g >> 1)) * 16, s01 = vslot(8 + 4 * (g >> 1)) * 16;
+        const int s10 = vslot(16 + 4 * (g >> 1)) * 16, s11 = vslot(24 + 4 * (g >> 1)) * 16;
+        auto vread = [&](int nb, u32x4* vb) {
+          const unsigned char* p0 = vb0 + nb * 2048;
+          const u32x2 a0 = lds_read_tr16(p0 + s00);
+          const u32x2 a1 = lds_read_tr16(p0 + s01);
+          const u32x2 b0 = lds_read_tr16(p0 + s10);
+          const u32x2 b1 = lds_read_tr16(p0 + s11);
+          vb[0] = u32x4{a0.x, a0.y, a1.x, a1.y};
+          vb[1] = u32x4{b0.x, b0.y, b1.x, b1.y};
+        };
+        // Column blocks go in pairs so that consecutive MFMAs never
+        // accumulate into the same block; the next pair's reads are issued
+        // before the current pair's MFMAs.
+        static_assert(C::NB % 2 == 0, "column blocks are processed in pairs");
+        u32x4 vcur[4], vnxt[4];
+        vread(0, vcur);
+        vread(1, vcur + 2);
 #pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const unsigned char* p0 = vbase + nb * 2048 + st * 512;
-            const u32x2 lo = lds_read_tr16(p0);
-            const u32x2 hi = lds_read_tr16(p0 + 256);
-            o[nb] = mfma32x32x16(pa[st], u32x4{lo.x, lo.y, hi.x, hi.y}, o[nb]);
+        for (int nb = 0; nb < C::NB; nb += 2) {
+          if (nb + 2 < C::NB) {
+            vread(nb + 2, vnxt);
+            vread(nb + 3, vnxt + 2);
           }
-          if ((nb & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+          o[nb] = mfma32x32x16(pa[0], vcur[0], o[nb]);
+          o[nb + 1] = mfma32x32x16(pa[0], vcur[2], o[nb + 1]);
+          o[nb] = mfma32x32x16(pa[1], vcur[1], o[nb]);
+          o[nb + 1] = mfma32x32x16(pa[1], vcur[3], o[nb + 1]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vcur[i] = vnxt[i];
         }
       }
       mask_cur = mask_next;
@@ -341,7 +426,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
         for (int i = 0; i < 16; ++i) {
           const int hr = 8 * (i >> 2) + 4 * half + (i & 3);
           out_stage[hr * C::OUT_ROW_U16 + 32 * nb + r32] =
-              (uint16_t)f32_to_bf16_bits(o[nb][i] * iv[i]);
+              __builtin_bit_cast(uint16_t, (__bf16)(o[nb][i] * iv[i]));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
