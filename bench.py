@@ -46,6 +46,16 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB (3 times), the "
+                        "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
+    p.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
+                                                            "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
+                   help="turn four rocprofv3 --pmc output folders (FETCH_SIZE / WRITE_SIZE of "
+                        "this bench, then of --copy-calibration) into "
+                        "profiles/traffic_attention_<workload>.json")
+    p.add_argument("--calibration-mib", type=int, default=1024,
+                   help="size the --copy-calibration run used (for --summarize-traffic)")
     return p.parse_args()
 
 
@@ -81,6 +91,61 @@ def traffic_from_profile(workload_name: str):
     if rec.get("kernel_source_sha256") != sha:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def _counter_rows(folder: str, counter: str):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    if not rows:
+        raise SystemExit(f"no {counter} rows under {folder}")
+    return rows
+
+
+def summarize_traffic(args):
+    """HBM bytes per attention launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch).
+
+    Each counter is scaled by the factor that maps its reading for a plain copy
+    of known size (calibration_mib MiB read and written once) onto that size.
+    """
+    from workloads import CONFIGS
+    fetch_dir, write_dir, cal_fetch_dir, cal_write_dir = args.summarize_traffic
+    known = args.calibration_mib * 2.0 ** 20
+    res = {"workload": CONFIGS[args.config]["name"],
+           "kernel_source_sha256": hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest(),
+           "calibration_copy_bytes": known}
+    for name, folder, cal in (("fetch", fetch_dir, cal_fetch_dir), ("write", write_dir, cal_write_dir)):
+        counter = "FETCH_SIZE" if name == "fetch" else "WRITE_SIZE"
+        attn = [v for k, v in _counter_rows(folder, counter) if "sparse_attn_kernel" in k]
+        copies = [v for k, v in _counter_rows(cal, counter)]
+        cal_kib = max(copies)  # the calibration copy is by far the largest dispatch
+        factor = known / (cal_kib * 1024.0)
+        res[f"{name}_kib_per_launch"] = float(np.mean(attn))
+        res[f"{name}_launches"] = len(attn)
+        res[f"calibration_{name}_kib"] = cal_kib
+        res[f"{name}_scale"] = factor
+        res[f"{name}_bytes_per_launch"] = float(np.mean(attn)) * 1024.0 * factor
+    res["hbm_bytes_per_launch"] = res["fetch_bytes_per_launch"] + res["write_bytes_per_launch"]
+    path = os.path.join(PROFILES, f"traffic_attention_{res['workload']}.json")
+    with open(path, "w") as f:
+        json.dump(res, f, indent=1)
+        f.write("\n")
+    print(json.dumps(res), flush=True)
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib * 2 ** 20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4, "repeats": 3}), flush=True)
 
 
 def cpu_baseline(wl, rs, sl, budget_s):
@@ -147,6 +212,13 @@ def main():
         print("bench.py measures one GPU: the DSA forward path here is a single-GPU build "
               "(no collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.summarize_traffic:
+        summarize_traffic(args)
+        return
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     import torch
 

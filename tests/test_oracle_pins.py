@@ -417,3 +417,61 @@ def test_oracle_detects_planted_mistakes():
     assert np.allclose(good[fin], brute[fin])
     assert not np.allclose(no_relu[fin], brute[fin])
     assert not np.allclose(flip[fin], brute[fin])
+
+
+def _attn_mutant(q, kv, idx, sink, scale, d_v, mistake):
+    """A deliberately wrong copy of the attention definition (fp64 loops)."""
+    T, H, _ = q.shape
+    out = np.zeros((T, H, d_v))
+    lse = np.zeros((T, H))
+    for t in range(T):
+        sel = [j for j in idx[t] if 0 <= j < kv.shape[0]]
+        kk = kv[sel]
+        for h in range(H):
+            if mistake == "transposed":
+                s = scale * (kk[:, : q.shape[2]] @ q[t].T)[:, (h + 1) % H]
+            else:
+                s = (1.0 if mistake == "no_scale" else scale) * (kk @ q[t, h])
+            m = s.max()
+            e = np.exp(s - m)
+            den = e.sum() + (np.exp(sink[h] - m) if sink is not None else 0.0)
+            out[t, h] = (e @ kk[:, :d_v]) / den
+            lse[t, h] = m + np.log(den if mistake == "sink_in_lse" else e.sum())
+    return out, lse
+
+
+def test_planted_topk_and_attention_mistakes_fail_their_pins():
+    """Typical slips in the top-K and attention definitions fail the pins above."""
+    rng = np.random.default_rng(31)
+    # top-K: ties to the higher column, or one column too few, disagree with
+    # the brute-force stable sort on a tie-heavy row.
+    x = np.round(rng.standard_normal(40) * 1.5) / 1.5
+    n, k = 35, 9
+    x[n - 1] = 10.0  # the row's last valid column is selected
+    exp = _topk_brute(x, n, k)
+    assert O.topk(x[None, :], [n], k)[0][0, :k].tolist() == exp
+    high_tie = sorted(sorted(range(n), key=lambda j: (-float(x[j]), -j))[:k])
+    short = sorted(sorted(range(n - 1), key=lambda j: (-float(x[j]), j))[:k])
+    assert high_tie != exp
+    assert short != exp
+    # attention: a missing scale, the sink inside the LSE, or a transposed
+    # head/key operand disagree with the dense-identity pin (SDPA).
+    T, H, D = 9, 3, 6
+    q = rng.standard_normal((T, H, D))
+    kv = rng.standard_normal((T, D))
+    sink = rng.standard_normal(H)
+    scale = 0.41
+    idx = _causal_full_indices(T, T)
+    causal = np.where(np.tril(np.ones((T, T), dtype=bool)), 0.0, -np.inf)
+    ref = _sdpa(q.transpose(1, 0, 2), np.broadcast_to(kv, (H, T, D)),
+                np.broadcast_to(kv, (H, T, D)), scale, causal).transpose(1, 0, 2)
+    good_o, good_l, _ = O.sparse_attention(q, kv, None, idx, None, None, scale, d_v=D)
+    np.testing.assert_allclose(good_o, ref, rtol=1e-12, atol=1e-13)
+    for mistake in ("no_scale", "transposed"):
+        o, _ = _attn_mutant(q, kv, idx, None, scale, D, mistake)
+        assert not np.allclose(o, ref, atol=1e-6), mistake
+    # sink in the LSE: breaks the closed form lse(sink) == lse(no sink)
+    _, l_mut = _attn_mutant(q, kv, idx, sink, scale, D, "sink_in_lse")
+    _, l_ok, _ = O.sparse_attention(q, kv, None, idx, None, sink, scale, d_v=D)
+    np.testing.assert_allclose(l_ok, good_l, rtol=1e-12)
+    assert not np.allclose(l_mut, good_l, atol=1e-6)
