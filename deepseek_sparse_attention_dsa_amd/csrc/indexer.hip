@@ -4,14 +4,18 @@
 // Forward": S[t, j] = sum_h W[t,h] * ReLU(Q[t,h,:] . K[start(t)+j, :]) with a
 // causal mask (ratio 1, no offsets), materialised as fp32 with local columns.
 //
-// Mapping: one workgroup = 4 waves = 8 consecutive query rows (2 per wave).
-// For each query the product Q_t[H x D] . K_tile^T[D x 64] runs on
-// v_mfma_f32_16x16x32_bf16 with heads on the M dimension, so each lane ends up
-// holding 4 heads x 1 key per 16x16 block; the ReLU * W head reduction is then
-// an in-lane FMA chain plus two cross-lane adds. Q fragments stay in VGPRs for
-// the whole key loop; each 64-key tile of K is staged once in LDS and shared
-// by the 8 queries of the workgroup. Workgroups are issued longest-row first
-// so the causal triangle's short rows fill the tail.
+// Mapping: one workgroup = 8 waves = 8 consecutive query rows, one per wave
+// (two waves per SIMD, so one wave's epilogue overlaps the other's MFMAs).
+// For its query, a wave computes Q_t[H x D] . K_tile^T[D x 32] on
+// v_mfma_f32_32x32x16_bf16 with heads on the M dimension (32 heads per MFMA
+// block): lane l ends up with key l % 32 and 16 of the block's heads, so the
+// ReLU * W head reduction is an in-lane max + FMA chain plus one exchange
+// between the two half-waves. Q fragments and the lane's 16 weights per head
+// block stay in registers for the whole key loop; 64-key tiles of K are
+// staged in a double-buffered LDS ring (16-byte padded rows, conflict-free
+// operand reads) and shared by the 8 queries. Each wave writes its 64 scores
+// of a tile as one contiguous 256-byte run. Workgroups are issued longest row
+// first so the causal triangle's short rows fill the tail.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -35,9 +39,7 @@ __global__ void packed_metadata_kernel(const int32_t* __restrict__ cu, int32_t n
 
 namespace {
 
-constexpr int kIdxWaves = 4;
-constexpr int kIdxQPerWave = 2;
-constexpr int kIdxRows = kIdxWaves * kIdxQPerWave;  // query rows per workgroup
+constexpr int kIdxWaves = 8;                        // = query rows per workgroup
 constexpr int kIdxTile = 64;                        // keys per LDS tile
 
 template <typename WT>
@@ -51,35 +53,40 @@ __device__ __forceinline__ float load_w<float>(const float* w, int64_t i) {
   return w[i];
 }
 
-// D: indexer head dim (64 or 128). MB: number of 16-head blocks (H <= 16*MB).
+// D: indexer head dim (64 or 128). MB: number of 32-head blocks (H <= 32*MB).
 template <int D, int MB, typename WT>
-__global__ __launch_bounds__(256, 2) void indexer_kernel(
+__global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const WT* __restrict__ w,
     const int32_t* __restrict__ row_starts, const int32_t* __restrict__ seq_lens, int64_t T,
     int H, int64_t row_begin, int64_t n_rows, float* __restrict__ scores, int64_t ld) {
-  constexpr int KS = D / 32;                 // MFMA k-steps over the head dim
-  constexpr int ROW_U32 = D / 2 + 4;         // LDS row stride in u32 (16 B pad)
-  __shared__ uint32_t ktile[kIdxTile * ROW_U32];
+  constexpr int KS = D / 16;                      // MFMA k-steps over the head dim
+  constexpr int ROW_B = 2 * D + 16;               // LDS row stride in bytes (16 B pad)
+  constexpr int TILE_B = kIdxTile * ROW_B;
+  constexpr int CHUNKS = kIdxTile * D / 8;        // 16-byte chunks per tile
+  constexpr int NT = kIdxWaves * 64;
+  constexpr int LOADS = (CHUNKS + NT - 1) / NT;   // 16-byte loads per thread and tile
+  __shared__ __attribute__((aligned(16))) unsigned char ktile[2 * TILE_B];
   __shared__ int32_t s_range[2];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int64_t n_qblk = (n_rows + kIdxRows - 1) / kIdxRows;
+  const int half = lane >> 5;
+  const int64_t n_qblk = (n_rows + kIdxWaves - 1) / kIdxWaves;
   const int64_t qblk = n_qblk - 1 - blockIdx.x;   // longest rows first
-  const int64_t r0 = qblk * kIdxRows;
+  const int64_t r0 = qblk * kIdxWaves;
 
   // Key range of the workgroup: union of [start, start + len) of its rows.
   if (threadIdx.x == 0) {
     int32_t kb = INT32_MAX, ke = 0;
-    for (int i = 0; i < kIdxRows; ++i) {
-      int64_t r = r0 + i;
+    for (int i = 0; i < kIdxWaves; ++i) {
+      const int64_t r = r0 + i;
       if (r < n_rows) {
-        int64_t t = row_begin + r;
-        int32_t s = row_starts[t];
-        int32_t n = seq_lens[t];
+        const int64_t t = row_begin + r;
+        const int32_t s0 = row_starts[t];
+        const int32_t n = (int32_t)min((int64_t)seq_lens[t], ld);
         if (n > 0) {
-          kb = min(kb, s);
-          ke = max(ke, s + n);
+          kb = min(kb, s0);
+          ke = max(ke, s0 + n);
         }
       }
     }
@@ -87,93 +94,143 @@ __global__ __launch_bounds__(256, 2) void indexer_kernel(
     s_range[1] = ke;
   }
 
-  // Per-query registers: Q fragments (A operand, heads as rows), weights of
-  // the 4 output rows this lane holds per head block, start and length.
-  u32x4 qa[kIdxQPerWave][MB][KS];
-  float wv[kIdxQPerWave][MB][4];
-  int32_t qstart[kIdxQPerWave], qlen[kIdxQPerWave];
-  int64_t qrow[kIdxQPerWave];
+  // This wave's query: Q fragments (A operand: lane -> head 32*mb + l%32,
+  // dims 16*ks + 8*half .. +7) and the weights of the 16 heads whose scores
+  // the lane receives per head block: 32*mb + 8*(i/4) + 4*half + i%4.
+  const int64_t r = r0 + wave;
+  const bool live = r < n_rows;
+  const int64_t t = row_begin + (live ? r : 0);
+  const int32_t qstart = live ? row_starts[t] : 0;
+  const int32_t qlen = live ? (int32_t)min((int64_t)seq_lens[t], ld) : 0;
+  u32x4 qa[MB][KS];
+  float wv[MB][16];
 #pragma unroll
-  for (int qi = 0; qi < kIdxQPerWave; ++qi) {
-    const int64_t r = r0 + wave * kIdxQPerWave + qi;
-    qrow[qi] = r;
-    const bool live = r < n_rows;
-    const int64_t t = row_begin + (live ? r : 0);
-    qstart[qi] = live ? row_starts[t] : 0;
-    int32_t n = live ? seq_lens[t] : 0;
-    qlen[qi] = (int32_t)min((int64_t)n, ld);
+  for (int mb = 0; mb < MB; ++mb) {
+    const int head = mb * 32 + (lane & 31);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int head = mb * 16 + (lane & 15);
+    for (int ks = 0; ks < KS; ++ks)
+      qa[mb][ks] = (live && head < H) ? load16(q + ((t * H + head) * D + ks * 16 + 8 * half))
+                                      : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (live && head < H)
-          qa[qi][mb][ks] = load16(q + ((t * H + head) * D + ks * 32 + 8 * (lane >> 4)));
-        else
-          qa[qi][mb][ks] = u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int oh = mb * 16 + 4 * (lane >> 4) + i;
-        wv[qi][mb][i] = (live && oh < H) ? load_w<WT>(w, t * H + oh) : 0.0f;
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int oh = mb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+      wv[mb][i] = (live && oh < H) ? load_w<WT>(w, t * H + oh) : 0.0f;
     }
   }
   __syncthreads();
   const int32_t kb = s_range[0];
   const int32_t ke = s_range[1];
+  if (kb >= ke) return;  // uniform: no row of the workgroup has a key
 
-  for (int32_t k0 = kb; k0 < ke; k0 += kIdxTile) {
-    // Stage keys [k0, k0 + 64) in LDS; rows past the range are zero.
-    constexpr int CHUNKS = kIdxTile * D / 8;  // 16-byte chunks per tile
+  // Staging of keys [k0, k0 + 64): thread -> chunks c = tid + NT*i.
+  u32x4 stage[LOADS];
+  auto load_tile = [&](int32_t k0) {
 #pragma unroll
-    for (int c = threadIdx.x; c < CHUNKS; c += 256) {
-      const int row = c / (D / 8);
-      const int col = c % (D / 8);
-      const int32_t key = k0 + row;
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (key < ke && key >= 0 && key < T) v = load16(k + (int64_t)key * D + col * 8);
-      *reinterpret_cast<u32x4*>(&ktile[row * ROW_U32 + col * 4]) = v;
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = threadIdx.x + NT * i;
+      const int32_t key = k0 + c / (D / 8);
+      stage[i] = u32x4{0u, 0u, 0u, 0u};
+      if (c < CHUNKS && key < ke && key >= 0 && key < T)
+        stage[i] = load16(k + (int64_t)key * D + (c % (D / 8)) * 8);
     }
-    __syncthreads();
-
-    float res[kIdxQPerWave];
+  };
+  auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int qi = 0; qi < kIdxQPerWave; ++qi) res[qi] = 0.0f;
+    for (int i = 0; i < LOADS; ++i) {
+      const int c = threadIdx.x + NT * i;
+      if (c < CHUNKS)
+        *reinterpret_cast<u32x4*>(ktile + buf * TILE_B + (c / (D / 8)) * ROW_B +
+                                  (c % (D / 8)) * 16) = stage[i];
+    }
+  };
 
+  // The epilogue of each 32-key block runs under the MFMAs of the next one:
+  // block 0 of tile i overlaps the epilogue of block 1 of tile i-1, block 1
+  // overlaps the epilogue of block 0 of tile i.
+  f32x16 acc0[MB], acc1[MB];  // block 0 / block 1 of the current tile
 #pragma unroll
-    for (int nb = 0; nb < kIdxTile / 16; ++nb) {
-      u32x4 kb_frag[KS];
-      const int krow = nb * 16 + (lane & 15);
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc0[mb][i] = acc1[mb][i] = 0.0f;
+  auto epilogue = [&](const f32x16* acc) -> float {
+    float p = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) p = fmaf(wv[mb][i], fmaxf(acc[mb][i], 0.0f), p);
+    return p;
+  };
+  // B operand: lane -> key 32*nb + l%32, dims 16*ks + 8*half .. +7
+  auto block_mfma = [&](const unsigned char* kt, int nb, f32x16* acc) {
+    u32x4 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[ks] = *reinterpret_cast<const u32x4*>(kt + (32 * nb + (lane & 31)) * ROW_B + ks * 32 +
+                                               16 * half);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        kb_frag[ks] = *reinterpret_cast<const u32x4*>(&ktile[krow * ROW_U32 + ks * 16 + 4 * (lane >> 4)]);
+        acc[mb] = mfma32x32x16(qa[mb][ks], kf[ks], ks == 0 ? f32x16{} : acc[mb]);
+    }
+  };
+  // Interleave: the block's operand reads first, then one MFMA per 4 VALU ops.
+  auto interleave = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // DS reads
 #pragma unroll
-      for (int qi = 0; qi < kIdxQPerWave; ++qi) {
-        float part = 0.0f;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(qa[qi][mb][ks], kb_frag[ks], acc);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) part = fmaf(wv[qi][mb][i], fmaxf(acc[i], 0.0f), part);
-        }
-        part += shfl_xor_f(part, 16);
-        part += shfl_xor_f(part, 32);
-        if ((lane >> 4) == nb) res[qi] = part;
-      }
+    for (int i = 0; i < MB * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 32 / KS, 0);  // VALU
+    }
+  };
+  // Lane l < 32 sums key l of block 0 over both half-waves, lane l >= 32
+  // key l - 32 of block 1: one exchange between the half-waves.
+  auto write_scores = [&](int32_t k0, float p0, float p1) {
+    const float mine = half ? p1 : p0;
+    const float other = half ? p0 : p1;
+    const float score = mine + shfl_xor_f(other, 32);
+    const int64_t j = (int64_t)(k0 + lane) - qstart;
+    if (j >= 0 && j < qlen) scores[r * ld + j] = score;
+  };
+
+  load_tile(kb);
+  store_tile(0);
+  __syncthreads();
+  int buf = 0;
+  bool pend = false;      // block 1 of tile pend_k0 awaits its epilogue
+  int32_t pend_k0 = 0;
+  float pend_p0 = 0.0f;   // its block-0 partial
+  for (int32_t k0 = kb; k0 < ke; k0 += kIdxTile) {
+    const bool more = k0 + kIdxTile < ke;  // uniform
+    if (more) load_tile(k0 + kIdxTile);
+
+    // Keys of this tile that belong to the query: [qstart, qstart + qlen).
+    const bool any = live && k0 < qstart + qlen && k0 + kIdxTile > qstart;  // wave-uniform
+    if (any) {
+      const unsigned char* kt = ktile + buf * TILE_B;
+      block_mfma(kt, 0, acc0);
+      const float p1_prev = epilogue(acc1);
+      interleave();
+      asm volatile("" ::"v"(p1_prev));  // keep the epilogue here, not sunk into the branch
+      if (pend) write_scores(pend_k0, pend_p0, p1_prev);
+      block_mfma(kt, 1, acc1);
+      const float p0 = epilogue(acc0);
+      interleave();
+      pend = true;
+      pend_k0 = k0;
+      pend_p0 = p0;
+    } else if (pend) {
+      write_scores(pend_k0, pend_p0, epilogue(acc1));
+      pend = false;
     }
 
-    // Lane l now holds the score of key k0 + l for each of its queries.
-#pragma unroll
-    for (int qi = 0; qi < kIdxQPerWave; ++qi) {
-      const int64_t j = (int64_t)(k0 + lane) - qstart[qi];
-      if (qrow[qi] < n_rows && j >= 0 && j < qlen[qi])
-        scores[qrow[qi] * ld + j] = res[qi];
+    if (more) {
+      store_tile(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
     }
-    __syncthreads();
   }
+  if (pend) write_scores(pend_k0, pend_p0, epilogue(acc1));
 }
 
 template <int D, int MB>
@@ -181,8 +238,8 @@ hipError_t launch_indexer_w(const void* q, const void* k, const void* w, int w_d
                             const int32_t* rs, const int32_t* sl, int64_t T, int H,
                             int64_t row_begin, int64_t n_rows, float* scores, int64_t ld,
                             hipStream_t st) {
-  const int64_t nblk = (n_rows + kIdxRows - 1) / kIdxRows;
-  dim3 grid((unsigned)nblk), block(256);
+  const int64_t nblk = (n_rows + kIdxWaves - 1) / kIdxWaves;
+  dim3 grid((unsigned)nblk), block(kIdxWaves * 64);
   if (w_dtype == 0)
     hipLaunchKernelGGL((indexer_kernel<D, MB, uint16_t>), grid, block, 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)w, rs, sl, T, H,
@@ -209,13 +266,12 @@ hipError_t launch_indexer(const void* q, const void* k, const void* w, int w_dty
                           int64_t row_begin, int64_t n_rows, float* scores, int64_t ld,
                           hipStream_t st) {
   if (n_rows == 0) return hipSuccess;
-  const int mb = (H + 15) / 16;
+  const int mb = (H + 31) / 32;
 #define DSA_IDX_CASE(DD, MM)                                                                   \
   if (D == DD && mb == MM)                                                                     \
     return launch_indexer_w<DD, MM>(q, k, w, w_dtype, rs, sl, T, H, row_begin, n_rows, scores, \
                                     ld, st);
-  DSA_IDX_CASE(128, 1) DSA_IDX_CASE(128, 2) DSA_IDX_CASE(128, 3) DSA_IDX_CASE(128, 4)
-  DSA_IDX_CASE(64, 1) DSA_IDX_CASE(64, 2) DSA_IDX_CASE(64, 3) DSA_IDX_CASE(64, 4)
+  DSA_IDX_CASE(128, 1) DSA_IDX_CASE(128, 2) DSA_IDX_CASE(64, 1) DSA_IDX_CASE(64, 2)
 #undef DSA_IDX_CASE
   return hipErrorInvalidValue;
 }
