@@ -42,6 +42,12 @@ namespace {
 constexpr int kIdxWaves = 8;                        // = query rows per workgroup
 constexpr int kIdxTile = 64;                        // keys per LDS tile
 
+// max(x, 0) for finite x as one v_med3_f32 (clamp to [0, FLT_MAX]); fmaxf
+// would first quiet a possible NaN in x with a second instruction.
+__device__ __forceinline__ float relu(float x) {
+  return __builtin_amdgcn_fmed3f(x, 0.0f, 3.40282347e38f);
+}
+
 template <typename WT>
 __device__ __forceinline__ float load_w(const WT* w, int64_t i);
 template <>
@@ -124,14 +130,22 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
 
   // Staging of keys [k0, k0 + 64): thread -> chunks c = tid + NT*i.
   u32x4 stage[LOADS];
+  // The staging has no branches: keys past the range are loaded from a
+  // clamped row (the validity bit is kept, not applied to the value of the
+  // load, which is still in flight) and zeroed when stored to LDS.
+  uint32_t stage_ok = 0;
   auto load_tile = [&](int32_t k0) {
+    stage_ok = 0;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const int c = threadIdx.x + NT * i;
-      const int32_t key = k0 + c / (D / 8);
-      stage[i] = u32x4{0u, 0u, 0u, 0u};
-      if (c < CHUNKS && key < ke && key >= 0 && key < T)
-        stage[i] = load16(k + (int64_t)key * D + (c % (D / 8)) * 8);
+      if (c < CHUNKS) {
+        const int32_t key = k0 + c / (D / 8);
+        const bool ok = key < ke && key >= 0 && key < T;
+        const int32_t kc = ok ? key : (int32_t)(T - 1);
+        stage[i] = load16(k + (int64_t)kc * D + (c % (D / 8)) * 8);
+        stage_ok |= ok ? (1u << i) : 0u;
+      }
     }
   };
   auto store_tile = [&](int buf) {
@@ -140,7 +154,8 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
       const int c = threadIdx.x + NT * i;
       if (c < CHUNKS)
         *reinterpret_cast<u32x4*>(ktile + buf * TILE_B + (c / (D / 8)) * ROW_B +
-                                  (c % (D / 8)) * 16) = stage[i];
+                                  (c % (D / 8)) * 16) =
+            ((stage_ok >> i) & 1u) ? stage[i] : u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -157,7 +172,7 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) p = fmaf(wv[mb][i], fmaxf(acc[mb][i], 0.0f), p);
+      for (int i = 0; i < 16; ++i) p = fmaf(wv[mb][i], relu(acc[mb][i]), p);
     return p;
   };
   // B operand: lane -> key 32*nb + l%32, dims 16*ks + 8*half .. +7
