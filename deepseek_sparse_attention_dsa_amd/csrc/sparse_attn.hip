@@ -14,19 +14,25 @@
 // v_mfma_f32_32x32x16_bf16 (the 16x16x32 form runs at half the bf16 rate on
 // gfx950).
 //  * The wave's 32 heads of Q stay in VGPRs for the whole row as the B
-//    operand of S^T = K_tile . Q^T; O[32 heads x D_v] accumulates in fp32
-//    registers (1 wave per SIMD: 144 + 256 registers for D_qk = 576).
+//    operand of S^T = K_tile . Q^T (one accumulator chain); O[32 heads x D_v]
+//    accumulates in fp32 registers (1 wave per SIMD: 144 + 256 registers for
+//    D_qk = 576).
 //  * Tiles of 32 selected KV rows are gathered with asynchronous
 //    global -> LDS copies (global_load_lds_dwordx4) into a 2-stage ring: the
-//    copy of tile i+1 runs while tile i is computed. Dims [16u, 16u+16) of
-//    the 32 rows form 1 KiB block u of 16-byte slots; row r, half h (dims
-//    16u + 8h .. +7) sits in slot 32*h + ((r + 4h + 8*(u%2)) mod 32). One
-//    copy instruction fills one block, lane l always copying the same row
-//    (one per block parity, so no lane looks up another lane's id). With
-//    this rotation the q.k operand read of a k-step is 1 KiB in lane order,
-//    and the two 16-lane groups of each half-wave of a transposed v read hit
-//    disjoint LDS banks. Invalid rows copy from a zero constant, so masked
-//    rows hold zeros (0 * V never meets a non-finite value).
+//    copies of tile i+1 are interleaved with the q.k MFMAs of tile i (during
+//    p.v they would compete with the transposed V reads for LDS). Rows
+//    8g .. 8g+7 (row group g) and dims 64s .. 64s+63 (segment s) of a tile
+//    form the 1 KiB block 4s + g: one copy instruction moves it as eight whole
+//    128-byte row segments, consecutive lanes taking consecutive 16-byte
+//    chunks of one row (8 cache-line requests, where 32 rows x 32 bytes would
+//    need 32; the gather runs about 1.5x faster that way, and only runs of
+//    consecutive lanes coalesce). Inside the block, the
+//    16-byte chunk c (dims 64s + 8c .. +7) of row 8g + r sits in slot
+//    8r + (c ^ f(r, g)) with f = 4*((r>>1)&1) + (r>>2) + 2*(g&1). Under this
+//    swizzle a q.k operand read (16 lanes: rows 16m .. 16m+15, one chunk) and
+//    a transposed v read (16 or 32 lanes: 4 rows x 2 or 4 chunks) touch
+//    every LDS bank at most once. Invalid rows copy from a zero constant, so
+//    masked rows hold zeros (0 * V never meets a non-finite value).
 //  * p.v reads V straight from the same row-major tile with
 //    ds_read_b64_tr_b16 (4 keys x 16 dims per 16-lane group, transposed), so
 //    no transposed copy of V is ever written.
@@ -53,6 +59,8 @@ __device__ const u32x4 g_zero_row[128] = {};
 namespace {
 
 constexpr int kBN = 32;          // key slots per tile
+constexpr int kCopyStart = 0;
+constexpr int kCopyTail = 32;
 constexpr float kHeadroom = 64.0f;  // logits may exceed the reference by 2^64
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963387f;
@@ -62,13 +70,17 @@ struct Cfg {
   static constexpr int NT = NW * 64;
   static constexpr int KS = DQK / 16;                       // q.k k-steps
   static constexpr int NB = DV / 32;                        // p.v column blocks
-  static constexpr int K_INST = DQK / 16;                   // copy instructions for K
-  static constexpr int V_INST = SHARED ? 0 : DV / 16;       // ... and for a separate V
+  static constexpr int K_SEG = DQK / 64;                    // 64-dim segments of a K row
+  static constexpr int V_SEG = SHARED ? 0 : DV / 64;        // ... of a separate V row
+  static constexpr int K_INST = 4 * K_SEG;                  // copy instructions (1 KiB blocks) for K
+  static constexpr int V_INST = 4 * V_SEG;                  // ... and for a separate V
+  static constexpr int GPW = 4 / NW;                        // row groups copied per wave
   static constexpr int INST = K_INST + V_INST;
   static constexpr int K_PER_WAVE = K_INST / NW;            // copies per wave and tile
   static constexpr int V_PER_WAVE = V_INST / NW;
   static constexpr int STAGE_BYTES = INST * 1024;
-  static_assert(K_INST % NW == 0 && V_INST % NW == 0, "copies must split evenly over waves");
+  static_assert(NW == 1 || NW == 2 || NW == 4, "row groups split evenly over waves");
+  static_assert(DQK % 64 == 0 && DV % 64 == 0, "rows are copied in 64-dim segments");
   static constexpr int V_BASE = SHARED ? 0 : K_INST * 1024; // byte offset of the V slots
   static constexpr int OUT_ROW_U16 = DV + 8;                // staged output row (bf16)
   static constexpr int STAGE_OUT_WAVES =
@@ -115,12 +127,12 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
   if (a.T_kv <= 0) L = 0;
   const int n_tiles = (L + kBN - 1) / kBN;
 
-  // Copy lanes: lane l fills slot l of every block, i.e. half h = l/32 of
-  // row (l%32 - 4h - 8*(u%2)) mod 32. rowE / rowO are its rows in even / odd
-  // blocks.
-  const int hcp = lane >> 5;
-  const int rowE = ((lane & 31) - 4 * hcp) & 31;
-  const int rowO = ((lane & 31) - 4 * hcp - 8) & 31;
+  // Every lane tracks the id of tile row lane % 32 (the key mask needs all
+  // 32). As a copy lane, lane l fills slot l of a block: row 8g + (l >> 3),
+  // chunk (l & 7) ^ f(l >> 3, g).
+  const int key_row = lane & 31;
+  const int crow = lane >> 3;
+  auto swz = [](int r, int g) -> int { return 4 * ((r >> 1) & 1) + (r >> 2) + 2 * (g & 1); };
 
   // Raw index of row `row` of the tile starting at slot j0 (-1 past the
   // valid prefix). It is validated only when used, one iteration later: a
@@ -136,55 +148,46 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
     return (raw >= 0 && (int64_t)raw < a.T_kv) ? raw : -1;
   };
 
-  // This wave's share of the asynchronous copies of one tile: wave w fills
-  // K blocks [w*K_PER_WAVE, (w+1)*K_PER_WAVE) (and the same range of V
-  // blocks). Copy j of the share moves one block; its offset within the row
-  // goes into the instruction's immediate, which shifts the LDS address as
-  // well, hence M0 = block base - offset. The copies of tile i+1 are spread
-  // over the q.k MFMAs of tile i so that their issue (back-pressured by the
-  // L2 -> LDS path) overlaps matrix work instead of stalling in front of it.
+  // This wave's share of the asynchronous copies of one tile: wave w copies
+  // row groups g = GPW*w + gi (gi < GPW) of every segment. Copy j of the
+  // share moves block (g = GPW*w + j % GPW, s = j / GPW) of K, then the
+  // same for a separate V. The segment offset 128*s goes into the
+  // instruction's immediate, which shifts the LDS address as well, hence
+  // M0 = block base - 128*s.
   const uint32_t smem_base = lds_addr(smem);
   struct CopySrc {
-    const uint16_t* k0;  // even-parity block source
-    const uint16_t* k1;  // odd-parity block source
-    const uint16_t* v0;
-    const uint16_t* v1;
-    uint32_t km0, vm0;
+    const uint16_t* k[C::GPW];  // per row group: this lane's row + chunk
+    const uint16_t* v[SHARED ? 1 : C::GPW];
+    uint32_t m0;                // stage + first block of this wave's groups
   };
-  auto prep_copy = [&](uint32_t stage, int32_t idE, int32_t idO) -> CopySrc {
+  // idv: validated id of tile row lane % 32 (-1: zero row).
+  auto prep_copy = [&](uint32_t stage, int32_t idv) -> CopySrc {
     CopySrc cs;
-    const int hsel = 8 * hcp;
-    const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_zero_row) + hsel;
-    {
-      const int c0 = C::K_PER_WAVE * wave;
-      const uint16_t* sE = (idE >= 0 ? a.k + (int64_t)idE * a.ld_k + hsel : zero) + 16 * c0;
-      const uint16_t* sO = (idO >= 0 ? a.k + (int64_t)idO * a.ld_k + hsel : zero) + 16 * c0;
-      const bool flip = (c0 & 1) != 0;  // block c0 + j has parity (c0 + j) % 2
-      cs.k0 = flip ? sO : sE;
-      cs.k1 = flip ? sE : sO;
-      cs.km0 = __builtin_amdgcn_readfirstlane(stage + 1024u * (uint32_t)c0);
+    const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_zero_row);
+#pragma unroll
+    for (int gi = 0; gi < C::GPW; ++gi) {
+      const int g = C::GPW * wave + gi;
+      const int32_t id = __shfl(idv, 8 * g + crow, kWave);
+      const int chunk = (lane & 7) ^ swz(crow, g);
+      cs.k[gi] = (id >= 0 ? a.k + (int64_t)id * a.ld_k : zero) + 8 * chunk;
+      if constexpr (!SHARED) cs.v[gi] = (id >= 0 ? a.v + (int64_t)id * a.ld_v : zero) + 8 * chunk;
     }
-    cs.v0 = cs.v1 = nullptr;
-    cs.vm0 = 0;
-    if constexpr (!SHARED) {
-      const int c0 = C::V_PER_WAVE * wave;
-      const uint16_t* sE = (idE >= 0 ? a.v + (int64_t)idE * a.ld_v + hsel : zero) + 16 * c0;
-      const uint16_t* sO = (idO >= 0 ? a.v + (int64_t)idO * a.ld_v + hsel : zero) + 16 * c0;
-      const bool flip = (c0 & 1) != 0;
-      cs.v0 = flip ? sO : sE;
-      cs.v1 = flip ? sE : sO;
-      cs.vm0 = __builtin_amdgcn_readfirstlane(stage + C::V_BASE + 1024u * (uint32_t)c0);
-    }
+    if constexpr (SHARED) cs.v[0] = nullptr;
+    cs.m0 = __builtin_amdgcn_readfirstlane(stage + 1024u * (uint32_t)(C::GPW * wave));
     return cs;
   };
   constexpr int NCOPY = C::K_PER_WAVE + C::V_PER_WAVE;
+  static_assert(C::K_PER_WAVE == C::GPW * C::K_SEG && C::V_PER_WAVE == C::GPW * C::V_SEG,
+                "copy shares");
   auto copy_one = [&](const CopySrc& cs, auto jc) {
     constexpr int J = decltype(jc)::value;
     if constexpr (J < C::K_PER_WAVE) {
-      dma16_imm<32 * J>((J & 1) ? cs.k1 : cs.k0, cs.km0 + 992u * J);
+      constexpr int GI = J % C::GPW, S = J / C::GPW;
+      dma16_imm<128 * S>(cs.k[GI], cs.m0 + (uint32_t)(1024 * (4 * S + GI) - 128 * S));
     } else {
       constexpr int U = J - C::K_PER_WAVE;
-      dma16_imm<32 * U>((U & 1) ? cs.v1 : cs.v0, cs.vm0 + 992u * U);
+      constexpr int GI = U % C::GPW, S = U / C::GPW;
+      dma16_imm<128 * S>(cs.v[GI], cs.m0 + (uint32_t)(C::V_BASE + 1024 * (4 * S + GI) - 128 * S));
     }
   };
   auto copy_all = [&](const CopySrc& cs) {
@@ -223,18 +226,14 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
     l_run = 0.f;
     bool overflow = false;
 
-    int32_t idE_next = -1, idO_next = -1;
+    int32_t id_next = -1;
     uint32_t mask_cur = 0;
     if (n_tiles > 0) {
-      const int32_t idE = valid_id(load_id(0, rowE));
-      const int32_t idO = valid_id(load_id(0, rowO));
-      mask_cur = (uint32_t)ballot(idE >= 0);  // lanes 0..31 hold rows 0..31
+      const int32_t id0 = valid_id(load_id(0, key_row));
+      mask_cur = (uint32_t)ballot(id0 >= 0);  // lanes 0..31 hold rows 0..31
       if (pass == 1) __syncthreads();  // pass 0's last tile is consumed by every wave
-      copy_all(prep_copy(smem_base, idE, idO));
-      if (n_tiles > 1) {
-        idE_next = load_id(kBN, rowE);
-        idO_next = load_id(kBN, rowO);
-      }
+      copy_all(prep_copy(smem_base, id0));
+      if (n_tiles > 1) id_next = load_id(kBN, key_row);
     }
 
     for (int it = 0; it < n_tiles; ++it) {
@@ -244,26 +243,46 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
       const bool copy_next = it + 1 < n_tiles;  // uniform over the workgroup
       CopySrc cs{};
       if (copy_next) {
-        const int32_t idE = valid_id(idE_next);
-        const int32_t idO = valid_id(idO_next);
-        mask_next = (uint32_t)ballot(idE >= 0);
-        cs = prep_copy(smem_base + ((it + 1) & 1) * C::STAGE_BYTES, idE, idO);
+        const int32_t idv = valid_id(id_next);
+        mask_next = (uint32_t)ballot(idv >= 0);
+        cs = prep_copy(smem_base + ((it + 1) & 1) * C::STAGE_BYTES, idv);
       }
       const unsigned char* tile = smem + (it & 1) * C::STAGE_BYTES;
+      constexpr int S0 = kCopyStart;
+      constexpr int S1 =
+          C::KS + 2 * C::NB - kCopyTail > C::KS ? C::KS + 2 * C::NB - kCopyTail : C::KS;
+      constexpr int NSLOT = S1 - S0;
+      auto copies_at_slot = [&](auto slotc) {
+        constexpr int sl = decltype(slotc)::value - S0;
+        constexpr int j0 = sl < 0 ? 0 : sl < NSLOT ? (sl * NCOPY + NSLOT - 1) / NSLOT : NCOPY;
+        constexpr int j1 = sl < 0 ? 0 : sl < NSLOT ? ((sl + 1) * NCOPY + NSLOT - 1) / NSLOT : NCOPY;
+        if (copy_next) {
+          static_for<j1 - j0>([&](auto dj) {
+            copy_one(cs, std::integral_constant<int, j0 + decltype(dj)::value>{});
+          });
+        }
+      };
 
       // ---- S^T = K_tile . Q^T: lane holds head r32, keys 8*(i/4)+4*half+(i%4) ----
-      // Two accumulators (even / odd k-steps) keep consecutive MFMAs independent.
-      f32x16 sc, sc1;
+      // One accumulator chain: the copies interleaved with the k-steps keep
+      // dependent MFMAs apart, and a second chain would cost 16 registers and
+      // 16 adds per tile.
+      f32x16 sc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = sc1[i] = 0.f;
+      for (int i = 0; i < 16; ++i) sc[i] = 0.f;
       {
         // Operand reads run PF k-steps ahead of the MFMAs that use them.
-        // lane reads row r32, half `half` of block ks: slot
-        // 32*half + ((r32 + 4*half + 8*(ks%2)) mod 32)
-        const unsigned char* kE = tile + (32 * half + ((r32 + 4 * half) & 31)) * 16;
-        const unsigned char* kO = tile + (32 * half + ((r32 + 4 * half + 8) & 31)) * 16;
+        // k-step ks: the lane reads row r32 (group g = r32/8, r = r32%8),
+        // chunk c = 2*(ks%4) + half of segment ks/4, at slot 8r + (c ^ f);
+        // c ^ f = 2*((ks%4) ^ (f>>1)) + (half ^ (f&1)).
+        const int kg = r32 >> 3, kr = r32 & 7;
+        const int kf = swz(kr, kg);
+        const unsigned char* kbase = tile + kg * 1024 + kr * 128 + 16 * (half ^ (kf & 1));
+        const unsigned char* kq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) kq[q] = kbase + 32 * (q ^ (kf >> 1));
         auto kread = [&](int ks) -> u32x4 {
-          return *reinterpret_cast<const u32x4*>(((ks & 1) ? kO : kE) + ks * 1024);
+          return *reinterpret_cast<const u32x4*>(kq[ks & 3] + (ks >> 2) * 4096);
         };
         constexpr int PF = 4;
         u32x4 af[PF];
@@ -273,50 +292,49 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
           constexpr int ks = decltype(kc)::value;
           const u32x4 cur = af[ks % PF];
           if constexpr (ks + PF < C::KS) af[ks % PF] = kread(ks + PF);
-          if constexpr (ks & 1)
-            sc1 = mfma32x32x16(cur, qf[ks], sc1);
-          else
-            sc = mfma32x32x16(cur, qf[ks], sc);
-          // copies j with floor(j * KS / NCOPY) == ks go out at this k-step
-          constexpr int j0 = (ks * NCOPY + C::KS - 1) / C::KS;
-          constexpr int j1 = ((ks + 1) * NCOPY + C::KS - 1) / C::KS;
-          if (copy_next) {
-            static_for<j1 - j0>([&](auto dj) {
-              copy_one(cs, std::integral_constant<int, j0 + decltype(dj)::value>{});
-            });
-          }
+          sc = mfma32x32x16(cur, qf[ks], sc);
+          copies_at_slot(std::integral_constant<int, ks>{});
         });
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[i] += sc1[i];
-      }
-      if (copy_next) {
-        idE_next = (it + 2 < n_tiles) ? load_id((it + 2) * kBN, rowE) : -1;
-        idO_next = (it + 2 < n_tiles) ? load_id((it + 2) * kBN, rowO) : -1;
       }
 
+      if (copy_next) id_next = (it + 2 < n_tiles) ? load_id((it + 2) * kBN, key_row) : -1;
+
       // ---- softmax weights against the fixed reference, exp2 domain ----
-      float x[16];
+      // Tiles whose 32 slots are all valid (the usual case inside a compact
+      // prefix) skip the per-key mask. Scale and reference fold into one FMA
+      // (scale > 0, so the raw max scales to the scaled max). Once a pass has
+      // overflowed, its results are discarded and the row is run again, so
+      // no select guards the weights against it.
+      const bool full = mask_cur == 0xFFFFFFFFu;  // uniform
       float mloc = -__builtin_inff();
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = 8 * (i >> 2) + 4 * half + (i & 3);
-        const bool ok = (mask_cur >> key) & 1u;
-        x[i] = ok ? sc[i] * a.scale_log2 : -__builtin_inff();
-        mloc = fmaxf(mloc, x[i]);
+        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sc[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = 8 * (i >> 2) + 4 * half + (i & 3);
+          mloc = fmaxf(mloc, ((mask_cur >> key) & 1u) ? sc[i] : -__builtin_inff());
+        }
       }
-      mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
+      mloc = fmaxf(mloc, shfl_xor_f(mloc, 32)) * a.scale_log2;
       m_true = fmaxf(m_true, mloc);
       if (m_ref == -__builtin_inff()) m_ref = mloc;  // first tile with a valid key
       overflow |= mloc > m_ref + kHeadroom;
-      const bool live = (m_ref > -__builtin_inff()) && !overflow;
+      const float neg_ref = -m_ref;
       float p[16];
       float psum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = fast_exp2(x[i] - m_ref);  // masked keys: exp2(-inf) = 0
-        p[i] = live ? p[i] : 0.f;
-        psum += p[i];
+      for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(sc[i], a.scale_log2, neg_ref));
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = 8 * (i >> 2) + 4 * half + (i & 3);
+          p[i] = ((mask_cur >> key) & 1u) ? p[i] : 0.f;
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) psum += p[i];
       l_run += psum;
 
       // ---- O += P . V ----
@@ -329,30 +347,29 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
         pa[st][3] = pack_bf16x2(p[8 * st + 6], p[8 * st + 7]);
       }
       {
-        // Transposed reads: 16-lane group g reads keys 16*st + 4*(g/2) (+8),
-        // dims 32*nb + 16*(g%2); lane i of the group points at key + i/4,
-        // dim + 4*(i%4).
-        // Row key, dim d lives in block u = d/16 at slot
-        // 32*h + ((key + 4h + 8*(u%2)) mod 32), h = (d%16)/8, byte 2*(d%8).
-        // Group g reads block 2*nb + g%2, so u%2 = g%2; its lane li reads
-        // key + li/4 with dims + 4*(li%4), i.e. h = (li%4)/2, byte 8*(li%2).
-        const int g = lane >> 4, li = lane & 15;
-        const int vh = (li & 3) >> 1;
-        auto vslot = [&](int key) -> int {
-          return 32 * vh + ((key + (li >> 2) + 4 * vh + 8 * (g & 1)) & 31);
-        };
-        // The four transposed reads of column block nb+1 are issued before
-        // the two MFMAs of block nb.
-        // slot offsets of the 4 key groups used by a column block (st, lo/hi)
-        const unsigned char* vb0 = tile + C::V_BASE + (g & 1) * 1024 + 8 * (li & 1);
-        const int s00 = vslot(4 * (g >> 1)) * 16, s01 = vslot(8 + 4 * (g >> 1)) * 16;
-        const int s10 = vslot(16 + 4 * (g >> 1)) * 16, s11 = vslot(24 + 4 * (g >> 1)) * 16;
+        // Transposed reads: for column block nb and key half st, 16-lane
+        // group G reads keys 16*st + 8*b + 4*(G/2) .. +3 (b = 0, 1), dims
+        // 32*nb + 16*(G%2) .. +15; its lane li points at key + li/4, dims
+        // + 4*(li%4). Key 8g + r (g = 2*st + b, r = 4*(G/2) + li/4) and
+        // chunk c = 4*(nb%2) + 2*(G%2) + (li%4)/2 of segment nb/2 sit at slot
+        // 8r + (c ^ f(r, g)), where
+        //   c ^ f = 4*((nb%2) ^ (li/8)) + 2*((G%2) ^ b) + (((li/2)%2) ^ (G/2)).
+        const int G = lane >> 4, li = lane & 15;
+        const int vr = 4 * (G >> 1) + (li >> 2);
+        const unsigned char* vbase =
+            tile + C::V_BASE + vr * 128 + 16 * (((li >> 1) & 1) ^ (G >> 1)) + 8 * (li & 1);
+        const unsigned char* va[2][2];  // [nb % 2][b]
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+            va[pp][b] = vbase + 1024 * b + 16 * (4 * (pp ^ (li >> 3)) + 2 * ((G & 1) ^ b));
         auto vread = [&](int nb, u32x4* vb) {
-          const unsigned char* p0 = vb0 + nb * 2048;
-          const u32x2 a0 = lds_read_tr16(p0 + s00);
-          const u32x2 a1 = lds_read_tr16(p0 + s01);
-          const u32x2 b0 = lds_read_tr16(p0 + s10);
-          const u32x2 b1 = lds_read_tr16(p0 + s11);
+          const int so = (nb >> 1) * 4096;
+          const u32x2 a0 = lds_read_tr16(va[nb & 1][0] + so);
+          const u32x2 a1 = lds_read_tr16(va[nb & 1][1] + so);
+          const u32x2 b0 = lds_read_tr16(va[nb & 1][0] + so + 2048);
+          const u32x2 b1 = lds_read_tr16(va[nb & 1][1] + so + 2048);
           vb[0] = u32x4{a0.x, a0.y, a1.x, a1.y};
           vb[1] = u32x4{b0.x, b0.y, b1.x, b1.y};
         };
@@ -363,19 +380,23 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
         u32x4 vcur[4], vnxt[4];
         vread(0, vcur);
         vread(1, vcur + 2);
-#pragma unroll
-        for (int nb = 0; nb < C::NB; nb += 2) {
-          if (nb + 2 < C::NB) {
+        static_for<C::NB / 2>([&](auto pc) {
+          constexpr int nb = 2 * decltype(pc)::value;
+          if constexpr (nb + 2 < C::NB) {
             vread(nb + 2, vnxt);
             vread(nb + 3, vnxt + 2);
           }
           o[nb] = mfma32x32x16(pa[0], vcur[0], o[nb]);
+          copies_at_slot(std::integral_constant<int, C::KS + 2 * nb>{});
           o[nb + 1] = mfma32x32x16(pa[0], vcur[2], o[nb + 1]);
+          copies_at_slot(std::integral_constant<int, C::KS + 2 * nb + 1>{});
           o[nb] = mfma32x32x16(pa[1], vcur[1], o[nb]);
+          copies_at_slot(std::integral_constant<int, C::KS + 2 * nb + 2>{});
           o[nb + 1] = mfma32x32x16(pa[1], vcur[3], o[nb + 1]);
+          copies_at_slot(std::integral_constant<int, C::KS + 2 * nb + 3>{});
 #pragma unroll
           for (int i = 0; i < 4; ++i) vcur[i] = vnxt[i];
-        }
+        });
       }
       mask_cur = mask_next;
     }
