@@ -260,7 +260,7 @@ def main():
                 dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, wl.w, rs, sl, row_begin=r0, n_rows=n,
                                     scores=scores)
                 dsa.dsa_topk(scores[:n], sl[r0:r0 + n], K, row_starts=rs[r0:r0 + n],
-                             n_cols=max_len, indices=indices[r0:r0 + n],
+                             n_cols=min(max_len, r0 + n), indices=indices[r0:r0 + n],
                              topk_length=topk_length[r0:r0 + n])
         if timed:
             e1.record(stream)

@@ -327,7 +327,8 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
         dsa_indexer_fwd(q_idx, k_idx, w, row_starts, seq_lens, row_begin=r0, n_rows=n,
                         scores=scores, stream=stream)
         dsa_topk(scores[:n], seq_lens[r0:r0 + n], k, row_starts=row_starts[r0:r0 + n],
-                 n_cols=width, indices=indices[r0:r0 + n], topk_length=topk_length[r0:r0 + n],
+                 n_cols=min(width, r0 + n), indices=indices[r0:r0 + n],
+                 topk_length=topk_length[r0:r0 + n],
                  stream=stream)
     return indices, topk_length
 

@@ -1,5 +1,5 @@
-// Per-row radix top-K with per-row length, ordered compaction and
-// local -> global conversion, for gfx950.
+// Per-row top-K with per-row length, ordered compaction and local -> global
+// conversion, for gfx950.
 //
 // Semantics: cuDNN Frontend DSA page, section 5 "Indexer Top-K" (radix top-K
 // with a per-row effective length, top_k <= 2048) and section 4 (the
@@ -7,17 +7,36 @@
 // column); NeMo cudnn_dsa page (global coordinates, ascending valid prefix,
 // -1 suffix).
 //
-// One workgroup owns one row and keeps all of it on chip: wave w holds a
-// contiguous column range, read with 16-byte loads so that every load
-// instruction covers 1 KiB of the row; rows up to 32K columns sit in VGPRs,
-// 64K-column rows keep half of each wave's range in LDS. Scores become
-// order-preserving uint32 keys (-0.0 folded onto +0.0, so they tie as equal
-// values). Three LDS-histogram passes over 11/11/10-bit digits find the K-th
-// largest key theta and how many keys equal to theta are taken. A final pass
-// walks the columns in ascending order, using wave ballots and mbcnt prefix
-// counts, and drops each selected column straight into its output slot:
-// position = (#greater before it) + min(#equal before it, #equal taken).
-// The score row is read from HBM exactly once.
+// Scores become order-preserving uint32 keys (-0.0 folded onto +0.0, so they
+// tie as equal values; key 0 marks columns past the row end). Output
+// positions come from one rule: a selected column goes to
+// (#greater before it) + min(#equal before it, #equal taken).
+//
+// Rows of up to 4096 columns (topk_radix_kernel): one workgroup keeps the
+// row in VGPRs, finds the K-th largest key theta with three LDS-histogram
+// passes over 11/11/10-bit digits, then walks the columns in ascending order
+// with wave ballots and mbcnt prefix counts.
+//
+// Longer rows (topk_stream_kernel) are streamed once and never held on chip,
+// so several rows share a CU and one row's loads overlap another's work:
+//  1. Sampled lower bound lo: 64 runs of 64 contiguous columns spread over
+//     the row (4096 samples); lo is the sample of rank e + 4 sqrt(e) + 2 from
+//     the top, e = K * 4096 / n being the expected rank of the K-th largest
+//     key, i.e. about 4 standard deviations of the sampling noise above it.
+//     Rows of at most kCap columns take every column as a candidate.
+//  2. One streaming pass compares every score with lo and appends the
+//     columns at or above it, chunk by chunk (256 columns per wave load), to
+//     an LDS candidate list; a direct-mapped table of chunks records where
+//     each chunk's candidates went, which restores column order later. If
+//     fewer than K or more than kCap columns pass, the row is redone with
+//     radix passes that re-stream it (correct for any input, slow).
+//  3. theta among the candidates: a histogram over 2048 buckets linear in
+//     the score value between lo and the largest candidate (dense score
+//     ranges spread over many bins instead of piling onto a few exponent
+//     digits), then an exact rank inside the bucket holding the K-th largest
+//     (one wave when it has at most 64 members, radix passes otherwise).
+//  4. One thread per chunk walks its candidates in column order and writes
+//     the selected ones to their output slots.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -65,27 +84,121 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return before + incl - v;
 }
 
-// CR / CL: 4-column chunks per lane held in VGPRs / in LDS. Wave w owns the
-// columns [w * 256 * (CR + CL), (w + 1) * 256 * (CR + CL)); chunk c of a wave
-// covers 256 consecutive columns, 4 per lane.
-template <int WAVES, int CR, int CL>
-__global__ __launch_bounds__(64 * WAVES) void topk_kernel(
+constexpr int kBins = 2048;  // histogram bins
+
+// Radix passes (11/11/10 bits) that find theta, the remaining-th largest key
+// among the keys offered by `offer(f)`, which calls f(key) for every key of
+// the calling thread that takes part. Returns theta; *need_eq receives how
+// many keys equal to theta are taken.
+template <int WAVES, typename Offer>
+__device__ __forceinline__ uint32_t radix_select(uint32_t remaining, uint32_t* hist,
+                                                 uint32_t* s_wave, uint32_t* s_sel,
+                                                 uint32_t* need_eq, Offer&& offer) {
+  constexpr int NT = 64 * WAVES;
+  constexpr int BPT = kBins / NT;
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t dmask = pass == 2 ? 0x3ffu : 0x7ffu;
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
+    __syncthreads();
+    offer([&](uint32_t key) {
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+    });
+    __syncthreads();
+    // Thread tid owns bins [hi_bin - BPT + 1, hi_bin], highest bins first.
+    const int hi_bin = kBins - 1 - tid * BPT;
+    uint32_t local = 0;
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) local += hist[hi_bin - b];
+    uint32_t total;
+    const uint32_t above = block_exclusive_scan<WAVES>(local, s_wave, &total);
+    if (above < remaining && remaining <= above + local) {
+      uint32_t acc = above;
+      for (int b = 0; b < BPT; ++b) {
+        const uint32_t h = hist[hi_bin - b];
+        if (acc + h >= remaining) {
+          s_sel[0] = (uint32_t)(hi_bin - b);
+          s_sel[1] = acc;
+          break;
+        }
+        acc += h;
+      }
+    }
+    __syncthreads();
+    remaining -= s_sel[1];
+    prefix |= s_sel[0] << shift;
+    pmask |= dmask << shift;
+    __syncthreads();
+  }
+  *need_eq = remaining;
+  return prefix;
+}
+
+// Bucket of a key on a scale linear in the score value: monotone in the key,
+// so the buckets split the keys into ordered ranges.
+struct LinearBuckets {
+  float lo, scale;
+  __device__ __forceinline__ int operator()(uint32_t key) const {
+    const float x = (key_to_float(key) - lo) * scale;
+    if (!(x > 0.0f)) return 0;  // also NaN (inf * 0 when lo = -inf)
+    return x >= (float)(kBins - 1) ? kBins - 1 : (int)x;
+  }
+};
+
+// Max over the workgroup (s_red: WAVES words).
+template <int WAVES>
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* s_red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor(v, d, 64));
+  if (WAVES > 1) {
+    if (lane == 0) s_red[wave] = v;
+    __syncthreads();
+    v = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) v = max(v, s_red[w]);
+    __syncthreads();
+  }
+  return v;
+}
+
+// Ordered write of the selected keys of one thread's run, given the counts
+// of keys above / equal to theta before the run (in column order).
+struct Placer {
+  uint32_t theta, need_eq, k;
+  int32_t* out_idx;
+  float* out_val;
+  __device__ __forceinline__ void operator()(uint32_t key, int32_t gcol, uint32_t& g,
+                                             uint32_t& q) const {
+    const bool is_gt = key > theta, is_eq = key == theta;
+    const uint32_t pos = g + min(q, need_eq);
+    if ((is_gt || (is_eq && q < need_eq)) && pos < k) {
+      out_idx[pos] = gcol;
+      if (out_val) out_val[pos] = key_to_float(key);
+    }
+    g += is_gt;
+    q += is_eq;
+  }
+};
+
+// ------------------------------------------------ rows of <= 4096 columns --
+// CH: 4-column chunks per lane, held in VGPRs. Wave w owns the columns
+// [w * 256 * CH, (w + 1) * 256 * CH); chunk c of a wave covers 256
+// consecutive columns, 4 per lane.
+template <int WAVES, int CH>
+__global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
     const float* __restrict__ scores, int64_t ld, int64_t n_cols,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ row_starts, int k,
     int32_t* __restrict__ indices, int64_t ld_idx, int32_t* __restrict__ topk_length,
     float* __restrict__ values) {
   constexpr int NT = 64 * WAVES;
-  constexpr int NCH = CR + CL;
-  constexpr int NBINS = 2048;
-  constexpr int BPT = NBINS / NT;  // histogram bins owned per thread in the scan
-  static_assert(NBINS % NT == 0, "bins must split evenly over threads");
-
-  __shared__ uint32_t hist[NBINS];
-  __shared__ int32_t s_idx[2048];
-  __shared__ float s_val[2048];
+  static_assert(kBins % NT == 0, "bins must split evenly over threads");
+  __shared__ uint32_t hist[kBins];
   __shared__ uint32_t s_wave[2][WAVES > 1 ? WAVES : 1];
   __shared__ uint32_t s_sel[2];
-  __shared__ u32x4 lkeys[CL > 0 ? WAVES * CL * 64 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -94,7 +207,6 @@ __global__ __launch_bounds__(64 * WAVES) void topk_kernel(
   const float* row = scores + r * ld;
   int32_t* out_idx = indices + r * ld_idx;
   float* out_val = values ? values + r * ld_idx : nullptr;
-
   int64_t n64 = seq_lens[r];
   n64 = n64 < 0 ? 0 : (n64 > n_cols ? n_cols : n64);
   const int n = (int)n64;
@@ -110,86 +222,44 @@ __global__ __launch_bounds__(64 * WAVES) void topk_kernel(
     return;
   }
 
-  // ---- load the row as order-preserving keys (0 = past the row end) ----
-  const int wbase = wave * 256 * NCH;
-  u32x4 kreg[CR > 0 ? CR : 1];
-  auto lds_slot = [&](int c) -> u32x4* { return &lkeys[(wave * CL + (c - CR)) * 64 + lane]; };
+  // All loads are issued before any is used. Every load is a full 16-byte
+  // chunk inside the row's ld columns (ld is a multiple of 4 and >= n):
+  // chunks past the row read a clamped address and columns >= n become key 0.
+  const int wbase = wave * 256 * CH;
+  float4 raw[CH];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
+  for (int c = 0; c < CH; ++c) {
     const int col = wbase + c * 256 + lane * 4;
-    u32x4 kv;
-    if (col + 3 < n) {
-      const float4 v = *reinterpret_cast<const float4*>(row + col);
-      kv = u32x4{float_to_key(v.x), float_to_key(v.y), float_to_key(v.z), float_to_key(v.w)};
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) kv[e] = (col + e < n) ? float_to_key(row[col + e]) : 0u;
-    }
-    if (c < CR) kreg[c] = kv; else *lds_slot(c) = kv;
+    const int64_t colc = col < ld - 4 ? (int64_t)col : ld - 4;
+    raw[c] = *reinterpret_cast<const float4*>(row + colc);
   }
-  auto chunk = [&](int c) -> u32x4 { return c < CR ? kreg[c] : *lds_slot(c); };
+  u32x4 kreg[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int col = wbase + c * 256 + lane * 4;
+    kreg[c] = u32x4{col + 0 < n ? float_to_key(raw[c].x) : 0u, col + 1 < n ? float_to_key(raw[c].y) : 0u,
+                    col + 2 < n ? float_to_key(raw[c].z) : 0u, col + 3 < n ? float_to_key(raw[c].w) : 0u};
+  }
 
-  // ---- radix select of the K-th largest key ----
-  if (tid == 0) {
-    s_sel[0] = 0u;
-    s_sel[1] = 0u;
-  }
-  uint32_t prefix = 0, pmask = 0;
-  uint32_t remaining = (uint32_t)k;  // keys still to take among prefix matches
+  uint32_t need_eq;
+  const uint32_t theta = radix_select<WAVES>((uint32_t)k, hist, s_wave[0], s_sel, &need_eq,
+                                             [&](auto&& f) {
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t dmask = pass == 2 ? 0x3ffu : 0x7ffu;
-    for (int i = tid; i < NBINS; i += NT) hist[i] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      const u32x4 kv = chunk(c);
+    for (int c = 0; c < CH; ++c)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if ((kv[e] & pmask) == prefix) atomicAdd(&hist[(kv[e] >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    // Thread tid owns bins [hi_bin - BPT + 1, hi_bin], highest bins first.
-    const int hi_bin = NBINS - 1 - tid * BPT;
-    uint32_t local = 0;
-#pragma unroll
-    for (int b = 0; b < BPT; ++b) local += hist[hi_bin - b];
-    uint32_t total;
-    uint32_t above = block_exclusive_scan<WAVES>(local, s_wave[0], &total);
-    if (above < remaining && remaining <= above + local) {
-      uint32_t acc = above;
-      for (int b = 0; b < BPT; ++b) {
-        const uint32_t h = hist[hi_bin - b];
-        if (acc + h >= remaining) {
-          s_sel[0] = (uint32_t)(hi_bin - b);
-          s_sel[1] = acc;
-          break;
-        }
-        acc += h;
-      }
-    }
-    __syncthreads();
-    const uint32_t bin = s_sel[0];
-    remaining -= s_sel[1];
-    prefix |= bin << shift;
-    pmask |= dmask << shift;
-    __syncthreads();
-  }
-  const uint32_t theta = prefix;
-  const uint32_t need_eq = remaining;  // >= 1 keys equal to theta to take
+        if (kreg[c][e] != 0u) f(kreg[c][e]);
+  });
 
-  // ---- per-wave counts of keys above / equal to theta ----
+  // per-wave counts of keys above / equal to theta, then the waves before
   uint32_t lgt = 0, leq = 0;
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const u32x4 kv = chunk(c);
+  for (int c = 0; c < CH; ++c)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      lgt += kv[e] > theta;
-      leq += kv[e] == theta;
+      lgt += kreg[c][e] > theta;
+      leq += kreg[c][e] == theta;
     }
-  }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
     lgt += __shfl_xor(lgt, d, 64);
@@ -207,11 +277,11 @@ __global__ __launch_bounds__(64 * WAVES) void topk_kernel(
       eq_run += s_wave[1][w];
     }
   }
-
-  // ---- ordered compaction into LDS ----
+  // ordered compaction straight into the output
+  const Placer place{theta, need_eq, (uint32_t)k, out_idx, out_val};
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const u32x4 kv = chunk(c);
+  for (int c = 0; c < CH; ++c) {
+    const u32x4 kv = kreg[c];
     uint32_t below_gt = 0, below_eq = 0, tot_gt = 0, tot_eq = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -224,35 +294,311 @@ __global__ __launch_bounds__(64 * WAVES) void topk_kernel(
     }
     uint32_t g = gt_run + below_gt, q = eq_run + below_eq;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t kk = kv[e];
-      const bool is_gt = kk > theta, is_eq = kk == theta;
-      const uint32_t pos = g + min(q, need_eq);
-      if ((is_gt || (is_eq && q < need_eq)) && pos < (uint32_t)k) {
-        const int col = wbase + c * 256 + lane * 4 + e;
-        s_idx[pos] = base + col;
-        s_val[pos] = key_to_float(kk);
-      }
-      g += is_gt;
-      q += is_eq;
-    }
+    for (int e = 0; e < 4; ++e) place(kv[e], base + wbase + c * 256 + lane * 4 + e, g, q);
     gt_run += tot_gt;
     eq_run += tot_eq;
-  }
-  __syncthreads();
-  for (int i = tid; i < k; i += NT) {
-    out_idx[i] = s_idx[i];
-    if (out_val) out_val[i] = s_val[i];
   }
   if (tid == 0 && topk_length) topk_length[r] = k;
 }
 
-template <int WAVES, int CR, int CL>
-hipError_t launch_topk_cfg(const float* scores, int64_t ld, int64_t n_rows, int64_t n_cols,
-                           const int32_t* sl, const int32_t* rs, int k, int32_t* idx,
-                           int64_t ld_idx, int32_t* tl, float* vals, hipStream_t st) {
+// ------------------------------------------------ rows of > 4096 columns --
+constexpr int kSWaves = 4;
+constexpr int kSThreads = 64 * kSWaves;
+constexpr int kMaxChunks = 65536 / 256;  // 256-column chunks of the longest row
+constexpr int kCap = 3584;               // candidate list capacity
+constexpr int kBatch = 8;                // chunk loads in flight per wave
+static_assert(kMaxChunks == kSThreads, "one thread per chunk in the output walk");
+
+__global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
+    const float* __restrict__ scores, int64_t ld, int64_t n_cols,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ row_starts, int k,
+    int32_t* __restrict__ indices, int64_t ld_idx, int32_t* __restrict__ topk_length,
+    float* __restrict__ values) {
+  constexpr int NT = kSThreads;
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t s_ckey[kCap];
+  __shared__ uint16_t s_ccol[kCap];        // column within the row (< 65536)
+  __shared__ uint16_t s_cbase[kMaxChunks];  // chunk -> first candidate slot
+  __shared__ uint16_t s_ccnt[kMaxChunks];   // chunk -> candidate count
+  __shared__ uint32_t s_wave[kSWaves];
+  __shared__ uint32_t s_red[kSWaves];
+  __shared__ uint32_t s_sel[2];
+  __shared__ uint32_t s_cnt;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t r = blockIdx.x;
+  const float* row = scores + r * ld;
+  int32_t* out_idx = indices + r * ld_idx;
+  float* out_val = values ? values + r * ld_idx : nullptr;
+  int64_t n64 = seq_lens[r];
+  n64 = n64 < 0 ? 0 : (n64 > n_cols ? n_cols : n64);
+  const int n = (int)n64;
+  const int32_t base = row_starts ? row_starts[r] : 0;
+
+  if (n <= k) {
+    for (int i = tid; i < k; i += NT) {
+      out_idx[i] = i < n ? base + i : -1;
+      if (out_val) out_val[i] = i < n ? row[i] : -__builtin_inff();
+    }
+    if (tid == 0 && topk_length) topk_length[r] = n;
+    return;
+  }
+  const int nchunks = (n + 255) / 256;
+  constexpr int BPT = kBins / NT;
+
+  // Finds the bucket holding the `want`-th largest of the histogrammed keys
+  // (want >= 1): s_sel[0] = bucket, s_sel[1] = count in the buckets above.
+  auto find_bucket = [&](uint32_t want) {
+    const int hi_bin = kBins - 1 - tid * BPT;
+    uint32_t local = 0;
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) local += hist[hi_bin - b];
+    uint32_t total;
+    const uint32_t above = block_exclusive_scan<kSWaves>(local, s_wave, &total);
+    if (above < want && want <= above + local) {
+      uint32_t acc = above;
+      for (int b = 0; b < BPT; ++b) {
+        const uint32_t h = hist[hi_bin - b];
+        if (acc + h >= want) {
+          s_sel[0] = (uint32_t)(hi_bin - b);
+          s_sel[1] = acc;
+          break;
+        }
+        acc += h;
+      }
+    }
+    __syncthreads();
+  };
+
+  // ---- 1. sampled lower bound (rows of more than kCap columns) ----
+  uint32_t lo_key = 1u;  // the smallest valid key: every column is a candidate
+  if (n > kCap) {        // uniform; n > kCap >= 64 keeps every run inside the row
+    constexpr int S = 4096;  // 64 runs x 64 columns; n > 4096 keeps runs apart
+    const float e = (float)k * (float)S / (float)n;
+    const int rank = (int)ceilf(e + 4.0f * sqrtf(e) + 2.0f);
+    uint32_t skey[16];
+    uint32_t smax = 0, snmax = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int q = (tid >> 4) + 16 * j;  // run 0..63
+      const int64_t start = ((int64_t)q * (n - 64) / 63) & ~(int64_t)3;
+      const float4 v = *reinterpret_cast<const float4*>(row + start + 4 * (tid & 15));
+      skey[4 * j + 0] = float_to_key(v.x);
+      skey[4 * j + 1] = float_to_key(v.y);
+      skey[4 * j + 2] = float_to_key(v.z);
+      skey[4 * j + 3] = float_to_key(v.w);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      smax = max(smax, skey[i]);
+      snmax = max(snmax, ~skey[i]);
+    }
+    smax = block_max<kSWaves>(smax, s_red);
+    const uint32_t smin = ~block_max<kSWaves>(snmax, s_red);
+    const float flo = key_to_float(smin), span = key_to_float(smax) - flo;
+    const LinearBuckets sb{flo, span > 0.0f ? (float)kBins / span : 0.0f};
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
+    if (tid == 0) s_red[0] = 0xffffffffu;
+    __syncthreads();
+    int sbk[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sbk[i] = sb(skey[i]);
+      atomicAdd(&hist[sbk[i]], 1u);
+    }
+    __syncthreads();
+    if (rank < S) {  // uniform
+      find_bucket((uint32_t)rank);
+      // lo = the smallest sample key in the bucket: >= `rank` samples are >= lo
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (sbk[i] == (int)s_sel[0]) atomicMin(&s_red[0], skey[i]);
+      __syncthreads();
+      lo_key = s_red[0];
+    } else {
+      lo_key = smin;
+    }
+    __syncthreads();
+  }
+
+  // ---- 2. one streaming pass: candidates (score >= lo) by chunk ----
+  // key >= lo_key <=> score >= lo_f for every non-NaN score
+  const float lo_f = lo_key == 1u ? -__builtin_inff() : key_to_float(lo_key);
+  if (tid == 0) s_cnt = 0u;
+  __syncthreads();
+  for (int c0 = wave; c0 < nchunks; c0 += kSWaves * kBatch) {
+    float4 v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int ch = c0 + kSWaves * i;
+      const int64_t col = ch < nchunks ? (int64_t)ch * 256 + lane * 4 : 0;
+      const int64_t colc = col < ld - 4 ? col : ld - 4;
+      v[i] = *reinterpret_cast<const float4*>(row + colc);
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int ch = c0 + kSWaves * i;  // uniform
+      if (ch < nchunks) {
+        const int col = ch * 256 + lane * 4;
+        const float x[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint64_t bal[4];
+        uint32_t below = 0, cnt = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bal[e] = ballot(col + e < n && x[e] >= lo_f);
+          below += popc_below(bal[e]);
+          cnt += __popcll(bal[e]);
+        }
+        uint32_t slot = 0;
+        if (cnt > 0u) {  // uniform
+          if (lane == 0) slot = atomicAdd(&s_cnt, cnt);
+          slot = __shfl(slot, 0, 64);
+          if (slot + cnt <= (uint32_t)kCap) {
+            uint32_t pos = slot + below;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if ((bal[e] >> lane) & 1u) {
+                s_ckey[pos] = float_to_key(x[e]);
+                s_ccol[pos] = (uint16_t)(col + e);
+                ++pos;
+              }
+          }
+        }
+        if (lane == 0) {
+          s_cbase[ch] = (uint16_t)(slot < (uint32_t)kCap ? slot : 0u);
+          s_ccnt[ch] = (uint16_t)cnt;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const uint32_t ccount = s_cnt;
+
+  uint32_t theta, need_eq;
+  const Placer place{0u, 0u, (uint32_t)k, out_idx, out_val};
+  if (ccount >= (uint32_t)k && ccount <= (uint32_t)kCap) {  // uniform
+    const int nc = (int)ccount;
+    // ---- 3. theta among the candidates ----
+    uint32_t cmax = 0;
+    for (int i = tid; i < nc; i += NT) cmax = max(cmax, s_ckey[i]);
+    cmax = block_max<kSWaves>(cmax, s_red);
+    const float span = key_to_float(cmax) - lo_f;
+    const LinearBuckets cb{lo_f, span > 0.0f ? (float)kBins / span : 0.0f};
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
+    __syncthreads();
+    for (int i = tid; i < nc; i += NT) atomicAdd(&hist[cb(s_ckey[i])], 1u);
+    __syncthreads();
+    find_bucket((uint32_t)k);
+    const int bstar = (int)s_sel[0];
+    const uint32_t rem = (uint32_t)k - s_sel[1];  // >= 1 keys to take from bucket b*
+    __syncthreads();
+    // Members of bucket b* into a small list (order does not matter here).
+    if (tid == 0) s_sel[1] = 0u;
+    __syncthreads();
+    for (int i = tid; i < nc; i += NT) {
+      const uint32_t key = s_ckey[i];
+      if (cb(key) == bstar) {
+        const uint32_t at = atomicAdd(&s_sel[1], 1u);
+        if (at < 64u) hist[at] = key;  // the histogram is no longer needed
+      }
+    }
+    __syncthreads();
+    const uint32_t m = s_sel[1];
+    if (m <= 64u) {  // uniform: rank the members against each other in one wave
+      if (wave == 0) {
+        const uint32_t x = lane < (int)m ? hist[lane] : 0u;
+        uint32_t gt = 0, eq = 0;
+        for (uint32_t j = 0; j < m; ++j) {
+          const uint32_t y = hist[j];
+          gt += y > x;
+          eq += y == x;
+        }
+        if (lane < (int)m && gt < rem && rem <= gt + eq) {
+          s_red[0] = x;
+          s_red[1] = rem - gt;
+        }
+      }
+      __syncthreads();
+      theta = s_red[0];
+      need_eq = s_red[1];
+      __syncthreads();
+    } else {
+      theta = radix_select<kSWaves>(rem, hist, s_wave, s_sel, &need_eq, [&](auto&& f) {
+        for (int i = tid; i < nc; i += NT) {
+          const uint32_t key = s_ckey[i];
+          if (cb(key) == bstar) f(key);
+        }
+      });
+    }
+
+    // ---- 4. output: thread t walks chunk t's candidates in column order ----
+    const int cnt = tid < nchunks ? (int)s_ccnt[tid] : 0;
+    const int cbase = tid < nchunks ? (int)s_cbase[tid] : 0;
+    uint32_t ngt = 0, neq = 0;
+    for (int i = 0; i < cnt; ++i) {
+      const uint32_t key = s_ckey[cbase + i];
+      ngt += key > theta;
+      neq += key == theta;
+    }
+    uint32_t total;
+    const uint32_t before = block_exclusive_scan<kSWaves>(ngt | (neq << 16), s_wave, &total);
+    uint32_t g = before & 0xffffu, q = before >> 16;
+    const Placer pl{theta, need_eq, (uint32_t)k, out_idx, out_val};
+    for (int i = 0; i < cnt; ++i) pl(s_ckey[cbase + i], base + (int32_t)s_ccol[cbase + i], g, q);
+  } else {
+    // ---- fallback: radix passes that re-stream the row ----
+    const int nq = (n + 3) / 4;  // 16-byte groups of the row
+    auto keys_of = [&](int gq, uint32_t* kk) {
+      const float4 v = *reinterpret_cast<const float4*>(row + 4 * (int64_t)gq);
+      const float x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kk[e] = 4 * gq + e < n ? float_to_key(x[e]) : 0u;
+    };
+    theta = radix_select<kSWaves>((uint32_t)k, hist, s_wave, s_sel, &need_eq, [&](auto&& f) {
+      for (int gq = tid; gq < nq; gq += NT) {
+        uint32_t kk[4];
+        keys_of(gq, kk);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (kk[e] != 0u) f(kk[e]);
+      }
+    });
+    // thread t owns groups [t * P, t * P + P), in column order
+    const int P = (nq + NT - 1) / NT;
+    const int g0 = min(tid * P, nq), g1 = min(g0 + P, nq);
+    uint32_t ngt = 0, neq = 0;
+    for (int gq = g0; gq < g1; ++gq) {
+      uint32_t kk[4];
+      keys_of(gq, kk);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ngt += kk[e] > theta;
+        neq += kk[e] == theta;
+      }
+    }
+    uint32_t total;
+    const uint32_t before = block_exclusive_scan<kSWaves>(ngt | (neq << 16), s_wave, &total);
+    uint32_t g = before & 0xffffu, q = before >> 16;
+    const Placer pl{theta, need_eq, (uint32_t)k, out_idx, out_val};
+    for (int gq = g0; gq < g1; ++gq) {
+      uint32_t kk[4];
+      keys_of(gq, kk);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pl(kk[e], base + 4 * gq + e, g, q);
+    }
+  }
+  (void)place;
+  if (tid == 0 && topk_length) topk_length[r] = k;
+}
+
+template <int WAVES, int CH>
+hipError_t launch_radix(const float* scores, int64_t ld, int64_t n_rows, int64_t n_cols,
+                        const int32_t* sl, const int32_t* rs, int k, int32_t* idx,
+                        int64_t ld_idx, int32_t* tl, float* vals, hipStream_t st) {
   dim3 grid((unsigned)n_rows), block(64 * WAVES);
-  hipLaunchKernelGGL((topk_kernel<WAVES, CR, CL>), grid, block, 0, st, scores, ld, n_cols, sl, rs,
+  hipLaunchKernelGGL((topk_radix_kernel<WAVES, CH>), grid, block, 0, st, scores, ld, n_cols, sl, rs,
                      k, idx, ld_idx, tl, vals);
   return hipGetLastError();
 }
@@ -263,16 +609,21 @@ hipError_t launch_topk(const float* scores, int64_t ld, int64_t n_rows, int64_t 
                        const int32_t* seq_lens, const int32_t* row_starts, int k, int32_t* indices,
                        int64_t ld_idx, int32_t* topk_length, float* values, hipStream_t st) {
   if (n_rows == 0) return hipSuccess;
-#define DSA_TOPK_CFG(W, CR, CL)                                                                \
-  return launch_topk_cfg<W, CR, CL>(scores, ld, n_rows, n_cols, seq_lens, row_starts, k, indices, \
-                                    ld_idx, topk_length, values, st)
-  if (n_cols <= 256) DSA_TOPK_CFG(1, 1, 0);
-  if (n_cols <= 1024) DSA_TOPK_CFG(1, 4, 0);
-  if (n_cols <= 4096) DSA_TOPK_CFG(1, 16, 0);
-  if (n_cols <= 16384) DSA_TOPK_CFG(4, 16, 0);
-  if (n_cols <= 32768) DSA_TOPK_CFG(8, 16, 0);
-  if (n_cols <= 65536) DSA_TOPK_CFG(16, 8, 8);
-#undef DSA_TOPK_CFG
+  if (n_cols <= 256)
+    return launch_radix<1, 1>(scores, ld, n_rows, n_cols, seq_lens, row_starts, k, indices, ld_idx,
+                              topk_length, values, st);
+  if (n_cols <= 1024)
+    return launch_radix<1, 4>(scores, ld, n_rows, n_cols, seq_lens, row_starts, k, indices, ld_idx,
+                              topk_length, values, st);
+  if (n_cols <= 4096)
+    return launch_radix<1, 16>(scores, ld, n_rows, n_cols, seq_lens, row_starts, k, indices,
+                               ld_idx, topk_length, values, st);
+  if (n_cols <= 65536) {
+    dim3 grid((unsigned)n_rows), block(kSThreads);
+    hipLaunchKernelGGL(topk_stream_kernel, grid, block, 0, st, scores, ld, n_cols, seq_lens,
+                       row_starts, k, indices, ld_idx, topk_length, values);
+    return hipGetLastError();
+  }
   return hipErrorInvalidValue;
 }
 

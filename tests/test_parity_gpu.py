@@ -165,6 +165,36 @@ def test_topk_special_rows():
     assert gi[3].tolist() == list(range(k))
 
 
+@pytest.mark.parametrize("n_cols", [65536, 20000])
+def test_topk_adversarial_sample_rows(n_cols):
+    """Rows built against the kernel's sample of long rows (64 runs of 64
+    columns, run q starting at (q * (n - 64) // 63) rounded down to a multiple
+    of 4): the sampled lower bound then either admits fewer than K keys or
+    more than the candidate list holds, and the radix passes that re-stream
+    the row must take over. The oracle is independent of all this."""
+    say("topk adversarial sample rows", n_cols)
+    k = 2048
+    starts = ((np.arange(64) * (n_cols - 64)) // 63) & ~3
+    samp = np.unique((starts[:, None] + np.arange(64)[None, :]).ravel())
+    rng = np.random.default_rng(n_cols)
+    rows = []
+    r = -1.0 - rng.random(n_cols)
+    r[samp] = 1.0 + rng.random(len(samp))           # only the samples are large
+    rows.append(r)
+    r = 1.0 + rng.random(n_cols)
+    r[samp] = -1.0 - rng.random(len(samp))          # the samples are the smallest
+    rows.append(r)
+    r = np.round(1.0 + rng.random(n_cols), 1)       # ... with heavy ties
+    r[samp] = -1.0
+    rows.append(r)
+    r = rng.standard_normal(n_cols)                 # ordinary row (candidate path)
+    rows.append(r)
+    x = torch.tensor(np.stack(rows), dtype=torch.float32)
+    lens = torch.full((len(rows),), n_cols, dtype=torch.int32)
+    starts = torch.arange(len(rows), dtype=torch.int32) * 1000
+    _topk_check(x.to(DEV), lens.to(DEV), k, row_starts=starts.to(DEV), n_cols=n_cols)
+
+
 # ----------------------------------------------------------------- attention
 
 def _attn_case(T_kv, T_q, H, Dqk, Dv, shared, kw, seed, tl_mode="none", sink=True,
