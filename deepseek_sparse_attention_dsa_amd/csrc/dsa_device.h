@@ -68,9 +68,10 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_ptr) {
 // 16 bytes land at LDS byte address lds_base + 16 * l, lds_base being
 // wave-uniform. Issued through inline asm so that the compiler does not
 // insert its own (blanket) waits for it: the caller waits with
-// wait_vmcnt0() before reading the data.
+// wait_vmcnt0() before reading the data. The s_nop is the wait state an SALU
+// write of M0 needs before an instruction that reads M0 as an LDS address.
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
                : "v"(gptr), "s"(lds_base)
                : "memory");
@@ -80,7 +81,7 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
 // applies to both addresses: global gptr + IMM -> LDS lds_base + IMM + 16*l.
 template <int IMM>
 __device__ __forceinline__ void dma16_imm(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
                :
                : "v"(gptr), "s"(lds_base), "i"(IMM)
                : "memory");
