@@ -72,6 +72,42 @@ def packed_metadata(cu_seqlens, T: int):
     return starts, seq_lens
 
 
+def ratio_causal_metadata(cu_seqlens_q, cu_seqlens_k, T_q: int, ratio: int = 1,
+                          q_causal_offsets=None):
+    """Per-query key-segment start and visible key count, ratio-causal mask.
+
+    DSA page section 3 ("Indexer Forward"): for THD segment b, local query row
+    q_local may score local key column j only when
+        j < clamp((q_causal_offsets[b] + q_local + 1) // ratio, 0, seqlen_k_b),
+    where q_causal_offsets[b] is the global, uncompressed token position of the
+    segment's first query (zero for every segment when omitted) -- not its
+    storage offset -- and the key columns of segment b are a compressed prefix
+    starting at compressed column 0. cu_seqlens_q locates where segment b's
+    queries are stored, cu_seqlens_k where its keys are stored; seqlen_k_b is
+    cu_seqlens_k[b+1] - cu_seqlens_k[b]. `//` is floor division.
+
+    Returns (row_starts, seq_lens) as int64 arrays of length T_q: row_starts[t]
+    = cu_seqlens_k[b] (key row of local column 0), seq_lens[t] = the count
+    above. With ratio 1, no offsets and cu_seqlens_k == cu_seqlens_q this is
+    packed_metadata.
+    """
+    cq = np.asarray(cu_seqlens_q, dtype=np.int64)
+    ck = np.asarray(cu_seqlens_k, dtype=np.int64)
+    n_seq = len(cq) - 1
+    off = (np.zeros(n_seq, dtype=np.int64) if q_causal_offsets is None
+           else np.asarray(q_causal_offsets, dtype=np.int64))
+    starts = np.zeros(T_q, dtype=np.int64)
+    seq_lens = np.zeros(T_q, dtype=np.int64)
+    for b in range(n_seq):
+        seqlen_k = int(ck[b + 1] - ck[b])
+        for t in range(int(cq[b]), int(cq[b + 1])):
+            q_local = t - int(cq[b])
+            visible = (int(off[b]) + q_local + 1) // ratio
+            starts[t] = ck[b]
+            seq_lens[t] = min(max(visible, 0), seqlen_k)
+    return starts, seq_lens
+
+
 # ---------------------------------------------------------------------------
 # Step a1: lightning-indexer scores
 # ---------------------------------------------------------------------------
@@ -81,12 +117,13 @@ def indexer_scores(q_idx, k_idx, w, row_starts, seq_lens, rows, width=None):
 
     DSA page section 3: S[q, k] = sum_h ReLU(Q_h . K^T) * W_h with a
     ratio-causal mask; with ratio 1 and no causal offsets the valid columns of
-    local row q are k < q + 1 within its segment. The indexer K has one head
+    local row q are k < q + 1 within its segment (packed_metadata), in general
+    the counts of ratio_causal_metadata. The indexer K has one head
     (H_kv = 1), so every head h uses the same key row. Column j of row t is key
     start(t) + j (cudnn_dsa page, _topk_wrapper_chunked: scores [T, S_max] with
     causal lengths [T]); columns j >= seq_len(t) are -inf.
 
-    q_idx [T, H, D], k_idx [T, D], w [T, H] are float64. Returns float64
+    q_idx [T, H, D], k_idx [T_kv, D], w [T, H] are float64. Returns float64
     [len(rows), width].
     """
     rows = np.asarray(rows, dtype=np.int64)

@@ -157,6 +157,140 @@ def test_indexer_mask_invariant():
     assert np.array_equal(got[cu[1]:], got2[cu[1]:])
 
 
+# ------------------------------------------------------- ratio-causal mask --
+
+def _visible_columns(g, seqlen_k, ratio):
+    """Compressed key columns a query at global token position g may see.
+
+    Column c stands for the tokens c*ratio .. c*ratio + ratio - 1 (the keys
+    are a compressed prefix from column 0); it is visible once every one of
+    those tokens is at or before g. Enumerated token by token.
+    """
+    return [c for c in range(seqlen_k)
+            if all(tok <= g for tok in range(c * ratio, (c + 1) * ratio))]
+
+
+def _random_segments(rng, n_seq):
+    q_lens = rng.integers(0, 14, size=n_seq)
+    k_lens = rng.integers(0, 10, size=n_seq)
+    cq = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int64)
+    ck = np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int64)
+    return cq, ck
+
+
+def test_ratio_causal_metadata_matches_token_enumeration():
+    rng = np.random.default_rng(40)
+    for trial in range(60):
+        n_seq = int(rng.integers(1, 5))
+        cq, ck = _random_segments(rng, n_seq)
+        ratio = int(rng.integers(1, 6))
+        off = rng.integers(-9, 26, size=n_seq) if trial % 3 else None
+        T = int(cq[-1])
+        st, sl = O.ratio_causal_metadata(cq, ck, T, ratio, off)
+        for b in range(n_seq):
+            for t in range(int(cq[b]), int(cq[b + 1])):
+                g = (0 if off is None else int(off[b])) + t - int(cq[b])
+                vis = _visible_columns(g, int(ck[b + 1] - ck[b]), ratio)
+                assert vis == list(range(len(vis)))  # a prefix of the columns
+                assert sl[t] == len(vis), (trial, b, t)
+                assert st[t] == ck[b]
+
+
+def test_ratio_causal_metadata_reduces_to_packed_metadata():
+    # ratio 1, no offsets, keys stored like queries: the plain causal mask
+    cu = np.array([0, 4, 4, 13, 20])
+    st, sl = O.ratio_causal_metadata(cu, cu, 20)
+    st0, sl0 = O.packed_metadata(cu, 20)
+    assert np.array_equal(st, st0) and np.array_equal(sl, sl0)
+
+
+def test_ratio_causal_clamps():
+    # offsets before the timeline start see nothing until (g + 1) // ratio > 0;
+    # rows past the compressed prefix see the whole prefix
+    st, sl = O.ratio_causal_metadata([0, 6, 12], [0, 3, 5], 12, ratio=2,
+                                     q_causal_offsets=[-4, 40])
+    assert sl.tolist() == [0, 0, 0, 0, 0, 1] + [2] * 6
+    assert st.tolist() == [0] * 6 + [3] * 6
+
+
+@pytest.mark.parametrize("ratio", [1, 4])
+def test_query_offsets_split_equals_whole_sequence(ratio):
+    # One sequence of L tokens scored whole, and again with its queries split
+    # into three stored segments whose offsets are their global positions: each
+    # split row must get the same mask and the same scores as in the whole run.
+    rng = np.random.default_rng(41)
+    L, H, D = 23, 3, 5
+    Lk = L // ratio + 1
+    q = rng.standard_normal((L, H, D))
+    k = rng.standard_normal((Lk, D))
+    w = rng.standard_normal((L, H))
+    st, sl = O.ratio_causal_metadata([0, L], [0, Lk], L, ratio)
+    whole = O.indexer_scores(q, k, w, st, sl, np.arange(L), width=Lk)
+    cuts = [0, 7, 15, L]
+    k_rep = np.concatenate([k, k, k])                  # each segment stores the prefix
+    ck = [0, Lk, 2 * Lk, 3 * Lk]
+    st2, sl2 = O.ratio_causal_metadata(cuts, ck, L, ratio, q_causal_offsets=cuts[:3])
+    split = O.indexer_scores(q, k_rep, w, st2, sl2, np.arange(L), width=Lk)
+    assert np.array_equal(sl2, sl)
+    assert np.array_equal(np.isinf(split), np.isinf(whole))
+    fin = np.isfinite(whole)
+    np.testing.assert_allclose(split[fin], whole[fin], rtol=0, atol=0)
+
+
+def test_indexer_ratio_causal_bruteforce():
+    rng = np.random.default_rng(42)
+    cq = np.array([0, 9, 9, 20])
+    ck = np.array([0, 4, 6, 9])
+    off = [3, 0, 14]
+    ratio = 3
+    T, H, D = 20, 3, 4
+    q = rng.standard_normal((T, H, D))
+    k = rng.standard_normal((9, D))
+    w = rng.standard_normal((T, H))
+    st, sl = O.ratio_causal_metadata(cq, ck, T, ratio, off)
+    got = O.indexer_scores(q, k, w, st, sl, np.arange(T), width=6)
+    exp = np.full((T, 6), -np.inf)
+    for b in range(3):
+        for t in range(cq[b], cq[b + 1]):
+            for c in _visible_columns(off[b] + t - cq[b], int(ck[b + 1] - ck[b]), ratio):
+                tot = 0.0
+                for h in range(H):
+                    dot = sum(q[t, h, e] * k[ck[b] + c, e] for e in range(D))
+                    tot += w[t, h] * max(dot, 0.0)
+                exp[t, c] = tot
+    assert np.array_equal(np.isinf(got), np.isinf(exp))
+    fin = np.isfinite(exp)
+    np.testing.assert_allclose(got[fin], exp[fin], rtol=1e-12, atol=1e-12)
+
+
+def _ratio_mutant(cq, ck, T, ratio, off, mistake):
+    """A deliberately wrong copy of the ratio-causal count."""
+    sl = np.zeros(T, dtype=np.int64)
+    for b in range(len(cq) - 1):
+        for t in range(cq[b], cq[b + 1]):
+            ql = t - cq[b]
+            o = cq[b] if mistake == "storage_offset" else off[b]
+            if mistake == "no_plus_one":
+                v = (o + ql) // ratio
+            elif mistake == "ceil":
+                v = -((-(o + ql + 1)) // ratio)
+            else:
+                v = (o + ql + 1) // ratio
+            hi = 10 ** 9 if mistake == "no_upper_clamp" else ck[b + 1] - ck[b]
+            sl[t] = min(max(v, 0), hi)
+    return sl
+
+
+def test_planted_ratio_causal_mistakes_fail_their_pins():
+    cq, ck, off, ratio = [0, 10, 22], [0, 2, 4], [5, 1], 4
+    _, sl = O.ratio_causal_metadata(cq, ck, 22, ratio, off)
+    enum = [len(_visible_columns(off[b] + t - cq[b], ck[b + 1] - ck[b], ratio))
+            for b in range(2) for t in range(cq[b], cq[b + 1])]
+    assert sl.tolist() == enum
+    for mistake in ("no_plus_one", "ceil", "storage_offset", "no_upper_clamp"):
+        assert _ratio_mutant(cq, ck, 22, ratio, off, mistake).tolist() != enum, mistake
+
+
 # ------------------------------------------------------------------- top-K --
 
 def test_topk_golden_ties_and_signed_zero():
