@@ -23,7 +23,8 @@ import torch
 __all__ = [
     "DSA_BF16", "DSA_F32", "DSA_MAX_TOPK", "DSA_TOPK_MAX_COLS", "DSA_MAX_HEADS",
     "load_library", "library_path", "dsa_abi_version", "dsa_last_error",
-    "dsa_packed_metadata", "dsa_indexer_fwd", "dsa_topk", "dsa_sparse_attn_fwd",
+    "dsa_packed_metadata", "dsa_ratio_causal_metadata", "dsa_indexer_fwd", "dsa_topk",
+    "dsa_sparse_attn_fwd",
     "indexer_topk", "chunk_rows",
 ]
 
@@ -45,8 +46,9 @@ _SIGNATURES = {
     "dsa_last_error": ([], ctypes.c_char_p),
     "dsa_abi_version": ([], ctypes.c_int),
     "dsa_packed_metadata": ([_P, _I32, _I64, _P, _P, _P], ctypes.c_int),
-    "dsa_indexer_fwd": ([_P, _P, _P, _I32, _P, _P, _I64, _I32, _I32, _I64, _I64, _P, _I64, _P],
-                        ctypes.c_int),
+    "dsa_ratio_causal_metadata": ([_P, _P, _P, _I32, _I64, _I32, _P, _P, _P], ctypes.c_int),
+    "dsa_indexer_fwd": ([_P, _P, _P, _I32, _P, _P, _I64, _I64, _I32, _I32, _I64, _I64, _P, _I64,
+                         _P], ctypes.c_int),
     "dsa_topk": ([_P, _I64, _I64, _I64, _P, _P, _I32, _P, _I64, _P, _P, _P], ctypes.c_int),
     "dsa_sparse_attn_fwd": ([_P, _I64, _I32, _I32, _P, _I64, _I64, _P, _I64, _I32, _P, _I64,
                              _I32, _P, _P, _F32, _P, _P, _P, _P], ctypes.c_int),
@@ -149,6 +151,33 @@ def dsa_packed_metadata(cu_seqlens: torch.Tensor, T: int, row_starts=None, seq_l
     return row_starts, seq_lens
 
 
+def dsa_ratio_causal_metadata(cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, T_q: int,
+                              ratio: int = 1, q_causal_offsets: Optional[torch.Tensor] = None,
+                              row_starts=None, seq_lens=None, stream=None):
+    """Per-query key-segment start and visible key count of the ratio-causal mask."""
+    cu_q = _need(cu_seqlens_q, "cu_seqlens_q", torch.int32)
+    dev = cu_q.device
+    cu_k = _need(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev)
+    n_seq = cu_q.numel() - 1
+    if cu_k.numel() != n_seq + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need the same number of segments")
+    if q_causal_offsets is not None:
+        q_causal_offsets = _need(q_causal_offsets, "q_causal_offsets", torch.int32, dev)
+        if q_causal_offsets.numel() != n_seq:
+            raise ValueError("q_causal_offsets needs one entry per segment")
+    row_starts = (torch.empty(T_q, dtype=torch.int32, device=dev) if row_starts is None
+                  else _out(row_starts, "row_starts", torch.int32, dev))
+    seq_lens = (torch.empty(T_q, dtype=torch.int32, device=dev) if seq_lens is None
+                else _out(seq_lens, "seq_lens", torch.int32, dev))
+    if row_starts.numel() < T_q or seq_lens.numel() < T_q:
+        raise ValueError("row_starts and seq_lens need T_q entries")
+    lib = load_library()
+    _check(lib.dsa_ratio_causal_metadata(_ptr(cu_q), _ptr(cu_k), _ptr(q_causal_offsets), n_seq,
+                                         T_q, int(ratio), _ptr(row_starts), _ptr(seq_lens),
+                                         _stream(stream)))
+    return row_starts, seq_lens
+
+
 def dsa_indexer_fwd(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
                     row_starts: torch.Tensor, seq_lens: torch.Tensor, row_begin: int = 0,
                     n_rows: Optional[int] = None, scores: Optional[torch.Tensor] = None,
@@ -156,7 +185,8 @@ def dsa_indexer_fwd(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
     """Indexer scores [n_rows, ld] fp32 for rows [row_begin, row_begin + n_rows).
 
     `width` (>= the longest causal length of the rows) sizes a new score
-    buffer; its row stride is rounded up to a multiple of 4.
+    buffer; its row stride is rounded up to a multiple of 4. k_idx [T_kv, D]
+    may have another row count than q_idx (compressed keys).
     """
     if not isinstance(w, torch.Tensor) or w.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError(f"w must be a bfloat16 or float32 tensor (got {getattr(w, 'dtype', w)})")
@@ -167,16 +197,17 @@ def dsa_indexer_fwd(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
     row_starts = _need(row_starts, "row_starts", torch.int32, dev)
     seq_lens = _need(seq_lens, "seq_lens", torch.int32, dev)
     if q_idx.dim() != 3 or k_idx.dim() != 2 or w.dim() != 2:
-        raise ValueError("expected q_idx [T,H,D], k_idx [T,D], w [T,H]")
+        raise ValueError("expected q_idx [T,H,D], k_idx [T_kv,D], w [T,H]")
     T, H, D = q_idx.shape
-    if k_idx.shape != (T, D) or w.shape != (T, H):
+    T_kv = k_idx.shape[0]
+    if k_idx.shape[1] != D or w.shape != (T, H):
         raise ValueError(f"shape mismatch: q_idx {tuple(q_idx.shape)}, k_idx "
                          f"{tuple(k_idx.shape)}, w {tuple(w.shape)}")
     if n_rows is None:
         n_rows = T - row_begin
     if scores is None:
         if width is None:
-            width = T
+            width = T_kv
         ld = max(4, (int(width) + 3) // 4 * 4)
         scores = torch.empty((n_rows, ld), dtype=torch.float32, device=dev)
     else:
@@ -186,7 +217,7 @@ def dsa_indexer_fwd(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
     lib = load_library()
     _check(lib.dsa_indexer_fwd(_ptr(q_idx), _ptr(k_idx), _ptr(w),
                                DSA_BF16 if w.dtype == torch.bfloat16 else DSA_F32,
-                               _ptr(row_starts), _ptr(seq_lens), T, H, D, row_begin, n_rows,
+                               _ptr(row_starts), _ptr(seq_lens), T, T_kv, H, D, row_begin, n_rows,
                                _ptr(scores), scores.stride(0), _stream(stream)))
     return scores
 
@@ -306,18 +337,31 @@ def chunk_rows(T: int, width: int, cap_bytes: int = SCORE_CHUNK_BYTES) -> int:
 
 def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
                  cu_seqlens: torch.Tensor, k: int, max_seqlen: Optional[int] = None,
-                 rows_per_chunk: Optional[int] = None, stream=None):
+                 rows_per_chunk: Optional[int] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
+                 ratio: int = 1, q_causal_offsets: Optional[torch.Tensor] = None, stream=None):
     """Metadata + indexer scores + top-K over all rows, in score chunks.
 
     Returns (indices int32 [T, k] global ascending with -1 suffix,
-    topk_length int32 [T]). max_seqlen (the longest document) sizes each
-    chunk's score buffer; it defaults to T.
+    topk_length int32 [T]). With only cu_seqlens the mask is the causal mask
+    of packed documents and max_seqlen (the longest document, default T)
+    sizes each chunk's score buffer. Passing cu_seqlens_k, a ratio other than
+    1 or q_causal_offsets selects the ratio-causal mask (cu_seqlens then
+    locates the query segments, cu_seqlens_k the key segments, default
+    cu_seqlens); max_seqlen is then the longest key segment (default T_kv).
     """
     T = q_idx.shape[0]
+    T_kv = k_idx.shape[0]
     dev = q_idx.device
-    width = T if max_seqlen is None else int(max_seqlen)
+    ratio_causal = cu_seqlens_k is not None or int(ratio) != 1 or q_causal_offsets is not None
+    if ratio_causal:
+        width = T_kv if max_seqlen is None else int(max_seqlen)
+        row_starts, seq_lens = dsa_ratio_causal_metadata(
+            cu_seqlens, cu_seqlens if cu_seqlens_k is None else cu_seqlens_k, T, ratio,
+            q_causal_offsets, stream=stream)
+    else:
+        width = T if max_seqlen is None else int(max_seqlen)
+        row_starts, seq_lens = dsa_packed_metadata(cu_seqlens, T, stream=stream)
     rows = chunk_rows(T, width) if rows_per_chunk is None else int(rows_per_chunk)
-    row_starts, seq_lens = dsa_packed_metadata(cu_seqlens, T, stream=stream)
     indices = torch.empty((T, k), dtype=torch.int32, device=dev)
     topk_length = torch.empty((T,), dtype=torch.int32, device=dev)
     ld = max(4, (width + 3) // 4 * 4)
@@ -326,8 +370,10 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
         n = min(rows, T - r0)
         dsa_indexer_fwd(q_idx, k_idx, w, row_starts, seq_lens, row_begin=r0, n_rows=n,
                         scores=scores, stream=stream)
+        # plain causal rows never see more than r0 + n keys
+        n_cols = width if ratio_causal else min(width, r0 + n)
         dsa_topk(scores[:n], seq_lens[r0:r0 + n], k, row_starts=row_starts[r0:r0 + n],
-                 n_cols=min(width, r0 + n), indices=indices[r0:r0 + n],
+                 n_cols=n_cols, indices=indices[r0:r0 + n],
                  topk_length=topk_length[r0:r0 + n],
                  stream=stream)
     return indices, topk_length

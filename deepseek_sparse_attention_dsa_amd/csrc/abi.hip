@@ -77,10 +77,28 @@ int dsa_packed_metadata(const int32_t* cu_seqlens, int32_t n_seq, int64_t T, int
                                                   (hipStream_t)stream));
 }
 
+int dsa_ratio_causal_metadata(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              const int32_t* q_causal_offsets, int32_t n_seq, int64_t T_q,
+                              int32_t ratio, int32_t* row_starts, int32_t* seq_lens,
+                              void* stream) {
+  const char* fn = "dsa_ratio_causal_metadata";
+  REQUIRE(n_seq >= 1, DSA_ERR_VALUE, "%s: n_seq must be >= 1 (got %d)", fn, n_seq);
+  REQUIRE(T_q >= 0 && T_q <= INT32_MAX, DSA_ERR_VALUE, "%s: T_q must be in [0, 2^31-1] (got %lld)",
+          fn, (long long)T_q);
+  REQUIRE(ratio >= 1, DSA_ERR_VALUE, "%s: ratio must be >= 1 (got %d)", fn, ratio);
+  if (T_q == 0) return DSA_OK;
+  REQUIRE(cu_seqlens_q && cu_seqlens_k && row_starts && seq_lens, DSA_ERR_VALUE,
+          "%s: NULL pointer argument", fn);
+  if (int rc = check_device(fn)) return rc;
+  return launched(fn, dsa::launch_ratio_metadata(cu_seqlens_q, cu_seqlens_k, q_causal_offsets,
+                                                 n_seq, T_q, ratio, row_starts, seq_lens,
+                                                 (hipStream_t)stream));
+}
+
 int dsa_indexer_fwd(const void* q_idx, const void* k_idx, const void* w, int32_t w_dtype,
-                    const int32_t* row_starts, const int32_t* seq_lens, int64_t T, int32_t H_idx,
-                    int32_t D_idx, int64_t row_begin, int64_t n_rows, float* scores,
-                    int64_t ld_scores, void* stream) {
+                    const int32_t* row_starts, const int32_t* seq_lens, int64_t T, int64_t T_kv,
+                    int32_t H_idx, int32_t D_idx, int64_t row_begin, int64_t n_rows,
+                    float* scores, int64_t ld_scores, void* stream) {
   const char* fn = "dsa_indexer_fwd";
   REQUIRE(w_dtype == DSA_BF16 || w_dtype == DSA_F32, DSA_ERR_TYPE,
           "%s: w_dtype must be DSA_BF16 or DSA_F32 (got %d)", fn, w_dtype);
@@ -89,12 +107,13 @@ int dsa_indexer_fwd(const void* q_idx, const void* k_idx, const void* w, int32_t
   REQUIRE(D_idx == 64 || D_idx == 128, DSA_ERR_VALUE, "%s: D_idx must be 64 or 128 (got %d)", fn,
           D_idx);
   REQUIRE(T >= 0 && T <= INT32_MAX, DSA_ERR_VALUE, "%s: T must be in [0, 2^31-1]", fn);
+  REQUIRE(T_kv >= 0 && T_kv <= INT32_MAX, DSA_ERR_VALUE, "%s: T_kv must be in [0, 2^31-1]", fn);
   REQUIRE(row_begin >= 0 && n_rows >= 0 && row_begin + n_rows <= T, DSA_ERR_VALUE,
           "%s: rows [%lld, %lld) outside [0, T=%lld)", fn, (long long)row_begin,
           (long long)(row_begin + n_rows), (long long)T);
   REQUIRE(ld_scores >= 4 && ld_scores % 4 == 0, DSA_ERR_VALUE,
           "%s: ld_scores must be a positive multiple of 4 (got %lld)", fn, (long long)ld_scores);
-  if (n_rows == 0) return DSA_OK;
+  if (n_rows == 0 || T_kv == 0) return DSA_OK;
   REQUIRE(q_idx && k_idx && w && row_starts && seq_lens && scores, DSA_ERR_VALUE,
           "%s: NULL pointer argument", fn);
   REQUIRE(aligned(q_idx, 16) && aligned(k_idx, 16) && aligned(scores, 16), DSA_ERR_VALUE,
@@ -102,8 +121,8 @@ int dsa_indexer_fwd(const void* q_idx, const void* k_idx, const void* w, int32_t
   REQUIRE(aligned(w, w_dtype == DSA_F32 ? 4 : 2), DSA_ERR_VALUE, "%s: w misaligned", fn);
   REQUIRE(n_rows <= (int64_t)8 * INT32_MAX, DSA_ERR_VALUE, "%s: too many rows", fn);
   if (int rc = check_device(fn)) return rc;
-  return launched(fn, dsa::launch_indexer(q_idx, k_idx, w, w_dtype, row_starts, seq_lens, T, H_idx,
-                                          D_idx, row_begin, n_rows, scores, ld_scores,
+  return launched(fn, dsa::launch_indexer(q_idx, k_idx, w, w_dtype, row_starts, seq_lens, T_kv,
+                                          H_idx, D_idx, row_begin, n_rows, scores, ld_scores,
                                           (hipStream_t)stream));
 }
 

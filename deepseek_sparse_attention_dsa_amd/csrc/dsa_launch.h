@@ -10,8 +10,13 @@ namespace dsa {
 hipError_t launch_packed_metadata(const int32_t* cu, int32_t n_seq, int64_t T, int32_t* row_starts,
                                   int32_t* seq_lens, hipStream_t st);
 
+hipError_t launch_ratio_metadata(const int32_t* cu_q, const int32_t* cu_k, const int32_t* offsets,
+                                 int32_t n_seq, int64_t T_q, int32_t ratio, int32_t* row_starts,
+                                 int32_t* seq_lens, hipStream_t st);
+
+// T_kv: rows of k (key loads are clamped into [0, T_kv)).
 hipError_t launch_indexer(const void* q, const void* k, const void* w, int w_dtype,
-                          const int32_t* row_starts, const int32_t* seq_lens, int64_t T, int H,
+                          const int32_t* row_starts, const int32_t* seq_lens, int64_t T_kv, int H,
                           int D, int64_t row_begin, int64_t n_rows, float* scores, int64_t ld,
                           hipStream_t st);
 

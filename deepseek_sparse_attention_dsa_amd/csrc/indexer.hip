@@ -1,8 +1,11 @@
 // Packed-THD metadata and lightning-indexer score kernels for gfx950.
 //
 // Indexer scores follow the cuDNN Frontend DSA page, section 3 "Indexer
-// Forward": S[t, j] = sum_h W[t,h] * ReLU(Q[t,h,:] . K[start(t)+j, :]) with a
-// causal mask (ratio 1, no offsets), materialised as fp32 with local columns.
+// Forward": S[t, j] = sum_h W[t,h] * ReLU(Q[t,h,:] . K[start(t)+j, :]) for
+// j < len(t), materialised as fp32 with local columns. start(t) and len(t)
+// come from one of the two metadata kernels: the plain causal mask of packed
+// documents, or the section's ratio-causal mask with per-segment query
+// causal offsets.
 //
 // Mapping: one workgroup = 8 waves = 8 consecutive query rows, one per wave
 // (two waves per SIMD, so one wave's epilogue overlaps the other's MFMAs).
@@ -37,6 +40,33 @@ __global__ void packed_metadata_kernel(const int32_t* __restrict__ cu, int32_t n
   seq_lens[t] = (int32_t)(t - s + 1);
 }
 
+// Ratio-causal mask (DSA page, section 3): query row t of segment b sees the
+// first clamp(floor((off[b] + t - cu_q[b] + 1) / ratio), 0, |K segment b|)
+// compressed keys of its segment, which start at key row cu_k[b].
+__global__ void ratio_metadata_kernel(const int32_t* __restrict__ cu_q,
+                                      const int32_t* __restrict__ cu_k,
+                                      const int32_t* __restrict__ offsets, int32_t n_seq,
+                                      int64_t T_q, int32_t ratio,
+                                      int32_t* __restrict__ row_starts,
+                                      int32_t* __restrict__ seq_lens) {
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T_q) return;
+  // largest segment b in [0, n_seq) with cu_q[b] <= t (skips empty segments)
+  int lo = 0, hi = n_seq - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int64_t kb = cu_k[lo];
+  const int64_t klen = (int64_t)cu_k[lo + 1] - kb;
+  // global position of the query, plus one; non-positive sees nothing
+  const int64_t g1 = (offsets ? (int64_t)offsets[lo] : 0) + (t - cu_q[lo]) + 1;
+  int64_t n = g1 > 0 ? g1 / ratio : 0;
+  n = n < klen ? n : klen;
+  row_starts[t] = (int32_t)kb;
+  seq_lens[t] = (int32_t)(n > 0 ? n : 0);
+}
+
 namespace {
 
 constexpr int kIdxWaves = 8;                        // = query rows per workgroup
@@ -63,7 +93,7 @@ __device__ __forceinline__ float load_w<float>(const float* w, int64_t i) {
 template <int D, int MB, typename WT>
 __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const WT* __restrict__ w,
-    const int32_t* __restrict__ row_starts, const int32_t* __restrict__ seq_lens, int64_t T,
+    const int32_t* __restrict__ row_starts, const int32_t* __restrict__ seq_lens, int64_t T_kv,
     int H, int64_t row_begin, int64_t n_rows, float* __restrict__ scores, int64_t ld) {
   constexpr int KS = D / 16;                      // MFMA k-steps over the head dim
   constexpr int ROW_B = 2 * D + 16;               // LDS row stride in bytes (16 B pad)
@@ -141,8 +171,8 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
       const int c = threadIdx.x + NT * i;
       if (c < CHUNKS) {
         const int32_t key = k0 + c / (D / 8);
-        const bool ok = key < ke && key >= 0 && key < T;
-        const int32_t kc = ok ? key : (int32_t)(T - 1);
+        const bool ok = key < ke && key >= 0 && key < T_kv;
+        const int32_t kc = ok ? key : (int32_t)(T_kv - 1);
         stage[i] = load16(k + (int64_t)kc * D + (c % (D / 8)) * 8);
         stage_ok |= ok ? (1u << i) : 0u;
       }
@@ -250,18 +280,18 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
 
 template <int D, int MB>
 hipError_t launch_indexer_w(const void* q, const void* k, const void* w, int w_dtype,
-                            const int32_t* rs, const int32_t* sl, int64_t T, int H,
+                            const int32_t* rs, const int32_t* sl, int64_t T_kv, int H,
                             int64_t row_begin, int64_t n_rows, float* scores, int64_t ld,
                             hipStream_t st) {
   const int64_t nblk = (n_rows + kIdxWaves - 1) / kIdxWaves;
   dim3 grid((unsigned)nblk), block(kIdxWaves * 64);
   if (w_dtype == 0)
     hipLaunchKernelGGL((indexer_kernel<D, MB, uint16_t>), grid, block, 0, st,
-                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)w, rs, sl, T, H,
+                       (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)w, rs, sl, T_kv, H,
                        row_begin, n_rows, scores, ld);
   else
     hipLaunchKernelGGL((indexer_kernel<D, MB, float>), grid, block, 0, st, (const uint16_t*)q,
-                       (const uint16_t*)k, (const float*)w, rs, sl, T, H, row_begin, n_rows,
+                       (const uint16_t*)k, (const float*)w, rs, sl, T_kv, H, row_begin, n_rows,
                        scores, ld);
   return hipGetLastError();
 }
@@ -276,15 +306,25 @@ hipError_t launch_packed_metadata(const int32_t* cu, int32_t n_seq, int64_t T, i
   return hipGetLastError();
 }
 
+hipError_t launch_ratio_metadata(const int32_t* cu_q, const int32_t* cu_k, const int32_t* offsets,
+                                 int32_t n_seq, int64_t T_q, int32_t ratio, int32_t* rs,
+                                 int32_t* sl, hipStream_t st) {
+  if (T_q == 0) return hipSuccess;
+  dim3 grid((unsigned)((T_q + 255) / 256)), block(256);
+  hipLaunchKernelGGL(ratio_metadata_kernel, grid, block, 0, st, cu_q, cu_k, offsets, n_seq, T_q,
+                     ratio, rs, sl);
+  return hipGetLastError();
+}
+
 hipError_t launch_indexer(const void* q, const void* k, const void* w, int w_dtype,
-                          const int32_t* rs, const int32_t* sl, int64_t T, int H, int D,
+                          const int32_t* rs, const int32_t* sl, int64_t T_kv, int H, int D,
                           int64_t row_begin, int64_t n_rows, float* scores, int64_t ld,
                           hipStream_t st) {
   if (n_rows == 0) return hipSuccess;
   const int mb = (H + 31) / 32;
 #define DSA_IDX_CASE(DD, MM)                                                                   \
   if (D == DD && mb == MM)                                                                     \
-    return launch_indexer_w<DD, MM>(q, k, w, w_dtype, rs, sl, T, H, row_begin, n_rows, scores, \
+    return launch_indexer_w<DD, MM>(q, k, w, w_dtype, rs, sl, T_kv, H, row_begin, n_rows, scores, \
                                     ld, st);
   DSA_IDX_CASE(128, 1) DSA_IDX_CASE(128, 2) DSA_IDX_CASE(64, 1) DSA_IDX_CASE(64, 2)
 #undef DSA_IDX_CASE

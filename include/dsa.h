@@ -1,8 +1,10 @@
 /*
  * dsa.h - C ABI of the MI355X (gfx950) DeepSeek Sparse Attention forward path.
  *
- * Four stream-ordered calls cover the forward hot path of DSA:
+ * Five stream-ordered calls cover the forward hot path of DSA:
  *   dsa_packed_metadata  per-token document start and causal length (THD)
+ *   dsa_ratio_causal_metadata  the same for the ratio-causal mask with query
+ *                        causal offsets (compressed keys, split queries)
  *   dsa_indexer_fwd      lightning-indexer scores  sum_h W_h * ReLU(q_h . k)
  *   dsa_topk             per-row top-K select, ascending global indices, -1 pad
  *   dsa_sparse_attn_fwd  sparse MQA/GQA attention over the selected KV rows
@@ -54,7 +56,7 @@ typedef enum { DSA_BF16 = 0, DSA_F32 = 1 } dsa_dtype;
 const char* dsa_last_error(void);
 
 /* ABI version of this header (bumped on any signature change). */
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
 int dsa_abi_version(void);
 
 /* Limits enforced by the host checks. */
@@ -79,18 +81,53 @@ int dsa_packed_metadata(const int32_t* cu_seqlens, int32_t n_seq, int64_t T,
                         int32_t* row_starts, int32_t* seq_lens, void* stream);
 
 /*
+ * dsa_ratio_causal_metadata - step a0 for the ratio-causal mask.
+ * DSA page section 3 ("Indexer Forward"): THD segment b stores its queries at
+ * rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) and its compressed keys at rows
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1]); the keys are a compressed prefix that
+ * starts at compressed column 0. Local query row i of segment b
+ * (t = cu_seqlens_q[b] + i) may score local key column j only when
+ *   j < clamp(floor((q_causal_offsets[b] + i + 1) / ratio), 0,
+ *             cu_seqlens_k[b+1] - cu_seqlens_k[b])
+ * so this writes
+ *   row_starts[t] = cu_seqlens_k[b], seq_lens[t] = that bound.
+ * q_causal_offsets[b] is the global, uncompressed token position of segment
+ * b's first query (its place in the causal timeline, not where it is
+ * stored); NULL means 0 for every segment. The outputs feed dsa_indexer_fwd
+ * and dsa_topk as they are. ratio 1, no offsets and cu_seqlens_k ==
+ * cu_seqlens_q give exactly dsa_packed_metadata's result.
+ *   cu_seqlens_q, cu_seqlens_k  device int32 [n_seq + 1], starting at 0,
+ *               non-decreasing, cu_seqlens_q[n_seq] = T_q (not checked on
+ *               the host; a row past cu_seqlens_q[n_seq] is given the last
+ *               segment)
+ *   q_causal_offsets  device int32 [n_seq] or NULL
+ *   ratio       >= 1 (tokens per compressed key)
+ *   row_starts, seq_lens  device int32 [T_q] outputs
+ * Errors: n_seq < 1, T_q < 0 or T_q > INT32_MAX, ratio < 1, a NULL pointer
+ * (other than q_causal_offsets) with T_q > 0. T_q = 0 is a no-op.
+ */
+int dsa_ratio_causal_metadata(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              const int32_t* q_causal_offsets, int32_t n_seq, int64_t T_q,
+                              int32_t ratio, int32_t* row_starts, int32_t* seq_lens,
+                              void* stream);
+
+/*
  * dsa_indexer_fwd - step a1, lightning-indexer scores.
- * DSA page section 3 with ratio 1 and no causal offsets: for query row t and
- * local key column j < seq_lens[t],
+ * DSA page section 3: for query row t and local key column j < seq_lens[t]
+ * (the causal mask from dsa_packed_metadata, or the ratio-causal mask with
+ * query causal offsets from dsa_ratio_causal_metadata),
  *   scores[t - row_begin, j] = sum_h W[t, h] * max(0, sum_d q_idx[t, h, d] * k_idx[row_starts[t] + j, d])
  * The indexer key has a single head shared by all H_idx query heads. No
  * scaling is applied inside: W already carries any 1/sqrt(H) and 1/sqrt(D)
  * factors (cudnn_dsa page, cudnn_indexer_topk, head_weights).
  *   q_idx       device bf16 [T, H_idx, D_idx], contiguous
- *   k_idx       device bf16 [T, D_idx], contiguous
+ *   k_idx       device bf16 [T_kv, D_idx], contiguous
  *   w           device [T, H_idx], dtype w_dtype (DSA_BF16 or DSA_F32)
- *   row_starts, seq_lens  device int32 [T] (from dsa_packed_metadata)
+ *   row_starts, seq_lens  device int32 [T] (from either metadata call)
  *   T, H_idx, D_idx       H_idx in [1, 64], D_idx in {64, 128}
+ *   T_kv        rows of k_idx; key rows outside [0, T_kv) are never read
+ *               (row_starts[t] + seq_lens[t] <= T_kv is the caller's
+ *               contract; T_kv = 0 writes nothing)
  *   row_begin, n_rows     rows [row_begin, row_begin + n_rows) of T; the
  *                         caller chunks rows to bound the score buffer
  *   scores      device fp32 [n_rows, ld_scores] output, 16-byte aligned,
@@ -101,7 +138,7 @@ int dsa_packed_metadata(const int32_t* cu_seqlens, int32_t n_seq, int64_t T,
  * fp32 accumulation of bf16 products (MFMA), fp32 epilogue.
  */
 int dsa_indexer_fwd(const void* q_idx, const void* k_idx, const void* w, int32_t w_dtype,
-                    const int32_t* row_starts, const int32_t* seq_lens, int64_t T,
+                    const int32_t* row_starts, const int32_t* seq_lens, int64_t T, int64_t T_kv,
                     int32_t H_idx, int32_t D_idx, int64_t row_begin, int64_t n_rows,
                     float* scores, int64_t ld_scores, void* stream);
 

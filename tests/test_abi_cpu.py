@@ -25,24 +25,29 @@ FAKE2 = 3 << 20     # a second, distinct fake buffer
 
 TOPK_BASE = dict(scores=FAKE, ld=4096, n_rows=8, n_cols=4096, seq_lens=FAKE, row_starts=None,
                  k=64, indices=FAKE, ld_idx=64, tl=None, vals=None, stream=None)
-IDX_BASE = dict(q=FAKE, k=FAKE, w=FAKE, wd=0, rs=FAKE, sl=FAKE, T=256, H=4, D=64, rb=0, nr=256,
-                scores=FAKE, ld=256, stream=None)
+IDX_BASE = dict(q=FAKE, k=FAKE, w=FAKE, wd=0, rs=FAKE, sl=FAKE, T=256, Tkv=256, H=4, D=64, rb=0,
+                nr=256, scores=FAKE, ld=256, stream=None)
 ATTN_BASE = dict(q=FAKE, Tq=16, H=16, Dqk=576, k=FAKE, Tkv=16, ldk=576, v=None, ldv=0, Dv=512,
                  idx=FAKE, ldi=64, kw=64, tl=None, sink=None, scale=0.04, out=FAKE, lse=FAKE,
                  mx=None, stream=None)
 META_BASE = dict(cu=FAKE, n_seq=1, T=4, rs=FAKE, sl=FAKE, stream=None)
+RMETA_BASE = dict(cq=FAKE, ck=FAKE2, off=None, n_seq=2, T=4, ratio=4, rs=FAKE, sl=FAKE,
+                  stream=None)
 
 ORDER = {
     "topk": ["scores", "ld", "n_rows", "n_cols", "seq_lens", "row_starts", "k", "indices",
              "ld_idx", "tl", "vals", "stream"],
-    "idx": ["q", "k", "w", "wd", "rs", "sl", "T", "H", "D", "rb", "nr", "scores", "ld", "stream"],
+    "idx": ["q", "k", "w", "wd", "rs", "sl", "T", "Tkv", "H", "D", "rb", "nr", "scores", "ld",
+            "stream"],
     "attn": ["q", "Tq", "H", "Dqk", "k", "Tkv", "ldk", "v", "ldv", "Dv", "idx", "ldi", "kw", "tl",
              "sink", "scale", "out", "lse", "mx", "stream"],
     "meta": ["cu", "n_seq", "T", "rs", "sl", "stream"],
+    "rmeta": ["cq", "ck", "off", "n_seq", "T", "ratio", "rs", "sl", "stream"],
 }
-BASE = {"topk": TOPK_BASE, "idx": IDX_BASE, "attn": ATTN_BASE, "meta": META_BASE}
+BASE = {"topk": TOPK_BASE, "idx": IDX_BASE, "attn": ATTN_BASE, "meta": META_BASE,
+        "rmeta": RMETA_BASE}
 FN = {"topk": "dsa_topk", "idx": "dsa_indexer_fwd", "attn": "dsa_sparse_attn_fwd",
-      "meta": "dsa_packed_metadata"}
+      "meta": "dsa_packed_metadata", "rmeta": "dsa_ratio_causal_metadata"}
 
 CASES = [
     # top-K
@@ -60,6 +65,8 @@ CASES = [
     ("idx", dict(ld=254), EVALUE), ("idx", dict(q=None), EVALUE), ("idx", dict(k=FAKE + 2), EVALUE),
     ("idx", dict(scores=FAKE + 8), EVALUE), ("idx", dict(wd=1, w=FAKE + 2), EVALUE),
     ("idx", dict(T=-1), EVALUE), ("idx", dict(nr=0, q=None, k=None, w=None), OK),
+    ("idx", dict(Tkv=-1), EVALUE), ("idx", dict(Tkv=2 ** 31), EVALUE),
+    ("idx", dict(Tkv=0, q=None, k=None, w=None), OK), ("idx", dict(Tkv=64), ERUNTIME),
     ("idx", dict(), ERUNTIME), ("idx", dict(wd=1, D=128, H=64), ERUNTIME),
     # attention
     ("attn", dict(H=0), EVALUE), ("attn", dict(H=129), EVALUE),
@@ -81,6 +88,13 @@ CASES = [
     # metadata
     ("meta", dict(n_seq=0), EVALUE), ("meta", dict(T=-1), EVALUE), ("meta", dict(cu=None), EVALUE),
     ("meta", dict(T=0, cu=None, rs=None, sl=None), OK), ("meta", dict(), ERUNTIME),
+    # ratio-causal metadata
+    ("rmeta", dict(n_seq=0), EVALUE), ("rmeta", dict(T=-1), EVALUE),
+    ("rmeta", dict(ratio=0), EVALUE), ("rmeta", dict(ratio=-4), EVALUE),
+    ("rmeta", dict(cq=None), EVALUE), ("rmeta", dict(ck=None), EVALUE),
+    ("rmeta", dict(sl=None), EVALUE),
+    ("rmeta", dict(T=0, cq=None, ck=None, rs=None, sl=None), OK),
+    ("rmeta", dict(), ERUNTIME), ("rmeta", dict(off=FAKE2, ratio=1), ERUNTIME),
 ]
 
 _CHILD = r"""
@@ -124,8 +138,8 @@ def _declared_functions():
 
 def test_header_declares_the_path():
     names = _declared_functions()
-    for fn in ["dsa_packed_metadata", "dsa_indexer_fwd", "dsa_topk", "dsa_sparse_attn_fwd",
-               "dsa_last_error", "dsa_abi_version"]:
+    for fn in ["dsa_packed_metadata", "dsa_ratio_causal_metadata", "dsa_indexer_fwd", "dsa_topk",
+               "dsa_sparse_attn_fwd", "dsa_last_error", "dsa_abi_version"]:
         assert fn in names
 
 

@@ -12,5 +12,7 @@ from .gen import (  # noqa: F401
     config_doc_lens,
     make_config,
     make_custom,
+    make_split,
     qsa_routes,
+    SplitWorkload,
 )

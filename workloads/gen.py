@@ -178,3 +178,65 @@ def make_config(i: int, device="cpu", seed=None, stress=False) -> Workload:
                      routes_width=c["topk"] if c.get("qsa") else None, stress=stress,
                      value_std=c.get("value_std"), name=c["name"] + ("_stress" if stress else ""))
     return wl
+
+
+@dataclass
+class SplitWorkload:
+    """Queries and keys stored as THD segments of their own (ratio-causal mask).
+
+    Segment b stores q_lens[b] query rows and k_lens[b] (compressed) key rows;
+    offsets[b] is the global token position of its first query.
+    """
+    name: str
+    T_q: int
+    T_kv: int
+    cu_seqlens_q: torch.Tensor        # int32 [n_seq+1]
+    cu_seqlens_k: torch.Tensor        # int32 [n_seq+1]
+    q_causal_offsets: Optional[torch.Tensor]  # int32 [n_seq] or None
+    ratio: int
+    H: int
+    D_qk: int
+    D_v: int
+    q: Optional[torch.Tensor]         # bf16 [T_q, H, D_qk]
+    kv: Optional[torch.Tensor]        # bf16 [T_kv, D_qk], V = kv[:, :D_v]
+    H_idx: int
+    D_idx: int
+    q_idx: torch.Tensor               # bf16 [T_q, H_idx, D_idx]
+    k_idx: torch.Tensor               # bf16 [T_kv, D_idx]
+    w: torch.Tensor                   # bf16 [T_q, H_idx]
+    sink: Optional[torch.Tensor]      # fp32 [H]
+    topk: int
+    scale: float
+    seed: int = 0
+
+
+def make_split(q_lens, k_lens, offsets, ratio, H_idx=64, D_idx=128, H=0, D_qk=576, D_v=512,
+               topk=2048, seed=0, device="cpu", name="split"):
+    """Split-query / compressed-key workload with the named configs' recipe.
+
+    Draw order: q and kv (when H > 0), q_idx, k_idx, w, sink.
+    """
+    q_lens = [int(x) for x in q_lens]
+    k_lens = [int(x) for x in k_lens]
+    assert len(q_lens) == len(k_lens)
+    T_q, T_kv = int(sum(q_lens)), int(sum(k_lens))
+    cu_q = torch.tensor(np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32))
+    cu_k = torch.tensor(np.concatenate([[0], np.cumsum(k_lens)]).astype(np.int32))
+    off = None if offsets is None else torch.tensor(np.asarray(offsets, dtype=np.int32))
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    q = kv = sk = None
+    if H > 0:
+        q = _randn(gen, (T_q, H, D_qk), 1.0 / math.sqrt(D_qk), device)
+        kv = _randn(gen, (T_kv, D_qk), 1.0 / math.sqrt(D_qk), device)
+    q_idx = _randn(gen, (T_q, H_idx, D_idx), 1.0 / math.sqrt(D_idx), device)
+    k_idx = _randn(gen, (T_kv, D_idx), 1.0 / math.sqrt(D_idx), device)
+    w = _randn(gen, (T_q, H_idx), 1.0 / math.sqrt(H_idx), device)
+    if H > 0:
+        sk = torch.randn((H,), generator=gen, device=device, dtype=torch.float32)
+    return SplitWorkload(name=name, T_q=T_q, T_kv=T_kv, cu_seqlens_q=cu_q.to(device),
+                         cu_seqlens_k=cu_k.to(device),
+                         q_causal_offsets=None if off is None else off.to(device), ratio=int(ratio),
+                         H=H, D_qk=D_qk, D_v=D_v, q=q, kv=kv, H_idx=H_idx, D_idx=D_idx,
+                         q_idx=q_idx, k_idx=k_idx, w=w, sink=sk, topk=int(topk),
+                         scale=1.0 / math.sqrt(D_qk), seed=int(seed))
