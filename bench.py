@@ -2,8 +2,10 @@
 """Benchmark of the DSA forward hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-packed metadata -> lightning-indexer scores (row chunks under a 2 GiB score
-cap) -> radix top-K -> sparse attention forward. Inputs are generated on the
+metadata -> lightning-indexer scores (row chunks under a 2 GiB score cap) ->
+radix top-K -> sparse attention forward. Workloads 1-5 are packed documents
+(plain causal mask); 6 and 7 are split-query / compressed-key workloads
+(ratio-causal mask with query causal offsets). Inputs are generated on the
 GPU before the timed region and stay resident in HBM.
 
 Prints one JSON line. `value` is the sparse-attention forward throughput in
@@ -42,7 +44,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", type=int, default=2, help="workload 1..5 (default: 2)")
+    p.add_argument("--config", type=int, default=2, help="workload 1..7 (default: 2)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline")
@@ -64,9 +66,9 @@ def workload_counts(wl, seq_lens_np):
     c = {}
     K = wl.topk
     if wl.q_idx is not None:
-        pairs = int(sum(L * (L + 1) // 2 for L in wl.doc_lens))
-        c["indexer_flop"] = 2.0 * wl.H_idx * wl.D_idx * pairs
         sl = seq_lens_np.astype(np.int64)
+        pairs = int(sl.sum())  # scored (query, key) pairs: sum of the mask lengths
+        c["indexer_flop"] = 2.0 * wl.H_idx * wl.D_idx * pairs
         rd = 4.0 * float(sl[sl > K].sum()) + 8.0 * len(sl)
         wr = (4.0 * K + 4.0) * len(sl)
         c["topk_bytes"] = rd + wr
@@ -230,11 +232,20 @@ def main():
     torch.cuda.set_device(0)
     dsa.load_library()
     wl = make_config(args.config, device=dev)
+    split = bool(CONFIGS[args.config].get("split"))
     T, K = wl.T, wl.topk
-    max_len = max(wl.doc_lens)
+    # longest score row: the longest document, or the longest key segment
+    max_len = max(CONFIGS[args.config]["k_lens"]) if split else max(wl.doc_lens)
     has_indexer = wl.q_idx is not None
 
-    rs, sl = dsa.dsa_packed_metadata(wl.cu_seqlens, T)
+    def metadata(row_starts=None, seq_lens=None):
+        if split:
+            return dsa.dsa_ratio_causal_metadata(wl.cu_seqlens_q, wl.cu_seqlens_k, T, wl.ratio,
+                                                 wl.q_causal_offsets, row_starts=row_starts,
+                                                 seq_lens=seq_lens)
+        return dsa.dsa_packed_metadata(wl.cu_seqlens, T, row_starts=row_starts, seq_lens=seq_lens)
+
+    rs, sl = metadata()
     rows_per_chunk = dsa.chunk_rows(T, max_len)
     ld = max(4, (max_len + 3) // 4 * 4)
     scores = torch.empty((min(rows_per_chunk, T), ld), dtype=torch.float32, device=dev)
@@ -253,14 +264,16 @@ def main():
         e2 = torch.cuda.Event(enable_timing=True) if timed else None
         if timed:
             e0.record(stream)
-        dsa.dsa_packed_metadata(wl.cu_seqlens, T, row_starts=rs, seq_lens=sl)
+        metadata(rs, sl)
         if has_indexer:
             for r0 in range(0, T, rows_per_chunk):
                 n = min(rows_per_chunk, T - r0)
                 dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, wl.w, rs, sl, row_begin=r0, n_rows=n,
                                     scores=scores)
+                # plain causal rows never see more than r0 + n keys
+                n_cols = max_len if split else min(max_len, r0 + n)
                 dsa.dsa_topk(scores[:n], sl[r0:r0 + n], K, row_starts=rs[r0:r0 + n],
-                             n_cols=min(max_len, r0 + n), indices=indices[r0:r0 + n],
+                             n_cols=n_cols, indices=indices[r0:r0 + n],
                              topk_length=topk_length[r0:r0 + n])
         if timed:
             e1.record(stream)
@@ -316,12 +329,18 @@ def main():
         "data": "synthetic",
         "config": {"workload": CONFIGS[args.config]["name"], "T": T, "heads": wl.H,
                    "D_qk": wl.D_qk, "D_v": wl.D_v, "topk": K, "indexer_heads": wl.H_idx,
-                   "indexer_dim": wl.D_idx, "docs": len(wl.doc_lens), "parallelism": "none"},
+                   "indexer_dim": wl.D_idx, "parallelism": "none"},
         "indexer_topk_rows_per_s": rows_per_s,
         "stages": stages,
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if split:
+        c = CONFIGS[args.config]
+        rec["config"].update({"T_kv": wl.T_kv, "ratio": wl.ratio, "q_causal_offsets": c["offsets"],
+                              "segments": len(c["q_lens"])})
+    else:
+        rec["config"]["docs"] = len(wl.doc_lens)
     if not args.no_cpu_baseline:
         wl.extra["indices"] = indices
         wl.extra["topk_length"] = topk_length

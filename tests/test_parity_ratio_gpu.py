@@ -152,3 +152,45 @@ def test_last_rank_of_eight_way_split(ratio):
         ref_idx, _ = O.topk(sc.cpu().numpy().astype(np.float64), sl_ref[r:r + 1], K,
                             row_starts=st_ref[r:r + 1], n_cols=Tk)
         assert np.array_equal(gi[r], ref_idx[0]), r
+
+
+@pytest.mark.parametrize("cfg", [6, 7])
+def test_split_config_sampled(cfg):
+    """The split-query / compressed-key workloads as the bench runs them:
+    chained indexer + top-K, then attention over the selected global rows."""
+    from workloads import CONFIGS, make_config
+    from gpu_helpers import check_attention
+    say("config", cfg)
+    wl = make_config(cfg, device=DEV)
+    width = max(CONFIGS[cfg]["k_lens"])
+    K = wl.topk
+    idx, tl = dsa.indexer_topk(wl.q_idx, wl.k_idx, wl.w, wl.cu_seqlens_q, K,
+                               cu_seqlens_k=wl.cu_seqlens_k, ratio=wl.ratio,
+                               q_causal_offsets=wl.q_causal_offsets, max_seqlen=width)
+    out, lse, mx = dsa.dsa_sparse_attn_fwd(wl.q, wl.kv, idx, topk_length=tl, attn_sink=wl.sink,
+                                           softmax_scale=wl.scale)
+    rs, sl = _meta(wl)
+    torch.cuda.synchronize()
+    st_ref, sl_ref = _ref_meta(wl)
+    assert np.array_equal(i64(rs), st_ref) and np.array_equal(i64(sl), sl_ref)
+    T = wl.T_q
+    rows = np.array(sorted({0, 1, 2, 3, 5, T // 2, T - 2, T - 1}))
+    gi = i64(idx)
+    for r in rows:
+        sc = dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, wl.w, rs, sl, row_begin=int(r), n_rows=1,
+                                 width=width)
+        torch.cuda.synchronize()
+        check_indexer(sc, wl, [r], i64(rs), i64(sl))
+        ref_idx, _ = O.topk(sc.cpu().numpy().astype(np.float64), sl_ref[r:r + 1], K,
+                            row_starts=st_ref[r:r + 1], n_cols=width)
+        assert np.array_equal(gi[r], ref_idx[0]), r
+    check_attention(out, lse, mx, wl.q, wl.kv, None, idx, tl, wl.sink, wl.scale, wl.D_v, rows)
+    # whole-tensor properties at full size
+    tln = i64(tl)
+    assert np.array_equal(tln, np.minimum(sl_ref, K))
+    valid = gi >= 0
+    assert np.array_equal(valid.sum(1), tln)
+    assert np.all(np.where(valid, gi < (st_ref + sl_ref)[:, None], True))
+    assert np.all(np.diff(np.where(valid, gi, np.iinfo(np.int32).max), axis=1) >= 0)
+    fin = tln > 0
+    assert torch.isfinite(lse[torch.as_tensor(fin, device=DEV)]).all()

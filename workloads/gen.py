@@ -36,6 +36,15 @@ CONFIGS = {
     5: dict(name="qsa_B4x8192_H12_D256", doc_lens=[8192] * 4, H=12, D_qk=256, D_v=256,
             shared_kv=False, H_idx=0, D_idx=0, topk=512, scale=1.0 / 16.0, sink=False,
             qsa=True, value_std=1.0 / 16.0),
+    # One GPU's share of T = 65536 split 8 ways by query rows: the last 8192
+    # rows (global offset 57344) against all 65536 keys (ratio-causal mask
+    # with query causal offsets, ratio 1).
+    6: dict(name="cp8_last_rank_T65536", split=True, q_lens=[8192], k_lens=[65536],
+            offsets=[57344], ratio=1, H=64, D_qk=576, D_v=512, H_idx=64, D_idx=128, topk=2048),
+    # Compressed keys: T = 65536 queries over 16384 keys, one key per 4 tokens,
+    # top-512 (the DSA page's ratio-4 indexer example).
+    7: dict(name="ratio4_T65536_K512", split=True, q_lens=[65536], k_lens=[16384],
+            offsets=None, ratio=4, H=64, D_qk=576, D_v=512, H_idx=64, D_idx=128, topk=512),
 }
 
 
@@ -157,7 +166,7 @@ def make_custom(doc_lens, H, D_qk, D_v, shared_kv=True, H_idx=4, D_idx=64, topk=
 
 
 def config_doc_lens(i: int, seed=None) -> List[int]:
-    """Document lengths of a named workload (drawn before any tensor)."""
+    """Document lengths of a named packed workload (drawn before any tensor)."""
     c = CONFIGS[i]
     seed = 1000 + i if seed is None else int(seed)
     if c.get("doc_lens") is None:
@@ -167,10 +176,16 @@ def config_doc_lens(i: int, seed=None) -> List[int]:
     return list(c["doc_lens"])
 
 
-def make_config(i: int, device="cpu", seed=None, stress=False) -> Workload:
-    """One of the five named workloads; seed defaults to 1000 + i."""
+def make_config(i: int, device="cpu", seed=None, stress=False):
+    """One of the named workloads (a Workload, or a SplitWorkload for the
+    split-query / compressed-key ones); seed defaults to 1000 + i."""
     c = dict(CONFIGS[i])
     seed = 1000 + i if seed is None else int(seed)
+    if c.get("split"):
+        assert not stress
+        return make_split(c["q_lens"], c["k_lens"], c["offsets"], c["ratio"], H_idx=c["H_idx"],
+                          D_idx=c["D_idx"], H=c["H"], D_qk=c["D_qk"], D_v=c["D_v"],
+                          topk=c["topk"], seed=seed, device=device, name=c["name"])
     doc_lens = config_doc_lens(i, seed)
     wl = make_custom(doc_lens, c["H"], c["D_qk"], c["D_v"], shared_kv=c["shared_kv"],
                      H_idx=c["H_idx"], D_idx=c["D_idx"], topk=c["topk"], scale=c["scale"],
@@ -208,6 +223,12 @@ class SplitWorkload:
     topk: int
     scale: float
     seed: int = 0
+    v: Optional[torch.Tensor] = None  # values are always kv[:, :D_v] here
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def T(self) -> int:
+        return self.T_q
 
 
 def make_split(q_lens, k_lens, offsets, ratio, H_idx=64, D_idx=128, H=0, D_qk=576, D_v=512,
