@@ -11,7 +11,8 @@ Every function is written from the definitions on the pages:
   (docs.nvidia.com/cudnn/fe-oss-apis/dsa): section 1 "Sparse Attention
   Forward" (slot semantics, sink, LSE, empty rows, topk_length clamp, D_qk=576
   with V = first 512 dims), section 3 "Indexer Forward (score-only)" (score
-  formula and ratio-causal mask), section 4 "Combined Indexer Forward + Top-K"
+  formula, ratio-causal mask, and the FP8 / MXFP8 input precisions), section
+  4 "Combined Indexer Forward + Top-K"
   (deterministic tie-break toward the smallest index) and section 5
   "Indexer Top-K" (per-row effective length, top_k <= 2048).
 * "nemo_automodel...glm_moe_dsa.kernels.cudnn_dsa" API page:
@@ -137,6 +138,61 @@ def indexer_scores(q_idx, k_idx, w, row_starts, seq_lens, rows, width=None):
         logits = q_idx[t] @ keys.T                  # [H, n]   Q_h . K^T
         out[r, :n] = w[t] @ np.maximum(logits, 0.0)  # sum_h W_h * ReLU(.)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Step a1 in FP8: E4M3 inputs with per-token or per-block (MX) scales
+# ---------------------------------------------------------------------------
+
+def decode_e4m3(codes) -> np.ndarray:
+    """FP8 E4M3 bytes -> float64 (the OCP "E4M3FN" encoding the DSA page's FP8
+    paths use): sign bit, 4 exponent bits with bias 7, 3 mantissa bits. An
+    exponent field of 0 is subnormal, m/8 * 2^-6; S.1111.111 is NaN; there are
+    no infinities, so the largest magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    sign = np.where(c >> 7 == 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def decode_e8m0(codes) -> np.ndarray:
+    """E8M0 scale bytes -> float64: the power of two 2^(code - 127); 255 is NaN."""
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    return np.where(c == 255, np.nan, np.exp2(c - 127.0))
+
+
+def indexer_scores_fp8(q8, q_scale, k8, k_scale, w, row_starts, seq_lens, rows, width=None):
+    """Indexer scores of the FP8 path with per-token descales (DSA page,
+    section 3, precision "fp8" on SM90).
+
+    Q and K are E4M3 bytes; q_scale [T, H] and k_scale [T_kv] are fp32 descales
+    (one per token and head for Q, one per token for the single-head K). The
+    real inputs are the decoded values times their descale; the score is then
+    the section's definition on them (indexer_scores).
+    q8 [T, H, D] and k8 [T_kv, D] uint8, q_scale/k_scale/w float64.
+    """
+    q = decode_e4m3(q8) * np.asarray(q_scale, dtype=np.float64)[..., None]
+    k = decode_e4m3(k8) * np.asarray(k_scale, dtype=np.float64)[:, None]
+    return indexer_scores(q, k, w, row_starts, seq_lens, rows, width)
+
+
+def indexer_scores_mxfp8(q8, q_sf, k8, k_sf, w, row_starts, seq_lens, rows, width=None,
+                         block=32):
+    """Indexer scores of the block-scaled FP8 path (DSA page, section 3,
+    precision "mxfp8": E4M3 values with E8M0 scales, one per 32 consecutive
+    elements along the head dimension).
+
+    q8 [T, H, D], k8 [T_kv, D] uint8; q_sf [T, H, D/32], k_sf [T_kv, D/32]
+    uint8 E8M0. Element d of a row is decoded(d) * scale[d // 32]; the score
+    is then the section's definition on those values (indexer_scores).
+    """
+    q = decode_e4m3(q8) * np.repeat(decode_e8m0(q_sf), block, axis=-1)
+    k = decode_e4m3(k8) * np.repeat(decode_e8m0(k_sf), block, axis=-1)
+    return indexer_scores(q, k, w, row_starts, seq_lens, rows, width)
 
 
 # ---------------------------------------------------------------------------

@@ -291,6 +291,162 @@ def test_planted_ratio_causal_mistakes_fail_their_pins():
         assert _ratio_mutant(cq, ck, 22, ratio, off, mistake).tolist() != enum, mistake
 
 
+# ---------------------------------------------------------------- FP8 input --
+
+def test_decode_e4m3_matches_torch_float8_e4m3fn():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.decode_e4m3(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.isnan(got).sum() == 2
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+    # hand-derived values of the encoding
+    assert O.decode_e4m3([0x38, 0x7E, 0x01, 0x08, 0xC0])[:].tolist() == [1.0, 448.0, 2.0 ** -9,
+                                                                         2.0 ** -6, -2.0]
+
+
+def test_decode_e8m0_matches_torch_float8_e8m0fnu():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    got = O.decode_e8m0(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.isnan(got).sum() == 1
+    assert np.array_equal(got[:255], ref[:255])
+    assert O.decode_e8m0([127, 128, 0]).tolist() == [1.0, 2.0, 2.0 ** -127]
+
+
+def _e4m3_bytes(x32):
+    """Round float32 values to E4M3 bytes with torch's cast (nearest-even)."""
+    return torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _quant_err(x, scale):
+    """Rigorous bound of |dequant(quant(x)) - x| for E4M3 with descale `scale`:
+    half a unit in the last place, 2^-4 relative for normals, 2^-10 * scale in
+    the subnormal range."""
+    return np.maximum(np.abs(x) * 2.0 ** -4, scale * 2.0 ** -10)
+
+
+def _fp8_case(rng, T, H, D, spread):
+    """Real-valued indexer inputs whose magnitudes vary over tokens, heads and
+    32-element blocks by factors up to e^spread."""
+    q = rng.standard_normal((T, H, D)) * np.exp(spread * rng.standard_normal((T, H, 1)))
+    k = rng.standard_normal((T, D)) * np.exp(spread * rng.standard_normal((T, 1)))
+    blk = np.repeat(np.exp(spread * rng.standard_normal(D // 32)), 32)
+    return q * blk, k * blk[::-1], rng.standard_normal((T, H))
+
+
+def _score_bound(q, k, w, eq, ek, st, sl):
+    T = q.shape[0]
+    bound = np.zeros((T, T))
+    for t in range(T):
+        n, s0 = int(sl[t]), int(st[t])
+        kk, ee = np.abs(k[s0:s0 + n]), ek[s0:s0 + n]
+        per = (eq[t] @ (kk + ee).T) + (np.abs(q[t]) @ ee.T)   # [H, n]
+        bound[t, :n] = np.abs(w[t]) @ per
+    return bound
+
+
+def _fp8_per_token(q, k):
+    qs = np.abs(q).max(axis=2) / 448.0
+    ks = np.abs(k).max(axis=1) / 448.0
+    q8 = _e4m3_bytes(q / qs[..., None])
+    k8 = _e4m3_bytes(k / ks[:, None])
+    return q8, qs, k8, ks
+
+
+def _fp8_per_block(q, k):
+    def sf(x):
+        amax = np.abs(x.reshape(*x.shape[:-1], -1, 32)).max(axis=-1)
+        e = np.ceil(np.log2(amax / 448.0)).astype(np.int64)        # 2^e >= amax / 448
+        return (e + 127).astype(np.uint8), np.repeat(np.exp2(e.astype(np.float64)), 32, axis=-1)
+    q_sf, qs = sf(q)
+    k_sf, ks = sf(k)
+    return _e4m3_bytes(q / qs), q_sf, qs, _e4m3_bytes(k / ks), k_sf, ks
+
+
+def test_fp8_indexer_within_quantisation_bound():
+    rng = np.random.default_rng(50)
+    T, H, D = 24, 5, 64
+    q, k, w = _fp8_case(rng, T, H, D, 1.5)
+    st, sl = O.packed_metadata([0, 9, T], T)
+    exact = O.indexer_scores(q, k, w, st, sl, np.arange(T), width=T)
+    q8, qs, k8, ks = _fp8_per_token(q, k)
+    got = O.indexer_scores_fp8(q8, qs, k8, ks, w, st, sl, np.arange(T), width=T)
+    bound = _score_bound(q, k, w, _quant_err(q, qs[..., None]), _quant_err(k, ks[:, None]), st, sl)
+    fin = np.isfinite(exact)
+    assert np.array_equal(np.isfinite(got), fin)
+    assert np.all(np.abs(got[fin] - exact[fin]) <= bound[fin] * (1 + 1e-9))
+    # the bound is informative: the scores move by less than 10% of their scale
+    assert np.abs(got[fin] - exact[fin]).max() < 0.1 * np.abs(exact[fin]).max()
+
+
+def test_mxfp8_indexer_within_quantisation_bound():
+    rng = np.random.default_rng(51)
+    T, H, D = 20, 4, 128
+    q, k, w = _fp8_case(rng, T, H, D, 2.0)
+    st, sl = O.packed_metadata([0, 20], T)
+    exact = O.indexer_scores(q, k, w, st, sl, np.arange(T), width=T)
+    q8, q_sf, qs, k8, k_sf, ks = _fp8_per_block(q, k)
+    got = O.indexer_scores_mxfp8(q8, q_sf, k8, k_sf, w, st, sl, np.arange(T), width=T)
+    bound = _score_bound(q, k, w, _quant_err(q, qs), _quant_err(k, ks), st, sl)
+    fin = np.isfinite(exact)
+    assert np.all(np.abs(got[fin] - exact[fin]) <= bound[fin] * (1 + 1e-9))
+    assert np.abs(got[fin] - exact[fin]).max() < 0.1 * np.abs(exact[fin]).max()
+
+
+def test_fp8_scale_transfer_invariance():
+    # moving a power of two from a key's descale into every query descale
+    # changes no score (both enter the same product)
+    rng = np.random.default_rng(52)
+    T, H, D = 16, 3, 32
+    q8 = rng.integers(0, 256, (T, H, D)).astype(np.uint8)
+    k8 = rng.integers(0, 256, (T, D)).astype(np.uint8)
+    q8[(q8 & 0x7F) == 0x7F] = 0x11                             # no NaN codes
+    k8[(k8 & 0x7F) == 0x7F] = 0x22
+    qs = np.exp(rng.standard_normal((T, H)))
+    ks = np.exp(rng.standard_normal(T))
+    w = rng.standard_normal((T, H))
+    st, sl = O.packed_metadata([0, T], T)
+    a = O.indexer_scores_fp8(q8, qs, k8, ks, w, st, sl, np.arange(T))
+    b = O.indexer_scores_fp8(q8, qs * 4.0, k8, ks / 4.0, w, st, sl, np.arange(T))
+    fin = np.isfinite(a)
+    np.testing.assert_allclose(b[fin], a[fin], rtol=1e-13, atol=1e-300)
+
+
+def test_planted_fp8_mistakes_fail_the_bound():
+    rng = np.random.default_rng(53)
+    T, H, D = 24, 5, 64
+    q, k, w = _fp8_case(rng, T, H, D, 1.5)
+    st, sl = O.packed_metadata([0, T], T)
+    exact = O.indexer_scores(q, k, w, st, sl, np.arange(T), width=T)
+    fin = np.isfinite(exact)
+    q8, qs, k8, ks = _fp8_per_token(q, k)
+    bound = _score_bound(q, k, w, _quant_err(q, qs[..., None]), _quant_err(k, ks[:, None]), st, sl)
+    qd, kd = O.decode_e4m3(q8), O.decode_e4m3(k8)
+    mutants = {
+        "key descales of other keys": (qd * qs[..., None], kd * ks[::-1, None]),
+        "descale divided": (qd / qs[..., None], kd / ks[:, None]),
+        "head descale of head 0": (qd * qs[:, :1, None], kd * ks[:, None]),
+    }
+    for name, (qm, km) in mutants.items():
+        bad = O.indexer_scores(qm, km, w, st, sl, np.arange(T), width=T)
+        assert np.any(np.abs(bad[fin] - exact[fin]) > bound[fin]), name
+    # MX: the block scale of element d taken as d % (D/32) instead of d // 32
+    T, H, D = 12, 3, 128
+    q, k, w = _fp8_case(rng, T, H, D, 2.0)
+    st, sl = O.packed_metadata([0, T], T)
+    exact = O.indexer_scores(q, k, w, st, sl, np.arange(T), width=T)
+    fin = np.isfinite(exact)
+    q8, q_sf, qs, k8, k_sf, ks = _fp8_per_block(q, k)
+    bound = _score_bound(q, k, w, _quant_err(q, qs), _quant_err(k, ks), st, sl)
+    inter = lambda c: np.tile(O.decode_e8m0(c), 32)  # noqa: E731
+    bad = O.indexer_scores(O.decode_e4m3(q8) * inter(q_sf), O.decode_e4m3(k8) * inter(k_sf), w,
+                           st, sl, np.arange(T), width=T)
+    assert np.any(np.abs(bad[fin] - exact[fin]) > bound[fin])
+
+
 # ------------------------------------------------------------------- top-K --
 
 def test_topk_golden_ties_and_signed_zero():
