@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", type=int, default=2, help="workload 1..7 (default: 2)")
+    p.add_argument("--config", type=int, default=2, help="workload 1..10 (default: 2)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline")
@@ -189,16 +189,31 @@ def cpu_baseline(wl, rs, sl, budget_s):
     sample = f"attention on {n_att} random rows ({t_att:.1f} s)"
     # indexer + top-K on sampled rows
     if wl.q_idx is not None:
-        k_idx = f64(wl.k_idx)
+        fp8 = wl.extra.get("fp8")
+        if fp8:
+            i64 = lambda t: t.cpu().numpy().astype(np.int64)  # noqa: E731
+            mx = fp8["scaling"] == "mx"
+            k8 = i64(fp8["k8"])
+            ks = i64(fp8["k_scale"]) if mx else fp8["k_scale"].cpu().numpy().astype(np.float64)
+        else:
+            k_idx = f64(wl.k_idx)
         n_idx, t_idx = 0, 0.0
         while t_idx < budget_s * 0.5 and n_idx < T:
             rows = rows_order[n_idx:n_idx + 16]
             sel = torch.as_tensor(rows, device=wl.q_idx.device)
-            q = f64(wl.q_idx[sel])
             w = f64(wl.w[sel])
             st, ln = rs_np[rows].astype(np.int64), sl_np[rows].astype(np.int64)
-            t0 = time.perf_counter()
-            sc = O.indexer_scores(q, k_idx, w, st, ln, np.arange(len(rows)))
+            if fp8:
+                q8 = i64(fp8["q8"][sel])
+                qs = (i64(fp8["q_scale"][sel]) if mx
+                      else fp8["q_scale"][sel].cpu().numpy().astype(np.float64))
+                fn = O.indexer_scores_mxfp8 if mx else O.indexer_scores_fp8
+                t0 = time.perf_counter()
+                sc = fn(q8, qs, k8, ks, w, st, ln, np.arange(len(rows)))
+            else:
+                q = f64(wl.q_idx[sel])
+                t0 = time.perf_counter()
+                sc = O.indexer_scores(q, k_idx, w, st, ln, np.arange(len(rows)))
             O.topk(sc, ln, wl.topk, row_starts=st)
             t_idx += time.perf_counter() - t0
             n_idx += len(rows)
@@ -233,6 +248,7 @@ def main():
     dsa.load_library()
     wl = make_config(args.config, device=dev)
     split = bool(CONFIGS[args.config].get("split"))
+    fp8 = wl.extra.get("fp8") if hasattr(wl, "extra") else None
     T, K = wl.T, wl.topk
     # longest score row: the longest document, or the longest key segment
     max_len = max(CONFIGS[args.config]["k_lens"]) if split else max(wl.doc_lens)
@@ -246,6 +262,8 @@ def main():
         return dsa.dsa_packed_metadata(wl.cu_seqlens, T, row_starts=row_starts, seq_lens=seq_lens)
 
     rs, sl = metadata()
+    if fp8:
+        fp8_scaling = dsa.DSA_MXFP8 if fp8["scaling"] == "mx" else dsa.DSA_FP8_PER_TOKEN
     rows_per_chunk = dsa.chunk_rows(T, max_len)
     ld = max(4, (max_len + 3) // 4 * 4)
     scores = torch.empty((min(rows_per_chunk, T), ld), dtype=torch.float32, device=dev)
@@ -268,8 +286,13 @@ def main():
         if has_indexer:
             for r0 in range(0, T, rows_per_chunk):
                 n = min(rows_per_chunk, T - r0)
-                dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, wl.w, rs, sl, row_begin=r0, n_rows=n,
-                                    scores=scores)
+                if fp8:
+                    dsa.dsa_indexer_fwd_fp8(fp8["q8"], fp8["q_scale"], fp8["k8"], fp8["k_scale"],
+                                            wl.w, rs, sl, scaling=fp8_scaling, row_begin=r0,
+                                            n_rows=n, scores=scores)
+                else:
+                    dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, wl.w, rs, sl, row_begin=r0,
+                                        n_rows=n, scores=scores)
                 # plain causal rows never see more than r0 + n keys
                 n_cols = max_len if split else min(max_len, r0 + n)
                 dsa.dsa_topk(scores[:n], sl[r0:r0 + n], K, row_starts=rs[r0:r0 + n],
@@ -335,6 +358,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    rec["config"]["indexer_inputs"] = (
+        "bf16" if not fp8 else ("e4m3+e8m0/32" if fp8["scaling"] == "mx" else "e4m3+fp32/token"))
     if split:
         c = CONFIGS[args.config]
         rec["config"].update({"T_kv": wl.T_kv, "ratio": wl.ratio, "q_causal_offsets": c["offsets"],

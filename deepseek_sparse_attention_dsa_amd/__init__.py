@@ -23,13 +23,15 @@ import torch
 __all__ = [
     "DSA_BF16", "DSA_F32", "DSA_MAX_TOPK", "DSA_TOPK_MAX_COLS", "DSA_MAX_HEADS",
     "load_library", "library_path", "dsa_abi_version", "dsa_last_error",
-    "dsa_packed_metadata", "dsa_ratio_causal_metadata", "dsa_indexer_fwd", "dsa_topk",
+    "dsa_packed_metadata", "dsa_ratio_causal_metadata", "dsa_indexer_fwd",
+    "dsa_indexer_fwd_fp8", "DSA_FP8_PER_TOKEN", "DSA_MXFP8", "dsa_topk",
     "dsa_sparse_attn_fwd",
     "indexer_topk", "chunk_rows",
 ]
 
 DSA_OK, DSA_ERR_TYPE, DSA_ERR_VALUE, DSA_ERR_RUNTIME = 0, 1, 2, 3
 DSA_BF16, DSA_F32 = 0, 1
+DSA_FP8_PER_TOKEN, DSA_MXFP8 = 0, 1
 DSA_MAX_TOPK = 2048
 DSA_TOPK_MAX_COLS = 65536
 DSA_MAX_HEADS = 128
@@ -49,6 +51,8 @@ _SIGNATURES = {
     "dsa_ratio_causal_metadata": ([_P, _P, _P, _I32, _I64, _I32, _P, _P, _P], ctypes.c_int),
     "dsa_indexer_fwd": ([_P, _P, _P, _I32, _P, _P, _I64, _I64, _I32, _I32, _I64, _I64, _P, _I64,
                          _P], ctypes.c_int),
+    "dsa_indexer_fwd_fp8": ([_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I64, _I64, _I32, _I32,
+                             _I64, _I64, _P, _I64, _P], ctypes.c_int),
     "dsa_topk": ([_P, _I64, _I64, _I64, _P, _P, _I32, _P, _I64, _P, _P, _P], ctypes.c_int),
     "dsa_sparse_attn_fwd": ([_P, _I64, _I32, _I32, _P, _I64, _I64, _P, _I64, _I32, _P, _I64,
                              _I32, _P, _P, _F32, _P, _P, _P, _P], ctypes.c_int),
@@ -222,6 +226,70 @@ def dsa_indexer_fwd(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
     return scores
 
 
+def _fp8_bytes(t, name, dev):
+    if not isinstance(t, torch.Tensor) or t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError(f"{name} must be a uint8 or float8_e4m3fn tensor")
+    return _need(t.view(torch.uint8), name, torch.uint8, dev)
+
+
+def dsa_indexer_fwd_fp8(q8: torch.Tensor, q_scale: torch.Tensor, k8: torch.Tensor,
+                        k_scale: torch.Tensor, w: torch.Tensor, row_starts: torch.Tensor,
+                        seq_lens: torch.Tensor, scaling: int = DSA_MXFP8, row_begin: int = 0,
+                        n_rows: Optional[int] = None, scores: Optional[torch.Tensor] = None,
+                        width: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Indexer scores from FP8 E4M3 q8 [T,H,128] / k8 [T_kv,128].
+
+    scaling DSA_FP8_PER_TOKEN: q_scale fp32 [T,H], k_scale fp32 [T_kv]
+    descales; DSA_MXFP8: q_scale uint8 E8M0 [T,H,4], k_scale uint8 [T_kv,4].
+    Other arguments as dsa_indexer_fwd.
+    """
+    if not isinstance(w, torch.Tensor) or w.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"w must be a bfloat16 or float32 tensor (got {getattr(w, 'dtype', w)})")
+    if scaling not in (DSA_FP8_PER_TOKEN, DSA_MXFP8):
+        raise ValueError(f"unknown scaling {scaling}")
+    dev = q8.device
+    q8 = _fp8_bytes(q8, "q8", dev)
+    k8 = _fp8_bytes(k8, "k8", dev)
+    sdt = torch.float32 if scaling == DSA_FP8_PER_TOKEN else torch.uint8
+    if isinstance(q_scale, torch.Tensor) and q_scale.dtype == torch.float8_e8m0fnu:
+        q_scale = q_scale.view(torch.uint8)
+    if isinstance(k_scale, torch.Tensor) and k_scale.dtype == torch.float8_e8m0fnu:
+        k_scale = k_scale.view(torch.uint8)
+    q_scale = _need(q_scale, "q_scale", sdt, dev)
+    k_scale = _need(k_scale, "k_scale", sdt, dev)
+    w = _need(w, "w", w.dtype, dev)
+    row_starts = _need(row_starts, "row_starts", torch.int32, dev)
+    seq_lens = _need(seq_lens, "seq_lens", torch.int32, dev)
+    if q8.dim() != 3 or k8.dim() != 2 or w.dim() != 2:
+        raise ValueError("expected q8 [T,H,D], k8 [T_kv,D], w [T,H]")
+    T, H, D = q8.shape
+    T_kv = k8.shape[0]
+    nb = D // 32
+    qs_shape = (T, H) if scaling == DSA_FP8_PER_TOKEN else (T, H, nb)
+    ks_shape = (T_kv,) if scaling == DSA_FP8_PER_TOKEN else (T_kv, nb)
+    if (k8.shape[1] != D or w.shape != (T, H) or tuple(q_scale.shape) != qs_shape
+            or tuple(k_scale.shape) != ks_shape):
+        raise ValueError(f"shape mismatch: q8 {tuple(q8.shape)}, k8 {tuple(k8.shape)}, w "
+                         f"{tuple(w.shape)}, q_scale {tuple(q_scale.shape)}, k_scale "
+                         f"{tuple(k_scale.shape)}")
+    if n_rows is None:
+        n_rows = T - row_begin
+    if scores is None:
+        width = T_kv if width is None else width
+        ld = max(4, (int(width) + 3) // 4 * 4)
+        scores = torch.empty((n_rows, ld), dtype=torch.float32, device=dev)
+    else:
+        scores = _out(scores, "scores", torch.float32, dev)
+        if scores.dim() != 2 or scores.shape[0] < n_rows:
+            raise ValueError("scores must be 2-D with at least n_rows rows")
+    lib = load_library()
+    _check(lib.dsa_indexer_fwd_fp8(_ptr(q8), _ptr(q_scale), _ptr(k8), _ptr(k_scale), int(scaling),
+                                   _ptr(w), DSA_BF16 if w.dtype == torch.bfloat16 else DSA_F32,
+                                   _ptr(row_starts), _ptr(seq_lens), T, T_kv, H, D, row_begin,
+                                   n_rows, _ptr(scores), scores.stride(0), _stream(stream)))
+    return scores
+
+
 def dsa_topk(scores: torch.Tensor, seq_lens: torch.Tensor, k: int,
              row_starts: Optional[torch.Tensor] = None, n_cols: Optional[int] = None,
              indices: Optional[torch.Tensor] = None, topk_length: Optional[torch.Tensor] = None,
@@ -338,7 +406,9 @@ def chunk_rows(T: int, width: int, cap_bytes: int = SCORE_CHUNK_BYTES) -> int:
 def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
                  cu_seqlens: torch.Tensor, k: int, max_seqlen: Optional[int] = None,
                  rows_per_chunk: Optional[int] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
-                 ratio: int = 1, q_causal_offsets: Optional[torch.Tensor] = None, stream=None):
+                 ratio: int = 1, q_causal_offsets: Optional[torch.Tensor] = None,
+                 q_scale: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
+                 fp8_scaling: Optional[int] = None, stream=None):
     """Metadata + indexer scores + top-K over all rows, in score chunks.
 
     Returns (indices int32 [T, k] global ascending with -1 suffix,
@@ -348,7 +418,12 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
     1 or q_causal_offsets selects the ratio-causal mask (cu_seqlens then
     locates the query segments, cu_seqlens_k the key segments, default
     cu_seqlens); max_seqlen is then the longest key segment (default T_kv).
+    FP8 inputs (q_idx / k_idx as uint8 or float8_e4m3fn) take q_scale,
+    k_scale and fp8_scaling as dsa_indexer_fwd_fp8 does.
     """
+    fp8 = q_idx.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if fp8 and (q_scale is None or k_scale is None or fp8_scaling is None):
+        raise ValueError("FP8 indexer inputs need q_scale, k_scale and fp8_scaling")
     T = q_idx.shape[0]
     T_kv = k_idx.shape[0]
     dev = q_idx.device
@@ -368,8 +443,13 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
     scores = torch.empty((min(rows, T), ld), dtype=torch.float32, device=dev)
     for r0 in range(0, T, rows):
         n = min(rows, T - r0)
-        dsa_indexer_fwd(q_idx, k_idx, w, row_starts, seq_lens, row_begin=r0, n_rows=n,
-                        scores=scores, stream=stream)
+        if fp8:
+            dsa_indexer_fwd_fp8(q_idx, q_scale, k_idx, k_scale, w, row_starts, seq_lens,
+                                scaling=fp8_scaling, row_begin=r0, n_rows=n, scores=scores,
+                                stream=stream)
+        else:
+            dsa_indexer_fwd(q_idx, k_idx, w, row_starts, seq_lens, row_begin=r0, n_rows=n,
+                            scores=scores, stream=stream)
         # plain causal rows never see more than r0 + n keys
         n_cols = width if ratio_causal else min(width, r0 + n)
         dsa_topk(scores[:n], seq_lens[r0:r0 + n], k, row_starts=row_starts[r0:r0 + n],

@@ -126,6 +126,41 @@ int dsa_indexer_fwd(const void* q_idx, const void* k_idx, const void* w, int32_t
                                           (hipStream_t)stream));
 }
 
+int dsa_indexer_fwd_fp8(const void* q8, const void* q_scale, const void* k8, const void* k_scale,
+                        int32_t scaling, const void* w, int32_t w_dtype,
+                        const int32_t* row_starts, const int32_t* seq_lens, int64_t T,
+                        int64_t T_kv, int32_t H_idx, int32_t D_idx, int64_t row_begin,
+                        int64_t n_rows, float* scores, int64_t ld_scores, void* stream) {
+  const char* fn = "dsa_indexer_fwd_fp8";
+  REQUIRE(w_dtype == DSA_BF16 || w_dtype == DSA_F32, DSA_ERR_TYPE,
+          "%s: w_dtype must be DSA_BF16 or DSA_F32 (got %d)", fn, w_dtype);
+  REQUIRE(scaling == DSA_FP8_PER_TOKEN || scaling == DSA_MXFP8, DSA_ERR_VALUE,
+          "%s: scaling must be DSA_FP8_PER_TOKEN or DSA_MXFP8 (got %d)", fn, scaling);
+  REQUIRE(H_idx >= 1 && H_idx <= 64, DSA_ERR_VALUE, "%s: H_idx must be in [1, 64] (got %d)", fn,
+          H_idx);
+  REQUIRE(D_idx == 128, DSA_ERR_VALUE, "%s: D_idx must be 128 (got %d)", fn, D_idx);
+  REQUIRE(T >= 0 && T <= INT32_MAX, DSA_ERR_VALUE, "%s: T must be in [0, 2^31-1]", fn);
+  REQUIRE(T_kv >= 0 && T_kv <= INT32_MAX, DSA_ERR_VALUE, "%s: T_kv must be in [0, 2^31-1]", fn);
+  REQUIRE(row_begin >= 0 && n_rows >= 0 && row_begin + n_rows <= T, DSA_ERR_VALUE,
+          "%s: rows [%lld, %lld) outside [0, T=%lld)", fn, (long long)row_begin,
+          (long long)(row_begin + n_rows), (long long)T);
+  REQUIRE(ld_scores >= 4 && ld_scores % 4 == 0, DSA_ERR_VALUE,
+          "%s: ld_scores must be a positive multiple of 4 (got %lld)", fn, (long long)ld_scores);
+  if (n_rows == 0 || T_kv == 0) return DSA_OK;
+  REQUIRE(q8 && q_scale && k8 && k_scale && w && row_starts && seq_lens && scores, DSA_ERR_VALUE,
+          "%s: NULL pointer argument", fn);
+  REQUIRE(aligned(q8, 16) && aligned(k8, 16) && aligned(scores, 16), DSA_ERR_VALUE,
+          "%s: q8, k8 and scores must be 16-byte aligned", fn);
+  REQUIRE(aligned(k_scale, 4) && (scaling == DSA_MXFP8 || aligned(q_scale, 4)), DSA_ERR_VALUE,
+          "%s: scale tensors misaligned", fn);
+  REQUIRE(aligned(w, w_dtype == DSA_F32 ? 4 : 2), DSA_ERR_VALUE, "%s: w misaligned", fn);
+  if (int rc = check_device(fn)) return rc;
+  return launched(fn, dsa::launch_indexer_fp8(q8, q_scale, k8, k_scale, scaling == DSA_MXFP8, w,
+                                              w_dtype, row_starts, seq_lens, T_kv, H_idx,
+                                              row_begin, n_rows, scores, ld_scores,
+                                              (hipStream_t)stream));
+}
+
 int dsa_topk(const float* scores, int64_t ld_scores, int64_t n_rows, int64_t n_cols,
              const int32_t* seq_lens, const int32_t* row_starts, int32_t k, int32_t* indices,
              int64_t ld_indices, int32_t* topk_length, float* values, void* stream) {

@@ -53,6 +53,27 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, c
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// One v_mfma_f32_32x32x64_f8f6f4 on FP8 E4M3 (OCP) operands:
+// D[32x32] = A[32x64] * B[64x32] + C, fp32 accumulation. Lane l supplies A
+// row (l % 32) and B column (l % 32); byte j of its 32 covers
+// k = 32*(j/16) + 16*(l/32) + (j%16). D has the mfma32x32x16 layout. The
+// unscaled instruction is the scaled builtin with constant zero scales.
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(const i32x8& a, const i32x8& b,
+                                                   const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// The block-scaled form (v_mfma_scale_f32_32x32x64_f8f6f4): byte 0 of sa is
+// the E8M0 scale of A row (l % 32) over k block l/32 (k = 32*(l/32) .. +31),
+// byte 0 of sb the scale of B column (l % 32) over the same k block; every
+// product of a block is multiplied by 2^(sa-127) * 2^(sb-127).
+__device__ __forceinline__ f32x16 mfma32x32x64_mxfp8(const i32x8& a, int sa, const i32x8& b,
+                                                     int sb, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
 // ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives 16-bit
 // element (i % 4) of the 8-byte reads of source lanes i/4, 4 + i/4, 8 + i/4
 // and 12 + i/4. With source lane j pointing at row r0 + j/4, column
@@ -101,6 +122,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+// Sum over the two half-waves in one VALU exchange (v_permlane32_swap):
+// lane l < 32 gets a[l] + a[l + 32], lane l >= 32 gets b[l - 32] + b[l].
+__device__ __forceinline__ float halfwave_sums(float a, float b) {
+  const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false,
+                                                  false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, kWave); }
 
 // Number of set bits of `mask` in lanes strictly below the calling lane.

@@ -20,6 +20,12 @@ hipError_t launch_indexer(const void* q, const void* k, const void* w, int w_dty
                           int D, int64_t row_begin, int64_t n_rows, float* scores, int64_t ld,
                           hipStream_t st);
 
+// FP8 indexer: mx selects E8M0 block scales (true) or fp32 per-token descales.
+hipError_t launch_indexer_fp8(const void* q, const void* qs, const void* k, const void* ks,
+                              bool mx, const void* w, int w_dtype, const int32_t* rs,
+                              const int32_t* sl, int64_t T_kv, int H, int64_t row_begin,
+                              int64_t n_rows, float* scores, int64_t ld, hipStream_t st);
+
 hipError_t launch_topk(const float* scores, int64_t ld, int64_t n_rows, int64_t n_cols,
                        const int32_t* seq_lens, const int32_t* row_starts, int k, int32_t* indices,
                        int64_t ld_idx, int32_t* topk_length, float* values, hipStream_t st);

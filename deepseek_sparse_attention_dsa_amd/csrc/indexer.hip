@@ -230,12 +230,11 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
   };
   // Lane l < 32 sums key l of block 0 over both half-waves, lane l >= 32
   // key l - 32 of block 1: one exchange between the half-waves.
+  float* const srow = scores + r * ld;
   auto write_scores = [&](int32_t k0, float p0, float p1) {
-    const float mine = half ? p1 : p0;
-    const float other = half ? p0 : p1;
-    const float score = mine + shfl_xor_f(other, 32);
-    const int64_t j = (int64_t)(k0 + lane) - qstart;
-    if (j >= 0 && j < qlen) scores[r * ld + j] = score;
+    const float score = halfwave_sums(p0, p1);
+    const int32_t j = k0 + lane - qstart;
+    if ((uint32_t)j < (uint32_t)qlen) srow[j] = score;
   };
 
   load_tile(kb);

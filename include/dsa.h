@@ -6,6 +6,8 @@
  *   dsa_ratio_causal_metadata  the same for the ratio-causal mask with query
  *                        causal offsets (compressed keys, split queries)
  *   dsa_indexer_fwd      lightning-indexer scores  sum_h W_h * ReLU(q_h . k)
+ *   dsa_indexer_fwd_fp8  the same scores from FP8 (E4M3) Q and K with
+ *                        per-token descales or per-32 E8M0 block scales
  *   dsa_topk             per-row top-K select, ascending global indices, -1 pad
  *   dsa_sparse_attn_fwd  sparse MQA/GQA attention over the selected KV rows
  *
@@ -51,12 +53,19 @@ typedef enum {
 
 typedef enum { DSA_BF16 = 0, DSA_F32 = 1 } dsa_dtype;
 
+/* Scale forms of FP8 indexer inputs (DSA page section 3, "Precision paths"). */
+typedef enum {
+  DSA_FP8_PER_TOKEN = 0, /* fp32 descales: q [T, H_idx], k [T_kv]            */
+  DSA_MXFP8 = 1          /* E8M0 bytes per 32 elements: q [T, H_idx, D/32],
+                            k [T_kv, D/32]                                  */
+} dsa_fp8_scaling;
+
 /* Message for the last non-OK status returned on the calling thread
  * (thread-local, valid until the next call on that thread). Never NULL. */
 const char* dsa_last_error(void);
 
 /* ABI version of this header (bumped on any signature change). */
-#define DSA_ABI_VERSION 2
+#define DSA_ABI_VERSION 3
 int dsa_abi_version(void);
 
 /* Limits enforced by the host checks. */
@@ -141,6 +150,38 @@ int dsa_indexer_fwd(const void* q_idx, const void* k_idx, const void* w, int32_t
                     const int32_t* row_starts, const int32_t* seq_lens, int64_t T, int64_t T_kv,
                     int32_t H_idx, int32_t D_idx, int64_t row_begin, int64_t n_rows,
                     float* scores, int64_t ld_scores, void* stream);
+
+/*
+ * dsa_indexer_fwd_fp8 - step a1 from FP8 inputs.
+ * DSA page section 3, "Precision paths": Q and K are FP8 E4M3 (the OCP
+ * encoding: bias 7, no infinities, S.1111.111 = NaN, max 448) with either
+ *   DSA_FP8_PER_TOKEN: fp32 descales q_scale [T, H_idx] (one per token and
+ *     head) and k_scale [T_kv] (one per key token), real values being
+ *     E4M3 value * descale; descales must be >= 0;
+ *   DSA_MXFP8: E8M0 scale bytes (2^(byte - 127)) q_scale [T, H_idx, D_idx/32]
+ *     and k_scale [T_kv, D_idx/32], one per 32 consecutive elements of the
+ *     head dim; real values being E4M3 value * 2^(byte - 127).
+ * The scores are dsa_indexer_fwd's definition on those real values, with the
+ * same row, column, mask and buffer conventions:
+ *   scores[t - row_begin, j] = sum_h W[t, h] * max(0, Q[t, h, :] . K[row_starts[t] + j, :])
+ *   q8          device uint8 E4M3 [T, H_idx, D_idx], 16-byte aligned
+ *   k8          device uint8 E4M3 [T_kv, D_idx], 16-byte aligned
+ *   q_scale, k_scale  device, layout by `scaling`; k_scale 4-byte aligned
+ *   w, w_dtype  device [T, H_idx], DSA_BF16 or DSA_F32 (W as in
+ *               dsa_indexer_fwd; a caller may pre-multiply the query
+ *               descales into fp32 W and pass unit q descales)
+ *   D_idx       128 (the section's head-dim constraint); H_idx in [1, 64]
+ *   other arguments as for dsa_indexer_fwd.
+ * E4M3 products are exact; the MFMA sums them in fp32 (per 32-element block
+ * for MXFP8), then the epilogue is fp32. NaN codes give unspecified scores.
+ * Errors: as dsa_indexer_fwd, plus DSA_ERR_VALUE for an unknown scaling or
+ * D_idx != 128.
+ */
+int dsa_indexer_fwd_fp8(const void* q8, const void* q_scale, const void* k8, const void* k_scale,
+                        int32_t scaling, const void* w, int32_t w_dtype,
+                        const int32_t* row_starts, const int32_t* seq_lens, int64_t T,
+                        int64_t T_kv, int32_t H_idx, int32_t D_idx, int64_t row_begin,
+                        int64_t n_rows, float* scores, int64_t ld_scores, void* stream);
 
 /*
  * dsa_topk - steps a2 + a3, radix top-K with per-row length, compaction and

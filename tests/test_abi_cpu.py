@@ -31,6 +31,8 @@ ATTN_BASE = dict(q=FAKE, Tq=16, H=16, Dqk=576, k=FAKE, Tkv=16, ldk=576, v=None, 
                  idx=FAKE, ldi=64, kw=64, tl=None, sink=None, scale=0.04, out=FAKE, lse=FAKE,
                  mx=None, stream=None)
 META_BASE = dict(cu=FAKE, n_seq=1, T=4, rs=FAKE, sl=FAKE, stream=None)
+F8_BASE = dict(q=FAKE, qs=FAKE2, k=FAKE, ks=FAKE2, sc=1, w=FAKE, wd=0, rs=FAKE, sl=FAKE, T=256,
+               Tkv=256, H=64, D=128, rb=0, nr=256, scores=FAKE, ld=256, stream=None)
 RMETA_BASE = dict(cq=FAKE, ck=FAKE2, off=None, n_seq=2, T=4, ratio=4, rs=FAKE, sl=FAKE,
                   stream=None)
 
@@ -43,11 +45,14 @@ ORDER = {
              "sink", "scale", "out", "lse", "mx", "stream"],
     "meta": ["cu", "n_seq", "T", "rs", "sl", "stream"],
     "rmeta": ["cq", "ck", "off", "n_seq", "T", "ratio", "rs", "sl", "stream"],
+    "f8": ["q", "qs", "k", "ks", "sc", "w", "wd", "rs", "sl", "T", "Tkv", "H", "D", "rb", "nr",
+           "scores", "ld", "stream"],
 }
 BASE = {"topk": TOPK_BASE, "idx": IDX_BASE, "attn": ATTN_BASE, "meta": META_BASE,
-        "rmeta": RMETA_BASE}
+        "rmeta": RMETA_BASE, "f8": F8_BASE}
 FN = {"topk": "dsa_topk", "idx": "dsa_indexer_fwd", "attn": "dsa_sparse_attn_fwd",
-      "meta": "dsa_packed_metadata", "rmeta": "dsa_ratio_causal_metadata"}
+      "meta": "dsa_packed_metadata", "rmeta": "dsa_ratio_causal_metadata",
+      "f8": "dsa_indexer_fwd_fp8"}
 
 CASES = [
     # top-K
@@ -95,6 +100,15 @@ CASES = [
     ("rmeta", dict(sl=None), EVALUE),
     ("rmeta", dict(T=0, cq=None, ck=None, rs=None, sl=None), OK),
     ("rmeta", dict(), ERUNTIME), ("rmeta", dict(off=FAKE2, ratio=1), ERUNTIME),
+    # FP8 indexer
+    ("f8", dict(wd=3), ETYPE), ("f8", dict(sc=2), EVALUE), ("f8", dict(sc=-1), EVALUE),
+    ("f8", dict(D=64), EVALUE), ("f8", dict(H=0), EVALUE), ("f8", dict(H=65), EVALUE),
+    ("f8", dict(qs=None), EVALUE), ("f8", dict(ks=None), EVALUE), ("f8", dict(k=FAKE + 8), EVALUE),
+    ("f8", dict(ks=FAKE2 + 2), EVALUE), ("f8", dict(sc=0, qs=FAKE2 + 2), EVALUE),
+    ("f8", dict(sc=1, qs=FAKE2 + 1), ERUNTIME), ("f8", dict(ld=250), EVALUE),
+    ("f8", dict(rb=100, nr=200), EVALUE), ("f8", dict(Tkv=-1), EVALUE),
+    ("f8", dict(nr=0, q=None, k=None), OK), ("f8", dict(Tkv=0, q=None), OK),
+    ("f8", dict(), ERUNTIME), ("f8", dict(sc=0, wd=1), ERUNTIME),
 ]
 
 _CHILD = r"""
@@ -138,8 +152,9 @@ def _declared_functions():
 
 def test_header_declares_the_path():
     names = _declared_functions()
-    for fn in ["dsa_packed_metadata", "dsa_ratio_causal_metadata", "dsa_indexer_fwd", "dsa_topk",
-               "dsa_sparse_attn_fwd", "dsa_last_error", "dsa_abi_version"]:
+    for fn in ["dsa_packed_metadata", "dsa_ratio_causal_metadata", "dsa_indexer_fwd",
+               "dsa_indexer_fwd_fp8", "dsa_topk", "dsa_sparse_attn_fwd", "dsa_last_error",
+               "dsa_abi_version"]:
         assert fn in names
 
 

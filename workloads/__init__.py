@@ -13,6 +13,7 @@ from .gen import (  # noqa: F401
     make_config,
     make_custom,
     make_split,
+    quantize_fp8,
     qsa_routes,
     SplitWorkload,
 )

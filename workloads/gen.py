@@ -45,6 +45,11 @@ CONFIGS = {
     # top-512 (the DSA page's ratio-4 indexer example).
     7: dict(name="ratio4_T65536_K512", split=True, q_lens=[65536], k_lens=[16384],
             offsets=None, ratio=4, H=64, D_qk=576, D_v=512, H_idx=64, D_idx=128, topk=512),
+    # Workloads 2 and 4 with FP8 indexer inputs (same seeds and bf16 values,
+    # quantised by quantize_fp8): E8M0 block scales, or fp32 per-token descales.
+    8: dict(name="single_T4096_mxfp8", base=2, indexer_fp8="mx"),
+    9: dict(name="long_T65536_mxfp8", base=4, indexer_fp8="mx"),
+    10: dict(name="long_T65536_fp8_per_token", base=4, indexer_fp8="per_token"),
 }
 
 
@@ -180,6 +185,14 @@ def make_config(i: int, device="cpu", seed=None, stress=False):
     """One of the named workloads (a Workload, or a SplitWorkload for the
     split-query / compressed-key ones); seed defaults to 1000 + i."""
     c = dict(CONFIGS[i])
+    if c.get("indexer_fp8"):
+        wl = make_config(c["base"], device=device, seed=seed, stress=stress)
+        wl.name = c["name"] + ("_stress" if stress else "")
+        block = 32 if c["indexer_fp8"] == "mx" else None
+        q8, qs = quantize_fp8(wl.q_idx, block)
+        k8, ks = quantize_fp8(wl.k_idx, block)
+        wl.extra["fp8"] = dict(scaling=c["indexer_fp8"], q8=q8, q_scale=qs, k8=k8, k_scale=ks)
+        return wl
     seed = 1000 + i if seed is None else int(seed)
     if c.get("split"):
         assert not stress
@@ -261,3 +274,24 @@ def make_split(q_lens, k_lens, offsets, ratio, H_idx=64, D_idx=128, H=0, D_qk=57
                          H=H, D_qk=D_qk, D_v=D_v, q=q, kv=kv, H_idx=H_idx, D_idx=D_idx,
                          q_idx=q_idx, k_idx=k_idx, w=w, sink=sk, topk=int(topk),
                          scale=1.0 / math.sqrt(D_qk), seed=int(seed))
+
+
+def quantize_fp8(x: torch.Tensor, block: Optional[int] = None):
+    """E4M3 bytes and scales of x (bf16/fp32 [..., D]) through torch's float8 casts.
+
+    block None: one fp32 descale per row of the last dim, amax / 448 (1.0 for
+    an all-zero row). block 32: one E8M0 byte per 32 elements, the smallest
+    power of two 2^e >= amax / 448 (code e + 127). Returns (uint8 codes,
+    scales): scales fp32 [...] or uint8 [..., D / block].
+    """
+    xf = x.float()
+    if block is None:
+        amax = xf.abs().amax(dim=-1)
+        scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        q = (xf / scale[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        return q, scale
+    xb = xf.reshape(*xf.shape[:-1], -1, block)
+    amax = xb.abs().amax(dim=-1)
+    e = torch.ceil(torch.log2(torch.clamp(amax / 448.0, min=2.0 ** -127))).clamp(-127, 127)
+    q = (xb / torch.exp2(e)[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    return q.reshape(x.shape), (e + 127).to(torch.uint8)
