@@ -140,6 +140,23 @@ __device__ __forceinline__ uint32_t popc_below(uint64_t mask) {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// Raw buffer descriptor (word 3 = 0x00020000 on gfx9: 32-bit data, stride 0)
+// of `bytes` bytes at `base`, which must be the same in every lane of the
+// wave: it is taken from the first active lane. The hardware range check
+// drops stores at byte offsets >= bytes and reads such loads as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint64_t pu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(uintptr_t)pu, 0,
+                                           __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
+}
+
+__device__ __forceinline__ void buffer_store_f32(float v, __amdgpu_buffer_rsrc_t rsrc,
+                                                 uint32_t byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), rsrc, (int)byte_off, 0, 0);
+}
+
 __device__ __forceinline__ u32x4 load16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

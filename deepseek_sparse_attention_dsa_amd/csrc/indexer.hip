@@ -229,52 +229,47 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
     }
   };
   // Lane l < 32 sums key l of block 0 over both half-waves, lane l >= 32
-  // key l - 32 of block 1: one exchange between the half-waves.
-  float* const srow = scores + r * ld;
+  // key l - 32 of block 1: one exchange between the half-waves. Scores go
+  // through a buffer descriptor of the wave's row whose range is the row's
+  // valid columns: stores of other columns are dropped by the hardware range
+  // check, so the tile loop has no branches.
+  const __amdgpu_buffer_rsrc_t srow = raw_buffer(scores + r * ld, (uint32_t)qlen * 4u);
   auto write_scores = [&](int32_t k0, float p0, float p1) {
-    const float score = halfwave_sums(p0, p1);
-    const int32_t j = k0 + lane - qstart;
-    if ((uint32_t)j < (uint32_t)qlen) srow[j] = score;
+    buffer_store_f32(halfwave_sums(p0, p1), srow,
+                     (uint32_t)(k0 + lane - qstart) * 4u);  // negative: dropped
   };
 
+  // Every wave runs every tile of the workgroup's key range (a row's keys
+  // outside its own range are computed and their stores dropped). The first
+  // pending write targets columns before the row, so it is dropped too.
   load_tile(kb);
   store_tile(0);
   __syncthreads();
   int buf = 0;
-  bool pend = false;      // block 1 of tile pend_k0 awaits its epilogue
-  int32_t pend_k0 = 0;
-  float pend_p0 = 0.0f;   // its block-0 partial
+  int32_t pend_k0 = qstart - 64;  // block 1 of tile pend_k0 awaits its epilogue
+  float pend_p0 = 0.0f;           // its block-0 partial
   for (int32_t k0 = kb; k0 < ke; k0 += kIdxTile) {
-    const bool more = k0 + kIdxTile < ke;  // uniform
-    if (more) load_tile(k0 + kIdxTile);
+    load_tile(k0 + kIdxTile);  // zeroed past the range, so the last one is harmless
+    const unsigned char* kt = ktile + buf * TILE_B;
+    // Each group pairs a block's MFMAs with the previous block's epilogue;
+    // the fences keep the scheduler from filling the VALU slots with the
+    // epilogue that waits on these very MFMAs.
+    block_mfma(kt, 0, acc0);
+    const float p1_prev = epilogue(acc1);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    write_scores(pend_k0, pend_p0, p1_prev);
+    block_mfma(kt, 1, acc1);
+    pend_p0 = epilogue(acc0);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    pend_k0 = k0;
 
-    // Keys of this tile that belong to the query: [qstart, qstart + qlen).
-    const bool any = live && k0 < qstart + qlen && k0 + kIdxTile > qstart;  // wave-uniform
-    if (any) {
-      const unsigned char* kt = ktile + buf * TILE_B;
-      block_mfma(kt, 0, acc0);
-      const float p1_prev = epilogue(acc1);
-      interleave();
-      asm volatile("" ::"v"(p1_prev));  // keep the epilogue here, not sunk into the branch
-      if (pend) write_scores(pend_k0, pend_p0, p1_prev);
-      block_mfma(kt, 1, acc1);
-      const float p0 = epilogue(acc0);
-      interleave();
-      pend = true;
-      pend_k0 = k0;
-      pend_p0 = p0;
-    } else if (pend) {
-      write_scores(pend_k0, pend_p0, epilogue(acc1));
-      pend = false;
-    }
-
-    if (more) {
-      store_tile(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-    }
+    store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
   }
-  if (pend) write_scores(pend_k0, pend_p0, epilogue(acc1));
+  write_scores(pend_k0, pend_p0, epilogue(acc1));
 }
 
 template <int D, int MB>

@@ -223,64 +223,58 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   };
   // Lane l < 32 sums key l of block 0 over both half-waves, lane l >= 32 key
   // l - 32 of block 1; the key descale (per-token form) multiplies the sum.
-  float* const srow = scores + r * ld;
+  // Scores go through a buffer descriptor of the wave's row whose range is
+  // the row's valid columns: stores of other columns are dropped by the
+  // hardware range check, so the tile loop has no branches.
+  const __amdgpu_buffer_rsrc_t srow = raw_buffer(scores + r * ld, (uint32_t)qlen * 4u);
   auto write_scores = [&](int32_t k0, float p0, float p1, float kscl) {
     float score = halfwave_sums(p0, p1);
     if constexpr (!MX) score *= kscl;
-    const int32_t j = k0 + lane - qstart;
-    if ((uint32_t)j < (uint32_t)qlen) srow[j] = score;
+    buffer_store_f32(score, srow, (uint32_t)(k0 + lane - qstart) * 4u);  // negative: dropped
   };
 
+  // Every wave runs every tile of the workgroup's key range (a row's keys
+  // outside its own range are computed and their stores dropped). The first
+  // pending write targets columns before the row, so it is dropped too.
   load_tile(kb);
   store_tile(0);
   __syncthreads();
   int buf = 0;
-  bool pend = false;
-  int32_t pend_k0 = 0;
+  int32_t pend_k0 = qstart - 64;
   float pend_p0 = 0.0f;
   float pend_ks = 0.0f;  // descale of key pend_k0 + lane
   for (int32_t k0 = kb; k0 < ke; k0 += kF8Tile) {
-    const bool more = k0 + kF8Tile < ke;  // uniform
-    if (more) load_tile(k0 + kF8Tile);
+    load_tile(k0 + kF8Tile);  // zeroed past the range, so the last one is harmless
 
     BOp cur, nxt;
     read_block(buf, 0, cur);
 #pragma unroll
     for (int pr = 0; pr < kF8Pairs; ++pr) {
       const int32_t kp = k0 + 64 * pr;
-      const bool any = live && kp < qstart + qlen && kp + 64 > qstart;  // wave-uniform
-      if (any) {
-        const float kscl = MX ? 0.0f : __uint_as_float(kscale[buf][64 * pr + lane]);
-        read_block(buf, 2 * pr + 1, nxt);
-        block_mfma(cur, acc0);
-        const float p1_prev = epilogue(acc1);
-        interleave();
-        asm volatile("" ::"v"(p1_prev));  // keep the epilogue here, not sunk into the branch
-        if (pend) write_scores(pend_k0, pend_p0, p1_prev, pend_ks);
-        if (pr + 1 < kF8Pairs) read_block(buf, 2 * pr + 2, cur);
-        block_mfma(nxt, acc1);
-        const float p0 = epilogue(acc0);
-        interleave();
-        pend = true;
-        pend_k0 = kp;
-        pend_p0 = p0;
-        pend_ks = kscl;
-      } else {
-        if (pend) {
-          write_scores(pend_k0, pend_p0, epilogue(acc1), pend_ks);
-          pend = false;
-        }
-        if (pr + 1 < kF8Pairs) read_block(buf, 2 * pr + 2, cur);
-      }
+      const float kscl = MX ? 0.0f : __uint_as_float(kscale[buf][64 * pr + lane]);
+      read_block(buf, 2 * pr + 1, nxt);
+      // Each group pairs a block's MFMAs with the previous block's epilogue;
+      // the fences keep the scheduler from filling the VALU slots with the
+      // epilogue that waits on these very MFMAs.
+      block_mfma(cur, acc0);
+      const float p1_prev = epilogue(acc1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      write_scores(pend_k0, pend_p0, p1_prev, pend_ks);
+      if (pr + 1 < kF8Pairs) read_block(buf, 2 * pr + 2, cur);
+      block_mfma(nxt, acc1);
+      pend_p0 = epilogue(acc0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      pend_k0 = kp;
+      pend_ks = kscl;
     }
 
-    if (more) {
-      store_tile(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-    }
+    store_tile(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
   }
-  if (pend) write_scores(pend_k0, pend_p0, epilogue(acc1), pend_ks);
+  write_scores(pend_k0, pend_p0, epilogue(acc1), pend_ks);
 }
 
 template <int MB, bool MX>
