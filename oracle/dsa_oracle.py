@@ -239,6 +239,39 @@ def topk(scores, seq_lens, k: int, row_starts=None, n_cols=None):
     return idx.astype(np.int32), length.astype(np.int32)
 
 
+def topk_softmax(scores, seq_lens, k: int, row_starts=None, n_cols=None):
+    """Top-K with its logits, softmax and log-sum-exp: the outputs of the
+    combined indexer + top-K path.
+
+    DSA page section 4 (indices, logits of the selected slots, softmax over
+    them, LSE; padded slots -1 / -inf) with the selected set and slot order of
+    topk(); section 6 defines the softmax: predict[i] = softmax_i of the
+    indexer score at the selected index i. lse is the natural log of the sum
+    of exp(logit) over the selected slots; softmax = exp(logit - lse),
+    0 in padded slots; a row with no selected slot has lse = +inf (the
+    pages' empty-row convention for LSE).
+    Returns (indices int32, lengths int32, logits, softmax, lse) with float64
+    values.
+    """
+    scores = np.asarray(scores, dtype=np.float64)
+    idx, length = topk(scores, seq_lens, k, row_starts=row_starts, n_cols=n_cols)
+    n_rows = scores.shape[0]
+    logits = np.full((n_rows, k), NEG_INF)
+    soft = np.zeros((n_rows, k))
+    lse = np.full(n_rows, np.inf)
+    for r in range(n_rows):
+        m = int(length[r])
+        if m == 0:
+            continue
+        base = 0 if row_starts is None else int(row_starts[r])
+        v = scores[r, idx[r, :m].astype(np.int64) - base]
+        top = v.max()
+        lse[r] = top + np.log(np.exp(v - top).sum())
+        logits[r, :m] = v
+        soft[r, :m] = np.exp(v - lse[r])
+    return idx, length, logits, soft, lse
+
+
 # ---------------------------------------------------------------------------
 # Steps a4 / a5: sparse attention forward
 # ---------------------------------------------------------------------------

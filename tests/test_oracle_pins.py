@@ -530,6 +530,61 @@ def test_topk_invariants_random():
                 assert tie_sel.max() < tie_uns.min()
 
 
+# ------------------------------------------------- top-K softmax and LSE --
+
+def test_topk_softmax_matches_scipy_and_indexer_recompute():
+    from scipy.special import logsumexp, softmax
+    rng = np.random.default_rng(60)
+    T, H, D, K = 40, 3, 5, 7
+    q = rng.standard_normal((T, H, D))
+    k = rng.standard_normal((T, D))
+    w = rng.standard_normal((T, H))
+    cu = np.array([0, 13, 13, 40])
+    st, sl = O.packed_metadata(cu, T)
+    sc = O.indexer_scores(q, k, w, st, sl, np.arange(T), width=T)
+    idx, ln, logits, soft, lse = O.topk_softmax(sc, sl, K, row_starts=st, n_cols=T)
+    for t in range(T):
+        m = int(ln[t])
+        sel = idx[t, :m].astype(np.int64)
+        # section 6: softmax of the indexer score recomputed at the selected keys
+        rec = np.array([w[t] @ np.maximum(q[t] @ k[j], 0.0) for j in sel])
+        np.testing.assert_allclose(logits[t, :m], rec, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(soft[t, :m], softmax(rec), rtol=1e-12, atol=1e-15)
+        assert abs(lse[t] - logsumexp(rec)) < 1e-12
+        assert np.all(logits[t, m:] == -np.inf) and np.all(soft[t, m:] == 0.0)
+        assert abs(soft[t, :m].sum() - 1.0) < 1e-12
+
+
+def test_topk_softmax_closed_forms():
+    # equal logits: softmax 1/m and lse = v + ln m; one column: softmax 1, lse = v;
+    # an empty row: lse = +inf, no slot
+    x = np.array([[2.5] * 6, [-1.0, 0, 0, 0, 0, 0], [9.0] * 6])
+    idx, ln, logits, soft, lse = O.topk_softmax(x, [6, 1, 0], 4)
+    np.testing.assert_allclose(soft[0], 0.25)
+    assert abs(lse[0] - (2.5 + math.log(4))) < 1e-14
+    assert soft[1].tolist() == [1.0, 0, 0, 0] and lse[1] == -1.0
+    assert ln[2] == 0 and lse[2] == np.inf and np.all(idx[2] == -1)
+
+
+def test_planted_topk_softmax_mistakes_fail():
+    # Normalising over the whole row instead of the selected slots, or an LSE
+    # that drops its max term, break the pins above (softmax sums to 1 over
+    # the selected slots; lse equals scipy's logsumexp of the selected logits).
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(61)
+    lens = [30, 12, 9]
+    x = rng.standard_normal((3, 30)) * 3
+    idx, ln, logits, soft, lse = O.topk_softmax(x, lens, 8)
+    for r in range(3):
+        m = int(ln[r])
+        v = logits[r, :m]
+        assert abs(lse[r] - logsumexp(v)) < 1e-12
+        whole = logsumexp(x[r, :lens[r]])
+        assert abs(np.exp(v - whole).sum() - 1.0) > 1e-3        # row-normalised: not 1
+        no_max = np.log(np.exp(v - v.max()).sum())
+        assert abs(no_max - logsumexp(v)) > 1e-3                 # max term dropped
+
+
 # --------------------------------------------------------------- attention --
 
 def test_attention_golden():
