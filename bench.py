@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=2, help="workload 1..10 (default: 2)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--fused", action="store_true",
+                   help="one combined indexer + top-K launch instead of score chunks + dsa_topk "
+                        "(rows of <= 4096 columns)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -262,11 +265,15 @@ def main():
         return dsa.dsa_packed_metadata(wl.cu_seqlens, T, row_starts=row_starts, seq_lens=seq_lens)
 
     rs, sl = metadata()
+    fused = has_indexer and args.fused
+    if fused and max_len > dsa.DSA_FUSED_MAX_COLS:
+        raise SystemExit(f"--fused takes rows of at most {dsa.DSA_FUSED_MAX_COLS} columns")
     if fp8:
         fp8_scaling = dsa.DSA_MXFP8 if fp8["scaling"] == "mx" else dsa.DSA_FP8_PER_TOKEN
     rows_per_chunk = dsa.chunk_rows(T, max_len)
     ld = max(4, (max_len + 3) // 4 * 4)
-    scores = torch.empty((min(rows_per_chunk, T), ld), dtype=torch.float32, device=dev)
+    scores = (None if fused else
+              torch.empty((min(rows_per_chunk, T), ld), dtype=torch.float32, device=dev))
     indices = torch.empty((T, K), dtype=torch.int32, device=dev) if has_indexer else wl.routes
     topk_length = torch.empty((T,), dtype=torch.int32, device=dev) if has_indexer else None
     out = torch.empty((T, wl.H, wl.D_v), dtype=torch.bfloat16, device=dev)
@@ -283,7 +290,16 @@ def main():
         if timed:
             e0.record(stream)
         metadata(rs, sl)
-        if has_indexer:
+        if has_indexer and fused:
+            if fp8:
+                dsa.dsa_indexer_topk_fused(fp8["q8"], fp8["k8"], wl.w, rs, sl, K, max_len,
+                                           q_scale=fp8["q_scale"], k_scale=fp8["k_scale"],
+                                           fp8_scaling=fp8_scaling, indices=indices,
+                                           topk_length=topk_length)
+            else:
+                dsa.dsa_indexer_topk_fused(wl.q_idx, wl.k_idx, wl.w, rs, sl, K, max_len,
+                                           indices=indices, topk_length=topk_length)
+        elif has_indexer:
             for r0 in range(0, T, rows_per_chunk):
                 n = min(rows_per_chunk, T - r0)
                 if fp8:
@@ -334,7 +350,8 @@ def main():
         stages["metadata+indexer+topk"] = {"ms": float(np.mean(idx_ms)), "rows_per_s": rows_per_s,
                                            "indexer_algorithmic_flop": cnt["indexer_flop"],
                                            "topk_algorithmic_bytes": cnt["topk_bytes"],
-                                           "chunks": math.ceil(T / rows_per_chunk)}
+                                           "chunks": 0 if fused else math.ceil(T / rows_per_chunk),
+                                           "combined_launch": fused}
 
     roofline = {"kernel": "sparse_attn_kernel", "bound": "mfma", "achieved": attn_tflops,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

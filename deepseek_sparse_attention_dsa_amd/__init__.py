@@ -25,6 +25,7 @@ __all__ = [
     "load_library", "library_path", "dsa_abi_version", "dsa_last_error",
     "dsa_packed_metadata", "dsa_ratio_causal_metadata", "dsa_indexer_fwd",
     "dsa_indexer_fwd_fp8", "DSA_FP8_PER_TOKEN", "DSA_MXFP8", "dsa_topk",
+    "dsa_indexer_topk_fused", "DSA_FUSED_MAX_COLS",
     "dsa_sparse_attn_fwd",
     "indexer_topk", "chunk_rows",
 ]
@@ -35,6 +36,8 @@ DSA_FP8_PER_TOKEN, DSA_MXFP8 = 0, 1
 DSA_MAX_TOPK = 2048
 DSA_TOPK_MAX_COLS = 65536
 DSA_MAX_HEADS = 128
+DSA_FUSED_MAX_COLS = 4096
+DSA_INDEXER_BF16, DSA_INDEXER_FP8, DSA_INDEXER_MXFP8 = 0, 1, 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -53,6 +56,9 @@ _SIGNATURES = {
                          _P], ctypes.c_int),
     "dsa_indexer_fwd_fp8": ([_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I64, _I64, _I32, _I32,
                              _I64, _I64, _P, _I64, _P], ctypes.c_int),
+    "dsa_indexer_topk_fused": ([_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I64, _I64, _I32, _I32,
+                                _I64, _I64, _I64, _I32, _P, _I64, _P, _P, _P, _P, _P],
+                               ctypes.c_int),
     "dsa_topk": ([_P, _I64, _I64, _I64, _P, _P, _I32, _P, _I64, _P, _P, _P], ctypes.c_int),
     "dsa_sparse_attn_fwd": ([_P, _I64, _I32, _I32, _P, _I64, _I64, _P, _I64, _I32, _P, _I64,
                              _I32, _P, _P, _F32, _P, _P, _P, _P], ctypes.c_int),
@@ -392,6 +398,76 @@ def dsa_sparse_attn_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor
     return out, lse, max_logits
 
 
+def dsa_indexer_topk_fused(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
+                           row_starts: torch.Tensor, seq_lens: torch.Tensor, k: int, n_cols: int,
+                           q_scale: Optional[torch.Tensor] = None,
+                           k_scale: Optional[torch.Tensor] = None,
+                           fp8_scaling: Optional[int] = None, row_begin: int = 0,
+                           n_rows: Optional[int] = None, indices: Optional[torch.Tensor] = None,
+                           topk_length: Optional[torch.Tensor] = None, return_logits: bool = False,
+                           return_softmax: bool = False, return_lse: bool = False, stream=None):
+    """Indexer scores + top-k in one launch (rows of at most 4096 columns).
+
+    Returns (indices int32 [n_rows, k], topk_length int32 [n_rows], logits |
+    None, softmax | None, lse | None). bf16 q_idx / k_idx, or FP8 ones with
+    q_scale, k_scale and fp8_scaling as dsa_indexer_fwd_fp8 takes them.
+    """
+    if not isinstance(w, torch.Tensor) or w.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"w must be a bfloat16 or float32 tensor (got {getattr(w, 'dtype', w)})")
+    dev = q_idx.device
+    fp8 = isinstance(q_idx, torch.Tensor) and q_idx.dtype in (torch.uint8, torch.float8_e4m3fn)
+    if fp8:
+        if fp8_scaling not in (DSA_FP8_PER_TOKEN, DSA_MXFP8):
+            raise ValueError("FP8 inputs need fp8_scaling DSA_FP8_PER_TOKEN or DSA_MXFP8")
+        precision = DSA_INDEXER_FP8 if fp8_scaling == DSA_FP8_PER_TOKEN else DSA_INDEXER_MXFP8
+        q_idx = _fp8_bytes(q_idx, "q_idx", dev)
+        k_idx = _fp8_bytes(k_idx, "k_idx", dev)
+        sdt = torch.float32 if fp8_scaling == DSA_FP8_PER_TOKEN else torch.uint8
+        q_scale = _need(q_scale.view(torch.uint8) if q_scale is not None and
+                        q_scale.dtype == torch.float8_e8m0fnu else q_scale, "q_scale", sdt, dev)
+        k_scale = _need(k_scale.view(torch.uint8) if k_scale is not None and
+                        k_scale.dtype == torch.float8_e8m0fnu else k_scale, "k_scale", sdt, dev)
+    else:
+        precision = DSA_INDEXER_BF16
+        q_idx = _need(q_idx, "q_idx", torch.bfloat16)
+        k_idx = _need(k_idx, "k_idx", torch.bfloat16, dev)
+    w = _need(w, "w", w.dtype, dev)
+    row_starts = _need(row_starts, "row_starts", torch.int32, dev)
+    seq_lens = _need(seq_lens, "seq_lens", torch.int32, dev)
+    if q_idx.dim() != 3 or k_idx.dim() != 2 or w.dim() != 2:
+        raise ValueError("expected q_idx [T,H,D], k_idx [T_kv,D], w [T,H]")
+    T, H, D = q_idx.shape
+    T_kv = k_idx.shape[0]
+    if k_idx.shape[1] != D or w.shape != (T, H):
+        raise ValueError(f"shape mismatch: q_idx {tuple(q_idx.shape)}, k_idx "
+                         f"{tuple(k_idx.shape)}, w {tuple(w.shape)}")
+    if fp8:
+        nb = D // 32
+        qs_shape = (T, H) if fp8_scaling == DSA_FP8_PER_TOKEN else (T, H, nb)
+        ks_shape = (T_kv,) if fp8_scaling == DSA_FP8_PER_TOKEN else (T_kv, nb)
+        if tuple(q_scale.shape) != qs_shape or tuple(k_scale.shape) != ks_shape:
+            raise ValueError("scale shapes do not match q_idx / k_idx")
+    if n_rows is None:
+        n_rows = T - row_begin
+    indices = (torch.empty((n_rows, k), dtype=torch.int32, device=dev) if indices is None
+               else _out(indices, "indices", torch.int32, dev))
+    topk_length = (torch.empty((n_rows,), dtype=torch.int32, device=dev) if topk_length is None
+                   else _out(topk_length, "topk_length", torch.int32, dev))
+    ld = indices.stride(0)
+    logits = (torch.empty((n_rows, ld), dtype=torch.float32, device=dev)[:, :k]
+              if return_logits else None)
+    softmax = (torch.empty((n_rows, ld), dtype=torch.float32, device=dev)[:, :k]
+               if return_softmax else None)
+    lse = torch.empty((n_rows,), dtype=torch.float32, device=dev) if return_lse else None
+    lib = load_library()
+    _check(lib.dsa_indexer_topk_fused(
+        _ptr(q_idx), _ptr(q_scale) if fp8 else None, _ptr(k_idx), _ptr(k_scale) if fp8 else None,
+        precision, _ptr(w), DSA_BF16 if w.dtype == torch.bfloat16 else DSA_F32, _ptr(row_starts),
+        _ptr(seq_lens), T, T_kv, H, D, row_begin, n_rows, int(n_cols), int(k), _ptr(indices), ld,
+        _ptr(topk_length), _ptr(logits), _ptr(softmax), _ptr(lse), _stream(stream)))
+    return indices, topk_length, logits, softmax, lse
+
+
 # Score-buffer cap per chunk of rows (2 GiB, the cap the NeMo cudnn_dsa page
 # applies to its score / top-K scratch).
 SCORE_CHUNK_BYTES = 2 * 1024 * 1024 * 1024
@@ -408,7 +484,8 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
                  rows_per_chunk: Optional[int] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
                  ratio: int = 1, q_causal_offsets: Optional[torch.Tensor] = None,
                  q_scale: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
-                 fp8_scaling: Optional[int] = None, stream=None):
+                 fp8_scaling: Optional[int] = None, fused: Optional[bool] = None,
+                 return_softmax: bool = False, stream=None):
     """Metadata + indexer scores + top-K over all rows, in score chunks.
 
     Returns (indices int32 [T, k] global ascending with -1 suffix,
@@ -420,6 +497,11 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
     cu_seqlens); max_seqlen is then the longest key segment (default T_kv).
     FP8 inputs (q_idx / k_idx as uint8 or float8_e4m3fn) take q_scale,
     k_scale and fp8_scaling as dsa_indexer_fwd_fp8 does.
+    fused=True (or return_softmax=True) replaces the score chunks by one
+    dsa_indexer_topk_fused launch (rows of at most DSA_FUSED_MAX_COLS
+    columns, no score buffer); only that path gives return_softmax, which
+    returns (indices, topk_length, logits, softmax, lse). The score-chunk
+    path is the default: on MI355X it is the faster of the two.
     """
     fp8 = q_idx.dtype in (torch.uint8, torch.float8_e4m3fn)
     if fp8 and (q_scale is None or k_scale is None or fp8_scaling is None):
@@ -436,6 +518,19 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
     else:
         width = T if max_seqlen is None else int(max_seqlen)
         row_starts, seq_lens = dsa_packed_metadata(cu_seqlens, T, stream=stream)
+    if fused is None:
+        fused = return_softmax
+    if return_softmax and not fused:
+        raise ValueError("return_softmax needs the fused path (rows of at most "
+                         f"{DSA_FUSED_MAX_COLS} columns)")
+    if fused:
+        if width > DSA_FUSED_MAX_COLS:
+            raise ValueError(f"the fused path takes rows of at most {DSA_FUSED_MAX_COLS} columns")
+        res = dsa_indexer_topk_fused(q_idx, k_idx, w, row_starts, seq_lens, k, max(width, 1),
+                                     q_scale=q_scale, k_scale=k_scale, fp8_scaling=fp8_scaling,
+                                     return_logits=return_softmax, return_softmax=return_softmax,
+                                     return_lse=return_softmax, stream=stream)
+        return res if return_softmax else res[:2]
     rows = chunk_rows(T, width) if rows_per_chunk is None else int(rows_per_chunk)
     indices = torch.empty((T, k), dtype=torch.int32, device=dev)
     topk_length = torch.empty((T,), dtype=torch.int32, device=dev)

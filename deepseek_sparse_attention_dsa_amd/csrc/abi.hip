@@ -10,6 +10,7 @@
 
 #include "dsa.h"
 #include "dsa_launch.h"
+#include "dsa_select.h"
 
 namespace {
 
@@ -159,6 +160,57 @@ int dsa_indexer_fwd_fp8(const void* q8, const void* q_scale, const void* k8, con
                                               w_dtype, row_starts, seq_lens, T_kv, H_idx,
                                               row_begin, n_rows, scores, ld_scores,
                                               (hipStream_t)stream));
+}
+
+int dsa_indexer_topk_fused(const void* q_idx, const void* q_scale, const void* k_idx,
+                           const void* k_scale, int32_t precision, const void* w,
+                           int32_t w_dtype, const int32_t* row_starts, const int32_t* seq_lens,
+                           int64_t T, int64_t T_kv, int32_t H_idx, int32_t D_idx,
+                           int64_t row_begin, int64_t n_rows, int64_t n_cols, int32_t k,
+                           int32_t* indices, int64_t ld_indices, int32_t* topk_length,
+                           float* logits, float* softmax, float* lse, void* stream) {
+  const char* fn = "dsa_indexer_topk_fused";
+  REQUIRE(w_dtype == DSA_BF16 || w_dtype == DSA_F32, DSA_ERR_TYPE,
+          "%s: w_dtype must be DSA_BF16 or DSA_F32 (got %d)", fn, w_dtype);
+  REQUIRE(precision == DSA_INDEXER_BF16 || precision == DSA_INDEXER_FP8 ||
+              precision == DSA_INDEXER_MXFP8,
+          DSA_ERR_VALUE, "%s: unknown precision %d", fn, precision);
+  const bool fp8 = precision != DSA_INDEXER_BF16;
+  REQUIRE(H_idx >= 1 && H_idx <= 64, DSA_ERR_VALUE, "%s: H_idx must be in [1, 64] (got %d)", fn,
+          H_idx);
+  REQUIRE(D_idx == 128 || (!fp8 && D_idx == 64), DSA_ERR_VALUE,
+          "%s: D_idx must be 128 (or 64 for bf16 inputs; got %d)", fn, D_idx);
+  REQUIRE(T >= 0 && T <= INT32_MAX, DSA_ERR_VALUE, "%s: T must be in [0, 2^31-1]", fn);
+  REQUIRE(T_kv >= 0 && T_kv <= INT32_MAX, DSA_ERR_VALUE, "%s: T_kv must be in [0, 2^31-1]", fn);
+  REQUIRE(row_begin >= 0 && n_rows >= 0 && row_begin + n_rows <= T, DSA_ERR_VALUE,
+          "%s: rows [%lld, %lld) outside [0, T=%lld)", fn, (long long)row_begin,
+          (long long)(row_begin + n_rows), (long long)T);
+  REQUIRE(n_cols >= 1 && n_cols <= DSA_FUSED_MAX_COLS, DSA_ERR_VALUE,
+          "%s: n_cols must be in [1, %d] (got %lld)", fn, DSA_FUSED_MAX_COLS, (long long)n_cols);
+  REQUIRE(k >= 1 && k <= DSA_MAX_TOPK, DSA_ERR_VALUE, "%s: k must be in [1, %d] (got %d)", fn,
+          DSA_MAX_TOPK, k);
+  REQUIRE(ld_indices >= k, DSA_ERR_VALUE, "%s: ld_indices (%lld) < k (%d)", fn,
+          (long long)ld_indices, k);
+  if (n_rows == 0) return DSA_OK;
+  REQUIRE(q_idx && (k_idx || T_kv == 0) && w && row_starts && seq_lens && indices &&
+              (!fp8 || (q_scale && (k_scale || T_kv == 0))),
+          DSA_ERR_VALUE, "%s: NULL pointer argument", fn);
+  REQUIRE(aligned(q_idx, 16) && aligned(k_idx, 16), DSA_ERR_VALUE,
+          "%s: q_idx and k_idx must be 16-byte aligned", fn);
+  REQUIRE(!fp8 || (aligned(k_scale, 4) && (precision == DSA_INDEXER_MXFP8 || aligned(q_scale, 4))),
+          DSA_ERR_VALUE, "%s: scale tensors misaligned", fn);
+  REQUIRE(aligned(w, w_dtype == DSA_F32 ? 4 : 2), DSA_ERR_VALUE, "%s: w misaligned", fn);
+  if (int rc = check_device(fn)) return rc;
+  // (T_kv = 0: every row is empty; the kernels then load no key.)
+  dsa::FusedArgs fa{k, indices, ld_indices, topk_length, logits, softmax, lse};
+  if (fp8)
+    return launched(fn, dsa::launch_indexer_topk_fp8(q_idx, q_scale, k_idx, k_scale,
+                                                     precision == DSA_INDEXER_MXFP8, w, w_dtype,
+                                                     row_starts, seq_lens, T_kv, H_idx, row_begin,
+                                                     n_rows, n_cols, fa, (hipStream_t)stream));
+  return launched(fn, dsa::launch_indexer_topk(q_idx, k_idx, w, w_dtype, row_starts, seq_lens,
+                                               T_kv, H_idx, D_idx, row_begin, n_rows, n_cols, fa,
+                                               (hipStream_t)stream));
 }
 
 int dsa_topk(const float* scores, int64_t ld_scores, int64_t n_rows, int64_t n_cols,

@@ -26,6 +26,19 @@ hipError_t launch_indexer_fp8(const void* q, const void* qs, const void* k, cons
                               const int32_t* sl, int64_t T_kv, int H, int64_t row_begin,
                               int64_t n_rows, float* scores, int64_t ld, hipStream_t st);
 
+struct FusedArgs;
+
+// Combined indexer + top-k (rows of at most 4096 columns): bf16 or FP8 inputs.
+hipError_t launch_indexer_topk(const void* q, const void* k, const void* w, int w_dtype,
+                               const int32_t* rs, const int32_t* sl, int64_t T_kv, int H, int D,
+                               int64_t row_begin, int64_t n_rows, int64_t n_cols,
+                               const FusedArgs& fa, hipStream_t st);
+hipError_t launch_indexer_topk_fp8(const void* q, const void* qs, const void* k, const void* ks,
+                                   bool mx, const void* w, int w_dtype, const int32_t* rs,
+                                   const int32_t* sl, int64_t T_kv, int H, int64_t row_begin,
+                                   int64_t n_rows, int64_t n_cols, const FusedArgs& fa,
+                                   hipStream_t st);
+
 hipError_t launch_topk(const float* scores, int64_t ld, int64_t n_rows, int64_t n_cols,
                        const int32_t* seq_lens, const int32_t* row_starts, int k, int32_t* indices,
                        int64_t ld_idx, int32_t* topk_length, float* values, hipStream_t st);

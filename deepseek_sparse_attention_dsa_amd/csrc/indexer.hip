@@ -21,6 +21,7 @@
 // first so the causal triangle's short rows fill the tail.
 #include "dsa_device.h"
 #include "dsa_launch.h"
+#include "dsa_select.h"
 
 namespace dsa {
 
@@ -90,19 +91,27 @@ __device__ __forceinline__ float load_w<float>(const float* w, int64_t i) {
 }
 
 // D: indexer head dim (64 or 128). MB: number of 32-head blocks (H <= 32*MB).
-template <int D, int MB, typename WT>
+// FUSE: the scores of each row stay in LDS (ld is then the column cap, at
+// most kFuseMaxCols) and the wave selects its row's top-k into `fa` instead
+// of writing scores; with D = 128 the key tile is then single-buffered so
+// that eight 4096-column rows fit next to it.
+template <int D, int MB, typename WT, bool FUSE>
 __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const WT* __restrict__ w,
     const int32_t* __restrict__ row_starts, const int32_t* __restrict__ seq_lens, int64_t T_kv,
-    int H, int64_t row_begin, int64_t n_rows, float* __restrict__ scores, int64_t ld) {
+    int H, int64_t row_begin, int64_t n_rows, float* __restrict__ scores, int64_t ld,
+    FusedArgs fa) {
   constexpr int KS = D / 16;                      // MFMA k-steps over the head dim
   constexpr int ROW_B = 2 * D + 16;               // LDS row stride in bytes (16 B pad)
   constexpr int TILE_B = kIdxTile * ROW_B;
   constexpr int CHUNKS = kIdxTile * D / 8;        // 16-byte chunks per tile
   constexpr int NT = kIdxWaves * 64;
   constexpr int LOADS = (CHUNKS + NT - 1) / NT;   // 16-byte loads per thread and tile
-  __shared__ __attribute__((aligned(16))) unsigned char ktile[2 * TILE_B];
+  constexpr int NBUF = (FUSE && D == 128) ? 1 : 2;  // key tiles in the LDS ring
+  __shared__ __attribute__((aligned(16))) unsigned char ktile[NBUF * TILE_B];
   __shared__ int32_t s_range[2];
+  __shared__ __attribute__((aligned(16))) float s_rows[FUSE ? kIdxWaves * kFuseRowStride : 4];
+  static_assert(!FUSE || NBUF * TILE_B >= kIdxWaves * 256 * 4, "select histograms fit the ring");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -110,6 +119,7 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
   const int64_t n_qblk = (n_rows + kIdxWaves - 1) / kIdxWaves;
   const int64_t qblk = n_qblk - 1 - blockIdx.x;   // longest rows first
   const int64_t r0 = qblk * kIdxWaves;
+  const int64_t cap = T_kv > 0 ? ld : 0;  // longest row length taken (no keys: none)
 
   // Key range of the workgroup: union of [start, start + len) of its rows.
   if (threadIdx.x == 0) {
@@ -119,7 +129,7 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
       if (r < n_rows) {
         const int64_t t = row_begin + r;
         const int32_t s0 = row_starts[t];
-        const int32_t n = (int32_t)min((int64_t)seq_lens[t], ld);
+        const int32_t n = (int32_t)min((int64_t)seq_lens[t], cap);
         if (n > 0) {
           kb = min(kb, s0);
           ke = max(ke, s0 + n);
@@ -137,7 +147,8 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
   const bool live = r < n_rows;
   const int64_t t = row_begin + (live ? r : 0);
   const int32_t qstart = live ? row_starts[t] : 0;
-  const int32_t qlen = live ? (int32_t)min((int64_t)seq_lens[t], ld) : 0;
+  // valid columns of the row, >= 0 (the range checks of the score writes rely on it)
+  const int32_t qlen = live ? (int32_t)max((int64_t)0, min((int64_t)seq_lens[t], cap)) : 0;
   u32x4 qa[MB][KS];
   float wv[MB][16];
 #pragma unroll
@@ -156,7 +167,12 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
   __syncthreads();
   const int32_t kb = s_range[0];
   const int32_t ke = s_range[1];
-  if (kb >= ke) return;  // uniform: no row of the workgroup has a key
+  if (kb >= ke) {  // uniform: no row of the workgroup has a key
+    if constexpr (FUSE)
+      if (live)
+        wave_topk_row(s_rows, 0, 0, nullptr, fa, r);  // writes the empty row
+    return;
+  }
 
   // Staging of keys [k0, k0 + 64): thread -> chunks c = tid + NT*i.
   u32x4 stage[LOADS];
@@ -233,10 +249,18 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
   // through a buffer descriptor of the wave's row whose range is the row's
   // valid columns: stores of other columns are dropped by the hardware range
   // check, so the tile loop has no branches.
-  const __amdgpu_buffer_rsrc_t srow = raw_buffer(scores + r * ld, (uint32_t)qlen * 4u);
+  // (FUSE: the row lives in LDS; columns outside the row go to a spare slot.)
+  const __amdgpu_buffer_rsrc_t srow =
+      raw_buffer(FUSE ? (const void*)scores : (const void*)(scores + r * ld),
+                 FUSE ? 0u : (uint32_t)qlen * 4u);
+  float* const lrow = s_rows + (FUSE ? wave * kFuseRowStride : 0);
   auto write_scores = [&](int32_t k0, float p0, float p1) {
-    buffer_store_f32(halfwave_sums(p0, p1), srow,
-                     (uint32_t)(k0 + lane - qstart) * 4u);  // negative: dropped
+    const float score = halfwave_sums(p0, p1);
+    const uint32_t j = (uint32_t)(k0 + lane - qstart);
+    if constexpr (FUSE)
+      lrow[j < (uint32_t)qlen ? j : (uint32_t)kFuseMaxCols] = score;
+    else
+      buffer_store_f32(score, srow, j * 4u);  // negative: dropped
   };
 
   // Every wave runs every tile of the workgroup's key range (a row's keys
@@ -265,28 +289,40 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
     __builtin_amdgcn_sched_barrier(0);
     pend_k0 = k0;
 
-    store_tile(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
+    if constexpr (NBUF == 2) {
+      store_tile(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    } else {
+      __syncthreads();  // every wave is done with the tile
+      store_tile(0);
+      __syncthreads();
+    }
   }
   write_scores(pend_k0, pend_p0, epilogue(acc1));
+  if constexpr (FUSE) {
+    __syncthreads();  // the tile ring is free: it holds the select histograms now
+    if (live)
+      wave_topk_row(lrow, qlen, row_starts[t], reinterpret_cast<uint32_t*>(ktile) + 256 * wave,
+                    fa, r);
+  }
 }
 
-template <int D, int MB>
+template <int D, int MB, bool FUSE>
 hipError_t launch_indexer_w(const void* q, const void* k, const void* w, int w_dtype,
                             const int32_t* rs, const int32_t* sl, int64_t T_kv, int H,
                             int64_t row_begin, int64_t n_rows, float* scores, int64_t ld,
-                            hipStream_t st) {
+                            const FusedArgs& fa, hipStream_t st) {
   const int64_t nblk = (n_rows + kIdxWaves - 1) / kIdxWaves;
   dim3 grid((unsigned)nblk), block(kIdxWaves * 64);
   if (w_dtype == 0)
-    hipLaunchKernelGGL((indexer_kernel<D, MB, uint16_t>), grid, block, 0, st,
+    hipLaunchKernelGGL((indexer_kernel<D, MB, uint16_t, FUSE>), grid, block, 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)w, rs, sl, T_kv, H,
-                       row_begin, n_rows, scores, ld);
+                       row_begin, n_rows, scores, ld, fa);
   else
-    hipLaunchKernelGGL((indexer_kernel<D, MB, float>), grid, block, 0, st, (const uint16_t*)q,
-                       (const uint16_t*)k, (const float*)w, rs, sl, T_kv, H, row_begin, n_rows,
-                       scores, ld);
+    hipLaunchKernelGGL((indexer_kernel<D, MB, float, FUSE>), grid, block, 0, st,
+                       (const uint16_t*)q, (const uint16_t*)k, (const float*)w, rs, sl, T_kv, H,
+                       row_begin, n_rows, scores, ld, fa);
   return hipGetLastError();
 }
 
@@ -316,10 +352,26 @@ hipError_t launch_indexer(const void* q, const void* k, const void* w, int w_dty
                           hipStream_t st) {
   if (n_rows == 0) return hipSuccess;
   const int mb = (H + 31) / 32;
-#define DSA_IDX_CASE(DD, MM)                                                                   \
-  if (D == DD && mb == MM)                                                                     \
-    return launch_indexer_w<DD, MM>(q, k, w, w_dtype, rs, sl, T_kv, H, row_begin, n_rows, scores, \
-                                    ld, st);
+  const FusedArgs none{};
+#define DSA_IDX_CASE(DD, MM)                                                                  \
+  if (D == DD && mb == MM)                                                                    \
+    return launch_indexer_w<DD, MM, false>(q, k, w, w_dtype, rs, sl, T_kv, H, row_begin,     \
+                                           n_rows, scores, ld, none, st);
+  DSA_IDX_CASE(128, 1) DSA_IDX_CASE(128, 2) DSA_IDX_CASE(64, 1) DSA_IDX_CASE(64, 2)
+#undef DSA_IDX_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_indexer_topk(const void* q, const void* k, const void* w, int w_dtype,
+                               const int32_t* rs, const int32_t* sl, int64_t T_kv, int H, int D,
+                               int64_t row_begin, int64_t n_rows, int64_t n_cols,
+                               const FusedArgs& fa, hipStream_t st) {
+  if (n_rows == 0) return hipSuccess;
+  const int mb = (H + 31) / 32;
+#define DSA_IDX_CASE(DD, MM)                                                                 \
+  if (D == DD && mb == MM)                                                                   \
+    return launch_indexer_w<DD, MM, true>(q, k, w, w_dtype, rs, sl, T_kv, H, row_begin,     \
+                                          n_rows, nullptr, n_cols, fa, st);
   DSA_IDX_CASE(128, 1) DSA_IDX_CASE(128, 2) DSA_IDX_CASE(64, 1) DSA_IDX_CASE(64, 2)
 #undef DSA_IDX_CASE
   return hipErrorInvalidValue;

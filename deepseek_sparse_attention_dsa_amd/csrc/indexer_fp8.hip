@@ -19,13 +19,13 @@
 //   their rows.
 #include "dsa_device.h"
 #include "dsa_launch.h"
+#include "dsa_select.h"
 
 namespace dsa {
 namespace {
 
 constexpr int kF8Waves = 8;     // query rows per workgroup
-constexpr int kF8Pairs = 2;    // 64-key pairs of 32-key blocks per LDS tile
-constexpr int kF8Tile = 64 * kF8Pairs;  // keys per LDS tile
+constexpr int kF8Pairs = 2;    // 64-key pairs of 32-key blocks per LDS tile (scores to HBM)
 constexpr int kF8D = 128;       // head dim (bytes per FP8 row)
 constexpr int kF8KS = kF8D / 64;  // MFMA k-steps over the head dim
 constexpr int kF8RowB = kF8D + 16;  // LDS row stride in bytes (16 B pad: conflict-free b128 reads)
@@ -47,13 +47,17 @@ __device__ __forceinline__ float load_wf<float>(const float* w, int64_t i) {
 
 // MB: number of 32-head blocks (H <= 32*MB). MX: block-scaled (true) or
 // per-token descales (false). qs / ks: fp32 descales [T, H] / [T_kv]
-// (per-token) or E8M0 bytes [T, H, 4] / [T_kv, 4] (MX).
-template <int MB, typename WT, bool MX>
+// (per-token) or E8M0 bytes [T, H, 4] / [T_kv, 4] (MX). P: 64-key pairs per
+// LDS tile. FUSE: the scores of each row stay in LDS (ld is then the column
+// cap, at most kFuseMaxCols) and the wave selects its row's top-k into `fa`
+// instead of writing scores.
+template <int MB, typename WT, bool MX, int P, bool FUSE>
 __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ qs, const uint8_t* __restrict__ k,
     const void* __restrict__ ks, const WT* __restrict__ w, const int32_t* __restrict__ row_starts,
     const int32_t* __restrict__ seq_lens, int64_t T_kv, int H, int64_t row_begin, int64_t n_rows,
-    float* __restrict__ scores, int64_t ld) {
+    float* __restrict__ scores, int64_t ld, FusedArgs fa) {
+  constexpr int kF8Tile = 64 * P;  // keys per LDS tile
   constexpr int TILE_B = kF8Tile * kF8RowB;
   constexpr int CHUNKS = kF8Tile * kF8D / 16;   // 16-byte chunks per tile
   constexpr int NT = kF8Waves * 64;
@@ -62,6 +66,8 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char ktile[2 * TILE_B];
   __shared__ uint32_t kscale[2][kF8Tile];  // per key: fp32 descale bits, or 4 E8M0 bytes
   __shared__ int32_t s_range[2];
+  __shared__ __attribute__((aligned(16))) float s_rows[FUSE ? kF8Waves * kFuseRowStride : 4];
+  static_assert(!FUSE || 2 * TILE_B >= kF8Waves * 256 * 4, "select histograms fit the tile ring");
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -69,6 +75,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   const int64_t n_qblk = (n_rows + kF8Waves - 1) / kF8Waves;
   const int64_t qblk = n_qblk - 1 - blockIdx.x;   // longest rows first
   const int64_t r0 = qblk * kF8Waves;
+  const int64_t cap = T_kv > 0 ? ld : 0;  // longest row length taken (no keys: none)
 
   if (threadIdx.x == 0) {
     int32_t kb = INT32_MAX, ke = 0;
@@ -77,7 +84,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
       if (r < n_rows) {
         const int64_t t = row_begin + r;
         const int32_t s0 = row_starts[t];
-        const int32_t n = (int32_t)min((int64_t)seq_lens[t], ld);
+        const int32_t n = (int32_t)min((int64_t)seq_lens[t], cap);
         if (n > 0) {
           kb = min(kb, s0);
           ke = max(ke, s0 + n);
@@ -94,7 +101,8 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   const bool live = r < n_rows;
   const int64_t t = row_begin + (live ? r : 0);
   const int32_t qstart = live ? row_starts[t] : 0;
-  const int32_t qlen = live ? (int32_t)min((int64_t)seq_lens[t], ld) : 0;
+  // valid columns of the row, >= 0 (the range checks of the score writes rely on it)
+  const int32_t qlen = live ? (int32_t)max((int64_t)0, min((int64_t)seq_lens[t], cap)) : 0;
   i32x8 qa[MB][kF8KS];
   int qsc[MB][kF8KS];  // MX: E8M0 byte of block 2s + half of the lane's head
   float wv[MB][16];
@@ -125,7 +133,12 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   __syncthreads();
   const int32_t kb = s_range[0];
   const int32_t ke = s_range[1];
-  if (kb >= ke) return;  // uniform: no row of the workgroup has a key
+  if (kb >= ke) {  // uniform: no row of the workgroup has a key
+    if constexpr (FUSE)
+      if (live)
+        wave_topk_row(s_rows, 0, 0, nullptr, fa, r);  // writes the empty row
+    return;
+  }
 
   // Staging of keys [k0, k0 + kF8Tile): thread -> 16-byte chunks
   // c = tid + NT*i (key c / 8); threads below kF8Tile also fetch the scale
@@ -226,11 +239,19 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   // Scores go through a buffer descriptor of the wave's row whose range is
   // the row's valid columns: stores of other columns are dropped by the
   // hardware range check, so the tile loop has no branches.
-  const __amdgpu_buffer_rsrc_t srow = raw_buffer(scores + r * ld, (uint32_t)qlen * 4u);
+  // (FUSE: the row lives in LDS; columns outside the row go to a spare slot.)
+  const __amdgpu_buffer_rsrc_t srow =
+      raw_buffer(FUSE ? (const void*)scores : (const void*)(scores + r * ld),
+                 FUSE ? 0u : (uint32_t)qlen * 4u);
+  float* const lrow = s_rows + (FUSE ? wave * kFuseRowStride : 0);
   auto write_scores = [&](int32_t k0, float p0, float p1, float kscl) {
     float score = halfwave_sums(p0, p1);
     if constexpr (!MX) score *= kscl;
-    buffer_store_f32(score, srow, (uint32_t)(k0 + lane - qstart) * 4u);  // negative: dropped
+    const uint32_t j = (uint32_t)(k0 + lane - qstart);
+    if constexpr (FUSE)
+      lrow[j < (uint32_t)qlen ? j : (uint32_t)kFuseMaxCols] = score;
+    else
+      buffer_store_f32(score, srow, j * 4u);  // negative: dropped
   };
 
   // Every wave runs every tile of the workgroup's key range (a row's keys
@@ -249,7 +270,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
     BOp cur, nxt;
     read_block(buf, 0, cur);
 #pragma unroll
-    for (int pr = 0; pr < kF8Pairs; ++pr) {
+    for (int pr = 0; pr < P; ++pr) {
       const int32_t kp = k0 + 64 * pr;
       const float kscl = MX ? 0.0f : __uint_as_float(kscale[buf][64 * pr + lane]);
       read_block(buf, 2 * pr + 1, nxt);
@@ -261,7 +282,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
       interleave();
       __builtin_amdgcn_sched_barrier(0);
       write_scores(pend_k0, pend_p0, p1_prev, pend_ks);
-      if (pr + 1 < kF8Pairs) read_block(buf, 2 * pr + 2, cur);
+      if (pr + 1 < P) read_block(buf, 2 * pr + 2, cur);
       block_mfma(nxt, acc1);
       pend_p0 = epilogue(acc0);
       interleave();
@@ -275,23 +296,30 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
     buf ^= 1;
   }
   write_scores(pend_k0, pend_p0, epilogue(acc1), pend_ks);
+  if constexpr (FUSE) {
+    __syncthreads();  // the tile ring is free: it holds the select histograms now
+    if (live)
+      wave_topk_row(lrow, qlen, row_starts[t], reinterpret_cast<uint32_t*>(ktile) + 256 * wave,
+                    fa, r);
+  }
 }
 
-template <int MB, bool MX>
+template <int MB, bool MX, bool FUSE>
 hipError_t launch_fp8_w(const void* q, const void* qs, const void* k, const void* ks,
                         const void* w, int w_dtype, const int32_t* rs, const int32_t* sl,
                         int64_t T_kv, int H, int64_t row_begin, int64_t n_rows, float* scores,
-                        int64_t ld, hipStream_t st) {
+                        int64_t ld, const FusedArgs& fa, hipStream_t st) {
+  constexpr int P = FUSE ? 1 : kF8Pairs;
   const int64_t nblk = (n_rows + kF8Waves - 1) / kF8Waves;
   dim3 grid((unsigned)nblk), block(kF8Waves * 64);
   if (w_dtype == 0)
-    hipLaunchKernelGGL((indexer_fp8_kernel<MB, uint16_t, MX>), grid, block, 0, st,
+    hipLaunchKernelGGL((indexer_fp8_kernel<MB, uint16_t, MX, P, FUSE>), grid, block, 0, st,
                        (const uint8_t*)q, qs, (const uint8_t*)k, ks, (const uint16_t*)w, rs, sl,
-                       T_kv, H, row_begin, n_rows, scores, ld);
+                       T_kv, H, row_begin, n_rows, scores, ld, fa);
   else
-    hipLaunchKernelGGL((indexer_fp8_kernel<MB, float, MX>), grid, block, 0, st,
+    hipLaunchKernelGGL((indexer_fp8_kernel<MB, float, MX, P, FUSE>), grid, block, 0, st,
                        (const uint8_t*)q, qs, (const uint8_t*)k, ks, (const float*)w, rs, sl, T_kv,
-                       H, row_begin, n_rows, scores, ld);
+                       H, row_begin, n_rows, scores, ld, fa);
   return hipGetLastError();
 }
 
@@ -303,10 +331,27 @@ hipError_t launch_indexer_fp8(const void* q, const void* qs, const void* k, cons
                               int64_t n_rows, float* scores, int64_t ld, hipStream_t st) {
   if (n_rows == 0) return hipSuccess;
   const int mb = (H + 31) / 32;
-#define DSA_F8_CASE(MM, XX)                                                                   \
-  if (mb == MM && mx == XX)                                                                   \
-    return launch_fp8_w<MM, XX>(q, qs, k, ks, w, w_dtype, rs, sl, T_kv, H, row_begin, n_rows, \
-                                scores, ld, st);
+  const FusedArgs none{};
+#define DSA_F8_CASE(MM, XX)                                                                    \
+  if (mb == MM && mx == XX)                                                                    \
+    return launch_fp8_w<MM, XX, false>(q, qs, k, ks, w, w_dtype, rs, sl, T_kv, H, row_begin, \
+                                       n_rows, scores, ld, none, st);
+  DSA_F8_CASE(1, false) DSA_F8_CASE(2, false) DSA_F8_CASE(1, true) DSA_F8_CASE(2, true)
+#undef DSA_F8_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_indexer_topk_fp8(const void* q, const void* qs, const void* k, const void* ks,
+                                   bool mx, const void* w, int w_dtype, const int32_t* rs,
+                                   const int32_t* sl, int64_t T_kv, int H, int64_t row_begin,
+                                   int64_t n_rows, int64_t n_cols, const FusedArgs& fa,
+                                   hipStream_t st) {
+  if (n_rows == 0) return hipSuccess;
+  const int mb = (H + 31) / 32;
+#define DSA_F8_CASE(MM, XX)                                                                  \
+  if (mb == MM && mx == XX)                                                                  \
+    return launch_fp8_w<MM, XX, true>(q, qs, k, ks, w, w_dtype, rs, sl, T_kv, H, row_begin, \
+                                      n_rows, nullptr, n_cols, fa, st);
   DSA_F8_CASE(1, false) DSA_F8_CASE(2, false) DSA_F8_CASE(1, true) DSA_F8_CASE(2, true)
 #undef DSA_F8_CASE
   return hipErrorInvalidValue;

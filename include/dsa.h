@@ -9,6 +9,8 @@
  *   dsa_indexer_fwd_fp8  the same scores from FP8 (E4M3) Q and K with
  *                        per-token descales or per-32 E8M0 block scales
  *   dsa_topk             per-row top-K select, ascending global indices, -1 pad
+ *   dsa_indexer_topk_fused  indexer scores + top-K (+ logits, softmax, LSE)
+ *                        in one launch, the scores kept on chip
  *   dsa_sparse_attn_fwd  sparse MQA/GQA attention over the selected KV rows
  *
  * Conventions shared by every call
@@ -65,13 +67,21 @@ typedef enum {
 const char* dsa_last_error(void);
 
 /* ABI version of this header (bumped on any signature change). */
-#define DSA_ABI_VERSION 3
+#define DSA_ABI_VERSION 4
 int dsa_abi_version(void);
 
 /* Limits enforced by the host checks. */
 #define DSA_MAX_TOPK 2048           /* top_k <= 2048 (DSA page, section 5)  */
 #define DSA_TOPK_MAX_COLS 65536     /* longest score row dsa_topk selects on */
 #define DSA_MAX_HEADS 128           /* attention query heads per call        */
+#define DSA_FUSED_MAX_COLS 4096     /* longest row dsa_indexer_topk_fused takes */
+
+/* Input precision of dsa_indexer_topk_fused. */
+typedef enum {
+  DSA_INDEXER_BF16 = 0,  /* bf16 q_idx / k_idx, no scales (dsa_indexer_fwd)  */
+  DSA_INDEXER_FP8 = 1,   /* E4M3 with per-token fp32 descales                */
+  DSA_INDEXER_MXFP8 = 2  /* E4M3 with E8M0 scales per 32 elements            */
+} dsa_indexer_precision;
 
 /*
  * dsa_packed_metadata - step a0.
@@ -212,6 +222,46 @@ int dsa_topk(const float* scores, int64_t ld_scores, int64_t n_rows, int64_t n_c
              const int32_t* seq_lens, const int32_t* row_starts, int32_t k,
              int32_t* indices, int64_t ld_indices, int32_t* topk_length, float* values,
              void* stream);
+
+/*
+ * dsa_indexer_topk_fused - steps a1 + a2 + a3 in one launch.
+ * DSA page section 4 (combined indexer forward + top-K: indices, logits and
+ * the softmax over the selected scores with its LSE, without dense scores;
+ * section 6 defines that softmax) with the selection and output form of
+ * dsa_topk. For query rows t in [row_begin, row_begin + n_rows), row
+ * r = t - row_begin of the outputs:
+ *   scores of row t: dsa_indexer_fwd's definition over local columns
+ *     j < n = clamp(seq_lens[t], 0, n_cols), from bf16 inputs
+ *     (DSA_INDEXER_BF16; q_scale and k_scale unused) or from FP8 inputs
+ *     with the scales of dsa_indexer_fwd_fp8 (DSA_INDEXER_FP8: per-token,
+ *     DSA_INDEXER_MXFP8: block-scaled);
+ *   indices[r, :], topk_length[r]: dsa_topk on those scores (k largest,
+ *     ties to the lower column, ascending, + row_starts[t], -1 suffix);
+ *   logits[r, i]  = the selected score, -inf in padded slots   (or NULL)
+ *   softmax[r, i] = exp(logits[r, i] - lse[r]), 0 in padded slots (or NULL)
+ *   lse[r]        = ln sum_i exp(logits[r, i]) over the selected slots,
+ *                   +inf for a row with no slot                 (or NULL)
+ * Each row's scores stay in the CU's local memory, so n_cols <=
+ * DSA_FUSED_MAX_COLS; a row whose seq_lens exceeds n_cols is treated as
+ * n_cols long (as dsa_topk does).
+ *   q_idx, k_idx, w, w_dtype, row_starts, seq_lens, T, T_kv, H_idx, D_idx,
+ *   row_begin, n_rows: as dsa_indexer_fwd (bf16) or dsa_indexer_fwd_fp8
+ *   k           1..DSA_MAX_TOPK
+ *   indices     device int32 [n_rows, ld_indices], ld_indices >= k; logits
+ *               and softmax use the same row stride
+ *   topk_length device int32 [n_rows] or NULL
+ * With T_kv = 0 every row is empty (k_idx and k_scale may then be NULL).
+ * Errors: those of dsa_indexer_fwd / dsa_indexer_fwd_fp8 and dsa_topk,
+ * DSA_ERR_VALUE for an unknown precision or n_cols outside
+ * [1, DSA_FUSED_MAX_COLS].
+ */
+int dsa_indexer_topk_fused(const void* q_idx, const void* q_scale, const void* k_idx,
+                           const void* k_scale, int32_t precision, const void* w,
+                           int32_t w_dtype, const int32_t* row_starts, const int32_t* seq_lens,
+                           int64_t T, int64_t T_kv, int32_t H_idx, int32_t D_idx,
+                           int64_t row_begin, int64_t n_rows, int64_t n_cols, int32_t k,
+                           int32_t* indices, int64_t ld_indices, int32_t* topk_length,
+                           float* logits, float* softmax, float* lse, void* stream);
 
 /*
  * dsa_sparse_attn_fwd - steps a4 / a5, sparse attention forward.

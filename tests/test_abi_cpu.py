@@ -33,6 +33,9 @@ ATTN_BASE = dict(q=FAKE, Tq=16, H=16, Dqk=576, k=FAKE, Tkv=16, ldk=576, v=None, 
 META_BASE = dict(cu=FAKE, n_seq=1, T=4, rs=FAKE, sl=FAKE, stream=None)
 F8_BASE = dict(q=FAKE, qs=FAKE2, k=FAKE, ks=FAKE2, sc=1, w=FAKE, wd=0, rs=FAKE, sl=FAKE, T=256,
                Tkv=256, H=64, D=128, rb=0, nr=256, scores=FAKE, ld=256, stream=None)
+FUSED_BASE = dict(q=FAKE, qs=None, k=FAKE, ks=None, prec=0, w=FAKE, wd=0, rs=FAKE, sl=FAKE,
+                  T=256, Tkv=256, H=64, D=128, rb=0, nr=256, nc=4096, kk=2048, idx=FAKE, ldi=2048,
+                  tl=None, lg=None, so=None, lse=None, stream=None)
 RMETA_BASE = dict(cq=FAKE, ck=FAKE2, off=None, n_seq=2, T=4, ratio=4, rs=FAKE, sl=FAKE,
                   stream=None)
 
@@ -47,12 +50,14 @@ ORDER = {
     "rmeta": ["cq", "ck", "off", "n_seq", "T", "ratio", "rs", "sl", "stream"],
     "f8": ["q", "qs", "k", "ks", "sc", "w", "wd", "rs", "sl", "T", "Tkv", "H", "D", "rb", "nr",
            "scores", "ld", "stream"],
+    "fused": ["q", "qs", "k", "ks", "prec", "w", "wd", "rs", "sl", "T", "Tkv", "H", "D", "rb", "nr",
+              "nc", "kk", "idx", "ldi", "tl", "lg", "so", "lse", "stream"],
 }
 BASE = {"topk": TOPK_BASE, "idx": IDX_BASE, "attn": ATTN_BASE, "meta": META_BASE,
-        "rmeta": RMETA_BASE, "f8": F8_BASE}
+        "rmeta": RMETA_BASE, "f8": F8_BASE, "fused": FUSED_BASE}
 FN = {"topk": "dsa_topk", "idx": "dsa_indexer_fwd", "attn": "dsa_sparse_attn_fwd",
       "meta": "dsa_packed_metadata", "rmeta": "dsa_ratio_causal_metadata",
-      "f8": "dsa_indexer_fwd_fp8"}
+      "f8": "dsa_indexer_fwd_fp8", "fused": "dsa_indexer_topk_fused"}
 
 CASES = [
     # top-K
@@ -109,6 +114,16 @@ CASES = [
     ("f8", dict(rb=100, nr=200), EVALUE), ("f8", dict(Tkv=-1), EVALUE),
     ("f8", dict(nr=0, q=None, k=None), OK), ("f8", dict(Tkv=0, q=None), OK),
     ("f8", dict(), ERUNTIME), ("f8", dict(sc=0, wd=1), ERUNTIME),
+    # combined indexer + top-K
+    ("fused", dict(wd=2), ETYPE), ("fused", dict(prec=3), EVALUE), ("fused", dict(nc=0), EVALUE),
+    ("fused", dict(nc=4097), EVALUE), ("fused", dict(kk=0), EVALUE), ("fused", dict(kk=2049), EVALUE),
+    ("fused", dict(ldi=2047), EVALUE), ("fused", dict(D=96), EVALUE),
+    ("fused", dict(prec=1, D=64), EVALUE), ("fused", dict(prec=1), EVALUE),
+    ("fused", dict(prec=2, qs=FAKE2, ks=FAKE2 + 1), EVALUE), ("fused", dict(idx=None), EVALUE),
+    ("fused", dict(H=65), EVALUE), ("fused", dict(rb=1), EVALUE), ("fused", dict(q=FAKE + 4), EVALUE),
+    ("fused", dict(nr=0, q=None, idx=None), OK), ("fused", dict(), ERUNTIME),
+    ("fused", dict(prec=2, qs=FAKE2 + 1, ks=FAKE2), ERUNTIME),
+    ("fused", dict(Tkv=0, D=64, kk=1, ldi=1), ERUNTIME),
 ]
 
 _CHILD = r"""
@@ -153,7 +168,8 @@ def _declared_functions():
 def test_header_declares_the_path():
     names = _declared_functions()
     for fn in ["dsa_packed_metadata", "dsa_ratio_causal_metadata", "dsa_indexer_fwd",
-               "dsa_indexer_fwd_fp8", "dsa_topk", "dsa_sparse_attn_fwd", "dsa_last_error",
+               "dsa_indexer_fwd_fp8", "dsa_indexer_topk_fused", "dsa_topk", "dsa_sparse_attn_fwd",
+               "dsa_last_error",
                "dsa_abi_version"]:
         assert fn in names
 
