@@ -318,3 +318,57 @@ def sparse_attention(q, k, v, indices, topk_length, sink, scale, d_v=None, rows=
         lse[r] = m + np.log(l)
         mx[r] = m
     return out, lse, mx
+
+
+def sparse_attention_backward(q, kv, indices, topk_length, sink, scale, dout, d_v, rows=None):
+    """Gradients of the sparse attention forward (shared latent KV: K = kv,
+    V = kv[:, :d_v]).
+
+    DSA page section 2 ("Sparse Attention Backward"): for the loss whose
+    gradient with respect to out is dout, returns dq [T_q, H, D_qk],
+    dkv [T_kv, D_qk] and d_sink [H]. Derived from section 1's forward: with
+    P_j = exp(s_j) / (sum_i exp(s_i) + exp(sink)) over the valid slots j of a
+    row and out = sum_j P_j v_j,
+        dP_j = dout . v_j,  D = sum_j P_j dP_j (= dout . out),
+        dS_j = P_j (dP_j - D),  dq = scale sum_j dS_j k_j,
+        dk_j += scale dS_j q,  dv_j += P_j dout,
+        d_sink += -P_sink D with P_sink = exp(sink) / (sum_i exp(s_i) + exp(sink)).
+    Duplicate slots contribute separately; dkv = dk with dv added to its
+    first d_v columns. Every quantity is recomputed from the inputs in
+    float64 (no forward output is trusted). Inputs float64; rows defaults to
+    every query row (dq rows outside `rows` are left zero).
+    """
+    Tq, H, Dqk = q.shape
+    Tkv = kv.shape[0]
+    kw = indices.shape[1]
+    v = kv[:, :d_v]
+    rows = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
+    dq = np.zeros_like(q)
+    dkv = np.zeros((Tkv, Dqk))
+    d_sink = np.zeros(H)
+    sk = None if sink is None else np.asarray(sink, dtype=np.float64)
+    for t in rows:
+        L = kw if topk_length is None else min(max(int(topk_length[t]), 0), kw)
+        ids = np.asarray(indices[t, :L], dtype=np.int64)
+        ids = ids[(ids >= 0) & (ids < Tkv)]
+        if len(ids) == 0:
+            continue
+        s = scale * (q[t] @ kv[ids].T)                       # [H, n]
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        z = e.sum(axis=1, keepdims=True)
+        if sk is not None:
+            z = z + np.exp(sk[:, None] - m)
+        P = e / z                                              # [H, n]
+        out = P @ v[ids]                                       # [H, d_v]
+        dP = dout[t] @ v[ids].T                                # [H, n]
+        D = (dout[t] * out).sum(axis=1, keepdims=True)         # [H, 1]
+        dS = P * (dP - D)
+        dq[t] = scale * (dS @ kv[ids])
+        np.add.at(dkv, ids, scale * (dS.T @ q[t]))             # dk
+        np.add.at(dkv[:, :d_v], ids, P.T @ dout[t])            # dv (shared columns)
+        if sk is not None:
+            p_sink = np.exp(sk - m[:, 0]) / z[:, 0]
+            d_sink += -p_sink * D[:, 0]
+    return dq, dkv, d_sink
+

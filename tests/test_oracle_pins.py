@@ -820,3 +820,115 @@ def test_planted_topk_and_attention_mistakes_fail_their_pins():
     _, l_ok, _ = O.sparse_attention(q, kv, None, idx, None, sink, scale, d_v=D)
     np.testing.assert_allclose(l_ok, good_l, rtol=1e-12)
     assert not np.allclose(l_mut, good_l, atol=1e-6)
+
+
+# ------------------------------------------------------ attention backward --
+
+def _bwd_case(rng, T=7, H=3, D=6, dv=4, K=5, dup=True):
+    q = rng.standard_normal((T, H, D))
+    kv = rng.standard_normal((T, D))
+    idx = np.full((T, K), -1, dtype=np.int64)
+    for t in range(T):
+        c = rng.permutation(t + 1)[: min(K, t + 1)]
+        idx[t, : len(c)] = c
+    if dup:
+        idx[T - 1, -1] = idx[T - 1, 0]  # a duplicated slot
+        idx[2, -1] = T + 5              # an out-of-range id: invalid slot
+    tl = np.array([min(K, t + 1) for t in range(T)])
+    tl[T - 1] = K
+    tl[2] = K
+    sink = rng.standard_normal(H)
+    dout = rng.standard_normal((T, H, dv))
+    return q, kv, idx, tl, sink, dout
+
+
+def _loss(q, kv, idx, tl, sink, scale, dout, dv):
+    out, _, _ = O.sparse_attention(q, kv, None, idx, tl, sink, scale, d_v=dv)
+    return float((out * dout).sum())
+
+
+def test_attention_backward_finite_differences():
+    rng = np.random.default_rng(70)
+    q, kv, idx, tl, sink, dout = _bwd_case(rng)
+    scale, dv = 0.37, 4
+    dq, dkv, ds = O.sparse_attention_backward(q, kv, idx, tl, sink, scale, dout, dv)
+    h = 1e-6
+    for arr, grad in ((q, dq), (kv, dkv), (sink, ds)):
+        flat, gflat = arr.reshape(-1), grad.reshape(-1)
+        for i in rng.choice(flat.size, size=min(12, flat.size), replace=False):
+            old = flat[i]
+            flat[i] = old + h
+            up = _loss(q, kv, idx, tl, sink, scale, dout, dv)
+            flat[i] = old - h
+            dn = _loss(q, kv, idx, tl, sink, scale, dout, dv)
+            flat[i] = old
+            assert abs((up - dn) / (2 * h) - gflat[i]) < 1e-7 * max(1.0, abs(gflat[i])), i
+
+
+def _dense_torch_grads(q, kv, sink, scale, dout, dv):
+    """Dense causal attention with a sink written in torch (fp64, CPU), its
+    gradients by autograd."""
+    T, H, D = q.shape
+    qt = torch.tensor(q, requires_grad=True)
+    kt = torch.tensor(kv, requires_grad=True)
+    st = torch.tensor(sink, requires_grad=True)
+    logits = scale * torch.einsum("thd,sd->ths", qt, kt)
+    causal = torch.tril(torch.ones(T, T, dtype=torch.bool))
+    logits = logits.masked_fill(~causal[:, None, :], float("-inf"))
+    full = torch.cat([logits, st[None, :, None].expand(T, H, 1)], dim=2)
+    w = torch.softmax(full, dim=2)[:, :, :T]
+    out = torch.einsum("ths,sd->thd", w, kt[:, :dv])
+    (out * torch.tensor(dout)).sum().backward()
+    return qt.grad.numpy(), kt.grad.numpy(), st.grad.numpy()
+
+
+def test_attention_backward_matches_autograd_of_dense_attention():
+    rng = np.random.default_rng(71)
+    T, H, D, dv = 9, 4, 8, 6
+    q = rng.standard_normal((T, H, D))
+    kv = rng.standard_normal((T, D))
+    sink = rng.standard_normal(H)
+    dout = rng.standard_normal((T, H, dv))
+    scale = 0.29
+    idx = _causal_full_indices(T, T)
+    dq, dkv, ds = O.sparse_attention_backward(q, kv, idx, None, sink, scale, dout, dv)
+    rq, rk, rs = _dense_torch_grads(q, kv, sink, scale, dout, dv)
+    np.testing.assert_allclose(dq, rq, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dkv, rk, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(ds, rs, rtol=1e-10, atol=1e-12)
+
+
+def test_planted_backward_mistakes_fail_autograd():
+    rng = np.random.default_rng(72)
+    T, H, D, dv = 6, 2, 5, 3
+    q = rng.standard_normal((T, H, D))
+    kv = rng.standard_normal((T, D))
+    sink = rng.standard_normal(H)
+    dout = rng.standard_normal((T, H, dv))
+    scale = 0.5
+    idx = _causal_full_indices(T, T)
+    rq, rk, rs = _dense_torch_grads(q, kv, sink, scale, dout, dv)
+    # mistakes written as edits of the definition: no -D term, sink sign,
+    # dv left out of the shared columns
+    def mutant(kind):
+        dq = np.zeros_like(q); dkv = np.zeros((T, D)); dsk = np.zeros(H)
+        for t in range(T):
+            ids = np.arange(t + 1)
+            s = scale * (q[t] @ kv[ids].T)
+            z = np.exp(s).sum(1, keepdims=True) + np.exp(sink)[:, None]
+            P = np.exp(s) / z
+            out = P @ kv[ids, :dv]
+            dP = dout[t] @ kv[ids, :dv].T
+            Dd = 0.0 if kind == "no_D" else (dout[t] * out).sum(1, keepdims=True)
+            dS = P * (dP - Dd)
+            dq[t] = scale * dS @ kv[ids]
+            dkv[ids] += scale * dS.T @ q[t]
+            if kind != "no_dv":
+                dkv[ids, :dv] += P.T @ dout[t]
+            psink = np.exp(sink) / z[:, 0]
+            dsk += (1 if kind == "sink_sign" else -1) * psink * (dout[t] * out).sum(1)
+        return dq, dkv, dsk
+    for kind in ("no_D", "sink_sign", "no_dv"):
+        dq, dkv, dsk = mutant(kind)
+        assert not (np.allclose(dq, rq) and np.allclose(dkv, rk) and np.allclose(dsk, rs)), kind
+
