@@ -26,7 +26,7 @@ __all__ = [
     "dsa_packed_metadata", "dsa_ratio_causal_metadata", "dsa_indexer_fwd",
     "dsa_indexer_fwd_fp8", "DSA_FP8_PER_TOKEN", "DSA_MXFP8", "dsa_topk",
     "dsa_indexer_topk_fused", "DSA_FUSED_MAX_COLS",
-    "dsa_sparse_attn_fwd",
+    "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_workspace_bytes",
     "indexer_topk", "chunk_rows",
 ]
 
@@ -60,6 +60,9 @@ _SIGNATURES = {
                                 _I64, _I64, _I64, _I32, _P, _I64, _P, _P, _P, _P, _P],
                                ctypes.c_int),
     "dsa_topk": ([_P, _I64, _I64, _I64, _P, _P, _I32, _P, _I64, _P, _P, _P], ctypes.c_int),
+    "dsa_sparse_attn_bwd_workspace_bytes": ([_I64, _I32, _I64, _I32, _I32], ctypes.c_int64),
+    "dsa_sparse_attn_bwd": ([_P, _I64, _I32, _I32, _P, _I64, _I64, _I32, _P, _I64, _I32, _P, _P,
+                             _F32, _P, _P, _P, _P, _P, _P, _P, _I64, _P], ctypes.c_int),
     "dsa_sparse_attn_fwd": ([_P, _I64, _I32, _I32, _P, _I64, _I64, _P, _I64, _I32, _P, _I64,
                              _I32, _P, _P, _F32, _P, _P, _P, _P], ctypes.c_int),
 }
@@ -466,6 +469,69 @@ def dsa_indexer_topk_fused(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Te
         _ptr(seq_lens), T, T_kv, H, D, row_begin, n_rows, int(n_cols), int(k), _ptr(indices), ld,
         _ptr(topk_length), _ptr(logits), _ptr(softmax), _ptr(lse), _stream(stream)))
     return indices, topk_length, logits, softmax, lse
+
+
+def dsa_sparse_attn_bwd_workspace_bytes(T_q: int, H: int, T_kv: int, D_qk: int,
+                                        k_width: int) -> int:
+    n = int(load_library().dsa_sparse_attn_bwd_workspace_bytes(T_q, H, T_kv, D_qk, k_width))
+    if n < 0:
+        raise ValueError("sizes out of contract for dsa_sparse_attn_bwd")
+    return n
+
+
+def dsa_sparse_attn_bwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,
+                        out: torch.Tensor, dout: torch.Tensor, lse: torch.Tensor,
+                        topk_length: Optional[torch.Tensor] = None,
+                        attn_sink: Optional[torch.Tensor] = None,
+                        softmax_scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                        dq: Optional[torch.Tensor] = None, dkv: Optional[torch.Tensor] = None,
+                        d_sink: Optional[torch.Tensor] = None, stream=None):
+    """Sparse attention backward for shared latent KV -> (dq, dkv, d_sink).
+
+    q [T_q,H,D_qk], kv [T_kv,D_qk] (V = kv[:, :512]), indices [T_q, k], out
+    and dout [T_q,H,512] bf16, lse [T_q,H] fp32 (the forward's). workspace:
+    a uint8 device tensor (allocated when None).
+    """
+    q = _need(q, "q", torch.bfloat16)
+    dev = q.device
+    kv = _need(kv, "kv", torch.bfloat16, dev)
+    if kv.dim() == 3 and kv.shape[1] == 1:
+        kv = kv[:, 0]
+    out = _need(out, "out", torch.bfloat16, dev)
+    dout = _need(dout, "dout", torch.bfloat16, dev)
+    lse = _need(lse, "lse", torch.float32, dev)
+    if indices.dtype != torch.int32:
+        raise TypeError("indices must be int32")
+    if indices.dim() != 2 or indices.stride(1) != 1:
+        raise ValueError("indices must be 2-D with unit column stride")
+    T_q, H, D = q.shape
+    T_kv = kv.shape[0]
+    if kv.shape[1] < D or out.shape != (T_q, H, 512) or dout.shape != (T_q, H, 512) or \
+            lse.shape != (T_q, H) or indices.shape[0] != T_q:
+        raise ValueError("shape mismatch among q, kv, indices, out, dout, lse")
+    if topk_length is not None:
+        topk_length = _need(topk_length, "topk_length", torch.int32, dev)
+    if attn_sink is not None:
+        attn_sink = _need(attn_sink, "attn_sink", torch.float32, dev)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    k_width = indices.shape[1]
+    need = dsa_sparse_attn_bwd_workspace_bytes(T_q, H, T_kv, D, k_width)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    else:
+        workspace = _out(workspace, "workspace", torch.uint8, dev)
+    dq = torch.empty_like(q) if dq is None else _out(dq, "dq", torch.bfloat16, dev)
+    dkv = (torch.empty((T_kv, D), dtype=torch.bfloat16, device=dev) if dkv is None
+           else _out(dkv, "dkv", torch.bfloat16, dev))
+    d_sink = (torch.empty((H,), dtype=torch.float32, device=dev) if d_sink is None
+              else _out(d_sink, "d_sink", torch.float32, dev))
+    lib = load_library()
+    _check(lib.dsa_sparse_attn_bwd(_ptr(q), T_q, H, D, _ptr(kv), T_kv, kv.stride(0), 512,
+                                   _ptr(indices), indices.stride(0), k_width, _ptr(topk_length),
+                                   _ptr(attn_sink), float(scale), _ptr(out), _ptr(dout), _ptr(lse),
+                                   _ptr(dq), _ptr(dkv), _ptr(d_sink), _ptr(workspace),
+                                   workspace.numel(), _stream(stream)))
+    return dq, dkv, d_sink
 
 
 # Score-buffer cap per chunk of rows (2 GiB, the cap the NeMo cudnn_dsa page

@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
-SOURCES = ["abi.hip", "indexer.hip", "indexer_fp8.hip", "topk.hip", "sparse_attn.hip"]
+SOURCES = ["abi.hip", "indexer.hip", "indexer_fp8.hip", "topk.hip", "sparse_attn.hip",
+           "sparse_attn_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 FLAGS = [

@@ -293,4 +293,99 @@ int dsa_sparse_attn_fwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk, con
   return launched(fn, dsa::launch_sparse_attn(a, D_qk, D_v, (hipStream_t)stream));
 }
 
+static int64_t bwd_fixed_bytes(int64_t T_q, int32_t H, int64_t T_kv, int32_t D_qk) {
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  return up(T_q * H * 4) * 2 + up(T_kv * D_qk * 4);
+}
+
+// Bytes of one query row of the P buffer (the dS buffer is the same size).
+static int64_t bwd_row_bytes(int32_t H, int32_t k_width) {
+  const int64_t hp = (H + 31) / 32 * 32, kw = ((int64_t)k_width + 31) / 32 * 32;
+  return kw * hp * 2;  // bf16
+}
+
+int64_t dsa_sparse_attn_bwd_workspace_bytes(int64_t T_q, int32_t H, int64_t T_kv, int32_t D_qk,
+                                            int32_t k_width) {
+  if (T_q < 0 || T_q > INT32_MAX || H < 1 || H > DSA_MAX_HEADS || T_kv < 0 || T_kv > INT32_MAX ||
+      (D_qk != 576 && D_qk != 512) || k_width < 0)
+    return -1;
+  const int64_t row = bwd_row_bytes(H, k_width);
+  int64_t rows = row ? ((int64_t)1 << 29) / row : T_q;  // P + dS within 1 GiB
+  rows = rows < 1 ? 1 : (rows > T_q ? T_q : rows);
+  return bwd_fixed_bytes(T_q, H, T_kv, D_qk) + (rows * row + 255) / 256 * 256 * 2;
+}
+
+int dsa_sparse_attn_bwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk, const void* kv,
+                        int64_t T_kv, int64_t ld_kv, int32_t D_v, const int32_t* indices,
+                        int64_t ld_indices, int32_t k_width, const int32_t* topk_length,
+                        const float* attn_sink, float softmax_scale, const void* out,
+                        const void* dout, const float* lse, void* dq, void* dkv, float* d_sink,
+                        void* workspace, int64_t workspace_bytes, void* stream) {
+  const char* fn = "dsa_sparse_attn_bwd";
+  REQUIRE(H >= 1 && H <= DSA_MAX_HEADS, DSA_ERR_VALUE, "%s: H must be in [1, %d] (got %d)", fn,
+          DSA_MAX_HEADS, H);
+  REQUIRE((D_qk == 576 || D_qk == 512) && D_v == 512, DSA_ERR_VALUE,
+          "%s: (D_qk, D_v) must be (576, 512) or (512, 512) (got (%d, %d))", fn, D_qk, D_v);
+  REQUIRE(T_q >= 0 && T_q <= INT32_MAX, DSA_ERR_VALUE, "%s: T_q out of range", fn);
+  REQUIRE(T_kv >= 0 && T_kv <= INT32_MAX, DSA_ERR_VALUE, "%s: T_kv out of range", fn);
+  REQUIRE(ld_kv >= D_qk && ld_kv % 8 == 0, DSA_ERR_VALUE,
+          "%s: ld_kv must be >= D_qk and a multiple of 8 (got %lld)", fn, (long long)ld_kv);
+  REQUIRE(ld_indices >= 1 && k_width >= 0 && k_width <= ld_indices, DSA_ERR_VALUE,
+          "%s: need 0 <= k_width <= ld_indices (got %d, %lld)", fn, k_width,
+          (long long)ld_indices);
+  REQUIRE(isfinite(softmax_scale) && softmax_scale > 0.0f, DSA_ERR_VALUE,
+          "%s: softmax_scale must be finite and > 0", fn);
+  REQUIRE((q && out && dout && lse && dq) || T_q == 0, DSA_ERR_VALUE, "%s: NULL pointer argument",
+          fn);
+  REQUIRE((kv && dkv) || T_kv == 0, DSA_ERR_VALUE, "%s: NULL kv or dkv", fn);
+  REQUIRE(indices || k_width == 0 || T_q == 0, DSA_ERR_VALUE, "%s: NULL indices", fn);
+  REQUIRE(aligned(q, 16) && aligned(kv, 16) && aligned(out, 16) && aligned(dout, 16) &&
+              aligned(dq, 16) && aligned(dkv, 16) && aligned(workspace, 256),
+          DSA_ERR_VALUE, "%s: q, kv, out, dout, dq, dkv need 16-byte and workspace 256-byte "
+          "alignment", fn);
+  const int64_t fixed = bwd_fixed_bytes(T_q, H, T_kv, D_qk);
+  const int64_t row = bwd_row_bytes(H, k_width);
+  const int64_t per_row_ws = (row + 255) / 256 * 256 * 2;  // P and dS, one row each
+  REQUIRE(workspace && workspace_bytes >= fixed + per_row_ws, DSA_ERR_VALUE,
+          "%s: workspace of %lld bytes is below the %lld bytes one row needs", fn,
+          (long long)workspace_bytes, (long long)(fixed + per_row_ws));
+  if (T_q == 0 && T_kv == 0 && !d_sink) return DSA_OK;
+  if (int rc = check_device(fn)) return rc;
+  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+  unsigned char* w = (unsigned char*)workspace;
+  dsa::BwdArgs a{};
+  a.q = (const uint16_t*)q;
+  a.kv = (const uint16_t*)kv;
+  a.T_q = T_q;
+  a.T_kv = kv ? T_kv : 0;
+  a.ld_kv = ld_kv;
+  a.H = H;
+  a.D_qk = D_qk;
+  a.D_v = D_v;
+  a.indices = indices;
+  a.ld_idx = ld_indices;
+  a.k_width = indices ? k_width : 0;
+  a.topk_length = topk_length;
+  a.sink = attn_sink;
+  a.scale = softmax_scale;
+  a.out = (const uint16_t*)out;
+  a.dout = (const uint16_t*)dout;
+  a.lse = lse;
+  a.logZ = (float*)w;
+  a.Dsum = (float*)(w + up(T_q * H * 4));
+  a.dkv_ws = (float*)(w + 2 * up(T_q * H * 4));
+  // P and dS buffers of `chunk` rows each
+  const int64_t per_buf = (workspace_bytes - fixed) / 2 / 256 * 256;
+  int64_t chunk = row ? per_buf / row : T_q;
+  chunk = chunk > T_q ? T_q : chunk;
+  if (chunk < 1) chunk = 1;
+  a.wsP = (uint16_t*)(w + fixed);
+  a.wsD = (uint16_t*)(w + fixed + up(chunk * row));
+  a.Kw = (k_width + 31) / 32 * 32;
+  a.dq = (uint16_t*)dq;
+  a.dkv = (uint16_t*)dkv;
+  a.d_sink = d_sink;
+  return launched(fn, dsa::launch_sparse_attn_bwd(a, chunk, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -65,4 +65,35 @@ struct AttnArgs {
 
 hipError_t launch_sparse_attn(const AttnArgs& a, int D_qk, int D_v, hipStream_t st);
 
+// Sparse attention backward (shared latent KV, D_v = 512).
+struct BwdArgs {
+  const uint16_t* q;        // [T_q, H, D_qk]
+  const uint16_t* kv;       // [T_kv, ld_kv]
+  int64_t T_q, T_kv, ld_kv;
+  int H, D_qk, D_v;
+  const int32_t* indices;   // [T_q, ld_idx]
+  int64_t ld_idx;
+  int k_width;
+  const int32_t* topk_length;
+  const float* sink;        // [H] or null
+  float scale;
+  const uint16_t* out;      // [T_q, H, D_v]
+  const uint16_t* dout;     // [T_q, H, D_v]
+  const float* lse;         // [T_q, H]
+  float* logZ;              // workspace [T_q, H]
+  float* Dsum;              // workspace [T_q, H]
+  uint16_t* wsP;            // workspace [chunk, Kw, 32*ceil(H/32)] bf16
+  uint16_t* wsD;            // same
+  int Kw;                   // k_width rounded up to 32
+  uint16_t* dq;             // [T_q, H, D_qk] bf16
+  float* dkv_ws;            // workspace [T_kv, D_qk] fp32
+  uint16_t* dkv;            // [T_kv, D_qk] bf16
+  float* d_sink;            // [H] or null
+  int64_t row0;             // first row of the current chunk
+};
+
+// Rows of P and dS that ws_rows_bytes of workspace hold.
+size_t sparse_attn_bwd_chunk_rows(int64_t T_q, int H, int k_width, size_t ws_rows_bytes);
+hipError_t launch_sparse_attn_bwd(BwdArgs a, int64_t chunk, hipStream_t st);
+
 }  // namespace dsa

@@ -1,0 +1,432 @@
+// Sparse MQA attention backward (shared latent KV) for gfx950.
+//
+// Semantics: cuDNN Frontend DSA page, section 2 "Sparse Attention Backward",
+// the gradient of section 1's forward. For query row t, head h and valid slot
+// j (key row k_j = kv[idx[t,j]], value v_j = its first D_v dims):
+//   P_j  = exp(s_j - log Z),  log Z = log(sum_i exp(s_i) + exp(sink_h))
+//        = log(exp(lse) + exp(sink_h))            (lse: the forward's KV-only LSE)
+//   dP_j = dout . v_j,  D = dout . out,  dS_j = P_j (dP_j - D)
+//   dq   = scale sum_j dS_j k_j
+//   dkv[idx_j]       += scale dS_j q          (all D_qk dims)
+//   dkv[idx_j, :D_v] += P_j dout              (the value dims)
+//   d_sink_h = -sum_t exp(sink_h - log Z) D
+// Duplicate slots contribute separately; invalid slots contribute nothing.
+//
+// Kernels (one pass each, over chunks of query rows; bf16 MFMA
+// v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+//  * bwd_prep_kernel: D and log Z per (t, h), one wave per pair.
+//  * bwd_sink_kernel: d_sink by a fixed-order reduction over t (deterministic).
+//  * bwd_scores_kernel<P>: gathers 32 selected KV rows per tile into LDS and
+//    computes S = q . K^T (q held in registers as the A operand); stores P as
+//    bf16, slot-major ([row][slot][head]).
+//  * bwd_scores_kernel<DS>: the same with dout as A and the value dims:
+//    dP = dout . V^T; stores scale * P * (dP - D) (dS, scale folded in).
+//  * bwd_dq_kernel: dq = dS . K with both operands read transposed from LDS
+//    (ds_read_b64_tr_b16), two waves per 32-head block splitting the dims.
+//  * bwd_dkv_kernel: per tile, dS^T . q + P^T . dout (the query's q and dout
+//    staged in LDS) added to an fp32 workspace with coalesced atomics.
+//  * bwd_convert_kernel: fp32 workspace -> bf16 dkv.
+#include "dsa_device.h"
+#include "dsa_launch.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kBT = 32;  // slots per tile
+constexpr float kLog2eB = 1.442695040888963387f;
+
+// C-layout row of value i of a 32x32 MFMA result for lane half `half`.
+__device__ __forceinline__ int crow(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------- D, log Z --
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t p = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (p >= a.T_q * a.H) return;
+  const int64_t t = p / a.H;
+  const int h = (int)(p - t * a.H);
+  // dout . out over the D_v dims, 8 per lane per step
+  float acc = 0.0f;
+  for (int d = 8 * lane; d < a.D_v; d += 512) {
+    const u32x4 g = load16(a.dout + (t * a.H + h) * a.D_v + d);
+    const u32x4 o = load16(a.out + (t * a.H + h) * a.D_v + d);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(bf16_bits_to_f32(g[e] & 0xffffu), bf16_bits_to_f32(o[e] & 0xffffu), acc);
+      acc = fmaf(bf16_bits_to_f32(g[e] >> 16), bf16_bits_to_f32(o[e] >> 16), acc);
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) {
+    const float lse = a.lse[t * a.H + h];
+    float lz = lse;
+    if (a.sink && lse < __builtin_inff()) {
+      const float s = a.sink[h];
+      const float m = fmaxf(lse, s);
+      lz = m + logf(expf(lse - m) + expf(s - m));
+    }
+    a.logZ[t * a.H + h] = lz;  // +inf for an empty row
+    a.Dsum[t * a.H + h] = acc;
+  }
+}
+
+// d_sink[h] = -sum_t exp(sink_h - logZ[t,h]) * D[t,h], fixed summation order.
+__global__ __launch_bounds__(256) void bwd_sink_kernel(BwdArgs a) {
+  __shared__ float s_part[256];
+  const int h = blockIdx.x;
+  const float s = a.sink[h];
+  float acc = 0.0f;
+  for (int64_t t = threadIdx.x; t < a.T_q; t += 256) {
+    const float lz = a.logZ[t * a.H + h];
+    if (lz < __builtin_inff()) acc += expf(s - lz) * a.Dsum[t * a.H + h];
+  }
+  s_part[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) s_part[threadIdx.x] += s_part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.d_sink[h] = -s_part[0];
+}
+
+// Slot ids of tile `tile` of row t (-1 when invalid) into s_ids[32].
+__device__ __forceinline__ void load_tile_ids(const BwdArgs& a, int64_t t, int L, int tile,
+                                              int32_t* s_ids) {
+  if (threadIdx.x < kBT) {
+    const int s = tile * kBT + threadIdx.x;
+    int32_t id = -1;
+    if (s < L) {
+      const int32_t v = a.indices[t * a.ld_idx + s];
+      id = (v >= 0 && v < a.T_kv) ? v : -1;
+    }
+    s_ids[threadIdx.x] = id;
+  }
+}
+
+// Gathers dims [0, DG) of the tile's 32 KV rows into a row-major LDS tile
+// (row stride RS bf16); invalid rows become zeros.
+template <int DG, int RS>
+__device__ __forceinline__ void gather_rows(const BwdArgs& a, const int32_t* s_ids,
+                                            uint16_t* tile) {
+  constexpr int CPR = DG / 8;  // 16-byte chunks per row
+  for (int c = threadIdx.x; c < kBT * CPR; c += blockDim.x) {
+    const int row = c / CPR, ch = c - row * CPR;
+    const int32_t id = s_ids[row];
+    const u32x4 v = id >= 0 ? load16(a.kv + (int64_t)id * a.ld_kv + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(tile + row * RS + 8 * ch) = v;
+  }
+}
+
+__device__ __forceinline__ int row_len(const BwdArgs& a, int64_t t) {
+  if (!a.topk_length) return a.k_width;
+  const int32_t L = a.topk_length[t];
+  return L < 0 ? 0 : (L > a.k_width ? a.k_width : L);
+}
+
+// ------------------------------------------------------------ P and dS --
+// One workgroup per query row of the chunk, one wave per 32 heads.
+// S[h][s] on 32x32x16: A = q (or dout) rows of the wave's heads from
+// registers, B = the gathered rows (k = dims) from LDS; C lane -> slot
+// column l%32, head rows crow(i).
+template <int DQK, int NW, bool DS>
+__global__ __launch_bounds__(NW * 64) void bwd_scores_kernel(BwdArgs a) {
+  constexpr int DG = DS ? 512 : DQK;   // dims of the product
+  constexpr int RS = DG + 8;           // LDS row stride (bf16): conflict-free b128 reads
+  constexpr int KS = DG / 16;
+  constexpr int HP = NW * 32;
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kBT * RS];
+  __shared__ int32_t s_ids[kBT];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, r32 = lane & 31;
+  const int64_t rc = blockIdx.x;            // row within the chunk
+  const int64_t t = a.row0 + rc;
+  const int L = row_len(a, t);
+  const int h0 = 32 * wave;
+  const int hA = h0 + r32;                  // A-operand head of this lane
+
+  u32x4 qa[KS];
+  {
+    const uint16_t* src = DS ? a.dout + (t * a.H + hA) * 512 : a.q + (t * a.H + hA) * DQK;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qa[ks] = hA < a.H ? load16(src + 16 * ks + 8 * half) : u32x4{0u, 0u, 0u, 0u};
+  }
+  float lz[16], dd[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int h = h0 + crow(i, half);
+    lz[i] = h < a.H ? a.logZ[t * a.H + h] : __builtin_inff();
+    dd[i] = (DS && h < a.H) ? a.Dsum[t * a.H + h] : 0.0f;
+  }
+  const float c2 = a.scale * kLog2eB;
+  uint16_t* wsP = a.wsP + rc * (int64_t)a.Kw * HP;
+  uint16_t* wsD = a.wsD + rc * (int64_t)a.Kw * HP;
+
+  const int ntiles = (L + kBT - 1) / kBT;
+  for (int tl = 0; tl < ntiles; ++tl) {
+    load_tile_ids(a, t, L, tl, s_ids);
+    __syncthreads();
+    gather_rows<DG, RS>(a, s_ids, tile);
+    __syncthreads();
+    f32x16 acc{};
+    const uint16_t* brow = tile + r32 * RS + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      acc = mfma32x32x16(qa[ks], *reinterpret_cast<const u32x4*>(brow + 16 * ks), acc);
+    const int slot = tl * kBT + r32;
+    const bool valid = s_ids[r32] >= 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t off = (int64_t)slot * HP + h0 + 8 * g + 4 * half;  // 4 consecutive heads
+      float v[4];
+      if constexpr (!DS) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = valid ? fast_exp2(acc[4 * g + e] * c2 - lz[4 * g + e] * kLog2eB) : 0.0f;
+      } else {
+        const u32x2 pp = *reinterpret_cast<const u32x2*>(wsP + off);
+        const float p[4] = {bf16_bits_to_f32(pp.x & 0xffffu), bf16_bits_to_f32(pp.x >> 16),
+                            bf16_bits_to_f32(pp.y & 0xffffu), bf16_bits_to_f32(pp.y >> 16)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = a.scale * p[e] * (acc[4 * g + e] - dd[4 * g + e]);
+      }
+      *reinterpret_cast<u32x2*>((DS ? wsD : wsP) + off) =
+          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
+    __syncthreads();  // tile and ids are reused
+  }
+}
+
+// ------------------------------------------------------------------- dq --
+// One workgroup per query row, waves (head block hb, dim half dh). dq[h][d]
+// on 32x32x16 with k = slots: A = dS (heads x slots) and B = K (slots x dims),
+// both read transposed from row-major LDS tiles ([slot][head], [slot][dim]).
+template <int DQK, int NW>
+__global__ __launch_bounds__(NW * 128) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int RS = DQK + 8;     // K tile row stride (bf16)
+  constexpr int HP = NW * 32;
+  constexpr int RSD = HP + 8;     // dS tile row stride (bf16)
+  constexpr int NBW = DQK / 64;   // 32-dim blocks per wave (half of the dims)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kBT * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t dst[kBT * RSD];
+  __shared__ int32_t s_ids[kBT];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, r32 = lane & 31;
+  const int hb = wave >> 1, dh = wave & 1;
+  const int64_t rc = blockIdx.x;
+  const int64_t t = a.row0 + rc;
+  const int L = row_len(a, t);
+  const uint16_t* wsD = a.wsD + rc * (int64_t)a.Kw * HP;
+  // transposed-read addressing: 16-lane group G reads rows r0 + li/4 (+4),
+  // columns c0 + 4*(li%4); lane li receives column c0 + li, 4 rows.
+  const int G = lane >> 4, li = lane & 15;
+  const int rsel = 8 * (G >> 1) + (li >> 2);        // slot within a 16-slot step
+  const int csel = 16 * (G & 1) + 4 * (li & 3);     // column within a 32-wide block
+
+  f32x16 acc[NBW];
+#pragma unroll
+  for (int b = 0; b < NBW; ++b) acc[b] = f32x16{};
+  const int ntiles = (L + kBT - 1) / kBT;
+  for (int tl = 0; tl < ntiles; ++tl) {
+    load_tile_ids(a, t, L, tl, s_ids);
+    __syncthreads();
+    gather_rows<DQK, RS>(a, s_ids, tile);
+    for (int c = threadIdx.x; c < kBT * HP / 8; c += blockDim.x) {
+      const int s = c / (HP / 8), ch = c - s * (HP / 8);
+      *reinterpret_cast<u32x4*>(dst + s * RSD + 8 * ch) =
+          load16(wsD + (int64_t)(tl * kBT + s) * HP + 8 * ch);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {  // 16-slot k-steps
+      const uint16_t* da = dst + (16 * st + rsel) * RSD + 32 * hb + csel;
+      const u32x2 a0 = lds_read_tr16(da);
+      const u32x2 a1 = lds_read_tr16(da + 4 * RSD);
+      const u32x4 av = u32x4{a0.x, a0.y, a1.x, a1.y};
+#pragma unroll
+      for (int b = 0; b < NBW; ++b) {
+        const uint16_t* kb = tile + (16 * st + rsel) * RS + (dh * NBW + b) * 32 + csel;
+        const u32x2 b0 = lds_read_tr16(kb);
+        const u32x2 b1 = lds_read_tr16(kb + 4 * RS);
+        acc[b] = mfma32x32x16(av, u32x4{b0.x, b0.y, b1.x, b1.y}, acc[b]);
+      }
+    }
+    __syncthreads();
+  }
+  // C: lane -> dim column, head rows crow(i); dS already carries the scale
+#pragma unroll
+  for (int b = 0; b < NBW; ++b) {
+    const int d = (dh * NBW + b) * 32 + r32;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int h = 32 * hb + crow(i, half);
+      if (h < a.H) a.dq[(t * a.H + h) * DQK + d] = (uint16_t)f32_to_bf16_bits(acc[b][i]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dkv --
+// One workgroup per (query row, 64-head chunk); NWD waves each own BPW
+// 32-dim blocks. C[s][d] on 32x32x16 with k = heads: A = dS^T / P^T
+// (slot rows, heads contiguous in the workspace), B = q / dout of the chunk's
+// heads read transposed from LDS ([head][dim]).
+template <int DQK, int NW, int NWD>
+__global__ __launch_bounds__(NWD * 64) void bwd_dkv_kernel(BwdArgs a) {
+  constexpr int HP = NW * 32;
+  constexpr int HC = HP % 64 == 0 ? 64 : 32;  // heads per chunk (divides HP)
+  constexpr int RQ = DQK + 8, RG = 512 + 8;
+  constexpr int NBLK = DQK / 32;
+  constexpr int BPW = NBLK / NWD;
+  static_assert(NBLK % NWD == 0, "dim blocks split evenly over waves");
+  __shared__ __attribute__((aligned(16))) uint16_t sq[HC * RQ];
+  __shared__ __attribute__((aligned(16))) uint16_t sg[HC * RG];
+  __shared__ int32_t s_ids[kBT];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, r32 = lane & 31;
+  const int64_t rc = blockIdx.x / (HP / HC);
+  const int hc0 = (int)(blockIdx.x % (HP / HC)) * HC;
+  const int64_t t = a.row0 + rc;
+  const int L = row_len(a, t);
+  if (L == 0) return;
+  // stage q and dout of the chunk's heads (zeros past H)
+  for (int c = threadIdx.x; c < HC * (DQK / 8); c += blockDim.x) {
+    const int h = c / (DQK / 8), ch = c - h * (DQK / 8);
+    const int hh = hc0 + h;
+    *reinterpret_cast<u32x4*>(sq + h * RQ + 8 * ch) =
+        hh < a.H ? load16(a.q + (t * a.H + hh) * DQK + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+  }
+  for (int c = threadIdx.x; c < HC * 64; c += blockDim.x) {
+    const int h = c / 64, ch = c - h * 64;
+    const int hh = hc0 + h;
+    *reinterpret_cast<u32x4*>(sg + h * RG + 8 * ch) =
+        hh < a.H ? load16(a.dout + (t * a.H + hh) * 512 + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
+  }
+  const uint16_t* wsP = a.wsP + rc * (int64_t)a.Kw * HP;
+  const uint16_t* wsD = a.wsD + rc * (int64_t)a.Kw * HP;
+  const int G = lane >> 4, li = lane & 15;
+  const int rsel = 8 * (G >> 1) + (li >> 2);
+  const int csel = 16 * (G & 1) + 4 * (li & 3);
+
+  const int ntiles = (L + kBT - 1) / kBT;
+  for (int tl = 0; tl < ntiles; ++tl) {
+    __syncthreads();  // staging done / previous tile's ids consumed
+    load_tile_ids(a, t, L, tl, s_ids);
+    __syncthreads();
+    f32x16 acc[BPW];
+#pragma unroll
+    for (int b = 0; b < BPW; ++b) acc[b] = f32x16{};
+    const int64_t srow = (int64_t)(tl * kBT + r32) * HP + hc0 + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < HC / 16; ++kk) {   // 16-head k-steps
+      const u32x4 ad = load16(wsD + srow + 16 * kk);
+      const u32x4 ap = load16(wsP + srow + 16 * kk);
+#pragma unroll
+      for (int b = 0; b < BPW; ++b) {
+        const int col = (wave * BPW + b) * 32;
+        const uint16_t* qb = sq + (16 * kk + rsel) * RQ + col + csel;
+        const u32x2 q0 = lds_read_tr16(qb);
+        const u32x2 q1 = lds_read_tr16(qb + 4 * RQ);
+        acc[b] = mfma32x32x16(ad, u32x4{q0.x, q0.y, q1.x, q1.y}, acc[b]);
+        if (col < 512) {
+          const uint16_t* gb = sg + (16 * kk + rsel) * RG + col + csel;
+          const u32x2 g0 = lds_read_tr16(gb);
+          const u32x2 g1 = lds_read_tr16(gb + 4 * RG);
+          acc[b] = mfma32x32x16(ap, u32x4{g0.x, g0.y, g1.x, g1.y}, acc[b]);
+        }
+      }
+    }
+    // C: lane -> dim column, slot rows crow(i)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int32_t id = s_ids[crow(i, half)];
+      if (id >= 0) {
+#pragma unroll
+        for (int b = 0; b < BPW; ++b)
+          atomicAdd(a.dkv_ws + (int64_t)id * DQK + (wave * BPW + b) * 32 + r32, acc[b][i]);
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void bwd_fill_kernel(float* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+__global__ __launch_bounds__(256) void bwd_convert_kernel(const float* p, uint16_t* o,
+                                                          int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) o[i] = (uint16_t)f32_to_bf16_bits(p[i]);
+}
+
+template <int DQK, int NW>
+hipError_t launch_bwd_nw(BwdArgs a, int64_t chunk, hipStream_t st) {
+  constexpr int NWD = DQK == 576 ? 6 : 4;
+  constexpr int HP = NW * 32;
+  constexpr int HC = HP % 64 == 0 ? 64 : 32;
+  for (int64_t r0 = 0; r0 < a.T_q; r0 += chunk) {
+    a.row0 = r0;
+    const int64_t n = a.T_q - r0 < chunk ? a.T_q - r0 : chunk;
+    hipLaunchKernelGGL((bwd_scores_kernel<DQK, NW, false>), dim3((unsigned)n), dim3(NW * 64), 0,
+                       st, a);
+    hipLaunchKernelGGL((bwd_scores_kernel<DQK, NW, true>), dim3((unsigned)n), dim3(NW * 64), 0,
+                       st, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<DQK, NW>), dim3((unsigned)n), dim3(NW * 128), 0, st, a);
+    hipLaunchKernelGGL((bwd_dkv_kernel<DQK, NW, NWD>), dim3((unsigned)(n * (HP / HC))),
+                       dim3(NWD * 64), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t sparse_attn_bwd_chunk_rows(int64_t T_q, int H, int k_width, size_t ws_rows_bytes) {
+  const int64_t HP = (H + 31) / 32 * 32;
+  const int64_t Kw = (k_width + kBT - 1) / kBT * kBT;
+  const int64_t per_row = 2 * Kw * HP * 2;  // P and dS, bf16
+  int64_t rows = per_row ? (int64_t)(ws_rows_bytes / per_row) : T_q;
+  return (size_t)(rows < T_q ? rows : T_q);
+}
+
+hipError_t launch_sparse_attn_bwd(BwdArgs a, int64_t chunk, hipStream_t st) {
+  const int64_t nkv = a.T_kv * a.D_qk;
+  if (nkv) hipLaunchKernelGGL(bwd_fill_kernel, dim3((unsigned)((nkv + 255) / 256)), dim3(256), 0,
+                              st, a.dkv_ws, nkv);
+  if (a.T_q > 0) {
+    const int64_t pairs = a.T_q * a.H;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, st, a);
+  }
+  if (a.d_sink) {
+    if (a.sink && a.T_q > 0)
+      hipLaunchKernelGGL(bwd_sink_kernel, dim3((unsigned)a.H), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(bwd_fill_kernel, dim3(1), dim3(256), 0, st, a.d_sink, (int64_t)a.H);
+  }
+  hipError_t e = hipSuccess;
+  if (a.T_q > 0 && a.k_width > 0) {
+    const int nw = (a.H + 31) / 32;
+#define DSA_BWD_CASE(DD, NN) \
+    if (a.D_qk == DD && nw == NN) e = launch_bwd_nw<DD, NN>(a, chunk, st); else
+    DSA_BWD_CASE(576, 1) DSA_BWD_CASE(576, 2) DSA_BWD_CASE(576, 3) DSA_BWD_CASE(576, 4)
+    DSA_BWD_CASE(512, 1) DSA_BWD_CASE(512, 2) DSA_BWD_CASE(512, 3) DSA_BWD_CASE(512, 4)
+    e = hipErrorInvalidValue;
+#undef DSA_BWD_CASE
+  } else if (a.T_q > 0) {
+    // no slot at all: dq is zero
+    const int64_t nq = a.T_q * a.H * a.D_qk;
+    hipLaunchKernelGGL(bwd_fill_kernel, dim3((unsigned)((nq / 2 + 255) / 256)), dim3(256), 0, st,
+                       reinterpret_cast<float*>(a.dq), nq / 2);
+  }
+  if (e != hipSuccess) return e;
+  if (nkv) hipLaunchKernelGGL(bwd_convert_kernel, dim3((unsigned)((nkv + 255) / 256)), dim3(256),
+                              0, st, a.dkv_ws, a.dkv, nkv);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -12,6 +12,7 @@
  *   dsa_indexer_topk_fused  indexer scores + top-K (+ logits, softmax, LSE)
  *                        in one launch, the scores kept on chip
  *   dsa_sparse_attn_fwd  sparse MQA/GQA attention over the selected KV rows
+ *   dsa_sparse_attn_bwd  its gradients (dq, dkv, d_sink) for shared latent KV
  *
  * Conventions shared by every call
  * --------------------------------
@@ -67,7 +68,7 @@ typedef enum {
 const char* dsa_last_error(void);
 
 /* ABI version of this header (bumped on any signature change). */
-#define DSA_ABI_VERSION 4
+#define DSA_ABI_VERSION 5
 int dsa_abi_version(void);
 
 /* Limits enforced by the host checks. */
@@ -300,6 +301,59 @@ int dsa_sparse_attn_fwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk,
                         const int32_t* topk_length, const float* attn_sink,
                         float softmax_scale, void* out, float* lse, float* max_logits,
                         void* stream);
+
+/*
+ * dsa_sparse_attn_bwd_workspace_bytes - device workspace dsa_sparse_attn_bwd
+ * uses for these sizes: fp32 statistics [T_q, H] x 2, an fp32 dkv
+ * accumulator [T_kv, D_qk], and bf16 P / dS rows of up to 1 GiB
+ * (P and dS of min(T_q, rows that fit) query rows at a time). Returns -1
+ * for sizes out of contract.
+ */
+int64_t dsa_sparse_attn_bwd_workspace_bytes(int64_t T_q, int32_t H, int64_t T_kv, int32_t D_qk,
+                                            int32_t k_width);
+
+/*
+ * dsa_sparse_attn_bwd - gradients of dsa_sparse_attn_fwd for shared latent
+ * KV (V = kv[:, :D_v]).
+ * DSA page section 2 ("Sparse Attention Backward", the gradient of section
+ * 1's forward): given the forward's out and KV-only lse and the gradient
+ * dout of a loss with respect to out, for query row t, head h and valid slot
+ * j (the validity rules of dsa_sparse_attn_fwd), with
+ * P_j = exp(s_j) / (sum_i exp(s_i) + exp(sink_h)), D = dout . out,
+ * dS_j = P_j (dout . v_j - D):
+ *   dq[t, h, :]        = scale sum_j dS_j kv[idx_j, :D_qk]
+ *   dkv[r, :]          = sum over slots with idx_j = r of scale dS_j q[t, h, :]
+ *                        (+ P_j dout[t, h, :] on the first D_v columns)
+ *   d_sink[h]          = -sum_t P_sink(t, h) D(t, h),
+ *                        P_sink = exp(sink_h) / (sum_i exp(s_i) + exp(sink_h))
+ * Duplicate slots contribute separately. P comes from the given lse
+ * (log of the denominator = log(exp(lse) + exp(sink))), D from the given
+ * out; an empty row (lse = +inf) contributes nothing.
+ *   q, kv, indices, ld_indices, k_width, topk_length, attn_sink,
+ *   softmax_scale: as dsa_sparse_attn_fwd; (D_qk, D_v) in {(576, 512),
+ *   (512, 512)}, v is kv[:, :512]; H in [1, DSA_MAX_HEADS]
+ *   out, dout   device bf16 [T_q, H, D_v], contiguous, 16-byte aligned
+ *   lse         device fp32 [T_q, H]
+ *   dq          device bf16 [T_q, H, D_qk] output
+ *   dkv         device bf16 [T_kv, D_qk] output (contiguous)
+ *   d_sink      device fp32 [H] output or NULL (0 when attn_sink is NULL)
+ *   workspace   device memory of workspace_bytes >=
+ *               dsa_sparse_attn_bwd_workspace_bytes(...) would give for one
+ *               row of P / dS (a larger workspace processes more rows per
+ *               pass), 256-byte aligned, owned by the caller
+ * bf16 MFMA products with fp32 accumulation; P and dS are rounded to bf16
+ * before the dq and dkv products; dkv accumulates in fp32 with atomics (the
+ * summation order, and so the last bits of dkv, may vary between runs);
+ * d_sink is summed in a fixed order.
+ * Errors: the checks of dsa_sparse_attn_fwd, DSA_ERR_VALUE for D_v != 512,
+ * a separate V, or a workspace too small for one row.
+ */
+int dsa_sparse_attn_bwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk, const void* kv,
+                        int64_t T_kv, int64_t ld_kv, int32_t D_v, const int32_t* indices,
+                        int64_t ld_indices, int32_t k_width, const int32_t* topk_length,
+                        const float* attn_sink, float softmax_scale, const void* out,
+                        const void* dout, const float* lse, void* dq, void* dkv, float* d_sink,
+                        void* workspace, int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

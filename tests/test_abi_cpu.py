@@ -36,6 +36,9 @@ F8_BASE = dict(q=FAKE, qs=FAKE2, k=FAKE, ks=FAKE2, sc=1, w=FAKE, wd=0, rs=FAKE, 
 FUSED_BASE = dict(q=FAKE, qs=None, k=FAKE, ks=None, prec=0, w=FAKE, wd=0, rs=FAKE, sl=FAKE,
                   T=256, Tkv=256, H=64, D=128, rb=0, nr=256, nc=4096, kk=2048, idx=FAKE, ldi=2048,
                   tl=None, lg=None, so=None, lse=None, stream=None)
+BWD_BASE = dict(q=FAKE, Tq=16, H=16, Dqk=576, kv=FAKE, Tkv=16, ldkv=576, Dv=512, idx=FAKE, ldi=64,
+                kw=64, tl=None, sink=None, scale=0.04, out=FAKE, dout=FAKE, lse=FAKE, dq=FAKE,
+                dkv=FAKE, ds=None, ws=FAKE2, wsb=1 << 24, stream=None)
 RMETA_BASE = dict(cq=FAKE, ck=FAKE2, off=None, n_seq=2, T=4, ratio=4, rs=FAKE, sl=FAKE,
                   stream=None)
 
@@ -52,12 +55,14 @@ ORDER = {
            "scores", "ld", "stream"],
     "fused": ["q", "qs", "k", "ks", "prec", "w", "wd", "rs", "sl", "T", "Tkv", "H", "D", "rb", "nr",
               "nc", "kk", "idx", "ldi", "tl", "lg", "so", "lse", "stream"],
+    "bwd": ["q", "Tq", "H", "Dqk", "kv", "Tkv", "ldkv", "Dv", "idx", "ldi", "kw", "tl", "sink",
+            "scale", "out", "dout", "lse", "dq", "dkv", "ds", "ws", "wsb", "stream"],
 }
 BASE = {"topk": TOPK_BASE, "idx": IDX_BASE, "attn": ATTN_BASE, "meta": META_BASE,
-        "rmeta": RMETA_BASE, "f8": F8_BASE, "fused": FUSED_BASE}
+        "rmeta": RMETA_BASE, "f8": F8_BASE, "fused": FUSED_BASE, "bwd": BWD_BASE}
 FN = {"topk": "dsa_topk", "idx": "dsa_indexer_fwd", "attn": "dsa_sparse_attn_fwd",
       "meta": "dsa_packed_metadata", "rmeta": "dsa_ratio_causal_metadata",
-      "f8": "dsa_indexer_fwd_fp8", "fused": "dsa_indexer_topk_fused"}
+      "f8": "dsa_indexer_fwd_fp8", "fused": "dsa_indexer_topk_fused", "bwd": "dsa_sparse_attn_bwd"}
 
 CASES = [
     # top-K
@@ -124,6 +129,14 @@ CASES = [
     ("fused", dict(nr=0, q=None, idx=None), OK), ("fused", dict(), ERUNTIME),
     ("fused", dict(prec=2, qs=FAKE2 + 1, ks=FAKE2), ERUNTIME),
     ("fused", dict(Tkv=0, D=64, kk=1, ldi=1), ERUNTIME),
+    # attention backward
+    ("bwd", dict(H=0), EVALUE), ("bwd", dict(H=129), EVALUE), ("bwd", dict(Dv=256), EVALUE),
+    ("bwd", dict(Dqk=256), EVALUE), ("bwd", dict(ldkv=570), EVALUE), ("bwd", dict(kw=65), EVALUE),
+    ("bwd", dict(scale=0.0), EVALUE), ("bwd", dict(scale="nan"), EVALUE),
+    ("bwd", dict(dout=None), EVALUE), ("bwd", dict(lse=None), EVALUE), ("bwd", dict(dkv=None), EVALUE),
+    ("bwd", dict(ws=None), EVALUE), ("bwd", dict(wsb=1024), EVALUE), ("bwd", dict(ws=FAKE2 + 16), EVALUE),
+    ("bwd", dict(out=FAKE + 8), EVALUE), ("bwd", dict(idx=None), EVALUE),
+    ("bwd", dict(), ERUNTIME), ("bwd", dict(Dqk=512, ldkv=512, sink=FAKE, ds=FAKE), ERUNTIME),
 ]
 
 _CHILD = r"""
@@ -162,13 +175,15 @@ def results():
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(dsa_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|const char\*)\s+(dsa_\w+)\s*\(", text,
+                                 flags=re.M)))
 
 
 def test_header_declares_the_path():
     names = _declared_functions()
     for fn in ["dsa_packed_metadata", "dsa_ratio_causal_metadata", "dsa_indexer_fwd",
                "dsa_indexer_fwd_fp8", "dsa_indexer_topk_fused", "dsa_topk", "dsa_sparse_attn_fwd",
+               "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_workspace_bytes",
                "dsa_last_error",
                "dsa_abi_version"]:
         assert fn in names
@@ -218,3 +233,13 @@ def test_python_binding_type_and_shape_errors():
                             torch.zeros(4, 64, dtype=torch.bfloat16),
                             torch.zeros(4, 2, dtype=torch.float16),
                             torch.zeros(4, dtype=torch.int32), torch.zeros(4, dtype=torch.int32))
+
+
+def test_backward_workspace_size_rule():
+    lib = dsa.load_library()
+    # statistics + dkv accumulator + P and dS of every row when they fit in 1 GiB
+    n = lib.dsa_sparse_attn_bwd_workspace_bytes(256, 16, 256, 576, 64)
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert n == 2 * up(256 * 16 * 4) + up(256 * 576 * 4) + 2 * up(256 * 64 * 32 * 2)
+    assert lib.dsa_sparse_attn_bwd_workspace_bytes(10, 0, 10, 576, 8) == -1
+    assert lib.dsa_sparse_attn_bwd_workspace_bytes(10, 8, 10, 256, 8) == -1

@@ -1,0 +1,126 @@
+"""Parity of the sparse attention backward (dsa_sparse_attn_bwd) with the CPU
+oracle's gradients (fp64, recomputed from the inputs).
+
+The GPU path takes the forward kernel's own bf16 out and fp32 lse, rounds P
+and dS to bf16 before the dq / dkv products and writes bf16 gradients, so
+each gradient is compared with max-abs error <= 2e-2 * ||ref||_inf and a
+relative Frobenius error <= 1e-2; d_sink (fp32, fixed-order sums) within
+1e-3 * max(1, ||ref||_inf).
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import deepseek_sparse_attention_dsa_amd as dsa
+from gpu_helpers import DEV, f64, i64, say
+from oracle import dsa_oracle as O
+from workloads import make_custom
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    dsa.load_library()
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def _indices(T, kw, T_kv, rng, dup=True, invalid=True, active=None):
+    idx = np.full((T, kw), -1, dtype=np.int32)
+    tl = np.zeros(T, dtype=np.int32)
+    for t in range(T):
+        if active is not None and not active[t]:
+            continue
+        n = min(kw, t + 1, T_kv)
+        c = np.sort(rng.choice(min(t + 1, T_kv), n, replace=False))
+        idx[t, :n] = c
+        tl[t] = n
+        if dup and n >= 3 and t % 5 == 1:
+            idx[t, n - 1] = idx[t, 0]          # duplicated slot
+        if invalid and n >= 4 and t % 7 == 3:
+            idx[t, 1] = T_kv + 9               # out-of-range id: invalid slot
+    return idx, tl
+
+
+def _check(name, got, ref, rel_max=2e-2, rel_fro=1e-2):
+    g = got.astype(np.float64)
+    scale = max(np.abs(ref).max(), 1e-30)
+    err = np.abs(g - ref).max() / scale
+    fro = np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)
+    say(f"  {name}: max {err:.2e} fro {fro:.2e}")
+    assert err <= rel_max, (name, err)
+    assert fro <= rel_fro, (name, fro)
+
+
+def _run(T, H, D, kw, seed, sink=True, stress=False, use_tl=True, active=None, rows=None):
+    wl = make_custom([T], H=H, D_qk=D, D_v=512, H_idx=0, seed=seed, device=DEV, sink=sink,
+                     stress=stress, topk=kw)
+    rng = np.random.default_rng(seed)
+    idx, tl = _indices(T, kw, T, rng, active=active)
+    idx_t = torch.from_numpy(idx).to(DEV)
+    tl_t = torch.from_numpy(tl).to(DEV) if use_tl else None
+    out, lse, _ = dsa.dsa_sparse_attn_fwd(wl.q, wl.kv, idx_t, topk_length=tl_t, attn_sink=wl.sink,
+                                          softmax_scale=wl.scale, return_max_logits=False)
+    g = torch.Generator(device=DEV).manual_seed(seed + 1)
+    dout = (torch.randn((T, H, 512), generator=g, device=DEV) / math.sqrt(512)).to(torch.bfloat16)
+    dq, dkv, ds = dsa.dsa_sparse_attn_bwd(wl.q, wl.kv, idx_t, out, dout, lse, topk_length=tl_t,
+                                          attn_sink=wl.sink, softmax_scale=wl.scale)
+    torch.cuda.synchronize()
+    sk = None if wl.sink is None else f64(wl.sink)
+    tl_ref = tl if use_tl else None
+    rq, rk, rs = O.sparse_attention_backward(f64(wl.q), f64(wl.kv), idx.astype(np.int64), tl_ref,
+                                             sk, wl.scale, f64(dout), 512, rows=rows)
+    sel = np.arange(T) if rows is None else np.asarray(rows)
+    _check("dq", f64(dq)[sel], rq[sel])
+    _check("dkv", f64(dkv), rk)
+    ds_np = ds.cpu().numpy().astype(np.float64)
+    if sk is None:
+        assert np.all(ds_np == 0.0)
+    else:
+        err = np.abs(ds_np - rs).max()
+        say(f"  d_sink: max abs {err:.2e} (ref max {np.abs(rs).max():.2e})")
+        assert err <= 1e-3 * max(1.0, np.abs(rs).max())
+
+
+@pytest.mark.parametrize("T,H,D,kw,sink,stress,use_tl", [
+    (64, 16, 576, 32, True, False, True),
+    (150, 64, 576, 64, True, True, True),
+    (97, 33, 512, 40, False, False, True),
+    (128, 128, 576, 96, True, True, False),
+    (70, 64, 512, 33, True, True, True),
+])
+def test_backward_small(T, H, D, kw, sink, stress, use_tl):
+    say("attention backward", T, H, D, kw, sink, stress, use_tl)
+    _run(T, H, D, kw, seed=T + H, sink=sink, stress=stress, use_tl=use_tl)
+
+
+def test_backward_full_size_sampled_rows():
+    """T = 4096, 64 heads, K = 2048 (the single_T4096 shapes): only sampled
+    rows carry slots, so dkv is the sum of their contributions alone and the
+    oracle covers every output."""
+    T = 4096
+    rows = [0, 1, 2047, 2048, 3000, 4095]
+    active = np.zeros(T, dtype=bool)
+    active[rows] = True
+    say("attention backward, full size, rows", rows)
+    _run(T, 64, 576, 2048, seed=7, stress=True, active=active, rows=rows)
+
+
+def test_backward_empty_rows_and_no_slots():
+    say("attention backward, empty rows")
+    T, H = 40, 16
+    wl = make_custom([T], H=H, D_qk=576, D_v=512, H_idx=0, seed=3, device=DEV)
+    idx = torch.full((T, 32), -1, dtype=torch.int32, device=DEV)
+    out, lse, _ = dsa.dsa_sparse_attn_fwd(wl.q, wl.kv, idx, attn_sink=wl.sink,
+                                          softmax_scale=wl.scale)
+    dout = torch.ones((T, H, 512), dtype=torch.bfloat16, device=DEV)
+    dq, dkv, ds = dsa.dsa_sparse_attn_bwd(wl.q, wl.kv, idx, out, dout, lse, attn_sink=wl.sink,
+                                          softmax_scale=wl.scale)
+    torch.cuda.synchronize()
+    assert torch.all(dq == 0) and torch.all(dkv == 0) and torch.all(ds == 0)
