@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--config", type=int, default=2, help="workload 1..10 (default: 2)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--backward", action="store_true",
+                   help="also time dsa_sparse_attn_bwd on the forward's outputs (shared latent KV "
+                        "workloads), reported as its own stage")
     p.add_argument("--fused", action="store_true",
                    help="one combined indexer + top-K launch instead of score chunks + dsa_topk "
                         "(rows of <= 4096 columns)")
@@ -361,6 +364,41 @@ def main():
     tb = traffic_from_profile(CONFIGS[args.config]["name"])
     if tb is not None:
         roofline["traffic"] = tb
+
+    if args.backward and wl.D_v == 512 and wl.v is None:
+        g = torch.Generator(device=dev).manual_seed(77)
+        dout = (torch.randn(out.shape, generator=g, device=dev) / math.sqrt(wl.D_v)).to(
+            torch.bfloat16)
+        ws = torch.empty(dsa.dsa_sparse_attn_bwd_workspace_bytes(T, wl.H, wl.kv.shape[0],
+                                                                 wl.D_qk, K),
+                         dtype=torch.uint8, device=dev)
+        dq = torch.empty_like(wl.q)
+        dkv = torch.empty((wl.kv.shape[0], wl.D_qk), dtype=torch.bfloat16, device=dev)
+        d_sink = torch.empty((wl.H,), dtype=torch.float32, device=dev)
+
+        def bwd():
+            dsa.dsa_sparse_attn_bwd(wl.q, wl.kv, indices, out, dout, lse, topk_length=topk_length,
+                                    attn_sink=wl.sink, softmax_scale=wl.scale, workspace=ws,
+                                    dq=dq, dkv=dkv, d_sink=d_sink)
+        for _ in range(max(1, args.warmup)):
+            bwd()
+        torch.cuda.synchronize()
+        bt = []
+        for _ in range(max(1, args.steps // 2)):
+            b0 = torch.cuda.Event(enable_timing=True)
+            b1 = torch.cuda.Event(enable_timing=True)
+            b0.record(stream)
+            bwd()
+            b1.record(stream)
+            torch.cuda.synchronize()
+            bt.append(b0.elapsed_time(b1))
+        bms = float(np.mean(bt))
+        # the five products per valid slot and head: s, dP, dq, dk, dv
+        bflop = 2.0 * (3 * wl.D_qk + 2 * wl.D_v) * wl.H * cnt["valid_slots"]
+        stages["attention_backward"] = {"ms": bms, "tflops": bflop / bms / 1e9,
+                                        "frac_bf16_peak": bflop / bms / 1e9 / PEAK_BF16_TFLOPS,
+                                        "algorithmic_flop": bflop,
+                                        "dkv_atomic_bytes": 4.0 * wl.D_qk * cnt["valid_slots"]}
 
     rec = {
         "metric": METRIC, "value": attn_tflops, "unit": "TFLOP/s", "n_gpus": 1,
