@@ -398,7 +398,7 @@ def main():
         stages["attention_backward"] = {"ms": bms, "tflops": bflop / bms / 1e9,
                                         "frac_bf16_peak": bflop / bms / 1e9 / PEAK_BF16_TFLOPS,
                                         "algorithmic_flop": bflop,
-                                        "dkv_atomic_bytes": 4.0 * wl.D_qk * cnt["valid_slots"]}
+                                        "dkv_row_bytes": 2.0 * wl.D_qk * cnt["valid_slots"]}
 
     rec = {
         "metric": METRIC, "value": attn_tflops, "unit": "TFLOP/s", "n_gpus": 1,

@@ -293,15 +293,26 @@ int dsa_sparse_attn_fwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk, con
   return launched(fn, dsa::launch_sparse_attn(a, D_qk, D_v, (hipStream_t)stream));
 }
 
+static int64_t up256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Statistics [T_q, H] x 2, the fp32 dkv accumulator, and the sort arrays.
 static int64_t bwd_fixed_bytes(int64_t T_q, int32_t H, int64_t T_kv, int32_t D_qk) {
-  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
-  return up(T_q * H * 4) * 2 + up(T_kv * D_qk * 4);
+  return up256(T_q * H * 4) * 2 + up256(T_kv * D_qk * 4) + up256(T_kv * 4) * 2 +
+         up256((T_kv + 1) * 4);
 }
 
-// Bytes of one query row of the P buffer (the dS buffer is the same size).
-static int64_t bwd_row_bytes(int32_t H, int32_t k_width) {
+// Per query row of a chunk: P and dS (bf16 [Kw, HP]), the dkv rows of its
+// slots (bf16 [parts, Kw, D_qk]) and its entries of the sorted slot list.
+struct BwdRow {
+  int64_t p, c, l;
+};
+static BwdRow bwd_row_bytes(int32_t H, int32_t k_width, int32_t D_qk) {
   const int64_t hp = (H + 31) / 32 * 32, kw = ((int64_t)k_width + 31) / 32 * 32;
-  return kw * hp * 2;  // bf16
+  const int64_t parts = hp % 64 == 0 ? hp / 64 : hp / 32;
+  return BwdRow{kw * hp * 2, parts * kw * D_qk * 2, kw * 4};
+}
+static int64_t bwd_chunk_bytes(const BwdRow& r, int64_t rows) {
+  return 2 * up256(rows * r.p) + up256(rows * r.c) + up256(rows * r.l);
 }
 
 int64_t dsa_sparse_attn_bwd_workspace_bytes(int64_t T_q, int32_t H, int64_t T_kv, int32_t D_qk,
@@ -309,10 +320,11 @@ int64_t dsa_sparse_attn_bwd_workspace_bytes(int64_t T_q, int32_t H, int64_t T_kv
   if (T_q < 0 || T_q > INT32_MAX || H < 1 || H > DSA_MAX_HEADS || T_kv < 0 || T_kv > INT32_MAX ||
       (D_qk != 576 && D_qk != 512) || k_width < 0)
     return -1;
-  const int64_t row = bwd_row_bytes(H, k_width);
-  int64_t rows = row ? ((int64_t)1 << 29) / row : T_q;  // P + dS within 1 GiB
+  const BwdRow row = bwd_row_bytes(H, k_width, D_qk);
+  const int64_t per = 2 * row.p + row.c + row.l;
+  int64_t rows = per ? ((int64_t)1 << 32) / per : T_q;  // chunk buffers within 4 GiB
   rows = rows < 1 ? 1 : (rows > T_q ? T_q : rows);
-  return bwd_fixed_bytes(T_q, H, T_kv, D_qk) + (rows * row + 255) / 256 * 256 * 2;
+  return bwd_fixed_bytes(T_q, H, T_kv, D_qk) + bwd_chunk_bytes(row, rows);
 }
 
 int dsa_sparse_attn_bwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk, const void* kv,
@@ -344,14 +356,12 @@ int dsa_sparse_attn_bwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk, con
           DSA_ERR_VALUE, "%s: q, kv, out, dout, dq, dkv need 16-byte and workspace 256-byte "
           "alignment", fn);
   const int64_t fixed = bwd_fixed_bytes(T_q, H, T_kv, D_qk);
-  const int64_t row = bwd_row_bytes(H, k_width);
-  const int64_t per_row_ws = (row + 255) / 256 * 256 * 2;  // P and dS, one row each
-  REQUIRE(workspace && workspace_bytes >= fixed + per_row_ws, DSA_ERR_VALUE,
+  const BwdRow row = bwd_row_bytes(H, k_width, D_qk);
+  REQUIRE(workspace && workspace_bytes >= fixed + bwd_chunk_bytes(row, 1), DSA_ERR_VALUE,
           "%s: workspace of %lld bytes is below the %lld bytes one row needs", fn,
-          (long long)workspace_bytes, (long long)(fixed + per_row_ws));
+          (long long)workspace_bytes, (long long)(fixed + bwd_chunk_bytes(row, 1)));
   if (T_q == 0 && T_kv == 0 && !d_sink) return DSA_OK;
   if (int rc = check_device(fn)) return rc;
-  auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
   unsigned char* w = (unsigned char*)workspace;
   dsa::BwdArgs a{};
   a.q = (const uint16_t*)q;
@@ -371,16 +381,29 @@ int dsa_sparse_attn_bwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk, con
   a.out = (const uint16_t*)out;
   a.dout = (const uint16_t*)dout;
   a.lse = lse;
-  a.logZ = (float*)w;
-  a.Dsum = (float*)(w + up(T_q * H * 4));
-  a.dkv_ws = (float*)(w + 2 * up(T_q * H * 4));
-  // P and dS buffers of `chunk` rows each
-  const int64_t per_buf = (workspace_bytes - fixed) / 2 / 256 * 256;
-  int64_t chunk = row ? per_buf / row : T_q;
-  chunk = chunk > T_q ? T_q : chunk;
-  if (chunk < 1) chunk = 1;
-  a.wsP = (uint16_t*)(w + fixed);
-  a.wsD = (uint16_t*)(w + fixed + up(chunk * row));
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    unsigned char* p = w + off;
+    off += up256(bytes);
+    return p;
+  };
+  a.logZ = (float*)take(T_q * H * 4);
+  a.Dsum = (float*)take(T_q * H * 4);
+  a.dkv_ws = (float*)take(T_kv * D_qk * 4);
+  a.cnt = (int32_t*)take(T_kv * 4);
+  a.cursor = (int32_t*)take(T_kv * 4);
+  a.offs = (int32_t*)take((T_kv + 1) * 4);
+  // the largest chunk of rows whose buffers fit the rest of the workspace
+  int64_t chunk = T_q > 0 ? T_q : 1;
+  while (chunk > 1 && fixed + bwd_chunk_bytes(row, chunk) > workspace_bytes) {
+    const int64_t per = 2 * row.p + row.c + row.l;
+    const int64_t fit = per ? (workspace_bytes - fixed) / per : chunk;
+    chunk = fit < chunk ? (fit > 1 ? fit : 1) : chunk - 1;
+  }
+  a.wsP = (uint16_t*)take(chunk * row.p);
+  a.wsD = (uint16_t*)take(chunk * row.p);
+  a.wsC = (uint16_t*)take(chunk * row.c);
+  a.list = (int32_t*)take(chunk * row.l);
   a.Kw = (k_width + 31) / 32 * 32;
   a.dq = (uint16_t*)dq;
   a.dkv = (uint16_t*)dkv;

@@ -84,6 +84,13 @@ struct BwdArgs {
   float* Dsum;              // workspace [T_q, H]
   uint16_t* wsP;            // workspace [chunk, Kw, 32*ceil(H/32)] bf16
   uint16_t* wsD;            // same
+  uint16_t* wsC;            // workspace [nparts, chunk, Kw, D_qk] bf16: dkv row per slot
+  int32_t* cnt;             // workspace [T_kv]: slots per KV row (chunk)
+  int32_t* offs;            // workspace [T_kv + 1]: list offsets
+  int32_t* cursor;          // workspace [T_kv]
+  int32_t* list;            // workspace [chunk * Kw]: slot rows grouped by KV row
+  int nparts;               // head parts of the dkv pass (64 heads each)
+  int64_t chunk_rows;       // rows of the P / dS / C buffers
   int Kw;                   // k_width rounded up to 32
   uint16_t* dq;             // [T_q, H, D_qk] bf16
   float* dkv_ws;            // workspace [T_kv, D_qk] fp32
@@ -92,8 +99,6 @@ struct BwdArgs {
   int64_t row0;             // first row of the current chunk
 };
 
-// Rows of P and dS that ws_rows_bytes of workspace hold.
-size_t sparse_attn_bwd_chunk_rows(int64_t T_q, int H, int k_width, size_t ws_rows_bytes);
 hipError_t launch_sparse_attn_bwd(BwdArgs a, int64_t chunk, hipStream_t st);
 
 }  // namespace dsa

@@ -24,7 +24,11 @@
 //  * bwd_dq_kernel: dq = dS . K with both operands read transposed from LDS
 //    (ds_read_b64_tr_b16), two waves per 32-head block splitting the dims.
 //  * bwd_dkv_kernel: per tile, dS^T . q + P^T . dout (the query's q and dout
-//    staged in LDS) added to an fp32 workspace with coalesced atomics.
+//    staged in LDS), each slot's row written once as bf16 (per 64-head part).
+//  * bwd_count / bwd_scan / bwd_place: a counting sort of the chunk's valid
+//    slots by KV row, giving each KV row the list of rows written for it.
+//  * bwd_reduce_kernel: one workgroup per KV row sums its list (and parts) in
+//    fp32 into the dkv workspace; no atomics touch the data.
 //  * bwd_convert_kernel: fp32 workspace -> bf16 dkv.
 #include "dsa_device.h"
 #include "dsa_launch.h"
@@ -341,16 +345,106 @@ __global__ __launch_bounds__(NWD * 64) void bwd_dkv_kernel(BwdArgs a) {
         }
       }
     }
-    // C: lane -> dim column, slot rows crow(i)
+    // C: lane -> dim column, slot rows crow(i); the row of slot s of this
+    // head part goes to wsC[part][rc][s] (bf16)
+    uint16_t* crow_base = a.wsC + ((int64_t)(hc0 / HC) * a.chunk_rows + rc) * a.Kw * DQK;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int32_t id = s_ids[crow(i, half)];
-      if (id >= 0) {
+      const int s = tl * kBT + crow(i, half);
 #pragma unroll
-        for (int b = 0; b < BPW; ++b)
-          atomicAdd(a.dkv_ws + (int64_t)id * DQK + (wave * BPW + b) * 32 + r32, acc[b][i]);
+      for (int b = 0; b < BPW; ++b)
+        crow_base[(int64_t)s * DQK + (wave * BPW + b) * 32 + r32] =
+            (uint16_t)f32_to_bf16_bits(acc[b][i]);
+    }
+  }
+}
+
+// ---------------------------------------------- sort of the slots by KV row --
+__global__ __launch_bounds__(256) void bwd_count_kernel(BwdArgs a) {
+  const int64_t t = a.row0 + blockIdx.x;
+  const int L = row_len(a, t);
+  for (int s = threadIdx.x; s < L; s += 256) {
+    const int32_t v = a.indices[t * a.ld_idx + s];
+    if (v >= 0 && v < a.T_kv) atomicAdd(&a.cnt[v], 1);
+  }
+}
+
+// offs = exclusive prefix sum of cnt (T_kv + 1 entries); cursor = 0.
+__global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
+  __shared__ int32_t s_w[16];
+  __shared__ int32_t s_carry;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int64_t base = 0; base <= a.T_kv; base += 1024) {
+    const int64_t i = base + tid;
+    const int32_t v = i < a.T_kv ? a.cnt[i] : 0;
+    int32_t incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int32_t o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) s_w[wave] = incl;
+    __syncthreads();
+    int32_t before = s_carry;
+    for (int w = 0; w < wave; ++w) before += s_w[w];
+    if (i <= a.T_kv) a.offs[i] = before + incl - v;
+    if (i < a.T_kv) a.cursor[i] = 0;
+    __syncthreads();
+    if (tid == 1023) s_carry = before + incl;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void bwd_place_kernel(BwdArgs a) {
+  const int64_t rc = blockIdx.x;
+  const int64_t t = a.row0 + rc;
+  const int L = row_len(a, t);
+  for (int s = threadIdx.x; s < L; s += 256) {
+    const int32_t v = a.indices[t * a.ld_idx + s];
+    if (v >= 0 && v < a.T_kv) {
+      const int32_t p = a.offs[v] + atomicAdd(&a.cursor[v], 1);
+      a.list[p] = (int32_t)(rc * a.Kw + s);
+    }
+  }
+}
+
+// dkv_ws[r] += the sum of the rows listed for KV row r (all head parts).
+// 256 threads: three rows at a time, 72 threads x 8 columns per row.
+template <int DQK>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
+  constexpr int CPR = DQK / 8;  // 16-byte chunks per row
+  constexpr int RPI = 256 / CPR;
+  __shared__ float s_acc[RPI][DQK];
+  const int64_t r = blockIdx.x;
+  const int32_t b = a.offs[r], e = a.offs[r + 1];
+  if (b == e) return;  // uniform
+  const int tid = threadIdx.x;
+  const int ro = tid / CPR, ch = tid - ro * CPR;
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (ro < RPI) {
+    const int64_t part_stride = a.chunk_rows * a.Kw;
+    for (int32_t p = b + ro; p < e; p += RPI) {
+      const int64_t c = a.list[p];
+      for (int part = 0; part < a.nparts; ++part) {
+        const u32x4 v = load16(a.wsC + (c + part * part_stride) * DQK + 8 * ch);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] += bf16_bits_to_f32(v[k] & 0xffffu);
+          acc[2 * k + 1] += bf16_bits_to_f32(v[k] >> 16);
+        }
       }
     }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s_acc[ro][8 * ch + k] = acc[k];
+  }
+  __syncthreads();
+  for (int d = tid; d < DQK; d += 256) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < RPI; ++k) sum += s_acc[k][d];
+    a.dkv_ws[r * DQK + d] += sum;
   }
 }
 
@@ -370,6 +464,8 @@ hipError_t launch_bwd_nw(BwdArgs a, int64_t chunk, hipStream_t st) {
   constexpr int NWD = DQK == 576 ? 6 : 4;
   constexpr int HP = NW * 32;
   constexpr int HC = HP % 64 == 0 ? 64 : 32;
+  a.nparts = HP / HC;
+  a.chunk_rows = chunk;
   for (int64_t r0 = 0; r0 < a.T_q; r0 += chunk) {
     a.row0 = r0;
     const int64_t n = a.T_q - r0 < chunk ? a.T_q - r0 : chunk;
@@ -380,19 +476,19 @@ hipError_t launch_bwd_nw(BwdArgs a, int64_t chunk, hipStream_t st) {
     hipLaunchKernelGGL((bwd_dq_kernel<DQK, NW>), dim3((unsigned)n), dim3(NW * 128), 0, st, a);
     hipLaunchKernelGGL((bwd_dkv_kernel<DQK, NW, NWD>), dim3((unsigned)(n * (HP / HC))),
                        dim3(NWD * 64), 0, st, a);
+    if (a.T_kv > 0) {
+      hipLaunchKernelGGL(bwd_fill_kernel, dim3((unsigned)((a.T_kv + 255) / 256)), dim3(256), 0,
+                         st, reinterpret_cast<float*>(a.cnt), a.T_kv);
+      hipLaunchKernelGGL(bwd_count_kernel, dim3((unsigned)n), dim3(256), 0, st, a);
+      hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, st, a);
+      hipLaunchKernelGGL(bwd_place_kernel, dim3((unsigned)n), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((bwd_reduce_kernel<DQK>), dim3((unsigned)a.T_kv), dim3(256), 0, st, a);
+    }
   }
   return hipGetLastError();
 }
 
 }  // namespace
-
-size_t sparse_attn_bwd_chunk_rows(int64_t T_q, int H, int k_width, size_t ws_rows_bytes) {
-  const int64_t HP = (H + 31) / 32 * 32;
-  const int64_t Kw = (k_width + kBT - 1) / kBT * kBT;
-  const int64_t per_row = 2 * Kw * HP * 2;  // P and dS, bf16
-  int64_t rows = per_row ? (int64_t)(ws_rows_bytes / per_row) : T_q;
-  return (size_t)(rows < T_q ? rows : T_q);
-}
 
 hipError_t launch_sparse_attn_bwd(BwdArgs a, int64_t chunk, hipStream_t st) {
   const int64_t nkv = a.T_kv * a.D_qk;

@@ -305,9 +305,10 @@ int dsa_sparse_attn_fwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk,
 /*
  * dsa_sparse_attn_bwd_workspace_bytes - device workspace dsa_sparse_attn_bwd
  * uses for these sizes: fp32 statistics [T_q, H] x 2, an fp32 dkv
- * accumulator [T_kv, D_qk], and bf16 P / dS rows of up to 1 GiB
- * (P and dS of min(T_q, rows that fit) query rows at a time). Returns -1
- * for sizes out of contract.
+ * accumulator [T_kv, D_qk], the slot-sort arrays [T_kv], and per query row
+ * of a chunk its bf16 P and dS, the bf16 dkv rows of its slots and its slot
+ * list, for chunks of up to 4 GiB (min(T_q, rows that fit) rows at a
+ * time). Returns -1 for sizes out of contract.
  */
 int64_t dsa_sparse_attn_bwd_workspace_bytes(int64_t T_q, int32_t H, int64_t T_kv, int32_t D_qk,
                                             int32_t k_width);
@@ -337,14 +338,17 @@ int64_t dsa_sparse_attn_bwd_workspace_bytes(int64_t T_q, int32_t H, int64_t T_kv
  *   dq          device bf16 [T_q, H, D_qk] output
  *   dkv         device bf16 [T_kv, D_qk] output (contiguous)
  *   d_sink      device fp32 [H] output or NULL (0 when attn_sink is NULL)
- *   workspace   device memory of workspace_bytes >=
- *               dsa_sparse_attn_bwd_workspace_bytes(...) would give for one
- *               row of P / dS (a larger workspace processes more rows per
- *               pass), 256-byte aligned, owned by the caller
+ *   workspace   device memory, 256-byte aligned, owned by the caller, of
+ *               workspace_bytes bytes: at least what one query row needs
+ *               (fixed statistics plus one row of the chunk buffers);
+ *               dsa_sparse_attn_bwd_workspace_bytes gives a size that holds
+ *               up to 4 GiB of chunk buffers, and a larger workspace
+ *               processes more query rows per pass
  * bf16 MFMA products with fp32 accumulation; P and dS are rounded to bf16
- * before the dq and dkv products; dkv accumulates in fp32 with atomics (the
- * summation order, and so the last bits of dkv, may vary between runs);
- * d_sink is summed in a fixed order.
+ * before the dq and dkv products, and each slot's dkv row (summed over the
+ * heads) to bf16 before the per-KV-row sum, which is fp32; the order of
+ * that sum follows the slot sort, which uses atomic counters, so the last
+ * bits of dkv may vary between runs. d_sink is summed in a fixed order.
  * Errors: the checks of dsa_sparse_attn_fwd, DSA_ERR_VALUE for D_v != 512,
  * a separate V, or a workspace too small for one row.
  */

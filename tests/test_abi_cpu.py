@@ -237,9 +237,12 @@ def test_python_binding_type_and_shape_errors():
 
 def test_backward_workspace_size_rule():
     lib = dsa.load_library()
-    # statistics + dkv accumulator + P and dS of every row when they fit in 1 GiB
+    # statistics, dkv accumulator and sort arrays, then P, dS, the per-slot dkv
+    # rows and the slot list of every row when they fit in 4 GiB
     n = lib.dsa_sparse_attn_bwd_workspace_bytes(256, 16, 256, 576, 64)
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    assert n == 2 * up(256 * 16 * 4) + up(256 * 576 * 4) + 2 * up(256 * 64 * 32 * 2)
+    fixed = 2 * up(256 * 16 * 4) + up(256 * 576 * 4) + 2 * up(256 * 4) + up(257 * 4)
+    rows = 2 * up(256 * 64 * 32 * 2) + up(256 * 64 * 576 * 2) + up(256 * 64 * 4)
+    assert n == fixed + rows
     assert lib.dsa_sparse_attn_bwd_workspace_bytes(10, 0, 10, 576, 8) == -1
     assert lib.dsa_sparse_attn_bwd_workspace_bytes(10, 8, 10, 256, 8) == -1
