@@ -164,13 +164,18 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
   auto prep_copy = [&](uint32_t stage, int32_t idv) -> CopySrc {
     CopySrc cs;
     const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_zero_row);
+    int32_t idg[C::GPW];
+#pragma unroll
+    for (int gi = 0; gi < C::GPW; ++gi)
+      idg[gi] = __shfl(idv, 8 * (C::GPW * wave + gi) + crow, kWave);  // all shuffles first
 #pragma unroll
     for (int gi = 0; gi < C::GPW; ++gi) {
       const int g = C::GPW * wave + gi;
-      const int32_t id = __shfl(idv, 8 * g + crow, kWave);
       const int chunk = (lane & 7) ^ swz(crow, g);
-      cs.k[gi] = (id >= 0 ? a.k + (int64_t)id * a.ld_k : zero) + 8 * chunk;
-      if constexpr (!SHARED) cs.v[gi] = (id >= 0 ? a.v + (int64_t)id * a.ld_v : zero) + 8 * chunk;
+      const bool ok = idg[gi] >= 0;
+      const uint64_t row = ok ? (uint64_t)(uint32_t)idg[gi] : 0ull;
+      cs.k[gi] = (ok ? a.k : zero) + row * (uint64_t)a.ld_k + 8 * chunk;
+      if constexpr (!SHARED) cs.v[gi] = (ok ? a.v : zero) + row * (uint64_t)a.ld_v + 8 * chunk;
     }
     if constexpr (SHARED) cs.v[0] = nullptr;
     cs.m0 = __builtin_amdgcn_readfirstlane(stage + 1024u * (uint32_t)(C::GPW * wave));
@@ -301,38 +306,33 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
 
       // ---- softmax weights against the fixed reference, exp2 domain ----
       // Tiles whose 32 slots are all valid (the usual case inside a compact
-      // prefix) skip the per-key mask. Scale and reference fold into one FMA
-      // (scale > 0, so the raw max scales to the scaled max). Once a pass has
-      // overflowed, its results are discarded and the row is run again, so
-      // no select guards the weights against it.
+      // prefix) skip the mask; otherwise masked scores become -inf once, so
+      // the max ignores them and their weights come out as exp2(-inf) = 0.
+      // Scale and reference fold into one FMA (scale > 0, so the raw max
+      // scales to the scaled max). Until some key of the row is valid the
+      // reference is -inf and every score of the tile is -inf: any finite
+      // offset then gives zero weights. Once a pass has overflowed, its
+      // results are discarded and the row is run again, so no select guards
+      // the weights against it.
       const bool full = mask_cur == 0xFFFFFFFFu;  // uniform
-      float mloc = -__builtin_inff();
-      if (full) {
+      if (!full) {
+        const uint32_t mh = mask_cur >> (4 * half);  // key 8*(i/4) + 4*half + i%4
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sc[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = 8 * (i >> 2) + 4 * half + (i & 3);
-          mloc = fmaxf(mloc, ((mask_cur >> key) & 1u) ? sc[i] : -__builtin_inff());
-        }
+        for (int i = 0; i < 16; ++i)
+          if (!((mh >> (8 * (i >> 2) + (i & 3))) & 1u)) sc[i] = -__builtin_inff();
       }
-      mloc = fmaxf(mloc, shfl_xor_f(mloc, 32)) * a.scale_log2;
+      float mloc = sc[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, sc[i]);
+      mloc = halfwave_max(mloc) * a.scale_log2;
       m_true = fmaxf(m_true, mloc);
       if (m_ref == -__builtin_inff()) m_ref = mloc;  // first tile with a valid key
       overflow |= mloc > m_ref + kHeadroom;
-      const float neg_ref = -m_ref;
+      const float neg_ref = m_ref == -__builtin_inff() ? 0.f : -m_ref;
       float p[16];
       float psum = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(sc[i], a.scale_log2, neg_ref));
-      if (!full) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = 8 * (i >> 2) + 4 * half + (i & 3);
-          p[i] = ((mask_cur >> key) & 1u) ? p[i] : 0.f;
-        }
-      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) psum += p[i];
       l_run += psum;
@@ -364,38 +364,29 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int b = 0; b < 2; ++b)
             va[pp][b] = vbase + 1024 * b + 16 * (4 * (pp ^ (li >> 3)) + 2 * ((G & 1) ^ b));
-        auto vread = [&](int nb, u32x4* vb) {
-          const int so = (nb >> 1) * 4096;
-          const u32x2 a0 = lds_read_tr16(va[nb & 1][0] + so);
-          const u32x2 a1 = lds_read_tr16(va[nb & 1][1] + so);
-          const u32x2 b0 = lds_read_tr16(va[nb & 1][0] + so + 2048);
-          const u32x2 b1 = lds_read_tr16(va[nb & 1][1] + so + 2048);
-          vb[0] = u32x4{a0.x, a0.y, a1.x, a1.y};
-          vb[1] = u32x4{b0.x, b0.y, b1.x, b1.y};
-        };
-        // Column blocks go in pairs so that consecutive MFMAs never
-        // accumulate into the same block; the next pair's reads are issued
-        // before the current pair's MFMAs.
+        // MFMA f (f = 0 .. 2*NB-1) accumulates column block
+        // nb = 2*(f/4) + f%2 over key half st = (f/2)%2: pairs of blocks, so
+        // consecutive MFMAs never accumulate into the same block. Its V
+        // fragment is read VPF MFMAs ahead.
         static_assert(C::NB % 2 == 0, "column blocks are processed in pairs");
-        u32x4 vcur[4], vnxt[4];
-        vread(0, vcur);
-        vread(1, vcur + 2);
-        static_for<C::NB / 2>([&](auto pc) {
-          constexpr int nb = 2 * decltype(pc)::value;
-          if constexpr (nb + 2 < C::NB) {
-            vread(nb + 2, vnxt);
-            vread(nb + 3, vnxt + 2);
-          }
-          o[nb] = mfma32x32x16(pa[0], vcur[0], o[nb]);
-          copies_at_slot(std::integral_constant<int, C::KS + 2 * nb>{});
-          o[nb + 1] = mfma32x32x16(pa[0], vcur[2], o[nb + 1]);
-          copies_at_slot(std::integral_constant<int, C::KS + 2 * nb + 1>{});
-          o[nb] = mfma32x32x16(pa[1], vcur[1], o[nb]);
-          copies_at_slot(std::integral_constant<int, C::KS + 2 * nb + 2>{});
-          o[nb + 1] = mfma32x32x16(pa[1], vcur[3], o[nb + 1]);
-          copies_at_slot(std::integral_constant<int, C::KS + 2 * nb + 3>{});
+        auto vfrag = [&](int f) -> u32x4 {
+          const int nb = 2 * (f >> 2) + (f & 1), st = (f >> 1) & 1;
+          const int so = (nb >> 1) * 4096 + st * 2048;
+          const u32x2 x0 = lds_read_tr16(va[nb & 1][0] + so);
+          const u32x2 x1 = lds_read_tr16(va[nb & 1][1] + so);
+          return u32x4{x0.x, x0.y, x1.x, x1.y};
+        };
+        constexpr int VPF = 4;
+        u32x4 vq[VPF];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) vcur[i] = vnxt[i];
+        for (int i = 0; i < VPF; ++i) vq[i] = vfrag(i);
+        static_for<2 * C::NB>([&](auto fc) {
+          constexpr int f = decltype(fc)::value;
+          constexpr int nb = 2 * (f >> 2) + (f & 1), st = (f >> 1) & 1;
+          const u32x4 cur = vq[f % VPF];
+          if constexpr (f + VPF < 2 * C::NB) vq[f % VPF] = vfrag(f + VPF);
+          o[nb] = mfma32x32x16(pa[st], cur, o[nb]);
+          copies_at_slot(std::integral_constant<int, C::KS + f>{});
         });
       }
       mask_cur = mask_next;
