@@ -108,6 +108,32 @@ __device__ __forceinline__ void dma16_imm(const void* gptr, uint32_t lds_base) {
                : "memory");
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor words (gfx9: 32-bit data, stride 0, range checked)
+// over `bytes` bytes at `base`; base and bytes must be wave-uniform.
+__device__ __forceinline__ i32x4 buffer_rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Asynchronous 16-byte-per-lane copy through a buffer descriptor:
+// bytes voff + IMM .. +15 of the buffer -> LDS lds_base + IMM + 16*l (the
+// same addressing as dma16_imm, measured on the device). Lanes whose range
+// falls outside the descriptor write zeros (also measured).
+template <int IMM>
+__device__ __forceinline__ void dma16_buf_imm(uint32_t voff, i32x4 rsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen offset:%3 lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_base), "i"(IMM)
+               : "memory");
+}
+
 // s_waitcnt vmcnt(0) through the builtin, so that the compiler's own wait
 // tracking also knows that every earlier vector-memory load has completed.
 __device__ __forceinline__ void wait_vmcnt0() {

@@ -61,6 +61,10 @@ struct AttnArgs {
   uint16_t* out;
   float* lse;
   float* max_logits;
+  // Filled by the launcher: byte extents of K and V as read through buffer
+  // descriptors, and their row strides in bytes.
+  uint32_t span_k, span_v;
+  uint32_t row_bytes_k, row_bytes_v;
 };
 
 hipError_t launch_sparse_attn(const AttnArgs& a, int D_qk, int D_v, hipStream_t st);

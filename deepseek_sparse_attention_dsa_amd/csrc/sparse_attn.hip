@@ -103,7 +103,7 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl<0, N>(f);
 }
 
-template <int DQK, int DV, bool SHARED, int NW>
+template <int DQK, int DV, bool SHARED, int NW, bool BUF>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
   using C = Cfg<DQK, DV, SHARED, NW>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * C::STAGE_BYTES];
@@ -155,15 +155,26 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
   // instruction's immediate, which shifts the LDS address as well, hence
   // M0 = block base - 128*s.
   const uint32_t smem_base = lds_addr(smem);
+  // Copy sources. BUF: 32-bit byte offsets into buffer descriptors over K
+  // and V (rows of at most 2^31 bytes in all); a masked row gets an offset
+  // past the descriptor's range, which the hardware reads as zeros. Else
+  // 64-bit addresses, with masked rows read from a zero constant.
   struct CopySrc {
-    const uint16_t* k[C::GPW];  // per row group: this lane's row + chunk
-    const uint16_t* v[SHARED ? 1 : C::GPW];
+    const uint16_t* k[BUF ? 1 : C::GPW];  // per row group: this lane's row + chunk
+    const uint16_t* v[(BUF || SHARED) ? 1 : C::GPW];
+    uint32_t ko[BUF ? C::GPW : 1];
+    uint32_t vo[(BUF && !SHARED) ? C::GPW : 1];
     uint32_t m0;                // stage + first block of this wave's groups
   };
+  i32x4 rsrc_k{}, rsrc_v{};
+  if constexpr (BUF) {
+    rsrc_k = buffer_rsrc_words(a.k, a.span_k);
+    if constexpr (!SHARED) rsrc_v = buffer_rsrc_words(a.v, a.span_v);
+  }
+  constexpr uint32_t kPastRange = 0x80000000u;  // > every descriptor range, no wrap
   // idv: validated id of tile row lane % 32 (-1: zero row).
   auto prep_copy = [&](uint32_t stage, int32_t idv) -> CopySrc {
     CopySrc cs;
-    const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_zero_row);
     int32_t idg[C::GPW];
 #pragma unroll
     for (int gi = 0; gi < C::GPW; ++gi)
@@ -173,11 +184,19 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
       const int g = C::GPW * wave + gi;
       const int chunk = (lane & 7) ^ swz(crow, g);
       const bool ok = idg[gi] >= 0;
-      const uint64_t row = ok ? (uint64_t)(uint32_t)idg[gi] : 0ull;
-      cs.k[gi] = (ok ? a.k : zero) + row * (uint64_t)a.ld_k + 8 * chunk;
-      if constexpr (!SHARED) cs.v[gi] = (ok ? a.v : zero) + row * (uint64_t)a.ld_v + 8 * chunk;
+      if constexpr (BUF) {
+        // ids < 2^24 and row strides < 2^24 bytes here (the host checks the
+        // span), so one 24-bit multiply-add forms the offset
+        cs.ko[gi] = ok ? __umul24((uint32_t)idg[gi], a.row_bytes_k) + 16u * chunk : kPastRange;
+        if constexpr (!SHARED)
+          cs.vo[gi] = ok ? __umul24((uint32_t)idg[gi], a.row_bytes_v) + 16u * chunk : kPastRange;
+      } else {
+        const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_zero_row);
+        const uint64_t row = ok ? (uint64_t)(uint32_t)idg[gi] : 0ull;
+        cs.k[gi] = (ok ? a.k : zero) + row * (uint64_t)a.ld_k + 8 * chunk;
+        if constexpr (!SHARED) cs.v[gi] = (ok ? a.v : zero) + row * (uint64_t)a.ld_v + 8 * chunk;
+      }
     }
-    if constexpr (SHARED) cs.v[0] = nullptr;
     cs.m0 = __builtin_amdgcn_readfirstlane(stage + 1024u * (uint32_t)(C::GPW * wave));
     return cs;
   };
@@ -188,11 +207,15 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
     constexpr int J = decltype(jc)::value;
     if constexpr (J < C::K_PER_WAVE) {
       constexpr int GI = J % C::GPW, S = J / C::GPW;
-      dma16_imm<128 * S>(cs.k[GI], cs.m0 + (uint32_t)(1024 * (4 * S + GI) - 128 * S));
+      const uint32_t m0 = cs.m0 + (uint32_t)(1024 * (4 * S + GI) - 128 * S);
+      if constexpr (BUF) dma16_buf_imm<128 * S>(cs.ko[GI], rsrc_k, m0);
+      else dma16_imm<128 * S>(cs.k[GI], m0);
     } else {
       constexpr int U = J - C::K_PER_WAVE;
       constexpr int GI = U % C::GPW, S = U / C::GPW;
-      dma16_imm<128 * S>(cs.v[GI], cs.m0 + (uint32_t)(C::V_BASE + 1024 * (4 * S + GI) - 128 * S));
+      const uint32_t m0 = cs.m0 + (uint32_t)(C::V_BASE + 1024 * (4 * S + GI) - 128 * S);
+      if constexpr (BUF) dma16_buf_imm<128 * S>(cs.vo[GI], rsrc_v, m0);
+      else dma16_imm<128 * S>(cs.v[GI], m0);
     }
   };
   auto copy_all = [&](const CopySrc& cs) {
@@ -269,12 +292,15 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
       };
 
       // ---- S^T = K_tile . Q^T: lane holds head r32, keys 8*(i/4)+4*half+(i%4) ----
-      // One accumulator chain: the copies interleaved with the k-steps keep
-      // dependent MFMAs apart, and a second chain would cost 16 registers and
-      // 16 adds per tile.
+      // One accumulator chain (dependent MFMAs of one shape issue back to
+      // back; a second chain would cost 16 registers and 16 adds per tile).
+      // The chain is written as inline MFMAs so that S accumulates in VGPRs:
+      // the compiler keeps every MFMA result of this kernel in AGPRs, which
+      // O fills completely, and would otherwise move S and one O block
+      // between the two files every tile. The wait states that the compiler
+      // inserts after its own MFMAs are given explicitly after the chain
+      // (the softmax reads S with VALU instructions).
       f32x16 sc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sc[i] = 0.f;
       {
         // Operand reads run PF k-steps ahead of the MFMAs that use them.
         // k-step ks: the lane reads row r32 (group g = r32/8, r = r32%8),
@@ -297,9 +323,13 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
           constexpr int ks = decltype(kc)::value;
           const u32x4 cur = af[ks % PF];
           if constexpr (ks + PF < C::KS) af[ks % PF] = kread(ks + PF);
-          sc = mfma32x32x16(cur, qf[ks], sc);
+          if constexpr (ks == 0)
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(sc) : "v"(cur), "v"(qf[ks]));
+          else
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sc) : "v"(cur), "v"(qf[ks]));
           copies_at_slot(std::integral_constant<int, ks>{});
         });
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sc));
       }
 
       if (copy_next) id_next = (it + 2 < n_tiles) ? load_id((it + 2) * kBN, key_row) : -1;
@@ -458,25 +488,48 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
   }
 }
 
-template <int DQK, int DV, bool SHARED>
-hipError_t launch_cfg(const AttnArgs& a, hipStream_t st) {
+template <int DQK, int DV, bool SHARED, bool BUF>
+hipError_t launch_nw(const AttnArgs& a, hipStream_t st) {
   const int nw = (a.H + 31) / 32;
   dim3 grid((unsigned)a.T_q);
   switch (nw) {
     case 1:
-      hipLaunchKernelGGL((sparse_attn_kernel<DQK, DV, SHARED, 1>), grid, dim3(64), 0, st, a);
+      hipLaunchKernelGGL((sparse_attn_kernel<DQK, DV, SHARED, 1, BUF>), grid, dim3(64), 0, st, a);
       break;
     case 2:
-      hipLaunchKernelGGL((sparse_attn_kernel<DQK, DV, SHARED, 2>), grid, dim3(128), 0, st, a);
+      hipLaunchKernelGGL((sparse_attn_kernel<DQK, DV, SHARED, 2, BUF>), grid, dim3(128), 0, st, a);
       break;
     case 3:
     case 4:
-      hipLaunchKernelGGL((sparse_attn_kernel<DQK, DV, SHARED, 4>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((sparse_attn_kernel<DQK, DV, SHARED, 4, BUF>), grid, dim3(256), 0, st, a);
       break;
     default:
       return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// Bytes from a row-major matrix's first element to the end of its last row's
+// first `dims` elements (0 without rows).
+int64_t row_span(int64_t rows, int64_t ld, int dims) {
+  return rows > 0 ? ((rows - 1) * ld + dims) * 2 : 0;
+}
+
+template <int DQK, int DV, bool SHARED>
+hipError_t launch_cfg(AttnArgs a, hipStream_t st) {
+  // Buffer-descriptor copies take 32-bit offsets below kPastRange (2^31):
+  // used whenever every K and V byte the kernel reads lies below it.
+  const int64_t sk = row_span(a.T_kv, a.ld_k, DQK);
+  const int64_t sv = SHARED ? 0 : row_span(a.T_kv, a.ld_v, DV);
+  const int64_t lim = (int64_t)1 << 31;
+  if (sk < lim && sv < lim && a.ld_k * 2 < (1 << 24) && a.ld_v * 2 < (1 << 24)) {
+    a.span_k = (uint32_t)sk;
+    a.span_v = (uint32_t)sv;
+    a.row_bytes_k = (uint32_t)(a.ld_k * 2);
+    a.row_bytes_v = (uint32_t)(a.ld_v * 2);
+    return launch_nw<DQK, DV, SHARED, true>(a, st);
+  }
+  return launch_nw<DQK, DV, SHARED, false>(a, st);
 }
 
 }  // namespace

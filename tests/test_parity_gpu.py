@@ -335,6 +335,45 @@ def test_attention_dense_identity_on_gpu():
     assert np.abs(got - ref).max() <= 2e-2 * np.abs(ref).max()
 
 
+@pytest.mark.parametrize("shared", [True, False])
+def test_attention_kv_beyond_2gib(shared):
+    """K (and V) spanning more than 2^31 bytes: the kernel then gathers through
+    64-bit addresses instead of 32-bit buffer offsets. Ids above 2^31 / row
+    bytes are drawn on purpose. The oracle sees only the gathered rows (the
+    attention of a row depends on nothing else), remapped to a compact KV."""
+    Dqk, Dv, H = (576, 512, 64) if shared else (256, 256, 12)
+    T_kv = (1 << 31) // (2 * Dqk) + 40000
+    say("attention KV beyond 2 GiB", shared, T_kv)
+    gen = torch.Generator(device=DEV).manual_seed(11)
+    kv = torch.randn((T_kv, Dqk), generator=gen, device=DEV, dtype=torch.float32)
+    kv = (kv / math.sqrt(Dqk)).to(torch.bfloat16)
+    v = None
+    if not shared:
+        v = (torch.randn((T_kv, Dv), generator=gen, device=DEV) / math.sqrt(Dv)).to(torch.bfloat16)
+    T_q, kw = 24, 96
+    q = (torch.randn((T_q, H, Dqk), generator=gen, device=DEV) / math.sqrt(Dqk)).to(torch.bfloat16)
+    g = np.random.default_rng(5)
+    lo = (1 << 31) // (2 * Dqk) - 2000
+    idx = np.where(g.random((T_q, kw)) < 0.5, g.integers(lo, T_kv, size=(T_q, kw)),
+                   g.integers(0, T_kv, size=(T_q, kw))).astype(np.int64)
+    idx[g.random((T_q, kw)) < 0.05] = -1
+    idx[0, :4] = [T_kv - 1, 0, T_kv - 1, -1]
+    scale = 1.0 / math.sqrt(Dqk)
+    sink = torch.randn((H,), generator=gen, device=DEV)
+    out, lse, mx = dsa.dsa_sparse_attn_fwd(q, kv, torch.from_numpy(idx.astype(np.int32)).to(DEV),
+                                           attn_sink=sink, softmax_scale=scale, v=v, d_v=Dv)
+    torch.cuda.synchronize()
+    uniq = np.unique(idx[idx >= 0])
+    remap = np.full(idx.shape, -1, dtype=np.int32)
+    remap[idx >= 0] = np.searchsorted(uniq, idx[idx >= 0])
+    ut = torch.from_numpy(uniq).to(DEV)
+    kv_small = kv[ut].contiguous()
+    v_small = None if v is None else v[ut].contiguous()
+    del kv, v
+    check_attention(out, lse, mx, q, kv_small, v_small, torch.from_numpy(remap).to(DEV), None,
+                    sink, scale, Dv, np.arange(T_q))
+
+
 # ------------------------------------------------------- named workloads
 
 def _pipeline(wl, max_seqlen=None):
