@@ -156,11 +156,12 @@ __device__ __forceinline__ float halfwave_sums(float a, float b) {
                                                   false);
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
-// max(v[l], v[l ^ 32]) in every lane, through one v_permlane32_swap.
+// max(v[l], v[l ^ 32]) in every lane, through one v_permlane32_swap (IEEE
+// maximum: a NaN operand gives NaN).
 __device__ __forceinline__ float halfwave_max(float v) {
   const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
                                                   false);
-  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(s[0]), __uint_as_float(s[1]));
 }
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, kWave); }
 

@@ -351,11 +351,12 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
         for (int i = 0; i < 16; ++i)
           if (!((mh >> (8 * (i >> 2) + (i & 3))) & 1u)) sc[i] = -__builtin_inff();
       }
+      // IEEE maximum (v_maximum3_f32): no NaN quieting of each operand
       float mloc = sc[0];
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, sc[i]);
+      for (int i = 1; i < 16; ++i) mloc = __builtin_elementwise_maximum(mloc, sc[i]);
       mloc = halfwave_max(mloc) * a.scale_log2;
-      m_true = fmaxf(m_true, mloc);
+      m_true = __builtin_elementwise_maximum(m_true, mloc);
       if (m_ref == -__builtin_inff()) m_ref = mloc;  // first tile with a valid key
       overflow |= mloc > m_ref + kHeadroom;
       const float neg_ref = m_ref == -__builtin_inff() ? 0.f : -m_ref;
