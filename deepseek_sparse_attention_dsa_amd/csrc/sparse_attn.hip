@@ -222,14 +222,27 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
     static_for<NCOPY>([&](auto jc) { copy_one(cs, jc); });
   };
 
+  // The first two tiles' ids are loaded before Q, so that the first copies
+  // can be issued while the Q loads are still in flight.
+  const int32_t id_first = n_tiles > 0 ? load_id(0, key_row) : -1;
+  const int32_t id_second = n_tiles > 1 ? load_id(kBN, key_row) : -1;
+
   // Q fragments (B operand): lane -> head h0 + r32, dims 16*ks + 8*half .. +7.
   u32x4 qf[C::KS];
   {
+    // Unconditional loads (lanes past the last head read the last head's
+    // row, then zero it), so that the compiler's wait for the ids above
+    // counts every Q load as issued after them.
     const int head = h0 + r32;
-    const uint16_t* qrow = a.q + (t * a.H + head) * (int64_t)DQK + 8 * half;
+    const int hq = head < a.H ? head : a.H - 1;
+    const uint16_t* qrow = a.q + (t * a.H + hq) * (int64_t)DQK + 8 * half;
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      qf[ks] = (head < a.H) ? load16(qrow + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
+    for (int ks = 0; ks < C::KS; ++ks) qf[ks] = load16(qrow + 16 * ks);
+    if (h0 + 32 > a.H) {  // uniform: a partial head block
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        if (head >= a.H) qf[ks] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
 
   f32x16 o[C::NB];
@@ -257,11 +270,11 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
     int32_t id_next = -1;
     uint32_t mask_cur = 0;
     if (n_tiles > 0) {
-      const int32_t id0 = valid_id(load_id(0, key_row));
+      const int32_t id0 = valid_id(id_first);
       mask_cur = (uint32_t)ballot(id0 >= 0);  // lanes 0..31 hold rows 0..31
       if (pass == 1) __syncthreads();  // pass 0's last tile is consumed by every wave
       copy_all(prep_copy(smem_base, id0));
-      if (n_tiles > 1) id_next = load_id(kBN, key_row);
+      id_next = id_second;
     }
 
     for (int it = 0; it < n_tiles; ++it) {
