@@ -89,6 +89,19 @@ template <>
 __device__ __forceinline__ float load_w<float>(const float* w, int64_t i) {
   return w[i];
 }
+// Four consecutive weights w[i .. i+3] (i a multiple of 4, w 16-byte aligned).
+template <typename WT>
+__device__ __forceinline__ f32x4 load_w4(const WT* w, int64_t i);
+template <>
+__device__ __forceinline__ f32x4 load_w4<uint16_t>(const uint16_t* w, int64_t i) {
+  const u32x2 v = *reinterpret_cast<const u32x2*>(w + i);
+  return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
+               __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
+}
+template <>
+__device__ __forceinline__ f32x4 load_w4<float>(const float* w, int64_t i) {
+  return *reinterpret_cast<const f32x4*>(w + i);
+}
 
 // D: indexer head dim (64 or 128). MB: number of 32-head blocks (H <= 32*MB).
 // FUSE: the scores of each row stay in LDS (ld is then the column cap, at
@@ -109,7 +122,6 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
   constexpr int LOADS = (CHUNKS + NT - 1) / NT;   // 16-byte loads per thread and tile
   constexpr int NBUF = (FUSE && D == 128) ? 1 : 2;  // key tiles in the LDS ring
   __shared__ __attribute__((aligned(16))) unsigned char ktile[NBUF * TILE_B];
-  __shared__ int32_t s_range[2];
   __shared__ __attribute__((aligned(16))) float s_rows[FUSE ? kIdxWaves * kFuseRowStride : 4];
   static_assert(!FUSE || NBUF * TILE_B >= kIdxWaves * 256 * 4, "select histograms fit the ring");
 
@@ -121,58 +133,39 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
   const int64_t r0 = qblk * kIdxWaves;
   const int64_t cap = T_kv > 0 ? ld : 0;  // longest row length taken (no keys: none)
 
-  // Key range of the workgroup: union of [start, start + len) of its rows.
-  if (threadIdx.x == 0) {
-    int32_t kb = INT32_MAX, ke = 0;
-    for (int i = 0; i < kIdxWaves; ++i) {
-      const int64_t r = r0 + i;
-      if (r < n_rows) {
-        const int64_t t = row_begin + r;
-        const int32_t s0 = row_starts[t];
-        const int32_t n = (int32_t)min((int64_t)seq_lens[t], cap);
-        if (n > 0) {
-          kb = min(kb, s0);
-          ke = max(ke, s0 + n);
-        }
-      }
-    }
-    s_range[0] = kb;
-    s_range[1] = ke;
-  }
-
-  // This wave's query: Q fragments (A operand: lane -> head 32*mb + l%32,
-  // dims 16*ks + 8*half .. +7) and the weights of the 16 heads whose scores
-  // the lane receives per head block: 32*mb + 8*(i/4) + 4*half + i%4.
+  // Rows of the workgroup: lane i < kIdxWaves holds row r0 + i's start and
+  // valid length (>= 0; the range checks of the score writes rely on it).
+  // Every wave forms the key range [kb, kb) of the workgroup from them, the
+  // union of its rows' ranges, so the first key tile is requested before
+  // anything else and without a barrier.
   const int64_t r = r0 + wave;
   const bool live = r < n_rows;
   const int64_t t = row_begin + (live ? r : 0);
-  const int32_t qstart = live ? row_starts[t] : 0;
-  // valid columns of the row, >= 0 (the range checks of the score writes rely on it)
-  const int32_t qlen = live ? (int32_t)max((int64_t)0, min((int64_t)seq_lens[t], cap)) : 0;
-  u32x4 qa[MB][KS];
-  float wv[MB][16];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int head = mb * 32 + (lane & 31);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qa[mb][ks] = (live && head < H) ? load16(q + ((t * H + head) * D + ks * 16 + 8 * half))
-                                      : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int oh = mb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-      wv[mb][i] = (live && oh < H) ? load_w<WT>(w, t * H + oh) : 0.0f;
-    }
+  int32_t m_s0 = 0, m_n = 0;
+  if (lane < kIdxWaves && r0 + lane < n_rows) {
+    const int64_t tt = row_begin + r0 + lane;
+    m_s0 = row_starts[tt];
+    m_n = (int32_t)max((int64_t)0, min((int64_t)seq_lens[tt], cap));
   }
-  __syncthreads();
-  const int32_t kb = s_range[0];
-  const int32_t ke = s_range[1];
+  int32_t kb = m_n > 0 ? m_s0 : INT32_MAX, ke = m_n > 0 ? m_s0 + m_n : 0;
+#pragma unroll
+  for (int m = 1; m < kIdxWaves; m <<= 1) {
+    kb = min(kb, __shfl_xor(kb, m, kWave));
+    ke = max(ke, __shfl_xor(ke, m, kWave));
+  }
+  kb = __builtin_amdgcn_readfirstlane(kb);
+  ke = __builtin_amdgcn_readfirstlane(ke);
+  const int32_t qstart = __shfl(m_s0, wave, kWave);
+  const int32_t qlen = __shfl(m_n, wave, kWave);
   if (kb >= ke) {  // uniform: no row of the workgroup has a key
     if constexpr (FUSE)
       if (live)
         wave_topk_row(s_rows, 0, 0, nullptr, fa, r);  // writes the empty row
     return;
   }
+
+  u32x4 qa[MB][KS];  // filled after the first key tile is requested
+  float wv[MB][16];
 
   // Staging of keys [k0, k0 + 64): thread -> chunks c = tid + NT*i.
   u32x4 stage[LOADS];
@@ -267,6 +260,49 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
   // outside its own range are computed and their stores dropped). The first
   // pending write targets columns before the row, so it is dropped too.
   load_tile(kb);
+
+  // This wave's query: Q fragments (A operand: lane -> head 32*mb + l%32,
+  // dims 16*ks + 8*half .. +7) and the weights of the 16 heads whose scores
+  // the lane receives per head block: 32*mb + 8*(i/4) + 4*half + i%4. The
+  // loads are unconditional (clamped head, then zeroed), so that waiting
+  // for the key tile does not wait for them.
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int head = mb * 32 + (lane & 31);
+    const int hq = head < H ? head : H - 1;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qa[mb][ks] = load16(q + ((t * H + hq) * D + ks * 16 + 8 * half));
+    if (H % 4 == 0) {  // uniform: runs of 4 heads are whole and aligned
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int oh0 = mb * 32 + 8 * j + 4 * half;
+        const f32x4 v = load_w4<WT>(w, t * H + (oh0 < H ? oh0 : 0));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) wv[mb][4 * j + c] = v[c];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int oh = mb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        wv[mb][i] = load_w<WT>(w, t * H + (oh < H ? oh : 0));
+      }
+    }
+  }
+  if (!live || 32 * MB > H) {  // uniform per wave: zero what is past the row or the heads
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int head = mb * 32 + (lane & 31);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        if (!live || head >= H) qa[mb][ks] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int oh = mb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (!live || oh >= H) wv[mb][i] = 0.0f;
+      }
+    }
+  }
+
   store_tile(0);
   __syncthreads();
   int buf = 0;

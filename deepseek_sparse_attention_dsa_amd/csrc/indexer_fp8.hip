@@ -77,24 +77,6 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   const int64_t r0 = qblk * kF8Waves;
   const int64_t cap = T_kv > 0 ? ld : 0;  // longest row length taken (no keys: none)
 
-  if (threadIdx.x == 0) {
-    int32_t kb = INT32_MAX, ke = 0;
-    for (int i = 0; i < kF8Waves; ++i) {
-      const int64_t r = r0 + i;
-      if (r < n_rows) {
-        const int64_t t = row_begin + r;
-        const int32_t s0 = row_starts[t];
-        const int32_t n = (int32_t)min((int64_t)seq_lens[t], cap);
-        if (n > 0) {
-          kb = min(kb, s0);
-          ke = max(ke, s0 + n);
-        }
-      }
-    }
-    s_range[0] = kb;
-    s_range[1] = ke;
-  }
-
   // This wave's query. A operand of k-step s for head 32*mb + l%32: bytes
   // 64s + 16*half .. +15 and 64s + 32 + 16*half .. +15 of the head's row.
   const int64_t r = r0 + wave;
@@ -130,6 +112,10 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
       wv[mb][i] = wf;
     }
   }
+  // Key range of the workgroup (after the Q loads, so that wave 0's loads of
+  // both are in flight together).
+  if (threadIdx.x < 64)
+    wave_key_range(row_starts, seq_lens, row_begin, r0, n_rows, kF8Waves, cap, s_range);
   __syncthreads();
   const int32_t kb = s_range[0];
   const int32_t ke = s_range[1];
