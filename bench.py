@@ -14,6 +14,9 @@ attention kernel's time measured with HIP events inside the timed steps);
 `indexer_topk_rows_per_s` is the second half of the metric; `ms_per_step` is
 the whole path. `roofline` describes the dominant kernel; `cpu_baseline` is
 the fp64 CPU oracle timed on a bounded sample of the same workload.
+`stages_flushed` repeats the stage timings over a few extra steps that each
+start after 512 MiB were written, so that the 256 MB MALL holds none of the
+step's inputs (the main figures are warm: back-to-back steps).
 """
 
 from __future__ import annotations
@@ -52,6 +55,9 @@ def parse():
     p.add_argument("--fused", action="store_true",
                    help="one combined indexer + top-K launch instead of score chunks + dsa_topk "
                         "(rows of <= 4096 columns)")
+    p.add_argument("--flush-steps", type=int, default=5,
+                   help="extra steps, each after writing 512 MiB so that the 256 MB MALL holds "
+                        "none of the step's inputs, reported as stages_flushed (0: none)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -286,7 +292,7 @@ def main():
 
     ev = {}
 
-    def step(timed: bool):
+    def step(timed: bool, key: str = "steps"):
         e0 = torch.cuda.Event(enable_timing=True) if timed else None
         e1 = torch.cuda.Event(enable_timing=True) if timed else None
         e2 = torch.cuda.Event(enable_timing=True) if timed else None
@@ -324,7 +330,7 @@ def main():
                                 lse=lse, max_logits=max_logits)
         if timed:
             e2.record(stream)
-            ev.setdefault("steps", []).append((e0, e1, e2))
+            ev.setdefault(key, []).append((e0, e1, e2))
 
     for _ in range(args.warmup):
         step(False)
@@ -334,6 +340,13 @@ def main():
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if args.flush_steps > 0:
+        flush = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+        for i in range(args.flush_steps):
+            flush.fill_(float(i))  # evicts the step's inputs from the MALL (outside the events)
+            step(True, "flushed")
+        torch.cuda.synchronize()
+        del flush
 
     idx_ms = [a.elapsed_time(b) for a, b, _ in ev["steps"]]
     att_ms = [b.elapsed_time(c) for _, b, c in ev["steps"]]
@@ -355,6 +368,15 @@ def main():
                                            "topk_algorithmic_bytes": cnt["topk_bytes"],
                                            "chunks": 0 if fused else math.ceil(T / rows_per_chunk),
                                            "combined_launch": fused}
+
+    stages_flushed = None
+    if "flushed" in ev:
+        f_att = float(np.mean([b.elapsed_time(c) for _, b, c in ev["flushed"]]))
+        stages_flushed = {"steps": len(ev["flushed"]), "attention": {
+            "ms": f_att, "tflops": cnt["attn_flop"] / f_att / 1e9}}
+        if has_indexer:
+            f_idx = float(np.mean([a.elapsed_time(b) for a, b, _ in ev["flushed"]]))
+            stages_flushed["metadata+indexer+topk"] = {"ms": f_idx, "rows_per_s": T / f_idx * 1e3}
 
     roofline = {"kernel": "sparse_attn_kernel", "bound": "mfma", "achieved": attn_tflops,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -410,6 +432,7 @@ def main():
                    "indexer_dim": wl.D_idx, "parallelism": "none"},
         "indexer_topk_rows_per_s": rows_per_s,
         "stages": stages,
+        "stages_flushed": stages_flushed,
         "roofline": roofline,
         "cpu_baseline": None,
     }
