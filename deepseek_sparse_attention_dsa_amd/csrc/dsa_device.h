@@ -1,6 +1,8 @@
 // Device-side helpers shared by the gfx950 DSA kernels (internal header).
 #pragma once
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -109,6 +111,19 @@ __device__ __forceinline__ void dma16_imm(const void* gptr, uint32_t lds_base) {
 }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Calls f(std::integral_constant<int, i>{}) for i = 0 .. N-1 (compile-time i).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<0, N>(f);
+}
 
 // Raw buffer descriptor words (gfx9: 32-bit data, stride 0, range checked)
 // over `bytes` bytes at `base`; base and bytes must be wave-uniform.

@@ -101,6 +101,8 @@ struct BwdArgs {
   uint16_t* dkv;            // [T_kv, D_qk] bf16
   float* d_sink;            // [H] or null
   int64_t row0;             // first row of the current chunk
+  uint32_t span_kv;         // launcher: bytes of kv read through a buffer descriptor
+  uint32_t row_bytes;       // launcher: ld_kv * 2
 };
 
 hipError_t launch_sparse_attn_bwd(BwdArgs a, int64_t chunk, hipStream_t st);

@@ -90,18 +90,6 @@ struct Cfg {
   static_assert(DQK <= 1024 && DV <= 1024, "zero row covers 1024 dims");
 };
 
-// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1 (compile-time i).
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for_impl(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for_impl<I + 1, N>(f);
-  }
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl<0, N>(f);
-}
 
 template <int DQK, int DV, bool SHARED, int NW, bool BUF>
 __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {

@@ -16,11 +16,10 @@
 // v_mfma_f32_32x32x16_bf16, fp32 accumulation):
 //  * bwd_prep_kernel: D and log Z per (t, h), one wave per pair.
 //  * bwd_sink_kernel: d_sink by a fixed-order reduction over t (deterministic).
-//  * bwd_scores_kernel<P>: gathers 32 selected KV rows per tile into LDS and
-//    computes S = q . K^T (q held in registers as the A operand); stores P as
-//    bf16, slot-major ([row][slot][head]).
-//  * bwd_scores_kernel<DS>: the same with dout as A and the value dims:
-//    dP = dout . V^T; stores scale * P * (dP - D) (dS, scale folded in).
+//  * bwd_pds_kernel: gathers 32 selected KV rows per tile into an LDS ring
+//    with asynchronous copies and computes S = q . K^T and dP = dout . V^T
+//    from the same fragment reads; stores P and dS = scale * P * (dP - D)
+//    (scale folded in) as bf16, slot-major ([row][slot][head]).
 //  * bwd_dq_kernel: dq = dS . K with both operands read transposed from LDS
 //    (ds_read_b64_tr_b16), two waves per 32-head block splitting the dims.
 //  * bwd_dkv_kernel: per tile, dS^T . q + P^T . dout (the query's q and dout
@@ -133,77 +132,218 @@ __device__ __forceinline__ int row_len(const BwdArgs& a, int64_t t) {
   return L < 0 ? 0 : (L > a.k_width ? a.k_width : L);
 }
 
-// ------------------------------------------------------------ P and dS --
-// One workgroup per query row of the chunk, one wave per 32 heads.
-// S[h][s] on 32x32x16: A = q (or dout) rows of the wave's heads from
-// registers, B = the gathered rows (k = dims) from LDS; C lane -> slot
-// column l%32, head rows crow(i).
-template <int DQK, int NW, bool DS>
-__global__ __launch_bounds__(NW * 64) void bwd_scores_kernel(BwdArgs a) {
-  constexpr int DG = DS ? 512 : DQK;   // dims of the product
-  constexpr int RS = DG + 8;           // LDS row stride (bf16): conflict-free b128 reads
-  constexpr int KS = DG / 16;
+// ---------------------------------------------------------- P and dS, fused --
+// One workgroup per query row of the chunk; wave w < NW owns heads
+// 32w .. 32w+31 (NWC waves are launched: NW, or 4 when NW = 3, the extra wave
+// only copying). Per tile of 32 slots, with the gathered rows as the B operand
+// (lane -> slot l%32, k = dims) of v_mfma_f32_32x32x16_bf16:
+//   S  = q . K^T     A = q of the wave's heads, held in AGPRs   (DQK/16 k-steps)
+//   dP = dout . V^T  A = dout of the wave's heads, in VGPRs     (32 k-steps)
+// Each fragment read from LDS feeds both products (V is the first 512 dims
+// of K). C lane -> slot column l%32, head rows crow(i). Then
+//   P = exp2(S scale log2e - log Z log2e),  dS = scale P (dP - D)
+// both written as bf16 to the slot-major workspaces ([row][slot][head]);
+// invalid slots and heads past H write zeros. The S chain uses the compiler's
+// MFMA (its accumulator in AGPRs, q where the allocator puts it); the dP chain
+// is written inline with its accumulator in VGPRs, so that the two
+// accumulators and both operand sets fit the register files together, and
+// the wait states the compiler would insert before VALU reads of dP are
+// given after the chain.
+//
+// The tiles are gathered as in the forward kernel: asynchronous LDS copies
+// into a 2-stage ring, the copies of tile i+1 interleaved with the MFMAs of
+// tile i. Rows 8g .. 8g+7 and dims 64s .. 64s+63 of a tile form the 1 KiB
+// block 4s + g, copied as eight 128-byte row segments; chunk c of row 8g + r
+// sits in slot 8r + (c ^ f(r, g)), f = 4*((r>>1)&1) + (r>>2) + 2*(g&1), which
+// keeps the fragment reads (16 lanes: 16 rows, one chunk) conflict-free. With
+// BUF the copies go through a buffer descriptor over kv with 32-bit row
+// offsets and masked rows read as zeros past its range; else through 64-bit
+// addresses with masked rows read from a zero constant.
+__device__ const u32x4 g_bwd_zero_row[128] = {};
+
+template <int DQK, int NW, int NWC, bool BUF>
+__global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
+  constexpr int KS = DQK / 16;            // S k-steps
+  constexpr int KV = 512 / 16;            // dP k-steps (the value dims)
+  constexpr int K_SEG = DQK / 64;         // 64-dim segments of a row
+  constexpr int GPW = 4 / NWC;            // row groups copied per wave
+  constexpr int NCOPY = GPW * K_SEG;      // copies per wave and tile
+  constexpr int STAGE = 4 * K_SEG * 1024;
   constexpr int HP = NW * 32;
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kBT * RS];
-  __shared__ int32_t s_ids[kBT];
+  static_assert(NWC == 1 || NWC == 2 || NWC == 4, "row groups split evenly over waves");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, r32 = lane & 31;
-  const int64_t rc = blockIdx.x;            // row within the chunk
+  const int64_t rc = blockIdx.x;
   const int64_t t = a.row0 + rc;
   const int L = row_len(a, t);
+  const int n_tiles = (L + kBT - 1) / kBT;
+  const bool comp = wave < NW;  // uniform
   const int h0 = 32 * wave;
-  const int hA = h0 + r32;                  // A-operand head of this lane
+  const int hA = h0 + r32;
 
-  u32x4 qa[KS];
-  {
-    const uint16_t* src = DS ? a.dout + (t * a.H + hA) * 512 : a.q + (t * a.H + hA) * DQK;
+  const int key_row = lane & 31;
+  const int crw = lane >> 3;
+  auto swz = [](int r, int g) -> int { return 4 * ((r >> 1) & 1) + (r >> 2) + 2 * (g & 1); };
+  auto load_id = [&](int j0, int row) -> int32_t {
+    const int j = j0 + row;
+    int32_t raw = -1;
+    if (j < L) raw = a.indices[t * a.ld_idx + j];
+    return raw;
+  };
+  auto valid_id = [&](int32_t raw) -> int32_t {
+    return (raw >= 0 && (int64_t)raw < a.T_kv) ? raw : -1;
+  };
+  // ids of the first two tiles before anything else
+  const int32_t id_first = n_tiles > 0 ? load_id(0, key_row) : -1;
+  const int32_t id_second = n_tiles > 1 ? load_id(kBT, key_row) : -1;
+
+  const uint32_t smem_base = lds_addr(smem);
+  struct CopySrc {
+    const uint16_t* k[BUF ? 1 : GPW];
+    uint32_t ko[BUF ? GPW : 1];
+    uint32_t m0;
+  };
+  i32x4 rsrc{};
+  if constexpr (BUF) rsrc = buffer_rsrc_words(a.kv, a.span_kv);
+  constexpr uint32_t kPastRange = 0x80000000u;
+  auto prep_copy = [&](uint32_t stage, int32_t idv) -> CopySrc {
+    CopySrc cs;
+    int32_t idg[GPW];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qa[ks] = hA < a.H ? load16(src + 16 * ks + 8 * half) : u32x4{0u, 0u, 0u, 0u};
+    for (int gi = 0; gi < GPW; ++gi) idg[gi] = __shfl(idv, 8 * (GPW * wave + gi) + crw, kWave);
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      const int g = GPW * wave + gi;
+      const int chunk = (lane & 7) ^ swz(crw, g);
+      const bool ok = idg[gi] >= 0;
+      if constexpr (BUF) {
+        cs.ko[gi] = ok ? __umul24((uint32_t)idg[gi], a.row_bytes) + 16u * chunk : kPastRange;
+      } else {
+        const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_bwd_zero_row);
+        const uint64_t row = ok ? (uint64_t)(uint32_t)idg[gi] : 0ull;
+        cs.k[gi] = (ok ? a.kv : zero) + row * (uint64_t)a.ld_kv + 8 * chunk;
+      }
+    }
+    cs.m0 = __builtin_amdgcn_readfirstlane(stage + 1024u * (uint32_t)(GPW * wave));
+    return cs;
+  };
+  auto copy_one = [&](const CopySrc& cs, auto jc) {
+    constexpr int J = decltype(jc)::value;
+    constexpr int GI = J % GPW, S = J / GPW;
+    const uint32_t m0 = cs.m0 + (uint32_t)(1024 * (4 * S + GI) - 128 * S);
+    if constexpr (BUF) dma16_buf_imm<128 * S>(cs.ko[GI], rsrc, m0);
+    else dma16_imm<128 * S>(cs.k[GI], m0);
+  };
+
+  // A operands: lane -> head hA, dims 16*ks + 8*half .. +7 (clamped head,
+  // zeroed past H).
+  u32x4 qa[KS], ga[KV];
+  {
+    const int hq = hA < a.H ? hA : a.H - 1;
+    const uint16_t* qs = a.q + (t * a.H + hq) * (int64_t)DQK + 8 * half;
+    const uint16_t* gs = a.dout + (t * a.H + hq) * (int64_t)512 + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qa[ks] = load16(qs + 16 * ks);
+#pragma unroll
+    for (int ks = 0; ks < KV; ++ks) ga[ks] = load16(gs + 16 * ks);
+    if (hA >= a.H) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qa[ks] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int ks = 0; ks < KV; ++ks) ga[ks] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
-  float lz[16], dd[16];
+  float lz2[16], dd[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int h = h0 + crow(i, half);
-    lz[i] = h < a.H ? a.logZ[t * a.H + h] : __builtin_inff();
-    dd[i] = (DS && h < a.H) ? a.Dsum[t * a.H + h] : 0.0f;
+    lz2[i] = h < a.H ? a.logZ[t * a.H + h] * kLog2eB : __builtin_inff();
+    dd[i] = h < a.H ? a.Dsum[t * a.H + h] : 0.0f;
   }
   const float c2 = a.scale * kLog2eB;
   uint16_t* wsP = a.wsP + rc * (int64_t)a.Kw * HP;
   uint16_t* wsD = a.wsD + rc * (int64_t)a.Kw * HP;
 
-  const int ntiles = (L + kBT - 1) / kBT;
-  for (int tl = 0; tl < ntiles; ++tl) {
-    load_tile_ids(a, t, L, tl, s_ids);
-    __syncthreads();
-    gather_rows<DG, RS>(a, s_ids, tile);
-    __syncthreads();
-    f32x16 acc{};
-    const uint16_t* brow = tile + r32 * RS + 8 * half;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      acc = mfma32x32x16(qa[ks], *reinterpret_cast<const u32x4*>(brow + 16 * ks), acc);
-    const int slot = tl * kBT + r32;
-    const bool valid = s_ids[r32] >= 0;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int64_t off = (int64_t)slot * HP + h0 + 8 * g + 4 * half;  // 4 consecutive heads
-      float v[4];
-      if constexpr (!DS) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          v[e] = valid ? fast_exp2(acc[4 * g + e] * c2 - lz[4 * g + e] * kLog2eB) : 0.0f;
-      } else {
-        const u32x2 pp = *reinterpret_cast<const u32x2*>(wsP + off);
-        const float p[4] = {bf16_bits_to_f32(pp.x & 0xffffu), bf16_bits_to_f32(pp.x >> 16),
-                            bf16_bits_to_f32(pp.y & 0xffffu), bf16_bits_to_f32(pp.y >> 16)};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = a.scale * p[e] * (acc[4 * g + e] - dd[4 * g + e]);
-      }
-      *reinterpret_cast<u32x2*>((DS ? wsD : wsP) + off) =
-          u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  int32_t id_next = id_second;
+  uint32_t mask_cur = 0;
+  if (n_tiles > 0) {
+    const int32_t id0 = valid_id(id_first);
+    mask_cur = (uint32_t)ballot(id0 >= 0);
+    const CopySrc cs0 = prep_copy(smem_base, id0);
+    static_for<NCOPY>([&](auto jc) { copy_one(cs0, jc); });
+  }
+  for (int it = 0; it < n_tiles; ++it) {
+    wait_vmcnt0();
+    __syncthreads();  // tile it has landed in every wave's share; tile it-1 is consumed
+    uint32_t mask_next = 0;
+    const bool copy_next = it + 1 < n_tiles;  // uniform
+    CopySrc cs{};
+    if (copy_next) {
+      const int32_t idv = valid_id(id_next);
+      mask_next = (uint32_t)ballot(idv >= 0);
+      cs = prep_copy(smem_base + ((it + 1) & 1) * STAGE, idv);
     }
-    __syncthreads();  // tile and ids are reused
+    auto copies_at = [&](auto kc) {  // copies spread over the S k-steps
+      constexpr int ks = decltype(kc)::value;
+      constexpr int j0 = (ks * NCOPY + KS - 1) / KS, j1 = ((ks + 1) * NCOPY + KS - 1) / KS;
+      if (copy_next)
+        static_for<j1 - j0>([&](auto dj) {
+          copy_one(cs, std::integral_constant<int, j0 + decltype(dj)::value>{});
+        });
+    };
+    const unsigned char* tile = smem + (it & 1) * STAGE;
+    f32x16 sacc, dacc;
+    if (comp) {
+      // fragment of k-step ks: row r32 (group kg, row kr), chunk 2*(ks%4) + half of
+      // segment ks/4 at slot 8*kr + (chunk ^ f)
+      const int kg = r32 >> 3, kr = r32 & 7, kf = swz(kr, kg);
+      const unsigned char* kbase = tile + kg * 1024 + kr * 128 + 16 * (half ^ (kf & 1));
+      const unsigned char* kq[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) kq[q] = kbase + 32 * (q ^ (kf >> 1));
+      auto kread = [&](int ks) -> u32x4 {
+        return *reinterpret_cast<const u32x4*>(kq[ks & 3] + (ks >> 2) * 4096);
+      };
+      constexpr int PF = 4;
+      u32x4 bf[PF];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) bf[i] = kread(i);
+      static_for<KS>([&](auto kc) {
+        constexpr int ks = decltype(kc)::value;
+        const u32x4 cur = bf[ks % PF];
+        if constexpr (ks + PF < KS) bf[ks % PF] = kread(ks + PF);
+        sacc = mfma32x32x16(qa[ks], cur, ks == 0 ? f32x16{} : sacc);
+        if constexpr (ks == 0)
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(dacc) : "v"(ga[0]), "v"(cur));
+        else if constexpr (ks < KV)
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(dacc) : "v"(ga[ks]), "v"(cur));
+        copies_at(kc);
+      });
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(dacc));
+    } else {
+      static_for<KS>([&](auto kc) { copies_at(kc); });
+    }
+    if (copy_next) id_next = (it + 2 < n_tiles) ? load_id((it + 2) * kBT, key_row) : -1;
+    if (comp) {
+      const int slot = it * kBT + r32;
+      const bool valid = (mask_cur >> r32) & 1u;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float pv[4], dv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * g + e;
+          const float p = valid ? fast_exp2(fmaf(sacc[i], c2, -lz2[i])) : 0.0f;
+          pv[e] = p;
+          dv[e] = a.scale * p * (dacc[i] - dd[i]);
+        }
+        const int64_t off = (int64_t)slot * HP + h0 + 8 * g + 4 * half;  // 4 consecutive heads
+        *reinterpret_cast<u32x2*>(wsP + off) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
+        *reinterpret_cast<u32x2*>(wsD + off) = u32x2{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3])};
+      }
+    }
+    mask_cur = mask_next;
   }
 }
 
@@ -466,13 +606,22 @@ hipError_t launch_bwd_nw(BwdArgs a, int64_t chunk, hipStream_t st) {
   constexpr int HC = HP % 64 == 0 ? 64 : 32;
   a.nparts = HP / HC;
   a.chunk_rows = chunk;
+  // Buffer-descriptor gathers take 32-bit offsets below 2^31: used whenever
+  // every kv byte read lies below that.
+  const int64_t span = a.T_kv > 0 ? ((a.T_kv - 1) * a.ld_kv + DQK) * 2 : 0;
+  const bool buf = span < ((int64_t)1 << 31) && a.ld_kv * 2 < (1 << 24);
+  a.span_kv = buf ? (uint32_t)span : 0u;
+  a.row_bytes = buf ? (uint32_t)(a.ld_kv * 2) : 0u;
   for (int64_t r0 = 0; r0 < a.T_q; r0 += chunk) {
     a.row0 = r0;
     const int64_t n = a.T_q - r0 < chunk ? a.T_q - r0 : chunk;
-    hipLaunchKernelGGL((bwd_scores_kernel<DQK, NW, false>), dim3((unsigned)n), dim3(NW * 64), 0,
-                       st, a);
-    hipLaunchKernelGGL((bwd_scores_kernel<DQK, NW, true>), dim3((unsigned)n), dim3(NW * 64), 0,
-                       st, a);
+    constexpr int NWC = NW == 3 ? 4 : NW;
+    if (buf)
+      hipLaunchKernelGGL((bwd_pds_kernel<DQK, NW, NWC, true>), dim3((unsigned)n), dim3(NWC * 64), 0,
+                         st, a);
+    else
+      hipLaunchKernelGGL((bwd_pds_kernel<DQK, NW, NWC, false>), dim3((unsigned)n),
+                         dim3(NWC * 64), 0, st, a);
     hipLaunchKernelGGL((bwd_dq_kernel<DQK, NW>), dim3((unsigned)n), dim3(NW * 128), 0, st, a);
     hipLaunchKernelGGL((bwd_dkv_kernel<DQK, NW, NWD>), dim3((unsigned)(n * (HP / HC))),
                        dim3(NWD * 64), 0, st, a);
