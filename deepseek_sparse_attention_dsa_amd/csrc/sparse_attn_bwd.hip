@@ -20,8 +20,9 @@
 //    with asynchronous copies and computes S = q . K^T and dP = dout . V^T
 //    from the same fragment reads; stores P and dS = scale * P * (dP - D)
 //    (scale folded in) as bf16, slot-major ([row][slot][head]).
-//  * bwd_dq_kernel: dq = dS . K with both operands read transposed from LDS
-//    (ds_read_b64_tr_b16), two waves per 32-head block splitting the dims.
+//  * bwd_dq_ring_kernel: dq = dS . K with both operands read transposed from
+//    LDS (ds_read_b64_tr_b16), two waves per 32-head block splitting the
+//    dims; K gathered into the same copy ring as bwd_pds_kernel.
 //  * bwd_dkv_kernel: per tile, dS^T . q + P^T . dout (the query's q and dout
 //    staged in LDS), each slot's row written once as bf16 (per 64-head part).
 //  * bwd_count / bwd_scan / bwd_place: a counting sort of the chunk's valid
@@ -109,20 +110,6 @@ __device__ __forceinline__ void load_tile_ids(const BwdArgs& a, int64_t t, int L
       id = (v >= 0 && v < a.T_kv) ? v : -1;
     }
     s_ids[threadIdx.x] = id;
-  }
-}
-
-// Gathers dims [0, DG) of the tile's 32 KV rows into a row-major LDS tile
-// (row stride RS bf16); invalid rows become zeros.
-template <int DG, int RS>
-__device__ __forceinline__ void gather_rows(const BwdArgs& a, const int32_t* s_ids,
-                                            uint16_t* tile) {
-  constexpr int CPR = DG / 8;  // 16-byte chunks per row
-  for (int c = threadIdx.x; c < kBT * CPR; c += blockDim.x) {
-    const int row = c / CPR, ch = c - row * CPR;
-    const int32_t id = s_ids[row];
-    const u32x4 v = id >= 0 ? load16(a.kv + (int64_t)id * a.ld_kv + 8 * ch) : u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(tile + row * RS + 8 * ch) = v;
   }
 }
 
@@ -347,61 +334,161 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
   }
 }
 
-// ------------------------------------------------------------------- dq --
-// One workgroup per query row, waves (head block hb, dim half dh). dq[h][d]
-// on 32x32x16 with k = slots: A = dS (heads x slots) and B = K (slots x dims),
-// both read transposed from row-major LDS tiles ([slot][head], [slot][dim]).
-template <int DQK, int NW>
-__global__ __launch_bounds__(NW * 128) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int RS = DQK + 8;     // K tile row stride (bf16)
+// ---------------------------------------------------------- dq, ring --
+// One workgroup per query row, waves (head block hb = w/2, dim half dh = w%2).
+// dq[h][d] on 32x32x16 with k = slots: A = dS (heads x slots) and B = K
+// (slots x dims), both read transposed (ds_read_b64_tr_b16). The K tiles are
+// gathered into the same swizzled 2-stage ring as bwd_pds_kernel (copies of
+// tile i+1 issued by the first min(2*NW, 4) waves between the MFMAs of tile
+// i); each tile's dS rows ([slot][head], contiguous in the workspace) are
+// loaded one tile ahead into registers and stored to a padded LDS tile.
+// Lane half h of an MFMA operand covers slots 16*st + 4h + 0..3 and
+// 16*st + 8 + 4h + 0..3 of k-step st, in both operands.
+template <int DQK, int NW, bool BUF>
+__global__ __launch_bounds__(NW * 128, NW <= 2 ? 2 : 1) void bwd_dq_ring_kernel(BwdArgs a) {
+  constexpr int NWQ = 2 * NW;             // waves
+  constexpr int NCW = NWQ < 4 ? NWQ : 4;  // copying waves
+  constexpr int GPW = 4 / NCW;            // row groups copied per copying wave
+  constexpr int K_SEG = DQK / 64;
+  constexpr int NCOPY = GPW * K_SEG;
+  constexpr int STAGE = 4 * K_SEG * 1024;
   constexpr int HP = NW * 32;
-  constexpr int RSD = HP + 8;     // dS tile row stride (bf16)
-  constexpr int NBW = DQK / 64;   // 32-dim blocks per wave (half of the dims)
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kBT * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t dst[kBT * RSD];
-  __shared__ int32_t s_ids[kBT];
+  constexpr int RSD = HP + 8;             // dS tile row stride (bf16): conflict-free reads
+  constexpr int NBW = DQK / 64;           // 32-dim blocks per wave (half the dims)
+  static_assert(NWQ * 64 == kBT * HP / 8, "one 16-byte dS chunk per thread and tile");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t sds[kBT * RSD];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, r32 = lane & 31;
+  const int lane = threadIdx.x & 63, half = lane >> 5, r32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // scalar
   const int hb = wave >> 1, dh = wave & 1;
+  const bool copier = wave < NCW;  // uniform
   const int64_t rc = blockIdx.x;
   const int64_t t = a.row0 + rc;
   const int L = row_len(a, t);
+  const int n_tiles = (L + kBT - 1) / kBT;
   const uint16_t* wsD = a.wsD + rc * (int64_t)a.Kw * HP;
-  // transposed-read addressing: 16-lane group G reads rows r0 + li/4 (+4),
-  // columns c0 + 4*(li%4); lane li receives column c0 + li, 4 rows.
+
+  const int key_row = lane & 31;
+  const int crw = lane >> 3;
+  auto swz = [](int r, int g) -> int { return 4 * ((r >> 1) & 1) + (r >> 2) + 2 * (g & 1); };
+  auto load_id = [&](int j0, int row) -> int32_t {
+    const int j = j0 + row;
+    int32_t raw = -1;
+    if (j < L) raw = a.indices[t * a.ld_idx + j];
+    return raw;
+  };
+  auto valid_id = [&](int32_t raw) -> int32_t {
+    return (raw >= 0 && (int64_t)raw < a.T_kv) ? raw : -1;
+  };
+  const int32_t id_first = n_tiles > 0 ? load_id(0, key_row) : -1;
+  const int32_t id_second = n_tiles > 1 ? load_id(kBT, key_row) : -1;
+  // this thread's 16-byte chunk of a tile's dS rows
+  const int dslot = threadIdx.x / (HP / 8), dch = threadIdx.x % (HP / 8);
+  auto load_ds = [&](int tl) -> u32x4 { return load16(wsD + (int64_t)(tl * kBT + dslot) * HP + 8 * dch); };
+  u32x4 ds_next = n_tiles > 0 ? load_ds(0) : u32x4{0u, 0u, 0u, 0u};
+
+  const uint32_t smem_base = lds_addr(smem);
+  struct CopySrc {
+    const uint16_t* k[BUF ? 1 : GPW];
+    uint32_t ko[BUF ? GPW : 1];
+    uint32_t m0;
+  };
+  i32x4 rsrc{};
+  if constexpr (BUF) rsrc = buffer_rsrc_words(a.kv, a.span_kv);
+  constexpr uint32_t kPastRange = 0x80000000u;
+  auto prep_copy = [&](uint32_t stage, int32_t idv) -> CopySrc {
+    CopySrc cs;
+    int32_t idg[GPW];
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) idg[gi] = __shfl(idv, 8 * (GPW * wave + gi) + crw, kWave);
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      const int g = GPW * wave + gi;
+      const int chunk = (lane & 7) ^ swz(crw, g);
+      const bool ok = idg[gi] >= 0;
+      if constexpr (BUF) {
+        cs.ko[gi] = ok ? __umul24((uint32_t)idg[gi], a.row_bytes) + 16u * chunk : kPastRange;
+      } else {
+        const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_bwd_zero_row);
+        const uint64_t row = ok ? (uint64_t)(uint32_t)idg[gi] : 0ull;
+        cs.k[gi] = (ok ? a.kv : zero) + row * (uint64_t)a.ld_kv + 8 * chunk;
+      }
+    }
+    cs.m0 = __builtin_amdgcn_readfirstlane(stage + 1024u * (uint32_t)(GPW * wave));
+    return cs;
+  };
+  auto copy_one = [&](const CopySrc& cs, auto jc) {
+    constexpr int J = decltype(jc)::value;
+    constexpr int GI = J % GPW, S = J / GPW;
+    const uint32_t m0 = cs.m0 + (uint32_t)(1024 * (4 * S + GI) - 128 * S);
+    if constexpr (BUF) dma16_buf_imm<128 * S>(cs.ko[GI], rsrc, m0);
+    else dma16_imm<128 * S>(cs.k[GI], m0);
+  };
+
+  // Transposed-read addressing (16-lane group G = lane/16, lane li = lane%16):
+  // dS: rows (slots) 16*st + 4*(G/2) + li/4 (+8), columns 32*hb + 16*(G%2) +
+  // 4*(li%4); K: the forward kernel's V reads on the swizzled tile (column
+  // block nb = 32 dims, key half st).
   const int G = lane >> 4, li = lane & 15;
-  const int rsel = 8 * (G >> 1) + (li >> 2);        // slot within a 16-slot step
-  const int csel = 16 * (G & 1) + 4 * (li & 3);     // column within a 32-wide block
+  const uint16_t* dsa_ptr = sds + (4 * (G >> 1) + (li >> 2)) * RSD + 32 * hb + 16 * (G & 1) + 4 * (li & 3);
+  const int vr = 4 * (G >> 1) + (li >> 2);
+  const int vb0 = vr * 128 + 16 * (((li >> 1) & 1) ^ (G >> 1)) + 8 * (li & 1);
+  int voff[2][2];  // [nb % 2][b]
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) voff[pp][b] = vb0 + 1024 * b + 16 * (4 * (pp ^ (li >> 3)) + 2 * ((G & 1) ^ b));
 
   f32x16 acc[NBW];
 #pragma unroll
   for (int b = 0; b < NBW; ++b) acc[b] = f32x16{};
-  const int ntiles = (L + kBT - 1) / kBT;
-  for (int tl = 0; tl < ntiles; ++tl) {
-    load_tile_ids(a, t, L, tl, s_ids);
-    __syncthreads();
-    gather_rows<DQK, RS>(a, s_ids, tile);
-    for (int c = threadIdx.x; c < kBT * HP / 8; c += blockDim.x) {
-      const int s = c / (HP / 8), ch = c - s * (HP / 8);
-      *reinterpret_cast<u32x4*>(dst + s * RSD + 8 * ch) =
-          load16(wsD + (int64_t)(tl * kBT + s) * HP + 8 * ch);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {  // 16-slot k-steps
-      const uint16_t* da = dst + (16 * st + rsel) * RSD + 32 * hb + csel;
-      const u32x2 a0 = lds_read_tr16(da);
-      const u32x2 a1 = lds_read_tr16(da + 4 * RSD);
+
+  int32_t id_next = id_second;
+  if (n_tiles > 0 && copier) {
+    const CopySrc cs0 = prep_copy(smem_base, valid_id(id_first));
+    static_for<NCOPY>([&](auto jc) { copy_one(cs0, jc); });
+  }
+  for (int it = 0; it < n_tiles; ++it) {
+    wait_vmcnt0();
+    __syncthreads();  // K tile it landed; every wave is done with tile it-1 and the dS tile
+    *reinterpret_cast<u32x4*>(sds + dslot * RSD + 8 * dch) = ds_next;
+    if (it + 1 < n_tiles) ds_next = load_ds(it + 1);
+    __syncthreads();  // dS of tile it visible
+    const bool copy_next = it + 1 < n_tiles;  // uniform
+    CopySrc cs{};
+    if (copy_next && copier) cs = prep_copy(smem_base + ((it + 1) & 1) * STAGE, valid_id(id_next));
+    auto copies_at = [&](auto fc) {  // copies spread over the wave's 2*NBW MFMAs
+      constexpr int f = decltype(fc)::value;
+      constexpr int NS = 2 * NBW;
+      constexpr int j0 = (f * NCOPY + NS - 1) / NS, j1 = ((f + 1) * NCOPY + NS - 1) / NS;
+      if (copy_next && copier)
+        static_for<j1 - j0>([&](auto dj) {
+          copy_one(cs, std::integral_constant<int, j0 + decltype(dj)::value>{});
+        });
+    };
+    const unsigned char* tile = smem + (it & 1) * STAGE;
+    auto kfrag = [&](int nb, int st) -> u32x4 {
+      const int so = (nb >> 1) * 4096 + st * 2048;
+      const u32x2 x0 = lds_read_tr16(tile + voff[nb & 1][0] + so);
+      const u32x2 x1 = lds_read_tr16(tile + voff[nb & 1][1] + so);
+      return u32x4{x0.x, x0.y, x1.x, x1.y};
+    };
+    static_for<2>([&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      const u32x2 a0 = lds_read_tr16(dsa_ptr + 16 * st * RSD);
+      const u32x2 a1 = lds_read_tr16(dsa_ptr + (16 * st + 8) * RSD);
       const u32x4 av = u32x4{a0.x, a0.y, a1.x, a1.y};
-#pragma unroll
-      for (int b = 0; b < NBW; ++b) {
-        const uint16_t* kb = tile + (16 * st + rsel) * RS + (dh * NBW + b) * 32 + csel;
-        const u32x2 b0 = lds_read_tr16(kb);
-        const u32x2 b1 = lds_read_tr16(kb + 4 * RS);
-        acc[b] = mfma32x32x16(av, u32x4{b0.x, b0.y, b1.x, b1.y}, acc[b]);
-      }
-    }
-    __syncthreads();
+      u32x4 kb = kfrag(dh * NBW, st);
+      static_for<NBW>([&](auto bc) {
+        constexpr int b = decltype(bc)::value;
+        const u32x4 cur = kb;
+        if constexpr (b + 1 < NBW) kb = kfrag(dh * NBW + b + 1, st);
+        acc[b] = mfma32x32x16(av, cur, acc[b]);
+        copies_at(std::integral_constant<int, st * NBW + b>{});
+      });
+    });
+    if (copy_next) id_next = (it + 2 < n_tiles) ? load_id((it + 2) * kBT, key_row) : -1;
   }
   // C: lane -> dim column, head rows crow(i); dS already carries the scale
 #pragma unroll
@@ -622,7 +709,12 @@ hipError_t launch_bwd_nw(BwdArgs a, int64_t chunk, hipStream_t st) {
     else
       hipLaunchKernelGGL((bwd_pds_kernel<DQK, NW, NWC, false>), dim3((unsigned)n),
                          dim3(NWC * 64), 0, st, a);
-    hipLaunchKernelGGL((bwd_dq_kernel<DQK, NW>), dim3((unsigned)n), dim3(NW * 128), 0, st, a);
+    if (buf)
+      hipLaunchKernelGGL((bwd_dq_ring_kernel<DQK, NW, true>), dim3((unsigned)n), dim3(NW * 128), 0,
+                         st, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_ring_kernel<DQK, NW, false>), dim3((unsigned)n), dim3(NW * 128),
+                         0, st, a);
     hipLaunchKernelGGL((bwd_dkv_kernel<DQK, NW, NWD>), dim3((unsigned)(n * (HP / HC))),
                        dim3(NWD * 64), 0, st, a);
     if (a.T_kv > 0) {
