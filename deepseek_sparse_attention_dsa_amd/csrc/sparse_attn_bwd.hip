@@ -99,20 +99,6 @@ __global__ __launch_bounds__(256) void bwd_sink_kernel(BwdArgs a) {
   if (threadIdx.x == 0) a.d_sink[h] = -s_part[0];
 }
 
-// Slot ids of tile `tile` of row t (-1 when invalid) into s_ids[32].
-__device__ __forceinline__ void load_tile_ids(const BwdArgs& a, int64_t t, int L, int tile,
-                                              int32_t* s_ids) {
-  if (threadIdx.x < kBT) {
-    const int s = tile * kBT + threadIdx.x;
-    int32_t id = -1;
-    if (s < L) {
-      const int32_t v = a.indices[t * a.ld_idx + s];
-      id = (v >= 0 && v < a.T_kv) ? v : -1;
-    }
-    s_ids[threadIdx.x] = id;
-  }
-}
-
 __device__ __forceinline__ int row_len(const BwdArgs& a, int64_t t) {
   if (!a.topk_length) return a.k_width;
   const int32_t L = a.topk_length[t];
@@ -506,7 +492,9 @@ __global__ __launch_bounds__(NW * 128, NW <= 2 ? 2 : 1) void bwd_dq_ring_kernel(
 // One workgroup per (query row, 64-head chunk); NWD waves each own BPW
 // 32-dim blocks. C[s][d] on 32x32x16 with k = heads: A = dS^T / P^T
 // (slot rows, heads contiguous in the workspace), B = q / dout of the chunk's
-// heads read transposed from LDS ([head][dim]).
+// heads read transposed from LDS ([head][dim]). (The transposed product, with
+// runs of 4 dims per lane stored 8 bytes at a time, measured slower: its
+// stores coalesce less than these 2-byte stores of 32 consecutive dims.)
 template <int DQK, int NW, int NWD>
 __global__ __launch_bounds__(NWD * 64) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int HP = NW * 32;
@@ -517,7 +505,6 @@ __global__ __launch_bounds__(NWD * 64) void bwd_dkv_kernel(BwdArgs a) {
   static_assert(NBLK % NWD == 0, "dim blocks split evenly over waves");
   __shared__ __attribute__((aligned(16))) uint16_t sq[HC * RQ];
   __shared__ __attribute__((aligned(16))) uint16_t sg[HC * RG];
-  __shared__ int32_t s_ids[kBT];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, r32 = lane & 31;
   const int64_t rc = blockIdx.x / (HP / HC);
@@ -544,46 +531,76 @@ __global__ __launch_bounds__(NWD * 64) void bwd_dkv_kernel(BwdArgs a) {
   const int rsel = 8 * (G >> 1) + (li >> 2);
   const int csel = 16 * (G & 1) + 4 * (li & 3);
 
+  // Per tile: wait for everything issued one tile earlier (this tile's A
+  // fragments, the stores of two tiles back), then issue the stores of the
+  // previous tile and the A loads of the next one, then this tile's MFMAs.
+  // A fragments alternate between two register sets, so no move waits on a
+  // load in flight.
+  constexpr int NK = HC / 16;
   const int ntiles = (L + kBT - 1) / kBT;
-  for (int tl = 0; tl < ntiles; ++tl) {
-    __syncthreads();  // staging done / previous tile's ids consumed
-    load_tile_ids(a, t, L, tl, s_ids);
-    __syncthreads();
+  u32x4 adA[NK], apA[NK], adB[NK], apB[NK];
+  auto load_a = [&](int tl, u32x4* ad, u32x4* ap) {
+    const int64_t srow = (int64_t)(tl * kBT + r32) * HP + hc0 + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      ad[kk] = load16(wsD + srow + 16 * kk);
+      ap[kk] = load16(wsP + srow + 16 * kk);
+    }
+  };
+  // C: lane -> dim column, slot rows crow(i); the row of slot s of this head
+  // part goes to wsC[part][rc][s] (bf16). pend holds the previous tile's.
+  uint16_t* crow_base = a.wsC + ((int64_t)(hc0 / HC) * a.chunk_rows + rc) * a.Kw * DQK;
+  uint32_t pend[BPW][16];
+  int pend_tl = -1;
+  auto store_pending = [&]() {
+    if (pend_tl < 0) return;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s = pend_tl * kBT + crow(i, half);
+#pragma unroll
+      for (int b = 0; b < BPW; ++b)
+        crow_base[(int64_t)s * DQK + (wave * BPW + b) * 32 + r32] = (uint16_t)pend[b][i];
+    }
+  };
+  auto body = [&](int tl, const u32x4* ad, const u32x4* ap, u32x4* nad, u32x4* nap) {
+    wait_vmcnt0();
+    store_pending();
+    if (tl + 1 < ntiles) load_a(tl + 1, nad, nap);
     f32x16 acc[BPW];
 #pragma unroll
     for (int b = 0; b < BPW; ++b) acc[b] = f32x16{};
-    const int64_t srow = (int64_t)(tl * kBT + r32) * HP + hc0 + 8 * half;
 #pragma unroll
-    for (int kk = 0; kk < HC / 16; ++kk) {   // 16-head k-steps
-      const u32x4 ad = load16(wsD + srow + 16 * kk);
-      const u32x4 ap = load16(wsP + srow + 16 * kk);
+    for (int kk = 0; kk < NK; ++kk) {   // 16-head k-steps
 #pragma unroll
       for (int b = 0; b < BPW; ++b) {
         const int col = (wave * BPW + b) * 32;
         const uint16_t* qb = sq + (16 * kk + rsel) * RQ + col + csel;
         const u32x2 q0 = lds_read_tr16(qb);
         const u32x2 q1 = lds_read_tr16(qb + 4 * RQ);
-        acc[b] = mfma32x32x16(ad, u32x4{q0.x, q0.y, q1.x, q1.y}, acc[b]);
+        acc[b] = mfma32x32x16(ad[kk], u32x4{q0.x, q0.y, q1.x, q1.y}, acc[b]);
         if (col < 512) {
           const uint16_t* gb = sg + (16 * kk + rsel) * RG + col + csel;
           const u32x2 g0 = lds_read_tr16(gb);
           const u32x2 g1 = lds_read_tr16(gb + 4 * RG);
-          acc[b] = mfma32x32x16(ap, u32x4{g0.x, g0.y, g1.x, g1.y}, acc[b]);
+          acc[b] = mfma32x32x16(ap[kk], u32x4{g0.x, g0.y, g1.x, g1.y}, acc[b]);
         }
       }
     }
-    // C: lane -> dim column, slot rows crow(i); the row of slot s of this
-    // head part goes to wsC[part][rc][s] (bf16)
-    uint16_t* crow_base = a.wsC + ((int64_t)(hc0 / HC) * a.chunk_rows + rc) * a.Kw * DQK;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int s = tl * kBT + crow(i, half);
+    for (int b = 0; b < BPW; ++b)
 #pragma unroll
-      for (int b = 0; b < BPW; ++b)
-        crow_base[(int64_t)s * DQK + (wave * BPW + b) * 32 + r32] =
-            (uint16_t)f32_to_bf16_bits(acc[b][i]);
-    }
+      for (int i = 0; i < 16; ++i) pend[b][i] = f32_to_bf16_bits(acc[b][i]);
+    pend_tl = tl;
+  };
+  __syncthreads();  // q and dout staged
+  if (ntiles > 0) load_a(0, adA, apA);
+  for (int tl = 0; tl < ntiles;) {
+    body(tl, adA, apA, adB, apB);
+    if (++tl >= ntiles) break;
+    body(tl, adB, apB, adA, apA);
+    ++tl;
   }
+  store_pending();
 }
 
 // ---------------------------------------------- sort of the slots by KV row --
