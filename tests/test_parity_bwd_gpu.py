@@ -94,6 +94,8 @@ def _run(T, H, D, kw, seed, sink=True, stress=False, use_tl=True, active=None, r
     (97, 33, 512, 40, False, False, True),
     (128, 128, 576, 96, True, True, False),
     (70, 64, 512, 33, True, True, True),
+    (60, 80, 576, 48, True, False, True),
+    (45, 96, 512, 40, True, True, True),
 ])
 def test_backward_small(T, H, D, kw, sink, stress, use_tl):
     say("attention backward", T, H, D, kw, sink, stress, use_tl)
@@ -124,3 +126,48 @@ def test_backward_empty_rows_and_no_slots():
                                           softmax_scale=wl.scale)
     torch.cuda.synchronize()
     assert torch.all(dq == 0) and torch.all(dkv == 0) and torch.all(ds == 0)
+
+
+def test_backward_kv_beyond_2gib():
+    """A latent KV spanning more than 2^31 bytes: the gathers then take 64-bit
+    addresses instead of 32-bit buffer offsets. Ids above 2^31 / row bytes are
+    drawn on purpose. The oracle sees the gathered rows only (remapped to a
+    compact KV); every KV row no slot selects must get a zero gradient."""
+    D, H, T_q, kw = 576, 64, 24, 64
+    T_kv = (1 << 31) // (2 * D) + 40000
+    say("attention backward, KV beyond 2 GiB", T_kv)
+    gen = torch.Generator(device=DEV).manual_seed(21)
+    kv = (torch.randn((T_kv, D), generator=gen, device=DEV) / math.sqrt(D)).to(torch.bfloat16)
+    q = (torch.randn((T_q, H, D), generator=gen, device=DEV) / math.sqrt(D)).to(torch.bfloat16)
+    sink = torch.randn((H,), generator=gen, device=DEV)
+    rng = np.random.default_rng(8)
+    lo = (1 << 31) // (2 * D) - 2000
+    idx = np.empty((T_q, kw), dtype=np.int64)
+    for t in range(T_q):
+        idx[t] = np.sort(np.concatenate([rng.choice(np.arange(lo, T_kv), kw // 2, replace=False),
+                                         rng.choice(lo, kw // 2, replace=False)]))
+    idx[3, 5] = -1
+    scale = 1.0 / math.sqrt(D)
+    idx_t = torch.from_numpy(idx.astype(np.int32)).to(DEV)
+    out, lse, _ = dsa.dsa_sparse_attn_fwd(q, kv, idx_t, attn_sink=sink, softmax_scale=scale,
+                                          return_max_logits=False)
+    dout = (torch.randn((T_q, H, 512), generator=gen, device=DEV) / math.sqrt(512)).to(torch.bfloat16)
+    dq, dkv, ds = dsa.dsa_sparse_attn_bwd(q, kv, idx_t, out, dout, lse, attn_sink=sink,
+                                          softmax_scale=scale)
+    torch.cuda.synchronize()
+    uniq = np.unique(idx[idx >= 0])
+    remap = np.full(idx.shape, -1, dtype=np.int64)
+    remap[idx >= 0] = np.searchsorted(uniq, idx[idx >= 0])
+    ut = torch.from_numpy(uniq).to(DEV)
+    touched = torch.zeros(T_kv, dtype=torch.bool, device=DEV)
+    touched[ut] = True
+    assert not torch.any(dkv[~touched] != 0), "a KV row no slot selects got a gradient"
+    kv_small = kv[ut].contiguous()
+    dkv_small = dkv[ut].contiguous()
+    del kv, dkv
+    rq, rk, rs = O.sparse_attention_backward(f64(q), f64(kv_small), remap, None, f64(sink), scale,
+                                             f64(dout), 512)
+    _check("dq", f64(dq), rq)
+    _check("dkv", f64(dkv_small), rk)
+    err = np.abs(ds.cpu().numpy().astype(np.float64) - rs).max()
+    assert err <= 1e-3 * max(1.0, np.abs(rs).max())
