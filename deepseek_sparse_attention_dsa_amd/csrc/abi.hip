@@ -297,23 +297,30 @@ static int64_t up256(int64_t x) { return (x + 255) / 256 * 256; }
 
 // Statistics [T_q, H] x 2, the fp32 dkv accumulator, and the sort arrays.
 static int64_t bwd_fixed_bytes(int64_t T_q, int32_t H, int64_t T_kv, int32_t D_qk) {
-  return up256(T_q * H * 4) * 2 + up256(T_kv * D_qk * 4) + up256(T_kv * 4) * 2 +
-         up256((T_kv + 1) * 4);
+  return up256(T_q * H * 4) * 2 + up256(T_kv * D_qk * 4) + up256(T_kv * 4) +
+         up256((T_kv + 1) * 4) + up256(256 * 4);
 }
 
 // Per query row of a chunk: P and dS (bf16 [Kw, HP]), the dkv rows of its
-// slots (bf16 [parts, Kw, D_qk]) and its entries of the sorted slot list.
+// slots (bf16 [parts, Kw, D_qk]) and, per slot, its entry of the sorted slot
+// list and the radix sort's two key / value buffers; plus the sort's digit
+// histograms, 256 per 4096 slots.
 struct BwdRow {
-  int64_t p, c, l;
+  int64_t p, c, l, kw;
 };
 static BwdRow bwd_row_bytes(int32_t H, int32_t k_width, int32_t D_qk) {
   const int64_t hp = (H + 31) / 32 * 32, kw = ((int64_t)k_width + 31) / 32 * 32;
   const int64_t parts = hp % 64 == 0 ? hp / 64 : hp / 32;
-  return BwdRow{kw * hp * 2, parts * kw * D_qk * 2, kw * 4};
+  return BwdRow{kw * hp * 2, parts * kw * D_qk * 2, kw * 4, kw};
+}
+static int64_t bwd_hist_bytes(const BwdRow& r, int64_t rows) {
+  return (rows * r.kw + 4095) / 4096 * 256 * 4;
 }
 static int64_t bwd_chunk_bytes(const BwdRow& r, int64_t rows) {
-  return 2 * up256(rows * r.p) + up256(rows * r.c) + up256(rows * r.l);
+  return 2 * up256(rows * r.p) + up256(rows * r.c) + 5 * up256(rows * r.l) +
+         up256(bwd_hist_bytes(r, rows));
 }
+static int64_t bwd_per_row(const BwdRow& r) { return 2 * r.p + r.c + 5 * r.l + r.kw / 16 + 1; }
 
 int64_t dsa_sparse_attn_bwd_workspace_bytes(int64_t T_q, int32_t H, int64_t T_kv, int32_t D_qk,
                                             int32_t k_width) {
@@ -321,7 +328,7 @@ int64_t dsa_sparse_attn_bwd_workspace_bytes(int64_t T_q, int32_t H, int64_t T_kv
       (D_qk != 576 && D_qk != 512) || k_width < 0)
     return -1;
   const BwdRow row = bwd_row_bytes(H, k_width, D_qk);
-  const int64_t per = 2 * row.p + row.c + row.l;
+  const int64_t per = bwd_per_row(row);
   int64_t rows = per ? ((int64_t)1 << 32) / per : T_q;  // chunk buffers within 4 GiB
   rows = rows < 1 ? 1 : (rows > T_q ? T_q : rows);
   return bwd_fixed_bytes(T_q, H, T_kv, D_qk) + bwd_chunk_bytes(row, rows);
@@ -391,12 +398,14 @@ int dsa_sparse_attn_bwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk, con
   a.Dsum = (float*)take(T_q * H * 4);
   a.dkv_ws = (float*)take(T_kv * D_qk * 4);
   a.cnt = (int32_t*)take(T_kv * 4);
-  a.cursor = (int32_t*)take(T_kv * 4);
   a.offs = (int32_t*)take((T_kv + 1) * 4);
+  a.sort_tot = (uint32_t*)take(256 * 4);
   // the largest chunk of rows whose buffers fit the rest of the workspace
+  // (slot numbers rows * Kw are int32)
   int64_t chunk = T_q > 0 ? T_q : 1;
+  if (row.kw > 0 && chunk > INT32_MAX / row.kw) chunk = INT32_MAX / row.kw;
   while (chunk > 1 && fixed + bwd_chunk_bytes(row, chunk) > workspace_bytes) {
-    const int64_t per = 2 * row.p + row.c + row.l;
+    const int64_t per = bwd_per_row(row);
     const int64_t fit = per ? (workspace_bytes - fixed) / per : chunk;
     chunk = fit < chunk ? (fit > 1 ? fit : 1) : chunk - 1;
   }
@@ -404,6 +413,11 @@ int dsa_sparse_attn_bwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk, con
   a.wsD = (uint16_t*)take(chunk * row.p);
   a.wsC = (uint16_t*)take(chunk * row.c);
   a.list = (int32_t*)take(chunk * row.l);
+  for (int k = 0; k < 2; ++k) {
+    a.sort_keys[k] = (int32_t*)take(chunk * row.l);
+    a.sort_vals[k] = (int32_t*)take(chunk * row.l);
+  }
+  a.sort_hist = (uint32_t*)take(bwd_hist_bytes(row, chunk));
   a.Kw = (k_width + 31) / 32 * 32;
   a.dq = (uint16_t*)dq;
   a.dkv = (uint16_t*)dkv;

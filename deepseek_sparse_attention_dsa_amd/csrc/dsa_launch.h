@@ -91,8 +91,11 @@ struct BwdArgs {
   uint16_t* wsC;            // workspace [nparts, chunk, Kw, D_qk] bf16: dkv row per slot
   int32_t* cnt;             // workspace [T_kv]: slots per KV row (chunk)
   int32_t* offs;            // workspace [T_kv + 1]: list offsets
-  int32_t* cursor;          // workspace [T_kv]
   int32_t* list;            // workspace [chunk * Kw]: slot rows grouped by KV row
+  int32_t* sort_keys[2];    // workspace [chunk * Kw] each: radix sort keys between passes
+  int32_t* sort_vals[2];    // same, slot numbers
+  uint32_t* sort_hist;      // workspace [256, ceil(chunk * Kw / 4096)]
+  uint32_t* sort_tot;       // workspace [256]
   int nparts;               // head parts of the dkv pass (64 heads each)
   int64_t chunk_rows;       // rows of the P / dS / C buffers
   int Kw;                   // k_width rounded up to 32

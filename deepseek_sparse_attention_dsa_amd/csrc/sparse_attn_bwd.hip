@@ -25,8 +25,10 @@
 //    dims; K gathered into the same copy ring as bwd_pds_kernel.
 //  * bwd_dkv_kernel: per tile, dS^T . q + P^T . dout (the query's q and dout
 //    staged in LDS), each slot's row written once as bf16 (per 64-head part).
-//  * bwd_count / bwd_scan / bwd_place: a counting sort of the chunk's valid
-//    slots by KV row, giving each KV row the list of rows written for it.
+//  * bwd_count / bwd_scan: slots per KV row and the offsets of their lists;
+//    bwd_sort_{hist,scan,scatter}: a stable radix sort of the chunk's valid
+//    slots by KV row, giving each KV row the ascending list of the slot rows
+//    written for it (no atomics decide an order, so dkv is reproducible).
 //  * bwd_reduce_kernel: one workgroup per KV row sums its list (and parts) in
 //    fp32 into the dkv workspace; no atomics touch the data.
 //  * bwd_convert_kernel: fp32 workspace -> bf16 dkv.
@@ -613,7 +615,7 @@ __global__ __launch_bounds__(256) void bwd_count_kernel(BwdArgs a) {
   }
 }
 
-// offs = exclusive prefix sum of cnt (T_kv + 1 entries); cursor = 0.
+// offs = exclusive prefix sum of cnt (T_kv + 1 entries).
 __global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
   __shared__ int32_t s_w[16];
   __shared__ int32_t s_carry;
@@ -634,23 +636,163 @@ __global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
     int32_t before = s_carry;
     for (int w = 0; w < wave; ++w) before += s_w[w];
     if (i <= a.T_kv) a.offs[i] = before + incl - v;
-    if (i < a.T_kv) a.cursor[i] = 0;
     __syncthreads();
     if (tid == 1023) s_carry = before + incl;
     __syncthreads();
   }
 }
 
-__global__ __launch_bounds__(256) void bwd_place_kernel(BwdArgs a) {
-  const int64_t rc = blockIdx.x;
-  const int64_t t = a.row0 + rc;
-  const int L = row_len(a, t);
-  for (int s = threadIdx.x; s < L; s += 256) {
-    const int32_t v = a.indices[t * a.ld_idx + s];
-    if (v >= 0 && v < a.T_kv) {
-      const int32_t p = a.offs[v] + atomicAdd(&a.cursor[v], 1);
-      a.list[p] = (int32_t)(rc * a.Kw + s);
+// Stable LSD radix sort of the chunk's valid slots by KV row, 8 bits a pass:
+// the items are the slot numbers c = rc * Kw + s in ascending order, so each
+// KV row's list comes out in ascending c and the per-row sums of
+// bwd_reduce_kernel run in an order fixed by the inputs alone. Per pass a
+// digit histogram per tile of 4096 items (bwd_sort_hist_kernel), a scan per
+// digit over the tiles (bwd_sort_scan_kernel) and a scatter that ranks each
+// item among the equal digits before it in its tile (bwd_sort_scatter_kernel).
+constexpr int kSortWaves = 4, kSortIter = 16;
+constexpr int kSortTile = kSortWaves * kSortIter * 64;
+
+struct SortPass {
+  const int32_t* key_in;  // null on the first pass: the items are the index rows
+  const int32_t* val_in;
+  int32_t* key_out;       // null on the last pass
+  int32_t* val_out;
+  int64_t n_items;        // first pass: rows * Kw slot numbers
+  int shift;
+  int nblk;
+};
+
+// Item i of a pass: its key (KV row) and value (slot number) when valid.
+__device__ __forceinline__ bool sort_item(const BwdArgs& a, const SortPass& p, int64_t i,
+                                          int32_t n_valid, int32_t& key, int32_t& val) {
+  if (!p.key_in) {
+    if (i >= p.n_items) return false;
+    const int64_t rc = i / a.Kw;
+    const int s = (int)(i - rc * a.Kw);
+    const int64_t t = a.row0 + rc;
+    if (s >= row_len(a, t)) return false;
+    key = a.indices[t * a.ld_idx + s];
+    val = (int32_t)i;
+    return key >= 0 && key < a.T_kv;
+  }
+  if (i >= n_valid) return false;
+  key = p.key_in[i];
+  val = p.val_in[i];
+  return true;
+}
+
+__global__ __launch_bounds__(256) void bwd_sort_hist_kernel(BwdArgs a, SortPass p) {
+  __shared__ uint32_t s_h[256];
+  const int tid = threadIdx.x;
+  s_h[tid] = 0;
+  __syncthreads();
+  const int32_t n_valid = p.key_in ? a.offs[a.T_kv] : 0;
+  const int64_t base = (int64_t)blockIdx.x * kSortTile;
+  for (int k = 0; k < kSortTile / 256; ++k) {
+    int32_t key, val;
+    if (sort_item(a, p, base + 256 * k + tid, n_valid, key, val))
+      atomicAdd(&s_h[(key >> p.shift) & 255], 1u);
+  }
+  __syncthreads();
+  a.sort_hist[(int64_t)tid * p.nblk + blockIdx.x] = s_h[tid];
+}
+
+// In place: hist[d][b] = the items of digit d in tiles before b; tot[d] = all.
+__global__ __launch_bounds__(256) void bwd_sort_scan_kernel(BwdArgs a, SortPass p) {
+  __shared__ uint32_t s_w[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t* h = a.sort_hist + (int64_t)blockIdx.x * p.nblk;
+  uint32_t carry = 0;
+  for (int b0 = 0; b0 < p.nblk; b0 += 256) {
+    const int i = b0 + tid;
+    const uint32_t v = i < p.nblk ? h[i] : 0u;
+    uint32_t incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
     }
+    if (lane == 63) s_w[wave] = incl;
+    __syncthreads();
+    uint32_t before = carry;
+    for (int w = 0; w < wave; ++w) before += s_w[w];
+    if (i < p.nblk) h[i] = before + incl - v;
+    carry += s_w[0] + s_w[1] + s_w[2] + s_w[3];
+    __syncthreads();
+  }
+  if (tid == 0) a.sort_tot[blockIdx.x] = carry;
+}
+
+__global__ __launch_bounds__(256) void bwd_sort_scatter_kernel(BwdArgs a, SortPass p) {
+  __shared__ uint32_t s_cnt[kSortWaves][256];  // per wave: items of each digit so far
+  __shared__ uint32_t s_base[256];
+  __shared__ uint32_t s_w[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t n_valid = p.key_in ? a.offs[a.T_kv] : 0;
+  const int64_t tile0 = (int64_t)blockIdx.x * kSortTile;
+  if (p.key_in && tile0 >= n_valid) return;  // uniform
+#pragma unroll
+  for (int w = 0; w < kSortWaves; ++w) s_cnt[w][tid] = 0;
+  {
+    // digit d's first output position in this tile: all smaller digits plus
+    // digit d's items in earlier tiles
+    const uint32_t tot = a.sort_tot[tid];
+    uint32_t incl = tot;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = __shfl_up(incl, d, 64);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) s_w[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+    for (int w = 0; w < wave; ++w) before += s_w[w];
+    s_base[tid] = before + incl - tot + a.sort_hist[(int64_t)tid * p.nblk + blockIdx.x];
+  }
+  __syncthreads();
+  // Wave w ranks its 1024 consecutive items 64 at a time; lanes with equal
+  // digits find each other with one ballot per digit bit.
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int64_t i0 = tile0 + (int64_t)wave * (kSortIter * 64) + lane;
+  int32_t key[kSortIter], val[kSortIter];
+  uint32_t rk[kSortIter];
+#pragma unroll
+  for (int it = 0; it < kSortIter; ++it) {
+    const bool ok = sort_item(a, p, i0 + 64 * it, n_valid, key[it], val[it]);
+    const uint32_t d = ok ? ((uint32_t)key[it] >> p.shift) & 255u : 0u;
+    uint64_t peers = __ballot(ok);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const uint64_t m = __ballot((d >> b) & 1u);
+      peers &= ((d >> b) & 1u) ? m : ~m;
+    }
+    uint32_t r = 0xffffffffu;
+    if (ok) {
+      const uint32_t prev = s_cnt[wave][d];
+      r = ((prev + (uint32_t)__popcll(peers & below)) << 8) | d;
+      if ((peers & below) == 0) s_cnt[wave][d] = prev + (uint32_t)__popcll(peers);
+    }
+    rk[it] = r;
+  }
+  __syncthreads();
+  {
+    uint32_t run = 0;
+#pragma unroll
+    for (int w = 0; w < kSortWaves; ++w) {
+      const uint32_t c = s_cnt[w][tid];
+      s_cnt[w][tid] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < kSortIter; ++it) {
+    if (rk[it] == 0xffffffffu) continue;
+    const uint32_t d = rk[it] & 255u;
+    const uint32_t pos = s_base[d] + s_cnt[wave][d] + (rk[it] >> 8);
+    if (pos >= (uint32_t)p.n_items) continue;  // cannot happen: a rank below all items
+    if (p.key_out) p.key_out[pos] = key[it];
+    p.val_out[pos] = val[it];
   }
 }
 
@@ -739,7 +881,24 @@ hipError_t launch_bwd_nw(BwdArgs a, int64_t chunk, hipStream_t st) {
                          st, reinterpret_cast<float*>(a.cnt), a.T_kv);
       hipLaunchKernelGGL(bwd_count_kernel, dim3((unsigned)n), dim3(256), 0, st, a);
       hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, st, a);
-      hipLaunchKernelGGL(bwd_place_kernel, dim3((unsigned)n), dim3(256), 0, st, a);
+      // keys below T_kv: 8 bits a pass, the last pass writes the list
+      const int bits = a.T_kv > 1 ? 32 - __builtin_clz((uint32_t)(a.T_kv - 1)) : 0;
+      const int passes = bits > 8 ? (bits + 7) / 8 : 1;
+      SortPass p{};
+      p.n_items = n * a.Kw;
+      p.nblk = (int)((p.n_items + kSortTile - 1) / kSortTile);
+      for (int ps = 0; ps < passes; ++ps) {
+        const bool last = ps + 1 == passes;
+        p.shift = 8 * ps;
+        p.key_out = last ? nullptr : a.sort_keys[ps & 1];
+        p.val_out = last ? a.list : a.sort_vals[ps & 1];
+        hipLaunchKernelGGL(bwd_sort_hist_kernel, dim3((unsigned)p.nblk), dim3(256), 0, st, a, p);
+        hipLaunchKernelGGL(bwd_sort_scan_kernel, dim3(256), dim3(256), 0, st, a, p);
+        hipLaunchKernelGGL(bwd_sort_scatter_kernel, dim3((unsigned)p.nblk), dim3(256), 0, st, a,
+                           p);
+        p.key_in = a.sort_keys[ps & 1];
+        p.val_in = a.sort_vals[ps & 1];
+      }
       hipLaunchKernelGGL((bwd_reduce_kernel<DQK>), dim3((unsigned)a.T_kv), dim3(256), 0, st, a);
     }
   }

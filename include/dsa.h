@@ -305,10 +305,11 @@ int dsa_sparse_attn_fwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk,
 /*
  * dsa_sparse_attn_bwd_workspace_bytes - device workspace dsa_sparse_attn_bwd
  * uses for these sizes: fp32 statistics [T_q, H] x 2, an fp32 dkv
- * accumulator [T_kv, D_qk], the slot-sort arrays [T_kv], and per query row
- * of a chunk its bf16 P and dS, the bf16 dkv rows of its slots and its slot
- * list, for chunks of up to 4 GiB (min(T_q, rows that fit) rows at a
- * time). Returns -1 for sizes out of contract.
+ * accumulator [T_kv, D_qk], per-KV-row counts and offsets [T_kv], and per
+ * query row of a chunk its bf16 P and dS, the bf16 dkv rows of its slots,
+ * its slot list and the slot sort's key / value buffers, for chunks of up
+ * to 4 GiB (min(T_q, rows that fit) rows at a time). Returns -1 for sizes
+ * out of contract.
  */
 int64_t dsa_sparse_attn_bwd_workspace_bytes(int64_t T_q, int32_t H, int64_t T_kv, int32_t D_qk,
                                             int32_t k_width);
@@ -346,9 +347,10 @@ int64_t dsa_sparse_attn_bwd_workspace_bytes(int64_t T_q, int32_t H, int64_t T_kv
  *               processes more query rows per pass
  * bf16 MFMA products with fp32 accumulation; P and dS are rounded to bf16
  * before the dq and dkv products, and each slot's dkv row (summed over the
- * heads) to bf16 before the per-KV-row sum, which is fp32; the order of
- * that sum follows the slot sort, which uses atomic counters, so the last
- * bits of dkv may vary between runs. d_sink is summed in a fixed order.
+ * heads) to bf16 before the per-KV-row sum, which is fp32 and runs over
+ * the slots in ascending (row, slot) order within each chunk of query rows
+ * (a stable sort, no atomics on the order): equal inputs and workspace
+ * sizes give identical bits. d_sink is summed in a fixed order.
  * Errors: the checks of dsa_sparse_attn_fwd, DSA_ERR_VALUE for D_v != 512,
  * a separate V, or a workspace too small for one row.
  */

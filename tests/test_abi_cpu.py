@@ -237,12 +237,15 @@ def test_python_binding_type_and_shape_errors():
 
 def test_backward_workspace_size_rule():
     lib = dsa.load_library()
-    # statistics, dkv accumulator and sort arrays, then P, dS, the per-slot dkv
-    # rows and the slot list of every row when they fit in 4 GiB
+    # statistics, dkv accumulator, per-KV-row counts and offsets and the radix
+    # sort's 256 digit totals, then P, dS, the per-slot dkv rows, the slot
+    # list and the sort's two key / value buffers of every row, and the sort's
+    # 256 digit counts per 4096 slots, when they fit in 4 GiB
     n = lib.dsa_sparse_attn_bwd_workspace_bytes(256, 16, 256, 576, 64)
     up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    fixed = 2 * up(256 * 16 * 4) + up(256 * 576 * 4) + 2 * up(256 * 4) + up(257 * 4)
-    rows = 2 * up(256 * 64 * 32 * 2) + up(256 * 64 * 576 * 2) + up(256 * 64 * 4)
+    fixed = 2 * up(256 * 16 * 4) + up(256 * 576 * 4) + up(256 * 4) + up(257 * 4) + up(1024)
+    rows = (2 * up(256 * 64 * 32 * 2) + up(256 * 64 * 576 * 2) + 5 * up(256 * 64 * 4)
+            + up(4 * 1024))
     assert n == fixed + rows
     assert lib.dsa_sparse_attn_bwd_workspace_bytes(10, 0, 10, 576, 8) == -1
     assert lib.dsa_sparse_attn_bwd_workspace_bytes(10, 8, 10, 256, 8) == -1

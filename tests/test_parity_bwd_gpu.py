@@ -171,3 +171,49 @@ def test_backward_kv_beyond_2gib():
     _check("dkv", f64(dkv_small), rk)
     err = np.abs(ds.cpu().numpy().astype(np.float64) - rs).max()
     assert err <= 1e-3 * max(1.0, np.abs(rs).max())
+
+
+def test_backward_reproducible_and_chunked():
+    """dkv is summed per KV row in ascending slot order (a stable radix sort
+    of the slots, no atomics), so repeated calls give identical bits, also
+    with a workspace holding stale data; a workspace that holds only a few
+    rows at a time (several chunks) stays within the oracle's tolerance.
+    T_kv = 600 needs two 8-bit sort passes; most KV rows sit in hundreds of
+    lists and every fifth row repeats a slot."""
+    T, H, D, kw = 600, 64, 576, 256
+    wl = make_custom([T], H=H, D_qk=D, D_v=512, H_idx=0, seed=31, device=DEV, sink=True,
+                     topk=kw)
+    rng = np.random.default_rng(31)
+    idx, tl = _indices(T, kw, T, rng)
+    idx_t = torch.from_numpy(idx).to(DEV)
+    tl_t = torch.from_numpy(tl).to(DEV)
+    out, lse, _ = dsa.dsa_sparse_attn_fwd(wl.q, wl.kv, idx_t, topk_length=tl_t, attn_sink=wl.sink,
+                                          softmax_scale=wl.scale, return_max_logits=False)
+    g = torch.Generator(device=DEV).manual_seed(32)
+    dout = (torch.randn((T, H, 512), generator=g, device=DEV) / math.sqrt(512)).to(torch.bfloat16)
+    need = dsa.dsa_sparse_attn_bwd_workspace_bytes(T, H, T, D, kw)
+    runs = []
+    for fill in (0, 0xA5, 0x3C):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device=DEV)
+        runs.append(dsa.dsa_sparse_attn_bwd(wl.q, wl.kv, idx_t, out, dout, lse, topk_length=tl_t,
+                                            attn_sink=wl.sink, softmax_scale=wl.scale,
+                                            workspace=ws))
+        torch.cuda.synchronize()
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            assert torch.equal(a, b)
+    say("  three calls: identical dq, dkv, d_sink")
+    # a workspace for about 37 rows: 17 chunks
+    full = dsa.dsa_sparse_attn_bwd_workspace_bytes(37, H, T, D, kw)
+    ws = torch.full((full,), 0x5A, dtype=torch.uint8, device=DEV)
+    dq, dkv, ds = dsa.dsa_sparse_attn_bwd(wl.q, wl.kv, idx_t, out, dout, lse, topk_length=tl_t,
+                                          attn_sink=wl.sink, softmax_scale=wl.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, runs[0][0])
+    rq, rk, rs = O.sparse_attention_backward(f64(wl.q), f64(wl.kv), idx.astype(np.int64), tl,
+                                             f64(wl.sink), wl.scale, f64(dout), 512)
+    _check("dq", f64(dq), rq)
+    _check("dkv", f64(dkv), rk)
+    _check("dkv (one chunk)", f64(runs[0][1]), rk)
+    err = np.abs(ds.cpu().numpy().astype(np.float64) - rs).max()
+    assert err <= 1e-3 * max(1.0, np.abs(rs).max())
