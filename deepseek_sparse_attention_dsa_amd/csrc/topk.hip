@@ -12,10 +12,13 @@
 // positions come from one rule: a selected column goes to
 // (#greater before it) + min(#equal before it, #equal taken).
 //
-// Rows of up to 4096 columns (topk_radix_kernel): one workgroup keeps the
-// row in VGPRs, finds the K-th largest key theta with three LDS-histogram
-// passes over 11/11/10-bit digits, then walks the columns in ascending order
-// with wave ballots and mbcnt prefix counts.
+// Rows of up to 4096 columns (topk_radix_kernel): one workgroup (four waves
+// from 1025 columns up) keeps the row in VGPRs, counts its keys into 2048
+// buckets linear in the score between the row's extremes, ranks the few
+// members of the bucket holding the K-th largest key exactly to find theta
+// (radix passes over 11/11/10-bit digits when a bucket holds more than 64),
+// then walks the columns in ascending order with wave ballots and mbcnt
+// prefix counts.
 //
 // Longer rows (topk_stream_kernel) are streamed once and never held on chip,
 // so several rows share a CU and one row's loads overlap another's work:
@@ -165,6 +168,34 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* s_red) {
   return v;
 }
 
+// Finds the bucket holding the `want`-th largest of the keys counted in
+// hist (1 <= want <= their number): s_sel[0] = bucket, s_sel[1] = count in
+// the buckets above it. Ends with a barrier.
+template <int WAVES>
+__device__ __forceinline__ void find_bucket(const uint32_t* hist, uint32_t want, uint32_t* s_wave,
+                                            uint32_t* s_sel) {
+  constexpr int BPT = kBins / (64 * WAVES);
+  const int hi_bin = kBins - 1 - (int)threadIdx.x * BPT;  // thread owns [hi_bin - BPT + 1, hi_bin]
+  uint32_t local = 0;
+#pragma unroll
+  for (int b = 0; b < BPT; ++b) local += hist[hi_bin - b];
+  uint32_t total;
+  const uint32_t above = block_exclusive_scan<WAVES>(local, s_wave, &total);
+  if (above < want && want <= above + local) {
+    uint32_t acc = above;
+    for (int b = 0; b < BPT; ++b) {
+      const uint32_t h = hist[hi_bin - b];
+      if (acc + h >= want) {
+        s_sel[0] = (uint32_t)(hi_bin - b);
+        s_sel[1] = acc;
+        break;
+      }
+      acc += h;
+    }
+  }
+  __syncthreads();
+}
+
 // Ordered write of the selected keys of one thread's run, given the counts
 // of keys above / equal to theta before the run (in column order).
 struct Placer {
@@ -199,6 +230,8 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t s_wave[2][WAVES > 1 ? WAVES : 1];
   __shared__ uint32_t s_sel[2];
+  __shared__ uint32_t s_mem[64];
+  __shared__ uint32_t s_cnt;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -214,9 +247,17 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
 
   if (n <= k) {
     // Every causal column is selected; no select needed.
-    for (int i = tid; i < k; i += NT) {
-      out_idx[i] = i < n ? base + i : -1;
-      if (out_val) out_val[i] = i < n ? row[i] : -__builtin_inff();
+    if (!out_val && (k & 3) == 0 && ((uintptr_t)out_idx & 15u) == 0) {
+      // 16-byte stores of four consecutive slots
+      for (int i = 4 * tid; i < k; i += 4 * NT)
+        *reinterpret_cast<i32x4*>(out_idx + i) =
+            i32x4{i + 0 < n ? base + i + 0 : -1, i + 1 < n ? base + i + 1 : -1,
+                  i + 2 < n ? base + i + 2 : -1, i + 3 < n ? base + i + 3 : -1};
+    } else {
+      for (int i = tid; i < k; i += NT) {
+        out_idx[i] = i < n ? base + i : -1;
+        if (out_val) out_val[i] = i < n ? row[i] : -__builtin_inff();
+      }
     }
     if (tid == 0 && topk_length) topk_length[r] = n;
     return;
@@ -241,15 +282,83 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
                     col + 2 < n ? float_to_key(raw[c].z) : 0u, col + 3 < n ? float_to_key(raw[c].w) : 0u};
   }
 
-  uint32_t need_eq;
-  const uint32_t theta = radix_select<WAVES>((uint32_t)k, hist, s_wave[0], s_sel, &need_eq,
-                                             [&](auto&& f) {
+  // theta: one histogram over kBins buckets linear in the score between the
+  // row's smallest and largest valid scores (monotone in the key), then the
+  // members of the bucket holding the k-th largest key are ranked exactly:
+  // by one wave when there are at most 64 of them, else by radix passes
+  // restricted to the bucket (heavy ties, infinite scores).
+  uint32_t kmax = 0u, knmax = 0u;
 #pragma unroll
-    for (int c = 0; c < CH; ++c)
+  for (int c = 0; c < CH; ++c)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (kreg[c][e] != 0u) f(kreg[c][e]);
-  });
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = kreg[c][e];
+      kmax = max(kmax, key);
+      knmax = max(knmax, key != 0u ? ~key : 0u);
+    }
+  kmax = block_max<WAVES>(kmax, s_wave[1]);
+  const uint32_t kmin = ~block_max<WAVES>(knmax, s_wave[1]);
+  const float flo = key_to_float(kmin), span = key_to_float(kmax) - flo;
+  const LinearBuckets lb{flo, span > 0.0f ? (float)kBins / span : 0.0f};
+  for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
+  if (tid == 0) s_cnt = 0u;
+  __syncthreads();
+  uint16_t bk[CH][4];
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      bk[c][e] = (uint16_t)lb(kreg[c][e]);
+      if (kreg[c][e] != 0u) atomicAdd(&hist[bk[c][e]], 1u);
+    }
+  __syncthreads();
+  find_bucket<WAVES>(hist, (uint32_t)k, s_wave[0], s_sel);
+  const uint32_t bstar = s_sel[0];
+  const uint32_t rem = (uint32_t)k - s_sel[1];  // >= 1 keys to take from bucket bstar
+  // members of bucket bstar into a small list (order does not matter here)
+#pragma unroll
+  for (int c = 0; c < CH; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool mem = kreg[c][e] != 0u && bk[c][e] == bstar;
+      const uint64_t bal = ballot(mem);
+      if (bal != 0u) {  // uniform
+        uint32_t at = 0u;
+        if (lane == 0) at = atomicAdd(&s_cnt, (uint32_t)__popcll(bal));
+        at = __shfl(at, 0, 64) + popc_below(bal);
+        if (mem && at < 64u) s_mem[at] = kreg[c][e];
+      }
+    }
+  __syncthreads();
+  const uint32_t m = s_cnt;
+  uint32_t theta, need_eq;
+  if (m <= 64u) {  // uniform
+    if (wave == 0) {
+      const uint32_t x = lane < (int)m ? s_mem[lane] : 0u;
+      uint32_t gt = 0u, eq = 0u;
+      for (uint32_t j = 0; j < m; ++j) {
+        const uint32_t y = s_mem[j];
+        gt += y > x;
+        eq += y == x;
+      }
+      if (lane < (int)m && gt < rem && rem <= gt + eq) {  // equal members write equal values
+        s_sel[0] = x;
+        s_sel[1] = rem - gt;
+      }
+    }
+    __syncthreads();
+    theta = s_sel[0];
+    need_eq = s_sel[1];
+  } else {
+    theta = radix_select<WAVES>(rem, hist, s_wave[0], s_sel, &need_eq, [&](auto&& f) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (kreg[c][e] != 0u && bk[c][e] == bstar) f(kreg[c][e]);
+    });
+  }
+  __syncthreads();  // s_wave is reused below
 
   // per-wave counts of keys above / equal to theta, then the waves before
   uint32_t lgt = 0, leq = 0;
@@ -616,7 +725,7 @@ hipError_t launch_topk(const float* scores, int64_t ld, int64_t n_rows, int64_t 
     return launch_radix<1, 4>(scores, ld, n_rows, n_cols, seq_lens, row_starts, k, indices, ld_idx,
                               topk_length, values, st);
   if (n_cols <= 4096)
-    return launch_radix<1, 16>(scores, ld, n_rows, n_cols, seq_lens, row_starts, k, indices,
+    return launch_radix<4, 4>(scores, ld, n_rows, n_cols, seq_lens, row_starts, k, indices,
                                ld_idx, topk_length, values, st);
   if (n_cols <= 65536) {
     dim3 grid((unsigned)n_rows), block(kSThreads);

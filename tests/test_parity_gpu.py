@@ -139,9 +139,10 @@ def test_topk_synthetic(n_cols, kind):
                     row_starts=starts.to(DEV) if k != 7 else None, n_cols=n_cols)
 
 
-def test_topk_special_rows():
-    say("topk special rows")
-    n_cols, k = 3000, 64
+@pytest.mark.parametrize("n_cols", [200, 1000, 3000])
+def test_topk_special_rows(n_cols):
+    say("topk special rows", n_cols)
+    k = 64
     rows = []
     rows.append(np.full(n_cols, 0.25))                       # all equal -> first K
     rows.append(np.arange(n_cols, dtype=np.float64))         # increasing -> last K
@@ -154,6 +155,15 @@ def test_topk_special_rows():
     rows.append(r)                                           # -inf is a value
     r = np.random.default_rng(0).standard_normal(n_cols)
     r[r < 1.5] = 1.5                                         # huge tie at the boundary
+    rows.append(r)
+    r = np.random.default_rng(1).standard_normal(n_cols)
+    r[[5, 17, n_cols - 1]] = np.inf                          # +inf scores
+    rows.append(r)
+    one_up = float(np.nextafter(np.float32(1.0), np.float32(2.0)))
+    rows.append(np.where(np.arange(n_cols) % 3 == 0, one_up, 1.0))  # span of one ulp
+    r = np.random.default_rng(2).standard_normal(n_cols)
+    low = r < 2.5                                            # the boundary falls inside it
+    r[low] = 1.0 + np.float32(2.0 ** -20) * np.cumsum(low)[low]     # dense distinct cluster
     rows.append(r)
     x = torch.tensor(np.stack(rows), dtype=torch.float32)
     lens = torch.full((len(rows),), n_cols, dtype=torch.int32)
