@@ -211,6 +211,35 @@ __device__ __forceinline__ void wave_key_range(const int32_t* row_starts, const 
   }
 }
 
+// Wave-wide inclusive scan / reductions on DPP lane moves (no LDS round
+// trips): row_shr 1, 2, 4, 8 inside each 16-lane row, then row_bcast 15 and
+// row_bcast 31 carry the row totals upwards (GFX9 DPP controls).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t v, Op op, uint32_t ident) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x111, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x112, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x114, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x118, 0xf, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x142, 0xa, 0xf, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)ident, (int)v, 0x143, 0xc, 0xf, false));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = wave_incl_scan_dpp(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; }, 0u);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = wave_incl_scan_dpp(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; }, 0xffffffffu);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  const uint32_t s = wave_incl_scan_dpp(
+      __float_as_uint(v),
+      [](uint32_t a, uint32_t b) { return __float_as_uint(__uint_as_float(a) + __uint_as_float(b)); },
+      0u);
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)s, 63));
+}
+
 // Number of set bits of `mask` in lanes strictly below the calling lane.
 __device__ __forceinline__ uint32_t popc_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

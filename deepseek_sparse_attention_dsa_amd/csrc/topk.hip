@@ -63,14 +63,9 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
                                                          uint32_t* total) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    uint32_t o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
+  const uint32_t incl = wave_incl_scan_dpp(v, [](uint32_t a, uint32_t b) { return a + b; }, 0u);
   if (WAVES == 1) {
-    *total = __shfl(incl, 63, 64);
+    *total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
     return incl - v;
   }
   if (lane == 63) s_wave[wave] = incl;
@@ -144,19 +139,20 @@ __device__ __forceinline__ uint32_t radix_select(uint32_t remaining, uint32_t* h
 // so the buckets split the keys into ordered ranges.
 struct LinearBuckets {
   float lo, scale;
-  __device__ __forceinline__ int operator()(uint32_t key) const {
-    const float x = (key_to_float(key) - lo) * scale;
+  // (-0.0 and +0.0 land in the same bucket, as their keys are equal)
+  __device__ __forceinline__ int of_value(float v) const {
+    const float x = (v - lo) * scale;
     if (!(x > 0.0f)) return 0;  // also NaN (inf * 0 when lo = -inf)
     return x >= (float)(kBins - 1) ? kBins - 1 : (int)x;
   }
+  __device__ __forceinline__ int operator()(uint32_t key) const { return of_value(key_to_float(key)); }
 };
 
 // Max over the workgroup (s_red: WAVES words).
 template <int WAVES>
 __device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* s_red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, (uint32_t)__shfl_xor(v, d, 64));
+  v = wave_max_u32(v);
   if (WAVES > 1) {
     if (lane == 0) s_red[wave] = v;
     __syncthreads();
@@ -227,7 +223,7 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
     float* __restrict__ values) {
   constexpr int NT = 64 * WAVES;
   static_assert(kBins % NT == 0, "bins must split evenly over threads");
-  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t hist[kBins + 64];  // + a spare output slot per lane
   __shared__ uint32_t s_wave[2][WAVES > 1 ? WAVES : 1];
   __shared__ uint32_t s_sel[2];
   __shared__ uint32_t s_mem[64];
@@ -286,7 +282,8 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
   // row's smallest and largest valid scores (monotone in the key), then the
   // members of the bucket holding the k-th largest key are ranked exactly:
   // by one wave when there are at most 64 of them, else by radix passes
-  // restricted to the bucket (heavy ties, infinite scores).
+  // restricted to the bucket (heavy ties, infinite scores). Wave-wide
+  // reductions and scans run on DPP lane moves; the waves meet in LDS.
   uint32_t kmax = 0u, knmax = 0u;
 #pragma unroll
   for (int c = 0; c < CH; ++c)
@@ -296,19 +293,30 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
       kmax = max(kmax, key);
       knmax = max(knmax, key != 0u ? ~key : 0u);
     }
-  kmax = block_max<WAVES>(kmax, s_wave[1]);
-  const uint32_t kmin = ~block_max<WAVES>(knmax, s_wave[1]);
-  const float flo = key_to_float(kmin), span = key_to_float(kmax) - flo;
-  const LinearBuckets lb{flo, span > 0.0f ? (float)kBins / span : 0.0f};
+  kmax = wave_max_u32(kmax);
+  knmax = wave_max_u32(knmax);
   for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
   if (tid == 0) s_cnt = 0u;
+  if (WAVES > 1 && lane == 0) {
+    s_wave[0][wave] = kmax;
+    s_wave[1][wave] = knmax;
+  }
   __syncthreads();
+  if (WAVES > 1) {
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+      kmax = max(kmax, s_wave[0][w]);
+      knmax = max(knmax, s_wave[1][w]);
+    }
+  }
+  const float flo = key_to_float(~knmax), span = key_to_float(kmax) - flo;
+  const LinearBuckets lb{flo, span > 0.0f ? (float)kBins / span : 0.0f};
   uint16_t bk[CH][4];
 #pragma unroll
   for (int c = 0; c < CH; ++c)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      bk[c][e] = (uint16_t)lb(kreg[c][e]);
+      bk[c][e] = (uint16_t)lb.of_value(raw[c][e]);
       if (kreg[c][e] != 0u) atomicAdd(&hist[bk[c][e]], 1u);
     }
   __syncthreads();
@@ -358,54 +366,62 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
           if (kreg[c][e] != 0u && bk[c][e] == bstar) f(kreg[c][e]);
     });
   }
-  __syncthreads();  // s_wave is reused below
 
-  // per-wave counts of keys above / equal to theta, then the waves before
-  uint32_t lgt = 0, leq = 0;
-#pragma unroll
-  for (int c = 0; c < CH; ++c)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      lgt += kreg[c][e] > theta;
-      leq += kreg[c][e] == theta;
-    }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    lgt += __shfl_xor(lgt, d, 64);
-    leq += __shfl_xor(leq, d, 64);
-  }
-  uint32_t gt_run = 0, eq_run = 0;
-  if (WAVES > 1) {
-    if (lane == 0) {
-      s_wave[0][wave] = lgt;
-      s_wave[1][wave] = leq;
-    }
-    __syncthreads();
-    for (int w = 0; w < wave; ++w) {
-      gt_run += s_wave[0][w];
-      eq_run += s_wave[1][w];
-    }
-  }
-  // ordered compaction straight into the output
-  const Placer place{theta, need_eq, (uint32_t)k, out_idx, out_val};
+  // Output positions follow column order (wave, chunk, lane, element). Per
+  // chunk, each lane counts its keys above and equal to theta, packed as
+  // (above | equal << 16) (both < 2^16), and the wave scans the packed counts
+  // over its lanes; the waves' totals meet in LDS.
+  uint32_t excl[CH], chunk_base[CH];
+  uint32_t wave_tot = 0u;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
-    const u32x4 kv = kreg[c];
-    uint32_t below_gt = 0, below_eq = 0, tot_gt = 0, tot_eq = 0;
+    uint32_t p = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      p += (kreg[c][e] > theta ? 1u : 0u) + (kreg[c][e] == theta ? 0x10000u : 0u);
+    const uint32_t incl = wave_incl_scan_dpp(p, [](uint32_t a, uint32_t b) { return a + b; }, 0u);
+    excl[c] = incl - p;
+    chunk_base[c] = wave_tot;
+    wave_tot += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  }
+  uint32_t wave_base = 0u;
+  if (WAVES > 1) {
+    __syncthreads();  // every wave has read theta from s_sel and left the scans of s_wave
+    if (lane == 0) s_wave[1][wave] = wave_tot;
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) wave_base += w < wave ? s_wave[1][w] : 0u;
+  }
+  // Without values and with 16-byte aligned output rows, the k slots are
+  // staged in LDS (the histogram is free now; k <= kBins; unselected columns
+  // write a spare slot of their lane) and leave in 16-byte stores; otherwise
+  // they are written in place.
+  const bool staged = !out_val && (k & 3) == 0 && ((uintptr_t)out_idx & 15u) == 0;  // uniform
+  if (staged) __syncthreads();  // the histogram's last readers are done
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    uint32_t cnt = wave_base + chunk_base[c] + excl[c];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint64_t bg = ballot(kv[e] > theta);
-      const uint64_t be = ballot(kv[e] == theta);
-      below_gt += popc_below(bg);
-      below_eq += popc_below(be);
-      tot_gt += __popcll(bg);
-      tot_eq += __popcll(be);
+      const uint32_t key = kreg[c][e];
+      const bool is_gt = key > theta, is_eq = key == theta;
+      const uint32_t ng = cnt & 0xffffu, nq = cnt >> 16;
+      const uint32_t pos = ng + min(nq, need_eq);
+      const bool take = (is_gt || (is_eq && nq < need_eq)) && pos < (uint32_t)k;
+      const int32_t gcol = base + wbase + c * 256 + lane * 4 + e;
+      if (staged) {
+        hist[take ? pos : (uint32_t)(kBins + lane)] = (uint32_t)gcol;
+      } else if (take) {
+        out_idx[pos] = gcol;
+        if (out_val) out_val[pos] = key_to_float(key);
+      }
+      cnt += (is_gt ? 1u : 0u) + (is_eq ? 0x10000u : 0u);
     }
-    uint32_t g = gt_run + below_gt, q = eq_run + below_eq;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) place(kv[e], base + wbase + c * 256 + lane * 4 + e, g, q);
-    gt_run += tot_gt;
-    eq_run += tot_eq;
+  }
+  if (staged) {
+    __syncthreads();
+    for (int i = 4 * tid; i < k; i += 4 * NT)
+      *reinterpret_cast<u32x4*>(out_idx + i) = *reinterpret_cast<const u32x4*>(hist + i);
   }
   if (tid == 0 && topk_length) topk_length[r] = k;
 }
