@@ -333,7 +333,7 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
       if (bal != 0u) {  // uniform
         uint32_t at = 0u;
         if (lane == 0) at = atomicAdd(&s_cnt, (uint32_t)__popcll(bal));
-        at = __shfl(at, 0, 64) + popc_below(bal);
+        at = (uint32_t)__builtin_amdgcn_readlane((int)at, 0) + popc_below(bal);
         if (mem && at < 64u) s_mem[at] = kreg[c][e];
       }
     }
@@ -344,8 +344,8 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
     if (wave == 0) {
       const uint32_t x = lane < (int)m ? s_mem[lane] : 0u;
       uint32_t gt = 0u, eq = 0u;
-      for (uint32_t j = 0; j < m; ++j) {
-        const uint32_t y = s_mem[j];
+      for (uint32_t j = 0; j < m; ++j) {  // member j broadcast from lane j
+        const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, (int)j);
         gt += y > x;
         eq += y == x;
       }
