@@ -12,13 +12,13 @@
 // positions come from one rule: a selected column goes to
 // (#greater before it) + min(#equal before it, #equal taken).
 //
-// Rows of up to 4096 columns (topk_radix_kernel): one workgroup (four waves
-// from 1025 columns up) keeps the row in VGPRs, counts its keys into 2048
-// buckets linear in the score between the row's extremes, ranks the few
-// members of the bucket holding the K-th largest key exactly to find theta
-// (radix passes over 11/11/10-bit digits when a bucket holds more than 64),
-// then walks the columns in ascending order with wave ballots and mbcnt
-// prefix counts.
+// Rows of up to 8192 columns (topk_radix_kernel): one workgroup (four waves
+// from 1025 columns up, eight from 4097) keeps the row in VGPRs, counts its
+// keys into 2048 buckets linear in the score between the row's extremes,
+// ranks the few members of the bucket holding the K-th largest key exactly to
+// find theta (radix passes over 11/11/10-bit digits when a bucket holds more
+// than 64), then places the selected columns in ascending order from
+// per-lane counts scanned on DPP lane moves.
 //
 // Longer rows (topk_stream_kernel) are streamed once and never held on chip,
 // so several rows share a CU and one row's loads overlap another's work:
@@ -211,7 +211,7 @@ struct Placer {
   }
 };
 
-// ------------------------------------------------ rows of <= 4096 columns --
+// ------------------------------------------------ rows of <= 8192 columns --
 // CH: 4-column chunks per lane, held in VGPRs. Wave w owns the columns
 // [w * 256 * CH, (w + 1) * 256 * CH); chunk c of a wave covers 256
 // consecutive columns, 4 per lane.
@@ -426,7 +426,7 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
   if (tid == 0 && topk_length) topk_length[r] = k;
 }
 
-// ------------------------------------------------ rows of > 4096 columns --
+// ------------------------------------------------- rows of > 8192 columns --
 constexpr int kSWaves = 4;
 constexpr int kSThreads = 64 * kSWaves;
 constexpr int kMaxChunks = 65536 / 256;  // 256-column chunks of the longest row
@@ -463,9 +463,16 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
   const int32_t base = row_starts ? row_starts[r] : 0;
 
   if (n <= k) {
-    for (int i = tid; i < k; i += NT) {
-      out_idx[i] = i < n ? base + i : -1;
-      if (out_val) out_val[i] = i < n ? row[i] : -__builtin_inff();
+    if (!out_val && (k & 3) == 0 && ((uintptr_t)out_idx & 15u) == 0) {
+      for (int i = 4 * tid; i < k; i += 4 * NT)
+        *reinterpret_cast<i32x4*>(out_idx + i) =
+            i32x4{i + 0 < n ? base + i + 0 : -1, i + 1 < n ? base + i + 1 : -1,
+                  i + 2 < n ? base + i + 2 : -1, i + 3 < n ? base + i + 3 : -1};
+    } else {
+      for (int i = tid; i < k; i += NT) {
+        out_idx[i] = i < n ? base + i : -1;
+        if (out_val) out_val[i] = i < n ? row[i] : -__builtin_inff();
+      }
     }
     if (tid == 0 && topk_length) topk_length[r] = n;
     return;
@@ -742,7 +749,10 @@ hipError_t launch_topk(const float* scores, int64_t ld, int64_t n_rows, int64_t 
                               topk_length, values, st);
   if (n_cols <= 4096)
     return launch_radix<4, 4>(scores, ld, n_rows, n_cols, seq_lens, row_starts, k, indices,
-                               ld_idx, topk_length, values, st);
+                              ld_idx, topk_length, values, st);
+  if (n_cols <= 8192)
+    return launch_radix<8, 4>(scores, ld, n_rows, n_cols, seq_lens, row_starts, k, indices,
+                              ld_idx, topk_length, values, st);
   if (n_cols <= 65536) {
     dim3 grid((unsigned)n_rows), block(kSThreads);
     hipLaunchKernelGGL(topk_stream_kernel, grid, block, 0, st, scores, ld, n_cols, seq_lens,

@@ -139,7 +139,7 @@ def test_topk_synthetic(n_cols, kind):
                     row_starts=starts.to(DEV) if k != 7 else None, n_cols=n_cols)
 
 
-@pytest.mark.parametrize("n_cols", [200, 1000, 3000])
+@pytest.mark.parametrize("n_cols", [200, 1000, 3000, 6000, 12000])
 def test_topk_special_rows(n_cols):
     say("topk special rows", n_cols)
     k = 64
