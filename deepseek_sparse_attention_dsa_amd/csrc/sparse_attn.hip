@@ -233,6 +233,11 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
     }
   }
 
+  // The head's sink logit, loaded now so that its latency is not paid after
+  // the last tile.
+  const float sink_logit =
+      (a.sink && h0 + r32 < a.H) ? a.sink[h0 + r32] : -__builtin_inff();
+
   f32x16 o[C::NB];
   float m_ref = -__builtin_inff();   // exp2 reference (log2 units) of head r32
   float m_true = -__builtin_inff();  // true running max of head r32
@@ -437,7 +442,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
   float inv = 0.f;
   if (!empty) {
     float denom = l_tot;
-    if (a.sink && head < a.H) denom += fast_exp2(a.sink[head] * kLog2e - m_ref);
+    if (a.sink && head < a.H) denom += fast_exp2(sink_logit * kLog2e - m_ref);
     inv = 1.0f / denom;
   }
   if (half == 0 && head < a.H) {
@@ -477,13 +482,36 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
     }
     __syncthreads();
     if (mine) {
-      for (int c = lane; c < 32 * CH; c += 64) {
-        const int hr = c / CH;
-        const int cc = c - hr * CH;
-        const int hh = h0 + hr;
-        if (hh < a.H) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(out_stage + hr * C::OUT_ROW_U16 + 8 * cc);
-          *reinterpret_cast<u32x4*>(a.out + (t * a.H + hh) * (int64_t)DV + 8 * cc) = v;
+      // Lane chunk c = lane + 64 * j: head row c / CH, 16-byte chunk c % CH.
+      constexpr int PER_LANE = 32 * CH / 64;
+      static_assert((32 * CH) % 64 == 0 && PER_LANE % 8 == 0, "store batches");
+      if (h0 + 32 <= a.H) {  // uniform: a whole head block, stores in batches of 8
+        uint16_t* orow = a.out + (t * a.H + h0) * (int64_t)DV;
+#pragma unroll
+        for (int j0 = 0; j0 < PER_LANE; j0 += 8) {
+          u32x4 v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int c = lane + 64 * (j0 + j);
+            v[j] = *reinterpret_cast<const u32x4*>(out_stage + (c / CH) * C::OUT_ROW_U16 +
+                                                   8 * (c % CH));
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int c = lane + 64 * (j0 + j);
+            *reinterpret_cast<u32x4*>(orow + (c / CH) * DV + 8 * (c % CH)) = v[j];
+          }
+        }
+      } else {
+        for (int c = lane; c < 32 * CH; c += 64) {
+          const int hr = c / CH;
+          const int cc = c - hr * CH;
+          const int hh = h0 + hr;
+          if (hh < a.H) {
+            const u32x4 v =
+                *reinterpret_cast<const u32x4*>(out_stage + hr * C::OUT_ROW_U16 + 8 * cc);
+            *reinterpret_cast<u32x4*>(a.out + (t * a.H + hh) * (int64_t)DV + 8 * cc) = v;
+          }
         }
       }
     }
