@@ -123,17 +123,21 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
   auto swz = [](int r, int g) -> int { return 4 * ((r >> 1) & 1) + (r >> 2) + 2 * (g & 1); };
 
   // Raw index of row `row` of the tile starting at slot j0 (-1 past the
-  // valid prefix). It is validated only when used, one iteration later: a
-  // compare right after the load would make the compiler wait for every
-  // outstanding vector-memory operation, the tile copies included.
+  // row's k_width slots; the valid prefix L is applied when the id is
+  // validated, so that these loads need not wait for topk_length). It is
+  // validated only when used, one iteration later: a compare right after the
+  // load would make the compiler wait for every outstanding vector-memory
+  // operation, the tile copies included.
   auto load_id = [&](int j0, int row) -> int32_t {
     const int j = j0 + row;
     int32_t raw = -1;
-    if (j < L) raw = idx_row[j];
+    if (j < a.k_width) raw = idx_row[j];
     return raw;
   };
-  auto valid_id = [&](int32_t raw) -> int32_t {
-    return (raw >= 0 && (int64_t)raw < a.T_kv) ? raw : -1;
+  // raw: the id of slot j; -1 unless j is inside the valid prefix and the id
+  // inside [0, T_kv)
+  auto valid_id = [&](int32_t raw, int j) -> int32_t {
+    return (j < L && raw >= 0 && (int64_t)raw < a.T_kv) ? raw : -1;
   };
 
   // This wave's share of the asynchronous copies of one tile: wave w copies
@@ -210,10 +214,11 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
     static_for<NCOPY>([&](auto jc) { copy_one(cs, jc); });
   };
 
-  // The first two tiles' ids are loaded before Q, so that the first copies
-  // can be issued while the Q loads are still in flight.
-  const int32_t id_first = n_tiles > 0 ? load_id(0, key_row) : -1;
-  const int32_t id_second = n_tiles > 1 ? load_id(kBN, key_row) : -1;
+  // The first two tiles' ids are loaded before Q (and together with
+  // topk_length), so that the first copies can be issued while the Q loads
+  // are still in flight.
+  const int32_t id_first = load_id(0, key_row);
+  const int32_t id_second = load_id(kBN, key_row);
 
   // Q fragments (B operand): lane -> head h0 + r32, dims 16*ks + 8*half .. +7.
   u32x4 qf[C::KS];
@@ -263,7 +268,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
     int32_t id_next = -1;
     uint32_t mask_cur = 0;
     if (n_tiles > 0) {
-      const int32_t id0 = valid_id(id_first);
+      const int32_t id0 = valid_id(id_first, key_row);
       mask_cur = (uint32_t)ballot(id0 >= 0);  // lanes 0..31 hold rows 0..31
       if (pass == 1) __syncthreads();  // pass 0's last tile is consumed by every wave
       copy_all(prep_copy(smem_base, id0));
@@ -277,7 +282,7 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
       const bool copy_next = it + 1 < n_tiles;  // uniform over the workgroup
       CopySrc cs{};
       if (copy_next) {
-        const int32_t idv = valid_id(id_next);
+        const int32_t idv = valid_id(id_next, (it + 1) * kBN + key_row);
         mask_next = (uint32_t)ballot(idv >= 0);
         cs = prep_copy(smem_base + ((it + 1) & 1) * C::STAGE_BYTES, idv);
       }
