@@ -88,6 +88,10 @@ def workload_counts(wl, seq_lens_np):
     else:
         c["valid_slots"] = float((wl.routes >= 0).sum().item())
     c["attn_flop"] = 2.0 * (wl.D_qk + wl.D_v) * wl.H * c["valid_slots"]
+    # bytes of selected KV rows the attention kernel gathers (bf16; a shared
+    # latent row serves as both key and value)
+    gathered_dims = wl.D_qk + (0 if wl.v is None else wl.D_v)
+    c["attn_gathered_bytes"] = 2.0 * gathered_dims * c["valid_slots"]
     return c
 
 
@@ -358,7 +362,11 @@ def main():
 
     stages = {"attention": {"ms": float(np.mean(att_ms)), "tflops": attn_tflops,
                             "frac_bf16_peak": attn_tflops / PEAK_BF16_TFLOPS,
-                            "algorithmic_flop": cnt["attn_flop"]}}
+                            "algorithmic_flop": cnt["attn_flop"],
+                            # gathers are served mostly by L2 and the MALL, so this
+                            # rate can exceed the HBM peak
+                            "gathered_bytes": cnt["attn_gathered_bytes"],
+                            "gather_tb_per_s": cnt["attn_gathered_bytes"] / att_s / 1e12}}
     rows_per_s = None
     if has_indexer:
         idx_s = float(np.mean(idx_ms)) / 1e3
