@@ -14,7 +14,7 @@
 // block): lane l ends up with key l % 32 and 16 of the block's heads, so the
 // ReLU * W head reduction is an in-lane max + FMA chain plus one exchange
 // between the two half-waves. Q fragments and the lane's 16 weights per head
-// block stay in registers for the whole key loop; 64-key tiles of K are
+// block stay in registers for the whole key loop; 128-key tiles of K are
 // staged in a double-buffered LDS ring (16-byte padded rows, conflict-free
 // operand reads) and shared by the 8 queries. Each wave writes its 64 scores
 // of a tile as one contiguous 256-byte run. Workgroups are issued longest row
@@ -71,7 +71,7 @@ __global__ void ratio_metadata_kernel(const int32_t* __restrict__ cu_q,
 namespace {
 
 constexpr int kIdxWaves = 8;                        // = query rows per workgroup
-constexpr int kIdxTile = 64;                        // keys per LDS tile
+constexpr int kIdxHalf = 64;                        // keys per pipelined pair of 32-key blocks
 
 // max(x, 0) for finite x as one v_med3_f32 (clamp to [0, FLT_MAX]); fmaxf
 // would first quiet a possible NaN in x with a second instruction.
@@ -116,8 +116,11 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
     FusedArgs fa) {
   constexpr int KS = D / 16;                      // MFMA k-steps over the head dim
   constexpr int ROW_B = 2 * D + 16;               // LDS row stride in bytes (16 B pad)
-  constexpr int TILE_B = kIdxTile * ROW_B;
-  constexpr int CHUNKS = kIdxTile * D / 8;        // 16-byte chunks per tile
+  // keys per LDS tile: 128 (one barrier per 128 keys); 64 when the rows'
+  // scores share the LDS
+  constexpr int TILE = FUSE ? 64 : 128;
+  constexpr int TILE_B = TILE * ROW_B;
+  constexpr int CHUNKS = TILE * D / 8;            // 16-byte chunks per tile
   constexpr int NT = kIdxWaves * 64;
   constexpr int LOADS = (CHUNKS + NT - 1) / NT;   // 16-byte loads per thread and tile
   constexpr int NBUF = (FUSE && D == 128) ? 1 : 2;  // key tiles in the LDS ring
@@ -306,24 +309,36 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
   store_tile(0);
   __syncthreads();
   int buf = 0;
-  int32_t pend_k0 = qstart - 64;  // block 1 of tile pend_k0 awaits its epilogue
+  int32_t pend_k0 = qstart - 64;  // the second block of the pair at pend_k0 awaits its epilogue
   float pend_p0 = 0.0f;           // its block-0 partial
-  for (int32_t k0 = kb; k0 < ke; k0 += kIdxTile) {
-    load_tile(k0 + kIdxTile);  // zeroed past the range, so the last one is harmless
+  for (int32_t k0 = kb; k0 < ke; k0 += TILE) {
+    load_tile(k0 + TILE);  // zeroed past the range, so the last one is harmless
     const unsigned char* kt = ktile + buf * TILE_B;
     // Each group pairs a block's MFMAs with the previous block's epilogue;
     // the fences keep the scheduler from filling the VALU slots with the
-    // epilogue that waits on these very MFMAs.
-    block_mfma(kt, 0, acc0);
-    const float p1_prev = epilogue(acc1);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    write_scores(pend_k0, pend_p0, p1_prev);
-    block_mfma(kt, 1, acc1);
-    pend_p0 = epilogue(acc0);
-    interleave();
-    __builtin_amdgcn_sched_barrier(0);
-    pend_k0 = k0;
+    // epilogue that waits on these very MFMAs. A tile is two or four blocks
+    // of 32 keys, taken in pairs; a pair wholly past the range is skipped.
+    auto pair = [&](int hp) {
+      block_mfma(kt, 2 * hp, acc0);
+      const float p1_prev = epilogue(acc1);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      write_scores(pend_k0, pend_p0, p1_prev);
+      block_mfma(kt, 2 * hp + 1, acc1);
+      pend_p0 = epilogue(acc0);
+      interleave();
+      __builtin_amdgcn_sched_barrier(0);
+      pend_k0 = k0 + kIdxHalf * hp;
+    };
+    if constexpr (TILE == kIdxHalf) {
+      pair(0);
+    } else {
+#pragma unroll
+      for (int hp = 0; hp < TILE / kIdxHalf; ++hp) {
+        if (hp > 0 && k0 + kIdxHalf * hp >= ke) break;  // uniform
+        pair(hp);
+      }
+    }
 
     if constexpr (NBUF == 2) {
       store_tile(buf ^ 1);
