@@ -478,31 +478,10 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
     return;
   }
   const int nchunks = (n + 255) / 256;
-  constexpr int BPT = kBins / NT;
 
-  // Finds the bucket holding the `want`-th largest of the histogrammed keys
-  // (want >= 1): s_sel[0] = bucket, s_sel[1] = count in the buckets above.
-  auto find_bucket = [&](uint32_t want) {
-    const int hi_bin = kBins - 1 - tid * BPT;
-    uint32_t local = 0;
-#pragma unroll
-    for (int b = 0; b < BPT; ++b) local += hist[hi_bin - b];
-    uint32_t total;
-    const uint32_t above = block_exclusive_scan<kSWaves>(local, s_wave, &total);
-    if (above < want && want <= above + local) {
-      uint32_t acc = above;
-      for (int b = 0; b < BPT; ++b) {
-        const uint32_t h = hist[hi_bin - b];
-        if (acc + h >= want) {
-          s_sel[0] = (uint32_t)(hi_bin - b);
-          s_sel[1] = acc;
-          break;
-        }
-        acc += h;
-      }
-    }
-    __syncthreads();
-  };
+  // the bucket holding the want-th largest of the histogrammed keys:
+  // s_sel[0] = bucket, s_sel[1] = count in the buckets above it
+  auto find_bucket_s = [&](uint32_t want) { find_bucket<kSWaves>(hist, want, s_wave, s_sel); };
 
   // ---- 1. sampled lower bound (rows of more than kCap columns) ----
   uint32_t lo_key = 1u;  // the smallest valid key: every column is a candidate
@@ -542,7 +521,7 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
     }
     __syncthreads();
     if (rank < S) {  // uniform
-      find_bucket((uint32_t)rank);
+      find_bucket_s((uint32_t)rank);
       // lo = the smallest sample key in the bucket: >= `rank` samples are >= lo
 #pragma unroll
       for (int i = 0; i < 16; ++i)
@@ -622,7 +601,7 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
     __syncthreads();
     for (int i = tid; i < nc; i += NT) atomicAdd(&hist[cb(s_ckey[i])], 1u);
     __syncthreads();
-    find_bucket((uint32_t)k);
+    find_bucket_s((uint32_t)k);
     const int bstar = (int)s_sel[0];
     const uint32_t rem = (uint32_t)k - s_sel[1];  // >= 1 keys to take from bucket b*
     __syncthreads();
