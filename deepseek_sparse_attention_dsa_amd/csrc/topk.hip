@@ -7,6 +7,10 @@
 // column); NeMo cudnn_dsa page (global coordinates, ascending valid prefix,
 // -1 suffix).
 //
+// One workgroup per row; workgroups take the rows in reverse order, so a
+// causal sequence's long rows (the ones that need a selection) start first
+// and the short closed-form rows fill the tail.
+//
 // Scores become order-preserving uint32 keys (-0.0 folded onto +0.0, so they
 // tie as equal values; key 0 marks columns past the row end). Output
 // positions come from one rule: a selected column goes to
@@ -232,7 +236,7 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t r = blockIdx.x;
+  const int64_t r = (int64_t)gridDim.x - 1 - blockIdx.x;  // long rows first
   const float* row = scores + r * ld;
   int32_t* out_idx = indices + r * ld_idx;
   float* out_val = values ? values + r * ld_idx : nullptr;
@@ -453,7 +457,7 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int64_t r = blockIdx.x;
+  const int64_t r = (int64_t)gridDim.x - 1 - blockIdx.x;  // long rows first
   const float* row = scores + r * ld;
   int32_t* out_idx = indices + r * ld_idx;
   float* out_val = values ? values + r * ld_idx : nullptr;
