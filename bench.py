@@ -8,15 +8,23 @@ radix top-K -> sparse attention forward. Workloads 1-5 are packed documents
 (ratio-causal mask with query causal offsets). Inputs are generated on the
 GPU before the timed region and stay resident in HBM.
 
+The default workload is 4, `long_T65536` (one sequence of 65 536 tokens,
+64 attention heads over a 576/512 latent KV, a 64 x 128 indexer, top-2048):
+the largest single-GPU configuration of the path.
+
 Prints one JSON line. `value` is the sparse-attention forward throughput in
 TFLOP/s (algorithmic FLOP: 2*(D_qk+D_v) per valid slot per head, over the
 attention kernel's time measured with HIP events inside the timed steps);
 `indexer_topk_rows_per_s` is the second half of the metric; `ms_per_step` is
-the whole path. `roofline` describes the dominant kernel; `cpu_baseline` is
-the fp64 CPU oracle timed on a bounded sample of the same workload.
-`stages_flushed` repeats the stage timings over a few extra steps that each
-start after 512 MiB were written, so that the 256 MB MALL holds none of the
-step's inputs (the main figures are warm: back-to-back steps).
+the whole path. Every launch of a timed step is bracketed by its own pair of
+HIP events on the launch stream, so each stage (indexer, top-K, attention)
+has its own kernel time and roofline in `rooflines`; `roofline` is the one of
+the stage with the most kernel time (the dominant kernel). `cpu_baseline` is
+the fp64 CPU oracle, run by a pool of single-threaded worker processes (one
+per host core available, at most 16) on a bounded seeded sample of the same
+workload. `stages_flushed` repeats the stage timings over a few extra steps
+that each start after 512 MiB were written, so that the 256 MB MALL holds
+none of the step's inputs (the main figures are warm: back-to-back steps).
 """
 
 from __future__ import annotations
@@ -26,8 +34,8 @@ import hashlib
 import json
 import math
 import os
-import platform
 import sys
+import tempfile
 import time
 
 import numpy as np
@@ -37,9 +45,20 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse-attn fwd TFLOP/s + indexer+topK rows/s at 1 MI355X; % of roofline"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
-ATTN_SRC = os.path.join(ROOT, "deepseek_sparse_attention_dsa_amd", "csrc", "sparse_attn.hip")
+CSRC = os.path.join(ROOT, "deepseek_sparse_attention_dsa_amd", "csrc")
+DEFAULT_CONFIG = 4
+
+# Kernel families of the path: the stage they belong to, the source file they
+# are built from, and the substrings that name their dispatches in rocprofv3.
+KERNELS = {
+    "attention": ("sparse_attn.hip", ("sparse_attn_kernel",)),
+    "indexer": ("indexer.hip", ("indexer_kernel<",)),
+    "indexer_fp8": ("indexer_fp8.hip", ("indexer_fp8_kernel",)),
+    "topk": ("topk.hip", ("topk_radix_kernel", "topk_stream_kernel")),
+}
 
 
 def parse():
@@ -47,7 +66,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--config", type=int, default=2, help="workload 1..10 (default: 2)")
+    p.add_argument("--config", type=int, default=DEFAULT_CONFIG,
+                   help=f"workload 1..10 (default: {DEFAULT_CONFIG})")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--backward", action="store_true",
                    help="also time dsa_sparse_attn_bwd on the forward's outputs (shared latent KV "
@@ -58,20 +78,26 @@ def parse():
     p.add_argument("--flush-steps", type=int, default=5,
                    help="extra steps, each after writing 512 MiB so that the 256 MB MALL holds "
                         "none of the step's inputs, reported as stages_flushed (0: none)")
-    p.add_argument("--cpu-seconds", type=float, default=15.0,
-                   help="approximate CPU time budget of the oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=20.0,
+                   help="approximate wall time of the oracle baseline (both legs)")
+    p.add_argument("--cpu-workers", type=int, default=0,
+                   help="oracle worker processes (0: the host cores available, at most 16)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (3 times), the "
                         "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
-    p.add_argument("--summarize-traffic", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
-                                                            "CAL_FETCH_DIR", "CAL_WRITE_DIR"),
-                   help="turn four rocprofv3 --pmc output folders (FETCH_SIZE / WRITE_SIZE of "
-                        "this bench, then of --copy-calibration) into "
-                        "profiles/traffic_attention_<workload>.json")
+    p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                   help="FETCH_DIR WRITE_DIR CAL_FETCH_DIR CAL_WRITE_DIR [SQ_DIR ...]: turn "
+                        "rocprofv3 --pmc output folders of this bench (FETCH_SIZE, WRITE_SIZE, "
+                        "then any other counter groups) and of --copy-calibration into "
+                        "profiles/counters_<workload>.json")
     p.add_argument("--calibration-mib", type=int, default=1024,
-                   help="size the --copy-calibration run used (for --summarize-traffic)")
+                   help="size the --copy-calibration run used (for --summarize-counters)")
     return p.parse_args()
 
+
+# ---------------------------------------------------------------------------
+# Algorithmic work
+# ---------------------------------------------------------------------------
 
 def workload_counts(wl, seq_lens_np):
     """Algorithmic work of one step (what the method must do)."""
@@ -81,6 +107,8 @@ def workload_counts(wl, seq_lens_np):
         sl = seq_lens_np.astype(np.int64)
         pairs = int(sl.sum())  # scored (query, key) pairs: sum of the mask lengths
         c["indexer_flop"] = 2.0 * wl.H_idx * wl.D_idx * pairs
+        # top-K reads each score row with more than K columns once, plus the
+        # row's start and length, and writes K indices and the row's length
         rd = 4.0 * float(sl[sl > K].sum()) + 8.0 * len(sl)
         wr = (4.0 * K + 4.0) * len(sl)
         c["topk_bytes"] = rd + wr
@@ -95,64 +123,113 @@ def workload_counts(wl, seq_lens_np):
     return c
 
 
-def traffic_from_profile(workload_name: str):
-    """HBM bytes per attention launch from committed rocprofv3 counters.
+# ---------------------------------------------------------------------------
+# rocprofv3 counter summaries
+# ---------------------------------------------------------------------------
 
-    Returns None unless profiles/traffic_<workload>.json exists and was taken
-    from the current attention kernel source (sha256 match).
-    """
-    path = os.path.join(PROFILES, f"traffic_attention_{workload_name}.json")
-    if not os.path.exists(path):
-        return None
-    rec = json.load(open(path))
-    sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != sha:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+def kernel_source_sha(family: str) -> str:
+    """sha256 over the family's source file and every shared header."""
+    src, _ = KERNELS[family]
+    h = hashlib.sha256()
+    for name in [src] + sorted(f for f in os.listdir(CSRC) if f.endswith(".h")):
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()
 
 
-def _counter_rows(folder: str, counter: str):
+def family_of(kernel_name: str):
+    for fam, (_, keys) in KERNELS.items():
+        if any(k in kernel_name for k in keys):
+            return fam
+    return None
+
+
+def _counter_rows(folder: str):
+    """(dispatch id, kernel name, counter, value) from rocprofv3 counter CSVs."""
     import csv
     import glob
     rows = []
     for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
         for r in csv.DictReader(open(f)):
-            if r["Counter_Name"] == counter:
-                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+            rows.append((int(r.get("Dispatch_Id", 0) or 0), r["Kernel_Name"], r["Counter_Name"],
+                         float(r["Counter_Value"])))
     if not rows:
-        raise SystemExit(f"no {counter} rows under {folder}")
+        raise SystemExit(f"no counter rows under {folder}")
     return rows
 
 
-def summarize_traffic(args):
-    """HBM bytes per attention launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch).
+def _per_family(rows):
+    """{family: {counter: [value per dispatch]}} (values summed over a dispatch's rows)."""
+    acc = {}
+    for did, kname, cname, val in rows:
+        fam = family_of(kname)
+        if fam is None:
+            continue
+        acc.setdefault(fam, {}).setdefault(cname, {}).setdefault(did, 0.0)
+        acc[fam][cname][did] += val
+    return {f: {c: list(d.values()) for c, d in cs.items()} for f, cs in acc.items()}
 
-    Each counter is scaled by the factor that maps its reading for a plain copy
-    of known size (calibration_mib MiB read and written once) onto that size.
+
+def summarize_counters(args):
+    """profiles/counters_<workload>.json from rocprofv3 --pmc runs of this bench.
+
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by the factor that
+    maps the same counter's reading for a plain copy of known size
+    (calibration_mib MiB read and written once) onto that size. Other counters
+    are reported as their mean per dispatch.
     """
     from workloads import CONFIGS
-    fetch_dir, write_dir, cal_fetch_dir, cal_write_dir = args.summarize_traffic
+    dirs = args.summarize_counters
+    if len(dirs) < 4:
+        raise SystemExit("--summarize-counters FETCH_DIR WRITE_DIR CAL_FETCH_DIR CAL_WRITE_DIR "
+                         "[SQ_DIR ...]")
+    fetch_dir, write_dir, cal_fetch_dir, cal_write_dir = dirs[:4]
     known = args.calibration_mib * 2.0 ** 20
-    res = {"workload": CONFIGS[args.config]["name"],
-           "kernel_source_sha256": hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest(),
-           "calibration_copy_bytes": known}
-    for name, folder, cal in (("fetch", fetch_dir, cal_fetch_dir), ("write", write_dir, cal_write_dir)):
+    res = {"workload": CONFIGS[args.config]["name"], "calibration_copy_bytes": known,
+           "kernels": {}}
+    for name, folder, cal in (("fetch", fetch_dir, cal_fetch_dir),
+                              ("write", write_dir, cal_write_dir)):
         counter = "FETCH_SIZE" if name == "fetch" else "WRITE_SIZE"
-        attn = [v for k, v in _counter_rows(folder, counter) if "sparse_attn_kernel" in k]
-        copies = [v for k, v in _counter_rows(cal, counter)]
-        cal_kib = max(copies)  # the calibration copy is by far the largest dispatch
+        cal_kib = max(v for _, _, c, v in _counter_rows(cal) if c == counter)
         factor = known / (cal_kib * 1024.0)
-        res[f"{name}_kib_per_launch"] = float(np.mean(attn))
-        res[f"{name}_launches"] = len(attn)
         res[f"calibration_{name}_kib"] = cal_kib
         res[f"{name}_scale"] = factor
-        res[f"{name}_bytes_per_launch"] = float(np.mean(attn)) * 1024.0 * factor
-    res["hbm_bytes_per_launch"] = res["fetch_bytes_per_launch"] + res["write_bytes_per_launch"]
-    path = os.path.join(PROFILES, f"traffic_attention_{res['workload']}.json")
+        for fam, cs in _per_family(_counter_rows(folder)).items():
+            vals = cs.get(counter, [])
+            if not vals:
+                continue
+            k = res["kernels"].setdefault(fam, {"kernel_source_sha256": kernel_source_sha(fam)})
+            k[f"{name}_kib_per_launch"] = float(np.mean(vals))
+            k[f"{name}_launches"] = len(vals)
+            k[f"{name}_bytes_per_launch"] = float(np.mean(vals)) * 1024.0 * factor
+    for folder in dirs[4:]:
+        for fam, cs in _per_family(_counter_rows(folder)).items():
+            k = res["kernels"].setdefault(fam, {"kernel_source_sha256": kernel_source_sha(fam)})
+            for cname, vals in cs.items():
+                k[cname] = float(np.mean(vals))
+                k.setdefault("launches", len(vals))
+    for fam, k in res["kernels"].items():
+        if "fetch_bytes_per_launch" in k and "write_bytes_per_launch" in k:
+            k["hbm_bytes_per_launch"] = k["fetch_bytes_per_launch"] + k["write_bytes_per_launch"]
+    path = os.path.join(PROFILES, f"counters_{res['workload']}.json")
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
         f.write("\n")
     print(json.dumps(res), flush=True)
+
+
+def traffic_from_profile(workload_name: str, family: str):
+    """HBM bytes per launch of a kernel family from committed rocprofv3 counters.
+
+    None unless profiles/counters_<workload>.json holds the family and was
+    taken from the current source of its kernels (sha256 match).
+    """
+    path = os.path.join(PROFILES, f"counters_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    k = json.load(open(path)).get("kernels", {}).get(family)
+    if not k or k.get("kernel_source_sha256") != kernel_source_sha(family):
+        return None
+    return k.get("hbm_bytes_per_launch")
 
 
 def copy_calibration(mib: int):
@@ -166,77 +243,189 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_bytes": n * 4, "repeats": 3}), flush=True)
 
 
-def cpu_baseline(wl, rs, sl, budget_s):
-    """Time the fp64 oracle on a bounded, seeded sample of the workload's rows."""
-    from threadpoolctl import threadpool_info
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a pool of single-threaded processes
+# ---------------------------------------------------------------------------
 
+_W = {}  # per-worker arrays (loaded once by the pool initializer)
+
+
+def _worker_init(folder: str):
     from oracle import dsa_oracle as O
+    _W["O"] = O
+    for f in os.listdir(folder):
+        if f.endswith(".npy"):
+            a = np.load(os.path.join(folder, f), mmap_mode="r")
+            _W[f[:-4]] = a
+    meta = json.load(open(os.path.join(folder, "meta.json")))
+    _W["meta"] = meta
+    if "kv_bits" in _W:
+        _W["kv"] = O.bf16_bits_to_f64(_W["kv_bits"])
+        _W["v"] = O.bf16_bits_to_f64(_W["v_bits"]) if "v_bits" in _W else None
+    if "k_idx_bits" in _W:
+        _W["k_idx"] = O.bf16_bits_to_f64(_W["k_idx_bits"])
+
+
+def _worker_attention(rows):
+    """Oracle attention on sample rows `rows` (indices into the saved sample)."""
+    O, m = _W["O"], _W["meta"]
+    q = O.bf16_bits_to_f64(np.asarray(_W["q_bits"][rows]))
+    idx = np.asarray(_W["att_idx"][rows]).astype(np.int64)
+    tl = np.asarray(_W["att_tl"][rows]) if "att_tl" in _W else None
+    sink = np.asarray(_W["sink"]) if "sink" in _W else None
+    O.sparse_attention(q, _W["kv"], _W["v"], idx, tl, sink, m["scale"], d_v=m["d_v"])
+    valid = (idx >= 0) if tl is None else (np.arange(idx.shape[1])[None, :] < tl[:, None])
+    return 2.0 * (m["d_qk"] + m["d_v"]) * m["H"] * float(valid.sum())
+
+
+def _worker_indexer_topk(rows):
+    """Oracle indexer scores + top-K on sample rows `rows`."""
+    O, m = _W["O"], _W["meta"]
+    q = O.bf16_bits_to_f64(np.asarray(_W["qi_bits"][rows]))
+    w = O.bf16_bits_to_f64(np.asarray(_W["w_bits"][rows]))
+    st = np.asarray(_W["idx_rs"][rows]).astype(np.int64)
+    ln = np.asarray(_W["idx_sl"][rows]).astype(np.int64)
+    sc = O.indexer_scores(q, _W["k_idx"], w, st, ln, np.arange(len(rows)))
+    O.topk(sc, ln, m["topk"], row_starts=st)
+    return len(rows)
+
+
+def _worker_ready(_):
+    time.sleep(0.3)  # long enough that each worker takes one of the warm-up tasks
+    return os.getpid()
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def _timed_map(pool, fn, chunks):
+    t0 = time.perf_counter()
+    res = list(pool.map(fn, chunks))
+    return time.perf_counter() - t0, res
+
+
+def cpu_baseline(wl, rs, sl, indices, topk_length, budget_s, workers):
+    """Time the fp64 oracle on a bounded, seeded sample of the workload's rows.
+
+    Rows are drawn at random (seed 1234) from the whole workload; each leg
+    first runs one row per worker to measure the per-row cost, then a sample
+    sized to about budget_s / 2 of wall time, spread over the workers in
+    chunks of rows. The rate is sample work over the wall time of that map.
+    """
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
     from workloads import bf16_to_numpy_bits
 
     import torch
 
-    f64 = lambda t: O.bf16_bits_to_f64(bf16_to_numpy_bits(t))  # noqa: E731
-    threads = max([d.get("num_threads", 1) for d in threadpool_info()] or [1])
-    rng = np.random.default_rng(1234)
+    P = workers or min(16, len(os.sched_getaffinity(0)))
     T = wl.T
-    rs_np, sl_np = rs.cpu().numpy(), sl.cpu().numpy()
-    res = {"kind": "oracle", "cores": int(threads), "cpu": platform.processor() or platform.machine()}
-    # attention: the oracle on sampled rows with the GPU path's own indices
-    kv = f64(wl.kv)
-    v = None if wl.v is None else f64(wl.v)
-    sink = None if wl.sink is None else wl.sink.cpu().numpy().astype(np.float64)
-    idx_all, tl_all = wl.extra["indices"], wl.extra["topk_length"]
-    n_att, t_att, flop_att = 0, 0.0, 0.0
-    rows_order = rng.permutation(T)
-    while t_att < budget_s * 0.5 and n_att < T:
-        rows = rows_order[n_att:n_att + 8]
-        sel = torch.as_tensor(rows, device=wl.q.device)
-        q = f64(wl.q[sel])
-        idx = idx_all[sel].cpu().numpy().astype(np.int64)
-        tl = None if tl_all is None else tl_all[sel].cpu().numpy()
-        t0 = time.perf_counter()
-        O.sparse_attention(q, kv, v, idx, tl, sink, wl.scale, d_v=wl.D_v)
-        t_att += time.perf_counter() - t0
-        valid = (idx >= 0) if tl is None else (np.arange(idx.shape[1])[None, :] < tl[:, None])
-        flop_att += 2.0 * (wl.D_qk + wl.D_v) * wl.H * float(valid.sum())
-        n_att += len(rows)
-    res["value"] = flop_att / t_att / 1e12
-    res["unit"] = "TFLOP/s"
-    sample = f"attention on {n_att} random rows ({t_att:.1f} s)"
-    # indexer + top-K on sampled rows
-    if wl.q_idx is not None:
-        fp8 = wl.extra.get("fp8")
-        if fp8:
-            i64 = lambda t: t.cpu().numpy().astype(np.int64)  # noqa: E731
-            mx = fp8["scaling"] == "mx"
-            k8 = i64(fp8["k8"])
-            ks = i64(fp8["k_scale"]) if mx else fp8["k_scale"].cpu().numpy().astype(np.float64)
-        else:
-            k_idx = f64(wl.k_idx)
-        n_idx, t_idx = 0, 0.0
-        while t_idx < budget_s * 0.5 and n_idx < T:
-            rows = rows_order[n_idx:n_idx + 16]
-            sel = torch.as_tensor(rows, device=wl.q_idx.device)
-            w = f64(wl.w[sel])
-            st, ln = rs_np[rows].astype(np.int64), sl_np[rows].astype(np.int64)
-            if fp8:
-                q8 = i64(fp8["q8"][sel])
-                qs = (i64(fp8["q_scale"][sel]) if mx
-                      else fp8["q_scale"][sel].cpu().numpy().astype(np.float64))
-                fn = O.indexer_scores_mxfp8 if mx else O.indexer_scores_fp8
-                t0 = time.perf_counter()
-                sc = fn(q8, qs, k8, ks, w, st, ln, np.arange(len(rows)))
+    rng = np.random.default_rng(1234)
+    order = rng.permutation(T)
+    n_take = min(T, 4096)
+    take = np.sort(order[:n_take])
+    sel = torch.as_tensor(take, device=wl.q.device)
+    folder = tempfile.mkdtemp(prefix="dsa_oracle_", dir="/tmp")
+    meta = {"scale": float(wl.scale), "d_v": int(wl.D_v), "d_qk": int(wl.D_qk), "H": int(wl.H),
+            "topk": int(wl.topk)}
+    json.dump(meta, open(os.path.join(folder, "meta.json"), "w"))
+    save = lambda n, a: np.save(os.path.join(folder, n + ".npy"), a)  # noqa: E731
+    save("q_bits", bf16_to_numpy_bits(wl.q[sel]))
+    save("kv_bits", bf16_to_numpy_bits(wl.kv))
+    if wl.v is not None:
+        save("v_bits", bf16_to_numpy_bits(wl.v))
+    save("att_idx", indices[sel].cpu().numpy())
+    if topk_length is not None:
+        save("att_tl", topk_length[sel].cpu().numpy())
+    if wl.sink is not None:
+        save("sink", wl.sink.cpu().numpy().astype(np.float64))
+    has_idx = wl.q_idx is not None
+    if has_idx:
+        save("qi_bits", bf16_to_numpy_bits(wl.q_idx[sel]))
+        save("k_idx_bits", bf16_to_numpy_bits(wl.k_idx))
+        save("w_bits", bf16_to_numpy_bits(wl.w[sel]))
+        save("idx_rs", rs[sel].cpu().numpy())
+        save("idx_sl", sl[sel].cpu().numpy())
+    # shuffled positions into the saved sample, so every chunk is a random draw
+    pos = rng.permutation(n_take)
+
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                           "MKL_NUM_THREADS")}
+    for k in saved:
+        os.environ[k] = "1"
+    res = {"kind": "oracle", "cores": P, "cpu": _cpu_model(),
+           "threads_per_worker": 1, "host_cores_visible": len(os.sched_getaffinity(0))}
+    try:
+        # spawned workers (a fresh interpreter each: nothing of this process's GPU
+        # state is inherited); a worker that dies raises instead of hanging
+        with ProcessPoolExecutor(P, mp_context=mp.get_context("spawn"), initializer=_worker_init,
+                                 initargs=(folder,)) as pool:
+            # start and initialise every worker before anything is timed
+            pids = set()
+            for _ in range(4):
+                pids |= set(pool.map(_worker_ready, range(P)))
+                if len(pids) >= P:
+                    break
+
+            def leg(fn, start):
+                # calibration: one row per worker
+                cal = [pos[(start + i) % n_take: (start + i) % n_take + 1] for i in range(P)]
+                t_cal, _ = _timed_map(pool, fn, cal)
+                per_row = max(t_cal, 1e-3)  # one row per worker, in parallel
+                n_rows = int(min(n_take, max(P, P * (budget_s / 2.0) / per_row)))
+                chunk = max(1, n_rows // (4 * P))
+                rows = [pos[(start + i) % n_take] for i in range(n_rows)]
+                chunks = [np.sort(np.array(rows[i:i + chunk])) for i in range(0, n_rows, chunk)]
+                t, out = _timed_map(pool, fn, chunks)
+                return n_rows, t, out
+
+            n_att, t_att, flops = leg(_worker_attention, 0)
+            res["value"] = float(sum(flops)) / t_att / 1e12
+            res["unit"] = "TFLOP/s"
+            sample = (f"subset: attention on {n_att} random rows of {T} ({t_att:.1f} s wall on "
+                      f"{P} processes)")
+            if has_idx:
+                n_idx, t_idx, _ = leg(_worker_indexer_topk, n_take // 2)
+                res["indexer_topk_rows_per_s"] = n_idx / t_idx
+                sample += (f"; indexer+top-K on {n_idx} random rows of {T} ({t_idx:.1f} s wall "
+                           f"on {P} processes)")
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
             else:
-                q = f64(wl.q_idx[sel])
-                t0 = time.perf_counter()
-                sc = O.indexer_scores(q, k_idx, w, st, ln, np.arange(len(rows)))
-            O.topk(sc, ln, wl.topk, row_starts=st)
-            t_idx += time.perf_counter() - t0
-            n_idx += len(rows)
-        res["indexer_topk_rows_per_s"] = n_idx / t_idx
-        sample += f"; indexer+top-K on {n_idx} random rows ({t_idx:.1f} s)"
+                os.environ[k] = v
+        for f in os.listdir(folder):
+            os.remove(os.path.join(folder, f))
+        os.rmdir(folder)
     res["sample"] = sample
     return res
+
+
+# ---------------------------------------------------------------------------
+# The timed path
+# ---------------------------------------------------------------------------
+
+def roofline_entry(kernel, bound, algorithmic_total, launches, kernel_ms_total, peak, unit,
+                   traffic):
+    """Roofline of one kernel family over one step: achieved = algorithmic work per
+    launch / average launch duration (= step total / step kernel time)."""
+    per_launch = algorithmic_total / max(launches, 1)
+    avg_ms = kernel_ms_total / max(launches, 1)
+    scale = 1e12 if unit == "TFLOP/s" else 1e9
+    achieved = per_launch / (avg_ms / 1e3) / scale
+    return {"kernel": kernel, "bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "algorithmic_per_launch": per_launch,
+            "launches_per_step": launches, "avg_launch_ms": avg_ms, "traffic": traffic}
 
 
 def main():
@@ -246,8 +435,8 @@ def main():
               "(no collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    if args.summarize_traffic:
-        summarize_traffic(args)
+    if args.summarize_counters:
+        summarize_counters(args)
         return
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
@@ -263,6 +452,7 @@ def main():
     torch.cuda.set_device(0)
     dsa.load_library()
     wl = make_config(args.config, device=dev)
+    wname = CONFIGS[args.config]["name"]
     split = bool(CONFIGS[args.config].get("split"))
     fp8 = wl.extra.get("fp8") if hasattr(wl, "extra") else None
     T, K = wl.T, wl.topk
@@ -293,48 +483,56 @@ def main():
     lse = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
     max_logits = torch.empty((T, wl.H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    idx_family = "indexer_fp8" if fp8 else "indexer"
 
-    ev = {}
+    # (stage, start event, end event) per launch, per timed step
+    records = {}
 
     def step(timed: bool, key: str = "steps"):
-        e0 = torch.cuda.Event(enable_timing=True) if timed else None
-        e1 = torch.cuda.Event(enable_timing=True) if timed else None
-        e2 = torch.cuda.Event(enable_timing=True) if timed else None
-        if timed:
-            e0.record(stream)
-        metadata(rs, sl)
+        evs = []
+
+        def run(stage, fn):
+            if timed:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                evs.append((stage, a, b))
+            else:
+                fn()
+
+        run("metadata", lambda: metadata(rs, sl))
         if has_indexer and fused:
             if fp8:
-                dsa.dsa_indexer_topk_fused(fp8["q8"], fp8["k8"], wl.w, rs, sl, K, max_len,
-                                           q_scale=fp8["q_scale"], k_scale=fp8["k_scale"],
-                                           fp8_scaling=fp8_scaling, indices=indices,
-                                           topk_length=topk_length)
+                run("indexer_topk_fused", lambda: dsa.dsa_indexer_topk_fused(
+                    fp8["q8"], fp8["k8"], wl.w, rs, sl, K, max_len, q_scale=fp8["q_scale"],
+                    k_scale=fp8["k_scale"], fp8_scaling=fp8_scaling, indices=indices,
+                    topk_length=topk_length))
             else:
-                dsa.dsa_indexer_topk_fused(wl.q_idx, wl.k_idx, wl.w, rs, sl, K, max_len,
-                                           indices=indices, topk_length=topk_length)
+                run("indexer_topk_fused", lambda: dsa.dsa_indexer_topk_fused(
+                    wl.q_idx, wl.k_idx, wl.w, rs, sl, K, max_len, indices=indices,
+                    topk_length=topk_length))
         elif has_indexer:
             for r0 in range(0, T, rows_per_chunk):
                 n = min(rows_per_chunk, T - r0)
                 if fp8:
-                    dsa.dsa_indexer_fwd_fp8(fp8["q8"], fp8["q_scale"], fp8["k8"], fp8["k_scale"],
-                                            wl.w, rs, sl, scaling=fp8_scaling, row_begin=r0,
-                                            n_rows=n, scores=scores)
+                    run("indexer", lambda: dsa.dsa_indexer_fwd_fp8(
+                        fp8["q8"], fp8["q_scale"], fp8["k8"], fp8["k_scale"], wl.w, rs, sl,
+                        scaling=fp8_scaling, row_begin=r0, n_rows=n, scores=scores))
                 else:
-                    dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, wl.w, rs, sl, row_begin=r0,
-                                        n_rows=n, scores=scores)
+                    run("indexer", lambda: dsa.dsa_indexer_fwd(
+                        wl.q_idx, wl.k_idx, wl.w, rs, sl, row_begin=r0, n_rows=n, scores=scores))
                 # plain causal rows never see more than r0 + n keys
                 n_cols = max_len if split else min(max_len, r0 + n)
-                dsa.dsa_topk(scores[:n], sl[r0:r0 + n], K, row_starts=rs[r0:r0 + n],
-                             n_cols=n_cols, indices=indices[r0:r0 + n],
-                             topk_length=topk_length[r0:r0 + n])
+                run("topk", lambda: dsa.dsa_topk(
+                    scores[:n], sl[r0:r0 + n], K, row_starts=rs[r0:r0 + n], n_cols=n_cols,
+                    indices=indices[r0:r0 + n], topk_length=topk_length[r0:r0 + n]))
+        run("attention", lambda: dsa.dsa_sparse_attn_fwd(
+            wl.q, wl.kv, indices, topk_length=topk_length, attn_sink=wl.sink,
+            softmax_scale=wl.scale, v=wl.v, out=out, lse=lse, max_logits=max_logits))
         if timed:
-            e1.record(stream)
-        dsa.dsa_sparse_attn_fwd(wl.q, wl.kv, indices, topk_length=topk_length,
-                                attn_sink=wl.sink, softmax_scale=wl.scale, v=wl.v, out=out,
-                                lse=lse, max_logits=max_logits)
-        if timed:
-            e2.record(stream)
-            ev.setdefault(key, []).append((e0, e1, e2))
+            records.setdefault(key, []).append(evs)
 
     for _ in range(args.warmup):
         step(False)
@@ -352,48 +550,89 @@ def main():
         torch.cuda.synchronize()
         del flush
 
-    idx_ms = [a.elapsed_time(b) for a, b, _ in ev["steps"]]
-    att_ms = [b.elapsed_time(c) for _, b, c in ev["steps"]]
+    def stage_times(key):
+        """Mean per step of {stage: (kernel ms, launches)} and of the indexer-side span."""
+        per = {}
+        span = []
+        for evs in records[key]:
+            tot = {}
+            for stage, a, b in evs:
+                ms, n = tot.get(stage, (0.0, 0))
+                tot[stage] = (ms + a.elapsed_time(b), n + 1)
+            for stage, v in tot.items():
+                per.setdefault(stage, []).append(v)
+            # metadata + indexer + top-K, from the first launch to the last before attention
+            idx_evs = [(a, b) for s, a, b in evs if s != "attention"]
+            span.append(idx_evs[0][0].elapsed_time(idx_evs[-1][1]))
+        mean = {s: (float(np.mean([v[0] for v in vs])), vs[0][1]) for s, vs in per.items()}
+        return mean, float(np.mean(span))
+
+    st, idx_span_ms = stage_times("steps")
     sl_np = sl.cpu().numpy()
     cnt = workload_counts(wl, sl_np)
-    att_s = float(np.mean(att_ms)) / 1e3
+    att_ms = st["attention"][0]
+    att_s = att_ms / 1e3
     attn_tflops = cnt["attn_flop"] / att_s / 1e12
     ms_per_step = wall / args.steps * 1e3
 
-    stages = {"attention": {"ms": float(np.mean(att_ms)), "tflops": attn_tflops,
+    stages = {"attention": {"ms": att_ms, "tflops": attn_tflops,
                             "frac_bf16_peak": attn_tflops / PEAK_BF16_TFLOPS,
                             "algorithmic_flop": cnt["attn_flop"],
                             # gathers are served mostly by L2 and the MALL, so this
                             # rate can exceed the HBM peak
                             "gathered_bytes": cnt["attn_gathered_bytes"],
                             "gather_tb_per_s": cnt["attn_gathered_bytes"] / att_s / 1e12}}
+    rooflines = {"attention": roofline_entry(
+        "sparse_attn_kernel", "mfma", cnt["attn_flop"], 1, att_ms, PEAK_BF16_TFLOPS, "TFLOP/s",
+        traffic_from_profile(wname, "attention"))}
     rows_per_s = None
     if has_indexer:
-        idx_s = float(np.mean(idx_ms)) / 1e3
-        rows_per_s = T / idx_s
-        stages["metadata+indexer+topk"] = {"ms": float(np.mean(idx_ms)), "rows_per_s": rows_per_s,
-                                           "indexer_algorithmic_flop": cnt["indexer_flop"],
-                                           "topk_algorithmic_bytes": cnt["topk_bytes"],
-                                           "chunks": 0 if fused else math.ceil(T / rows_per_chunk),
-                                           "combined_launch": fused}
+        rows_per_s = T / (idx_span_ms / 1e3)
+        stages["metadata+indexer+topk"] = {
+            "ms": idx_span_ms, "rows_per_s": rows_per_s,
+            "metadata_ms": st["metadata"][0],
+            "indexer_algorithmic_flop": cnt["indexer_flop"],
+            "topk_algorithmic_bytes": cnt["topk_bytes"],
+            "chunks": 0 if fused else math.ceil(T / rows_per_chunk), "combined_launch": fused}
+        idx_peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
+        if fused:
+            ms, n = st["indexer_topk_fused"]
+            stages["indexer_topk_fused"] = {"ms": ms, "launches": n}
+            rooflines["indexer_topk_fused"] = roofline_entry(
+                "indexer_kernel (combined with top-K)", "mfma", cnt["indexer_flop"], n, ms,
+                idx_peak, "TFLOP/s", None)
+        else:
+            ims, n_i = st["indexer"]
+            tms, n_t = st["topk"]
+            stages["indexer"] = {"ms": ims, "launches": n_i,
+                                 "tflops": cnt["indexer_flop"] / (ims / 1e3) / 1e12}
+            stages["topk"] = {"ms": tms, "launches": n_t,
+                              "gb_per_s": cnt["topk_bytes"] / (tms / 1e3) / 1e9}
+            rooflines["indexer"] = roofline_entry(
+                "indexer_fp8_kernel" if fp8 else "indexer_kernel", "mfma", cnt["indexer_flop"],
+                n_i, ims, idx_peak, "TFLOP/s", traffic_from_profile(wname, idx_family))
+            rooflines["topk"] = roofline_entry(
+                "topk_radix_kernel + topk_stream_kernel", "hbm", cnt["topk_bytes"], n_t, tms,
+                PEAK_HBM_GBS, "GB/s", traffic_from_profile(wname, "topk"))
 
     stages_flushed = None
-    if "flushed" in ev:
-        f_att = float(np.mean([b.elapsed_time(c) for _, b, c in ev["flushed"]]))
-        stages_flushed = {"steps": len(ev["flushed"]), "attention": {
+    if "flushed" in records:
+        fst, f_span = stage_times("flushed")
+        f_att = fst["attention"][0]
+        stages_flushed = {"steps": len(records["flushed"]), "attention": {
             "ms": f_att, "tflops": cnt["attn_flop"] / f_att / 1e9}}
         if has_indexer:
-            f_idx = float(np.mean([a.elapsed_time(b) for a, b, _ in ev["flushed"]]))
-            stages_flushed["metadata+indexer+topk"] = {"ms": f_idx, "rows_per_s": T / f_idx * 1e3}
+            stages_flushed["metadata+indexer+topk"] = {"ms": f_span,
+                                                       "rows_per_s": T / f_span * 1e3}
+            if "indexer" in fst:
+                stages_flushed["indexer"] = {"ms": fst["indexer"][0]}
+                stages_flushed["topk"] = {"ms": fst["topk"][0]}
 
-    roofline = {"kernel": "sparse_attn_kernel", "bound": "mfma", "achieved": attn_tflops,
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": attn_tflops / PEAK_BF16_TFLOPS,
-                "algorithmic_per_launch": cnt["attn_flop"],
-                "avg_launch_ms": float(np.mean(att_ms)), "traffic": None}
-    tb = traffic_from_profile(CONFIGS[args.config]["name"])
-    if tb is not None:
-        roofline["traffic"] = tb
+    # the dominant kernel: the stage with the most kernel time per step
+    dominant = max(rooflines, key=lambda s: rooflines[s]["avg_launch_ms"] *
+                   rooflines[s]["launches_per_step"])
+    roofline = dict(rooflines[dominant])
+    roofline["stage"] = dominant
 
     if args.backward and wl.D_v == 512 and wl.v is None:
         g = torch.Generator(device=dev).manual_seed(77)
@@ -435,13 +674,14 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": CONFIGS[args.config]["name"], "T": T, "heads": wl.H,
+        "config": {"workload": wname, "T": T, "heads": wl.H,
                    "D_qk": wl.D_qk, "D_v": wl.D_v, "topk": K, "indexer_heads": wl.H_idx,
                    "indexer_dim": wl.D_idx, "parallelism": "none"},
         "indexer_topk_rows_per_s": rows_per_s,
         "stages": stages,
         "stages_flushed": stages_flushed,
         "roofline": roofline,
+        "rooflines": rooflines,
         "cpu_baseline": None,
     }
     rec["config"]["indexer_inputs"] = (
@@ -453,9 +693,8 @@ def main():
     else:
         rec["config"]["docs"] = len(wl.doc_lens)
     if not args.no_cpu_baseline:
-        wl.extra["indices"] = indices
-        wl.extra["topk_length"] = topk_length
-        rec["cpu_baseline"] = cpu_baseline(wl, rs, sl, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(wl, rs, sl, indices, topk_length, args.cpu_seconds,
+                                           args.cpu_workers)
     print(json.dumps(rec), flush=True)
 
 

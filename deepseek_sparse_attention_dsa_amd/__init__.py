@@ -25,6 +25,7 @@ __all__ = [
     "load_library", "library_path", "dsa_abi_version", "dsa_last_error",
     "dsa_packed_metadata", "dsa_ratio_causal_metadata", "dsa_indexer_fwd",
     "dsa_indexer_fwd_fp8", "DSA_FP8_PER_TOKEN", "DSA_MXFP8", "dsa_topk",
+    "dsa_topk_workspace_bytes",
     "dsa_indexer_topk_fused", "DSA_FUSED_MAX_COLS",
     "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_workspace_bytes",
     "indexer_topk", "chunk_rows",
@@ -60,6 +61,7 @@ _SIGNATURES = {
                                 _I64, _I64, _I64, _I32, _P, _I64, _P, _P, _P, _P, _P],
                                ctypes.c_int),
     "dsa_topk": ([_P, _I64, _I64, _I64, _P, _P, _I32, _P, _I64, _P, _P, _P], ctypes.c_int),
+    "dsa_topk_workspace_bytes": ([_I64, _I64, _I32], ctypes.c_int64),
     "dsa_sparse_attn_bwd_workspace_bytes": ([_I64, _I32, _I64, _I32, _I32], ctypes.c_int64),
     "dsa_sparse_attn_bwd": ([_P, _I64, _I32, _I32, _P, _I64, _I64, _I32, _P, _I64, _I32, _P, _P,
                              _F32, _P, _P, _P, _P, _P, _P, _P, _I64, _P], ctypes.c_int),
@@ -329,6 +331,14 @@ def dsa_topk(scores: torch.Tensor, seq_lens: torch.Tensor, k: int,
                         _ptr(row_starts), k, _ptr(indices), indices.stride(0), _ptr(topk_length),
                         _ptr(values), _stream(stream)))
     return indices, topk_length, values
+
+
+def dsa_topk_workspace_bytes(n_rows: int, n_cols: int, k: int) -> int:
+    """Device workspace dsa_topk needs (0: it keeps each row on chip)."""
+    n = int(load_library().dsa_topk_workspace_bytes(n_rows, n_cols, k))
+    if n < 0:
+        raise ValueError("sizes out of contract for dsa_topk")
+    return n
 
 
 def dsa_sparse_attn_fwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,

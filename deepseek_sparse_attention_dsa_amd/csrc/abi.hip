@@ -213,6 +213,14 @@ int dsa_indexer_topk_fused(const void* q_idx, const void* q_scale, const void* k
                                                (hipStream_t)stream));
 }
 
+int64_t dsa_topk_workspace_bytes(int64_t n_rows, int64_t n_cols, int32_t k) {
+  // Every row's working set stays in registers and LDS: no device workspace.
+  if (n_rows < 0 || n_rows > INT32_MAX || n_cols < 1 || n_cols > DSA_TOPK_MAX_COLS || k < 1 ||
+      k > DSA_MAX_TOPK)
+    return -1;
+  return 0;
+}
+
 int dsa_topk(const float* scores, int64_t ld_scores, int64_t n_rows, int64_t n_cols,
              const int32_t* seq_lens, const int32_t* row_starts, int32_t k, int32_t* indices,
              int64_t ld_indices, int32_t* topk_length, float* values, void* stream) {

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const WT* __restrict__ w,
     const int32_t* __restrict__ row_starts, const int32_t* __restrict__ seq_lens, int64_t T_kv,
     int H, int64_t row_begin, int64_t n_rows, float* __restrict__ scores, int64_t ld,
-    FusedArgs fa) {
+    FusedArgs fa, bool w_vec) {
   constexpr int KS = D / 16;                      // MFMA k-steps over the head dim
   constexpr int ROW_B = 2 * D + 16;               // LDS row stride in bytes (16 B pad)
   // keys per LDS tile: 128 (one barrier per 128 keys); 64 when the rows'
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
     const int hq = head < H ? head : H - 1;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qa[mb][ks] = load16(q + ((t * H + hq) * D + ks * 16 + 8 * half));
-    if (H % 4 == 0) {  // uniform: runs of 4 heads are whole and aligned
+    if (w_vec) {  // uniform: runs of 4 heads are whole, w aligned to 4 weights
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int oh0 = mb * 32 + 8 * j + 4 * half;
@@ -366,14 +366,19 @@ hipError_t launch_indexer_w(const void* q, const void* k, const void* w, int w_d
                             const FusedArgs& fa, hipStream_t st) {
   const int64_t nblk = (n_rows + kIdxWaves - 1) / kIdxWaves;
   dim3 grid((unsigned)nblk), block(kIdxWaves * 64);
+  // Four weights per load when every run of four heads starts at a multiple
+  // of four weights from an address aligned to four weights; otherwise one
+  // weight per load (w only needs its element alignment).
+  const size_t wbytes = w_dtype == 0 ? 2 : 4;
+  const bool w_vec = H % 4 == 0 && (uintptr_t)w % (4 * wbytes) == 0;
   if (w_dtype == 0)
     hipLaunchKernelGGL((indexer_kernel<D, MB, uint16_t, FUSE>), grid, block, 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)w, rs, sl, T_kv, H,
-                       row_begin, n_rows, scores, ld, fa);
+                       row_begin, n_rows, scores, ld, fa, w_vec);
   else
     hipLaunchKernelGGL((indexer_kernel<D, MB, float, FUSE>), grid, block, 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const float*)w, rs, sl, T_kv, H,
-                       row_begin, n_rows, scores, ld, fa);
+                       row_begin, n_rows, scores, ld, fa, w_vec);
   return hipGetLastError();
 }
 

@@ -9,6 +9,7 @@
  *   dsa_indexer_fwd_fp8  the same scores from FP8 (E4M3) Q and K with
  *                        per-token descales or per-32 E8M0 block scales
  *   dsa_topk             per-row top-K select, ascending global indices, -1 pad
+ *                        (dsa_topk_workspace_bytes: its workspace query, 0)
  *   dsa_indexer_topk_fused  indexer scores + top-K (+ logits, softmax, LSE)
  *                        in one launch, the scores kept on chip
  *   dsa_sparse_attn_fwd  sparse MQA/GQA attention over the selected KV rows
@@ -68,7 +69,7 @@ typedef enum {
 const char* dsa_last_error(void);
 
 /* ABI version of this header (bumped on any signature change). */
-#define DSA_ABI_VERSION 5
+#define DSA_ABI_VERSION 6
 int dsa_abi_version(void);
 
 /* Limits enforced by the host checks. */
@@ -142,7 +143,8 @@ int dsa_ratio_causal_metadata(const int32_t* cu_seqlens_q, const int32_t* cu_seq
  * factors (cudnn_dsa page, cudnn_indexer_topk, head_weights).
  *   q_idx       device bf16 [T, H_idx, D_idx], contiguous
  *   k_idx       device bf16 [T_kv, D_idx], contiguous
- *   w           device [T, H_idx], dtype w_dtype (DSA_BF16 or DSA_F32)
+ *   w           device [T, H_idx], dtype w_dtype (DSA_BF16 or DSA_F32),
+ *               aligned to its element size (any storage offset works)
  *   row_starts, seq_lens  device int32 [T] (from either metadata call)
  *   T, H_idx, D_idx       H_idx in [1, 64], D_idx in {64, 128}
  *   T_kv        rows of k_idx; key rows outside [0, T_kv) are never read
@@ -223,6 +225,16 @@ int dsa_topk(const float* scores, int64_t ld_scores, int64_t n_rows, int64_t n_c
              const int32_t* seq_lens, const int32_t* row_starts, int32_t k,
              int32_t* indices, int64_t ld_indices, int32_t* topk_length, float* values,
              void* stream);
+
+/*
+ * dsa_topk_workspace_bytes - device workspace dsa_topk needs for these sizes.
+ * The DSA page (section 4) has callers own every buffer, sizing them with a
+ * query before the call. dsa_topk keeps each row's working set on chip
+ * (registers and LDS) and takes no workspace argument, so this returns 0 for
+ * every size dsa_topk accepts (0 <= n_rows <= INT32_MAX, 1 <= n_cols <=
+ * DSA_TOPK_MAX_COLS, 1 <= k <= DSA_MAX_TOPK) and -1 for sizes it rejects.
+ */
+int64_t dsa_topk_workspace_bytes(int64_t n_rows, int64_t n_cols, int32_t k);
 
 /*
  * dsa_indexer_topk_fused - steps a1 + a2 + a3 in one launch.

@@ -184,6 +184,7 @@ def test_header_declares_the_path():
     for fn in ["dsa_packed_metadata", "dsa_ratio_causal_metadata", "dsa_indexer_fwd",
                "dsa_indexer_fwd_fp8", "dsa_indexer_topk_fused", "dsa_topk", "dsa_sparse_attn_fwd",
                "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_workspace_bytes",
+               "dsa_topk_workspace_bytes",
                "dsa_last_error",
                "dsa_abi_version"]:
         assert fn in names
@@ -249,3 +250,17 @@ def test_backward_workspace_size_rule():
     assert n == fixed + rows
     assert lib.dsa_sparse_attn_bwd_workspace_bytes(10, 0, 10, 576, 8) == -1
     assert lib.dsa_sparse_attn_bwd_workspace_bytes(10, 8, 10, 256, 8) == -1
+
+
+def test_topk_workspace_query():
+    # dsa_topk needs no workspace for any size it accepts, and the query
+    # rejects exactly the sizes dsa_topk rejects
+    lib = dsa.load_library()
+    assert lib.dsa_topk_workspace_bytes(65536, 65536, 2048) == 0
+    assert lib.dsa_topk_workspace_bytes(0, 1, 1) == 0
+    assert dsa.dsa_topk_workspace_bytes(8192, 4096, 64) == 0
+    for args in [(-1, 4096, 64), (8, 0, 64), (8, 65537, 64), (8, 4096, 0), (8, 4096, 2049),
+                 (2 ** 31, 4096, 64)]:
+        assert lib.dsa_topk_workspace_bytes(*args) == -1, args
+    with pytest.raises(ValueError):
+        dsa.dsa_topk_workspace_bytes(8, 4096, 4096)

@@ -69,6 +69,29 @@ def test_indexer_small(doc_lens, H, D, wdt):
     say("  worst rel err", err)
 
 
+@pytest.mark.parametrize("wdt", [torch.bfloat16, torch.float32])
+def test_indexer_weights_at_any_offset(wdt):
+    # W views at a storage offset that breaks the four-weight alignment take
+    # the one-weight loads; the scores are the same bits as from aligned W
+    say("indexer W offset", wdt)
+    wl = make_custom([300, 190], H=1, D_qk=256, D_v=256, H_idx=64, D_idx=128, seed=13, device=DEV)
+    w = wl.w.to(wdt)
+    base = torch.empty(w.numel() + 1, dtype=wdt, device=DEV)
+    base[1:].copy_(w.reshape(-1))
+    w_off = base[1:].view(w.shape)
+    assert w_off.data_ptr() % (4 * w_off.element_size()) != 0
+    rs, sl = _meta(wl)
+    a = dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, w, rs, sl, width=300)
+    b = dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, w_off, rs, sl, width=300)
+    torch.cuda.synchronize()
+    sln = i64(sl)
+    ga, gb = a.cpu().numpy(), b.cpu().numpy()
+    for t in range(wl.T):
+        assert np.array_equal(ga[t, :sln[t]].view(np.uint32), gb[t, :sln[t]].view(np.uint32)), t
+    wl.w = w
+    check_indexer(b, wl, np.arange(wl.T), i64(rs), sln)
+
+
 def test_indexer_chunk_offsets_and_untouched_columns():
     say("indexer chunk offsets")
     wl = make_custom([150, 333], H=1, D_qk=256, D_v=256, H_idx=64, D_idx=128, seed=5, device=DEV)
@@ -91,25 +114,41 @@ def test_indexer_chunk_offsets_and_untouched_columns():
 
 def _topk_check(scores: torch.Tensor, seq_lens: torch.Tensor, k: int, row_starts=None,
                 n_cols=None):
-    idx, tl, vals = dsa.dsa_topk(scores, seq_lens, k, row_starts=row_starts, n_cols=n_cols,
-                                 return_values=True)
-    torch.cuda.synchronize()
+    """Bit-exact top-K on both output paths of dsa_topk.
+
+    Without values the kernels stage the selected slots in LDS and write them
+    with 16-byte stores (and rows of at most k columns take the 16-byte closed
+    form): the path the pipeline uses. With values they write slot by slot.
+    Both calls write into buffers pre-filled with a sentinel, so an unwritten
+    slot shows up, and both are compared with the oracle on the same scores.
+    """
+    n_rows = scores.shape[0]
     sc = scores.detach().cpu().numpy()
     st = None if row_starts is None else i64(row_starts)
     ref_idx, ref_len = O.topk(sc.astype(np.float64), i64(seq_lens), k, row_starts=st,
                               n_cols=n_cols)
-    gi, gl = i64(idx), i64(tl)
-    bad = np.nonzero(np.any(gi != ref_idx, axis=1))[0]
-    assert len(bad) == 0, (bad[:5], gi[bad[:1]], ref_idx[bad[:1]])
-    assert np.array_equal(gl, ref_len)
-    # values: the selected scores (-0.0 may come back as +0.0), -inf padding
-    gv = vals.cpu().numpy().astype(np.float64)
-    for r in range(sc.shape[0]):
-        m = ref_len[r]
-        loc = ref_idx[r, :m] - (0 if st is None else st[r])
-        assert np.array_equal(gv[r, :m], sc[r, loc].astype(np.float64))
-        assert np.all(gv[r, m:] == -np.inf)
-    return idx, tl
+    res = {}
+    for with_values in (False, True):
+        idx = torch.full((n_rows, k), 0x7F7F7F7F, dtype=torch.int32, device=DEV)
+        tl = torch.full((n_rows,), -7, dtype=torch.int32, device=DEV)
+        _, _, vals = dsa.dsa_topk(scores, seq_lens, k, row_starts=row_starts, n_cols=n_cols,
+                                  indices=idx, topk_length=tl, return_values=with_values)
+        torch.cuda.synchronize()
+        gi, gl = i64(idx), i64(tl)
+        bad = np.nonzero(np.any(gi != ref_idx, axis=1))[0]
+        assert len(bad) == 0, (with_values, bad[:5], gi[bad[:1]], ref_idx[bad[:1]])
+        assert np.array_equal(gl, ref_len), with_values
+        res[with_values] = (idx, tl)
+        if not with_values:
+            continue
+        # values: the selected scores (-0.0 may come back as +0.0), -inf padding
+        gv = vals.cpu().numpy().astype(np.float64)
+        for r in range(n_rows):
+            m = ref_len[r]
+            loc = ref_idx[r, :m] - (0 if st is None else st[r])
+            assert np.array_equal(gv[r, :m], sc[r, loc].astype(np.float64))
+            assert np.all(gv[r, m:] == -np.inf)
+    return res[False]
 
 
 @pytest.mark.parametrize("n_cols", [100, 256, 1000, 4096, 5000, 16384, 20000, 40000, 65536])
@@ -386,6 +425,16 @@ def test_attention_kv_beyond_2gib(shared):
 
 # ------------------------------------------------------- named workloads
 
+def _assert_topk_is_oracle(idx, tl, scores, seq_lens, k, row_starts, n_cols=None):
+    """The selection a pipeline used equals the oracle's on the same fp32 scores."""
+    ref_idx, ref_len = O.topk(scores.detach().cpu().numpy().astype(np.float64), i64(seq_lens), k,
+                              row_starts=i64(row_starts), n_cols=n_cols)
+    gi = i64(idx)
+    bad = np.nonzero(np.any(gi != ref_idx, axis=1))[0]
+    assert len(bad) == 0, (bad[:5], gi[bad[:1]], ref_idx[bad[:1]])
+    assert np.array_equal(i64(tl), ref_len)
+
+
 def _pipeline(wl, max_seqlen=None):
     idx, tl = dsa.indexer_topk(wl.q_idx, wl.k_idx, wl.w, wl.cu_seqlens, wl.topk,
                                max_seqlen=max_seqlen)
@@ -404,6 +453,7 @@ def test_config1_full():
                                            softmax_scale=wl.scale)
     torch.cuda.synchronize()
     check_indexer(sc, wl, np.arange(wl.T), i64(rs), i64(sl))
+    _assert_topk_is_oracle(idx, tl, sc, sl, wl.topk, rs)  # the pipeline's own selection
     _topk_check(sc, sl, wl.topk, row_starts=rs)
     check_attention(out, lse, mx, wl.q, wl.kv, None, idx, tl, wl.sink, wl.scale, 512,
                     np.arange(wl.T))
@@ -430,6 +480,7 @@ def test_config2(stress):
     out, lse, mx = dsa.dsa_sparse_attn_fwd(wl.q, wl.kv, idx, topk_length=tl, attn_sink=wl.sink,
                                            softmax_scale=wl.scale)
     torch.cuda.synchronize()
+    _assert_topk_is_oracle(idx, tl, sc, sl, wl.topk, rs)  # the pipeline's own selection
     if not stress:
         check_indexer(sc, wl, np.arange(wl.T), i64(rs), i64(sl))
         _topk_check(sc, sl, wl.topk, row_starts=rs)
@@ -466,6 +517,29 @@ def test_config3_sampled():
         assert np.array_equal(i64(idx)[r], ref_idx[0]) and i64(tl)[r] == ref_len[0]
     check_attention(out, lse, mx, wl.q, wl.kv, None, idx, tl, wl.sink, wl.scale, 512,
                     rows[:: max(1, len(rows) // 16)])
+    # stress variant of the attention (same indexer inputs, so the same selection)
+    del out, lse, mx
+    wls = make_config(3, device=DEV, stress=True)
+    out, lse, mx = dsa.dsa_sparse_attn_fwd(wls.q, wls.kv, idx, topk_length=tl, attn_sink=wls.sink,
+                                           softmax_scale=wls.scale)
+    torch.cuda.synchronize()
+    check_attention(out, lse, mx, wls.q, wls.kv, None, idx, tl, wls.sink, wls.scale, 512,
+                    rows[:: max(1, len(rows) // 16)])
+
+
+def _c4_rows(T, chunk_rows, K):
+    """Sampled rows of the T=65536 workload: the first and last rows of every
+    score chunk, both sides of the top-K regimes (closed form up to K columns,
+    rows held on chip up to 8192 columns, streamed rows beyond), and seeded
+    random rows; 64 in all."""
+    edges = []
+    for c0 in range(0, T, chunk_rows):
+        edges += [c0, c0 + 1, c0 + chunk_rows - 1]
+    regimes = [K - 2, K - 1, K, K + 1, 4095, 4096, 8191, 8192, 8193, 16385, 32768, T - 2, T - 1]
+    base = np.unique(np.array([r for r in edges + regimes if 0 <= r < T]))
+    rng = np.random.default_rng(4)
+    extra = rng.choice(np.setdiff1d(np.arange(T), base), 64 - len(base), replace=False)
+    return np.sort(np.concatenate([base, extra]))
 
 
 def test_config4_sampled():
@@ -474,7 +548,9 @@ def test_config4_sampled():
     idx, tl, out, lse, mx = _pipeline(wl)
     torch.cuda.synchronize()
     rs, sl = _meta(wl)
-    rows = np.array([0, 2047, 2048, 30000, 65535])
+    rows = _c4_rows(wl.T, dsa.chunk_rows(wl.T, wl.T), wl.topk)
+    assert len(rows) == 64
+    gi_all, gl_all = i64(idx), i64(tl)
     for r in rows:
         sc = dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, wl.w, rs, sl, row_begin=int(r), n_rows=1,
                                  width=wl.T)
@@ -482,7 +558,7 @@ def test_config4_sampled():
         check_indexer(sc, wl, [r], i64(rs), i64(sl))
         ref_idx, ref_len = O.topk(sc.cpu().numpy().astype(np.float64), i64(sl)[[r]], wl.topk,
                                   row_starts=i64(rs)[[r]], n_cols=wl.T)
-        assert np.array_equal(i64(idx)[r], ref_idx[0]) and i64(tl)[r] == ref_len[0]
+        assert np.array_equal(gi_all[r], ref_idx[0]) and gl_all[r] == ref_len[0], int(r)
     check_attention(out, lse, mx, wl.q, wl.kv, None, idx, tl, wl.sink, wl.scale, 512, rows)
     # whole-tensor properties at full size
     gi = idx.cpu().numpy()
@@ -494,6 +570,16 @@ def test_config4_sampled():
     assert np.all(np.where(valid, gi <= t[:, None], True))
     assert np.all(np.diff(np.where(valid, gi, np.iinfo(np.int32).max), axis=1)[:, :] >= 0)
     assert torch.isfinite(lse).all() and torch.isfinite(out.float()).all()
+    # stress variant of the attention (same indexer inputs, so the same selection;
+    # queries scaled to logits of std ~4, sinks near the LSE)
+    del out, lse, mx
+    wls = make_config(4, device=DEV, stress=True)
+    del wl
+    out, lse, mx = dsa.dsa_sparse_attn_fwd(wls.q, wls.kv, idx, topk_length=tl, attn_sink=wls.sink,
+                                           softmax_scale=wls.scale)
+    torch.cuda.synchronize()
+    check_attention(out, lse, mx, wls.q, wls.kv, None, idx, tl, wls.sink, wls.scale, 512,
+                    rows[::2])
 
 
 def test_config5_sampled():
