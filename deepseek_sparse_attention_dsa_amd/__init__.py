@@ -67,7 +67,10 @@ _SIGNATURES = {
                              _F32, _P, _P, _P, _P, _P, _P, _P, _I64, _P], ctypes.c_int),
     "dsa_sparse_attn_fwd": ([_P, _I64, _I32, _I32, _P, _I64, _I64, _P, _I64, _I32, _P, _I64,
                              _I32, _P, _P, _F32, _P, _P, _P, _P], ctypes.c_int),
+    "dsa_sparse_attn_bwd_noalloc": ([_P, _I64, _I32, _I32, _P, _I64, _I64, _I32, _P, _I64, _I32,
+                                     _P, _P, _F32, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
 }
+DSA_NOALLOC_SCRATCH_BYTES = 256 * 1024 * 1024
 
 
 def library_path() -> str:

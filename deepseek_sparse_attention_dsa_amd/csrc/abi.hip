@@ -52,6 +52,33 @@ int check_device(const char* fn) {
   return DSA_OK;
 }
 
+// Scratch of dsa_sparse_attn_bwd_noalloc, for callers that cannot allocate.
+// One copy per device, at its own address, held until the process ends; every
+// call on a device shares it. In host code `scratch` names a host-side stand-in,
+// never the device memory: its device address is looked up once per device
+// (with that device current) and only that address is passed to kernels.
+__device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+void* g_scratch_ptr[kMaxDev];
+char g_scratch_err[kMaxDev][128];
+std::once_flag g_scratch_once[kMaxDev];
+
+// Device address of `scratch` on device `dev` (current), or NULL if the
+// lookup failed (the reason is in g_scratch_err[dev]).
+void* noalloc_scratch(int dev) {
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr || (uintptr_t)p % 256 != 0) {
+      snprintf(g_scratch_err[dev], sizeof(g_scratch_err[dev]), "hipGetSymbolAddress: %s",
+               e != hipSuccess ? hipGetErrorString(e) : "bad address");
+      g_scratch_ptr[dev] = nullptr;
+    } else {
+      g_scratch_ptr[dev] = p;
+    }
+  });
+  return g_scratch_ptr[dev];
+}
+
 int launched(const char* fn, hipError_t e) {
   if (e != hipSuccess) return fail(DSA_ERR_RUNTIME, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return DSA_OK;
@@ -342,13 +369,47 @@ int64_t dsa_sparse_attn_bwd_workspace_bytes(int64_t T_q, int32_t H, int64_t T_kv
   return bwd_fixed_bytes(T_q, H, T_kv, D_qk) + bwd_chunk_bytes(row, rows);
 }
 
+// The backward of both entry points. `noalloc`: the workspace is the no-alloc
+// scratch of the current device (its size is a fixed maximum, so a size
+// beyond it is reported as such and nothing is launched).
+static int bwd_run(const char* fn, const void* q, int64_t T_q, int32_t H, int32_t D_qk,
+                   const void* kv, int64_t T_kv, int64_t ld_kv, int32_t D_v,
+                   const int32_t* indices, int64_t ld_indices, int32_t k_width,
+                   const int32_t* topk_length, const float* attn_sink, float softmax_scale,
+                   const void* out, const void* dout, const float* lse, void* dq, void* dkv,
+                   float* d_sink, void* workspace, int64_t workspace_bytes, bool noalloc,
+                   void* stream);
+
 int dsa_sparse_attn_bwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk, const void* kv,
                         int64_t T_kv, int64_t ld_kv, int32_t D_v, const int32_t* indices,
                         int64_t ld_indices, int32_t k_width, const int32_t* topk_length,
                         const float* attn_sink, float softmax_scale, const void* out,
                         const void* dout, const float* lse, void* dq, void* dkv, float* d_sink,
                         void* workspace, int64_t workspace_bytes, void* stream) {
-  const char* fn = "dsa_sparse_attn_bwd";
+  return bwd_run("dsa_sparse_attn_bwd", q, T_q, H, D_qk, kv, T_kv, ld_kv, D_v, indices,
+                 ld_indices, k_width, topk_length, attn_sink, softmax_scale, out, dout, lse, dq,
+                 dkv, d_sink, workspace, workspace_bytes, false, stream);
+}
+
+int dsa_sparse_attn_bwd_noalloc(const void* q, int64_t T_q, int32_t H, int32_t D_qk,
+                                const void* kv, int64_t T_kv, int64_t ld_kv, int32_t D_v,
+                                const int32_t* indices, int64_t ld_indices, int32_t k_width,
+                                const int32_t* topk_length, const float* attn_sink,
+                                float softmax_scale, const void* out, const void* dout,
+                                const float* lse, void* dq, void* dkv, float* d_sink,
+                                void* stream) {
+  return bwd_run("dsa_sparse_attn_bwd_noalloc", q, T_q, H, D_qk, kv, T_kv, ld_kv, D_v, indices,
+                 ld_indices, k_width, topk_length, attn_sink, softmax_scale, out, dout, lse, dq,
+                 dkv, d_sink, nullptr, DSA_NOALLOC_SCRATCH_BYTES, true, stream);
+}
+
+static int bwd_run(const char* fn, const void* q, int64_t T_q, int32_t H, int32_t D_qk,
+                   const void* kv, int64_t T_kv, int64_t ld_kv, int32_t D_v,
+                   const int32_t* indices, int64_t ld_indices, int32_t k_width,
+                   const int32_t* topk_length, const float* attn_sink, float softmax_scale,
+                   const void* out, const void* dout, const float* lse, void* dq, void* dkv,
+                   float* d_sink, void* workspace, int64_t workspace_bytes, bool noalloc,
+                   void* stream) {
   REQUIRE(H >= 1 && H <= DSA_MAX_HEADS, DSA_ERR_VALUE, "%s: H must be in [1, %d] (got %d)", fn,
           DSA_MAX_HEADS, H);
   REQUIRE((D_qk == 576 || D_qk == 512) && D_v == 512, DSA_ERR_VALUE,
@@ -372,11 +433,26 @@ int dsa_sparse_attn_bwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk, con
           "alignment", fn);
   const int64_t fixed = bwd_fixed_bytes(T_q, H, T_kv, D_qk);
   const BwdRow row = bwd_row_bytes(H, k_width, D_qk);
-  REQUIRE(workspace && workspace_bytes >= fixed + bwd_chunk_bytes(row, 1), DSA_ERR_VALUE,
-          "%s: workspace of %lld bytes is below the %lld bytes one row needs", fn,
-          (long long)workspace_bytes, (long long)(fixed + bwd_chunk_bytes(row, 1)));
+  if (noalloc) {
+    REQUIRE(fixed + bwd_chunk_bytes(row, 1) <= workspace_bytes, DSA_ERR_VALUE,
+            "%s: these sizes need %lld bytes of scratch for one query row, more than the "
+            "%lld-byte no-alloc scratch (use dsa_sparse_attn_bwd with a workspace)", fn,
+            (long long)(fixed + bwd_chunk_bytes(row, 1)), (long long)workspace_bytes);
+  } else {
+    REQUIRE(workspace && workspace_bytes >= fixed + bwd_chunk_bytes(row, 1), DSA_ERR_VALUE,
+            "%s: workspace of %lld bytes is below the %lld bytes one row needs", fn,
+            (long long)workspace_bytes, (long long)(fixed + bwd_chunk_bytes(row, 1)));
+  }
   if (T_q == 0 && T_kv == 0 && !d_sink) return DSA_OK;
   if (int rc = check_device(fn)) return rc;
+  if (noalloc) {
+    int dev = -1;
+    (void)hipGetDevice(&dev);  // valid: check_device has just succeeded
+    workspace = noalloc_scratch(dev);
+    if (!workspace)
+      return fail(DSA_ERR_RUNTIME, "%s: the no-alloc scratch of device %d has no address (%s)",
+                  fn, dev, g_scratch_err[dev]);
+  }
   unsigned char* w = (unsigned char*)workspace;
   dsa::BwdArgs a{};
   a.q = (const uint16_t*)q;

@@ -14,6 +14,8 @@
  *                        in one launch, the scores kept on chip
  *   dsa_sparse_attn_fwd  sparse MQA/GQA attention over the selected KV rows
  *   dsa_sparse_attn_bwd  its gradients (dq, dkv, d_sink) for shared latent KV
+ *                        (dsa_sparse_attn_bwd_noalloc: the same without a
+ *                        caller workspace, for callers that cannot allocate)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -69,7 +71,7 @@ typedef enum {
 const char* dsa_last_error(void);
 
 /* ABI version of this header (bumped on any signature change). */
-#define DSA_ABI_VERSION 6
+#define DSA_ABI_VERSION 7
 int dsa_abi_version(void);
 
 /* Limits enforced by the host checks. */
@@ -77,6 +79,8 @@ int dsa_abi_version(void);
 #define DSA_TOPK_MAX_COLS 65536     /* longest score row dsa_topk selects on */
 #define DSA_MAX_HEADS 128           /* attention query heads per call        */
 #define DSA_FUSED_MAX_COLS 4096     /* longest row dsa_indexer_topk_fused takes */
+/* Device scratch of dsa_sparse_attn_bwd_noalloc (bytes, per device). */
+#define DSA_NOALLOC_SCRATCH_BYTES (256ll * 1024 * 1024)
 
 /* Input precision of dsa_indexer_topk_fused. */
 typedef enum {
@@ -372,6 +376,37 @@ int dsa_sparse_attn_bwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk, con
                         const float* attn_sink, float softmax_scale, const void* out,
                         const void* dout, const float* lse, void* dq, void* dkv, float* d_sink,
                         void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * dsa_sparse_attn_bwd_noalloc - dsa_sparse_attn_bwd for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid allocation): the same gradients from the same
+ * kernels, with the workspace replaced by a scratch array that the library
+ * keeps in device memory, DSA_NOALLOC_SCRATCH_BYTES per device, held from the
+ * first call on a device until the process ends. The call allocates and
+ * frees nothing.
+ *   Arguments: as dsa_sparse_attn_bwd, without workspace / workspace_bytes.
+ *   Results: bit for bit those of dsa_sparse_attn_bwd given a workspace of
+ *   DSA_NOALLOC_SCRATCH_BYTES bytes (the workspace size sets the chunks of
+ *   query rows, and with them the order of the dkv sums).
+ *   Sizes: the scratch must hold the fixed buffers plus one query row's
+ *   (dsa_sparse_attn_bwd_workspace_bytes with T_q = 1 and the same other
+ *   sizes, plus the [T_q, H] statistics); larger sizes return DSA_ERR_VALUE
+ *   with nothing launched.
+ *   Concurrency: every call on a device uses that device's one scratch
+ *   array, which keeps the previous call's contents (each call clears what
+ *   it needs zeroed). Calls that overlap on one device (other streams, other
+ *   threads) race on it; order them on one stream.
+ * Errors: those of dsa_sparse_attn_bwd; DSA_ERR_RUNTIME if the scratch's
+ * device address cannot be obtained.
+ */
+int dsa_sparse_attn_bwd_noalloc(const void* q, int64_t T_q, int32_t H, int32_t D_qk,
+                                const void* kv, int64_t T_kv, int64_t ld_kv, int32_t D_v,
+                                const int32_t* indices, int64_t ld_indices, int32_t k_width,
+                                const int32_t* topk_length, const float* attn_sink,
+                                float softmax_scale, const void* out, const void* dout,
+                                const float* lse, void* dq, void* dkv, float* d_sink,
+                                void* stream);
 
 #ifdef __cplusplus
 }

@@ -39,6 +39,7 @@ FUSED_BASE = dict(q=FAKE, qs=None, k=FAKE, ks=None, prec=0, w=FAKE, wd=0, rs=FAK
 BWD_BASE = dict(q=FAKE, Tq=16, H=16, Dqk=576, kv=FAKE, Tkv=16, ldkv=576, Dv=512, idx=FAKE, ldi=64,
                 kw=64, tl=None, sink=None, scale=0.04, out=FAKE, dout=FAKE, lse=FAKE, dq=FAKE,
                 dkv=FAKE, ds=None, ws=FAKE2, wsb=1 << 24, stream=None)
+NOALLOC_BASE = {k: v for k, v in BWD_BASE.items() if k not in ("ws", "wsb")}
 RMETA_BASE = dict(cq=FAKE, ck=FAKE2, off=None, n_seq=2, T=4, ratio=4, rs=FAKE, sl=FAKE,
                   stream=None)
 
@@ -57,12 +58,16 @@ ORDER = {
               "nc", "kk", "idx", "ldi", "tl", "lg", "so", "lse", "stream"],
     "bwd": ["q", "Tq", "H", "Dqk", "kv", "Tkv", "ldkv", "Dv", "idx", "ldi", "kw", "tl", "sink",
             "scale", "out", "dout", "lse", "dq", "dkv", "ds", "ws", "wsb", "stream"],
+    "noalloc": ["q", "Tq", "H", "Dqk", "kv", "Tkv", "ldkv", "Dv", "idx", "ldi", "kw", "tl",
+                "sink", "scale", "out", "dout", "lse", "dq", "dkv", "ds", "stream"],
 }
 BASE = {"topk": TOPK_BASE, "idx": IDX_BASE, "attn": ATTN_BASE, "meta": META_BASE,
-        "rmeta": RMETA_BASE, "f8": F8_BASE, "fused": FUSED_BASE, "bwd": BWD_BASE}
+        "rmeta": RMETA_BASE, "f8": F8_BASE, "fused": FUSED_BASE, "bwd": BWD_BASE,
+        "noalloc": NOALLOC_BASE}
 FN = {"topk": "dsa_topk", "idx": "dsa_indexer_fwd", "attn": "dsa_sparse_attn_fwd",
       "meta": "dsa_packed_metadata", "rmeta": "dsa_ratio_causal_metadata",
-      "f8": "dsa_indexer_fwd_fp8", "fused": "dsa_indexer_topk_fused", "bwd": "dsa_sparse_attn_bwd"}
+      "f8": "dsa_indexer_fwd_fp8", "fused": "dsa_indexer_topk_fused", "bwd": "dsa_sparse_attn_bwd",
+      "noalloc": "dsa_sparse_attn_bwd_noalloc"}
 
 CASES = [
     # top-K
@@ -137,6 +142,14 @@ CASES = [
     ("bwd", dict(ws=None), EVALUE), ("bwd", dict(wsb=1024), EVALUE), ("bwd", dict(ws=FAKE2 + 16), EVALUE),
     ("bwd", dict(out=FAKE + 8), EVALUE), ("bwd", dict(idx=None), EVALUE),
     ("bwd", dict(), ERUNTIME), ("bwd", dict(Dqk=512, ldkv=512, sink=FAKE, ds=FAKE), ERUNTIME),
+    # attention backward on the no-alloc scratch: the same checks, plus sizes
+    # whose fixed buffers and one query row exceed the scratch
+    ("noalloc", dict(H=0), EVALUE), ("noalloc", dict(Dv=256), EVALUE),
+    ("noalloc", dict(scale=0.0), EVALUE), ("noalloc", dict(dout=None), EVALUE),
+    ("noalloc", dict(out=FAKE + 8), EVALUE),
+    ("noalloc", dict(Tkv=1 << 17), EVALUE),     # fp32 dkv accumulator alone: 302 MB
+    ("noalloc", dict(Tq=1 << 20, H=128), EVALUE),  # [T_q, H] statistics: 1 GiB
+    ("noalloc", dict(), ERUNTIME), ("noalloc", dict(Tkv=1 << 16), ERUNTIME),
 ]
 
 _CHILD = r"""
