@@ -61,6 +61,7 @@ namespace {
 constexpr int kBN = 32;          // key slots per tile
 constexpr int kCopyStart = 0;
 constexpr int kCopyTail = 32;
+constexpr int kPvGroup = 4;      // column blocks per k-step group of the P.V MFMAs
 constexpr float kHeadroom = 64.0f;  // logits may exceed the reference by 2^64
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963387f;
@@ -179,9 +180,14 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
       if constexpr (BUF) {
         // ids < 2^24 and row strides < 2^24 bytes here (the host checks the
         // span), so one 24-bit multiply-add forms the offset
-        cs.ko[gi] = ok ? __umul24((uint32_t)idg[gi], a.row_bytes_k) + 16u * chunk : kPastRange;
-        if constexpr (!SHARED)
-          cs.vo[gi] = ok ? __umul24((uint32_t)idg[gi], a.row_bytes_v) + 16u * chunk : kPastRange;
+        // (the multiply-add on every lane and a select, not a branch)
+        const uint32_t idu = (uint32_t)idg[gi];
+        const uint32_t ko = __umul24(idu, a.row_bytes_k) + 16u * chunk;
+        cs.ko[gi] = ok ? ko : kPastRange;
+        if constexpr (!SHARED) {
+          const uint32_t vo = __umul24(idu, a.row_bytes_v) + 16u * chunk;
+          cs.vo[gi] = ok ? vo : kPastRange;
+        }
       } else {
         const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_zero_row);
         const uint64_t row = ok ? (uint64_t)(uint32_t)idg[gi] : 0ull;
@@ -212,6 +218,64 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
   };
   auto copy_all = [&](const CopySrc& cs) {
     static_for<NCOPY>([&](auto jc) { copy_one(cs, jc); });
+  };
+  // The q.k MFMA of one k-step with copy J issued around it: the MFMA sits
+  // between the M0 write and the copy, so it is the wait state the copy's M0
+  // read needs (copy_one pays an s_nop for it). FIRST: the chain's first
+  // MFMA (no accumulator input).
+  auto mfma_with_copy = [&](f32x16& acc, const u32x4& ka, const u32x4& qb, const CopySrc& cs,
+                            auto jc, auto firstc) {
+    constexpr int J = decltype(jc)::value;
+    constexpr bool FIRST = decltype(firstc)::value;
+    constexpr bool IS_K = J < C::K_PER_WAVE;
+    constexpr int U = IS_K ? J : J - C::K_PER_WAVE;
+    constexpr int GI = U % C::GPW, S = U / C::GPW;
+    constexpr int IMM = 128 * S;
+    const uint32_t m0 =
+        cs.m0 + (uint32_t)((IS_K ? 0 : C::V_BASE) + 1024 * (4 * S + GI) - 128 * S);
+    if constexpr (BUF) {
+      uint32_t voff;
+      i32x4 rs;
+      if constexpr (IS_K) {
+        voff = cs.ko[GI];
+        rs = rsrc_k;
+      } else {
+        voff = cs.vo[GI];
+        rs = rsrc_v;
+      }
+      if constexpr (FIRST)
+        asm volatile(
+            "s_mov_b32 m0, %3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n\t"
+            "buffer_load_dwordx4 %4, %5, 0 offen offset:%6 lds"
+            : "=v"(acc)
+            : "v"(ka), "v"(qb), "s"(m0), "v"(voff), "s"(rs), "i"(IMM)
+            : "memory");
+      else
+        asm volatile(
+            "s_mov_b32 m0, %3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+            "buffer_load_dwordx4 %4, %5, 0 offen offset:%6 lds"
+            : "+v"(acc)
+            : "v"(ka), "v"(qb), "s"(m0), "v"(voff), "s"(rs), "i"(IMM)
+            : "memory");
+    } else {
+      const uint16_t* gp;
+      if constexpr (IS_K) gp = cs.k[GI];
+      else gp = cs.v[GI];
+      if constexpr (FIRST)
+        asm volatile(
+            "s_mov_b32 m0, %3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n\t"
+            "global_load_lds_dwordx4 %4, off offset:%5"
+            : "=v"(acc)
+            : "v"(ka), "v"(qb), "s"(m0), "v"(gp), "i"(IMM)
+            : "memory");
+      else
+        asm volatile(
+            "s_mov_b32 m0, %3\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+            "global_load_lds_dwordx4 %4, off offset:%5"
+            : "+v"(acc)
+            : "v"(ka), "v"(qb), "s"(m0), "v"(gp), "i"(IMM)
+            : "memory");
+    }
   };
 
   // The first two tiles' ids are loaded before Q (and together with
@@ -278,28 +342,32 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
     for (int it = 0; it < n_tiles; ++it) {
       wait_vmcnt0();
       __syncthreads();  // every wave's copies of tile it have landed; tile it-1 is consumed
-      uint32_t mask_next = 0;
       const bool copy_next = it + 1 < n_tiles;  // uniform over the workgroup
-      CopySrc cs{};
-      if (copy_next) {
-        const int32_t idv = valid_id(id_next, (it + 1) * kBN + key_row);
-        mask_next = (uint32_t)ballot(idv >= 0);
-        cs = prep_copy(smem_base + ((it + 1) & 1) * C::STAGE_BYTES, idv);
-      }
+      // The copies of tile it+1 go out unconditionally: after the last tile
+      // every slot is past the valid prefix, so they fill the free stage
+      // with zeros (out-of-range offsets, or the zero row) and no branch per
+      // copy is needed. They are waited for before the LDS is reused.
+      const int32_t idv = valid_id(id_next, (it + 1) * kBN + key_row);
+      const uint32_t mask_next = (uint32_t)ballot(idv >= 0);
+      const CopySrc cs = prep_copy(smem_base + ((it + 1) & 1) * C::STAGE_BYTES, idv);
       const unsigned char* tile = smem + (it & 1) * C::STAGE_BYTES;
       constexpr int S0 = kCopyStart;
       constexpr int S1 =
           C::KS + 2 * C::NB - kCopyTail > C::KS ? C::KS + 2 * C::NB - kCopyTail : C::KS;
       constexpr int NSLOT = S1 - S0;
-      auto copies_at_slot = [&](auto slotc) {
-        constexpr int sl = decltype(slotc)::value - S0;
-        constexpr int j0 = sl < 0 ? 0 : sl < NSLOT ? (sl * NCOPY + NSLOT - 1) / NSLOT : NCOPY;
-        constexpr int j1 = sl < 0 ? 0 : sl < NSLOT ? ((sl + 1) * NCOPY + NSLOT - 1) / NSLOT : NCOPY;
-        if (copy_next) {
-          static_for<j1 - j0>([&](auto dj) {
-            copy_one(cs, std::integral_constant<int, j0 + decltype(dj)::value>{});
-          });
-        }
+      // copies [j0, j1) of the share go out at slot sl (the q.k k-steps, then
+      // the p.v MFMAs): the copies spread evenly over slots S0 .. S1-1
+      auto slot_first = [](int slot) constexpr -> int {
+        const int sl = slot - S0;
+        return sl < 0 ? 0 : sl < NSLOT ? (sl * NCOPY + NSLOT - 1) / NSLOT : NCOPY;
+      };
+      auto copies_at_slot = [&](auto slotc, auto skipc) {
+        constexpr int slot = decltype(slotc)::value;
+        constexpr int SKIP = decltype(skipc)::value;  // leading copies already issued
+        constexpr int j0 = slot_first(slot) + SKIP, j1 = slot_first(slot + 1);
+        static_for<(j1 > j0 ? j1 - j0 : 0)>([&](auto dj) {
+          copy_one(cs, std::integral_constant<int, j0 + decltype(dj)::value>{});
+        });
       };
 
       // ---- S^T = K_tile . Q^T: lane holds head r32, keys 8*(i/4)+4*half+(i%4) ----
@@ -334,11 +402,18 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
           constexpr int ks = decltype(kc)::value;
           const u32x4 cur = af[ks % PF];
           if constexpr (ks + PF < C::KS) af[ks % PF] = kread(ks + PF);
-          if constexpr (ks == 0)
+          constexpr int jf = slot_first(ks);
+          constexpr bool with_copy = slot_first(ks + 1) > jf;
+          if constexpr (with_copy) {
+            // the slot's first copy around the MFMA, any others after it
+            mfma_with_copy(sc, cur, qf[ks], cs, std::integral_constant<int, jf>{},
+                           std::bool_constant<ks == 0>{});
+            copies_at_slot(std::integral_constant<int, ks>{}, std::integral_constant<int, 1>{});
+          } else if constexpr (ks == 0) {
             asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(sc) : "v"(cur), "v"(qf[ks]));
-          else
+          } else {
             asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sc) : "v"(cur), "v"(qf[ks]));
-          copies_at_slot(std::integral_constant<int, ks>{});
+          }
         });
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(sc));
       }
@@ -362,32 +437,33 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
         for (int i = 0; i < 16; ++i)
           if (!((mh >> (8 * (i >> 2) + (i & 3))) & 1u)) sc[i] = -__builtin_inff();
       }
-      // IEEE maximum (v_maximum3_f32): no NaN quieting of each operand
-      float mloc = sc[0];
+      // The scaled max of the head's 32 scores: the lane's 16 (IEEE maximum,
+      // v_maximum3_f32: no NaN quieting of each operand), then the half-wave
+      // exchange.
+      auto max_of = [&](float m, int i0, int i1) -> float {
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mloc = __builtin_elementwise_maximum(mloc, sc[i]);
-      mloc = halfwave_max(mloc) * a.scale_log2;
-      m_true = __builtin_elementwise_maximum(m_true, mloc);
-      if (m_ref == -__builtin_inff()) m_ref = mloc;  // first tile with a valid key
-      overflow |= mloc > m_ref + kHeadroom;
+        for (int i = i0; i < i1; ++i) m = __builtin_elementwise_maximum(m, sc[i]);
+        return m;
+      };
+      // The reference is the max of the first tile with a valid key, so that
+      // tile takes its max before the weights. Every tile finishes its max
+      // (for max_logits and the headroom check) in the shadow of the first
+      // P.V MFMAs; for the reference tile that repeats the same value.
+      const bool set_ref = ballot(m_ref == -__builtin_inff()) != 0;  // uniform
+      // the lane's max over sc[0..7] now (they become weights first), over
+      // all 16 before sc[8..15] become weights
+      const float m_lo = max_of(sc[0], 1, 8);
+      float m_lo_hi;
+      if (set_ref) {
+        m_lo_hi = max_of(m_lo, 8, 16);
+        const float m = halfwave_max(m_lo_hi) * a.scale_log2;
+        if (m_ref == -__builtin_inff()) m_ref = m;
+      }
       const float neg_ref = m_ref == -__builtin_inff() ? 0.f : -m_ref;
-      float p[16];
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(sc[i], a.scale_log2, neg_ref));
-#pragma unroll
-      for (int i = 0; i < 16; ++i) psum += p[i];
-      l_run += psum;
-
+      float mloc;
       // ---- O += P . V ----
       u32x4 pa[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        pa[st][0] = pack_bf16x2(p[8 * st + 0], p[8 * st + 1]);
-        pa[st][1] = pack_bf16x2(p[8 * st + 2], p[8 * st + 3]);
-        pa[st][2] = pack_bf16x2(p[8 * st + 4], p[8 * st + 5]);
-        pa[st][3] = pack_bf16x2(p[8 * st + 6], p[8 * st + 7]);
-      }
+      float psum = 0.f;
       {
         // Transposed reads: for column block nb and key half st, 16-lane
         // group G reads keys 16*st + 8*b + 4*(G/2) .. +3 (b = 0, 1), dims
@@ -406,33 +482,75 @@ __global__ __launch_bounds__(NW * 64, 1) void sparse_attn_kernel(AttnArgs a) {
 #pragma unroll
           for (int b = 0; b < 2; ++b)
             va[pp][b] = vbase + 1024 * b + 16 * (4 * (pp ^ (li >> 3)) + 2 * ((G & 1) ^ b));
-        // MFMA f (f = 0 .. 2*NB-1) accumulates column block
-        // nb = 2*(f/4) + f%2 over key half st = (f/2)%2: pairs of blocks, so
-        // consecutive MFMAs never accumulate into the same block. Its V
-        // fragment is read VPF MFMAs ahead.
-        static_assert(C::NB % 2 == 0, "column blocks are processed in pairs");
+        // The MFMAs run in groups of kPvGroup column blocks: k-step 0 of the
+        // group's blocks, then their k-step 1 (MFMA f accumulates block
+        // nb = kPvGroup*(f / (2*kPvGroup)) + f % kPvGroup over key half
+        // st = (f / kPvGroup) % 2), so the first kPvGroup MFMAs need only the
+        // k-step 0 weights and the k-step 1 weights are computed while they
+        // run; consecutive MFMAs never accumulate into the same block. (A
+        // longer first group would leave more time for them but spills
+        // registers.) Its V fragment is read VPF MFMAs ahead.
         auto vfrag = [&](int f) -> u32x4 {
-          const int nb = 2 * (f >> 2) + (f & 1), st = (f >> 1) & 1;
+          const int nb = (f / (2 * kPvGroup)) * kPvGroup + f % kPvGroup,
+                    st = (f / kPvGroup) % 2;
           const int so = (nb >> 1) * 4096 + st * 2048;
           const u32x2 x0 = lds_read_tr16(va[nb & 1][0] + so);
           const u32x2 x1 = lds_read_tr16(va[nb & 1][1] + so);
           return u32x4{x0.x, x0.y, x1.x, x1.y};
         };
+        static_assert(C::NB % kPvGroup == 0, "column blocks come in whole groups");
         constexpr int VPF = 4;
         u32x4 vq[VPF];
 #pragma unroll
         for (int i = 0; i < VPF; ++i) vq[i] = vfrag(i);
+        __builtin_amdgcn_sched_barrier(0);  // the first V reads go out before the weights
+        // Weights of k-step 0 of the P.V product (keys 0..15: sc[0..7]) first;
+        // those of k-step 1 (sc[8..15]) are computed under the k-step 0 MFMAs.
+        {
+          float p[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) p[i] = fast_exp2(fmaf(sc[i], a.scale_log2, neg_ref));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) psum += p[i];
+          pa[0] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                        pack_bf16x2(p[6], p[7])};
+        }
         static_for<2 * C::NB>([&](auto fc) {
           constexpr int f = decltype(fc)::value;
-          constexpr int nb = 2 * (f >> 2) + (f & 1), st = (f >> 1) & 1;
+          constexpr int nb = (f / (2 * kPvGroup)) * kPvGroup + f % kPvGroup,
+                        st = (f / kPvGroup) % 2;
           const u32x4 cur = vq[f % VPF];
           if constexpr (f + VPF < 2 * C::NB) vq[f % VPF] = vfrag(f + VPF);
           o[nb] = mfma32x32x16(pa[st], cur, o[nb]);
-          copies_at_slot(std::integral_constant<int, C::KS + f>{});
+          copies_at_slot(std::integral_constant<int, C::KS + f>{}, std::integral_constant<int, 0>{});
+          // VALU work in the shadow of this MFMA: the k-step 1 weights (two
+          // per MFMA) before MFMA kPvGroup needs them, then the tile max and
+          // the weight sum.
+          if constexpr (f == 0) m_lo_hi = max_of(m_lo, 8, 16);
+          if constexpr (f < kPvGroup) {
+            constexpr int i0 = 8 + f * 8 / kPvGroup, i1 = 8 + (f + 1) * 8 / kPvGroup;
+#pragma unroll
+            for (int i = i0; i < i1; ++i) sc[i] = fast_exp2(fmaf(sc[i], a.scale_log2, neg_ref));
+            if constexpr (f == kPvGroup - 1)
+              pa[1] = u32x4{pack_bf16x2(sc[8], sc[9]), pack_bf16x2(sc[10], sc[11]),
+                            pack_bf16x2(sc[12], sc[13]), pack_bf16x2(sc[14], sc[15])};
+          } else if constexpr (f == kPvGroup) {
+            mloc = halfwave_max(m_lo_hi) * a.scale_log2;
+          } else if constexpr (f == kPvGroup + 1) {
+#pragma unroll
+            for (int i = 8; i < 16; ++i) psum += sc[i];
+          }
+          __builtin_amdgcn_sched_barrier(0);
         });
       }
+      m_true = __builtin_elementwise_maximum(m_true, mloc);
+      overflow |= mloc > m_ref + kHeadroom;
+      l_run += psum;
       mask_cur = mask_next;
     }
+    // the last tile's zero-filling copies land before any LDS reuse (the
+    // next pass's copies, the output staging after the next barrier)
+    wait_vmcnt0();
     if (pass == 0) {
       const bool any = ballot(overflow) != 0;
       if (lane == 0) s_redo[wave] = any ? 1 : 0;
