@@ -42,8 +42,12 @@
 //     ranges spread over many bins instead of piling onto a few exponent
 //     digits), then an exact rank inside the bucket holding the K-th largest
 //     (one wave when it has at most 64 members, radix passes otherwise).
-//  4. One thread per chunk walks its candidates in column order and writes
-//     the selected ones to their output slots.
+//  4. Output: a scan of the chunk counts gives each chunk's first position
+//     in column order; every thread takes an equal share of the positions
+//     (its first chunk by binary search), counts the keys above and equal to
+//     theta, and after a scan of those counts places its selected keys,
+//     staged in LDS for 16-byte stores when no values are written.
+#include "dsa.h"
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -437,6 +441,7 @@ constexpr int kMaxChunks = 65536 / 256;  // 256-column chunks of the longest row
 constexpr int kCap = 3584;               // candidate list capacity
 constexpr int kBatch = 8;                // chunk loads in flight per wave
 static_assert(kMaxChunks == kSThreads, "one thread per chunk in the output walk");
+static_assert(kBins >= DSA_MAX_TOPK, "the histogram holds the staged output of a row");
 
 __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
     const float* __restrict__ scores, int64_t ld, int64_t n_cols,
@@ -448,7 +453,7 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
   __shared__ uint32_t s_ckey[kCap];
   __shared__ uint16_t s_ccol[kCap];        // column within the row (< 65536)
   __shared__ uint16_t s_cbase[kMaxChunks];  // chunk -> first candidate slot
-  __shared__ uint16_t s_ccnt[kMaxChunks];   // chunk -> candidate count
+  __shared__ uint16_t s_ccnt[kMaxChunks + 1];  // chunk -> candidate count, later its start
   __shared__ uint32_t s_wave[kSWaves];
   __shared__ uint32_t s_red[kSWaves];
   __shared__ uint32_t s_sel[2];
@@ -486,6 +491,20 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
   // the bucket holding the want-th largest of the histogrammed keys:
   // s_sel[0] = bucket, s_sel[1] = count in the buckets above it
   auto find_bucket_s = [&](uint32_t want) { find_bucket<kSWaves>(hist, want, s_wave, s_sel); };
+
+  // The streaming pass's first batch is requested now, so that its loads
+  // are in flight while the sample is taken.
+  float4 v[kBatch];
+  auto load_batch = [&](int c0) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int ch = c0 + kSWaves * i;
+      const int64_t col = ch < nchunks ? (int64_t)ch * 256 + lane * 4 : 0;
+      const int64_t colc = col < ld - 4 ? col : ld - 4;
+      v[i] = *reinterpret_cast<const float4*>(row + colc);
+    }
+  };
+  load_batch(wave);
 
   // ---- 1. sampled lower bound (rows of more than kCap columns) ----
   uint32_t lo_key = 1u;  // the smallest valid key: every column is a candidate
@@ -544,14 +563,7 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
   if (tid == 0) s_cnt = 0u;
   __syncthreads();
   for (int c0 = wave; c0 < nchunks; c0 += kSWaves * kBatch) {
-    float4 v[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int ch = c0 + kSWaves * i;
-      const int64_t col = ch < nchunks ? (int64_t)ch * 256 + lane * 4 : 0;
-      const int64_t colc = col < ld - 4 ? col : ld - 4;
-      v[i] = *reinterpret_cast<const float4*>(row + colc);
-    }
+    if (c0 != wave) load_batch(c0);  // the first batch is already in flight
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int ch = c0 + kSWaves * i;  // uniform
@@ -625,8 +637,8 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
       if (wave == 0) {
         const uint32_t x = lane < (int)m ? hist[lane] : 0u;
         uint32_t gt = 0, eq = 0;
-        for (uint32_t j = 0; j < m; ++j) {
-          const uint32_t y = hist[j];
+        for (uint32_t j = 0; j < m; ++j) {  // member j from its lane, not from LDS
+          const uint32_t y = (uint32_t)__builtin_amdgcn_readlane((int)x, (int)j);
           gt += y > x;
           eq += y == x;
         }
@@ -648,20 +660,58 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
       });
     }
 
-    // ---- 4. output: thread t walks chunk t's candidates in column order ----
-    const int cnt = tid < nchunks ? (int)s_ccnt[tid] : 0;
-    const int cbase = tid < nchunks ? (int)s_cbase[tid] : 0;
+    // ---- 4. output: the candidates in column order, an equal share each ----
+    // Chunk starts in column order (an exclusive scan of the chunk counts)
+    // replace the counts: chunk ch holds column-order positions
+    // [s_ccnt[ch], s_ccnt[ch + 1]), its candidates at slots s_cbase[ch] + ...
+    {
+      const uint32_t c = tid < nchunks ? (uint32_t)s_ccnt[tid] : 0u;
+      uint32_t tot;
+      const uint32_t cst = block_exclusive_scan<kSWaves>(c, s_wave, &tot);  // ends with a barrier
+      if (tid < nchunks) s_ccnt[tid] = (uint16_t)cst;
+      if (tid == 0) s_ccnt[nchunks] = (uint16_t)tot;
+      __syncthreads();
+    }
+    // thread t: positions [p0, p1); ch0 = the last chunk starting at or
+    // before p0 (empty chunks share the next one's start)
+    const int p0 = nc * tid / NT, p1 = nc * (tid + 1) / NT;
+    int lo = 0, hi = nchunks - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((int)s_ccnt[mid] <= p0) lo = mid; else hi = mid - 1;
+    }
+    const int ch0 = lo;
+    // f(slot) for the thread's positions in order
+    auto walk = [&](auto&& f) {
+      int ch = ch0, cend = s_ccnt[ch + 1];
+      int slot = s_cbase[ch] + (p0 - (int)s_ccnt[ch]);
+      for (int p = p0; p < p1; ++p, ++slot) {
+        while (p >= cend) {  // next non-empty chunk (p < nc keeps ch < nchunks)
+          ++ch;
+          cend = s_ccnt[ch + 1];
+          slot = s_cbase[ch];
+        }
+        f(slot);
+      }
+    };
     uint32_t ngt = 0, neq = 0;
-    for (int i = 0; i < cnt; ++i) {
-      const uint32_t key = s_ckey[cbase + i];
+    walk([&](int slot) {
+      const uint32_t key = s_ckey[slot];
       ngt += key > theta;
       neq += key == theta;
-    }
+    });
     uint32_t total;
     const uint32_t before = block_exclusive_scan<kSWaves>(ngt | (neq << 16), s_wave, &total);
     uint32_t g = before & 0xffffu, q = before >> 16;
-    const Placer pl{theta, need_eq, (uint32_t)k, out_idx, out_val};
-    for (int i = 0; i < cnt; ++i) pl(s_ckey[cbase + i], base + (int32_t)s_ccol[cbase + i], g, q);
+    const bool staged = !out_val && (k & 3) == 0 && ((uintptr_t)out_idx & 15u) == 0;
+    const Placer pl{theta, need_eq, (uint32_t)k, staged ? reinterpret_cast<int32_t*>(hist) : out_idx,
+                    out_val};
+    walk([&](int slot) { pl(s_ckey[slot], base + (int32_t)s_ccol[slot], g, q); });
+    if (staged) {
+      __syncthreads();
+      for (int i = 4 * tid; i < k; i += 4 * NT)
+        *reinterpret_cast<u32x4*>(out_idx + i) = *reinterpret_cast<const u32x4*>(hist + i);
+    }
   } else {
     // ---- fallback: radix passes that re-stream the row ----
     const int nq = (n + 3) / 4;  // 16-byte groups of the row
