@@ -33,10 +33,13 @@
 //     Rows of at most kCap columns take every column as a candidate.
 //  2. One streaming pass compares every score with lo and appends the
 //     columns at or above it, chunk by chunk (256 columns per wave load), to
-//     an LDS candidate list; a direct-mapped table of chunks records where
-//     each chunk's candidates went, which restores column order later. If
-//     fewer than K or more than kCap columns pass, the row is redone with
-//     radix passes that re-stream it (correct for any input, slow).
+//     an LDS candidate list: wave w takes chunks w, w + 4, ... and appends to
+//     its own quarter of the list with a counter in a register (no shared
+//     counter); a direct-mapped table of chunks records where each chunk's
+//     candidates went, which restores column order later. If fewer than K
+//     columns pass, or more than a quarter's kCap / 4 in some wave, the row
+//     is redone with radix passes that re-stream it (correct for any input,
+//     slow).
 //  3. theta among the candidates: a histogram over 2048 buckets linear in
 //     the score value between lo and the largest candidate (dense score
 //     ranges spread over many bins instead of piling onto a few exponent
@@ -438,7 +441,8 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
 constexpr int kSWaves = 4;
 constexpr int kSThreads = 64 * kSWaves;
 constexpr int kMaxChunks = 65536 / 256;  // 256-column chunks of the longest row
-constexpr int kCap = 3584;               // candidate list capacity
+constexpr int kCap = 4096;               // candidate list capacity
+constexpr int kWaveCap = kCap / kSWaves;  // ... in each wave's quarter
 constexpr int kBatch = 8;                // chunk loads in flight per wave
 static_assert(kMaxChunks == kSThreads, "one thread per chunk in the output walk");
 static_assert(kBins >= DSA_MAX_TOPK, "the histogram holds the staged output of a row");
@@ -451,13 +455,13 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
   constexpr int NT = kSThreads;
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t s_ckey[kCap];
-  __shared__ uint16_t s_ccol[kCap];        // column within the row (< 65536)
+  __shared__ uint8_t s_ccol[kCap];         // column within its 256-column chunk
   __shared__ uint16_t s_cbase[kMaxChunks];  // chunk -> first candidate slot
   __shared__ uint16_t s_ccnt[kMaxChunks + 1];  // chunk -> candidate count, later its start
   __shared__ uint32_t s_wave[kSWaves];
   __shared__ uint32_t s_red[kSWaves];
   __shared__ uint32_t s_sel[2];
-  __shared__ uint32_t s_cnt;
+  __shared__ uint32_t s_wcnt[kSWaves];     // candidates of each wave's quarter
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -560,8 +564,10 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
   // ---- 2. one streaming pass: candidates (score >= lo) by chunk ----
   // key >= lo_key <=> score >= lo_f for every non-NaN score
   const float lo_f = lo_key == 1u ? -__builtin_inff() : key_to_float(lo_key);
-  if (tid == 0) s_cnt = 0u;
-  __syncthreads();
+  // Each wave appends the candidates of its chunks to its own quarter of
+  // the list, counting in a register: no shared counter, no broadcast.
+  const uint32_t wbase = (uint32_t)(wave * kWaveCap);
+  uint32_t wcnt = 0;  // uniform; keeps counting past the quarter (overflow)
   for (int c0 = wave; c0 < nchunks; c0 += kSWaves * kBatch) {
     if (c0 != wave) load_batch(c0);  // the first batch is already in flight
 #pragma unroll
@@ -578,44 +584,56 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
           below += popc_below(bal[e]);
           cnt += __popcll(bal[e]);
         }
-        uint32_t slot = 0;
-        if (cnt > 0u) {  // uniform
-          if (lane == 0) slot = atomicAdd(&s_cnt, cnt);
-          slot = __shfl(slot, 0, 64);
-          if (slot + cnt <= (uint32_t)kCap) {
-            uint32_t pos = slot + below;
+        const uint32_t slot = wbase + wcnt;
+        if (cnt > 0u && wcnt + cnt <= (uint32_t)kWaveCap) {  // uniform
+          uint32_t pos = slot + below;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if ((bal[e] >> lane) & 1u) {
-                s_ckey[pos] = float_to_key(x[e]);
-                s_ccol[pos] = (uint16_t)(col + e);
-                ++pos;
-              }
-          }
+          for (int e = 0; e < 4; ++e)
+            if ((bal[e] >> lane) & 1u) {
+              s_ckey[pos] = float_to_key(x[e]);
+              s_ccol[pos] = (uint8_t)(4 * lane + e);
+              ++pos;
+            }
         }
         if (lane == 0) {
-          s_cbase[ch] = (uint16_t)(slot < (uint32_t)kCap ? slot : 0u);
+          s_cbase[ch] = (uint16_t)(wcnt + cnt <= (uint32_t)kWaveCap ? slot : 0u);
           s_ccnt[ch] = (uint16_t)cnt;
         }
+        wcnt += cnt;
       }
     }
   }
+  if (lane == 0) s_wcnt[wave] = wcnt;
   __syncthreads();
-  const uint32_t ccount = s_cnt;
+  uint32_t ccount = 0;
+  bool spill = false;  // some quarter overflowed
+#pragma unroll
+  for (int w = 0; w < kSWaves; ++w) {
+    ccount += s_wcnt[w];
+    spill |= s_wcnt[w] > (uint32_t)kWaveCap;
+  }
+  // f(key) for every candidate of the calling thread (the quarters in turn)
+  auto for_cands = [&](auto&& f) {
+#pragma unroll
+    for (int w = 0; w < kSWaves; ++w) {
+      const int cw = (int)s_wcnt[w];
+      for (int i = tid; i < cw; i += NT) f(s_ckey[w * kWaveCap + i]);
+    }
+  };
 
   uint32_t theta, need_eq;
   const Placer place{0u, 0u, (uint32_t)k, out_idx, out_val};
-  if (ccount >= (uint32_t)k && ccount <= (uint32_t)kCap) {  // uniform
+  if (ccount >= (uint32_t)k && !spill) {  // uniform
     const int nc = (int)ccount;
     // ---- 3. theta among the candidates ----
     uint32_t cmax = 0;
-    for (int i = tid; i < nc; i += NT) cmax = max(cmax, s_ckey[i]);
+    for_cands([&](uint32_t key) { cmax = max(cmax, key); });
     cmax = block_max<kSWaves>(cmax, s_red);
     const float span = key_to_float(cmax) - lo_f;
     const LinearBuckets cb{lo_f, span > 0.0f ? (float)kBins / span : 0.0f};
     for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
     __syncthreads();
-    for (int i = tid; i < nc; i += NT) atomicAdd(&hist[cb(s_ckey[i])], 1u);
+    for_cands([&](uint32_t key) { atomicAdd(&hist[cb(key)], 1u); });
     __syncthreads();
     find_bucket_s((uint32_t)k);
     const int bstar = (int)s_sel[0];
@@ -624,13 +642,12 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
     // Members of bucket b* into a small list (order does not matter here).
     if (tid == 0) s_sel[1] = 0u;
     __syncthreads();
-    for (int i = tid; i < nc; i += NT) {
-      const uint32_t key = s_ckey[i];
+    for_cands([&](uint32_t key) {
       if (cb(key) == bstar) {
         const uint32_t at = atomicAdd(&s_sel[1], 1u);
         if (at < 64u) hist[at] = key;  // the histogram is no longer needed
       }
-    }
+    });
     __syncthreads();
     const uint32_t m = s_sel[1];
     if (m <= 64u) {  // uniform: rank the members against each other in one wave
@@ -653,10 +670,9 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
       __syncthreads();
     } else {
       theta = radix_select<kSWaves>(rem, hist, s_wave, s_sel, &need_eq, [&](auto&& f) {
-        for (int i = tid; i < nc; i += NT) {
-          const uint32_t key = s_ckey[i];
+        for_cands([&](uint32_t key) {
           if (cb(key) == bstar) f(key);
-        }
+        });
       });
     }
 
@@ -681,7 +697,7 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
       if ((int)s_ccnt[mid] <= p0) lo = mid; else hi = mid - 1;
     }
     const int ch0 = lo;
-    // f(slot) for the thread's positions in order
+    // f(slot, chunk) for the thread's positions in order
     auto walk = [&](auto&& f) {
       int ch = ch0, cend = s_ccnt[ch + 1];
       int slot = s_cbase[ch] + (p0 - (int)s_ccnt[ch]);
@@ -691,11 +707,11 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
           cend = s_ccnt[ch + 1];
           slot = s_cbase[ch];
         }
-        f(slot);
+        f(slot, ch);
       }
     };
     uint32_t ngt = 0, neq = 0;
-    walk([&](int slot) {
+    walk([&](int slot, int) {
       const uint32_t key = s_ckey[slot];
       ngt += key > theta;
       neq += key == theta;
@@ -706,7 +722,7 @@ __global__ __launch_bounds__(kSThreads) void topk_stream_kernel(
     const bool staged = !out_val && (k & 3) == 0 && ((uintptr_t)out_idx & 15u) == 0;
     const Placer pl{theta, need_eq, (uint32_t)k, staged ? reinterpret_cast<int32_t*>(hist) : out_idx,
                     out_val};
-    walk([&](int slot) { pl(s_ckey[slot], base + (int32_t)s_ccol[slot], g, q); });
+    walk([&](int slot, int ch) { pl(s_ckey[slot], base + 256 * ch + (int32_t)s_ccol[slot], g, q); });
     if (staged) {
       __syncthreads();
       for (int i = 4 * tid; i < k; i += 4 * NT)
