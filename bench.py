@@ -73,8 +73,8 @@ def parse():
                    help="also time dsa_sparse_attn_bwd on the forward's outputs (shared latent KV "
                         "workloads), reported as its own stage")
     p.add_argument("--fused", action="store_true",
-                   help="one combined indexer + top-K launch instead of score chunks + dsa_topk "
-                        "(rows of <= 4096 columns)")
+                   help="dsa_indexer_topk_fused instead of score chunks + dsa_topk (no dense "
+                        "scores: on chip up to 4096 columns, a candidate buffer beyond)")
     p.add_argument("--flush-steps", type=int, default=5,
                    help="extra steps, each after writing 512 MiB so that the 256 MB MALL holds "
                         "none of the step's inputs, reported as stages_flushed (0: none)")
@@ -469,8 +469,13 @@ def main():
 
     rs, sl = metadata()
     fused = has_indexer and args.fused
-    if fused and max_len > dsa.DSA_FUSED_MAX_COLS:
-        raise SystemExit(f"--fused takes rows of at most {dsa.DSA_FUSED_MAX_COLS} columns")
+    long_fused = fused and max_len > dsa.DSA_FUSED_MAX_COLS
+    if long_fused and fp8:
+        raise SystemExit(f"--fused takes FP8 rows of at most {dsa.DSA_FUSED_MAX_COLS} columns")
+    cand = None
+    if long_fused:  # allocated once, outside the timed steps
+        cand = torch.empty((dsa.dsa_indexer_topk_cand_buffer_size(T, max_len, K),),
+                           dtype=torch.float32, device=dev)
     if fp8:
         fp8_scaling = dsa.DSA_MXFP8 if fp8["scaling"] == "mx" else dsa.DSA_FP8_PER_TOKEN
     rows_per_chunk = dsa.chunk_rows(T, max_len)
@@ -512,7 +517,7 @@ def main():
             else:
                 run("indexer_topk_fused", lambda: dsa.dsa_indexer_topk_fused(
                     wl.q_idx, wl.k_idx, wl.w, rs, sl, K, max_len, indices=indices,
-                    topk_length=topk_length))
+                    topk_length=topk_length, cand_buffer=cand))
         elif has_indexer:
             for r0 in range(0, T, rows_per_chunk):
                 n = min(rows_per_chunk, T - r0)
@@ -597,10 +602,15 @@ def main():
         idx_peak = PEAK_FP8_TFLOPS if fp8 else PEAK_BF16_TFLOPS
         if fused:
             ms, n = st["indexer_topk_fused"]
-            stages["indexer_topk_fused"] = {"ms": ms, "launches": n}
+            stages["indexer_topk_fused"] = {"ms": ms, "calls": n,
+                                            "candidate_buffer": long_fused}
+            if long_fused:
+                stages["indexer_topk_fused"]["rows_rescued"] = int(
+                    cand[:1].view(torch.int32).item())
             rooflines["indexer_topk_fused"] = roofline_entry(
-                "indexer_kernel (combined with top-K)", "mfma", cnt["indexer_flop"], n, ms,
-                idx_peak, "TFLOP/s", None)
+                "indexer_kernel (candidate mode) + topk_radix_kernel (candidates) + "
+                "indexer_rescue_kernel" if long_fused else "indexer_kernel (combined with top-K)",
+                "mfma", cnt["indexer_flop"], n, ms, idx_peak, "TFLOP/s", None)
         else:
             ims, n_i = st["indexer"]
             tms, n_t = st["topk"]

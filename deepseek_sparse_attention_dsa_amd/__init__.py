@@ -26,7 +26,7 @@ __all__ = [
     "dsa_packed_metadata", "dsa_ratio_causal_metadata", "dsa_indexer_fwd",
     "dsa_indexer_fwd_fp8", "DSA_FP8_PER_TOKEN", "DSA_MXFP8", "dsa_topk",
     "dsa_topk_workspace_bytes",
-    "dsa_indexer_topk_fused", "DSA_FUSED_MAX_COLS",
+    "dsa_indexer_topk_fused", "dsa_indexer_topk_cand_buffer_size", "DSA_FUSED_MAX_COLS",
     "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_workspace_bytes",
     "indexer_topk", "chunk_rows",
 ]
@@ -58,8 +58,9 @@ _SIGNATURES = {
     "dsa_indexer_fwd_fp8": ([_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I64, _I64, _I32, _I32,
                              _I64, _I64, _P, _I64, _P], ctypes.c_int),
     "dsa_indexer_topk_fused": ([_P, _P, _P, _P, _I32, _P, _I32, _P, _P, _I64, _I64, _I32, _I32,
-                                _I64, _I64, _I64, _I32, _P, _I64, _P, _P, _P, _P, _P],
-                               ctypes.c_int),
+                                _I64, _I64, _I64, _I32, _P, _I64, _P, _P, _P, _P, _P, _I64,
+                                _P], ctypes.c_int),
+    "dsa_indexer_topk_cand_buffer_size": ([_I64, _I64, _I32], ctypes.c_int64),
     "dsa_topk": ([_P, _I64, _I64, _I64, _P, _P, _I32, _P, _I64, _P, _P, _P], ctypes.c_int),
     "dsa_topk_workspace_bytes": ([_I64, _I64, _I32], ctypes.c_int64),
     "dsa_sparse_attn_bwd_workspace_bytes": ([_I64, _I32, _I64, _I32, _I32], ctypes.c_int64),
@@ -421,12 +422,17 @@ def dsa_indexer_topk_fused(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Te
                            fp8_scaling: Optional[int] = None, row_begin: int = 0,
                            n_rows: Optional[int] = None, indices: Optional[torch.Tensor] = None,
                            topk_length: Optional[torch.Tensor] = None, return_logits: bool = False,
-                           return_softmax: bool = False, return_lse: bool = False, stream=None):
-    """Indexer scores + top-k in one launch (rows of at most 4096 columns).
+                           return_softmax: bool = False, return_lse: bool = False,
+                           cand_buffer: Optional[torch.Tensor] = None, stream=None):
+    """Indexer scores + top-k without dense scores.
 
     Returns (indices int32 [n_rows, k], topk_length int32 [n_rows], logits |
     None, softmax | None, lse | None). bf16 q_idx / k_idx, or FP8 ones with
-    q_scale, k_scale and fp8_scaling as dsa_indexer_fwd_fp8 takes them.
+    q_scale, k_scale and fp8_scaling as dsa_indexer_fwd_fp8 takes them (FP8
+    only for n_cols <= DSA_FUSED_MAX_COLS). Rows longer than
+    DSA_FUSED_MAX_COLS go through the candidate path and need cand_buffer, a
+    float32 device tensor of dsa_indexer_topk_cand_buffer_size(n_rows,
+    n_cols, k) elements (allocated when None).
     """
     if not isinstance(w, torch.Tensor) or w.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError(f"w must be a bfloat16 or float32 tensor (got {getattr(w, 'dtype', w)})")
@@ -475,13 +481,27 @@ def dsa_indexer_topk_fused(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Te
     softmax = (torch.empty((n_rows, ld), dtype=torch.float32, device=dev)[:, :k]
                if return_softmax else None)
     lse = torch.empty((n_rows,), dtype=torch.float32, device=dev) if return_lse else None
+    need = dsa_indexer_topk_cand_buffer_size(n_rows, int(n_cols), int(k))
+    if need > 0 and cand_buffer is None:
+        cand_buffer = torch.empty((need,), dtype=torch.float32, device=dev)
+    elif cand_buffer is not None:
+        cand_buffer = _out(cand_buffer, "cand_buffer", torch.float32, dev)
     lib = load_library()
     _check(lib.dsa_indexer_topk_fused(
         _ptr(q_idx), _ptr(q_scale) if fp8 else None, _ptr(k_idx), _ptr(k_scale) if fp8 else None,
         precision, _ptr(w), DSA_BF16 if w.dtype == torch.bfloat16 else DSA_F32, _ptr(row_starts),
         _ptr(seq_lens), T, T_kv, H, D, row_begin, n_rows, int(n_cols), int(k), _ptr(indices), ld,
-        _ptr(topk_length), _ptr(logits), _ptr(softmax), _ptr(lse), _stream(stream)))
+        _ptr(topk_length), _ptr(logits), _ptr(softmax), _ptr(lse), _ptr(cand_buffer),
+        0 if cand_buffer is None else cand_buffer.numel(), _stream(stream)))
     return indices, topk_length, logits, softmax, lse
+
+
+def dsa_indexer_topk_cand_buffer_size(n_rows: int, n_cols: int, k: int) -> int:
+    """Floats of the candidate buffer dsa_indexer_topk_fused needs (0: none)."""
+    n = int(load_library().dsa_indexer_topk_cand_buffer_size(n_rows, n_cols, k))
+    if n < 0:
+        raise ValueError("sizes out of contract for dsa_indexer_topk_fused")
+    return n
 
 
 def dsa_sparse_attn_bwd_workspace_bytes(T_q: int, H: int, T_kv: int, D_qk: int,
@@ -577,10 +597,11 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
     FP8 inputs (q_idx / k_idx as uint8 or float8_e4m3fn) take q_scale,
     k_scale and fp8_scaling as dsa_indexer_fwd_fp8 does.
     fused=True (or return_softmax=True) replaces the score chunks by one
-    dsa_indexer_topk_fused launch (rows of at most DSA_FUSED_MAX_COLS
-    columns, no score buffer); only that path gives return_softmax, which
-    returns (indices, topk_length, logits, softmax, lse). The score-chunk
-    path is the default: on MI355X it is the faster of the two.
+    dsa_indexer_topk_fused call (no score buffer: rows of at most
+    DSA_FUSED_MAX_COLS columns stay on chip, longer bf16 rows go through a
+    candidate buffer); only that path gives return_softmax, which returns
+    (indices, topk_length, logits, softmax, lse). The score-chunk path is
+    the default.
     """
     fp8 = q_idx.dtype in (torch.uint8, torch.float8_e4m3fn)
     if fp8 and (q_scale is None or k_scale is None or fp8_scaling is None):
@@ -600,11 +621,11 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
     if fused is None:
         fused = return_softmax
     if return_softmax and not fused:
-        raise ValueError("return_softmax needs the fused path (rows of at most "
-                         f"{DSA_FUSED_MAX_COLS} columns)")
+        raise ValueError("return_softmax needs the fused path")
     if fused:
-        if width > DSA_FUSED_MAX_COLS:
-            raise ValueError(f"the fused path takes rows of at most {DSA_FUSED_MAX_COLS} columns")
+        if width > DSA_FUSED_MAX_COLS and fp8:
+            raise ValueError(f"the fused path takes FP8 rows of at most {DSA_FUSED_MAX_COLS} "
+                             "columns")
         res = dsa_indexer_topk_fused(q_idx, k_idx, w, row_starts, seq_lens, k, max(width, 1),
                                      q_scale=q_scale, k_scale=k_scale, fp8_scaling=fp8_scaling,
                                      return_logits=return_softmax, return_softmax=return_softmax,

@@ -189,13 +189,41 @@ int dsa_indexer_fwd_fp8(const void* q8, const void* q_scale, const void* k8, con
                                               (hipStream_t)stream));
 }
 
+// Layout of the candidate buffer of the combined path for long rows, in
+// 4-byte words: the queue length, the per-row counts and the queue, the
+// rescue's dense rows, then the candidate lists (16-byte aligned).
+struct CandLayout {
+  int64_t count, queue, spill, spill_ld, n_spill, cand, total;
+};
+static CandLayout cand_layout(int64_t n_rows, int64_t n_cols) {
+  CandLayout L;
+  auto up4 = [](int64_t x) { return (x + 3) / 4 * 4; };
+  L.count = 4;
+  L.queue = L.count + up4(n_rows);
+  L.spill = L.queue + up4(n_rows);
+  L.spill_ld = up4(n_cols);
+  L.n_spill = std::min<int64_t>(dsa::kCandSpillRows, n_rows);
+  L.cand = L.spill + L.n_spill * L.spill_ld;
+  L.total = L.cand + n_rows * dsa::kCandCap * 2;
+  return L;
+}
+
+int64_t dsa_indexer_topk_cand_buffer_size(int64_t n_rows, int64_t n_cols, int32_t k) {
+  if (n_rows < 0 || n_rows > INT32_MAX || n_cols < 1 || n_cols > DSA_TOPK_MAX_COLS || k < 1 ||
+      k > DSA_MAX_TOPK)
+    return -1;
+  if (n_cols <= DSA_FUSED_MAX_COLS || n_rows == 0) return 0;
+  return cand_layout(n_rows, n_cols).total;
+}
+
 int dsa_indexer_topk_fused(const void* q_idx, const void* q_scale, const void* k_idx,
                            const void* k_scale, int32_t precision, const void* w,
                            int32_t w_dtype, const int32_t* row_starts, const int32_t* seq_lens,
                            int64_t T, int64_t T_kv, int32_t H_idx, int32_t D_idx,
                            int64_t row_begin, int64_t n_rows, int64_t n_cols, int32_t k,
                            int32_t* indices, int64_t ld_indices, int32_t* topk_length,
-                           float* logits, float* softmax, float* lse, void* stream) {
+                           float* logits, float* softmax, float* lse, float* cand_buffer,
+                           int64_t cand_floats, void* stream) {
   const char* fn = "dsa_indexer_topk_fused";
   REQUIRE(w_dtype == DSA_BF16 || w_dtype == DSA_F32, DSA_ERR_TYPE,
           "%s: w_dtype must be DSA_BF16 or DSA_F32 (got %d)", fn, w_dtype);
@@ -212,13 +240,26 @@ int dsa_indexer_topk_fused(const void* q_idx, const void* q_scale, const void* k
   REQUIRE(row_begin >= 0 && n_rows >= 0 && row_begin + n_rows <= T, DSA_ERR_VALUE,
           "%s: rows [%lld, %lld) outside [0, T=%lld)", fn, (long long)row_begin,
           (long long)(row_begin + n_rows), (long long)T);
-  REQUIRE(n_cols >= 1 && n_cols <= DSA_FUSED_MAX_COLS, DSA_ERR_VALUE,
-          "%s: n_cols must be in [1, %d] (got %lld)", fn, DSA_FUSED_MAX_COLS, (long long)n_cols);
+  REQUIRE(n_cols >= 1 && n_cols <= DSA_TOPK_MAX_COLS, DSA_ERR_VALUE,
+          "%s: n_cols must be in [1, %d] (got %lld)", fn, DSA_TOPK_MAX_COLS, (long long)n_cols);
   REQUIRE(k >= 1 && k <= DSA_MAX_TOPK, DSA_ERR_VALUE, "%s: k must be in [1, %d] (got %d)", fn,
           DSA_MAX_TOPK, k);
   REQUIRE(ld_indices >= k, DSA_ERR_VALUE, "%s: ld_indices (%lld) < k (%d)", fn,
           (long long)ld_indices, k);
+  const bool long_rows = n_cols > DSA_FUSED_MAX_COLS;
+  REQUIRE(!long_rows || !fp8, DSA_ERR_VALUE,
+          "%s: rows longer than %d columns take bf16 inputs (DSA_INDEXER_BF16)", fn,
+          DSA_FUSED_MAX_COLS);
   if (n_rows == 0) return DSA_OK;
+  if (long_rows) {
+    const int64_t need = dsa_indexer_topk_cand_buffer_size(n_rows, n_cols, k);
+    REQUIRE(cand_buffer && cand_floats >= need, DSA_ERR_VALUE,
+            "%s: n_cols = %lld needs a candidate buffer of %lld floats "
+            "(dsa_indexer_topk_cand_buffer_size; got %lld)",
+            fn, (long long)n_cols, (long long)need, (long long)cand_floats);
+    REQUIRE(aligned(cand_buffer, 16), DSA_ERR_VALUE, "%s: cand_buffer must be 16-byte aligned",
+            fn);
+  }
   REQUIRE(q_idx && (k_idx || T_kv == 0) && w && row_starts && seq_lens && indices &&
               (!fp8 || (q_scale && (k_scale || T_kv == 0))),
           DSA_ERR_VALUE, "%s: NULL pointer argument", fn);
@@ -230,6 +271,33 @@ int dsa_indexer_topk_fused(const void* q_idx, const void* q_scale, const void* k
   if (int rc = check_device(fn)) return rc;
   // (T_kv = 0: every row is empty; the kernels then load no key.)
   dsa::FusedArgs fa{k, indices, ld_indices, topk_length, logits, softmax, lse};
+  if (long_rows) {
+    // Stage 1 (indexer pass appending candidates), stage 2 (select from the
+    // candidates; rows they cannot serve are queued), rescue (queued rows).
+    const CandLayout L = cand_layout(n_rows, n_cols);
+    uint32_t* buf = reinterpret_cast<uint32_t*>(cand_buffer);
+    dsa::CandArgs ca{buf + L.cand,
+                     dsa::kCandCap,
+                     reinterpret_cast<int32_t*>(buf + L.count),
+                     reinterpret_cast<int32_t*>(buf + L.queue),
+                     buf,
+                     cand_buffer + L.spill,
+                     L.spill_ld,
+                     (int)L.n_spill};
+    hipStream_t st = (hipStream_t)stream;
+    if (int rc = launched(fn, dsa::launch_indexer_cand(q_idx, k_idx, w, w_dtype, row_starts,
+                                                       seq_lens, T_kv, H_idx, D_idx, row_begin,
+                                                       n_rows, n_cols, k, ca, st)))
+      return rc;
+    const int64_t n_eff = T_kv > 0 ? n_cols : 0;
+    if (int rc = launched(fn, dsa::launch_topk_cand(seq_lens + row_begin, row_starts + row_begin,
+                                                    n_rows, n_eff, k, indices, ld_indices,
+                                                    topk_length, logits, softmax, lse, ca, st)))
+      return rc;
+    return launched(fn, dsa::launch_indexer_rescue(q_idx, k_idx, w, w_dtype, row_starts, seq_lens,
+                                                   T_kv, H_idx, D_idx, row_begin, n_rows, n_cols,
+                                                   fa, ca, st));
+  }
   if (fp8)
     return launched(fn, dsa::launch_indexer_topk_fp8(q_idx, q_scale, k_idx, k_scale,
                                                      precision == DSA_INDEXER_MXFP8, w, w_dtype,

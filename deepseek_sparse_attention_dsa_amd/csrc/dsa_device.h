@@ -232,6 +232,10 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   v = wave_incl_scan_dpp(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; }, 0xffffffffu);
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  v = wave_incl_scan_dpp(v, [](uint32_t a, uint32_t b) { return a + b; }, 0u);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
 __device__ __forceinline__ float wave_sum_f32(float v) {
   const uint32_t s = wave_incl_scan_dpp(
       __float_as_uint(v),

@@ -39,6 +39,40 @@ hipError_t launch_indexer_topk_fp8(const void* q, const void* qs, const void* k,
                                    int64_t n_rows, int64_t n_cols, const FusedArgs& fa,
                                    hipStream_t st);
 
+// Caller-owned buffer of the combined indexer + top-k for rows longer than
+// the on-chip path takes (DSA page section 4: candidates per row, then a
+// stage-2 select). Stage 1 (the indexer pass) appends each row's candidates;
+// stage 2 selects from them; rows whose list cannot hold their top k are
+// queued and redone by the rescue pass from recomputed dense scores.
+constexpr int64_t kCandCap = 8192;   // candidates kept per row
+constexpr int kCandSpillRows = 256;  // dense rows of the rescue pass (one per workgroup)
+struct CandArgs {
+  uint32_t* cand;      // [n_rows, kCandCap] (score bits, local column)
+  int64_t cap;         // kCandCap
+  int32_t* count;      // [n_rows] candidates found (also past cap)
+  int32_t* queue;      // [n_rows] rows queued for the rescue
+  uint32_t* n_queued;  // their number
+  float* spill;        // [n_spill, spill_ld] rescue score rows
+  int64_t spill_ld;
+  int n_spill;
+};
+
+// Stage 1: the indexer pass appending candidates (bf16 inputs).
+hipError_t launch_indexer_cand(const void* q, const void* k, const void* w, int w_dtype,
+                               const int32_t* rs, const int32_t* sl, int64_t T_kv, int H, int D,
+                               int64_t row_begin, int64_t n_rows, int64_t n_cols, int top_k,
+                               const CandArgs& ca, hipStream_t st);
+// Stage 2 (seq_lens and row_starts start at the first row).
+hipError_t launch_topk_cand(const int32_t* seq_lens, const int32_t* row_starts, int64_t n_rows,
+                            int64_t n_cols, int k, int32_t* indices, int64_t ld_idx,
+                            int32_t* topk_length, float* logits, float* softmax, float* lse,
+                            const CandArgs& ca, hipStream_t st);
+// Rescue of the queued rows.
+hipError_t launch_indexer_rescue(const void* q, const void* k, const void* w, int w_dtype,
+                                 const int32_t* rs, const int32_t* sl, int64_t T_kv, int H, int D,
+                                 int64_t row_begin, int64_t n_rows, int64_t n_cols,
+                                 const FusedArgs& fa, const CandArgs& ca, hipStream_t st);
+
 hipError_t launch_topk(const float* scores, int64_t ld, int64_t n_rows, int64_t n_cols,
                        const int32_t* seq_lens, const int32_t* row_starts, int k, int32_t* indices,
                        int64_t ld_idx, int32_t* topk_length, float* values, hipStream_t st);

@@ -21,6 +21,7 @@
 // first so the causal triangle's short rows fill the tail.
 #include "dsa_device.h"
 #include "dsa_launch.h"
+#include "dsa_rowsel.h"
 #include "dsa_select.h"
 
 namespace dsa {
@@ -103,17 +104,37 @@ __device__ __forceinline__ f32x4 load_w4<float>(const float* w, int64_t i) {
   return *reinterpret_cast<const f32x4*>(w + i);
 }
 
+// What the indexer pass does with the scores of its rows.
+enum : int {
+  kModeScores = 0,  // writes them to a dense score matrix
+  kModeFused = 1,   // keeps each row in LDS and selects its top-k there
+  kModeCand = 2,    // appends the columns at or above a per-row lower bound
+};
+constexpr int kSampleTiles = 8;  // key tiles sampled for the lower bound
+
 // D: indexer head dim (64 or 128). MB: number of 32-head blocks (H <= 32*MB).
-// FUSE: the scores of each row stay in LDS (ld is then the column cap, at
-// most kFuseMaxCols) and the wave selects its row's top-k into `fa` instead
-// of writing scores; with D = 128 the key tile is then single-buffered so
-// that eight 4096-column rows fit next to it.
-template <int D, int MB, typename WT, bool FUSE>
+// kModeFused: the scores of each row stay in LDS (ld is then the column cap,
+// at most kFuseMaxCols) and the wave selects its row's top-k into `fa`
+// instead of writing scores; with D = 128 the key tile is then
+// single-buffered so that eight 4096-column rows fit next to it.
+// kModeCand (stage 1 of the combined path for long rows; ld is the column
+// cap): when a row of the workgroup is longer than the candidate capacity,
+// kSampleTiles key tiles spread over the workgroup's key range are scored
+// first, and each such row takes as its lower bound lo the sample of rank
+// e + 6 sqrt(e) + 4 from the top, e = k * (valid samples) / (row length)
+// being the expected sample rank of the row's k-th largest score (about six
+// standard deviations of the sampling noise above it); shorter rows take
+// every column. The tile loop then appends each column whose score is at or
+// above lo to the row's candidate list as (order-preserving key, local
+// column), in column order, counting them all (also those past the cap).
+template <int D, int MB, typename WT, int MODE>
 __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const WT* __restrict__ w,
     const int32_t* __restrict__ row_starts, const int32_t* __restrict__ seq_lens, int64_t T_kv,
     int H, int64_t row_begin, int64_t n_rows, float* __restrict__ scores, int64_t ld,
-    FusedArgs fa, bool w_vec) {
+    FusedArgs fa, CandArgs ca, bool w_vec) {
+  constexpr bool FUSE = MODE == kModeFused;
+  constexpr bool CAND = MODE == kModeCand;
   constexpr int KS = D / 16;                      // MFMA k-steps over the head dim
   constexpr int ROW_B = 2 * D + 16;               // LDS row stride in bytes (16 B pad)
   // keys per LDS tile: 128 (one barrier per 128 keys); 64 when the rows'
@@ -126,6 +147,8 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
   constexpr int NBUF = (FUSE && D == 128) ? 1 : 2;  // key tiles in the LDS ring
   __shared__ __attribute__((aligned(16))) unsigned char ktile[NBUF * TILE_B];
   __shared__ __attribute__((aligned(16))) float s_rows[FUSE ? kIdxWaves * kFuseRowStride : 4];
+  // CAND: the sampled keys of each wave's row, lane-major (slot 64 i + lane)
+  __shared__ uint32_t s_samp[CAND ? kIdxWaves * 2 * kSampleTiles * 64 : 1];
   static_assert(!FUSE || NBUF * TILE_B >= kIdxWaves * 256 * 4, "select histograms fit the ring");
 
   const int lane = threadIdx.x & 63;
@@ -150,20 +173,26 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
     m_s0 = row_starts[tt];
     m_n = (int32_t)max((int64_t)0, min((int64_t)seq_lens[tt], cap));
   }
-  int32_t kb = m_n > 0 ? m_s0 : INT32_MAX, ke = m_n > 0 ? m_s0 + m_n : 0;
+  int32_t kb = m_n > 0 ? m_s0 : INT32_MAX, ke = m_n > 0 ? m_s0 + m_n : 0, nmax = m_n;
 #pragma unroll
   for (int m = 1; m < kIdxWaves; m <<= 1) {
     kb = min(kb, __shfl_xor(kb, m, kWave));
     ke = max(ke, __shfl_xor(ke, m, kWave));
+    nmax = max(nmax, __shfl_xor(nmax, m, kWave));
   }
   kb = __builtin_amdgcn_readfirstlane(kb);
   ke = __builtin_amdgcn_readfirstlane(ke);
+  nmax = __builtin_amdgcn_readfirstlane(nmax);
   const int32_t qstart = __shfl(m_s0, wave, kWave);
   const int32_t qlen = __shfl(m_n, wave, kWave);
+  if constexpr (CAND)
+    if (blockIdx.x == 0 && threadIdx.x == 0) *ca.n_queued = 0u;  // the stage-2 queue starts empty
   if (kb >= ke) {  // uniform: no row of the workgroup has a key
     if constexpr (FUSE)
       if (live)
         wave_topk_row(s_rows, 0, 0, nullptr, fa, r);  // writes the empty row
+    if constexpr (CAND)
+      if (live && lane == 0) ca.count[r] = 0;
     return;
   }
 
@@ -247,22 +276,56 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
   // check, so the tile loop has no branches.
   // (FUSE: the row lives in LDS; columns outside the row go to a spare slot.)
   const __amdgpu_buffer_rsrc_t srow =
-      raw_buffer(FUSE ? (const void*)scores : (const void*)(scores + r * ld),
-                 FUSE ? 0u : (uint32_t)qlen * 4u);
+      raw_buffer(MODE != kModeScores ? (const void*)scores : (const void*)(scores + r * ld),
+                 MODE != kModeScores ? 0u : (uint32_t)qlen * 4u);
   float* const lrow = s_rows + (FUSE ? wave * kFuseRowStride : 0);
+  // CAND: the row's lower bound and its candidates so far (wave-uniform),
+  // appended in column order as (score bits, local column) through a buffer
+  // descriptor of the row's cap entries: the hardware drops stores past the
+  // cap (the count still grows) and those of lanes that take nothing (an
+  // offset past the range). A score passes when its order-preserving signed
+  // form ord() is at least t_lo: the lower bound's form, INT32_MIN for
+  // every column, -1 for a bound of 0.0 (so that -0.0, form -1, passes).
+  int32_t t_lo = INT32_MIN;
+  uint32_t n_cand = 0u;
+  const __amdgpu_buffer_rsrc_t crow =
+      raw_buffer(CAND ? (const void*)(ca.cand + 2 * r * ca.cap) : (const void*)scores,
+                 CAND ? (uint32_t)(ca.cap * 8) : 0u);
+  auto ord = [](uint32_t b) -> int32_t {
+    return (int32_t)(b ^ ((uint32_t)((int32_t)b >> 31) >> 1));
+  };
+  // one column per lane: local column j of the row, its score's bits
+  auto append = [&](uint32_t bits, uint32_t j) {
+    const bool take = j < (uint32_t)qlen && ord(bits) >= t_lo;
+    const uint64_t tm = ballot(take);
+    const uint32_t off = take ? (n_cand + popc_below(tm)) * 8u : 0x80000000u;
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{bits, j}, crow, (int)off, 0, 0);
+    n_cand += (uint32_t)__popcll(tm);
+  };
   auto write_scores = [&](int32_t k0, float p0, float p1) {
     const float score = halfwave_sums(p0, p1);
     const uint32_t j = (uint32_t)(k0 + lane - qstart);
-    if constexpr (FUSE)
+    if constexpr (FUSE) {
       lrow[j < (uint32_t)qlen ? j : (uint32_t)kFuseMaxCols] = score;
-    else
+    } else if constexpr (CAND) {
+      append(__float_as_uint(score), j);
+    } else {
       buffer_store_f32(score, srow, j * 4u);  // negative: dropped
+    }
+  };
+
+  // CAND: whether the workgroup samples (a row longer than the capacity),
+  // and the first key of sample tile i (tiles of the workgroup's range).
+  const bool sample = CAND && nmax > (int32_t)ca.cap;  // uniform
+  const int32_t n_tiles = (ke - kb + TILE - 1) / TILE;
+  auto sample_start = [&](int i) -> int32_t {
+    return kb + TILE * (int32_t)(((int64_t)i * n_tiles) / kSampleTiles);
   };
 
   // Every wave runs every tile of the workgroup's key range (a row's keys
   // outside its own range are computed and their stores dropped). The first
   // pending write targets columns before the row, so it is dropped too.
-  load_tile(kb);
+  load_tile(sample ? sample_start(0) : kb);
 
   // This wave's query: Q fragments (A operand: lane -> head 32*mb + l%32,
   // dims 16*ks + 8*half .. +7) and the weights of the 16 heads whose scores
@@ -308,11 +371,85 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
 
   store_tile(0);
   __syncthreads();
+  // CAND: the sample tiles are scored once; the tile loop skips them and
+  // appends their saved keys in their place. Sample tile 0 is the range's
+  // first tile, the others are at least 8 tiles apart (a sampling workgroup
+  // has more than 64 tiles).
+  uint32_t* const wsamp = s_samp + (CAND ? wave * 2 * kSampleTiles * 64 + lane : 0);
+  auto append_saved = [&](int i) {
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp)
+      append(wsamp[64 * (2 * i + hp)],
+             (uint32_t)(sample_start(i) + kIdxHalf * hp + lane - qstart));
+  };
+  if constexpr (CAND) {
+    if (sample) {  // uniform
+      // The sample tiles go through the ring in turn (the last prefetch is
+      // the tile loop's first tile, the one after sample tile 0, which lands
+      // in buffer 0); lane l keeps the scores of keys s + l and s + 64 + l of
+      // each sample tile s in the wave's LDS slots.
+      static_assert(TILE == 2 * kIdxHalf && NBUF == 2 && kSampleTiles % 2 == 0, "sample layout");
+#pragma unroll 1
+      for (int i = 0; i < kSampleTiles; ++i) {
+        load_tile(i + 1 < kSampleTiles ? sample_start(i + 1) : kb + TILE);
+        const unsigned char* kt = ktile + (i & 1) * TILE_B;
+        const int32_t s0 = sample_start(i);
+#pragma unroll
+        for (int hp = 0; hp < 2; ++hp) {
+          block_mfma(kt, 2 * hp, acc0);
+          block_mfma(kt, 2 * hp + 1, acc1);
+          const float score = halfwave_sums(epilogue(acc0), epilogue(acc1));
+          const uint32_t j = (uint32_t)(s0 + kIdxHalf * hp + lane - qstart);
+          // (invalid: all-ones bits, whose key is 0)
+          wsamp[64 * (2 * i + hp)] = j < (uint32_t)qlen ? __float_as_uint(score) : 0xffffffffu;
+        }
+        store_tile((i + 1) & 1);
+        __syncthreads();
+      }
+      // The tile loop's first pending epilogue reads acc1 (its write is
+      // dropped); zeroed, the accumulators hold nothing across the search.
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc0[mb][i] = acc1[mb][i] = 0.0f;
+      if (qlen > (int32_t)ca.cap) {  // uniform per wave
+        uint32_t samp[2 * kSampleTiles];
+#pragma unroll
+        for (int i = 0; i < 2 * kSampleTiles; ++i)
+          samp[i] = fused_key(__uint_as_float(wsamp[64 * i]));
+        uint32_t nv = 0u;
+#pragma unroll
+        for (int i = 0; i < 2 * kSampleTiles; ++i) nv += samp[i] != 0u ? 1u : 0u;
+        nv = wave_sum_u32(nv);
+        const float e = (float)fa.k * (float)nv / (float)qlen;
+        const uint32_t rank = (uint32_t)ceilf(e + 6.0f * sqrtf(e) + 4.0f);
+        if (nv >= rank) {
+          // lo = the largest key v with at least `rank` samples >= v
+          uint32_t v = 0u;
+#pragma unroll 1
+          for (int b = 31; b >= 0; --b) {
+            const uint32_t c = v | (1u << b);
+            uint32_t n_ge = 0u;
+#pragma unroll
+            for (int i = 0; i < 2 * kSampleTiles; ++i) n_ge += samp[i] >= c ? 1u : 0u;
+            if (wave_sum_u32(n_ge) >= rank) v = c;
+          }
+          t_lo = v == fused_key(0.0f) ? -1 : ord(__float_as_uint(fused_value(v)));
+        }
+      }
+      append_saved(0);
+    }
+  }
   int buf = 0;
   int32_t pend_k0 = qstart - 64;  // the second block of the pair at pend_k0 awaits its epilogue
   float pend_p0 = 0.0f;           // its block-0 partial
-  for (int32_t k0 = kb; k0 < ke; k0 += TILE) {
-    load_tile(k0 + TILE);  // zeroed past the range, so the last one is harmless
+  int ns = 1;                     // CAND: the next sample tile the loop has not passed
+  int32_t ns_start = sample ? sample_start(1) : INT32_MAX;
+  for (int32_t k0 = sample ? kb + TILE : kb; k0 < ke;) {
+    int32_t k_next = k0 + TILE;
+    if constexpr (CAND)
+      if (k_next == ns_start) k_next += TILE;  // uniform
+    load_tile(k_next);  // zeroed past the range, so the last one is harmless
     const unsigned char* kt = ktile + buf * TILE_B;
     // Each group pairs a block's MFMAs with the previous block's epilogue;
     // the fences keep the scheduler from filling the VALU slots with the
@@ -340,6 +477,16 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
       }
     }
 
+    if constexpr (CAND) {
+      if (k0 + TILE == ns_start) {  // uniform: a sample tile comes next
+        write_scores(pend_k0, pend_p0, epilogue(acc1));
+        append_saved(ns);
+        pend_k0 = qstart - 64;  // the next tile's first pending write is dropped
+        ++ns;
+        ns_start = ns < kSampleTiles ? sample_start(ns) : INT32_MAX;
+      }
+    }
+
     if constexpr (NBUF == 2) {
       store_tile(buf ^ 1);
       __syncthreads();
@@ -349,8 +496,11 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
       store_tile(0);
       __syncthreads();
     }
+    k0 = k_next;
   }
   write_scores(pend_k0, pend_p0, epilogue(acc1));
+  if constexpr (CAND)
+    if (live && lane == 0) ca.count[r] = (int32_t)n_cand;
   if constexpr (FUSE) {
     __syncthreads();  // the tile ring is free: it holds the select histograms now
     if (live)
@@ -359,11 +509,177 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
   }
 }
 
-template <int D, int MB, bool FUSE>
+// Rescue pass of the combined path for long rows: the rows whose candidate
+// list could not hold their top k (too few or too many candidates, queued by
+// stage 2). Workgroup g takes queued rows g, g + G, ... (G workgroups); for
+// each it recomputes the row's dense scores into its own spill row, with the
+// arithmetic of the indexer pass (per 32-key block the MFMA chain over the
+// head dim from zero, the ReLU * weight chain over the heads in the same
+// order, the same half-wave sum, so every score is bit-identical to the
+// pass's), then selects exactly from them: theta by radix passes over the
+// row, then each thread counts its run of columns above and equal to theta
+// and, after a scan of the counts, places its selected columns.
+template <int D, int MB, typename WT>
+__global__ __launch_bounds__(kIdxWaves * 64) void indexer_rescue_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const WT* __restrict__ w,
+    const int32_t* __restrict__ row_starts, const int32_t* __restrict__ seq_lens, int64_t T_kv,
+    int H, int64_t row_begin, int64_t n_cols, FusedArgs fa, CandArgs ca, bool w_vec) {
+  constexpr int KS = D / 16;
+  constexpr int NT = kIdxWaves * 64;
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t s_wave[kIdxWaves];
+  __shared__ uint32_t s_sel[2];
+  __shared__ float s_fsum[kIdxWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const uint32_t n_queued = *ca.n_queued;
+  float* const spill = ca.spill + (int64_t)blockIdx.x * ca.spill_ld;
+  const int64_t col_cap = T_kv > 0 ? n_cols : 0;
+
+  auto block_sum = [&](float v) -> float {
+    v = wave_sum_f32(v);
+    if (lane == 0) s_fsum[wave] = v;
+    __syncthreads();
+    v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kIdxWaves; ++i) v += s_fsum[i];
+    __syncthreads();
+    return v;
+  };
+
+  for (uint32_t qi = blockIdx.x; qi < n_queued; qi += gridDim.x) {
+    const int64_t r = ca.queue[qi];
+    const int64_t t = row_begin + r;
+    const int32_t s0 = row_starts[t];
+    const int n = (int)max((int64_t)0, min((int64_t)seq_lens[t], col_cap));
+
+    // Query fragments and weights as the indexer pass loads them.
+    u32x4 qa[MB][KS];
+    float wv[MB][16];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int head = mb * 32 + (lane & 31);
+      const int hq = head < H ? head : H - 1;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qa[mb][ks] = head < H ? load16(q + ((t * H + hq) * D + ks * 16 + 8 * half))
+                              : u32x4{0u, 0u, 0u, 0u};
+      if (w_vec) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int oh0 = mb * 32 + 8 * j + 4 * half;
+          const f32x4 v = load_w4<WT>(w, t * H + (oh0 < H ? oh0 : 0));
+#pragma unroll
+          for (int c = 0; c < 4; ++c) wv[mb][4 * j + c] = oh0 + c < H ? v[c] : 0.0f;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int oh = mb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+          wv[mb][i] = oh < H ? load_w<WT>(w, t * H + oh) : 0.0f;
+        }
+      }
+    }
+    // Scores of keys s0 + 64 g + [0, 64) by wave g % 8: block 0 holds keys
+    // [0, 32), block 1 keys [32, 64) of the group.
+    for (int g = wave; 64 * g < n; g += kIdxWaves) {
+      float p[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        // (keys outside [0, T_kv) score 0, as the indexer pass zeroes them)
+        const int col = 64 * g + 32 * nb + (lane & 31);
+        const int64_t key = (int64_t)s0 + col;
+        const bool ok = col < n && key >= 0 && key < T_kv;
+        u32x4 kf[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          kf[ks] = load16(k + (ok ? key : 0) * D + ks * 16 + 8 * half);
+          if (!ok) kf[ks] = u32x4{0u, 0u, 0u, 0u};
+        }
+        f32x16 acc[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            acc[mb] = mfma32x32x16(qa[mb][ks], kf[ks], ks == 0 ? f32x16{} : acc[mb]);
+        float s = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) s = fmaf(wv[mb][i], relu(acc[mb][i]), s);
+        p[nb] = s;
+      }
+      const float score = halfwave_sums(p[0], p[1]);
+      if (64 * g + lane < n) spill[64 * g + lane] = score;
+    }
+    __syncthreads();  // the spill row is complete
+
+    int32_t* oi = fa.idx + r * fa.ld_idx;
+    float* ol = fa.logit ? fa.logit + r * fa.ld_idx : nullptr;
+    float* os = fa.soft ? fa.soft + r * fa.ld_idx : nullptr;
+    const uint32_t kk = (uint32_t)fa.k;
+    uint32_t kmax = 0u;
+    for (int i = tid; i < n; i += NT) kmax = max(kmax, float_to_key(spill[i]));
+    kmax = block_max<kIdxWaves>(kmax, s_wave);
+    const float vmax = key_to_float(kmax);
+    uint32_t theta = 0u, need_eq = 0u;
+    if ((uint32_t)n > kk)  // uniform
+      theta = radix_select<kIdxWaves>(kk, hist, s_wave, s_sel, &need_eq, [&](auto&& f) {
+        for (int i = tid; i < n; i += NT) f(float_to_key(spill[i]));
+      });
+    // (n <= k: theta = 0 takes every column, need_eq = 0)
+    float s = 0.0f;
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t key = float_to_key(spill[i]);
+      if (key > theta) s += __builtin_amdgcn_exp2f((key_to_float(key) - vmax) * kLog2e);
+    }
+    float ssum = block_sum(s);
+    if (need_eq) ssum += (float)need_eq * __builtin_amdgcn_exp2f((key_to_float(theta) - vmax) * kLog2e);
+    const uint32_t m = min((uint32_t)n, kk);
+    const float lse = m ? vmax + __logf(ssum) : __builtin_inff();
+    // Thread tid owns columns [c0, c1), in column order.
+    const int P = (n + NT - 1) / NT;
+    const int c0 = min(tid * P, n), c1 = min(c0 + P, n);
+    uint32_t ngt = 0u, neq = 0u;
+    for (int i = c0; i < c1; ++i) {
+      const uint32_t key = float_to_key(spill[i]);
+      ngt += key > theta;
+      neq += key == theta;
+    }
+    uint32_t tot;
+    uint32_t g = block_exclusive_scan<kIdxWaves>(ngt, s_wave, &tot);
+    uint32_t qn = block_exclusive_scan<kIdxWaves>(neq, s_wave, &tot);
+    for (int i = c0; i < c1; ++i) {
+      const uint32_t key = float_to_key(spill[i]);
+      const bool is_gt = key > theta, is_eq = key == theta;
+      const uint32_t pos = g + min(qn, need_eq);
+      if ((is_gt || (is_eq && qn < need_eq)) && pos < kk) {
+        const float v = key_to_float(key);
+        oi[pos] = s0 + i;
+        if (ol) ol[pos] = v;
+        if (os) os[pos] = __builtin_amdgcn_exp2f((v - lse) * kLog2e);
+      }
+      g += is_gt;
+      qn += is_eq;
+    }
+    for (uint32_t i = m + tid; i < kk; i += NT) {
+      oi[i] = -1;
+      if (ol) ol[i] = -__builtin_inff();
+      if (os) os[i] = 0.0f;
+    }
+    if (tid == 0) {
+      if (fa.len) fa.len[r] = (int32_t)m;
+      if (fa.lse) fa.lse[r] = lse;
+    }
+    __syncthreads();  // the spill row is read before the next row overwrites it
+  }
+}
+
+template <int D, int MB, int MODE>
 hipError_t launch_indexer_w(const void* q, const void* k, const void* w, int w_dtype,
                             const int32_t* rs, const int32_t* sl, int64_t T_kv, int H,
                             int64_t row_begin, int64_t n_rows, float* scores, int64_t ld,
-                            const FusedArgs& fa, hipStream_t st) {
+                            const FusedArgs& fa, const CandArgs& ca, hipStream_t st) {
   const int64_t nblk = (n_rows + kIdxWaves - 1) / kIdxWaves;
   dim3 grid((unsigned)nblk), block(kIdxWaves * 64);
   // Four weights per load when every run of four heads starts at a multiple
@@ -372,13 +688,13 @@ hipError_t launch_indexer_w(const void* q, const void* k, const void* w, int w_d
   const size_t wbytes = w_dtype == 0 ? 2 : 4;
   const bool w_vec = H % 4 == 0 && (uintptr_t)w % (4 * wbytes) == 0;
   if (w_dtype == 0)
-    hipLaunchKernelGGL((indexer_kernel<D, MB, uint16_t, FUSE>), grid, block, 0, st,
+    hipLaunchKernelGGL((indexer_kernel<D, MB, uint16_t, MODE>), grid, block, 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)w, rs, sl, T_kv, H,
-                       row_begin, n_rows, scores, ld, fa, w_vec);
+                       row_begin, n_rows, scores, ld, fa, ca, w_vec);
   else
-    hipLaunchKernelGGL((indexer_kernel<D, MB, float, FUSE>), grid, block, 0, st,
+    hipLaunchKernelGGL((indexer_kernel<D, MB, float, MODE>), grid, block, 0, st,
                        (const uint16_t*)q, (const uint16_t*)k, (const float*)w, rs, sl, T_kv, H,
-                       row_begin, n_rows, scores, ld, fa, w_vec);
+                       row_begin, n_rows, scores, ld, fa, ca, w_vec);
   return hipGetLastError();
 }
 
@@ -411,8 +727,9 @@ hipError_t launch_indexer(const void* q, const void* k, const void* w, int w_dty
   const FusedArgs none{};
 #define DSA_IDX_CASE(DD, MM)                                                                  \
   if (D == DD && mb == MM)                                                                    \
-    return launch_indexer_w<DD, MM, false>(q, k, w, w_dtype, rs, sl, T_kv, H, row_begin,     \
-                                           n_rows, scores, ld, none, st);
+    return launch_indexer_w<DD, MM, kModeScores>(q, k, w, w_dtype, rs, sl, T_kv, H,          \
+                                                 row_begin, n_rows, scores, ld, none, CandArgs{}, \
+                                                 st);
   DSA_IDX_CASE(128, 1) DSA_IDX_CASE(128, 2) DSA_IDX_CASE(64, 1) DSA_IDX_CASE(64, 2)
 #undef DSA_IDX_CASE
   return hipErrorInvalidValue;
@@ -426,10 +743,53 @@ hipError_t launch_indexer_topk(const void* q, const void* k, const void* w, int 
   const int mb = (H + 31) / 32;
 #define DSA_IDX_CASE(DD, MM)                                                                 \
   if (D == DD && mb == MM)                                                                   \
-    return launch_indexer_w<DD, MM, true>(q, k, w, w_dtype, rs, sl, T_kv, H, row_begin,     \
-                                          n_rows, nullptr, n_cols, fa, st);
+    return launch_indexer_w<DD, MM, kModeFused>(q, k, w, w_dtype, rs, sl, T_kv, H, row_begin, \
+                                                n_rows, nullptr, n_cols, fa, CandArgs{}, st);
   DSA_IDX_CASE(128, 1) DSA_IDX_CASE(128, 2) DSA_IDX_CASE(64, 1) DSA_IDX_CASE(64, 2)
 #undef DSA_IDX_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_indexer_cand(const void* q, const void* k, const void* w, int w_dtype,
+                               const int32_t* rs, const int32_t* sl, int64_t T_kv, int H, int D,
+                               int64_t row_begin, int64_t n_rows, int64_t n_cols, int top_k,
+                               const CandArgs& ca, hipStream_t st) {
+  if (n_rows == 0) return hipSuccess;
+  const int mb = (H + 31) / 32;
+  FusedArgs fa{};
+  fa.k = top_k;
+#define DSA_IDX_CASE(DD, MM)                                                                 \
+  if (D == DD && mb == MM)                                                                   \
+    return launch_indexer_w<DD, MM, kModeCand>(q, k, w, w_dtype, rs, sl, T_kv, H, row_begin, \
+                                               n_rows, nullptr, n_cols, fa, ca, st);
+  DSA_IDX_CASE(128, 1) DSA_IDX_CASE(128, 2) DSA_IDX_CASE(64, 1) DSA_IDX_CASE(64, 2)
+#undef DSA_IDX_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_indexer_rescue(const void* q, const void* k, const void* w, int w_dtype,
+                                 const int32_t* rs, const int32_t* sl, int64_t T_kv, int H, int D,
+                                 int64_t row_begin, int64_t n_rows, int64_t n_cols,
+                                 const FusedArgs& fa, const CandArgs& ca, hipStream_t st) {
+  if (n_rows == 0) return hipSuccess;
+  const int mb = (H + 31) / 32;
+  dim3 grid((unsigned)std::min<int64_t>(ca.n_spill, n_rows)), block(kIdxWaves * 64);
+  const size_t wbytes = w_dtype == 0 ? 2 : 4;
+  const bool w_vec = H % 4 == 0 && (uintptr_t)w % (4 * wbytes) == 0;
+#define DSA_RESCUE_CASE(DD, MM)                                                               \
+  if (D == DD && mb == MM) {                                                                  \
+    if (w_dtype == 0)                                                                         \
+      hipLaunchKernelGGL((indexer_rescue_kernel<DD, MM, uint16_t>), grid, block, 0, st,       \
+                         (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)w, rs, sl,  \
+                         T_kv, H, row_begin, n_cols, fa, ca, w_vec);                          \
+    else                                                                                      \
+      hipLaunchKernelGGL((indexer_rescue_kernel<DD, MM, float>), grid, block, 0, st,          \
+                         (const uint16_t*)q, (const uint16_t*)k, (const float*)w, rs, sl,     \
+                         T_kv, H, row_begin, n_cols, fa, ca, w_vec);                          \
+    return hipGetLastError();                                                                 \
+  }
+  DSA_RESCUE_CASE(128, 1) DSA_RESCUE_CASE(128, 2) DSA_RESCUE_CASE(64, 1) DSA_RESCUE_CASE(64, 2)
+#undef DSA_RESCUE_CASE
   return hipErrorInvalidValue;
 }
 

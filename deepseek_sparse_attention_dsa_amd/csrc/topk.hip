@@ -53,189 +53,46 @@
 #include "dsa.h"
 #include "dsa_device.h"
 #include "dsa_launch.h"
+#include "dsa_rowsel.h"
 
 namespace dsa {
 namespace {
-
-__device__ __forceinline__ uint32_t float_to_key(float f) {
-  uint32_t b = __float_as_uint(f);
-  if (b == 0x80000000u) b = 0u;  // -0.0 == +0.0
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_to_float(uint32_t key) {
-  uint32_t b = (key & 0x80000000u) ? (key & 0x7fffffffu) : ~key;
-  return __uint_as_float(b);
-}
-
-// Exclusive prefix sum over the threads of the workgroup (tid order).
-template <int WAVES>
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave,
-                                                         uint32_t* total) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_incl_scan_dpp(v, [](uint32_t a, uint32_t b) { return a + b; }, 0u);
-  if (WAVES == 1) {
-    *total = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-    return incl - v;
-  }
-  if (lane == 63) s_wave[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < WAVES; ++w) {
-    uint32_t t = s_wave[w];
-    before += (w < wave) ? t : 0u;
-    all += t;
-  }
-  __syncthreads();
-  *total = all;
-  return before + incl - v;
-}
-
-constexpr int kBins = 2048;  // histogram bins
-
-// Radix passes (11/11/10 bits) that find theta, the remaining-th largest key
-// among the keys offered by `offer(f)`, which calls f(key) for every key of
-// the calling thread that takes part. Returns theta; *need_eq receives how
-// many keys equal to theta are taken.
-template <int WAVES, typename Offer>
-__device__ __forceinline__ uint32_t radix_select(uint32_t remaining, uint32_t* hist,
-                                                 uint32_t* s_wave, uint32_t* s_sel,
-                                                 uint32_t* need_eq, Offer&& offer) {
-  constexpr int NT = 64 * WAVES;
-  constexpr int BPT = kBins / NT;
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, pmask = 0;
-#pragma unroll 1
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t dmask = pass == 2 ? 0x3ffu : 0x7ffu;
-    for (int i = tid; i < kBins; i += NT) hist[i] = 0u;
-    __syncthreads();
-    offer([&](uint32_t key) {
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
-    });
-    __syncthreads();
-    // Thread tid owns bins [hi_bin - BPT + 1, hi_bin], highest bins first.
-    const int hi_bin = kBins - 1 - tid * BPT;
-    uint32_t local = 0;
-#pragma unroll
-    for (int b = 0; b < BPT; ++b) local += hist[hi_bin - b];
-    uint32_t total;
-    const uint32_t above = block_exclusive_scan<WAVES>(local, s_wave, &total);
-    if (above < remaining && remaining <= above + local) {
-      uint32_t acc = above;
-      for (int b = 0; b < BPT; ++b) {
-        const uint32_t h = hist[hi_bin - b];
-        if (acc + h >= remaining) {
-          s_sel[0] = (uint32_t)(hi_bin - b);
-          s_sel[1] = acc;
-          break;
-        }
-        acc += h;
-      }
-    }
-    __syncthreads();
-    remaining -= s_sel[1];
-    prefix |= s_sel[0] << shift;
-    pmask |= dmask << shift;
-    __syncthreads();
-  }
-  *need_eq = remaining;
-  return prefix;
-}
-
-// Bucket of a key on a scale linear in the score value: monotone in the key,
-// so the buckets split the keys into ordered ranges.
-struct LinearBuckets {
-  float lo, scale;
-  // (-0.0 and +0.0 land in the same bucket, as their keys are equal)
-  __device__ __forceinline__ int of_value(float v) const {
-    const float x = (v - lo) * scale;
-    if (!(x > 0.0f)) return 0;  // also NaN (inf * 0 when lo = -inf)
-    return x >= (float)(kBins - 1) ? kBins - 1 : (int)x;
-  }
-  __device__ __forceinline__ int operator()(uint32_t key) const { return of_value(key_to_float(key)); }
-};
-
-// Max over the workgroup (s_red: WAVES words).
-template <int WAVES>
-__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* s_red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  v = wave_max_u32(v);
-  if (WAVES > 1) {
-    if (lane == 0) s_red[wave] = v;
-    __syncthreads();
-    v = 0;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) v = max(v, s_red[w]);
-    __syncthreads();
-  }
-  return v;
-}
-
-// Finds the bucket holding the `want`-th largest of the keys counted in
-// hist (1 <= want <= their number): s_sel[0] = bucket, s_sel[1] = count in
-// the buckets above it. Ends with a barrier.
-template <int WAVES>
-__device__ __forceinline__ void find_bucket(const uint32_t* hist, uint32_t want, uint32_t* s_wave,
-                                            uint32_t* s_sel) {
-  constexpr int BPT = kBins / (64 * WAVES);
-  const int hi_bin = kBins - 1 - (int)threadIdx.x * BPT;  // thread owns [hi_bin - BPT + 1, hi_bin]
-  uint32_t local = 0;
-#pragma unroll
-  for (int b = 0; b < BPT; ++b) local += hist[hi_bin - b];
-  uint32_t total;
-  const uint32_t above = block_exclusive_scan<WAVES>(local, s_wave, &total);
-  if (above < want && want <= above + local) {
-    uint32_t acc = above;
-    for (int b = 0; b < BPT; ++b) {
-      const uint32_t h = hist[hi_bin - b];
-      if (acc + h >= want) {
-        s_sel[0] = (uint32_t)(hi_bin - b);
-        s_sel[1] = acc;
-        break;
-      }
-      acc += h;
-    }
-  }
-  __syncthreads();
-}
-
-// Ordered write of the selected keys of one thread's run, given the counts
-// of keys above / equal to theta before the run (in column order).
-struct Placer {
-  uint32_t theta, need_eq, k;
-  int32_t* out_idx;
-  float* out_val;
-  __device__ __forceinline__ void operator()(uint32_t key, int32_t gcol, uint32_t& g,
-                                             uint32_t& q) const {
-    const bool is_gt = key > theta, is_eq = key == theta;
-    const uint32_t pos = g + min(q, need_eq);
-    if ((is_gt || (is_eq && q < need_eq)) && pos < k) {
-      out_idx[pos] = gcol;
-      if (out_val) out_val[pos] = key_to_float(key);
-    }
-    g += is_gt;
-    q += is_eq;
-  }
-};
 
 // ------------------------------------------------ rows of <= 8192 columns --
 // CH: 4-column chunks per lane, held in VGPRs. Wave w owns the columns
 // [w * 256 * CH, (w + 1) * 256 * CH); chunk c of a wave covers 256
 // consecutive columns, 4 per lane.
-template <int WAVES, int CH>
+//
+// CAND: stage 2 of the combined indexer + top-k for long rows (DSA page
+// section 4). The row is not a score row but its candidate list from the
+// indexer pass: (score, local column) pairs in column order,
+// every column whose score reached the row's lower bound. The list holds the
+// row's top k when it has between k and cap entries (or, for a row of at most
+// k columns, all of them); any other row is queued for the rescue pass and
+// left alone here. The selected scores, their softmax and its log-sum-exp
+// are written as well.
+struct CandSel {
+  const uint32_t* cand;  // [n_rows, cap] (score bits, local column) pairs
+  int64_t cap;           // = 64 * WAVES * 4 * CH
+  const int32_t* count;  // [n_rows] candidates found (may exceed cap)
+  int32_t* queue;        // [n_rows] rows left to the rescue pass
+  uint32_t* n_queued;    // their number (zeroed by the indexer pass)
+  float* soft;           // [n_rows, ld_idx] or null
+  float* lse;            // [n_rows] or null
+};
+
+template <int WAVES, int CH, bool CAND>
 __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
     const float* __restrict__ scores, int64_t ld, int64_t n_cols,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ row_starts, int k,
     int32_t* __restrict__ indices, int64_t ld_idx, int32_t* __restrict__ topk_length,
-    float* __restrict__ values) {
+    float* __restrict__ values, CandSel cs) {
   constexpr int NT = 64 * WAVES;
+  constexpr float kLog2e = 1.4426950408889634f;
   static_assert(kBins % NT == 0, "bins must split evenly over threads");
   __shared__ uint32_t hist[kBins + 64];  // + a spare output slot per lane
   __shared__ uint32_t s_wave[2][WAVES > 1 ? WAVES : 1];
+  __shared__ float s_fsum[WAVES];
   __shared__ uint32_t s_sel[2];
   __shared__ uint32_t s_mem[64];
   __shared__ uint32_t s_cnt;
@@ -244,15 +101,65 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t r = (int64_t)gridDim.x - 1 - blockIdx.x;  // long rows first
-  const float* row = scores + r * ld;
+  const float* row = CAND ? nullptr : scores + r * ld;
   int32_t* out_idx = indices + r * ld_idx;
   float* out_val = values ? values + r * ld_idx : nullptr;
   int64_t n64 = seq_lens[r];
   n64 = n64 < 0 ? 0 : (n64 > n_cols ? n_cols : n64);
   const int n = (int)n64;
   const int32_t base = row_starts ? row_starts[r] : 0;
+  float* out_soft = nullptr;
+  const uint32_t* crow = nullptr;
+  int nsel = n;  // entries to select from
+  if constexpr (CAND) {
+    out_soft = cs.soft ? cs.soft + r * ld_idx : nullptr;
+    crow = cs.cand + 2 * r * cs.cap;
+    const int32_t c = cs.count[r];
+    if (n <= k ? c != n : (c < k || c > cs.cap)) {  // uniform
+      if (tid == 0) cs.queue[atomicAdd(cs.n_queued, 1u)] = (int32_t)r;
+      return;
+    }
+    nsel = c;
+  }
+  // Sum over the workgroup of one float per thread.
+  auto block_sum = [&](float v) -> float {
+    v = wave_sum_f32(v);
+    if (WAVES == 1) return v;
+    if (lane == 0) s_fsum[wave] = v;
+    __syncthreads();
+    v = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) v += s_fsum[w];
+    __syncthreads();
+    return v;
+  };
 
-  if (n <= k) {
+  if (CAND && n <= k) {
+    // Every column is selected, in the list's (column) order.
+    uint32_t kmax = 0u;
+    for (int i = tid; i < nsel; i += NT) kmax = max(kmax, float_to_key(__uint_as_float(crow[2 * i])));
+    kmax = block_max<WAVES>(kmax, s_wave[0]);
+    const float vmax = key_to_float(kmax);
+    float s = 0.0f;
+    for (int i = tid; i < nsel; i += NT)
+      s += __builtin_amdgcn_exp2f((key_to_float(float_to_key(__uint_as_float(crow[2 * i]))) - vmax) *
+                                  kLog2e);
+    const float ssum = block_sum(s);
+    const float lse = nsel ? vmax + __logf(ssum) : __builtin_inff();
+    for (int i = tid; i < k; i += NT) {
+      const float v =
+          i < nsel ? key_to_float(float_to_key(__uint_as_float(crow[2 * i]))) : -__builtin_inff();
+      out_idx[i] = i < nsel ? base + (int32_t)crow[2 * i + 1] : -1;
+      if (out_val) out_val[i] = v;
+      if (out_soft) out_soft[i] = i < nsel ? __builtin_amdgcn_exp2f((v - lse) * kLog2e) : 0.0f;
+    }
+    if (tid == 0) {
+      if (topk_length) topk_length[r] = nsel;
+      if (cs.lse) cs.lse[r] = lse;
+    }
+    return;
+  }
+  if (!CAND && n <= k) {
     // Every causal column is selected; no select needed.
     if (!out_val && (k & 3) == 0 && ((uintptr_t)out_idx & 15u) == 0) {
       // 16-byte stores of four consecutive slots
@@ -273,20 +180,45 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
   // All loads are issued before any is used. Every load is a full 16-byte
   // chunk inside the row's ld columns (ld is a multiple of 4 and >= n):
   // chunks past the row read a clamped address and columns >= n become key 0.
+  // CAND: the entries are read as two 16-byte (key, column) pairs per lane
+  // and chunk, inside the row's cap entries; entries >= nsel become key 0.
   const int wbase = wave * 256 * CH;
   float4 raw[CH];
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int col = wbase + c * 256 + lane * 4;
-    const int64_t colc = col < ld - 4 ? (int64_t)col : ld - 4;
-    raw[c] = *reinterpret_cast<const float4*>(row + colc);
-  }
   u32x4 kreg[CH];
+  u32x4 creg[CAND ? CH : 1];
+  if constexpr (CAND) {
+    u32x4 pr[CH][2];  // only the filled entries are read
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int col = wbase + c * 256 + lane * 4;
-    kreg[c] = u32x4{col + 0 < n ? float_to_key(raw[c].x) : 0u, col + 1 < n ? float_to_key(raw[c].y) : 0u,
-                    col + 2 < n ? float_to_key(raw[c].z) : 0u, col + 3 < n ? float_to_key(raw[c].w) : 0u};
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e0 = wbase + c * 256 + lane * 4 + 2 * h;
+        pr[c][h] = e0 < nsel ? *reinterpret_cast<const u32x4*>(crow + 2 * e0) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int col = wbase + c * 256 + lane * 4;
+      kreg[c] = u32x4{col + 0 < nsel ? float_to_key(__uint_as_float(pr[c][0][0])) : 0u,
+                      col + 1 < nsel ? float_to_key(__uint_as_float(pr[c][0][2])) : 0u,
+                      col + 2 < nsel ? float_to_key(__uint_as_float(pr[c][1][0])) : 0u,
+                      col + 3 < nsel ? float_to_key(__uint_as_float(pr[c][1][2])) : 0u};
+      creg[c] = u32x4{pr[c][0][1], pr[c][0][3], pr[c][1][1], pr[c][1][3]};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) raw[c][e] = key_to_float(kreg[c][e]);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int col = wbase + c * 256 + lane * 4;
+      const int64_t colc = col < ld - 4 ? (int64_t)col : ld - 4;
+      raw[c] = *reinterpret_cast<const float4*>(row + colc);
+    }
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int col = wbase + c * 256 + lane * 4;
+      kreg[c] = u32x4{col + 0 < n ? float_to_key(raw[c].x) : 0u, col + 1 < n ? float_to_key(raw[c].y) : 0u,
+                      col + 2 < n ? float_to_key(raw[c].z) : 0u, col + 3 < n ? float_to_key(raw[c].w) : 0u};
+    }
   }
 
   // theta: one histogram over kBins buckets linear in the score between the
@@ -378,6 +310,23 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
     });
   }
 
+  // CAND: the softmax normaliser of the selected set (every key above theta
+  // and need_eq keys equal to it), as the on-chip combined path forms it.
+  float lse = 0.0f;
+  if (CAND && (out_soft || cs.lse)) {  // uniform
+    const float vmax = key_to_float(kmax);
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (kreg[c][e] > theta) s += __builtin_amdgcn_exp2f((raw[c][e] - vmax) * kLog2e);
+    float ssum = block_sum(s);
+    if (need_eq)
+      ssum += (float)need_eq * __builtin_amdgcn_exp2f((key_to_float(theta) - vmax) * kLog2e);
+    lse = vmax + __logf(ssum);
+  }
+
   // Output positions follow column order (wave, chunk, lane, element). Per
   // chunk, each lane counts its keys above and equal to theta, packed as
   // (above | equal << 16) (both < 2^16), and the wave scans the packed counts
@@ -407,7 +356,8 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
   // staged in LDS (the histogram is free now; k <= kBins; unselected columns
   // write a spare slot of their lane) and leave in 16-byte stores; otherwise
   // they are written in place.
-  const bool staged = !out_val && (k & 3) == 0 && ((uintptr_t)out_idx & 15u) == 0;  // uniform
+  const bool staged =
+      !out_val && !out_soft && (k & 3) == 0 && ((uintptr_t)out_idx & 15u) == 0;  // uniform
   if (staged) __syncthreads();  // the histogram's last readers are done
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
@@ -419,12 +369,14 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
       const uint32_t ng = cnt & 0xffffu, nq = cnt >> 16;
       const uint32_t pos = ng + min(nq, need_eq);
       const bool take = (is_gt || (is_eq && nq < need_eq)) && pos < (uint32_t)k;
-      const int32_t gcol = base + wbase + c * 256 + lane * 4 + e;
+      const int32_t gcol =
+          base + (CAND ? (int32_t)creg[c][e] : wbase + c * 256 + lane * 4 + e);
       if (staged) {
         hist[take ? pos : (uint32_t)(kBins + lane)] = (uint32_t)gcol;
       } else if (take) {
         out_idx[pos] = gcol;
         if (out_val) out_val[pos] = key_to_float(key);
+        if (out_soft) out_soft[pos] = __builtin_amdgcn_exp2f((raw[c][e] - lse) * kLog2e);
       }
       cnt += (is_gt ? 1u : 0u) + (is_eq ? 0x10000u : 0u);
     }
@@ -434,7 +386,10 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
     for (int i = 4 * tid; i < k; i += 4 * NT)
       *reinterpret_cast<u32x4*>(out_idx + i) = *reinterpret_cast<const u32x4*>(hist + i);
   }
-  if (tid == 0 && topk_length) topk_length[r] = k;
+  if (tid == 0) {
+    if (topk_length) topk_length[r] = k;
+    if (CAND && cs.lse) cs.lse[r] = lse;
+  }
 }
 
 // ------------------------------------------------- rows of > 8192 columns --
@@ -779,8 +734,8 @@ hipError_t launch_radix(const float* scores, int64_t ld, int64_t n_rows, int64_t
                         const int32_t* sl, const int32_t* rs, int k, int32_t* idx,
                         int64_t ld_idx, int32_t* tl, float* vals, hipStream_t st) {
   dim3 grid((unsigned)n_rows), block(64 * WAVES);
-  hipLaunchKernelGGL((topk_radix_kernel<WAVES, CH>), grid, block, 0, st, scores, ld, n_cols, sl, rs,
-                     k, idx, ld_idx, tl, vals);
+  hipLaunchKernelGGL((topk_radix_kernel<WAVES, CH, false>), grid, block, 0, st, scores, ld, n_cols,
+                     sl, rs, k, idx, ld_idx, tl, vals, CandSel{});
   return hipGetLastError();
 }
 
@@ -809,6 +764,20 @@ hipError_t launch_topk(const float* scores, int64_t ld, int64_t n_rows, int64_t 
     return hipGetLastError();
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_topk_cand(const int32_t* seq_lens, const int32_t* row_starts, int64_t n_rows,
+                            int64_t n_cols, int k, int32_t* indices, int64_t ld_idx,
+                            int32_t* topk_length, float* logits, float* softmax, float* lse,
+                            const CandArgs& ca, hipStream_t st) {
+  constexpr int kW = 8, kCh = 4;
+  static_assert(64 * kW * 4 * kCh == kCandCap, "one workgroup holds a full candidate list");
+  if (n_rows == 0) return hipSuccess;
+  const CandSel cs{ca.cand, ca.cap, ca.count, ca.queue, ca.n_queued, softmax, lse};
+  dim3 grid((unsigned)n_rows), block(64 * kW);
+  hipLaunchKernelGGL((topk_radix_kernel<kW, kCh, true>), grid, block, 0, st, nullptr, 0, n_cols,
+                     seq_lens, row_starts, k, indices, ld_idx, topk_length, logits, cs);
+  return hipGetLastError();
 }
 
 }  // namespace dsa

@@ -11,7 +11,10 @@
  *   dsa_topk             per-row top-K select, ascending global indices, -1 pad
  *                        (dsa_topk_workspace_bytes: its workspace query, 0)
  *   dsa_indexer_topk_fused  indexer scores + top-K (+ logits, softmax, LSE)
- *                        in one launch, the scores kept on chip
+ *                        without dense scores: kept on chip for rows of up
+ *                        to 4096 columns, reduced to per-row candidates in a
+ *                        caller-owned buffer for longer rows
+ *                        (dsa_indexer_topk_cand_buffer_size: its size query)
  *   dsa_sparse_attn_fwd  sparse MQA/GQA attention over the selected KV rows
  *   dsa_sparse_attn_bwd  its gradients (dq, dkv, d_sink) for shared latent KV
  *                        (dsa_sparse_attn_bwd_noalloc: the same without a
@@ -71,14 +74,15 @@ typedef enum {
 const char* dsa_last_error(void);
 
 /* ABI version of this header (bumped on any signature change). */
-#define DSA_ABI_VERSION 7
+#define DSA_ABI_VERSION 8
 int dsa_abi_version(void);
 
 /* Limits enforced by the host checks. */
 #define DSA_MAX_TOPK 2048           /* top_k <= 2048 (DSA page, section 5)  */
 #define DSA_TOPK_MAX_COLS 65536     /* longest score row dsa_topk selects on */
 #define DSA_MAX_HEADS 128           /* attention query heads per call        */
-#define DSA_FUSED_MAX_COLS 4096     /* longest row dsa_indexer_topk_fused takes */
+#define DSA_FUSED_MAX_COLS 4096     /* longest row dsa_indexer_topk_fused keeps
+                                       on chip (longer rows: candidate buffer) */
 /* Device scratch of dsa_sparse_attn_bwd_noalloc (bytes, per device). */
 #define DSA_NOALLOC_SCRATCH_BYTES (256ll * 1024 * 1024)
 
@@ -258,9 +262,25 @@ int64_t dsa_topk_workspace_bytes(int64_t n_rows, int64_t n_cols, int32_t k);
  *   softmax[r, i] = exp(logits[r, i] - lse[r]), 0 in padded slots (or NULL)
  *   lse[r]        = ln sum_i exp(logits[r, i]) over the selected slots,
  *                   +inf for a row with no slot                 (or NULL)
- * Each row's scores stay in the CU's local memory, so n_cols <=
- * DSA_FUSED_MAX_COLS; a row whose seq_lens exceeds n_cols is treated as
- * n_cols long (as dsa_topk does).
+ * A row whose seq_lens exceeds n_cols is treated as n_cols long (as dsa_topk
+ * does). No dense score matrix is written:
+ * - n_cols <= DSA_FUSED_MAX_COLS: each row's scores stay in the CU's local
+ *   memory and are selected there, in one launch; cand_buffer is unused
+ *   (may be NULL).
+ * - DSA_FUSED_MAX_COLS < n_cols <= DSA_TOPK_MAX_COLS (bf16 inputs only): the
+ *   DSA page's candidate scheme (section 4: a caller-owned candidate buffer,
+ *   then a stage-2 select). The indexer pass appends, for each row, the
+ *   columns whose score reaches a lower bound sampled from the row, as
+ *   (score key, column) pairs; a second launch selects the top k from them;
+ *   a third redoes exactly, from recomputed scores, any row whose candidates
+ *   could not hold its top k (rare; correct for every input, slower). The
+ *   result is the same as on the short-row path: dsa_topk of
+ *   dsa_indexer_fwd's scores, bit for bit.
+ *   cand_buffer  device float [cand_floats], 16-byte aligned, caller-owned
+ *                scratch of at least dsa_indexer_topk_cand_buffer_size(
+ *                n_rows, n_cols, k) floats; its contents on entry do not
+ *                matter and are overwritten. Calls that overlap in time must
+ *                not share one buffer.
  *   q_idx, k_idx, w, w_dtype, row_starts, seq_lens, T, T_kv, H_idx, D_idx,
  *   row_begin, n_rows: as dsa_indexer_fwd (bf16) or dsa_indexer_fwd_fp8
  *   k           1..DSA_MAX_TOPK
@@ -269,8 +289,10 @@ int64_t dsa_topk_workspace_bytes(int64_t n_rows, int64_t n_cols, int32_t k);
  *   topk_length device int32 [n_rows] or NULL
  * With T_kv = 0 every row is empty (k_idx and k_scale may then be NULL).
  * Errors: those of dsa_indexer_fwd / dsa_indexer_fwd_fp8 and dsa_topk,
- * DSA_ERR_VALUE for an unknown precision or n_cols outside
- * [1, DSA_FUSED_MAX_COLS].
+ * DSA_ERR_VALUE for an unknown precision, n_cols outside
+ * [1, DSA_TOPK_MAX_COLS], FP8 inputs with n_cols > DSA_FUSED_MAX_COLS, or a
+ * missing, misaligned or too small cand_buffer when n_cols >
+ * DSA_FUSED_MAX_COLS.
  */
 int dsa_indexer_topk_fused(const void* q_idx, const void* q_scale, const void* k_idx,
                            const void* k_scale, int32_t precision, const void* w,
@@ -278,7 +300,21 @@ int dsa_indexer_topk_fused(const void* q_idx, const void* q_scale, const void* k
                            int64_t T, int64_t T_kv, int32_t H_idx, int32_t D_idx,
                            int64_t row_begin, int64_t n_rows, int64_t n_cols, int32_t k,
                            int32_t* indices, int64_t ld_indices, int32_t* topk_length,
-                           float* logits, float* softmax, float* lse, void* stream);
+                           float* logits, float* softmax, float* lse, float* cand_buffer,
+                           int64_t cand_floats, void* stream);
+
+/*
+ * dsa_indexer_topk_cand_buffer_size - floats of the candidate buffer that
+ * dsa_indexer_topk_fused needs for these sizes (the DSA page, section 4,
+ * sizes its candidate buffer with such a query, in floats). 0 when
+ * n_cols <= DSA_FUSED_MAX_COLS or n_rows = 0 (no buffer is used), -1 for
+ * sizes the call rejects (n_rows outside [0, INT32_MAX], n_cols outside
+ * [1, DSA_TOPK_MAX_COLS], k outside [1, DSA_MAX_TOPK]). The size grows
+ * linearly with n_rows (8192 (score, column) pairs per row, plus up to 256
+ * rows of n_cols floats for the rescue); callers may split long row ranges
+ * with row_begin / n_rows to bound it.
+ */
+int64_t dsa_indexer_topk_cand_buffer_size(int64_t n_rows, int64_t n_cols, int32_t k);
 
 /*
  * dsa_sparse_attn_fwd - steps a4 / a5, sparse attention forward.

@@ -35,7 +35,11 @@ F8_BASE = dict(q=FAKE, qs=FAKE2, k=FAKE, ks=FAKE2, sc=1, w=FAKE, wd=0, rs=FAKE, 
                Tkv=256, H=64, D=128, rb=0, nr=256, scores=FAKE, ld=256, stream=None)
 FUSED_BASE = dict(q=FAKE, qs=None, k=FAKE, ks=None, prec=0, w=FAKE, wd=0, rs=FAKE, sl=FAKE,
                   T=256, Tkv=256, H=64, D=128, rb=0, nr=256, nc=4096, kk=2048, idx=FAKE, ldi=2048,
-                  tl=None, lg=None, so=None, lse=None, stream=None)
+                  tl=None, lg=None, so=None, lse=None, cb=None, cbn=0, stream=None)
+# floats of the candidate buffer for 256 rows of 4097 columns: 4-word header,
+# counts and queue (256 words each), 256 rescue rows of 4100 floats, and 256
+# lists of 8192 (key, column) pairs
+CAND_4097 = 4 + 256 + 256 + 256 * 4100 + 256 * 8192 * 2
 BWD_BASE = dict(q=FAKE, Tq=16, H=16, Dqk=576, kv=FAKE, Tkv=16, ldkv=576, Dv=512, idx=FAKE, ldi=64,
                 kw=64, tl=None, sink=None, scale=0.04, out=FAKE, dout=FAKE, lse=FAKE, dq=FAKE,
                 dkv=FAKE, ds=None, ws=FAKE2, wsb=1 << 24, stream=None)
@@ -55,7 +59,7 @@ ORDER = {
     "f8": ["q", "qs", "k", "ks", "sc", "w", "wd", "rs", "sl", "T", "Tkv", "H", "D", "rb", "nr",
            "scores", "ld", "stream"],
     "fused": ["q", "qs", "k", "ks", "prec", "w", "wd", "rs", "sl", "T", "Tkv", "H", "D", "rb", "nr",
-              "nc", "kk", "idx", "ldi", "tl", "lg", "so", "lse", "stream"],
+              "nc", "kk", "idx", "ldi", "tl", "lg", "so", "lse", "cb", "cbn", "stream"],
     "bwd": ["q", "Tq", "H", "Dqk", "kv", "Tkv", "ldkv", "Dv", "idx", "ldi", "kw", "tl", "sink",
             "scale", "out", "dout", "lse", "dq", "dkv", "ds", "ws", "wsb", "stream"],
     "noalloc": ["q", "Tq", "H", "Dqk", "kv", "Tkv", "ldkv", "Dv", "idx", "ldi", "kw", "tl",
@@ -126,7 +130,13 @@ CASES = [
     ("f8", dict(), ERUNTIME), ("f8", dict(sc=0, wd=1), ERUNTIME),
     # combined indexer + top-K
     ("fused", dict(wd=2), ETYPE), ("fused", dict(prec=3), EVALUE), ("fused", dict(nc=0), EVALUE),
-    ("fused", dict(nc=4097), EVALUE), ("fused", dict(kk=0), EVALUE), ("fused", dict(kk=2049), EVALUE),
+    ("fused", dict(nc=65537), EVALUE), ("fused", dict(kk=0), EVALUE), ("fused", dict(kk=2049), EVALUE),
+    # rows longer than the on-chip path: a candidate buffer of the queried size
+    ("fused", dict(nc=4097), EVALUE), ("fused", dict(nc=4097, cb=FAKE2, cbn=CAND_4097 - 1), EVALUE),
+    ("fused", dict(nc=4097, cb=FAKE2 + 4, cbn=CAND_4097), EVALUE),
+    ("fused", dict(nc=4097, cb=FAKE2, cbn=CAND_4097, prec=1, qs=FAKE2, ks=FAKE2), EVALUE),
+    ("fused", dict(nc=4097, cb=FAKE2, cbn=CAND_4097), ERUNTIME),
+    ("fused", dict(nc=65536, nr=0, cb=None), OK),
     ("fused", dict(ldi=2047), EVALUE), ("fused", dict(D=96), EVALUE),
     ("fused", dict(prec=1, D=64), EVALUE), ("fused", dict(prec=1), EVALUE),
     ("fused", dict(prec=2, qs=FAKE2, ks=FAKE2 + 1), EVALUE), ("fused", dict(idx=None), EVALUE),
@@ -197,7 +207,7 @@ def test_header_declares_the_path():
     for fn in ["dsa_packed_metadata", "dsa_ratio_causal_metadata", "dsa_indexer_fwd",
                "dsa_indexer_fwd_fp8", "dsa_indexer_topk_fused", "dsa_topk", "dsa_sparse_attn_fwd",
                "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_workspace_bytes",
-               "dsa_topk_workspace_bytes",
+               "dsa_topk_workspace_bytes", "dsa_indexer_topk_cand_buffer_size",
                "dsa_last_error",
                "dsa_abi_version"]:
         assert fn in names
@@ -263,6 +273,23 @@ def test_backward_workspace_size_rule():
     assert n == fixed + rows
     assert lib.dsa_sparse_attn_bwd_workspace_bytes(10, 0, 10, 576, 8) == -1
     assert lib.dsa_sparse_attn_bwd_workspace_bytes(10, 8, 10, 256, 8) == -1
+
+
+def test_cand_buffer_size_query():
+    # no buffer for rows the on-chip path takes; the layout's size otherwise;
+    # -1 exactly for the sizes the combined call rejects
+    lib = dsa.load_library()
+    assert lib.dsa_indexer_topk_cand_buffer_size(65536, 4096, 2048) == 0
+    assert lib.dsa_indexer_topk_cand_buffer_size(0, 65536, 2048) == 0
+    assert lib.dsa_indexer_topk_cand_buffer_size(256, 4097, 2048) == CAND_4097
+    assert dsa.dsa_indexer_topk_cand_buffer_size(256, 4097, 1) == CAND_4097
+    n = dsa.dsa_indexer_topk_cand_buffer_size(65536, 65536, 2048)
+    assert n == 4 + 2 * 65536 + 256 * 65536 + 65536 * 8192 * 2
+    for args in [(-1, 8192, 64), (8, 0, 64), (8, 65537, 64), (8, 8192, 0), (8, 8192, 2049),
+                 (2 ** 31, 8192, 64)]:
+        assert lib.dsa_indexer_topk_cand_buffer_size(*args) == -1, args
+        with pytest.raises(ValueError):
+            dsa.dsa_indexer_topk_cand_buffer_size(*args)
 
 
 def test_topk_workspace_query():
