@@ -752,16 +752,22 @@ def test_oracle_detects_planted_mistakes():
     good = O.indexer_scores(q, k, w, st, sl, np.arange(T), width=T)
     brute = _indexer_brute(q, k, w, cu)
     fin = np.isfinite(brute)
-    # dropped ReLU, sign flip of W and transposed head/dim use all differ
+    # a dropped ReLU, a sign flip of W, the ReLU applied after the head sum
+    # and the weights of the wrong query row all differ from brute force
     no_relu = np.full_like(good, -np.inf)
     flip = np.full_like(good, -np.inf)
+    relu_late = np.full_like(good, -np.inf)
+    wrong_row = np.full_like(good, -np.inf)
     for t in range(T):
         n, s0 = sl[t], st[t]
-        no_relu[t, :n] = w[t] @ (q[t] @ k[s0:s0 + n].T)
-        flip[t, :n] = -(w[t] @ np.maximum(q[t] @ k[s0:s0 + n].T, 0))
+        qk = q[t] @ k[s0:s0 + n].T  # [H, n]
+        no_relu[t, :n] = w[t] @ qk
+        flip[t, :n] = -(w[t] @ np.maximum(qk, 0))
+        relu_late[t, :n] = np.maximum(w[t] @ qk, 0)
+        wrong_row[t, :n] = w[(t + 1) % T] @ np.maximum(qk, 0)
     assert np.allclose(good[fin], brute[fin])
-    assert not np.allclose(no_relu[fin], brute[fin])
-    assert not np.allclose(flip[fin], brute[fin])
+    for mutant in (no_relu, flip, relu_late, wrong_row):
+        assert not np.allclose(mutant[fin], brute[fin])
 
 
 def _attn_mutant(q, kv, idx, sink, scale, d_v, mistake):
