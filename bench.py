@@ -53,12 +53,19 @@ DEFAULT_CONFIG = 4
 
 # Kernel families of the path: the stage they belong to, the source file they
 # are built from, and the substrings that name their dispatches in rocprofv3.
+# (The first family whose substring matches takes a dispatch: the candidate
+# path's instances come before their plain families.)
 KERNELS = {
     "attention": ("sparse_attn.hip", ("sparse_attn_kernel",)),
+    "indexer_cand": ("indexer.hip", ("indexer_kernel<128, 2, unsigned short, 2>",)),
+    "indexer_rescue": ("indexer.hip", ("indexer_rescue_kernel",)),
     "indexer": ("indexer.hip", ("indexer_kernel<",)),
     "indexer_fp8": ("indexer_fp8.hip", ("indexer_fp8_kernel",)),
+    "topk_cand": ("topk.hip", ("topk_radix_kernel<8, 4, true>",)),
     "topk": ("topk.hip", ("topk_radix_kernel", "topk_stream_kernel")),
 }
+# the kernels of one dsa_indexer_topk_fused call on rows longer than 4096 columns
+CAND_FAMILIES = ("indexer_cand", "topk_cand", "indexer_rescue")
 
 
 def parse():
@@ -72,9 +79,11 @@ def parse():
     p.add_argument("--backward", action="store_true",
                    help="also time dsa_sparse_attn_bwd on the forward's outputs (shared latent KV "
                         "workloads), reported as its own stage")
-    p.add_argument("--fused", action="store_true",
-                   help="dsa_indexer_topk_fused instead of score chunks + dsa_topk (no dense "
-                        "scores: on chip up to 4096 columns, a candidate buffer beyond)")
+    p.add_argument("--path", choices=("auto", "chunks", "fused"), default="auto",
+                   help="indexer + top-K: score chunks + dsa_topk, or dsa_indexer_topk_fused "
+                        "(no dense scores: on chip up to 4096 columns, a candidate buffer "
+                        "beyond); auto = fused for bf16 rows longer than 4096 columns, else "
+                        "chunks")
     p.add_argument("--flush-steps", type=int, default=5,
                    help="extra steps, each after writing 512 MiB so that the 256 MB MALL holds "
                         "none of the step's inputs, reported as stages_flushed (0: none)")
@@ -468,10 +477,13 @@ def main():
         return dsa.dsa_packed_metadata(wl.cu_seqlens, T, row_starts=row_starts, seq_lens=seq_lens)
 
     rs, sl = metadata()
-    fused = has_indexer and args.fused
-    long_fused = fused and max_len > dsa.DSA_FUSED_MAX_COLS
+    long_rows = max_len > dsa.DSA_FUSED_MAX_COLS
+    fused = has_indexer and (args.path == "fused" or (args.path == "auto" and long_rows and
+                                                      not fp8))
+    long_fused = fused and long_rows
     if long_fused and fp8:
-        raise SystemExit(f"--fused takes FP8 rows of at most {dsa.DSA_FUSED_MAX_COLS} columns")
+        raise SystemExit(f"--path fused takes FP8 rows of at most {dsa.DSA_FUSED_MAX_COLS} "
+                         "columns")
     cand = None
     if long_fused:  # allocated once, outside the timed steps
         cand = torch.empty((dsa.dsa_indexer_topk_cand_buffer_size(T, max_len, K),),
@@ -607,10 +619,14 @@ def main():
             if long_fused:
                 stages["indexer_topk_fused"]["rows_rescued"] = int(
                     cand[:1].view(torch.int32).item())
+            traffic = None
+            if long_fused:
+                parts = [traffic_from_profile(wname, f) for f in CAND_FAMILIES]
+                traffic = None if any(v is None for v in parts) else float(sum(parts))
             rooflines["indexer_topk_fused"] = roofline_entry(
                 "indexer_kernel (candidate mode) + topk_radix_kernel (candidates) + "
                 "indexer_rescue_kernel" if long_fused else "indexer_kernel (combined with top-K)",
-                "mfma", cnt["indexer_flop"], n, ms, idx_peak, "TFLOP/s", None)
+                "mfma", cnt["indexer_flop"], n, ms, idx_peak, "TFLOP/s", traffic)
         else:
             ims, n_i = st["indexer"]
             tms, n_t = st["topk"]

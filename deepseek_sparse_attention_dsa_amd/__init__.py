@@ -600,8 +600,9 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
     dsa_indexer_topk_fused call (no score buffer: rows of at most
     DSA_FUSED_MAX_COLS columns stay on chip, longer bf16 rows go through a
     candidate buffer); only that path gives return_softmax, which returns
-    (indices, topk_length, logits, softmax, lse). The score-chunk path is
-    the default.
+    (indices, topk_length, logits, softmax, lse). fused=None takes the
+    candidate buffer for bf16 rows longer than DSA_FUSED_MAX_COLS (the faster
+    path there on MI355X) and score chunks otherwise.
     """
     fp8 = q_idx.dtype in (torch.uint8, torch.float8_e4m3fn)
     if fp8 and (q_scale is None or k_scale is None or fp8_scaling is None):
@@ -619,7 +620,7 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
         width = T if max_seqlen is None else int(max_seqlen)
         row_starts, seq_lens = dsa_packed_metadata(cu_seqlens, T, stream=stream)
     if fused is None:
-        fused = return_softmax
+        fused = return_softmax or (width > DSA_FUSED_MAX_COLS and not fp8)
     if return_softmax and not fused:
         raise ValueError("return_softmax needs the fused path")
     if fused:

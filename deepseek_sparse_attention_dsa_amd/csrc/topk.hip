@@ -81,8 +81,10 @@ struct CandSel {
   float* lse;            // [n_rows] or null
 };
 
+// (CAND: six waves per SIMD, three workgroups per CU, hide the list loads)
 template <int WAVES, int CH, bool CAND>
-__global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(CAND ? 6 : 1)))
+void topk_radix_kernel(
     const float* __restrict__ scores, int64_t ld, int64_t n_cols,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ row_starts, int k,
     int32_t* __restrict__ indices, int64_t ld_idx, int32_t* __restrict__ topk_length,
@@ -183,9 +185,9 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
   // CAND: the entries are read as two 16-byte (key, column) pairs per lane
   // and chunk, inside the row's cap entries; entries >= nsel become key 0.
   const int wbase = wave * 256 * CH;
-  float4 raw[CH];
+  float4 raw[CAND ? 1 : CH];  // the scores (CAND: formed from the keys where used)
   u32x4 kreg[CH];
-  u32x4 creg[CAND ? CH : 1];
+  u32x2 creg[CAND ? CH : 1];  // CAND: the entries' columns, two 16-bit ones per word
   if constexpr (CAND) {
     u32x4 pr[CH][2];  // only the filled entries are read
 #pragma unroll
@@ -202,9 +204,8 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
                       col + 1 < nsel ? float_to_key(__uint_as_float(pr[c][0][2])) : 0u,
                       col + 2 < nsel ? float_to_key(__uint_as_float(pr[c][1][0])) : 0u,
                       col + 3 < nsel ? float_to_key(__uint_as_float(pr[c][1][2])) : 0u};
-      creg[c] = u32x4{pr[c][0][1], pr[c][0][3], pr[c][1][1], pr[c][1][3]};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) raw[c][e] = key_to_float(kreg[c][e]);
+      creg[c] = u32x2{(pr[c][0][1] & 0xffffu) | (pr[c][0][3] << 16),
+                      (pr[c][1][1] & 0xffffu) | (pr[c][1][3] << 16)};
     }
   } else {
 #pragma unroll
@@ -254,13 +255,18 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
   }
   const float flo = key_to_float(~knmax), span = key_to_float(kmax) - flo;
   const LinearBuckets lb{flo, span > 0.0f ? (float)kBins / span : 0.0f};
-  uint16_t bk[CH][4];
+  // bucket of entry (c, e): stored, or (CAND, fewer registers) formed again
+  uint16_t bk[CAND ? 1 : CH][4];
+  auto bucket = [&](int c, int e) -> uint32_t {
+    if constexpr (CAND) return (uint32_t)lb.of_value(key_to_float(kreg[c][e]));
+    else return bk[c][e];
+  };
 #pragma unroll
   for (int c = 0; c < CH; ++c)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      bk[c][e] = (uint16_t)lb.of_value(raw[c][e]);
-      if (kreg[c][e] != 0u) atomicAdd(&hist[bk[c][e]], 1u);
+      if constexpr (!CAND) bk[c][e] = (uint16_t)lb.of_value(raw[c][e]);
+      if (kreg[c][e] != 0u) atomicAdd(&hist[bucket(c, e)], 1u);
     }
   __syncthreads();
   find_bucket<WAVES>(hist, (uint32_t)k, s_wave[0], s_sel);
@@ -271,7 +277,7 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
   for (int c = 0; c < CH; ++c)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const bool mem = kreg[c][e] != 0u && bk[c][e] == bstar;
+      const bool mem = kreg[c][e] != 0u && bucket(c, e) == bstar;
       const uint64_t bal = ballot(mem);
       if (bal != 0u) {  // uniform
         uint32_t at = 0u;
@@ -306,7 +312,7 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
       for (int c = 0; c < CH; ++c)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (kreg[c][e] != 0u && bk[c][e] == bstar) f(kreg[c][e]);
+          if (kreg[c][e] != 0u && bucket(c, e) == bstar) f(kreg[c][e]);
     });
   }
 
@@ -320,7 +326,8 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
     for (int c = 0; c < CH; ++c)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (kreg[c][e] > theta) s += __builtin_amdgcn_exp2f((raw[c][e] - vmax) * kLog2e);
+        if (kreg[c][e] > theta)
+          s += __builtin_amdgcn_exp2f((key_to_float(kreg[c][e]) - vmax) * kLog2e);
     float ssum = block_sum(s);
     if (need_eq)
       ssum += (float)need_eq * __builtin_amdgcn_exp2f((key_to_float(theta) - vmax) * kLog2e);
@@ -370,13 +377,14 @@ __global__ __launch_bounds__(64 * WAVES) void topk_radix_kernel(
       const uint32_t pos = ng + min(nq, need_eq);
       const bool take = (is_gt || (is_eq && nq < need_eq)) && pos < (uint32_t)k;
       const int32_t gcol =
-          base + (CAND ? (int32_t)creg[c][e] : wbase + c * 256 + lane * 4 + e);
+          base + (CAND ? (int32_t)((creg[c][e >> 1] >> (16 * (e & 1))) & 0xffffu)
+                       : wbase + c * 256 + lane * 4 + e);
       if (staged) {
         hist[take ? pos : (uint32_t)(kBins + lane)] = (uint32_t)gcol;
       } else if (take) {
         out_idx[pos] = gcol;
         if (out_val) out_val[pos] = key_to_float(key);
-        if (out_soft) out_soft[pos] = __builtin_amdgcn_exp2f((raw[c][e] - lse) * kLog2e);
+        if (out_soft) out_soft[pos] = __builtin_amdgcn_exp2f((key_to_float(key) - lse) * kLog2e);
       }
       cnt += (is_gt ? 1u : 0u) + (is_eq ? 0x10000u : 0u);
     }

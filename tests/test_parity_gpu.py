@@ -435,9 +435,9 @@ def _assert_topk_is_oracle(idx, tl, scores, seq_lens, k, row_starts, n_cols=None
     assert np.array_equal(i64(tl), ref_len)
 
 
-def _pipeline(wl, max_seqlen=None):
+def _pipeline(wl, max_seqlen=None, fused=None):
     idx, tl = dsa.indexer_topk(wl.q_idx, wl.k_idx, wl.w, wl.cu_seqlens, wl.topk,
-                               max_seqlen=max_seqlen)
+                               max_seqlen=max_seqlen, fused=fused)[:2]
     out, lse, mx = dsa.dsa_sparse_attn_fwd(wl.q, wl.kv, idx, topk_length=tl, attn_sink=wl.sink,
                                            softmax_scale=wl.scale)
     return idx, tl, out, lse, mx
@@ -542,10 +542,13 @@ def _c4_rows(T, chunk_rows, K):
     return np.sort(np.concatenate([base, extra]))
 
 
-def test_config4_sampled():
-    say("config 4")
+@pytest.mark.parametrize("fused", [False, True], ids=["score_chunks", "candidates"])
+def test_config4_sampled(fused):
+    """Both indexer + top-K paths at T = 65536: score chunks + dsa_topk, and
+    the combined path's candidate buffer."""
+    say("config 4", "candidates" if fused else "score chunks")
     wl = make_config(4, device=DEV)
-    idx, tl, out, lse, mx = _pipeline(wl)
+    idx, tl, out, lse, mx = _pipeline(wl, fused=fused)
     torch.cuda.synchronize()
     rs, sl = _meta(wl)
     rows = _c4_rows(wl.T, dsa.chunk_rows(wl.T, wl.T), wl.topk)
@@ -570,6 +573,8 @@ def test_config4_sampled():
     assert np.all(np.where(valid, gi <= t[:, None], True))
     assert np.all(np.diff(np.where(valid, gi, np.iinfo(np.int32).max), axis=1)[:, :] >= 0)
     assert torch.isfinite(lse).all() and torch.isfinite(out.float()).all()
+    if fused:
+        return
     # stress variant of the attention (same indexer inputs, so the same selection;
     # queries scaled to logits of std ~4, sinks near the LSE)
     del out, lse, mx
