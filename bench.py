@@ -2,8 +2,11 @@
 """Benchmark of the DSA forward hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-metadata -> lightning-indexer scores (row chunks under a 2 GiB score cap) ->
-radix top-K -> sparse attention forward. Workloads 1-5 are packed documents
+metadata -> lightning-indexer scores -> radix top-K -> sparse attention
+forward. Indexer + top-K run (--path auto) as dsa_indexer_topk_fused with a
+candidate buffer for bf16 rows longer than 4096 columns (no dense scores),
+otherwise as row chunks of scores under a 2 GiB cap followed by dsa_topk.
+Workloads 1-5 are packed documents
 (plain causal mask); 6 and 7 are split-query / compressed-key workloads
 (ratio-causal mask with query causal offsets). Inputs are generated on the
 GPU before the timed region and stay resident in HBM.
@@ -17,8 +20,9 @@ TFLOP/s (algorithmic FLOP: 2*(D_qk+D_v) per valid slot per head, over the
 attention kernel's time measured with HIP events inside the timed steps);
 `indexer_topk_rows_per_s` is the second half of the metric; `ms_per_step` is
 the whole path. Every launch of a timed step is bracketed by its own pair of
-HIP events on the launch stream, so each stage (indexer, top-K, attention)
-has its own kernel time and roofline in `rooflines`; `roofline` is the one of
+HIP events on the launch stream, so each stage (indexer, top-K, or the
+combined call; attention) has its own kernel time and roofline in
+`rooflines`; `roofline` is the one of
 the stage with the most kernel time (the dominant kernel). `cpu_baseline` is
 the fp64 CPU oracle, run by a pool of single-threaded worker processes (one
 per host core available, at most 16) on a bounded seeded sample of the same
