@@ -10,7 +10,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 SOURCES = ["abi.hip", "indexer.hip", "indexer_fp8.hip", "topk.hip", "sparse_attn.hip",
-           "sparse_attn_bwd.hip"]
+           "sparse_gqa.hip", "sparse_attn_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 FLAGS = [

@@ -102,6 +102,9 @@ struct AttnArgs {
 };
 
 hipError_t launch_sparse_attn(const AttnArgs& a, int D_qk, int D_v, hipStream_t st);
+// The block-routed GQA form (D_qk = D_v = 256, separate V, H <= 16, K and V
+// spans below 2^31 bytes); hipErrorInvalidValue for anything else.
+hipError_t launch_sparse_gqa(AttnArgs a, hipStream_t st);
 
 // Sparse attention backward (shared latent KV, D_v = 512).
 struct BwdArgs {

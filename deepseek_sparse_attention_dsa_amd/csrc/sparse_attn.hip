@@ -693,7 +693,14 @@ hipError_t launch_sparse_attn(const AttnArgs& a, int D_qk, int D_v, hipStream_t 
   if (D_qk == 576 && D_v == 512 && shared) return launch_cfg<576, 512, true>(a, st);
   if (D_qk == 512 && D_v == 512 && shared) return launch_cfg<512, 512, true>(a, st);
   if (D_qk == 256 && D_v == 256 && shared) return launch_cfg<256, 256, true>(a, st);
-  if (D_qk == 256 && D_v == 256 && !shared) return launch_cfg<256, 256, false>(a, st);
+  if (D_qk == 256 && D_v == 256 && !shared) {
+    // at most 16 heads: the one-wave-per-row kernel of sparse_gqa.hip
+    if (a.H <= 16) {
+      const hipError_t e = launch_sparse_gqa(a, st);
+      if (e != hipErrorInvalidValue) return e;
+    }
+    return launch_cfg<256, 256, false>(a, st);
+  }
   return hipErrorInvalidValue;
 }
 

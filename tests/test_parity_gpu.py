@@ -363,6 +363,70 @@ def test_attention_reference_paths():
                         np.arange(4), atol_out=0.1)
 
 
+@pytest.mark.parametrize("H,kw,tl_mode,sink,stress,dup", [
+    (12, 512, "none", False, False, False),
+    (16, 96, "prefix", True, True, False),
+    (1, 33, "none", True, False, False),
+    (5, 200, "prefix", False, True, False),
+    (13, 47, "none", True, True, True),
+    (16, 1, "none", False, False, False),
+])
+def test_gqa_one_wave_per_row(H, kw, tl_mode, sink, stress, dup):
+    """The block-routed GQA form (D 256, separate V, at most 16 heads) runs on
+    its own one-wave-per-row kernel: head counts 1..16, widths that are not
+    multiples of the 32-slot tile, sinks, topk_length prefixes, duplicates."""
+    say("gqa", H, kw, tl_mode, sink, stress, dup)
+    T_kv, T_q = 700, 37
+    wl, q, kv, v, idx, tl = _attn_case(T_kv, T_q, H, 256, 256, False, kw, seed=H * 11 + kw,
+                                       tl_mode=tl_mode, sink=sink, stress=stress, dup=dup)
+    out, lse, mx = dsa.dsa_sparse_attn_fwd(q, kv, idx, topk_length=tl, attn_sink=wl.sink,
+                                           softmax_scale=wl.scale, v=v, d_v=256)
+    torch.cuda.synchronize()
+    check_attention(out, lse, mx, q, kv, v, idx, tl, wl.sink, wl.scale, 256, np.arange(T_q))
+
+
+def test_gqa_edge_rows_and_reference_paths():
+    """Empty rows (all ids invalid, topk_length 0, k_width 0), a single valid
+    slot deep in the row, the first valid key in a later tile, and logits far
+    above the first tile's max (the row runs again with its exact max)."""
+    say("gqa edge rows")
+    H, T_kv, kw = 12, 300, 160
+    wl = make_custom([T_kv], H=H, D_qk=256, D_v=256, shared_kv=False, H_idx=0, seed=21,
+                     device=DEV, value_std=1 / 16)
+    k = wl.kv.clone()
+    v = wl.v.clone()
+    q = wl.q[:8].clone()
+    k[100:, 0] = 32.0
+    q[6:, :, 0] = 64.0  # scaled logits ~ 2048 / 16 = 128 above the others (> 2^64 in exp2)
+    idx = np.full((8, kw), -1, dtype=np.int32)
+    idx[1, 70] = 9                               # one valid slot in the third tile
+    idx[2, :] = T_kv + np.arange(kw)             # every id out of range: empty
+    idx[3, 40:] = np.arange(kw - 40)             # first valid key in the second tile
+    idx[4, ::3] = np.arange(0, kw, 3)            # interleaved -1
+    idx[5, :] = np.arange(kw)                    # topk_length 0: empty
+    idx[6, :] = np.arange(kw)                    # keys 100.. huge from tile 4 on
+    idx[7, :100] = np.arange(100)                # the huge key only in the last tile
+    idx[7, 150] = 150
+    tl = np.full(8, kw, dtype=np.int32)
+    tl[5] = 0
+    idx_t = torch.from_numpy(idx).to(DEV)
+    tl_t = torch.from_numpy(tl).to(DEV)
+    sink = torch.randn((H,), generator=torch.Generator(device=DEV).manual_seed(4), device=DEV)
+    for sk in (None, sink):
+        out, lse, mx = dsa.dsa_sparse_attn_fwd(q, k, idx_t, topk_length=tl_t, attn_sink=sk,
+                                               softmax_scale=1 / 16, v=v, d_v=256)
+        torch.cuda.synchronize()
+        check_attention(out, lse, mx, q, k, v, idx_t, tl_t, sk, 1 / 16, 256, np.arange(8))
+        l = lse.cpu().numpy()
+        assert np.all(np.isposinf(l[[0, 2, 5]]))
+        assert np.all(out[[0, 2, 5]].float().cpu().numpy() == 0)
+    out, lse, mx = dsa.dsa_sparse_attn_fwd(q, k, idx_t[:, :0].contiguous(), softmax_scale=0.1,
+                                           v=v, d_v=256)
+    torch.cuda.synchronize()
+    assert torch.all(torch.isposinf(lse)) and torch.all(out == 0)
+    assert torch.all(torch.isneginf(mx))
+
+
 def test_attention_dense_identity_on_gpu():
     """Top-K covering every causal key and no sink == dense causal attention."""
     say("attention dense identity")
