@@ -101,8 +101,15 @@ def parse():
     p.add_argument("--summarize-counters", nargs="+", metavar="DIR",
                    help="FETCH_DIR WRITE_DIR CAL_FETCH_DIR CAL_WRITE_DIR [SQ_DIR ...]: turn "
                         "rocprofv3 --pmc output folders of this bench (FETCH_SIZE, WRITE_SIZE, "
-                        "then any other counter groups) and of --copy-calibration into "
-                        "profiles/counters_<workload>.json")
+                        "then any other counter groups; several runs of one group as "
+                        "comma-separated folders) and of --copy-calibration into "
+                        "profiles/counters_<workload>.json and .txt")
+    p.add_argument("--counter-trace", default="",
+                   help="with --summarize-counters: rocprofv3 --kernel-trace --stats folder(s) "
+                        "of the same bench command, for the kernels' mean durations")
+    p.add_argument("--counter-notes", default="",
+                   help="with --summarize-counters: a text file put at the top of the .txt "
+                        "summary (the commands that made the runs)")
     p.add_argument("--calibration-mib", type=int, default=1024,
                    help="size the --copy-calibration run used (for --summarize-counters)")
     return p.parse_args()
@@ -156,18 +163,78 @@ def family_of(kernel_name: str):
     return None
 
 
-def _counter_rows(folder: str):
-    """(dispatch id, kernel name, counter, value) from rocprofv3 counter CSVs."""
+def _counter_rows(folders: str):
+    """((run, dispatch id), kernel name, counter, value) from the rocprofv3
+    counter CSVs under one folder or several, comma-separated (one run each,
+    e.g. the same counters over the bench's two indexer + top-K paths)."""
     import csv
     import glob
     rows = []
-    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
-        for r in csv.DictReader(open(f)):
-            rows.append((int(r.get("Dispatch_Id", 0) or 0), r["Kernel_Name"], r["Counter_Name"],
-                         float(r["Counter_Value"])))
-    if not rows:
-        raise SystemExit(f"no counter rows under {folder}")
+    for i, folder in enumerate(folders.split(",")):
+        found = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+        if not found:
+            raise SystemExit(f"no counter rows under {folder}")
+        for f in found:
+            for r in csv.DictReader(open(f)):
+                rows.append(((i, int(r.get("Dispatch_Id", 0) or 0)), r["Kernel_Name"],
+                             r["Counter_Name"], float(r["Counter_Value"])))
     return rows
+
+
+def _trace_avg_ns(folders: str):
+    """{family: mean kernel duration in ns} from rocprofv3 --stats kernel_stats.csv files."""
+    import csv
+    import glob
+    acc = {}
+    for folder in folders.split(","):
+        for f in glob.glob(os.path.join(folder, "**", "*kernel_stats.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                fam = family_of(r["Name"])
+                if fam is not None:
+                    tot, n = acc.get(fam, (0.0, 0))
+                    acc[fam] = (tot + float(r["TotalDurationNs"]), n + int(r["Calls"]))
+    return {f: tot / n for f, (tot, n) in acc.items() if n}
+
+
+def render_counters(res, notes: str = "") -> str:
+    """Text summary of a counters JSON: per kernel family, the HBM bytes per
+    launch and the figures derived from the SQ and GRBM counters."""
+    out = [notes.rstrip() + "\n"] if notes else []
+    out.append(f"workload {res['workload']}; calibration (1 GiB device copy): FETCH_SIZE x "
+               f"{res['fetch_scale']:.3f}, WRITE_SIZE x {res['write_scale']:.3f}.")
+    out.append("Derived: clock = GRBM_GUI_ACTIVE / 8 XCDs / mean kernel time (kernel trace); "
+               "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8); "
+               "MFMA FLOP = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16; co-exec = "
+               "SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES; TA busy = TA_TA_BUSY / "
+               "(256 CUs x GRBM_GUI_ACTIVE / 8).\n")
+    for fam, k in res["kernels"].items():
+        out.append(f"{fam}:")
+        grbm = k.get("GRBM_GUI_ACTIVE")
+        line = []
+        if grbm and k.get("kernel_avg_ns"):
+            line.append(f"shader clock under load {grbm / 8 / k['kernel_avg_ns']:.2f} GHz "
+                        f"(kernel {k['kernel_avg_ns'] / 1e3:.1f} us)")
+        if grbm and "SQ_VALU_MFMA_BUSY_CYCLES" in k:
+            line.append(f"MFMA busy {100 * k['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * grbm / 8):.1f}% "
+                        "of SIMD cycles")
+        if line:
+            out.append("  " + "; ".join(line))
+        if k.get("SQ_INSTS_VALU_MFMA_MOPS_BF16"):
+            co = k.get("SQ_VALU_MFMA_COEXEC_CYCLES", 0) / max(k["SQ_VALU_MFMA_BUSY_CYCLES"], 1)
+            out.append(f"  MFMA FLOP {512 * k['SQ_INSTS_VALU_MFMA_MOPS_BF16']:.3e} per launch; "
+                       f"VALU/MFMA co-execution {100 * co:.1f}% of MFMA-busy cycles")
+        if "hbm_bytes_per_launch" in k:
+            out.append(f"  L2-to-fabric traffic (reads include Infinity Cache hits): FETCH "
+                       f"{k['fetch_bytes_per_launch'] / 1e9:.3f} GB + WRITE "
+                       f"{k['write_bytes_per_launch'] / 1e9:.3f} GB per launch")
+        if grbm and "TA_TA_BUSY" in k:
+            out.append(f"  TA busy {100 * k['TA_TA_BUSY'] / (256 * grbm / 8):.1f}%")
+        for c in ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "TCP_PENDING_STALL_CYCLES",
+                  "TCC_HIT_sum", "TCC_MISS_sum"):
+            if c in k:
+                out.append(f"  {c} {k[c]:.3e}")
+        out.append(f"  kernel source sha256 {k['kernel_source_sha256']}\n")
+    return "\n".join(out) + "\n"
 
 
 def _per_family(rows):
@@ -223,10 +290,17 @@ def summarize_counters(args):
     for fam, k in res["kernels"].items():
         if "fetch_bytes_per_launch" in k and "write_bytes_per_launch" in k:
             k["hbm_bytes_per_launch"] = k["fetch_bytes_per_launch"] + k["write_bytes_per_launch"]
+    if args.counter_trace:
+        for fam, ns in _trace_avg_ns(args.counter_trace).items():
+            if fam in res["kernels"]:
+                res["kernels"][fam]["kernel_avg_ns"] = ns
     path = os.path.join(PROFILES, f"counters_{res['workload']}.json")
     with open(path, "w") as f:
         json.dump(res, f, indent=1)
         f.write("\n")
+    notes = open(args.counter_notes).read() if args.counter_notes else ""
+    with open(os.path.join(PROFILES, f"counters_{res['workload']}.txt"), "w") as f:
+        f.write(render_counters(res, notes))
     print(json.dumps(res), flush=True)
 
 
