@@ -768,10 +768,13 @@ def main():
         bms = float(np.mean(bt))
         # the five products per valid slot and head: s, dP, dq, dk, dv
         bflop = 2.0 * (3 * wl.D_qk + 2 * wl.D_v) * wl.H * cnt["valid_slots"]
+        tiles = dsa.dsa_sparse_attn_bwd_kv_tiles(wl.kv.shape[0], K)
         stages["attention_backward"] = {"ms": bms, "tflops": bflop / bms / 1e9,
                                         "frac_bf16_peak": bflop / bms / 1e9 / PEAK_BF16_TFLOPS,
                                         "algorithmic_flop": bflop,
-                                        "dkv_row_bytes": 2.0 * wl.D_qk * cnt["valid_slots"]}
+                                        "dkv_scheme": "kv_tiles" if tiles else "per_slot_rows"}
+        if not tiles:  # bf16 dkv rows written and read back once per valid slot
+            stages["attention_backward"]["dkv_row_bytes"] = 2.0 * wl.D_qk * cnt["valid_slots"]
 
     rec = {
         "metric": METRIC, "value": attn_tflops, "unit": "TFLOP/s", "n_gpus": 1,

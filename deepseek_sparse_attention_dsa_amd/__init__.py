@@ -28,7 +28,7 @@ __all__ = [
     "dsa_topk_workspace_bytes",
     "dsa_indexer_topk_fused", "dsa_indexer_topk_cand_buffer_size", "DSA_FUSED_MAX_COLS",
     "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_workspace_bytes",
-    "indexer_topk", "chunk_rows",
+    "dsa_sparse_attn_bwd_kv_tiles", "indexer_topk", "chunk_rows",
 ]
 
 DSA_OK, DSA_ERR_TYPE, DSA_ERR_VALUE, DSA_ERR_RUNTIME = 0, 1, 2, 3
@@ -64,6 +64,7 @@ _SIGNATURES = {
     "dsa_topk": ([_P, _I64, _I64, _I64, _P, _P, _I32, _P, _I64, _P, _P, _P], ctypes.c_int),
     "dsa_topk_workspace_bytes": ([_I64, _I64, _I32], ctypes.c_int64),
     "dsa_sparse_attn_bwd_workspace_bytes": ([_I64, _I32, _I64, _I32, _I32], ctypes.c_int64),
+    "dsa_sparse_attn_bwd_kv_tiles": ([_I64, _I32], ctypes.c_int),
     "dsa_sparse_attn_bwd": ([_P, _I64, _I32, _I32, _P, _I64, _I64, _I32, _P, _I64, _I32, _P, _P,
                              _F32, _P, _P, _P, _P, _P, _P, _P, _I64, _P], ctypes.c_int),
     "dsa_sparse_attn_fwd": ([_P, _I64, _I32, _I32, _P, _I64, _I64, _P, _I64, _I32, _P, _I64,
@@ -510,6 +511,15 @@ def dsa_sparse_attn_bwd_workspace_bytes(T_q: int, H: int, T_kv: int, D_qk: int,
     if n < 0:
         raise ValueError("sizes out of contract for dsa_sparse_attn_bwd")
     return n
+
+
+def dsa_sparse_attn_bwd_kv_tiles(T_kv: int, k_width: int) -> bool:
+    """Whether dsa_sparse_attn_bwd computes dkv by KV tiles (dense selections)
+    rather than by per-slot rows, for these sizes."""
+    r = int(load_library().dsa_sparse_attn_bwd_kv_tiles(T_kv, k_width))
+    if r < 0:
+        raise ValueError("T_kv and k_width must be >= 0")
+    return r == 1
 
 
 def dsa_sparse_attn_bwd(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,

@@ -404,37 +404,62 @@ static int64_t bwd_fixed_bytes(int64_t T_q, int32_t H, int64_t T_kv, int32_t D_q
          up256((T_kv + 1) * 4) + up256(256 * 4);
 }
 
-// Per query row of a chunk: P and dS (bf16 [Kw, HP]), the dkv rows of its
-// slots (bf16 [parts, Kw, D_qk]) and, per slot, its entry of the sorted slot
-// list and the radix sort's two key / value buffers; plus the sort's digit
-// histograms, 256 per 4096 slots.
-struct BwdRow {
-  int64_t p, c, l, kw;
+// Per query row of a chunk: P and dS (bf16 [Kw, HP]) and then either
+//  * (per-slot dkv) the dkv rows of its slots (bf16 [parts, Kw, D_qk]) and,
+//    per slot, its entry of the sorted slot list and the radix sort's two key
+//    / value buffers; plus the sort's digit histograms, 256 per 4096 slots;
+//  * (KV-tile dkv) its slot map (int16 [ld_map]) and queue entry; plus per
+//    part of 64 rows an fp32 partial [ld_map, D_qk] and its tile flags.
+struct BwdShape {
+  bool tiles;
+  int64_t p, c, l, kw, ld_map, d_qk;
 };
-static BwdRow bwd_row_bytes(int32_t H, int32_t k_width, int32_t D_qk) {
+static BwdShape bwd_shape(int64_t T_kv, int32_t H, int32_t k_width, int32_t D_qk) {
   const int64_t hp = (H + 31) / 32 * 32, kw = ((int64_t)k_width + 31) / 32 * 32;
   const int64_t parts = hp % 64 == 0 ? hp / 64 : hp / 32;
-  return BwdRow{kw * hp * 2, parts * kw * D_qk * 2, kw * 4, kw};
+  const bool tiles = dsa::bwd_uses_kv_tiles(T_kv, k_width);
+  const int64_t ld_map = (T_kv + dsa::kBwdTileKV - 1) / dsa::kBwdTileKV * dsa::kBwdTileKV;
+  return BwdShape{tiles, kw * hp * 2, parts * kw * D_qk * 2, kw * 4, kw, ld_map, D_qk};
 }
-static int64_t bwd_hist_bytes(const BwdRow& r, int64_t rows) {
+static int64_t bwd_hist_bytes(const BwdShape& r, int64_t rows) {
   return (rows * r.kw + 4095) / 4096 * 256 * 4;
 }
-static int64_t bwd_chunk_bytes(const BwdRow& r, int64_t rows) {
+static int64_t bwd_chunk_bytes(const BwdShape& r, int64_t rows) {
+  if (r.tiles) {
+    const int64_t np = (rows + dsa::kBwdTileRows - 1) / dsa::kBwdTileRows;
+    return 2 * up256(rows * r.p) + up256(rows * r.ld_map * 2) +
+           up256(np * r.ld_map * r.d_qk * 4) + up256(np * (r.ld_map / dsa::kBwdTileKV) * 4) +
+           up256(4) + up256(rows * 4);
+  }
   return 2 * up256(rows * r.p) + up256(rows * r.c) + 5 * up256(rows * r.l) +
          up256(bwd_hist_bytes(r, rows));
 }
-static int64_t bwd_per_row(const BwdRow& r) { return 2 * r.p + r.c + 5 * r.l + r.kw / 16 + 1; }
+// The most rows (at least 1, at most T_q) whose chunk buffers take at most
+// `budget` bytes (the buffers grow with the rows).
+static int64_t bwd_fit_rows(const BwdShape& r, int64_t T_q, int64_t budget) {
+  int64_t lo = 1, hi = T_q > 1 ? T_q : 1;
+  if (r.kw > 0 && hi > INT32_MAX / r.kw) hi = INT32_MAX / r.kw;  // slot numbers are int32
+  if (bwd_chunk_bytes(r, hi) <= budget) return hi;
+  while (hi - lo > 1) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    if (bwd_chunk_bytes(r, mid) <= budget) lo = mid; else hi = mid;
+  }
+  return lo;
+}
 
 int64_t dsa_sparse_attn_bwd_workspace_bytes(int64_t T_q, int32_t H, int64_t T_kv, int32_t D_qk,
                                             int32_t k_width) {
   if (T_q < 0 || T_q > INT32_MAX || H < 1 || H > DSA_MAX_HEADS || T_kv < 0 || T_kv > INT32_MAX ||
       (D_qk != 576 && D_qk != 512) || k_width < 0)
     return -1;
-  const BwdRow row = bwd_row_bytes(H, k_width, D_qk);
-  const int64_t per = bwd_per_row(row);
-  int64_t rows = per ? ((int64_t)1 << 32) / per : T_q;  // chunk buffers within 4 GiB
-  rows = rows < 1 ? 1 : (rows > T_q ? T_q : rows);
+  const BwdShape row = bwd_shape(T_kv, H, k_width, D_qk);
+  const int64_t rows = bwd_fit_rows(row, T_q, (int64_t)1 << 32);  // chunk buffers within 4 GiB
   return bwd_fixed_bytes(T_q, H, T_kv, D_qk) + bwd_chunk_bytes(row, rows);
+}
+
+int dsa_sparse_attn_bwd_kv_tiles(int64_t T_kv, int32_t k_width) {
+  if (T_kv < 0 || k_width < 0) return -1;
+  return dsa::bwd_uses_kv_tiles(T_kv, k_width) ? 1 : 0;
 }
 
 // The backward of both entry points. `noalloc`: the workspace is the no-alloc
@@ -500,7 +525,7 @@ static int bwd_run(const char* fn, const void* q, int64_t T_q, int32_t H, int32_
           DSA_ERR_VALUE, "%s: q, kv, out, dout, dq, dkv need 16-byte and workspace 256-byte "
           "alignment", fn);
   const int64_t fixed = bwd_fixed_bytes(T_q, H, T_kv, D_qk);
-  const BwdRow row = bwd_row_bytes(H, k_width, D_qk);
+  const BwdShape row = bwd_shape(T_kv, H, k_width, D_qk);
   if (noalloc) {
     REQUIRE(fixed + bwd_chunk_bytes(row, 1) <= workspace_bytes, DSA_ERR_VALUE,
             "%s: these sizes need %lld bytes of scratch for one query row, more than the "
@@ -553,23 +578,27 @@ static int bwd_run(const char* fn, const void* q, int64_t T_q, int32_t H, int32_
   a.offs = (int32_t*)take((T_kv + 1) * 4);
   a.sort_tot = (uint32_t*)take(256 * 4);
   // the largest chunk of rows whose buffers fit the rest of the workspace
-  // (slot numbers rows * Kw are int32)
-  int64_t chunk = T_q > 0 ? T_q : 1;
-  if (row.kw > 0 && chunk > INT32_MAX / row.kw) chunk = INT32_MAX / row.kw;
-  while (chunk > 1 && fixed + bwd_chunk_bytes(row, chunk) > workspace_bytes) {
-    const int64_t per = bwd_per_row(row);
-    const int64_t fit = per ? (workspace_bytes - fixed) / per : chunk;
-    chunk = fit < chunk ? (fit > 1 ? fit : 1) : chunk - 1;
-  }
+  const int64_t chunk = bwd_fit_rows(row, T_q, workspace_bytes - fixed);
   a.wsP = (uint16_t*)take(chunk * row.p);
   a.wsD = (uint16_t*)take(chunk * row.p);
-  a.wsC = (uint16_t*)take(chunk * row.c);
-  a.list = (int32_t*)take(chunk * row.l);
-  for (int k = 0; k < 2; ++k) {
-    a.sort_keys[k] = (int32_t*)take(chunk * row.l);
-    a.sort_vals[k] = (int32_t*)take(chunk * row.l);
+  a.tiles = row.tiles;
+  if (row.tiles) {
+    const int64_t np = (chunk + dsa::kBwdTileRows - 1) / dsa::kBwdTileRows;
+    a.ld_map = row.ld_map;
+    a.map = (int16_t*)take(chunk * row.ld_map * 2);
+    a.part = (float*)take(np * row.ld_map * D_qk * 4);
+    a.part_flag = (int32_t*)take(np * (row.ld_map / dsa::kBwdTileKV) * 4);
+    a.dup_count = (uint32_t*)take(4);
+    a.dup_rows = (int32_t*)take(chunk * 4);
+  } else {
+    a.wsC = (uint16_t*)take(chunk * row.c);
+    a.list = (int32_t*)take(chunk * row.l);
+    for (int k = 0; k < 2; ++k) {
+      a.sort_keys[k] = (int32_t*)take(chunk * row.l);
+      a.sort_vals[k] = (int32_t*)take(chunk * row.l);
+    }
+    a.sort_hist = (uint32_t*)take(bwd_hist_bytes(row, chunk));
   }
-  a.sort_hist = (uint32_t*)take(bwd_hist_bytes(row, chunk));
   a.Kw = (k_width + 31) / 32 * 32;
   a.dq = (uint16_t*)dq;
   a.dkv = (uint16_t*)dkv;

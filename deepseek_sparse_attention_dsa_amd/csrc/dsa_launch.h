@@ -143,7 +143,28 @@ struct BwdArgs {
   int64_t row0;             // first row of the current chunk
   uint32_t span_kv;         // launcher: bytes of kv read through a buffer descriptor
   uint32_t row_bytes;       // launcher: ld_kv * 2
+  // KV-tile dkv (dense selections, see bwd_uses_kv_tiles): per chunk row the
+  // slot of each KV row ([chunk, ld_map] int16, -1: none), fp32 partial sums
+  // per (row part, KV tile) and whether each was written, rows with repeated
+  // ids (their slots are merged before the tile pass).
+  bool tiles;
+  int16_t* map;             // workspace [chunk, ld_map]
+  int64_t ld_map;           // T_kv rounded up to the KV tile
+  float* part;              // workspace [n_parts, ld_map, D_qk]
+  int32_t* part_flag;       // workspace [n_parts, ld_map / tile]
+  uint32_t* dup_count;      // workspace [1]
+  int32_t* dup_rows;        // workspace [chunk]
 };
+
+// Whether the backward takes the KV-tile dkv (dense selections: at least one
+// key in eight selected per row, up to 32768 KV rows and 8192 slots); the
+// workspace layout follows the same rule.
+constexpr int kBwdTileKV = 128;    // KV rows per tile
+constexpr int kBwdTileRows = 64;   // query rows per part
+inline bool bwd_uses_kv_tiles(int64_t T_kv, int32_t k_width) {
+  const int64_t kw = ((int64_t)k_width + 31) / 32 * 32;
+  return T_kv > 0 && T_kv <= 32768 && k_width > 0 && kw <= 8192 && 8 * (int64_t)k_width >= T_kv;
+}
 
 hipError_t launch_sparse_attn_bwd(BwdArgs a, int64_t chunk, hipStream_t st);
 

@@ -23,15 +23,23 @@
 //  * bwd_dq_ring_kernel: dq = dS . K with both operands read transposed from
 //    LDS (ds_read_b64_tr_b16), two waves per 32-head block splitting the
 //    dims; K gathered into the same copy ring as bwd_pds_kernel.
-//  * bwd_dkv_kernel: per tile, dS^T . q + P^T . dout (the query's q and dout
-//    staged in LDS), each slot's row written once as bf16 (per 64-head part).
-//  * bwd_count / bwd_scan: slots per KV row and the offsets of their lists;
-//    bwd_sort_{hist,scan,scatter}: a stable radix sort of the chunk's valid
-//    slots by KV row, giving each KV row the ascending list of the slot rows
-//    written for it (no atomics decide an order, so dkv is reproducible).
-//  * bwd_reduce_kernel: one workgroup per KV row sums its list (and parts) in
-//    fp32 into the dkv workspace; no atomics touch the data.
+//  * dkv, when rows select a large share of the KV rows (KV tiles):
+//    bwd_map_kernel: each row's slot per KV row (int16) and the queue of rows
+//    with repeated ids; bwd_merge_kernel: their repeated slots folded into
+//    the lowest one (ascending slot order); bwd_dkv_tile_kernel: per tile of
+//    128 KV rows and part of 64 query rows, dS^T . q + P^T . dout over the
+//    part's rows and heads, accumulated in registers (an fp32 partial per
+//    part); bwd_tile_reduce_kernel: the parts summed in ascending order.
+//  * dkv otherwise (per-slot rows): bwd_dkv_kernel: per tile, dS^T . q +
+//    P^T . dout (the query's q and dout staged in LDS), each slot's row
+//    written once as bf16 (per 64-head part); bwd_count / bwd_scan: slots per
+//    KV row and the offsets of their lists; bwd_sort_{hist,scan,scatter}: a
+//    stable radix sort of the chunk's valid slots by KV row, giving each KV
+//    row the ascending list of the slot rows written for it;
+//    bwd_reduce_kernel: one workgroup per KV row sums its list (and parts) in
+//    fp32 into the dkv workspace.
 //  * bwd_convert_kernel: fp32 workspace -> bf16 dkv.
+// No atomics decide the order of any sum, so dkv is reproducible.
 #include "dsa_device.h"
 #include "dsa_launch.h"
 
@@ -845,6 +853,387 @@ __global__ __launch_bounds__(256) void bwd_convert_kernel(const float* p, uint16
   if (i < n) o[i] = (uint16_t)f32_to_bf16_bits(p[i]);
 }
 
+// ------------------------------------------------ KV-tile dkv (dense rows) --
+// When each row selects a large share of the KV rows, dkv is computed per
+// tile of 128 KV rows as a dense product over the query rows that select
+// into it, instead of one dkv row per slot:
+//   dkv[j] += sum over rows t, heads h of  dS[t, slot_t(j), h] q[t, h]
+//                                        + P[t, slot_t(j), h] dout[t, h]
+// (zero where row t selects no slot for j). bwd_map_kernel writes, per row,
+// the slot that selects each KV row; bwd_merge_kernel folds repeated ids of
+// a row into the lowest such slot (sums in ascending slot order), after the
+// dq pass has read the per-slot values; bwd_dkv_tile_kernel accumulates one
+// (64-row part, KV tile) pair in registers and writes it as an fp32 partial;
+// bwd_tile_reduce_kernel adds the parts of each KV row in ascending order.
+// No atomics decide any sum, so dkv is reproducible.
+
+// Slot of each KV row for one query row (the lowest slot when an id repeats;
+// -1 where none), in windows of 8192 KV rows; rows with a repeated id are
+// queued for the merge.
+__global__ __launch_bounds__(256) void bwd_map_kernel(BwdArgs a) {
+  constexpr int W = 8192;
+  __shared__ int32_t s_m[W];
+  __shared__ int32_t s_dup;
+  const int tid = threadIdx.x;
+  const int64_t rc = blockIdx.x;
+  const int64_t t = a.row0 + rc;
+  const int L = row_len(a, t);
+  const int32_t* ix = a.indices + t * a.ld_idx;
+  if (tid == 0) s_dup = 0;
+  for (int64_t w0 = 0; w0 < a.ld_map; w0 += W) {
+    const int nw = (int)(a.ld_map - w0 < W ? a.ld_map - w0 : W);  // a multiple of 128
+    for (int j = tid; j < nw; j += 256) s_m[j] = INT32_MAX;
+    __syncthreads();
+    for (int s = tid; s < L; s += 256) {
+      const int32_t v = ix[s];
+      if (v >= 0 && v < a.T_kv && v >= w0 && v - w0 < nw) atomicMin(&s_m[v - w0], s);
+    }
+    __syncthreads();
+    for (int s = tid; s < L; s += 256) {
+      const int32_t v = ix[s];
+      if (v >= 0 && v < a.T_kv && v >= w0 && v - w0 < nw && s_m[v - w0] != s) s_dup = 1;
+    }
+    uint32_t* out = reinterpret_cast<uint32_t*>(a.map + rc * a.ld_map + w0);
+    for (int j = 2 * tid; j < nw; j += 512) {
+      const int32_t lo = s_m[j], hi = s_m[j + 1];
+      out[j >> 1] = (lo == INT32_MAX ? 0xffffu : (uint32_t)lo) |
+                    ((hi == INT32_MAX ? 0xffffu : (uint32_t)hi) << 16);
+    }
+    __syncthreads();
+  }
+  if (tid == 0 && s_dup) {
+    const uint32_t pos = atomicAdd(a.dup_count, 1u);
+    a.dup_rows[pos] = (int32_t)rc;
+  }
+}
+
+// For each queued row: its (id, slot) pairs sorted (bitonic, in LDS); each
+// run of one id with more than one slot is summed in ascending slot order,
+// in fp32, into the run's lowest slot (P and dS, every head).
+__global__ __launch_bounds__(256) void bwd_merge_kernel(BwdArgs a) {
+  constexpr int NMAX = 8192;  // slots per row (k_width rounded up to 32)
+  constexpr uint32_t kNone = 0xffffffffu;
+  __shared__ uint32_t s_k[NMAX];
+  if (blockIdx.x >= *a.dup_count) return;  // uniform
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t rc = a.dup_rows[blockIdx.x];
+  const int64_t t = a.row0 + rc;
+  const int L = row_len(a, t);
+  const int32_t* ix = a.indices + t * a.ld_idx;
+  int n2 = 64;
+  while (n2 < L) n2 <<= 1;
+  for (int i = tid; i < n2; i += 256) {
+    uint32_t k = kNone;
+    if (i < L) {
+      const int32_t v = ix[i];
+      if (v >= 0 && v < a.T_kv) k = ((uint32_t)v << 13) | (uint32_t)i;
+    }
+    s_k[i] = k;
+  }
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < n2; i += 256) {
+        const int o = i ^ j;
+        if (o > i) {
+          const uint32_t x = s_k[i], y = s_k[o];
+          if ((x > y) == ((i & k) == 0)) {
+            s_k[i] = y;
+            s_k[o] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int hp = (a.H + 31) / 32 * 32;
+  uint16_t* P = a.wsP + rc * (int64_t)a.Kw * hp;
+  uint16_t* D = a.wsD + rc * (int64_t)a.Kw * hp;
+  for (int i = wave; i < n2; i += 4) {
+    const uint32_t k = s_k[i];
+    if (k == kNone) break;  // the rest are unused
+    const uint32_t id = k >> 13;
+    if (i > 0 && (s_k[i - 1] >> 13) == id) continue;                       // not a run start
+    if (i + 1 >= n2 || s_k[i + 1] == kNone || (s_k[i + 1] >> 13) != id) continue;  // single
+    const int rep = (int)(k & 8191u);
+    for (int h = lane; h < hp; h += 64) {
+      float sp = 0.0f, sd = 0.0f;
+      for (int m = i; m < n2 && s_k[m] != kNone && (s_k[m] >> 13) == id; ++m) {
+        const int s = (int)(s_k[m] & 8191u);
+        sp += bf16_bits_to_f32(P[(int64_t)s * hp + h]);
+        sd += bf16_bits_to_f32(D[(int64_t)s * hp + h]);
+      }
+      P[(int64_t)rep * hp + h] = (uint16_t)f32_to_bf16_bits(sp);
+      D[(int64_t)rep * hp + h] = (uint16_t)f32_to_bf16_bits(sd);
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+
+// One (part of 64 query rows, tile of 128 KV rows) per workgroup, 4 waves.
+// C[j][d] over the tile's 128 KV rows and all D_qk dims: wave w holds
+// j 0..127 x d 128w .. 128w+127 (4 x 4 blocks of v_mfma_f32_32x32x16_bf16)
+// plus, for D_qk = 576, j 32w .. 32w+31 x d 512..575 (2 blocks): 288 fp32
+// accumulators, the 256 of the main blocks in AGPRs (the compiler's MFMA),
+// the other 32 in VGPRs (the MFMA written inline), so that no accumulator
+// moves between the register files inside the loop.
+// Per step (one query row, 16 heads) the k = heads operands are staged in
+// LDS by asynchronous copies through buffer descriptors:
+//   q rows (16 heads x D_qk) and dout rows (16 x 512), each row padded to a
+//   stride of 16 dwords modulo 64 banks, so that the transposed reads
+//   (ds_read_b64_tr_b16: 8 rows x 64 bytes) meet each bank at most twice --
+//   B operands;
+//   dS and P of the slot that selects each of the 128 KV rows ([k half][j]
+//   16-byte runs, zeros where none) -- A operands, one ds_read_b128 each.
+// Three stages: the copies of step s + 2 are issued after the barrier of
+// step s and overlap its reads and MFMAs. Parts are spread so that the
+// tiles of one part run on one XCD (block b on XCD b % 8) and share its L2
+// for q and dout.
+template <int DQK, int HP>
+__global__ __launch_bounds__(256, 1) void bwd_dkv_tile_kernel(BwdArgs a) {
+  constexpr int HS = HP / 16;                            // steps per query row
+  constexpr int RQ = DQK == 576 ? 608 : 544, RG = 544;   // LDS row strides (elements)
+  constexpr int QROWB = DQK * 2, QPADB = RQ * 2, GPADB = RG * 2;
+  constexpr int QIN = 16 * QPADB / 1024;                 // copies of the q block (19 or 17)
+  constexpr int QREG = 19 * 1024, GREG = 17 * 1024, AOFF = QREG + GREG;
+  constexpr int STAGE = AOFF + 8192;
+  constexpr int NST = 3;
+  constexpr int R = kBwdTileRows, BJ = kBwdTileKV;
+  constexpr int NX = DQK == 576 ? 2 : 0;      // blocks of dims 512..575 per wave
+  constexpr int NA = 8 + (NX > 0 ? 1 : 0), NB = 8 + NX;  // operand registers (u32x4) per step
+  constexpr uint32_t OOB = 0x80000000u;       // past every descriptor: reads zeros
+  static_assert(16 * QPADB % 1024 == 0 && QIN <= 19 && 16 * GPADB == GREG, "stage layout");
+  static_assert((QPADB / 4) % 64 == 16 || (QPADB / 4) % 64 == 48, "q row stride");
+  static_assert((GPADB / 4) % 64 == 16, "dout row stride");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[NST * STAGE];
+  __shared__ __attribute__((aligned(16))) int16_t s_map[R * BJ];
+  __shared__ int32_t s_rows[R];
+  __shared__ int32_t s_flag[R];
+  __shared__ int32_t s_nrows;
+
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, r32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nj = (int)(a.ld_map / BJ);
+  const int64_t n = a.T_q - a.row0 < a.chunk_rows ? a.T_q - a.row0 : a.chunk_rows;
+  const int np = (int)((n + R - 1) / R);
+  const int item = (int)(blockIdx.x >> 3);
+  const int p = 8 * (item / nj) + (int)(blockIdx.x & 7);
+  const int J = item % nj;
+  if (p >= np) return;  // uniform
+  const int64_t rbeg = (int64_t)p * R;
+  const int nr = (int)(n - rbeg < R ? n - rbeg : R);
+
+  // the part's map rows over this tile; rows that select into it
+  for (int c = tid; c < R * 16; c += 256) {
+    const int r = c >> 4, ch = c & 15;
+    const u32x4 v = r < nr ? load16(a.map + (rbeg + r) * a.ld_map + (int64_t)J * BJ + 8 * ch)
+                           : u32x4{~0u, ~0u, ~0u, ~0u};
+    *reinterpret_cast<u32x4*>(s_map + r * BJ + 8 * ch) = v;
+  }
+  __syncthreads();
+  for (int r = wave; r < R; r += 4) {
+    const uint32_t v = reinterpret_cast<const uint32_t*>(s_map + r * BJ)[lane];
+    const uint64_t any = __ballot(v != 0xffffffffu);
+    if (lane == 0) s_flag[r] = any != 0;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const bool f = s_flag[lane] != 0;
+    const uint64_t m = __ballot(f);
+    if (f) s_rows[__popcll(m & ((1ull << lane) - 1ull))] = lane;
+    if (lane == 0) s_nrows = __popcll(m);
+  }
+  __syncthreads();
+  const int nrows = s_nrows;
+  if (tid == 0) a.part_flag[(int64_t)p * nj + J] = nrows > 0 ? 1 : 0;
+  if (nrows == 0) return;  // uniform
+
+  // this wave's nine q / dout copies of a stage: copy k = wave + 4i covers
+  // 1 KiB of the padded LDS block; rel = its lane's byte offset from the
+  // step's first head row in global memory (OOB for padding)
+  uint32_t rel[9];
+#pragma unroll
+  for (int i = 0; i < 9; ++i) {
+    const int k = wave + 4 * i;
+    if (k < 19) {
+      const int b = 1024 * k + 16 * lane, r = b / QPADB, cb = b - r * QPADB;
+      rel[i] = (k < QIN && cb < QROWB) ? (uint32_t)(r * QROWB + cb) : OOB;
+    } else {
+      const int b = 1024 * (k - 19) + 16 * lane, r = b / GPADB, cb = b - r * GPADB;
+      rel[i] = cb < 1024 ? (uint32_t)(r * 1024 + cb) : OOB;
+    }
+  }
+  const uint32_t lds0 = lds_addr(smem);
+  const int64_t slab = (int64_t)a.Kw * HP;  // P / dS elements per chunk row
+  const int S = nrows * HS;
+  // prep(s): a step's descriptors, LDS stage and this lane's dS / P offset,
+  // set up a step ahead of its copies. Steps past the last get descriptors of
+  // no bytes: their copies read nothing and write zeros into a free stage, so
+  // every step issues the same 11 copies per wave.
+  struct Copies {
+    i32x4 rq, rg, rD, rP;
+    uint32_t base, va;
+  };
+  auto prep = [&](int s) {
+    Copies c;
+    const bool live = s < S;
+    const int ri = live ? s / HS : 0, hg = s % HS;
+    const int rl = __builtin_amdgcn_readfirstlane(s_rows[ri]);
+    const int slot = s_map[rl * BJ + 32 * wave + r32];
+    const int64_t rc = rbeg + rl, t = a.row0 + rc;
+    const int h0 = 16 * hg, hl = live && a.H - h0 > 0 ? a.H - h0 : 0;  // heads left from h0
+    c.rq = buffer_rsrc_words(a.q + (t * a.H + h0) * DQK, (uint32_t)(hl * QROWB));
+    c.rg = buffer_rsrc_words(a.dout + (t * a.H + h0) * 512, (uint32_t)(hl * 1024));
+    c.rD = buffer_rsrc_words(a.wsD + rc * slab, live ? (uint32_t)(slab * 2) : 0u);
+    c.rP = buffer_rsrc_words(a.wsP + rc * slab, live ? (uint32_t)(slab * 2) : 0u);
+    c.base = lds0 + (uint32_t)((s % NST) * STAGE);
+    c.va = slot >= 0 ? (uint32_t)(slot * HP + h0 + 8 * half) * 2u : OOB;
+    return c;
+  };
+  // copy i of this wave: 0..8 the q / dout copies, 9 dS, 10 P
+  auto copy = [&](const Copies& c, auto ic) {
+    constexpr int i = decltype(ic)::value;
+    if constexpr (i < 9) {
+      const int k = wave + 4 * i;
+      const bool isq = k < 19;
+      const i32x4 r = isq ? c.rq : c.rg;
+      const uint32_t lo = isq ? 1024u * (uint32_t)k : (uint32_t)QREG + 1024u * (uint32_t)(k - 19);
+      dma16_buf_imm<0>(rel[i], r, c.base + lo);
+    } else if constexpr (i == 9) {
+      dma16_buf_imm<0>(c.va, c.rD, c.base + (uint32_t)AOFF + 1024u * (uint32_t)wave);
+    } else {
+      dma16_buf_imm<0>(c.va, c.rP, c.base + (uint32_t)AOFF + 4096u + 1024u * (uint32_t)wave);
+    }
+  };
+
+  const int G = lane >> 4, li = lane & 15;
+  const int rsel = 8 * (G >> 1) + (li >> 2);
+  const int csel = 16 * (G & 1) + 4 * (li & 3);
+  f32x16 acc[4][4];
+  f32x16 accx[NX > 0 ? NX : 1];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[m][b] = f32x16{};
+#pragma unroll
+  for (int e = 0; e < (NX > 0 ? NX : 1); ++e) accx[e] = f32x16{};
+
+  // operands of step s: A = dS (0..3), P (4..7), dS of m-block w (8);
+  // B = q blocks (0..3), dout blocks (4..7), q dims 512.. (8, 9)
+  auto load_ops = [&](int s, u32x4* A, u32x4* B) {
+    const unsigned char* st = smem + (s % NST) * STAGE;
+    const uint16_t* sq = reinterpret_cast<const uint16_t*>(st);
+    const uint16_t* sg = reinterpret_cast<const uint16_t*>(st + QREG);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      A[m] = *reinterpret_cast<const u32x4*>(st + AOFF + 1024 * m + 16 * lane);
+      A[4 + m] = *reinterpret_cast<const u32x4*>(st + AOFF + 4096 + 1024 * m + 16 * lane);
+    }
+    if constexpr (NX > 0)
+      A[8] = *reinterpret_cast<const u32x4*>(st + AOFF + 1024 * wave + 16 * lane);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int col = 32 * (4 * wave + b);
+      const uint16_t* qb = sq + rsel * RQ + col + csel;
+      const u32x2 q0 = lds_read_tr16(qb), q1 = lds_read_tr16(qb + 4 * RQ);
+      B[b] = u32x4{q0.x, q0.y, q1.x, q1.y};
+      const uint16_t* gb = sg + rsel * RG + col + csel;
+      const u32x2 g0 = lds_read_tr16(gb), g1 = lds_read_tr16(gb + 4 * RG);
+      B[4 + b] = u32x4{g0.x, g0.y, g1.x, g1.y};
+    }
+#pragma unroll
+    for (int e = 0; e < NX; ++e) {
+      const uint16_t* qb = sq + rsel * RQ + 512 + 32 * e + csel;
+      const u32x2 q0 = lds_read_tr16(qb), q1 = lds_read_tr16(qb + 4 * RQ);
+      B[8 + e] = u32x4{q0.x, q0.y, q1.x, q1.y};
+    }
+  };
+  // the step's MFMAs (dS q blocks, the extra q dims, P dout blocks) with the
+  // 11 copies of step s + 2 issued between them, one after every third
+  auto mfmas = [&](const u32x4* A, const u32x4* B, const Copies& c) {
+    constexpr int NM = 32 + NX;
+    static_for<NM>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j < 16) {
+        constexpr int b = j / 4, m = j % 4;
+        acc[m][b] = mfma32x32x16(A[m], B[b], acc[m][b]);
+      } else if constexpr (j < 16 + NX) {
+        constexpr int e = j - 16;
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(accx[e]) : "v"(A[8]), "v"(B[8 + e]));
+      } else {
+        constexpr int b = (j - 16 - NX) / 4, m = (j - 16 - NX) % 4;
+        acc[m][b] = mfma32x32x16(A[4 + m], B[4 + b], acc[m][b]);
+      }
+      if constexpr (j % 3 == 1 && j / 3 < 11) copy(c, std::integral_constant<int, j / 3>{});
+    });
+  };
+  // step s: once its copies are in LDS (own copies waited for, then the
+  // barrier, which also ends every wave's reads of step s - 1), read its
+  // operands and multiply, issuing the copies of step s + 2 into the stage of
+  // step s - 1 between the MFMAs
+  static_assert(32 + NX >= 3 * 10 + 2, "every copy finds its MFMA");
+  u32x4 A[NA], B[NB];
+  {
+    const Copies c0 = prep(0), c1 = prep(1);
+    static_for<11>([&](auto ic) { copy(c0, ic); });
+    static_for<11>([&](auto ic) { copy(c1, ic); });
+  }
+  Copies cn = prep(2);
+  for (int s = 0; s < S; ++s) {
+    wait_vmcnt_le<11>();  // this wave's copies of step s are in LDS
+    __syncthreads();
+    load_ops(s, A, B);
+    mfmas(A, B, cn);
+    cn = prep(s + 3);
+  }
+  wait_vmcnt0();  // the copies issued past the last step
+
+  if constexpr (NX > 0)  // wait states before VALU reads of the inline MFMA results
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(accx[0]), "+v"(accx[1]));
+  float* out = a.part + ((int64_t)p * a.ld_map + (int64_t)J * BJ) * DQK;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        out[(int64_t)(32 * m + crow(i, half)) * DQK + 32 * (4 * wave + b) + r32] = acc[m][b][i];
+  if constexpr (NX > 0) {
+#pragma unroll
+    for (int e = 0; e < NX; ++e)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        out[(int64_t)(32 * wave + crow(i, half)) * DQK + 512 + 32 * e + r32] = accx[e][i];
+  }
+}
+
+// dkv_ws[j] += the written partials of KV row j, in ascending part order.
+template <int DQK>
+__global__ __launch_bounds__(256) void bwd_tile_reduce_kernel(BwdArgs a) {
+  constexpr int C4 = DQK / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.T_kv * C4) return;
+  const int64_t j = i / C4;
+  const int c = (int)(i - j * C4);
+  const int64_t n = a.T_q - a.row0 < a.chunk_rows ? a.T_q - a.row0 : a.chunk_rows;
+  const int np = (int)((n + kBwdTileRows - 1) / kBwdTileRows);
+  const int nj = (int)(a.ld_map / kBwdTileKV);
+  const int J = (int)(j / kBwdTileKV);
+  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int p = 0; p < np; ++p) {
+    if (!a.part_flag[(int64_t)p * nj + J]) continue;
+    s += *reinterpret_cast<const f32x4*>(a.part + ((int64_t)p * a.ld_map + j) * DQK + 4 * c);
+  }
+  f32x4* d = reinterpret_cast<f32x4*>(a.dkv_ws + j * DQK + 4 * c);
+  *d = *d + s;
+}
+
 template <int DQK, int NW>
 hipError_t launch_bwd_nw(BwdArgs a, int64_t chunk, hipStream_t st) {
   constexpr int NWD = DQK == 576 ? 6 : 4;
@@ -874,6 +1263,21 @@ hipError_t launch_bwd_nw(BwdArgs a, int64_t chunk, hipStream_t st) {
     else
       hipLaunchKernelGGL((bwd_dq_ring_kernel<DQK, NW, false>), dim3((unsigned)n), dim3(NW * 128),
                          0, st, a);
+    if (a.tiles) {
+      // KV-tile dkv: merge repeated ids after the dq pass has read them
+      hipLaunchKernelGGL(bwd_fill_kernel, dim3(1), dim3(256), 0, st,
+                         reinterpret_cast<float*>(a.dup_count), (int64_t)1);
+      hipLaunchKernelGGL(bwd_map_kernel, dim3((unsigned)n), dim3(256), 0, st, a);
+      hipLaunchKernelGGL(bwd_merge_kernel, dim3((unsigned)n), dim3(256), 0, st, a);
+      const int64_t nj = a.ld_map / kBwdTileKV;
+      const int64_t np = (n + kBwdTileRows - 1) / kBwdTileRows;
+      hipLaunchKernelGGL((bwd_dkv_tile_kernel<DQK, HP>), dim3((unsigned)(8 * nj * ((np + 7) / 8))),
+                         dim3(256), 0, st, a);
+      const int64_t nr = a.T_kv * (DQK / 4);
+      hipLaunchKernelGGL((bwd_tile_reduce_kernel<DQK>), dim3((unsigned)((nr + 255) / 256)),
+                         dim3(256), 0, st, a);
+      continue;
+    }
     hipLaunchKernelGGL((bwd_dkv_kernel<DQK, NW, NWD>), dim3((unsigned)(n * (HP / HC))),
                        dim3(NWD * 64), 0, st, a);
     if (a.T_kv > 0) {

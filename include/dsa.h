@@ -74,7 +74,7 @@ typedef enum {
 const char* dsa_last_error(void);
 
 /* ABI version of this header (bumped on any signature change). */
-#define DSA_ABI_VERSION 8
+#define DSA_ABI_VERSION 9
 int dsa_abi_version(void);
 
 /* Limits enforced by the host checks. */
@@ -358,13 +358,28 @@ int dsa_sparse_attn_fwd(const void* q, int64_t T_q, int32_t H, int32_t D_qk,
  * dsa_sparse_attn_bwd_workspace_bytes - device workspace dsa_sparse_attn_bwd
  * uses for these sizes: fp32 statistics [T_q, H] x 2, an fp32 dkv
  * accumulator [T_kv, D_qk], per-KV-row counts and offsets [T_kv], and per
- * query row of a chunk its bf16 P and dS, the bf16 dkv rows of its slots,
- * its slot list and the slot sort's key / value buffers, for chunks of up
- * to 4 GiB (min(T_q, rows that fit) rows at a time). Returns -1 for sizes
- * out of contract.
+ * query row of a chunk its bf16 P and dS plus the buffers of its dkv scheme,
+ * for chunks of up to 4 GiB (min(T_q, rows that fit) rows at a time):
+ *  - KV tiles, when every row may select at least one key in eight
+ *    (8 * k_width >= T_kv, T_kv <= 32768, k_width rounded up to 32 <= 8192):
+ *    an int16 slot map per row over T_kv rounded up to 128, and per part of
+ *    64 query rows an fp32 partial [T_kv rounded up to 128, D_qk] and its
+ *    tile flags;
+ *  - per-slot rows otherwise: the bf16 dkv rows of its slots, its slot list
+ *    and the slot sort's key / value buffers.
+ * Returns -1 for sizes out of contract.
  */
 int64_t dsa_sparse_attn_bwd_workspace_bytes(int64_t T_q, int32_t H, int64_t T_kv, int32_t D_qk,
                                             int32_t k_width);
+
+/*
+ * dsa_sparse_attn_bwd_kv_tiles - which dkv scheme dsa_sparse_attn_bwd takes
+ * for T_kv KV rows and k_width slots per row: 1 for KV tiles (8 * k_width >=
+ * T_kv, 0 < T_kv <= 32768, 0 < k_width rounded up to 32 <= 8192), 0 for
+ * per-slot rows (the rule of dsa_sparse_attn_bwd_workspace_bytes). Needs no
+ * device; -1 for T_kv or k_width below 0.
+ */
+int dsa_sparse_attn_bwd_kv_tiles(int64_t T_kv, int32_t k_width);
 
 /*
  * dsa_sparse_attn_bwd - gradients of dsa_sparse_attn_fwd for shared latent
@@ -398,11 +413,18 @@ int64_t dsa_sparse_attn_bwd_workspace_bytes(int64_t T_q, int32_t H, int64_t T_kv
  *               up to 4 GiB of chunk buffers, and a larger workspace
  *               processes more query rows per pass
  * bf16 MFMA products with fp32 accumulation; P and dS are rounded to bf16
- * before the dq and dkv products, and each slot's dkv row (summed over the
- * heads) to bf16 before the per-KV-row sum, which is fp32 and runs over
- * the slots in ascending (row, slot) order within each chunk of query rows
- * (a stable sort, no atomics on the order): equal inputs and workspace
- * sizes give identical bits. d_sink is summed in a fixed order.
+ * before the dq and dkv products. dkv by one of two schemes (the rule of
+ * dsa_sparse_attn_bwd_workspace_bytes):
+ *  - KV tiles: per tile of 128 KV rows and part of 64 query rows, dS^T q +
+ *    P^T dout over the part's rows and heads as one fp32 product (zeros
+ *    where a row selects no slot for a KV row; a row's repeated ids first
+ *    merged into its lowest slot, summed in ascending slot order and rounded
+ *    to bf16), the parts then added in ascending order;
+ *  - per-slot rows: each slot's dkv row (summed over the heads) rounded to
+ *    bf16, then summed per KV row in fp32 in ascending (row, slot) order
+ *    (a stable sort).
+ * No atomics decide an order: equal inputs and workspace sizes give
+ * identical bits. d_sink is summed in a fixed order.
  * Errors: the checks of dsa_sparse_attn_fwd, DSA_ERR_VALUE for D_v != 512,
  * a separate V, or a workspace too small for one row.
  */

@@ -207,9 +207,8 @@ def test_header_declares_the_path():
     for fn in ["dsa_packed_metadata", "dsa_ratio_causal_metadata", "dsa_indexer_fwd",
                "dsa_indexer_fwd_fp8", "dsa_indexer_topk_fused", "dsa_topk", "dsa_sparse_attn_fwd",
                "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_workspace_bytes",
-               "dsa_topk_workspace_bytes", "dsa_indexer_topk_cand_buffer_size",
-               "dsa_last_error",
-               "dsa_abi_version"]:
+               "dsa_sparse_attn_bwd_kv_tiles", "dsa_topk_workspace_bytes",
+               "dsa_indexer_topk_cand_buffer_size", "dsa_last_error", "dsa_abi_version"]:
         assert fn in names
 
 
@@ -261,16 +260,47 @@ def test_python_binding_type_and_shape_errors():
 
 def test_backward_workspace_size_rule():
     lib = dsa.load_library()
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    # Per-slot dkv (fewer than one key in eight selected: 8 * 64 < 1024):
     # statistics, dkv accumulator, per-KV-row counts and offsets and the radix
     # sort's 256 digit totals, then P, dS, the per-slot dkv rows, the slot
     # list and the sort's two key / value buffers of every row, and the sort's
     # 256 digit counts per 4096 slots, when they fit in 4 GiB
-    n = lib.dsa_sparse_attn_bwd_workspace_bytes(256, 16, 256, 576, 64)
-    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    fixed = 2 * up(256 * 16 * 4) + up(256 * 576 * 4) + up(256 * 4) + up(257 * 4) + up(1024)
+    n = lib.dsa_sparse_attn_bwd_workspace_bytes(256, 16, 1024, 576, 64)
+    fixed = 2 * up(256 * 16 * 4) + up(1024 * 576 * 4) + up(1024 * 4) + up(1025 * 4) + up(1024)
     rows = (2 * up(256 * 64 * 32 * 2) + up(256 * 64 * 576 * 2) + 5 * up(256 * 64 * 4)
             + up(4 * 1024))
     assert n == fixed + rows
+    # KV-tile dkv (8 * 64 >= 256): P and dS, the int16 slot map of every row
+    # over the KV rows rounded up to 128, an fp32 partial per part of 64 rows
+    # and its tile flags, the repeated-id queue and its count
+    n = lib.dsa_sparse_attn_bwd_workspace_bytes(256, 16, 256, 576, 64)
+    fixed = 2 * up(256 * 16 * 4) + up(256 * 576 * 4) + up(256 * 4) + up(257 * 4) + up(1024)
+    rows = (2 * up(256 * 64 * 32 * 2) + up(256 * 256 * 2) + up(4 * 256 * 576 * 4)
+            + up(4 * 2 * 4) + up(4) + up(256 * 4))
+    assert n == fixed + rows
+    # the rule's edges: 8 * k_width >= T_kv, at most 32768 KV rows and 8192 slots
+    def layout(tq, tkv, kw, d=512, h=16):
+        fx = 2 * up(tq * h * 4) + up(tkv * d * 4) + up(tkv * 4) + up((tkv + 1) * 4) + up(1024)
+        kwp, hp, ld = (kw + 31) // 32 * 32, (h + 31) // 32 * 32, (tkv + 127) // 128 * 128
+        npart = (tq + 63) // 64
+        tile = (2 * up(tq * kwp * hp * 2) + up(tq * ld * 2) + up(npart * ld * d * 4)
+                + up(npart * (ld // 128) * 4) + up(4) + up(tq * 4))
+        slot = (2 * up(tq * kwp * hp * 2) + up(tq * kwp * d * 2) + 5 * up(tq * kwp * 4)
+                + up((tq * kwp + 4095) // 4096 * 1024))
+        return fx + tile, fx + slot
+    for tq, tkv, kw, want_tiles in [(8, 800, 100, True), (8, 801, 100, False),
+                                    (8, 32768, 4096, True), (8, 32769, 8192, False),
+                                    (8, 4096, 8192, True), (8, 4096, 8193, False)]:
+        tile, slot = layout(tq, tkv, kw)
+        got = lib.dsa_sparse_attn_bwd_workspace_bytes(tq, 16, tkv, 512, kw)
+        assert got == (tile if want_tiles else slot), (tq, tkv, kw)
+        assert lib.dsa_sparse_attn_bwd_kv_tiles(tkv, kw) == int(want_tiles)
+        assert dsa.dsa_sparse_attn_bwd_kv_tiles(tkv, kw) is want_tiles
+    assert lib.dsa_sparse_attn_bwd_kv_tiles(0, 8) == 0
+    assert lib.dsa_sparse_attn_bwd_kv_tiles(8, 0) == 0
+    assert lib.dsa_sparse_attn_bwd_kv_tiles(-1, 8) == -1
+    assert lib.dsa_sparse_attn_bwd_kv_tiles(8, -1) == -1
     assert lib.dsa_sparse_attn_bwd_workspace_bytes(10, 0, 10, 576, 8) == -1
     assert lib.dsa_sparse_attn_bwd_workspace_bytes(10, 8, 10, 256, 8) == -1
 

@@ -88,7 +88,14 @@ def _run(T, H, D, kw, seed, sink=True, stress=False, use_tl=True, active=None, r
         assert err <= 1e-3 * max(1.0, np.abs(rs).max())
 
 
-@pytest.mark.parametrize("T,H,D,kw,sink,stress,use_tl", [
+def _kv_tiles(T_kv, kw):
+    """The library's choice of dkv scheme for these sizes (KV tiles or one
+    dkv row per slot)."""
+    return dsa.dsa_sparse_attn_bwd_kv_tiles(T_kv, kw)
+
+
+SMALL = [
+    # KV tiles
     (64, 16, 576, 32, True, False, True),
     (150, 64, 576, 64, True, True, True),
     (97, 33, 512, 40, False, False, True),
@@ -96,18 +103,34 @@ def _run(T, H, D, kw, seed, sink=True, stress=False, use_tl=True, active=None, r
     (70, 64, 512, 33, True, True, True),
     (60, 80, 576, 48, True, False, True),
     (45, 96, 512, 40, True, True, True),
-])
+    (300, 64, 576, 40, True, False, True),   # several parts and tiles, a ragged last tile
+    # one dkv row per slot
+    (300, 64, 576, 32, True, True, True),
+    (200, 33, 512, 24, True, False, True),
+    (400, 128, 576, 40, True, True, False),
+    (270, 96, 512, 33, False, False, True),
+]
+
+
+def test_small_cases_cover_both_dkv_schemes():
+    kinds = {_kv_tiles(T, kw) for T, _, _, kw, *_ in SMALL}
+    assert kinds == {True, False}
+
+
+@pytest.mark.parametrize("T,H,D,kw,sink,stress,use_tl", SMALL)
 def test_backward_small(T, H, D, kw, sink, stress, use_tl):
-    say("attention backward", T, H, D, kw, sink, stress, use_tl)
+    say("attention backward", T, H, D, kw, sink, stress, use_tl,
+        "kv tiles" if _kv_tiles(T, kw) else "per-slot rows")
     _run(T, H, D, kw, seed=T + H, sink=sink, stress=stress, use_tl=use_tl)
 
 
 def test_backward_full_size_sampled_rows():
-    """T = 4096, 64 heads, K = 2048 (the single_T4096 shapes): only sampled
-    rows carry slots, so dkv is the sum of their contributions alone and the
-    oracle covers every output."""
+    """T = 4096, 64 heads, K = 2048 (the single_T4096 shapes, KV tiles): only
+    sampled rows carry slots, so dkv is the sum of their contributions alone
+    and the oracle covers every output. The rows sit on both sides of the
+    64-row part and 128-row tile edges."""
     T = 4096
-    rows = [0, 1, 2047, 2048, 3000, 4095]
+    rows = [0, 1, 63, 64, 127, 128, 1000, 2047, 2048, 2049, 3000, 3071, 3072, 4031, 4095]
     active = np.zeros(T, dtype=bool)
     active[rows] = True
     say("attention backward, full size, rows", rows)
@@ -173,14 +196,19 @@ def test_backward_kv_beyond_2gib():
     assert err <= 1e-3 * max(1.0, np.abs(rs).max())
 
 
-def test_backward_reproducible_and_chunked():
-    """dkv is summed per KV row in ascending slot order (a stable radix sort
-    of the slots, no atomics), so repeated calls give identical bits, also
-    with a workspace holding stale data; a workspace that holds only a few
-    rows at a time (several chunks) stays within the oracle's tolerance.
-    T_kv = 600 needs two 8-bit sort passes; most KV rows sit in hundreds of
-    lists and every fifth row repeats a slot."""
-    T, H, D, kw = 600, 64, 576, 256
+@pytest.mark.parametrize("kw", [256, 64])
+def test_backward_reproducible_and_chunked(kw):
+    """No atomics decide a sum of dkv: the per-slot rows are summed per KV
+    row in ascending slot order (a stable radix sort of the slots), the KV
+    tiles' partials in ascending part order with repeated ids merged in
+    ascending slot order. So repeated calls give identical bits, also with a
+    workspace holding stale data; a workspace that holds only a few rows at a
+    time (several chunks) stays within the oracle's tolerance. k_width 256
+    takes KV tiles, 64 the per-slot rows (T_kv = 600 needs two 8-bit sort
+    passes); most KV rows are selected by hundreds of rows and every fifth
+    row repeats a slot."""
+    T, H, D = 600, 64, 576
+    assert _kv_tiles(T, kw) == (kw == 256)
     wl = make_custom([T], H=H, D_qk=D, D_v=512, H_idx=0, seed=31, device=DEV, sink=True,
                      topk=kw)
     rng = np.random.default_rng(31)
@@ -203,7 +231,7 @@ def test_backward_reproducible_and_chunked():
         for a, b in zip(runs[0], r):
             assert torch.equal(a, b)
     say("  three calls: identical dq, dkv, d_sink")
-    # a workspace for about 37 rows: 17 chunks
+    # a workspace for about 37 rows: many chunks
     full = dsa.dsa_sparse_attn_bwd_workspace_bytes(37, H, T, D, kw)
     ws = torch.full((full,), 0x5A, dtype=torch.uint8, device=DEV)
     dq, dkv, ds = dsa.dsa_sparse_attn_bwd(wl.q, wl.kv, idx_t, out, dout, lse, topk_length=tl_t,
