@@ -311,6 +311,11 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
     if (comp) {
       const int slot = it * kBT + r32;
       const bool valid = (mask_cur >> r32) & 1u;
+      // lane (slot, half) holds heads 8g + 4*half + 0..3 of its slot for
+      // g = 0..3 (the C layout); one v_permlane32_swap per word and pair of
+      // groups (2pi, 2pi + 1) gives half 0 heads 16pi + 0..7 and half 1
+      // heads 16pi + 8..15, stored as 16-byte runs
+      uint32_t pw[4][2], dw[4][2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         float pv[4], dv[4];
@@ -321,9 +326,26 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
           pv[e] = p;
           dv[e] = a.scale * p * (dacc[i] - dd[i]);
         }
-        const int64_t off = (int64_t)slot * HP + h0 + 8 * g + 4 * half;  // 4 consecutive heads
-        *reinterpret_cast<u32x2*>(wsP + off) = u32x2{pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3])};
-        *reinterpret_cast<u32x2*>(wsD + off) = u32x2{pack_bf16x2(dv[0], dv[1]), pack_bf16x2(dv[2], dv[3])};
+        pw[g][0] = pack_bf16x2(pv[0], pv[1]);
+        pw[g][1] = pack_bf16x2(pv[2], pv[3]);
+        dw[g][0] = pack_bf16x2(dv[0], dv[1]);
+        dw[g][1] = pack_bf16x2(dv[2], dv[3]);
+      }
+#pragma unroll
+      for (int pi = 0; pi < 2; ++pi) {
+        u32x4 po, dq4;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const auto sp = __builtin_amdgcn_permlane32_swap(pw[2 * pi][w], pw[2 * pi + 1][w], false, false);
+          const auto sd = __builtin_amdgcn_permlane32_swap(dw[2 * pi][w], dw[2 * pi + 1][w], false, false);
+          po[w] = sp[0];
+          po[2 + w] = sp[1];
+          dq4[w] = sd[0];
+          dq4[2 + w] = sd[1];
+        }
+        const int64_t off = (int64_t)slot * HP + h0 + 16 * pi + 8 * half;  // 8 consecutive heads
+        *reinterpret_cast<u32x4*>(wsP + off) = po;
+        *reinterpret_cast<u32x4*>(wsD + off) = dq4;
       }
     }
     mask_cur = mask_next;
