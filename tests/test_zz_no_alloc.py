@@ -86,14 +86,17 @@ def _check_vs_oracle(wl, idx, tl, dout, dq, dkv, d_sink, rows):
         assert err <= 2e-2, (name, err)
 
 
-# first call: 700 rows of up to 512 slots at 64 heads, two chunks of query rows
-# on the 256 MiB scratch; second call: smaller, 16 heads, D_qk 512, no sink
-@pytest.mark.parametrize("calls", [[(700, 64, 576, 512, 41, True), (300, 16, 512, 64, 42, False)]])
+# first call: 1600 rows of up to 1024 slots at 32 heads, dkv by KV tiles, two
+# chunks of query rows on the 256 MiB scratch (300 MB of buffers); second call:
+# smaller, 16 heads, D_qk 512, no sink, dkv by per-slot rows
+@pytest.mark.parametrize("calls", [[(1600, 32, 576, 1024, 41, True, True),
+                                    (300, 16, 512, 32, 42, False, False)]])
 def test_noalloc_matches_workspace_entry(calls):
     lib = dsa.load_library()
     ws = torch.empty(dsa.DSA_NOALLOC_SCRATCH_BYTES, dtype=torch.uint8, device=DEV)
-    for (T, H, D, kw, seed, sink) in calls:
-        say("no-alloc backward", dict(T=T, H=H, D=D, kw=kw, sink=sink))
+    for (T, H, D, kw, seed, sink, tiles) in calls:
+        assert dsa.dsa_sparse_attn_bwd_kv_tiles(T, kw) == tiles
+        say("no-alloc backward", dict(T=T, H=H, D=D, kw=kw, sink=sink, kv_tiles=tiles))
         wl, idx, tl, idx_t, tl_t, out, lse, dout = _inputs(T, H, D, kw, seed, sink)
         a = _call(lib, "dsa_sparse_attn_bwd_noalloc", wl, idx_t, tl_t, out, lse, dout)
         b = _call(lib, "dsa_sparse_attn_bwd", wl, idx_t, tl_t, out, lse, dout, workspace=ws)
