@@ -1,7 +1,8 @@
 /*
  * dsa.h - C ABI of the MI355X (gfx950) DeepSeek Sparse Attention forward path.
  *
- * Five stream-ordered calls cover the forward hot path of DSA:
+ * Stream-ordered calls covering the forward hot path of DSA and the sparse
+ * attention backward:
  *   dsa_packed_metadata  per-token document start and causal length (THD)
  *   dsa_ratio_causal_metadata  the same for the ratio-causal mask with query
  *                        causal offsets (compressed keys, split queries)
@@ -17,8 +18,11 @@
  *                        (dsa_indexer_topk_cand_buffer_size: its size query)
  *   dsa_sparse_attn_fwd  sparse MQA/GQA attention over the selected KV rows
  *   dsa_sparse_attn_bwd  its gradients (dq, dkv, d_sink) for shared latent KV
- *                        (dsa_sparse_attn_bwd_noalloc: the same without a
- *                        caller workspace, for callers that cannot allocate)
+ *                        (dsa_sparse_attn_bwd_workspace_bytes: its workspace
+ *                        query; dsa_sparse_attn_bwd_kv_tiles: which dkv
+ *                        scheme a shape takes; dsa_sparse_attn_bwd_noalloc:
+ *                        the same without a caller workspace, for callers
+ *                        that cannot allocate)
  *
  * Conventions shared by every call
  * --------------------------------
