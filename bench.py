@@ -4,7 +4,7 @@
 One step = one pass of the whole path over one batch of synthetic input:
 metadata -> lightning-indexer scores -> radix top-K -> sparse attention
 forward. Indexer + top-K run (--path auto) as dsa_indexer_topk_fused with a
-candidate buffer for bf16 rows longer than 4096 columns (no dense scores),
+candidate buffer for rows longer than 4096 columns (no dense scores),
 otherwise as row chunks of scores under a 2 GiB cap followed by dsa_topk.
 Workloads 1-5 are packed documents
 (plain causal mask); 6 and 7 are split-query / compressed-key workloads
@@ -64,12 +64,15 @@ KERNELS = {
     "indexer_cand": ("indexer.hip", ("indexer_kernel<128, 2, unsigned short, 2>",)),
     "indexer_rescue": ("indexer.hip", ("indexer_rescue_kernel",)),
     "indexer": ("indexer.hip", ("indexer_kernel<",)),
+    "indexer_fp8_cand": ("indexer_fp8.hip", (("indexer_fp8_kernel<", "false, true>"),)),
+    "indexer_rescue_fp8": ("indexer_fp8.hip", ("indexer_rescue_fp8_kernel",)),
     "indexer_fp8": ("indexer_fp8.hip", ("indexer_fp8_kernel",)),
     "topk_cand": ("topk.hip", ("topk_radix_kernel<8, 4, true>",)),
     "topk": ("topk.hip", ("topk_radix_kernel", "topk_stream_kernel")),
 }
 # the kernels of one dsa_indexer_topk_fused call on rows longer than 4096 columns
 CAND_FAMILIES = ("indexer_cand", "topk_cand", "indexer_rescue")
+CAND_FAMILIES_FP8 = ("indexer_fp8_cand", "topk_cand", "indexer_rescue_fp8")
 
 
 def parse():
@@ -86,7 +89,7 @@ def parse():
     p.add_argument("--path", choices=("auto", "chunks", "fused"), default="auto",
                    help="indexer + top-K: score chunks + dsa_topk, or dsa_indexer_topk_fused "
                         "(no dense scores: on chip up to 4096 columns, a candidate buffer "
-                        "beyond); auto = fused for bf16 rows longer than 4096 columns, else "
+                        "beyond); auto = fused for rows longer than 4096 columns, else "
                         "chunks")
     p.add_argument("--flush-steps", type=int, default=5,
                    help="extra steps, each after writing 512 MiB so that the 256 MB MALL holds "
@@ -158,7 +161,9 @@ def kernel_source_sha(family: str) -> str:
 
 def family_of(kernel_name: str):
     for fam, (_, keys) in KERNELS.items():
-        if any(k in kernel_name for k in keys):
+        # a key is a substring, or a tuple of substrings that must all occur
+        if any(all(p in kernel_name for p in ((k,) if isinstance(k, str) else k))
+               for k in keys):
             return fam
     return None
 
@@ -556,12 +561,8 @@ def main():
 
     rs, sl = metadata()
     long_rows = max_len > dsa.DSA_FUSED_MAX_COLS
-    fused = has_indexer and (args.path == "fused" or (args.path == "auto" and long_rows and
-                                                      not fp8))
+    fused = has_indexer and (args.path == "fused" or (args.path == "auto" and long_rows))
     long_fused = fused and long_rows
-    if long_fused and fp8:
-        raise SystemExit(f"--path fused takes FP8 rows of at most {dsa.DSA_FUSED_MAX_COLS} "
-                         "columns")
     cand = None
     if long_fused:  # allocated once, outside the timed steps
         cand = torch.empty((dsa.dsa_indexer_topk_cand_buffer_size(T, max_len, K),),
@@ -603,7 +604,7 @@ def main():
                 run("indexer_topk_fused", lambda: dsa.dsa_indexer_topk_fused(
                     fp8["q8"], fp8["k8"], wl.w, rs, sl, K, max_len, q_scale=fp8["q_scale"],
                     k_scale=fp8["k_scale"], fp8_scaling=fp8_scaling, indices=indices,
-                    topk_length=topk_length))
+                    topk_length=topk_length, cand_buffer=cand))
             else:
                 run("indexer_topk_fused", lambda: dsa.dsa_indexer_topk_fused(
                     wl.q_idx, wl.k_idx, wl.w, rs, sl, K, max_len, indices=indices,
@@ -699,11 +700,14 @@ def main():
                     cand[:1].view(torch.int32).item())
             traffic = None
             if long_fused:
-                parts = [traffic_from_profile(wname, f) for f in CAND_FAMILIES]
+                parts = [traffic_from_profile(wname, f)
+                         for f in (CAND_FAMILIES_FP8 if fp8 else CAND_FAMILIES)]
                 traffic = None if any(v is None for v in parts) else float(sum(parts))
+            kname = "indexer_fp8_kernel" if fp8 else "indexer_kernel"
             rooflines["indexer_topk_fused"] = roofline_entry(
-                "indexer_kernel (candidate mode) + topk_radix_kernel (candidates) + "
-                "indexer_rescue_kernel" if long_fused else "indexer_kernel (combined with top-K)",
+                f"{kname} (candidate mode) + topk_radix_kernel (candidates) + "
+                f"{kname.replace('indexer_', 'indexer_rescue_', 1)}" if long_fused
+                else f"{kname} (combined with top-K)",
                 "mfma", cnt["indexer_flop"], n, ms, idx_peak, "TFLOP/s", traffic)
         else:
             ims, n_i = st["indexer"]

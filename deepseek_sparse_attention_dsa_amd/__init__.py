@@ -429,9 +429,9 @@ def dsa_indexer_topk_fused(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Te
 
     Returns (indices int32 [n_rows, k], topk_length int32 [n_rows], logits |
     None, softmax | None, lse | None). bf16 q_idx / k_idx, or FP8 ones with
-    q_scale, k_scale and fp8_scaling as dsa_indexer_fwd_fp8 takes them (FP8
-    only for n_cols <= DSA_FUSED_MAX_COLS). Rows longer than
-    DSA_FUSED_MAX_COLS go through the candidate path and need cand_buffer, a
+    q_scale, k_scale and fp8_scaling as dsa_indexer_fwd_fp8 takes them. Rows
+    longer than DSA_FUSED_MAX_COLS go through the candidate path and need
+    cand_buffer, a
     float32 device tensor of dsa_indexer_topk_cand_buffer_size(n_rows,
     n_cols, k) elements (allocated when None).
     """
@@ -608,11 +608,11 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
     k_scale and fp8_scaling as dsa_indexer_fwd_fp8 does.
     fused=True (or return_softmax=True) replaces the score chunks by one
     dsa_indexer_topk_fused call (no score buffer: rows of at most
-    DSA_FUSED_MAX_COLS columns stay on chip, longer bf16 rows go through a
+    DSA_FUSED_MAX_COLS columns stay on chip, longer rows go through a
     candidate buffer); only that path gives return_softmax, which returns
     (indices, topk_length, logits, softmax, lse). fused=None takes the
-    candidate buffer for bf16 rows longer than DSA_FUSED_MAX_COLS (the faster
-    path there on MI355X) and score chunks otherwise.
+    candidate buffer for rows longer than DSA_FUSED_MAX_COLS (the faster path
+    there on MI355X) and score chunks otherwise.
     """
     fp8 = q_idx.dtype in (torch.uint8, torch.float8_e4m3fn)
     if fp8 and (q_scale is None or k_scale is None or fp8_scaling is None):
@@ -630,13 +630,10 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,
         width = T if max_seqlen is None else int(max_seqlen)
         row_starts, seq_lens = dsa_packed_metadata(cu_seqlens, T, stream=stream)
     if fused is None:
-        fused = return_softmax or (width > DSA_FUSED_MAX_COLS and not fp8)
+        fused = return_softmax or width > DSA_FUSED_MAX_COLS
     if return_softmax and not fused:
         raise ValueError("return_softmax needs the fused path")
     if fused:
-        if width > DSA_FUSED_MAX_COLS and fp8:
-            raise ValueError(f"the fused path takes FP8 rows of at most {DSA_FUSED_MAX_COLS} "
-                             "columns")
         res = dsa_indexer_topk_fused(q_idx, k_idx, w, row_starts, seq_lens, k, max(width, 1),
                                      q_scale=q_scale, k_scale=k_scale, fp8_scaling=fp8_scaling,
                                      return_logits=return_softmax, return_softmax=return_softmax,

@@ -247,9 +247,6 @@ int dsa_indexer_topk_fused(const void* q_idx, const void* q_scale, const void* k
   REQUIRE(ld_indices >= k, DSA_ERR_VALUE, "%s: ld_indices (%lld) < k (%d)", fn,
           (long long)ld_indices, k);
   const bool long_rows = n_cols > DSA_FUSED_MAX_COLS;
-  REQUIRE(!long_rows || !fp8, DSA_ERR_VALUE,
-          "%s: rows longer than %d columns take bf16 inputs (DSA_INDEXER_BF16)", fn,
-          DSA_FUSED_MAX_COLS);
   if (n_rows == 0) return DSA_OK;
   if (long_rows) {
     const int64_t need = dsa_indexer_topk_cand_buffer_size(n_rows, n_cols, k);
@@ -285,15 +282,26 @@ int dsa_indexer_topk_fused(const void* q_idx, const void* q_scale, const void* k
                      L.spill_ld,
                      (int)L.n_spill};
     hipStream_t st = (hipStream_t)stream;
-    if (int rc = launched(fn, dsa::launch_indexer_cand(q_idx, k_idx, w, w_dtype, row_starts,
-                                                       seq_lens, T_kv, H_idx, D_idx, row_begin,
-                                                       n_rows, n_cols, k, ca, st)))
+    const bool mx = precision == DSA_INDEXER_MXFP8;
+    if (int rc = launched(fn, fp8 ? dsa::launch_indexer_cand_fp8(q_idx, q_scale, k_idx, k_scale,
+                                                                mx, w, w_dtype, row_starts,
+                                                                seq_lens, T_kv, H_idx, row_begin,
+                                                                n_rows, n_cols, k, ca, st)
+                                  : dsa::launch_indexer_cand(q_idx, k_idx, w, w_dtype, row_starts,
+                                                             seq_lens, T_kv, H_idx, D_idx,
+                                                             row_begin, n_rows, n_cols, k, ca,
+                                                             st)))
       return rc;
     const int64_t n_eff = T_kv > 0 ? n_cols : 0;
     if (int rc = launched(fn, dsa::launch_topk_cand(seq_lens + row_begin, row_starts + row_begin,
                                                     n_rows, n_eff, k, indices, ld_indices,
                                                     topk_length, logits, softmax, lse, ca, st)))
       return rc;
+    if (fp8)
+      return launched(fn, dsa::launch_indexer_rescue_fp8(q_idx, q_scale, k_idx, k_scale, mx, w,
+                                                         w_dtype, row_starts, seq_lens, T_kv,
+                                                         H_idx, row_begin, n_rows, n_cols, fa,
+                                                         ca, st));
     return launched(fn, dsa::launch_indexer_rescue(q_idx, k_idx, w, w_dtype, row_starts, seq_lens,
                                                    T_kv, H_idx, D_idx, row_begin, n_rows, n_cols,
                                                    fa, ca, st));

@@ -72,6 +72,18 @@ hipError_t launch_indexer_rescue(const void* q, const void* k, const void* w, in
                                  const int32_t* rs, const int32_t* sl, int64_t T_kv, int H, int D,
                                  int64_t row_begin, int64_t n_rows, int64_t n_cols,
                                  const FusedArgs& fa, const CandArgs& ca, hipStream_t st);
+// The same two passes for FP8 (E4M3) inputs (mx: E8M0 block scales, else
+// fp32 per-token descales); stage 2 is launch_topk_cand.
+hipError_t launch_indexer_cand_fp8(const void* q, const void* qs, const void* k, const void* ks,
+                                   bool mx, const void* w, int w_dtype, const int32_t* rs,
+                                   const int32_t* sl, int64_t T_kv, int H, int64_t row_begin,
+                                   int64_t n_rows, int64_t n_cols, int top_k, const CandArgs& ca,
+                                   hipStream_t st);
+hipError_t launch_indexer_rescue_fp8(const void* q, const void* qs, const void* k, const void* ks,
+                                     bool mx, const void* w, int w_dtype, const int32_t* rs,
+                                     const int32_t* sl, int64_t T_kv, int H, int64_t row_begin,
+                                     int64_t n_rows, int64_t n_cols, const FusedArgs& fa,
+                                     const CandArgs& ca, hipStream_t st);
 
 hipError_t launch_topk(const float* scores, int64_t ld, int64_t n_rows, int64_t n_cols,
                        const int32_t* seq_lens, const int32_t* row_starts, int k, int32_t* indices,

@@ -19,6 +19,7 @@
 //   their rows.
 #include "dsa_device.h"
 #include "dsa_launch.h"
+#include "dsa_rescue.h"
 #include "dsa_select.h"
 
 namespace dsa {
@@ -29,6 +30,7 @@ constexpr int kF8Pairs = 2;    // 64-key pairs of 32-key blocks per LDS tile (sc
 constexpr int kF8D = 128;       // head dim (bytes per FP8 row)
 constexpr int kF8KS = kF8D / 64;  // MFMA k-steps over the head dim
 constexpr int kF8RowB = kF8D + 16;  // LDS row stride in bytes (16 B pad: conflict-free b128 reads)
+constexpr int kF8SampleTiles = 8;   // CAND: key tiles sampled for the lower bound
 
 __device__ __forceinline__ float relu_f8(float x) {
   return __builtin_amdgcn_fmed3f(x, 0.0f, 3.40282347e38f);
@@ -50,13 +52,16 @@ __device__ __forceinline__ float load_wf<float>(const float* w, int64_t i) {
 // (per-token) or E8M0 bytes [T, H, 4] / [T_kv, 4] (MX). P: 64-key pairs per
 // LDS tile. FUSE: the scores of each row stay in LDS (ld is then the column
 // cap, at most kFuseMaxCols) and the wave selects its row's top-k into `fa`
-// instead of writing scores.
-template <int MB, typename WT, bool MX, int P, bool FUSE>
+// instead of writing scores. CAND: the row's candidates are appended to
+// `ca` (the combined path's stage 1 for long rows, as the bf16 kernel's
+// candidate mode: sampled lower bound, appends in column order; ld is then
+// the column cap).
+template <int MB, typename WT, bool MX, int P, bool FUSE, bool CAND>
 __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ qs, const uint8_t* __restrict__ k,
     const void* __restrict__ ks, const WT* __restrict__ w, const int32_t* __restrict__ row_starts,
     const int32_t* __restrict__ seq_lens, int64_t T_kv, int H, int64_t row_begin, int64_t n_rows,
-    float* __restrict__ scores, int64_t ld, FusedArgs fa) {
+    float* __restrict__ scores, int64_t ld, FusedArgs fa, CandArgs ca) {
   constexpr int kF8Tile = 64 * P;  // keys per LDS tile
   constexpr int TILE_B = kF8Tile * kF8RowB;
   constexpr int CHUNKS = kF8Tile * kF8D / 16;   // 16-byte chunks per tile
@@ -68,6 +73,11 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   __shared__ int32_t s_range[2];
   __shared__ __attribute__((aligned(16))) float s_rows[FUSE ? kF8Waves * kFuseRowStride : 4];
   static_assert(!FUSE || 2 * TILE_B >= kF8Waves * 256 * 4, "select histograms fit the tile ring");
+  static_assert(!(FUSE && CAND), "one output mode");
+  // CAND: the sampled keys of each wave's row, lane-major (slot 64 i + lane),
+  // and the rows' valid lengths
+  __shared__ uint32_t s_samp[CAND ? kF8Waves * 2 * kF8SampleTiles * 64 : 1];
+  __shared__ int32_t s_qlen[kF8Waves];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -116,13 +126,21 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   // both are in flight together).
   if (threadIdx.x < 64)
     wave_key_range(row_starts, seq_lens, row_begin, r0, n_rows, kF8Waves, cap, s_range);
+  if (lane == 0) s_qlen[wave] = qlen;
   __syncthreads();
   const int32_t kb = s_range[0];
   const int32_t ke = s_range[1];
+  int32_t nmax = 0;
+#pragma unroll
+  for (int i = 0; i < kF8Waves; ++i) nmax = max(nmax, s_qlen[i]);
+  if constexpr (CAND)
+    if (blockIdx.x == 0 && threadIdx.x == 0) *ca.n_queued = 0u;  // the stage-2 queue starts empty
   if (kb >= ke) {  // uniform: no row of the workgroup has a key
     if constexpr (FUSE)
       if (live)
         wave_topk_row(s_rows, 0, 0, nullptr, fa, r);  // writes the empty row
+    if constexpr (CAND)
+      if (live && lane == 0) ca.count[r] = 0;
     return;
   }
 
@@ -227,17 +245,48 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   // hardware range check, so the tile loop has no branches.
   // (FUSE: the row lives in LDS; columns outside the row go to a spare slot.)
   const __amdgpu_buffer_rsrc_t srow =
-      raw_buffer(FUSE ? (const void*)scores : (const void*)(scores + r * ld),
-                 FUSE ? 0u : (uint32_t)qlen * 4u);
+      raw_buffer((FUSE || CAND) ? (const void*)scores : (const void*)(scores + r * ld),
+                 (FUSE || CAND) ? 0u : (uint32_t)qlen * 4u);
   float* const lrow = s_rows + (FUSE ? wave * kFuseRowStride : 0);
+  // CAND: the row's lower bound and its candidates so far (wave-uniform),
+  // appended in column order as (score bits, local column) through a buffer
+  // descriptor of the row's cap entries: the hardware drops stores past the
+  // cap (the count still grows) and those of lanes that take nothing (an
+  // offset past the range). A score passes when its order-preserving signed
+  // form ord() is at least t_lo: the lower bound's form, INT32_MIN for every
+  // column, -1 for a bound of 0.0 (so that -0.0, form -1, passes).
+  int32_t t_lo = INT32_MIN;
+  uint32_t n_cand = 0u;
+  const __amdgpu_buffer_rsrc_t crow =
+      raw_buffer(CAND ? (const void*)(ca.cand + 2 * r * ca.cap) : (const void*)scores,
+                 CAND ? (uint32_t)(ca.cap * 8) : 0u);
+  auto ord = [](uint32_t b) -> int32_t {
+    return (int32_t)(b ^ ((uint32_t)((int32_t)b >> 31) >> 1));
+  };
+  auto append = [&](uint32_t bits, uint32_t j) {
+    const bool take = j < (uint32_t)qlen && ord(bits) >= t_lo;
+    const uint64_t tm = ballot(take);
+    const uint32_t off = take ? (n_cand + popc_below(tm)) * 8u : 0x80000000u;
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{bits, j}, crow, (int)off, 0, 0);
+    n_cand += (uint32_t)__popcll(tm);
+  };
   auto write_scores = [&](int32_t k0, float p0, float p1, float kscl) {
     float score = halfwave_sums(p0, p1);
     if constexpr (!MX) score *= kscl;
     const uint32_t j = (uint32_t)(k0 + lane - qstart);
     if constexpr (FUSE)
       lrow[j < (uint32_t)qlen ? j : (uint32_t)kFuseMaxCols] = score;
+    else if constexpr (CAND)
+      append(__float_as_uint(score), j);
     else
       buffer_store_f32(score, srow, j * 4u);  // negative: dropped
+  };
+  // CAND: whether the workgroup samples (a row longer than the capacity),
+  // and the first key of sample tile i (tiles of the workgroup's range).
+  const bool sample = CAND && nmax > (int32_t)ca.cap;  // uniform
+  const int32_t n_tiles = (ke - kb + kF8Tile - 1) / kF8Tile;
+  auto sample_start = [&](int i) -> int32_t {
+    return kb + kF8Tile * (int32_t)(((int64_t)i * n_tiles) / kF8SampleTiles);
   };
 
   // Every wave runs every tile of the workgroup's key range (a row's keys
@@ -246,12 +295,89 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   load_tile(kb);
   store_tile(0);
   __syncthreads();
+  // CAND: the sample tiles are scored once; the tile loop skips them and
+  // appends their saved keys in their place. Sample tile 0 is the range's
+  // first tile, the others are at least 8 tiles apart (a sampling workgroup
+  // has more than 64 tiles).
+  uint32_t* const wsamp = s_samp + (CAND ? wave * 2 * kF8SampleTiles * 64 + lane : 0);
+  auto append_saved = [&](int i) {
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp)
+      append(wsamp[64 * (2 * i + hp)], (uint32_t)(sample_start(i) + 64 * hp + lane - qstart));
+  };
+  if constexpr (CAND) {
+    if (sample) {  // uniform
+      // The sample tiles go through the ring in turn (the last prefetch is
+      // the tile loop's first tile, the one after sample tile 0, which lands
+      // in buffer 0); lane l keeps the scores of keys s + l and s + 64 + l of
+      // each sample tile s in the wave's LDS slots.
+      static_assert(P == 2 && kF8SampleTiles % 2 == 0, "sample layout");
+#pragma unroll 1
+      for (int i = 0; i < kF8SampleTiles; ++i) {
+        load_tile(i + 1 < kF8SampleTiles ? sample_start(i + 1) : kb + kF8Tile);
+        const int sb = i & 1;
+        const int32_t s0 = sample_start(i);
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          BOp b0, b1;
+          read_block(sb, 2 * pr, b0);
+          read_block(sb, 2 * pr + 1, b1);
+          block_mfma(b0, acc0);
+          block_mfma(b1, acc1);
+          float score = halfwave_sums(epilogue(acc0), epilogue(acc1));
+          if constexpr (!MX) score *= __uint_as_float(kscale[sb][64 * pr + lane]);
+          const uint32_t j = (uint32_t)(s0 + 64 * pr + lane - qstart);
+          // (invalid: all-ones bits, whose key is 0)
+          wsamp[64 * (2 * i + pr)] = j < (uint32_t)qlen ? __float_as_uint(score) : 0xffffffffu;
+        }
+        store_tile((i + 1) & 1);
+        __syncthreads();
+      }
+      // The tile loop's first pending epilogue reads acc1 (its write is
+      // dropped); zeroed, the accumulators hold nothing across the search.
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc0[mb][i] = acc1[mb][i] = 0.0f;
+      if (qlen > (int32_t)ca.cap) {  // uniform per wave
+        uint32_t samp[2 * kF8SampleTiles];
+#pragma unroll
+        for (int i = 0; i < 2 * kF8SampleTiles; ++i)
+          samp[i] = fused_key(__uint_as_float(wsamp[64 * i]));
+        uint32_t nv = 0u;
+#pragma unroll
+        for (int i = 0; i < 2 * kF8SampleTiles; ++i) nv += samp[i] != 0u ? 1u : 0u;
+        nv = wave_sum_u32(nv);
+        const float e = (float)fa.k * (float)nv / (float)qlen;
+        const uint32_t rank = (uint32_t)ceilf(e + 6.0f * sqrtf(e) + 4.0f);
+        if (nv >= rank) {
+          // lo = the largest key v with at least `rank` samples >= v
+          uint32_t v = 0u;
+#pragma unroll 1
+          for (int b = 31; b >= 0; --b) {
+            const uint32_t c = v | (1u << b);
+            uint32_t n_ge = 0u;
+#pragma unroll
+            for (int i = 0; i < 2 * kF8SampleTiles; ++i) n_ge += samp[i] >= c ? 1u : 0u;
+            if (wave_sum_u32(n_ge) >= rank) v = c;
+          }
+          t_lo = v == fused_key(0.0f) ? -1 : ord(__float_as_uint(fused_value(v)));
+        }
+      }
+      append_saved(0);
+    }
+  }
   int buf = 0;
   int32_t pend_k0 = qstart - 64;
   float pend_p0 = 0.0f;
   float pend_ks = 0.0f;  // descale of key pend_k0 + lane
-  for (int32_t k0 = kb; k0 < ke; k0 += kF8Tile) {
-    load_tile(k0 + kF8Tile);  // zeroed past the range, so the last one is harmless
+  int ns = 1;            // CAND: the next sample tile the loop has not passed
+  int32_t ns_start = sample ? sample_start(1) : INT32_MAX;
+  for (int32_t k0 = sample ? kb + kF8Tile : kb; k0 < ke;) {
+    int32_t k_next = k0 + kF8Tile;
+    if constexpr (CAND)
+      if (k_next == ns_start) k_next += kF8Tile;  // uniform
+    load_tile(k_next);  // zeroed past the range, so the last one is harmless
 
     BOp cur, nxt;
     read_block(buf, 0, cur);
@@ -277,11 +403,23 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
       pend_ks = kscl;
     }
 
+    if constexpr (CAND) {
+      if (k0 + kF8Tile == ns_start) {  // uniform: a sample tile comes next
+        write_scores(pend_k0, pend_p0, epilogue(acc1), pend_ks);
+        append_saved(ns);
+        pend_k0 = qstart - 64;  // the next tile's first pending write is dropped
+        ++ns;
+        ns_start = ns < kF8SampleTiles ? sample_start(ns) : INT32_MAX;
+      }
+    }
     store_tile(buf ^ 1);
     __syncthreads();
     buf ^= 1;
+    k0 = k_next;
   }
   write_scores(pend_k0, pend_p0, epilogue(acc1), pend_ks);
+  if constexpr (CAND)
+    if (live && lane == 0) ca.count[r] = (int32_t)n_cand;
   if constexpr (FUSE) {
     __syncthreads();  // the tile ring is free: it holds the select histograms now
     if (live)
@@ -290,22 +428,132 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   }
 }
 
-template <int MB, bool MX, bool FUSE>
+// Rescue pass of the combined path for long FP8 rows (the rows stage 2
+// queued): workgroup g takes queued rows g, g + G, ...; for each it scores
+// the row into its own spill row with the arithmetic of the indexer pass
+// (per 32-key block the MFMA chain over the two 64-byte k-steps from zero,
+// the ReLU * weight chain over the heads in the same order, the same
+// half-wave sum, then the key's descale), so every score is bit-identical to
+// the pass's, and selects exactly from them (select_spill_row).
+template <int MB, typename WT, bool MX>
+__global__ __launch_bounds__(kF8Waves * 64) void indexer_rescue_fp8_kernel(
+    const uint8_t* __restrict__ q, const void* __restrict__ qs, const uint8_t* __restrict__ k,
+    const void* __restrict__ ks, const WT* __restrict__ w, const int32_t* __restrict__ row_starts,
+    const int32_t* __restrict__ seq_lens, int64_t T_kv, int H, int64_t row_begin, int64_t n_cols,
+    FusedArgs fa, CandArgs ca) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t s_wave[kF8Waves];
+  __shared__ uint32_t s_sel[2];
+  __shared__ float s_fsum[kF8Waves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+  const uint32_t n_queued = *ca.n_queued;
+  float* const spill = ca.spill + (int64_t)blockIdx.x * ca.spill_ld;
+  const int64_t col_cap = T_kv > 0 ? n_cols : 0;
+
+  for (uint32_t qi = blockIdx.x; qi < n_queued; qi += gridDim.x) {
+    const int64_t r = ca.queue[qi];
+    const int64_t t = row_begin + r;
+    const int32_t s0 = row_starts[t];
+    const int n = (int)max((int64_t)0, min((int64_t)seq_lens[t], col_cap));
+
+    // Query fragments, block scales and weights as the indexer pass loads them.
+    i32x8 qa[MB][kF8KS];
+    int qsc[MB][kF8KS];
+    float wv[MB][16];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int head = mb * 32 + (lane & 31);
+      const bool hv = head < H;
+      const uint8_t* qrow = q + (t * H + head) * kF8D;
+#pragma unroll
+      for (int s = 0; s < kF8KS; ++s) {
+        const u32x4 lo = hv ? load16(qrow + 64 * s + 16 * half) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 hi = hv ? load16(qrow + 64 * s + 32 + 16 * half) : u32x4{0u, 0u, 0u, 0u};
+        qa[mb][s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                          (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        if constexpr (MX)
+          qsc[mb][s] = hv ? (int)((const uint8_t*)qs)[(t * H + head) * 4 + 2 * s + half] : 127;
+        else
+          qsc[mb][s] = 0;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int oh = mb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        float wf = oh < H ? load_wf<WT>(w, t * H + oh) : 0.0f;
+        if constexpr (!MX) wf *= oh < H ? ((const float*)qs)[t * H + oh] : 0.0f;
+        wv[mb][i] = wf;
+      }
+    }
+    // Scores of keys s0 + 64 g + [0, 64) by wave g % 8: block 0 holds keys
+    // [0, 32), block 1 keys [32, 64) of the group. Keys outside [0, T_kv)
+    // read zero rows and a zero scale word, as the indexer pass stages them.
+    for (int g = wave; 64 * g < n; g += kF8Waves) {
+      float p[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int col = 64 * g + 32 * nb + (lane & 31);
+        const int64_t key = (int64_t)s0 + col;
+        const bool ok = col < n && key >= 0 && key < T_kv;
+        const uint8_t* krow = k + (ok ? key : 0) * kF8D;
+        i32x8 kf[kF8KS];
+#pragma unroll
+        for (int s = 0; s < kF8KS; ++s) {
+          u32x4 lo = load16(krow + 64 * s + 16 * half);
+          u32x4 hi = load16(krow + 64 * s + 32 + 16 * half);
+          if (!ok) lo = hi = u32x4{0u, 0u, 0u, 0u};
+          kf[s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        }
+        const uint32_t sw = (MX && ok) ? ((const uint32_t*)ks)[key] : 0u;
+        f32x16 acc[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+          for (int s = 0; s < kF8KS; ++s) {
+            if constexpr (MX)
+              acc[mb] = mfma32x32x64_mxfp8(qa[mb][s], qsc[mb][s], kf[s], (int)(sw >> (8 * (2 * s + half))),
+                                           s == 0 ? f32x16{} : acc[mb]);
+            else
+              acc[mb] = mfma32x32x64_fp8(qa[mb][s], kf[s], s == 0 ? f32x16{} : acc[mb]);
+          }
+        }
+        float sum = 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum = fmaf(wv[mb][i], relu_f8(acc[mb][i]), sum);
+        p[nb] = sum;
+      }
+      float score = halfwave_sums(p[0], p[1]);
+      const int colw = 64 * g + lane;  // the key this lane's score belongs to
+      if constexpr (!MX) {
+        const int64_t key = (int64_t)s0 + colw;
+        const bool ok = colw < n && key >= 0 && key < T_kv;
+        score *= ok ? ((const float*)ks)[key] : 0.0f;
+      }
+      if (colw < n) spill[colw] = score;
+    }
+    __syncthreads();  // the spill row is complete
+    select_spill_row<kF8Waves>(spill, n, s0, fa, r, hist, s_wave, s_sel, s_fsum);
+  }
+}
+
+template <int MB, bool MX, bool FUSE, bool CAND>
 hipError_t launch_fp8_w(const void* q, const void* qs, const void* k, const void* ks,
                         const void* w, int w_dtype, const int32_t* rs, const int32_t* sl,
                         int64_t T_kv, int H, int64_t row_begin, int64_t n_rows, float* scores,
-                        int64_t ld, const FusedArgs& fa, hipStream_t st) {
+                        int64_t ld, const FusedArgs& fa, const CandArgs& ca, hipStream_t st) {
   constexpr int P = FUSE ? 1 : kF8Pairs;
   const int64_t nblk = (n_rows + kF8Waves - 1) / kF8Waves;
   dim3 grid((unsigned)nblk), block(kF8Waves * 64);
   if (w_dtype == 0)
-    hipLaunchKernelGGL((indexer_fp8_kernel<MB, uint16_t, MX, P, FUSE>), grid, block, 0, st,
+    hipLaunchKernelGGL((indexer_fp8_kernel<MB, uint16_t, MX, P, FUSE, CAND>), grid, block, 0, st,
                        (const uint8_t*)q, qs, (const uint8_t*)k, ks, (const uint16_t*)w, rs, sl,
-                       T_kv, H, row_begin, n_rows, scores, ld, fa);
+                       T_kv, H, row_begin, n_rows, scores, ld, fa, ca);
   else
-    hipLaunchKernelGGL((indexer_fp8_kernel<MB, float, MX, P, FUSE>), grid, block, 0, st,
+    hipLaunchKernelGGL((indexer_fp8_kernel<MB, float, MX, P, FUSE, CAND>), grid, block, 0, st,
                        (const uint8_t*)q, qs, (const uint8_t*)k, ks, (const float*)w, rs, sl, T_kv,
-                       H, row_begin, n_rows, scores, ld, fa);
+                       H, row_begin, n_rows, scores, ld, fa, ca);
   return hipGetLastError();
 }
 
@@ -320,8 +568,8 @@ hipError_t launch_indexer_fp8(const void* q, const void* qs, const void* k, cons
   const FusedArgs none{};
 #define DSA_F8_CASE(MM, XX)                                                                    \
   if (mb == MM && mx == XX)                                                                    \
-    return launch_fp8_w<MM, XX, false>(q, qs, k, ks, w, w_dtype, rs, sl, T_kv, H, row_begin, \
-                                       n_rows, scores, ld, none, st);
+    return launch_fp8_w<MM, XX, false, false>(q, qs, k, ks, w, w_dtype, rs, sl, T_kv, H,      \
+                                              row_begin, n_rows, scores, ld, none, CandArgs{}, st);
   DSA_F8_CASE(1, false) DSA_F8_CASE(2, false) DSA_F8_CASE(1, true) DSA_F8_CASE(2, true)
 #undef DSA_F8_CASE
   return hipErrorInvalidValue;
@@ -336,8 +584,52 @@ hipError_t launch_indexer_topk_fp8(const void* q, const void* qs, const void* k,
   const int mb = (H + 31) / 32;
 #define DSA_F8_CASE(MM, XX)                                                                  \
   if (mb == MM && mx == XX)                                                                  \
-    return launch_fp8_w<MM, XX, true>(q, qs, k, ks, w, w_dtype, rs, sl, T_kv, H, row_begin, \
-                                      n_rows, nullptr, n_cols, fa, st);
+    return launch_fp8_w<MM, XX, true, false>(q, qs, k, ks, w, w_dtype, rs, sl, T_kv, H,      \
+                                             row_begin, n_rows, nullptr, n_cols, fa, CandArgs{},  \
+                                             st);
+  DSA_F8_CASE(1, false) DSA_F8_CASE(2, false) DSA_F8_CASE(1, true) DSA_F8_CASE(2, true)
+#undef DSA_F8_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_indexer_cand_fp8(const void* q, const void* qs, const void* k, const void* ks,
+                                   bool mx, const void* w, int w_dtype, const int32_t* rs,
+                                   const int32_t* sl, int64_t T_kv, int H, int64_t row_begin,
+                                   int64_t n_rows, int64_t n_cols, int top_k, const CandArgs& ca,
+                                   hipStream_t st) {
+  if (n_rows == 0) return hipSuccess;
+  const int mb = (H + 31) / 32;
+  FusedArgs fa{};
+  fa.k = top_k;
+#define DSA_F8_CASE(MM, XX)                                                                 \
+  if (mb == MM && mx == XX)                                                                 \
+    return launch_fp8_w<MM, XX, false, true>(q, qs, k, ks, w, w_dtype, rs, sl, T_kv, H,     \
+                                             row_begin, n_rows, nullptr, n_cols, fa, ca, st);
+  DSA_F8_CASE(1, false) DSA_F8_CASE(2, false) DSA_F8_CASE(1, true) DSA_F8_CASE(2, true)
+#undef DSA_F8_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_indexer_rescue_fp8(const void* q, const void* qs, const void* k, const void* ks,
+                                     bool mx, const void* w, int w_dtype, const int32_t* rs,
+                                     const int32_t* sl, int64_t T_kv, int H, int64_t row_begin,
+                                     int64_t n_rows, int64_t n_cols, const FusedArgs& fa,
+                                     const CandArgs& ca, hipStream_t st) {
+  if (n_rows == 0) return hipSuccess;
+  const int mb = (H + 31) / 32;
+  dim3 grid((unsigned)std::min<int64_t>(ca.n_spill, n_rows)), block(kF8Waves * 64);
+#define DSA_F8_CASE(MM, XX)                                                                     \
+  if (mb == MM && mx == XX) {                                                                   \
+    if (w_dtype == 0)                                                                           \
+      hipLaunchKernelGGL((indexer_rescue_fp8_kernel<MM, uint16_t, XX>), grid, block, 0, st,     \
+                         (const uint8_t*)q, qs, (const uint8_t*)k, ks, (const uint16_t*)w, rs,  \
+                         sl, T_kv, H, row_begin, n_cols, fa, ca);                               \
+    else                                                                                        \
+      hipLaunchKernelGGL((indexer_rescue_fp8_kernel<MM, float, XX>), grid, block, 0, st,        \
+                         (const uint8_t*)q, qs, (const uint8_t*)k, ks, (const float*)w, rs, sl, \
+                         T_kv, H, row_begin, n_cols, fa, ca);                                   \
+    return hipGetLastError();                                                                   \
+  }
   DSA_F8_CASE(1, false) DSA_F8_CASE(2, false) DSA_F8_CASE(1, true) DSA_F8_CASE(2, true)
 #undef DSA_F8_CASE
   return hipErrorInvalidValue;

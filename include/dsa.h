@@ -78,7 +78,7 @@ typedef enum {
 const char* dsa_last_error(void);
 
 /* ABI version of this header (bumped on any signature change). */
-#define DSA_ABI_VERSION 9
+#define DSA_ABI_VERSION 10
 int dsa_abi_version(void);
 
 /* Limits enforced by the host checks. */
@@ -271,7 +271,7 @@ int64_t dsa_topk_workspace_bytes(int64_t n_rows, int64_t n_cols, int32_t k);
  * - n_cols <= DSA_FUSED_MAX_COLS: each row's scores stay in the CU's local
  *   memory and are selected there, in one launch; cand_buffer is unused
  *   (may be NULL).
- * - DSA_FUSED_MAX_COLS < n_cols <= DSA_TOPK_MAX_COLS (bf16 inputs only): the
+ * - DSA_FUSED_MAX_COLS < n_cols <= DSA_TOPK_MAX_COLS (any precision): the
  *   DSA page's candidate scheme (section 4: a caller-owned candidate buffer,
  *   then a stage-2 select). The indexer pass appends, for each row, the
  *   columns whose score reaches a lower bound sampled from the row, as
@@ -294,9 +294,8 @@ int64_t dsa_topk_workspace_bytes(int64_t n_rows, int64_t n_cols, int32_t k);
  * With T_kv = 0 every row is empty (k_idx and k_scale may then be NULL).
  * Errors: those of dsa_indexer_fwd / dsa_indexer_fwd_fp8 and dsa_topk,
  * DSA_ERR_VALUE for an unknown precision, n_cols outside
- * [1, DSA_TOPK_MAX_COLS], FP8 inputs with n_cols > DSA_FUSED_MAX_COLS, or a
- * missing, misaligned or too small cand_buffer when n_cols >
- * DSA_FUSED_MAX_COLS.
+ * [1, DSA_TOPK_MAX_COLS], or a missing, misaligned or too small cand_buffer
+ * when n_cols > DSA_FUSED_MAX_COLS.
  */
 int dsa_indexer_topk_fused(const void* q_idx, const void* q_scale, const void* k_idx,
                            const void* k_scale, int32_t precision, const void* w,

@@ -134,7 +134,9 @@ CASES = [
     # rows longer than the on-chip path: a candidate buffer of the queried size
     ("fused", dict(nc=4097), EVALUE), ("fused", dict(nc=4097, cb=FAKE2, cbn=CAND_4097 - 1), EVALUE),
     ("fused", dict(nc=4097, cb=FAKE2 + 4, cbn=CAND_4097), EVALUE),
-    ("fused", dict(nc=4097, cb=FAKE2, cbn=CAND_4097, prec=1, qs=FAKE2, ks=FAKE2), EVALUE),
+    ("fused", dict(nc=4097, cb=FAKE2, cbn=CAND_4097, prec=1, qs=FAKE2, ks=FAKE2), ERUNTIME),
+    ("fused", dict(nc=4097, cb=FAKE2, cbn=CAND_4097, prec=2, qs=FAKE2, ks=FAKE2), ERUNTIME),
+    ("fused", dict(nc=4097, cb=FAKE2, cbn=CAND_4097 - 1, prec=2, qs=FAKE2, ks=FAKE2), EVALUE),
     ("fused", dict(nc=4097, cb=FAKE2, cbn=CAND_4097), ERUNTIME),
     ("fused", dict(nc=65536, nr=0, cb=None), OK),
     ("fused", dict(ldi=2047), EVALUE), ("fused", dict(D=96), EVALUE),

@@ -1,5 +1,6 @@
 """Parity of the combined indexer + top-K path for rows longer than 4096
-columns (dsa_indexer_topk_fused with a candidate buffer).
+columns (dsa_indexer_topk_fused with a candidate buffer), from bf16 or FP8
+indexer inputs.
 
 The indexer pass of that path computes every score with the standalone
 indexer's arithmetic, so its selection is compared bit-exactly with the
@@ -22,7 +23,7 @@ import torch
 import deepseek_sparse_attention_dsa_amd as dsa
 from gpu_helpers import DEV, i64, say
 from oracle import dsa_oracle as O
-from workloads import make_custom
+from workloads import make_custom, quantize_fp8
 
 pytestmark = pytest.mark.gpu
 
@@ -48,6 +49,25 @@ def _run(q, k_idx, w, rs, sl, k, n_cols, row_begin=0, n_rows=None, values=True, 
     torch.cuda.synchronize()
     rescued = int(buf[:1].view(torch.int32).item())
     return res, rescued
+
+
+def _quantize(q, k_idx, scaling):
+    """FP8 inputs of the call for q / k_idx ("per_token" or "mx"), or None."""
+    if scaling is None:
+        return q, k_idx, {}
+    block = 32 if scaling == "mx" else None
+    q8, qs = quantize_fp8(q, block)
+    k8, ks = quantize_fp8(k_idx, block)
+    mode = dsa.DSA_MXFP8 if scaling == "mx" else dsa.DSA_FP8_PER_TOKEN
+    return q8, k8, dict(q_scale=qs, k_scale=ks, fp8_scaling=mode)
+
+
+def _scores(q, k_idx, w, rs, sl, fp8, **kw):
+    """The standalone indexer's scores for the same inputs."""
+    if fp8:
+        return dsa.dsa_indexer_fwd_fp8(q, fp8["q_scale"], k_idx, fp8["k_scale"], w, rs, sl,
+                                       scaling=fp8["fp8_scaling"], **kw)
+    return dsa.dsa_indexer_fwd(q, k_idx, w, rs, sl, **kw)
 
 
 def _compare(res, sc, seq_lens, row_starts, k, n_cols, rows=None):
@@ -84,20 +104,28 @@ def _workload(doc_lens, H, D, wdt, k, seed):
     return wl, w
 
 
-@pytest.mark.parametrize("doc_lens,H,D,wdt,k", [
-    ([12288], 64, 128, torch.bfloat16, 2048),
-    ([9000, 700, 5200], 64, 128, torch.float32, 512),
-    ([6000, 4500], 32, 64, torch.bfloat16, 100),
-    ([10000], 17, 64, torch.float32, 1),
-    ([8193, 3], 33, 128, torch.bfloat16, 2047),
+@pytest.mark.parametrize("doc_lens,H,D,wdt,k,fp8", [
+    ([12288], 64, 128, torch.bfloat16, 2048, None),
+    ([9000, 700, 5200], 64, 128, torch.float32, 512, None),
+    ([6000, 4500], 32, 64, torch.bfloat16, 100, None),
+    ([10000], 17, 64, torch.float32, 1, None),
+    ([8193, 3], 33, 128, torch.bfloat16, 2047, None),
+    # FP8 inputs (D = 128): E8M0 block scales and fp32 per-token descales
+    ([12288], 64, 128, torch.bfloat16, 2048, "mx"),
+    ([12288], 64, 128, torch.bfloat16, 2048, "per_token"),
+    ([9000, 700, 5200], 64, 128, torch.float32, 512, "mx"),
+    ([8193, 3], 33, 128, torch.bfloat16, 2047, "per_token"),
+    ([10000], 17, 128, torch.float32, 1, "mx"),
+    ([6000, 4500], 8, 128, torch.bfloat16, 100, "per_token"),
 ])
-def test_cand_random_scores(doc_lens, H, D, wdt, k):
-    say("cand path", doc_lens, H, D, wdt, k)
+def test_cand_random_scores(doc_lens, H, D, wdt, k, fp8):
+    say("cand path", doc_lens, H, D, wdt, k, fp8)
     wl, w = _workload(doc_lens, H, D, wdt, k, seed=sum(doc_lens) + H)
+    q, k_idx, kw = _quantize(wl.q_idx, wl.k_idx, fp8)
     rs, sl = dsa.dsa_packed_metadata(wl.cu_seqlens, wl.T)
     n_cols = max(doc_lens)
-    res, rescued = _run(wl.q_idx, wl.k_idx, w, rs, sl, k, n_cols)
-    sc = dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, w, rs, sl, width=n_cols)
+    res, rescued = _run(q, k_idx, w, rs, sl, k, n_cols, **kw)
+    sc = _scores(q, k_idx, w, rs, sl, kw, width=n_cols)
     torch.cuda.synchronize()
     _compare(res, sc, sl, rs, k, n_cols)
     assert rescued == 0, "random scores leave no row to the rescue pass"
@@ -132,20 +160,26 @@ def _hot_prefix(doc_lens, H, D, seed, flat=False):
 # sample rank is below that, the bound lands among the hot scores and fewer
 # than k columns pass (k = 2048: the bound lands among the ordinary scores
 # near the k-th largest, and only part of the rows come short).
-@pytest.mark.parametrize("doc_lens,H,D,k,flat,all_long", [
-    ([10000], 64, 128, 2048, False, False),  # lower bound too high for some rows
-    ([9000], 8, 64, 64, True, True),         # all scores equal: the lists overflow
-    ([8500, 9300], 64, 128, 300, False, True),
-    ([9100], 20, 64, 200, False, True),
+@pytest.mark.parametrize("doc_lens,H,D,k,flat,all_long,fp8", [
+    ([10000], 64, 128, 2048, False, False, None),  # lower bound too high for some rows
+    ([9000], 8, 64, 64, True, True, None),         # all scores equal: the lists overflow
+    ([8500, 9300], 64, 128, 300, False, True, None),
+    ([9100], 20, 64, 200, False, True, None),
+    ([10000], 64, 128, 2048, False, False, "mx"),
+    ([9000], 8, 128, 64, True, True, "per_token"),
+    ([9000], 8, 128, 64, True, True, "mx"),
+    ([8500, 9300], 64, 128, 300, False, True, "per_token"),
+    ([9100], 20, 128, 200, False, True, "mx"),
 ])
-def test_cand_rescue(doc_lens, H, D, k, flat, all_long):
-    say("cand rescue", doc_lens, H, D, k, flat)
+def test_cand_rescue(doc_lens, H, D, k, flat, all_long, fp8):
+    say("cand rescue", doc_lens, H, D, k, flat, fp8)
     q, k_idx, w, cu = _hot_prefix(doc_lens, H, D, seed=sum(doc_lens) + k, flat=flat)
+    q, k_idx, kw = _quantize(q, k_idx, fp8)
     T = sum(doc_lens)
     rs, sl = dsa.dsa_packed_metadata(cu, T)
     n_cols = max(doc_lens)
-    res, rescued = _run(q, k_idx, w, rs, sl, k, n_cols)
-    sc = dsa.dsa_indexer_fwd(q, k_idx, w, rs, sl, width=n_cols)
+    res, rescued = _run(q, k_idx, w, rs, sl, k, n_cols, **kw)
+    sc = _scores(q, k_idx, w, rs, sl, kw, width=n_cols)
     torch.cuda.synchronize()
     _compare(res, sc, sl, rs, k, n_cols)
     # rows no longer than a list take every column and are never rescued
@@ -210,21 +244,23 @@ def _long_rows(T, k):
     return sorted(r for r in rows if 0 <= r < T)
 
 
-def test_cand_long_context_sampled():
+@pytest.mark.parametrize("fp8", [None, "mx", "per_token"])
+def test_cand_long_context_sampled(fp8):
     """One 65536-token sequence, indexer 64 x 128, top-2048, all rows in one
-    call: sampled rows (the selection regimes' edges and random ones)
-    against the oracle on each row's standalone scores."""
+    call (bf16 inputs, or their FP8 quantisation): sampled rows (the
+    selection regimes' edges and random ones) against the oracle on each
+    row's standalone scores."""
     T, k = 65536, 2048
-    say("cand long context", T)
+    say("cand long context", T, fp8)
     wl = make_custom([T], H=1, D_qk=64, D_v=64, H_idx=64, D_idx=128, topk=k, seed=1003,
                      device=DEV)
+    q, k_idx, kw = _quantize(wl.q_idx, wl.k_idx, fp8)
     rs, sl = dsa.dsa_packed_metadata(wl.cu_seqlens, T)
-    res, rescued = _run(wl.q_idx, wl.k_idx, wl.w, rs, sl, k, T)
+    res, rescued = _run(q, k_idx, wl.w, rs, sl, k, T, **kw)
     rows = _long_rows(T, k)
     sc = torch.empty((len(rows), T), dtype=torch.float32, device=DEV)
     for i, r in enumerate(rows):
-        dsa.dsa_indexer_fwd(wl.q_idx, wl.k_idx, wl.w, rs, sl, row_begin=r, n_rows=1,
-                            scores=sc[i:i + 1])
+        _scores(q, k_idx, wl.w, rs, sl, kw, row_begin=r, n_rows=1, scores=sc[i:i + 1])
     torch.cuda.synchronize()
     _compare(res, sc, sl, rs, k, T, rows=rows)
     assert rescued == 0
