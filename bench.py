@@ -29,6 +29,11 @@ per host core available, at most 16) on a bounded seeded sample of the same
 workload. `stages_flushed` repeats the stage timings over a few extra steps
 that each start after 512 MiB were written, so that the 256 MB MALL holds
 none of the step's inputs (the main figures are warm: back-to-back steps).
+`measured_peaks` holds what this device sustains, from the probes of
+libdsa_peaks.so run after the timed steps: an MFMA-only loop per MFMA form
+(bf16, FP8, MXFP8) and a 16-byte vector copy and read of 1 GiB; each
+roofline entry adds `measured_peak` and `frac_of_measured` beside the
+published `peak` and `frac`.
 """
 
 from __future__ import annotations
@@ -98,6 +103,8 @@ def parse():
                    help="approximate wall time of the oracle baseline (both legs)")
     p.add_argument("--cpu-workers", type=int, default=0,
                    help="oracle worker processes (0: the host cores available, at most 16)")
+    p.add_argument("--no-peaks", action="store_true",
+                   help="skip the measured-peak probes (MFMA loops, HBM copy and read)")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (3 times), the "
                         "known-size reference for the FETCH_SIZE / WRITE_SIZE counters")
@@ -507,6 +514,79 @@ def cpu_baseline(wl, rs, sl, indices, topk_length, budget_s, workers):
 # The timed path
 # ---------------------------------------------------------------------------
 
+def measure_peaks(stream, reps: int = 5):
+    """Rates this device sustains: MFMA-only loops (bf16, FP8, MXFP8; 4 waves per
+    SIMD, register operands) and a 1 GiB 16-byte vector copy and read, each the
+    median of `reps` launches after one warm-up, timed with events on `stream`."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "deepseek_sparse_attention_dsa_amd", "libdsa_peaks.so"))
+    lib.dsa_peak_mfma_flop.restype = ctypes.c_double
+    lib.dsa_peak_mfma_flop.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]
+    lib.dsa_peak_mfma.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    lib.dsa_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                  ctypes.c_int32, ctypes.c_void_p]
+    lib.dsa_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    threads = lib.dsa_peak_threads_per_block()
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(fn):
+        fn()
+        ms = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            rc = fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"peak probe failed ({rc})")
+            ms.append(a.elapsed_time(b))
+        return float(np.median(ms))
+
+    res = {"compute_units": n_cu}
+    blocks = 4 * n_cu  # four workgroups of four waves per CU: four waves per SIMD
+    sink = torch.empty((blocks * threads,), dtype=torch.float32, device="cuda:0")
+    for name, kind, iters in (("bf16", 0, 4000), ("fp8", 1, 2000), ("mxfp8", 2, 2000)):
+        ms = timed(lambda: lib.dsa_peak_mfma(kind, iters, blocks, ctypes.c_void_p(sink.data_ptr()),
+                                             sp))
+        res[f"{name}_mfma_tflops"] = lib.dsa_peak_mfma_flop(kind, iters, blocks) / ms / 1e9
+    del sink
+    nbytes = 1 << 30
+    src = torch.ones((nbytes // 4,), dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    cblocks = 4 * n_cu
+    wsink = torch.empty((cblocks * threads,), dtype=torch.int32, device="cuda:0")
+    ms = timed(lambda: lib.dsa_peak_copy(ctypes.c_void_p(src.data_ptr()),
+                                         ctypes.c_void_p(dst.data_ptr()), nbytes, cblocks, sp))
+    res["hbm_copy_gbs"] = 2.0 * nbytes / ms / 1e6
+    ms = timed(lambda: lib.dsa_peak_read(ctypes.c_void_p(src.data_ptr()), nbytes, cblocks,
+                                         ctypes.c_void_p(wsink.data_ptr()), sp))
+    res["hbm_read_gbs"] = nbytes / ms / 1e6
+    del src, dst, wsink
+    return res
+
+
+def add_measured(entry, peaks, mx=False):
+    """measured_peak / frac_of_measured of a roofline entry (its own MFMA form or
+    the HBM copy rate)."""
+    if not peaks:
+        return
+    if entry["unit"] == "GB/s":
+        m = peaks["hbm_copy_gbs"]
+    elif entry["peak"] == PEAK_FP8_TFLOPS:
+        m = peaks["mxfp8_mfma_tflops" if mx else "fp8_mfma_tflops"]
+    else:
+        m = peaks["bf16_mfma_tflops"]
+    entry["measured_peak"] = m
+    entry["frac_of_measured"] = entry["achieved"] / m
+
+
 def roofline_entry(kernel, bound, algorithmic_total, launches, kernel_ms_total, peak, unit,
                    traffic):
     """Roofline of one kernel family over one step: achieved = algorithmic work per
@@ -736,6 +816,10 @@ def main():
                 stages_flushed["indexer"] = {"ms": fst["indexer"][0]}
                 stages_flushed["topk"] = {"ms": fst["topk"][0]}
 
+    peaks = None if args.no_peaks else measure_peaks(stream)
+    for e in rooflines.values():
+        add_measured(e, peaks, mx=bool(fp8) and fp8["scaling"] == "mx")
+
     # the dominant kernel: the stage with the most kernel time per step
     dominant = max(rooflines, key=lambda s: rooflines[s]["avg_launch_ms"] *
                    rooflines[s]["launches_per_step"])
@@ -793,6 +877,7 @@ def main():
         "stages_flushed": stages_flushed,
         "roofline": roofline,
         "rooflines": rooflines,
+        "measured_peaks": peaks,
         "cpu_baseline": None,
     }
     rec["config"]["indexer_inputs"] = (

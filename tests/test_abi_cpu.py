@@ -336,3 +336,52 @@ def test_topk_workspace_query():
         assert lib.dsa_topk_workspace_bytes(*args) == -1, args
     with pytest.raises(ValueError):
         dsa.dsa_topk_workspace_bytes(8, 4096, 4096)
+
+
+PEAKS_HEADER = os.path.join(ROOT, "include", "dsa_peaks.h")
+PEAKS_LIB = os.path.join(ROOT, "deepseek_sparse_attention_dsa_amd", "libdsa_peaks.so")
+
+
+def _peaks_lib():
+    import ctypes
+    lib = ctypes.CDLL(PEAKS_LIB)
+    lib.dsa_peak_mfma_flop.restype = ctypes.c_double
+    lib.dsa_peak_mfma_flop.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32]
+    lib.dsa_peak_mfma.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.c_void_p]
+    lib.dsa_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                  ctypes.c_int32, ctypes.c_void_p]
+    lib.dsa_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+def test_peaks_library_exports_and_work_counts():
+    """The measurement probes: every declared symbol exported, the FLOP each
+    MFMA form performs, and invalid arguments rejected before any launch."""
+    text = re.sub(r"/\*.*?\*/", "", open(PEAKS_HEADER).read(), flags=re.S)
+    names = set(re.findall(r"^\s*(?:int|double)\s+(dsa_\w+)\s*\(", text, flags=re.M))
+    assert {"dsa_peak_mfma", "dsa_peak_mfma_flop", "dsa_peak_copy", "dsa_peak_read",
+            "dsa_peak_threads_per_block"} <= names
+    out = subprocess.run(["nm", "-D", "--defined-only", PEAKS_LIB], capture_output=True,
+                         text=True).stdout
+    assert names <= set(re.findall(r"\bT\s+(dsa_\w+)", out))
+    lib = _peaks_lib()
+    assert lib.dsa_peak_threads_per_block() == 256
+    # 4 chains x iters MFMAs per wave, 4 waves per workgroup
+    assert lib.dsa_peak_mfma_flop(0, 10, 3) == 2 * 32 * 32 * 16 * 4 * 10 * 4 * 3
+    assert lib.dsa_peak_mfma_flop(1, 10, 3) == 2 * 32 * 32 * 64 * 4 * 10 * 4 * 3
+    assert lib.dsa_peak_mfma_flop(2, 1, 1) == 2 * 32 * 32 * 64 * 4 * 4
+    for bad in [(3, 10, 3), (0, 0, 3), (0, 10, 0)]:
+        assert lib.dsa_peak_mfma_flop(*bad) == -1.0
+    assert lib.dsa_peak_mfma(0, 0, 4, FAKE, None) == 1
+    assert lib.dsa_peak_mfma(0, 10, 0, FAKE, None) == 1
+    assert lib.dsa_peak_mfma(0, 10, 4, None, None) == 1
+    assert lib.dsa_peak_mfma(0, 10, 4, FAKE + 4, None) == 1
+    assert lib.dsa_peak_mfma(7, 10, 4, FAKE, None) == 1
+    assert lib.dsa_peak_copy(FAKE, FAKE2, 100, 4, None) == 1
+    assert lib.dsa_peak_copy(FAKE, FAKE2, 0, 4, None) == 1
+    assert lib.dsa_peak_copy(FAKE + 8, FAKE2, 4096, 4, None) == 1
+    assert lib.dsa_peak_copy(None, FAKE2, 4096, 4, None) == 1
+    assert lib.dsa_peak_read(FAKE, 4096, 0, FAKE2, None) == 1
+    assert lib.dsa_peak_read(FAKE, 4096, 4, None, None) == 1
