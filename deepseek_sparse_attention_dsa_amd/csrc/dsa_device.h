@@ -180,37 +180,6 @@ __device__ __forceinline__ float halfwave_max(float v) {
 }
 __device__ __forceinline__ int shfl_xor_i(int v, int m) { return __shfl_xor(v, m, kWave); }
 
-// Key range of a workgroup's rows r0 .. r0 + rows - 1 (rows <= 64): the union
-// of [row_starts[t], row_starts[t] + min(seq_lens[t], cap)) over its rows
-// t = row_begin + r with r < n_rows, written to s_range[0..1] as
-// [kb, ke) (kb >= ke: no keys). Called by every lane of one wave: lane i
-// loads row i, so the loads of all rows are in flight together.
-__device__ __forceinline__ void wave_key_range(const int32_t* row_starts, const int32_t* seq_lens,
-                                               int64_t row_begin, int64_t r0, int64_t n_rows,
-                                               int rows, int64_t cap, int32_t* s_range) {
-  const int lane = __lane_id();
-  int32_t kb = INT32_MAX, ke = 0;
-  const int64_t r = r0 + lane;
-  if (lane < rows && r < n_rows) {
-    const int64_t t = row_begin + r;
-    const int32_t s0 = row_starts[t];
-    const int32_t n = (int32_t)min((int64_t)seq_lens[t], cap);
-    if (n > 0) {
-      kb = s0;
-      ke = s0 + n;
-    }
-  }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    kb = min(kb, __shfl_xor(kb, m, kWave));
-    ke = max(ke, __shfl_xor(ke, m, kWave));
-  }
-  if (lane == 0) {
-    s_range[0] = kb;
-    s_range[1] = ke;
-  }
-}
-
 // Wave-wide inclusive scan / reductions on DPP lane moves (no LDS round
 // trips): row_shr 1, 2, 4, 8 inside each 16-lane row, then row_bcast 15 and
 // row_bcast 31 carry the row totals upwards (GFX9 DPP controls).

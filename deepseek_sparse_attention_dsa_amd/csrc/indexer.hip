@@ -273,8 +273,12 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
   // Lane l < 32 sums key l of block 0 over both half-waves, lane l >= 32
   // key l - 32 of block 1: one exchange between the half-waves. Scores go
   // through a buffer descriptor of the wave's row whose range is the row's
-  // valid columns: stores of other columns are dropped by the hardware range
-  // check, so the tile loop has no branches.
+  // valid columns; a column outside the row takes an offset past the range
+  // (a select, so the tile loop has no branches), whose store the hardware
+  // drops. The offset is selected rather than left to wrap below zero: the
+  // compiler may move a constant part of it into the instruction's offset
+  // field, and the range check then sees a wrapped register part and drops
+  // valid stores too.
   // (FUSE: the row lives in LDS; columns outside the row go to a spare slot.)
   const __amdgpu_buffer_rsrc_t srow =
       raw_buffer(MODE != kModeScores ? (const void*)scores : (const void*)(scores + r * ld),
@@ -311,7 +315,7 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
     } else if constexpr (CAND) {
       append(__float_as_uint(score), j);
     } else {
-      buffer_store_f32(score, srow, j * 4u);  // negative: dropped
+      buffer_store_f32(score, srow, j < (uint32_t)qlen ? j * 4u : 0x80000000u);
     }
   };
 

@@ -7,10 +7,13 @@
 // S[t, j] = sum_h W[t,h] * ReLU(Q[t,h,:] . K[start(t)+j, :]), head dim 128.
 //
 // The mapping is the one of the bf16 indexer kernel (one query row per wave,
-// 8 waves per workgroup, 64-key tiles of K in a double-buffered LDS ring, the
+// 8 waves per workgroup, key tiles in a double-buffered LDS ring, the
 // epilogue of each 32-key block under the MFMAs of the next), with the dot
 // products on v_mfma_(scale_)f32_32x32x64_f8f6f4: two k-steps of 64 over the
-// head dim instead of eight of 16, at twice the bf16 rate per FLOP.
+// head dim instead of eight of 16, at twice the bf16 rate per FLOP. A tile is
+// 256 keys (one barrier per 256 keys: the FP8 MFMAs of a tile take half the
+// time of the bf16 ones, so the per-tile cost weighs twice as much), 64 in
+// the combined launch whose LDS holds the rows' scores.
 // - Per-token descales: ReLU(a * x) = a * ReLU(x) for a >= 0, so the query
 //   descale of head h folds into W[t,h] and the key descale multiplies the
 //   finished score of its key; the MFMAs run unscaled.
@@ -26,7 +29,7 @@ namespace dsa {
 namespace {
 
 constexpr int kF8Waves = 8;     // query rows per workgroup
-constexpr int kF8Pairs = 2;    // 64-key pairs of 32-key blocks per LDS tile (scores to HBM)
+constexpr int kF8Pairs = 4;    // 64-key pairs of 32-key blocks per LDS tile (scores, candidates)
 constexpr int kF8D = 128;       // head dim (bytes per FP8 row)
 constexpr int kF8KS = kF8D / 64;  // MFMA k-steps over the head dim
 constexpr int kF8RowB = kF8D + 16;  // LDS row stride in bytes (16 B pad: conflict-free b128 reads)
@@ -46,6 +49,19 @@ template <>
 __device__ __forceinline__ float load_wf<float>(const float* w, int64_t i) {
   return w[i];
 }
+// Four consecutive weights w[i .. i+3] (i a multiple of 4, w aligned to 4 weights).
+template <typename WT>
+__device__ __forceinline__ f32x4 load_wf4(const WT* w, int64_t i);
+template <>
+__device__ __forceinline__ f32x4 load_wf4<uint16_t>(const uint16_t* w, int64_t i) {
+  const u32x2 v = *reinterpret_cast<const u32x2*>(w + i);
+  return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xffff0000u),
+               __uint_as_float(v[1] << 16), __uint_as_float(v[1] & 0xffff0000u)};
+}
+template <>
+__device__ __forceinline__ f32x4 load_wf4<float>(const float* w, int64_t i) {
+  return *reinterpret_cast<const f32x4*>(w + i);
+}
 
 // MB: number of 32-head blocks (H <= 32*MB). MX: block-scaled (true) or
 // per-token descales (false). qs / ks: fp32 descales [T, H] / [T_kv]
@@ -61,7 +77,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
     const uint8_t* __restrict__ q, const void* __restrict__ qs, const uint8_t* __restrict__ k,
     const void* __restrict__ ks, const WT* __restrict__ w, const int32_t* __restrict__ row_starts,
     const int32_t* __restrict__ seq_lens, int64_t T_kv, int H, int64_t row_begin, int64_t n_rows,
-    float* __restrict__ scores, int64_t ld, FusedArgs fa, CandArgs ca) {
+    float* __restrict__ scores, int64_t ld, FusedArgs fa, CandArgs ca, bool w_vec) {
   constexpr int kF8Tile = 64 * P;  // keys per LDS tile
   constexpr int TILE_B = kF8Tile * kF8RowB;
   constexpr int CHUNKS = kF8Tile * kF8D / 16;   // 16-byte chunks per tile
@@ -70,14 +86,12 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   static_assert(CHUNKS % NT == 0 && kF8Tile <= NT, "whole chunks per thread");
   __shared__ __attribute__((aligned(16))) unsigned char ktile[2 * TILE_B];
   __shared__ uint32_t kscale[2][kF8Tile];  // per key: fp32 descale bits, or 4 E8M0 bytes
-  __shared__ int32_t s_range[2];
   __shared__ __attribute__((aligned(16))) float s_rows[FUSE ? kF8Waves * kFuseRowStride : 4];
   static_assert(!FUSE || 2 * TILE_B >= kF8Waves * 256 * 4, "select histograms fit the tile ring");
   static_assert(!(FUSE && CAND), "one output mode");
   // CAND: the sampled keys of each wave's row, lane-major (slot 64 i + lane),
   // and the rows' valid lengths
-  __shared__ uint32_t s_samp[CAND ? kF8Waves * 2 * kF8SampleTiles * 64 : 1];
-  __shared__ int32_t s_qlen[kF8Waves];
+  __shared__ uint32_t s_samp[CAND ? kF8Waves * P * kF8SampleTiles * 64 : 1];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -87,52 +101,32 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   const int64_t r0 = qblk * kF8Waves;
   const int64_t cap = T_kv > 0 ? ld : 0;  // longest row length taken (no keys: none)
 
-  // This wave's query. A operand of k-step s for head 32*mb + l%32: bytes
-  // 64s + 16*half .. +15 and 64s + 32 + 16*half .. +15 of the head's row.
+  // Rows of the workgroup: lane i < kF8Waves holds row r0 + i's start and
+  // valid length (>= 0; the range checks of the score writes rely on it).
+  // Every wave forms the workgroup's key range [kb, ke), the union of its
+  // rows' ranges, and the longest row from them, so that the first key tile
+  // is requested before the query loads and without a barrier.
   const int64_t r = r0 + wave;
   const bool live = r < n_rows;
   const int64_t t = row_begin + (live ? r : 0);
-  const int32_t qstart = live ? row_starts[t] : 0;
-  // valid columns of the row, >= 0 (the range checks of the score writes rely on it)
-  const int32_t qlen = live ? (int32_t)max((int64_t)0, min((int64_t)seq_lens[t], cap)) : 0;
-  i32x8 qa[MB][kF8KS];
-  int qsc[MB][kF8KS];  // MX: E8M0 byte of block 2s + half of the lane's head
-  float wv[MB][16];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int head = mb * 32 + (lane & 31);
-    const bool hv = live && head < H;
-    const uint8_t* qrow = q + (t * H + head) * kF8D;
-#pragma unroll
-    for (int s = 0; s < kF8KS; ++s) {
-      const u32x4 lo = hv ? load16(qrow + 64 * s + 16 * half) : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 hi = hv ? load16(qrow + 64 * s + 32 + 16 * half) : u32x4{0u, 0u, 0u, 0u};
-      qa[mb][s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      if constexpr (MX)
-        qsc[mb][s] = hv ? (int)((const uint8_t*)qs)[(t * H + head) * 4 + 2 * s + half] : 127;
-      else
-        qsc[mb][s] = 0;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int oh = mb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-      float wf = (live && oh < H) ? load_wf<WT>(w, t * H + oh) : 0.0f;
-      if constexpr (!MX) wf *= (live && oh < H) ? ((const float*)qs)[t * H + oh] : 0.0f;
-      wv[mb][i] = wf;
-    }
+  int32_t m_s0 = 0, m_n = 0;
+  if (lane < kF8Waves && r0 + lane < n_rows) {
+    const int64_t tt = row_begin + r0 + lane;
+    m_s0 = row_starts[tt];
+    m_n = (int32_t)max((int64_t)0, min((int64_t)seq_lens[tt], cap));
   }
-  // Key range of the workgroup (after the Q loads, so that wave 0's loads of
-  // both are in flight together).
-  if (threadIdx.x < 64)
-    wave_key_range(row_starts, seq_lens, row_begin, r0, n_rows, kF8Waves, cap, s_range);
-  if (lane == 0) s_qlen[wave] = qlen;
-  __syncthreads();
-  const int32_t kb = s_range[0];
-  const int32_t ke = s_range[1];
-  int32_t nmax = 0;
+  int32_t kb = m_n > 0 ? m_s0 : INT32_MAX, ke = m_n > 0 ? m_s0 + m_n : 0, nmax = m_n;
 #pragma unroll
-  for (int i = 0; i < kF8Waves; ++i) nmax = max(nmax, s_qlen[i]);
+  for (int m = 1; m < kF8Waves; m <<= 1) {
+    kb = min(kb, __shfl_xor(kb, m, kWave));
+    ke = max(ke, __shfl_xor(ke, m, kWave));
+    nmax = max(nmax, __shfl_xor(nmax, m, kWave));
+  }
+  kb = __builtin_amdgcn_readfirstlane(kb);
+  ke = __builtin_amdgcn_readfirstlane(ke);
+  nmax = __builtin_amdgcn_readfirstlane(nmax);
+  const int32_t qstart = __shfl(m_s0, wave, kWave);
+  const int32_t qlen = __shfl(m_n, wave, kWave);
   if constexpr (CAND)
     if (blockIdx.x == 0 && threadIdx.x == 0) *ca.n_queued = 0u;  // the stage-2 queue starts empty
   if (kb >= ke) {  // uniform: no row of the workgroup has a key
@@ -143,6 +137,12 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
       if (live && lane == 0) ca.count[r] = 0;
     return;
   }
+  // This wave's query (loaded after the first key tile is requested). A
+  // operand of k-step s for head 32*mb + l%32: bytes 64s + 16*half .. +15 and
+  // 64s + 32 + 16*half .. +15 of the head's row.
+  i32x8 qa[MB][kF8KS];
+  int qsc[MB][kF8KS];  // MX: E8M0 byte of block 2s + half of the lane's head
+  float wv[MB][16];
 
   // Staging of keys [k0, k0 + kF8Tile): thread -> 16-byte chunks
   // c = tid + NT*i (key c / 8); threads below kF8Tile also fetch the scale
@@ -241,8 +241,12 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   // Lane l < 32 sums key l of block 0 over both half-waves, lane l >= 32 key
   // l - 32 of block 1; the key descale (per-token form) multiplies the sum.
   // Scores go through a buffer descriptor of the wave's row whose range is
-  // the row's valid columns: stores of other columns are dropped by the
-  // hardware range check, so the tile loop has no branches.
+  // the row's valid columns; a column outside the row takes an offset past
+  // the range (a select, so the tile loop has no branches), whose store the
+  // hardware drops. The offset is selected rather than left to wrap below
+  // zero: the compiler may move a constant part of it into the instruction's
+  // offset field, and the range check then sees a wrapped register part and
+  // drops valid stores too.
   // (FUSE: the row lives in LDS; columns outside the row go to a spare slot.)
   const __amdgpu_buffer_rsrc_t srow =
       raw_buffer((FUSE || CAND) ? (const void*)scores : (const void*)(scores + r * ld),
@@ -279,7 +283,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
     else if constexpr (CAND)
       append(__float_as_uint(score), j);
     else
-      buffer_store_f32(score, srow, j * 4u);  // negative: dropped
+      buffer_store_f32(score, srow, j < (uint32_t)qlen ? j * 4u : 0x80000000u);
   };
   // CAND: whether the workgroup samples (a row longer than the capacity),
   // and the first key of sample tile i (tiles of the workgroup's range).
@@ -293,32 +297,108 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   // outside its own range are computed and their stores dropped). The first
   // pending write targets columns before the row, so it is dropped too.
   load_tile(kb);
+
+  // Query fragments, MX block scales and the weights of the 16 heads whose
+  // scores the lane receives per head block (32*mb + 8*(i/4) + 4*half +
+  // i%4; per-token: times the query descale). The loads are unconditional
+  // (clamped head, then zeroed) and all issued before any of their values is
+  // used, so they are in flight together.
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int head = mb * 32 + (lane & 31);
+    const int hq = head < H ? head : H - 1;
+    const uint8_t* qrow = q + (t * H + hq) * kF8D;
+#pragma unroll
+    for (int s = 0; s < kF8KS; ++s) {
+      const u32x4 lo = load16(qrow + 64 * s + 16 * half);
+      const u32x4 hi = load16(qrow + 64 * s + 32 + 16 * half);
+      qa[mb][s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                        (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      if constexpr (MX)
+        qsc[mb][s] = (int)((const uint8_t*)qs)[(t * H + hq) * 4 + 2 * s + half];
+      else
+        qsc[mb][s] = 0;
+    }
+  }
+  if (w_vec) {  // uniform: runs of 4 heads are whole, w (and qs) aligned to 4 entries
+    f32x4 wr[MB][4], dr[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int oh0 = mb * 32 + 8 * j + 4 * half;
+        const int64_t i0 = t * H + (oh0 < H ? oh0 : 0);
+        wr[mb][j] = load_wf4<WT>(w, i0);
+        if constexpr (!MX) dr[mb][j] = *reinterpret_cast<const f32x4*>((const float*)qs + i0);
+      }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          wv[mb][4 * j + c] = MX ? wr[mb][j][c] : wr[mb][j][c] * dr[mb][j][c];
+  } else {
+    float dr[MB][16];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int oh = mb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        const int64_t i0 = t * H + (oh < H ? oh : 0);
+        wv[mb][i] = load_wf<WT>(w, i0);
+        if constexpr (!MX) dr[mb][i] = ((const float*)qs)[i0];
+      }
+    if constexpr (!MX)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) wv[mb][i] *= dr[mb][i];
+  }
+  if (!live || 32 * MB > H) {  // uniform per wave: zero what is past the row or the heads
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int head = mb * 32 + (lane & 31);
+#pragma unroll
+      for (int s = 0; s < kF8KS; ++s)
+        if (!live || head >= H) {
+          qa[mb][s] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+          if constexpr (MX) qsc[mb][s] = 127;
+        }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int oh = mb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (!live || oh >= H) wv[mb][i] = 0.0f;
+      }
+    }
+  }
+
   store_tile(0);
   __syncthreads();
   // CAND: the sample tiles are scored once; the tile loop skips them and
   // appends their saved keys in their place. Sample tile 0 is the range's
-  // first tile, the others are at least 8 tiles apart (a sampling workgroup
-  // has more than 64 tiles).
-  uint32_t* const wsamp = s_samp + (CAND ? wave * 2 * kF8SampleTiles * 64 + lane : 0);
+  // first tile, the others are at least 4 tiles apart (a sampling workgroup
+  // has more than 32 tiles of 256 keys).
+  uint32_t* const wsamp = s_samp + (CAND ? wave * P * kF8SampleTiles * 64 + lane : 0);
   auto append_saved = [&](int i) {
 #pragma unroll
-    for (int hp = 0; hp < 2; ++hp)
-      append(wsamp[64 * (2 * i + hp)], (uint32_t)(sample_start(i) + 64 * hp + lane - qstart));
+    for (int hp = 0; hp < P; ++hp)
+      append(wsamp[64 * (P * i + hp)], (uint32_t)(sample_start(i) + 64 * hp + lane - qstart));
   };
   if constexpr (CAND) {
     if (sample) {  // uniform
       // The sample tiles go through the ring in turn (the last prefetch is
       // the tile loop's first tile, the one after sample tile 0, which lands
-      // in buffer 0); lane l keeps the scores of keys s + l and s + 64 + l of
-      // each sample tile s in the wave's LDS slots.
-      static_assert(P == 2 && kF8SampleTiles % 2 == 0, "sample layout");
+      // in buffer 0); lane l keeps the scores of keys s + 64 p + l (p < P)
+      // of each sample tile s in the wave's LDS slots.
+      static_assert(kF8SampleTiles % 2 == 0, "sample layout");
 #pragma unroll 1
       for (int i = 0; i < kF8SampleTiles; ++i) {
         load_tile(i + 1 < kF8SampleTiles ? sample_start(i + 1) : kb + kF8Tile);
         const int sb = i & 1;
         const int32_t s0 = sample_start(i);
 #pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
+        for (int pr = 0; pr < P; ++pr) {
           BOp b0, b1;
           read_block(sb, 2 * pr, b0);
           read_block(sb, 2 * pr + 1, b1);
@@ -328,7 +408,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
           if constexpr (!MX) score *= __uint_as_float(kscale[sb][64 * pr + lane]);
           const uint32_t j = (uint32_t)(s0 + 64 * pr + lane - qstart);
           // (invalid: all-ones bits, whose key is 0)
-          wsamp[64 * (2 * i + pr)] = j < (uint32_t)qlen ? __float_as_uint(score) : 0xffffffffu;
+          wsamp[64 * (P * i + pr)] = j < (uint32_t)qlen ? __float_as_uint(score) : 0xffffffffu;
         }
         store_tile((i + 1) & 1);
         __syncthreads();
@@ -340,13 +420,13 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc0[mb][i] = acc1[mb][i] = 0.0f;
       if (qlen > (int32_t)ca.cap) {  // uniform per wave
-        uint32_t samp[2 * kF8SampleTiles];
+        uint32_t samp[P * kF8SampleTiles];
 #pragma unroll
-        for (int i = 0; i < 2 * kF8SampleTiles; ++i)
+        for (int i = 0; i < P * kF8SampleTiles; ++i)
           samp[i] = fused_key(__uint_as_float(wsamp[64 * i]));
         uint32_t nv = 0u;
 #pragma unroll
-        for (int i = 0; i < 2 * kF8SampleTiles; ++i) nv += samp[i] != 0u ? 1u : 0u;
+        for (int i = 0; i < P * kF8SampleTiles; ++i) nv += samp[i] != 0u ? 1u : 0u;
         nv = wave_sum_u32(nv);
         const float e = (float)fa.k * (float)nv / (float)qlen;
         const uint32_t rank = (uint32_t)ceilf(e + 6.0f * sqrtf(e) + 4.0f);
@@ -358,7 +438,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
             const uint32_t c = v | (1u << b);
             uint32_t n_ge = 0u;
 #pragma unroll
-            for (int i = 0; i < 2 * kF8SampleTiles; ++i) n_ge += samp[i] >= c ? 1u : 0u;
+            for (int i = 0; i < P * kF8SampleTiles; ++i) n_ge += samp[i] >= c ? 1u : 0u;
             if (wave_sum_u32(n_ge) >= rank) v = c;
           }
           t_lo = v == fused_key(0.0f) ? -1 : ord(__float_as_uint(fused_value(v)));
@@ -546,14 +626,18 @@ hipError_t launch_fp8_w(const void* q, const void* qs, const void* k, const void
   constexpr int P = FUSE ? 1 : kF8Pairs;
   const int64_t nblk = (n_rows + kF8Waves - 1) / kF8Waves;
   dim3 grid((unsigned)nblk), block(kF8Waves * 64);
+  // vector loads of 4 weights (and, per-token, 4 query descales) per run of heads
+  const uintptr_t wbytes = w_dtype == 0 ? 2 : 4;
+  const bool w_vec = H % 4 == 0 && (uintptr_t)w % (4 * wbytes) == 0 &&
+                     (MX || (uintptr_t)qs % 16 == 0);
   if (w_dtype == 0)
     hipLaunchKernelGGL((indexer_fp8_kernel<MB, uint16_t, MX, P, FUSE, CAND>), grid, block, 0, st,
                        (const uint8_t*)q, qs, (const uint8_t*)k, ks, (const uint16_t*)w, rs, sl,
-                       T_kv, H, row_begin, n_rows, scores, ld, fa, ca);
+                       T_kv, H, row_begin, n_rows, scores, ld, fa, ca, w_vec);
   else
     hipLaunchKernelGGL((indexer_fp8_kernel<MB, float, MX, P, FUSE, CAND>), grid, block, 0, st,
                        (const uint8_t*)q, qs, (const uint8_t*)k, ks, (const float*)w, rs, sl, T_kv,
-                       H, row_begin, n_rows, scores, ld, fa, ca);
+                       H, row_begin, n_rows, scores, ld, fa, ca, w_vec);
   return hipGetLastError();
 }
 
