@@ -85,7 +85,12 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
   constexpr int LOADS = CHUNKS / NT;            // 16-byte chunks per thread and tile
   static_assert(CHUNKS % NT == 0 && kF8Tile <= NT, "whole chunks per thread");
   __shared__ __attribute__((aligned(16))) unsigned char ktile[2 * TILE_B];
-  __shared__ uint32_t kscale[2][kF8Tile];  // per key: fp32 descale bits, or 4 E8M0 bytes
+  // per key: fp32 descale bits, or its 4 E8M0 block scales; stored
+  // transposed so that a lane reads the words of all its keys in a tile with
+  // one or two 16-byte reads: MX word of block nb for key 32*nb + l at
+  // l*2P + nb, per-token descale of key 64*p + l at l*P + p
+  constexpr int NSC = MX ? 2 * P : P;  // scale words per lane and tile
+  __shared__ __attribute__((aligned(16))) uint32_t kscale[2][kF8Tile];
   __shared__ __attribute__((aligned(16))) float s_rows[FUSE ? kF8Waves * kFuseRowStride : 4];
   static_assert(!FUSE || 2 * TILE_B >= kF8Waves * 256 * 4, "select histograms fit the tile ring");
   static_assert(!(FUSE && CAND), "one output mode");
@@ -180,7 +185,9 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
           ((stage_ok >> i) & 1u) ? stage[i] : u32x4{0u, 0u, 0u, 0u};
     }
     const int c = threadIdx.x;
-    if (c < kF8Tile) kscale[buf][c] = stage_sc_ok ? stage_sc : 0u;
+    if (c < kF8Tile)
+      kscale[buf][MX ? (c % 32) * NSC + c / 32 : (c % 64) * NSC + c / 64] =
+          stage_sc_ok ? stage_sc : 0u;
   };
 
   f32x16 acc0[MB], acc1[MB];
@@ -195,6 +202,27 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) p = fmaf(wv[mb][i], relu_f8(acc[mb][i]), p);
     return p;
+  };
+  // The lane's scale words of the tile in buffer buf (read once per tile).
+  uint32_t tsc[NSC];
+  auto read_scales = [&](int buf) {
+    const uint32_t* src = kscale[buf] + (MX ? (lane & 31) : lane) * NSC;
+    if constexpr (NSC % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < NSC / 4; ++i) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + 4 * i);
+        tsc[4 * i] = v.x;
+        tsc[4 * i + 1] = v.y;
+        tsc[4 * i + 2] = v.z;
+        tsc[4 * i + 3] = v.w;
+      }
+    } else if constexpr (NSC == 2) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+      tsc[0] = v.x;
+      tsc[1] = v.y;
+    } else {
+      tsc[0] = src[0];
+    }
   };
   // B operand of k-step s: key 32*nb + l%32, bytes as for A. A block's
   // operands are read from LDS one block ahead of its MFMAs.
@@ -211,7 +239,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
       o.kf[s] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
     }
-    o.sw = MX ? kscale[buf][32 * nb + (lane & 31)] : 0u;
+    o.sw = MX ? tsc[nb] : 0u;
   };
   auto block_mfma = [&](const BOp& o, f32x16* acc) {
     if constexpr (MX) {
@@ -231,7 +259,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
     }
   };
   auto interleave = [&]() {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kF8KS + (MX ? 1 : 0), 0);  // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kF8KS, 0);  // DS reads
 #pragma unroll
     for (int i = 0; i < MB * kF8KS; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);             // MFMA
@@ -397,6 +425,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
         load_tile(i + 1 < kF8SampleTiles ? sample_start(i + 1) : kb + kF8Tile);
         const int sb = i & 1;
         const int32_t s0 = sample_start(i);
+        read_scales(sb);
 #pragma unroll
         for (int pr = 0; pr < P; ++pr) {
           BOp b0, b1;
@@ -405,7 +434,7 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
           block_mfma(b0, acc0);
           block_mfma(b1, acc1);
           float score = halfwave_sums(epilogue(acc0), epilogue(acc1));
-          if constexpr (!MX) score *= __uint_as_float(kscale[sb][64 * pr + lane]);
+          if constexpr (!MX) score *= __uint_as_float(tsc[pr]);
           const uint32_t j = (uint32_t)(s0 + 64 * pr + lane - qstart);
           // (invalid: all-ones bits, whose key is 0)
           wsamp[64 * (P * i + pr)] = j < (uint32_t)qlen ? __float_as_uint(score) : 0xffffffffu;
@@ -460,11 +489,12 @@ __global__ __launch_bounds__(kF8Waves * 64, 1) void indexer_fp8_kernel(
     load_tile(k_next);  // zeroed past the range, so the last one is harmless
 
     BOp cur, nxt;
+    read_scales(buf);
     read_block(buf, 0, cur);
 #pragma unroll
     for (int pr = 0; pr < P; ++pr) {
       const int32_t kp = k0 + 64 * pr;
-      const float kscl = MX ? 0.0f : __uint_as_float(kscale[buf][64 * pr + lane]);
+      const float kscl = MX ? 0.0f : __uint_as_float(tsc[pr]);
       read_block(buf, 2 * pr + 1, nxt);
       // Each group pairs a block's MFMAs with the previous block's epilogue;
       // the fences keep the scheduler from filling the VALU slots with the
