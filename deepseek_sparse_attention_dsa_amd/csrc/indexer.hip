@@ -374,6 +374,11 @@ __global__ __launch_bounds__(kIdxWaves * 64, 1) void indexer_kernel(
     }
   }
 
+  // Every prologue load (the first tile, then the query and the weights) is
+  // complete before the tile loop. Left to the compiler, the waits for the
+  // query fragments land inside the loop, where their counts then also wait
+  // for the next tile's prefetch on every iteration.
+  wait_vmcnt0();
   store_tile(0);
   __syncthreads();
   // CAND: the sample tiles are scored once; the tile loop skips them and
