@@ -73,18 +73,17 @@ __device__ void wave_topk_row(const float* row, int n, int32_t base, uint32_t* h
   // taken. With n <= k every valid key (> 0) is taken.
   //
   // Histogram passes (256 bins in LDS, lane l owning bins 255-4l .. 252-4l)
-  // find the bin holding the remaining-th largest member key; count(key)
-  // gives a member's bin, or -1 for a non-member.
-  auto find_bin = [&](uint32_t remaining, uint32_t* above_out, auto&& bin_of) -> uint32_t {
+  // find the bin holding the remaining-th largest member key; bin_of(key)
+  // gives a member's bin, or -1 for a non-member. visit(f) calls f on every
+  // key the pass looks at (the lane's columns, or a member list).
+  auto find_bin = [&](uint32_t remaining, uint32_t* above_out, auto&& visit,
+                      auto&& bin_of) -> uint32_t {
     *reinterpret_cast<u32x4*>(hist + 4 * lane) = u32x4{0u, 0u, 0u, 0u};
     wave_lds_order();
-#pragma unroll
-    for (int c = 0; c < kFuseChunks; ++c)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int b = bin_of(kreg[c][e]);
-        if (b >= 0) atomicAdd(&hist[b], 1u);
-      }
+    visit([&](uint32_t key) {
+      const int b = bin_of(key);
+      if (b >= 0) atomicAdd(&hist[b], 1u);
+    });
     wave_lds_order();
     const u32x4 h = *reinterpret_cast<const u32x4*>(hist + 252 - 4 * lane);
     const uint32_t local = h.x + h.y + h.z + h.w;
@@ -107,6 +106,12 @@ __device__ void wave_topk_row(const float* row, int n, int32_t base, uint32_t* h
     *above_out = (uint32_t)__builtin_amdgcn_readlane((int)before, src);
     wave_lds_order();  // the next pass clears the bins
     return (uint32_t)__builtin_amdgcn_readlane((int)bin, src);
+  };
+  auto visit_cols = [&](auto&& f) {
+#pragma unroll
+    for (int c = 0; c < kFuseChunks; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f(kreg[c][e]);
   };
   uint32_t theta = 0, need_eq = 0;
   if ((uint32_t)n > k) {
@@ -132,20 +137,41 @@ __device__ void wave_topk_row(const float* row, int n, int32_t base, uint32_t* h
         return b > 255 ? 255 : b;
       };
       uint32_t above;
-      bucket = (int)find_bin(remaining, &above, lin);
+      bucket = (int)find_bin(remaining, &above, visit_cols, lin);
       remaining -= above;
     }
+    // The chosen bucket's members (every valid key without the linear pass)
+    // move, in column order, to a list in the row's own LDS, which is free
+    // once the keys sit in registers: the radix passes then visit the
+    // members only, instead of every column four times.
+    uint32_t* list = reinterpret_cast<uint32_t*>(const_cast<float*>(row));
+    uint32_t n_mem = 0;
+    wave_lds_order();  // every lane has read its keys from the row
+#pragma unroll
+    for (int c = 0; c < kFuseChunks; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = kreg[c][e];
+        bool mem = key != 0u;
+        if (bucket >= 0) {
+          const int b = (int)((fused_value(key) - lo) * scale);
+          mem = mem && (b > 255 ? 255 : b) == bucket;
+        }
+        const uint64_t bm = ballot(mem);
+        if (mem) list[n_mem + popc_below(bm)] = key;
+        n_mem += (uint32_t)__popcll(bm);
+      }
+    wave_lds_order();
+    auto visit_list = [&](auto&& f) {
+      for (uint32_t i = lane; i < n_mem; i += 64) f(list[i]);
+    };
     uint32_t prefix = 0, pmask = 0;
 #pragma unroll 1
     for (int pass = 0; pass < 4; ++pass) {
       const int shift = 24 - 8 * pass;
       uint32_t above;
-      const uint32_t bin = find_bin(remaining, &above, [&](uint32_t key) -> int {
-        if (key == 0u || (key & pmask) != prefix) return -1;
-        if (bucket >= 0) {
-          const int b = (int)((fused_value(key) - lo) * scale);
-          if ((b > 255 ? 255 : b) != bucket) return -1;
-        }
+      const uint32_t bin = find_bin(remaining, &above, visit_list, [&](uint32_t key) -> int {
+        if ((key & pmask) != prefix) return -1;
         return (int)((key >> shift) & 255u);
       });
       remaining -= above;
