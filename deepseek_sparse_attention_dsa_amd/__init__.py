@@ -28,7 +28,7 @@ __all__ = [
     "dsa_topk_workspace_bytes",
     "dsa_indexer_topk_fused", "dsa_indexer_topk_cand_buffer_size", "DSA_FUSED_MAX_COLS",
     "dsa_sparse_attn_fwd", "dsa_sparse_attn_bwd", "dsa_sparse_attn_bwd_workspace_bytes",
-    "dsa_sparse_attn_bwd_kv_tiles", "indexer_topk", "chunk_rows",
+    "dsa_sparse_attn_bwd_kv_tiles", "indexer_topk", "chunk_rows", "sparse_gqa_attention",
 ]
 
 DSA_OK, DSA_ERR_TYPE, DSA_ERR_VALUE, DSA_ERR_RUNTIME = 0, 1, 2, 3
@@ -586,6 +586,68 @@ def chunk_rows(T: int, width: int, cap_bytes: int = SCORE_CHUNK_BYTES) -> int:
     """Rows per score chunk so that [rows, width] fp32 stays under the cap."""
     ld = max(4, (int(width) + 3) // 4 * 4)
     return max(1, min(T, cap_bytes // (4 * ld)))
+
+
+def sparse_gqa_attention(query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                         selected_token_ids: torch.Tensor,
+                         softmax_scale: Optional[float] = None) -> torch.Tensor:
+    """Block-routed sparse GQA over batched tensors -> out bf16 [B, S, H_q, 256].
+
+    The layout of NeMo-QSA `cudnn_sparse_gqa_attention`: query [B, S, H_q,
+    256], key / value [B, S, H_kv, 256] (bf16), selected_token_ids [B, S, W]
+    int32 / int64 ids into the same batch row's sequence (ids outside [0, S)
+    are padding), one route set per token shared by the KV heads. Each KV
+    head and its H_q / H_kv query heads form an independent head group, run
+    as its own dsa_sparse_attn_fwd call per batch row (the pages' (24, 2)
+    case is two (12, 1) groups); strided inputs are copied to contiguous
+    per-group buffers first; everything runs on the current stream.
+    softmax_scale defaults to 1/sqrt(256). Raises
+    TypeError for non-bf16 tensors or non-integer ids, ValueError for shapes,
+    head counts (H_q a multiple of H_kv, at most 16 query heads per group)
+    or the scale.
+    """
+    for name, t in (("query", query), ("key", key), ("value", value)):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be a bfloat16 tensor")
+    if not isinstance(selected_token_ids, torch.Tensor) or selected_token_ids.dtype not in (
+            torch.int32, torch.int64):
+        raise TypeError("selected_token_ids must be an int32 or int64 tensor")
+    if query.dim() != 4 or key.dim() != 4 or query.shape[3] != 256:
+        raise ValueError("expected query [B, S, H_q, 256] and key / value [B, S, H_kv, 256]")
+    B, S, H_q, D = query.shape
+    H_kv = key.shape[2]
+    if tuple(key.shape) != (B, S, H_kv, D) or tuple(value.shape) != tuple(key.shape):
+        raise ValueError(f"shape mismatch: query {tuple(query.shape)}, key {tuple(key.shape)}, "
+                         f"value {tuple(value.shape)}")
+    if H_kv < 1 or H_q % H_kv != 0 or H_q // H_kv > 16:
+        raise ValueError(f"unsupported heads ({H_q}, {H_kv}): H_q must be a multiple of H_kv "
+                         "with at most 16 query heads per KV head")
+    if (selected_token_ids.dim() != 3 or tuple(selected_token_ids.shape[:2]) != (B, S)
+            or selected_token_ids.shape[2] < 1):
+        raise ValueError("selected_token_ids must be [B, S, W] with W >= 1")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(D)
+    if not (math.isfinite(softmax_scale) and softmax_scale > 0):
+        raise ValueError("softmax_scale must be finite and positive")
+    dev = query.device
+    for name, t in (("key", key), ("value", value), ("selected_token_ids", selected_token_ids)):
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    ids = selected_token_ids
+    if ids.dtype == torch.int64:  # narrowing must not turn an invalid id into a valid one
+        ids = torch.where((ids < 0) | (ids >= S), torch.full_like(ids, -1), ids)
+    ids = ids.to(torch.int32)
+    G = H_q // H_kv
+    out = torch.empty((B, S, H_q, D), dtype=torch.bfloat16, device=dev)
+    for b in range(B):
+        idx = ids[b].contiguous()
+        for g in range(H_kv):
+            o, _, _ = dsa_sparse_attn_fwd(
+                query[b, :, G * g:G * (g + 1), :].contiguous(), key[b, :, g, :].contiguous(),
+                idx, softmax_scale=softmax_scale, v=value[b, :, g, :].contiguous(), d_v=D,
+                return_max_logits=False)
+            out[b, :, G * g:G * (g + 1), :] = o
+    return out
 
 
 def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor,

@@ -13,6 +13,7 @@ import subprocess
 import sys
 
 import pytest
+import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dsa.h")
@@ -385,3 +386,30 @@ def test_peaks_library_exports_and_work_counts():
     assert lib.dsa_peak_copy(None, FAKE2, 4096, 4, None) == 1
     assert lib.dsa_peak_read(FAKE, 4096, 0, FAKE2, None) == 1
     assert lib.dsa_peak_read(FAKE, 4096, 4, None, None) == 1
+
+
+def test_batched_gqa_validation():
+    """sparse_gqa_attention rejects bad types, shapes, head layouts and scales
+    before touching a device (CPU tensors: shape checks come first)."""
+    bf = torch.bfloat16
+    q = torch.zeros((2, 8, 24, 256), dtype=bf)
+    k = torch.zeros((2, 8, 2, 256), dtype=bf)
+    ids = torch.zeros((2, 8, 4), dtype=torch.int32)
+    with pytest.raises(TypeError):
+        dsa.sparse_gqa_attention(q.float(), k, k, ids)
+    with pytest.raises(TypeError):
+        dsa.sparse_gqa_attention(q, k, k, ids.float())
+    with pytest.raises(ValueError):  # 24 query heads over 5 KV heads
+        dsa.sparse_gqa_attention(q, torch.zeros((2, 8, 5, 256), dtype=bf),
+                                 torch.zeros((2, 8, 5, 256), dtype=bf), ids)
+    with pytest.raises(ValueError):  # 24 query heads over one KV head: a group of 24
+        dsa.sparse_gqa_attention(q, k[:, :, :1], k[:, :, :1], ids)
+    with pytest.raises(ValueError):  # head dim 128
+        dsa.sparse_gqa_attention(q[..., :128], k[..., :128], k[..., :128], ids)
+    with pytest.raises(ValueError):  # value shape
+        dsa.sparse_gqa_attention(q, k, k[:, :7], ids)
+    with pytest.raises(ValueError):  # ids not [B, S, W]
+        dsa.sparse_gqa_attention(q, k, k, ids[:, :7])
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        with pytest.raises(ValueError):
+            dsa.sparse_gqa_attention(q, k, k, ids, softmax_scale=bad)
