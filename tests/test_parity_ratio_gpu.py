@@ -154,6 +154,39 @@ def test_last_rank_of_eight_way_split(ratio):
         assert np.array_equal(gi[r], ref_idx[0]), r
 
 
+@pytest.mark.parametrize("ratio,scaling", [(1, "mx"), (4, "per_token")])
+def test_last_rank_fp8_candidate_path(ratio, scaling):
+    """The same rank share from FP8 indexer inputs: indexer_topk takes the
+    combined candidate path for these long rows; sampled rows against the
+    oracle's top-K on the standalone FP8 scores."""
+    from workloads import quantize_fp8
+    T, Tq, K = 65536, 8192, 2048
+    Tk = T // ratio
+    say("rank share fp8", Tq, Tk, ratio, scaling)
+    wl = make_split([Tq], [Tk], [T - Tq], ratio, seed=70 + ratio, device=DEV)
+    block = 32 if scaling == "mx" else None
+    q8, qs = quantize_fp8(wl.q_idx, block)
+    k8, ks = quantize_fp8(wl.k_idx, block)
+    mode = dsa.DSA_MXFP8 if scaling == "mx" else dsa.DSA_FP8_PER_TOKEN
+    idx, tl = dsa.indexer_topk(q8, k8, wl.w, wl.cu_seqlens_q, K, cu_seqlens_k=wl.cu_seqlens_k,
+                               ratio=ratio, q_causal_offsets=wl.q_causal_offsets, max_seqlen=Tk,
+                               q_scale=qs, k_scale=ks, fp8_scaling=mode)
+    rs, sl = _meta(wl)
+    torch.cuda.synchronize()
+    st_ref, sl_ref = _ref_meta(wl)
+    assert np.array_equal(i64(tl), np.minimum(sl_ref, K))
+    rng = np.random.default_rng(10 + ratio)
+    rows = sorted(set([0, 1, 2047, 2048, 4095, Tq - 2, Tq - 1] + rng.integers(0, Tq, 5).tolist()))
+    gi = i64(idx)
+    for r in rows:
+        sc = dsa.dsa_indexer_fwd_fp8(q8, qs, k8, ks, wl.w, rs, sl, scaling=mode, row_begin=int(r),
+                                     n_rows=1, width=Tk)
+        torch.cuda.synchronize()
+        ref_idx, _ = O.topk(sc.cpu().numpy().astype(np.float64), sl_ref[r:r + 1], K,
+                            row_starts=st_ref[r:r + 1], n_cols=Tk)
+        assert np.array_equal(gi[r], ref_idx[0]), r
+
+
 @pytest.mark.parametrize("cfg", [6, 7])
 def test_split_config_sampled(cfg):
     """The split-query / compressed-key workloads as the bench runs them:
