@@ -109,6 +109,16 @@ __global__ __launch_bounds__(256) void bwd_sink_kernel(BwdArgs a) {
   if (threadIdx.x == 0) a.d_sink[h] = -s_part[0];
 }
 
+// s_waitcnt vmcnt(N): at most N vector-memory operations of the wave still
+// in flight (they complete in issue order), through the builtin so that the
+// compiler's own wait tracking knows it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ int row_len(const BwdArgs& a, int64_t t) {
   if (!a.topk_length) return a.k_width;
   const int32_t L = a.topk_length[t];
@@ -168,11 +178,12 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
   const int key_row = lane & 31;
   const int crw = lane >> 3;
   auto swz = [](int r, int g) -> int { return 4 * ((r >> 1) & 1) + (r >> 2) + 2 * (g & 1); };
-  auto load_id = [&](int j0, int row) -> int32_t {
+  auto load_id = [&](int j0, int row) -> int32_t {  // L > 0
+    // unconditional (clamped) load, replaced past L afterwards: a predicated
+    // load is waited for at its branch's end
     const int j = j0 + row;
-    int32_t raw = -1;
-    if (j < L) raw = a.indices[t * a.ld_idx + j];
-    return raw;
+    const int32_t raw = a.indices[t * a.ld_idx + (j < L ? j : L - 1)];
+    return j < L ? raw : -1;
   };
   auto valid_id = [&](int32_t raw) -> int32_t {
     return (raw >= 0 && (int64_t)raw < a.T_kv) ? raw : -1;
@@ -237,12 +248,21 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
       for (int ks = 0; ks < KV; ++ks) ga[ks] = u32x4{0u, 0u, 0u, 0u};
     }
   }
+  // log Z and D of the lane's 16 heads: unconditional loads (clamped head)
+  // replaced past H afterwards, so that all are in flight together
   float lz2[16], dd[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int h = h0 + crow(i, half);
-    lz2[i] = h < a.H ? a.logZ[t * a.H + h] * kLog2eB : __builtin_inff();
-    dd[i] = h < a.H ? a.Dsum[t * a.H + h] : 0.0f;
+    const int64_t o = t * a.H + (h < a.H ? h : a.H - 1);
+    lz2[i] = a.logZ[o];
+    dd[i] = a.Dsum[o];
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bool hv = h0 + crow(i, half) < a.H;
+    lz2[i] = hv ? lz2[i] * kLog2eB : __builtin_inff();
+    dd[i] = hv ? dd[i] : 0.0f;
   }
   const float c2 = a.scale * kLog2eB;
   uint16_t* wsP = a.wsP + rc * (int64_t)a.Kw * HP;
@@ -255,10 +275,10 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
     mask_cur = (uint32_t)ballot(id0 >= 0);
     const CopySrc cs0 = prep_copy(smem_base, id0);
     static_for<NCOPY>([&](auto jc) { copy_one(cs0, jc); });
+    wait_vmcnt0();
+    __syncthreads();  // tile 0 has landed in every wave's share
   }
   for (int it = 0; it < n_tiles; ++it) {
-    wait_vmcnt0();
-    __syncthreads();  // tile it has landed in every wave's share; tile it-1 is consumed
     uint32_t mask_next = 0;
     const bool copy_next = it + 1 < n_tiles;  // uniform
     CopySrc cs{};
@@ -267,9 +287,16 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
       mask_next = (uint32_t)ballot(idv >= 0);
       cs = prep_copy(smem_base + ((it + 1) & 1) * STAGE, idv);
     }
-    auto copies_at = [&](auto kc) {  // copies spread over the S k-steps
+    // ids of tile it + 2 (all -1 past the last tile), loaded ahead of this
+    // tile's copies and stores so that the wait at the tile's end covers them
+    int32_t id_after = load_id((it + 2) * kBT, key_row);
+    // copies spread over the first two thirds of the S k-steps, so that
+    // most have landed by the wait after the k-loop
+    auto copies_at = [&](auto kc) {
       constexpr int ks = decltype(kc)::value;
-      constexpr int j0 = (ks * NCOPY + KS - 1) / KS, j1 = ((ks + 1) * NCOPY + KS - 1) / KS;
+      constexpr int KF = KS * 2 / 3;
+      constexpr int j0 = ks < KF ? (ks * NCOPY + KF - 1) / KF : NCOPY;
+      constexpr int j1 = ks < KF ? ((ks + 1) * NCOPY + KF - 1) / KF : NCOPY;
       if (copy_next)
         static_for<j1 - j0>([&](auto dj) {
           copy_one(cs, std::integral_constant<int, j0 + decltype(dj)::value>{});
@@ -307,7 +334,9 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
     } else {
       static_for<KS>([&](auto kc) { copies_at(kc); });
     }
-    if (copy_next) id_next = (it + 2 < n_tiles) ? load_id((it + 2) * kBT, key_row) : -1;
+    // the ids are taken here, ahead of the stores: a first use after them
+    // would wait for the stores as well
+    asm volatile("" : "+v"(id_after));
     if (comp) {
       const int slot = it * kBT + r32;
       const bool valid = (mask_cur >> r32) & 1u;
@@ -348,7 +377,17 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
         *reinterpret_cast<u32x4*>(wsD + off) = dq4;
       }
     }
+    id_next = id_after;
     mask_cur = mask_next;
+    if (copy_next) {  // uniform
+      // Tile it + 1 has landed in this wave's share. This tile's four P / dS
+      // stores were issued after its copies and the ids' load, so they may
+      // stay in flight: waiting for them too cost every tile a store round
+      // trip.
+      if (comp) wait_vmcnt_le<4>();  // uniform
+      else wait_vmcnt0();
+      __syncthreads();  // every wave's share has landed; tile it is consumed
+    }
   }
 }
 
@@ -989,13 +1028,6 @@ __global__ __launch_bounds__(256) void bwd_merge_kernel(BwdArgs a) {
       D[(int64_t)rep * hp + h] = (uint16_t)f32_to_bf16_bits(sd);
     }
   }
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
-  asm volatile("" ::: "memory");
 }
 
 // One (part of 64 query rows, tile of 128 KV rows) per workgroup, 4 waves.
