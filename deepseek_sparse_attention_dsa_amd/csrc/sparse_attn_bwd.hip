@@ -19,7 +19,9 @@
 //  * bwd_pds_kernel: gathers 32 selected KV rows per tile into an LDS ring
 //    with asynchronous copies and computes S = q . K^T and dP = dout . V^T
 //    from the same fragment reads; stores P and dS = scale * P * (dP - D)
-//    (scale folded in) as bf16, slot-major ([row][slot][head]).
+//    (scale folded in) as bf16, in 16-head chunks ([row][head / 16][slot]
+//    [head % 16]): with ascending ids, the slots of a run of KV rows are
+//    consecutive, and so are their chunks.
 //  * bwd_dq_ring_kernel: dq = dS . K with both operands read transposed from
 //    LDS (ds_read_b64_tr_b16), two waves per 32-head block splitting the
 //    dims; K gathered into the same copy ring as bwd_pds_kernel.
@@ -48,6 +50,11 @@ namespace {
 
 constexpr int kBT = 32;  // slots per tile
 constexpr float kLog2eB = 1.442695040888963387f;
+
+// Element offset of (slot, head h) in one row's P or dS: [h / 16][Kw][h % 16].
+__device__ __forceinline__ int64_t pds_off(int slot, int h, int Kw) {
+  return ((int64_t)(h >> 4) * Kw + slot) * 16 + (h & 15);
+}
 
 // C-layout row of value i of a 32x32 MFMA result for lane half `half`.
 __device__ __forceinline__ int crow(int i, int half) { return 8 * (i >> 2) + 4 * half + (i & 3); }
@@ -135,7 +142,7 @@ __device__ __forceinline__ int row_len(const BwdArgs& a, int64_t t) {
 // Each fragment read from LDS feeds both products (V is the first 512 dims
 // of K). C lane -> slot column l%32, head rows crow(i). Then
 //   P = exp2(S scale log2e - log Z log2e),  dS = scale P (dP - D)
-// both written as bf16 to the slot-major workspaces ([row][slot][head]);
+// both written as bf16 to the workspaces in 16-head chunks (pds_off);
 // invalid slots and heads past H write zeros. The S chain uses the compiler's
 // MFMA (its accumulator in AGPRs, q where the allocator puts it); the dP chain
 // is written inline with its accumulator in VGPRs, so that the two
@@ -372,7 +379,7 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
           dq4[w] = sd[0];
           dq4[2 + w] = sd[1];
         }
-        const int64_t off = (int64_t)slot * HP + h0 + 16 * pi + 8 * half;  // 8 consecutive heads
+        const int64_t off = pds_off(slot, h0 + 16 * pi + 8 * half, a.Kw);  // 8 consecutive heads
         *reinterpret_cast<u32x4*>(wsP + off) = po;
         *reinterpret_cast<u32x4*>(wsD + off) = dq4;
       }
@@ -397,8 +404,9 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
 // (slots x dims), both read transposed (ds_read_b64_tr_b16). The K tiles are
 // gathered into the same swizzled 2-stage ring as bwd_pds_kernel (copies of
 // tile i+1 issued by the first min(2*NW, 4) waves between the MFMAs of tile
-// i); each tile's dS rows ([slot][head], contiguous in the workspace) are
-// loaded one tile ahead into registers and stored to a padded LDS tile.
+// i); each tile's dS (32 slots x 16 heads contiguous per 16-head chunk in
+// the workspace) is loaded one tile ahead into registers and stored to a
+// padded [slot][head] LDS tile.
 // Lane half h of an MFMA operand covers slots 16*st + 4h + 0..3 and
 // 16*st + 8 + 4h + 0..3 of k-step st, in both operands.
 template <int DQK, int NW, bool BUF>
@@ -442,7 +450,7 @@ __global__ __launch_bounds__(NW * 128, NW <= 2 ? 2 : 1) void bwd_dq_ring_kernel(
   const int32_t id_second = n_tiles > 1 ? load_id(kBT, key_row) : -1;
   // this thread's 16-byte chunk of a tile's dS rows
   const int dslot = threadIdx.x / (HP / 8), dch = threadIdx.x % (HP / 8);
-  auto load_ds = [&](int tl) -> u32x4 { return load16(wsD + (int64_t)(tl * kBT + dslot) * HP + 8 * dch); };
+  auto load_ds = [&](int tl) -> u32x4 { return load16(wsD + pds_off(tl * kBT + dslot, 8 * dch, a.Kw)); };
   u32x4 ds_next = n_tiles > 0 ? load_ds(0) : u32x4{0u, 0u, 0u, 0u};
 
   const uint32_t smem_base = lds_addr(smem);
@@ -562,7 +570,7 @@ __global__ __launch_bounds__(NW * 128, NW <= 2 ? 2 : 1) void bwd_dq_ring_kernel(
 // ------------------------------------------------------------------ dkv --
 // One workgroup per (query row, 64-head chunk); NWD waves each own BPW
 // 32-dim blocks. C[s][d] on 32x32x16 with k = heads: A = dS^T / P^T
-// (slot rows, heads contiguous in the workspace), B = q / dout of the chunk's
+// (16 heads of 32 slots contiguous in the workspace), B = q / dout of the chunk's
 // heads read transposed from LDS ([head][dim]). (The transposed product, with
 // runs of 4 dims per lane stored 8 bytes at a time, measured slower: its
 // stores coalesce less than these 2-byte stores of 32 consecutive dims.)
@@ -611,11 +619,11 @@ __global__ __launch_bounds__(NWD * 64) void bwd_dkv_kernel(BwdArgs a) {
   const int ntiles = (L + kBT - 1) / kBT;
   u32x4 adA[NK], apA[NK], adB[NK], apB[NK];
   auto load_a = [&](int tl, u32x4* ad, u32x4* ap) {
-    const int64_t srow = (int64_t)(tl * kBT + r32) * HP + hc0 + 8 * half;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      ad[kk] = load16(wsD + srow + 16 * kk);
-      ap[kk] = load16(wsP + srow + 16 * kk);
+      const int64_t o = pds_off(tl * kBT + r32, hc0 + 16 * kk + 8 * half, a.Kw);
+      ad[kk] = load16(wsD + o);
+      ap[kk] = load16(wsP + o);
     }
   };
   // C: lane -> dim column, slot rows crow(i); the row of slot s of this head
@@ -1021,11 +1029,11 @@ __global__ __launch_bounds__(256) void bwd_merge_kernel(BwdArgs a) {
       float sp = 0.0f, sd = 0.0f;
       for (int m = i; m < n2 && s_k[m] != kNone && (s_k[m] >> 13) == id; ++m) {
         const int s = (int)(s_k[m] & 8191u);
-        sp += bf16_bits_to_f32(P[(int64_t)s * hp + h]);
-        sd += bf16_bits_to_f32(D[(int64_t)s * hp + h]);
+        sp += bf16_bits_to_f32(P[pds_off(s, h, a.Kw)]);
+        sd += bf16_bits_to_f32(D[pds_off(s, h, a.Kw)]);
       }
-      P[(int64_t)rep * hp + h] = (uint16_t)f32_to_bf16_bits(sp);
-      D[(int64_t)rep * hp + h] = (uint16_t)f32_to_bf16_bits(sd);
+      P[pds_off(rep, h, a.Kw)] = (uint16_t)f32_to_bf16_bits(sp);
+      D[pds_off(rep, h, a.Kw)] = (uint16_t)f32_to_bf16_bits(sd);
     }
   }
 }
@@ -1045,8 +1053,8 @@ __global__ __launch_bounds__(256) void bwd_merge_kernel(BwdArgs a) {
 //   B operands;
 //   dS and P of the slot that selects each of the 128 KV rows ([k half][j]
 //   16-byte runs, zeros where none) -- A operands, one ds_read_b128 each.
-// Three stages: the copies of step s + 2 are issued after the barrier of
-// step s and overlap its reads and MFMAs. Parts are spread so that the
+// Three stages; the copies of step s + 3 and the LDS reads of the operands
+// overlap the MFMAs (see the step loop). Parts are spread so that the
 // tiles of one part run on one XCD (block b on XCD b % 8) and share its L2
 // for q and dout.
 template <int DQK, int HP>
@@ -1060,7 +1068,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_tile_kernel(BwdArgs a) {
   constexpr int NST = 3;
   constexpr int R = kBwdTileRows, BJ = kBwdTileKV;
   constexpr int NX = DQK == 576 ? 2 : 0;      // blocks of dims 512..575 per wave
-  constexpr int NA = 8 + (NX > 0 ? 1 : 0), NB = 8 + NX;  // operand registers (u32x4) per step
   constexpr uint32_t OOB = 0x80000000u;       // past every descriptor: reads zeros
   static_assert(16 * QPADB % 1024 == 0 && QIN <= 19 && 16 * GPADB == GREG, "stage layout");
   static_assert((QPADB / 4) % 64 == 16 || (QPADB / 4) % 64 == 48, "q row stride");
@@ -1105,6 +1112,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_tile_kernel(BwdArgs a) {
   }
   __syncthreads();
   const int nrows = s_nrows;
+  const int rows_v = lane < nrows ? s_rows[lane] : 0;  // lane i: i-th selecting row
   if (tid == 0) a.part_flag[(int64_t)p * nj + J] = nrows > 0 ? 1 : 0;
   if (nrows == 0) return;  // uniform
 
@@ -1138,7 +1146,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_tile_kernel(BwdArgs a) {
     Copies c;
     const bool live = s < S;
     const int ri = live ? s / HS : 0, hg = s % HS;
-    const int rl = __builtin_amdgcn_readfirstlane(s_rows[ri]);
+    const int rl = __builtin_amdgcn_readlane(rows_v, ri);
     const int slot = s_map[rl * BJ + 32 * wave + r32];
     const int64_t rc = rbeg + rl, t = a.row0 + rc;
     const int h0 = 16 * hg, hl = live && a.H - h0 > 0 ? a.H - h0 : 0;  // heads left from h0
@@ -1147,7 +1155,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_tile_kernel(BwdArgs a) {
     c.rD = buffer_rsrc_words(a.wsD + rc * slab, live ? (uint32_t)(slab * 2) : 0u);
     c.rP = buffer_rsrc_words(a.wsP + rc * slab, live ? (uint32_t)(slab * 2) : 0u);
     c.base = lds0 + (uint32_t)((s % NST) * STAGE);
-    c.va = slot >= 0 ? (uint32_t)(slot * HP + h0 + 8 * half) * 2u : OOB;
+    c.va = slot >= 0 ? (uint32_t)pds_off(slot, h0 + 8 * half, a.Kw) * 2u : OOB;
     return c;
   };
   // copy i of this wave: 0..8 the q / dout copies, 9 dS, 10 P
@@ -1178,73 +1186,99 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_tile_kernel(BwdArgs a) {
 #pragma unroll
   for (int e = 0; e < (NX > 0 ? NX : 1); ++e) accx[e] = f32x16{};
 
-  // operands of step s: A = dS (0..3), P (4..7), dS of m-block w (8);
-  // B = q blocks (0..3), dout blocks (4..7), q dims 512.. (8, 9)
-  auto load_ops = [&](int s, u32x4* A, u32x4* B) {
+  // Each step is two halves: the dS q products (18 MFMAs for D_qk = 576)
+  // on operand set X, then the P dout products (16) on set Y. Each set is
+  // read from LDS while the other half multiplies: Y of step s during its
+  // first half, X of step s + 1 during its second half, after the barrier in
+  // the middle of step s (own copies of step s + 1 waited for; every wave's
+  // reads of step s ended). The 11 copies of step s + 3 go into the stage of
+  // step s between the MFMAs from that barrier to the next one: 6 in the
+  // second half of step s, 5 in the first half of step s + 1.
+  // X: dS of m-blocks 0..3 (0..3), dS of m-block w (4), q blocks (5..8),
+  // q dims 512.. (9, 10); Y: P of m-blocks 0..3 (0..3), dout blocks (4..7).
+  constexpr int NXR = 9 + NX, NYR = 8;
+  auto load_x = [&](int s, u32x4* X) {
     const unsigned char* st = smem + (s % NST) * STAGE;
     const uint16_t* sq = reinterpret_cast<const uint16_t*>(st);
-    const uint16_t* sg = reinterpret_cast<const uint16_t*>(st + QREG);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      A[m] = *reinterpret_cast<const u32x4*>(st + AOFF + 1024 * m + 16 * lane);
-      A[4 + m] = *reinterpret_cast<const u32x4*>(st + AOFF + 4096 + 1024 * m + 16 * lane);
-    }
+    for (int m = 0; m < 4; ++m)
+      X[m] = *reinterpret_cast<const u32x4*>(st + AOFF + 1024 * m + 16 * lane);
     if constexpr (NX > 0)
-      A[8] = *reinterpret_cast<const u32x4*>(st + AOFF + 1024 * wave + 16 * lane);
+      X[4] = *reinterpret_cast<const u32x4*>(st + AOFF + 1024 * wave + 16 * lane);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const int col = 32 * (4 * wave + b);
-      const uint16_t* qb = sq + rsel * RQ + col + csel;
+      const uint16_t* qb = sq + rsel * RQ + 32 * (4 * wave + b) + csel;
       const u32x2 q0 = lds_read_tr16(qb), q1 = lds_read_tr16(qb + 4 * RQ);
-      B[b] = u32x4{q0.x, q0.y, q1.x, q1.y};
-      const uint16_t* gb = sg + rsel * RG + col + csel;
-      const u32x2 g0 = lds_read_tr16(gb), g1 = lds_read_tr16(gb + 4 * RG);
-      B[4 + b] = u32x4{g0.x, g0.y, g1.x, g1.y};
+      X[5 + b] = u32x4{q0.x, q0.y, q1.x, q1.y};
     }
 #pragma unroll
     for (int e = 0; e < NX; ++e) {
       const uint16_t* qb = sq + rsel * RQ + 512 + 32 * e + csel;
       const u32x2 q0 = lds_read_tr16(qb), q1 = lds_read_tr16(qb + 4 * RQ);
-      B[8 + e] = u32x4{q0.x, q0.y, q1.x, q1.y};
+      X[9 + e] = u32x4{q0.x, q0.y, q1.x, q1.y};
     }
   };
-  // the step's MFMAs (dS q blocks, the extra q dims, P dout blocks) with the
-  // 11 copies of step s + 2 issued between them, one after every third
-  auto mfmas = [&](const u32x4* A, const u32x4* B, const Copies& c) {
-    constexpr int NM = 32 + NX;
-    static_for<NM>([&](auto jc) {
+  auto load_y = [&](int s, u32x4* Y) {
+    const unsigned char* st = smem + (s % NST) * STAGE;
+    const uint16_t* sg = reinterpret_cast<const uint16_t*>(st + QREG);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      Y[m] = *reinterpret_cast<const u32x4*>(st + AOFF + 4096 + 1024 * m + 16 * lane);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint16_t* gb = sg + rsel * RG + 32 * (4 * wave + b) + csel;
+      const u32x2 g0 = lds_read_tr16(gb), g1 = lds_read_tr16(gb + 4 * RG);
+      Y[4 + b] = u32x4{g0.x, g0.y, g1.x, g1.y};
+    }
+  };
+  // first half: copies 6..10 of c after MFMAs 1, 4, 7, 10, 13
+  auto mfma_x = [&](const u32x4* X, const Copies& c) {
+    static_for<16 + NX>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
       if constexpr (j < 16) {
         constexpr int b = j / 4, m = j % 4;
-        acc[m][b] = mfma32x32x16(A[m], B[b], acc[m][b]);
-      } else if constexpr (j < 16 + NX) {
-        constexpr int e = j - 16;
-        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(accx[e]) : "v"(A[8]), "v"(B[8 + e]));
+        acc[m][b] = mfma32x32x16(X[m], X[5 + b], acc[m][b]);
       } else {
-        constexpr int b = (j - 16 - NX) / 4, m = (j - 16 - NX) % 4;
-        acc[m][b] = mfma32x32x16(A[4 + m], B[4 + b], acc[m][b]);
+        constexpr int e = j - 16;
+        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(accx[e]) : "v"(X[4]), "v"(X[9 + e]));
       }
-      if constexpr (j % 3 == 1 && j / 3 < 11) copy(c, std::integral_constant<int, j / 3>{});
+      if constexpr (j % 3 == 1 && j / 3 < 5) copy(c, std::integral_constant<int, 6 + j / 3>{});
     });
   };
-  // step s: once its copies are in LDS (own copies waited for, then the
-  // barrier, which also ends every wave's reads of step s - 1), read its
-  // operands and multiply, issuing the copies of step s + 2 into the stage of
-  // step s - 1 between the MFMAs
-  static_assert(32 + NX >= 3 * 10 + 2, "every copy finds its MFMA");
-  u32x4 A[NA], B[NB];
+  // second half: copies 0..5 of c after MFMAs 0, 3, 6, 9, 12, 15
+  auto mfma_y = [&](const u32x4* Y, const Copies& c) {
+    static_for<16>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      constexpr int b = j / 4, m = j % 4;
+      acc[m][b] = mfma32x32x16(Y[m], Y[4 + b], acc[m][b]);
+      if constexpr (j % 3 == 0) copy(c, std::integral_constant<int, j / 3>{});
+    });
+  };
+  u32x4 X[NXR], Y[NYR];
+  Copies cw = prep(2);
   {
     const Copies c0 = prep(0), c1 = prep(1);
     static_for<11>([&](auto ic) { copy(c0, ic); });
     static_for<11>([&](auto ic) { copy(c1, ic); });
+    static_for<6>([&](auto ic) { copy(cw, ic); });
   }
-  Copies cn = prep(2);
+  wait_vmcnt_le<17>();  // this wave's copies of step 0 are in LDS
+  __syncthreads();
+  load_x(0, X);
   for (int s = 0; s < S; ++s) {
-    wait_vmcnt_le<11>();  // this wave's copies of step s are in LDS
+    // (scheduling barriers: the MFMAs of a half stay on their side of the
+    // workgroup barrier, with the other set's reads issued ahead of them)
+    const Copies cn = prep(s + 3);
+    load_y(s, Y);
+    mfma_x(X, cw);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt_le<11>();  // this wave's copies of step s + 1 are in LDS
     __syncthreads();
-    load_ops(s, A, B);
-    mfmas(A, B, cn);
-    cn = prep(s + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    cw = cn;
+    load_x(s + 1, X);  // past the last step: unused values
+    mfma_y(Y, cw);
+    __builtin_amdgcn_sched_barrier(0);
   }
   wait_vmcnt0();  // the copies issued past the last step
 
