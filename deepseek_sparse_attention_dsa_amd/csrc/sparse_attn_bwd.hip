@@ -145,10 +145,10 @@ __device__ __forceinline__ int row_len(const BwdArgs& a, int64_t t) {
 // both written as bf16 to the workspaces in 16-head chunks (pds_off);
 // invalid slots and heads past H write zeros. The S chain uses the compiler's
 // MFMA (its accumulator in AGPRs, q where the allocator puts it); the dP chain
-// is written inline with its accumulator in VGPRs, so that the two
-// accumulators and both operand sets fit the register files together, and
-// the wait states the compiler would insert before VALU reads of dP are
-// given after the chain.
+// is written inline with its accumulator in AGPRs, and the wait states the
+// compiler would insert before reads of dP are given after the chain. Two
+// sets of both accumulators alternate between tiles: P and dS of tile i - 1
+// are computed and stored between the MFMAs of tile i.
 //
 // The tiles are gathered as in the forward kernel: asynchronous LDS copies
 // into a 2-stage ring, the copies of tile i+1 interleaved with the MFMAs of
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
   const int64_t t = a.row0 + rc;
   const int L = row_len(a, t);
   const int n_tiles = (L + kBT - 1) / kBT;
-  const bool comp = wave < NW;  // uniform
+  const bool comp = NW == NWC || wave < NW;  // uniform; every wave when NW == NWC
   const int h0 = 32 * wave;
   const int hA = h0 + r32;
 
@@ -191,6 +191,10 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
     const int j = j0 + row;
     const int32_t raw = a.indices[t * a.ld_idx + (j < L ? j : L - 1)];
     return j < L ? raw : -1;
+  };
+  auto load_id_raw = [&](int j0, int row) -> int32_t {  // L > 0; checked against L at use
+    const int j = j0 + row;
+    return a.indices[t * a.ld_idx + (j < L ? j : L - 1)];
   };
   auto valid_id = [&](int32_t raw) -> int32_t {
     return (raw >= 0 && (int64_t)raw < a.T_kv) ? raw : -1;
@@ -285,18 +289,71 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
     wait_vmcnt0();
     __syncthreads();  // tile 0 has landed in every wave's share
   }
-  for (int it = 0; it < n_tiles; ++it) {
+  // The epilogue of tile it - 1 (P and dS from its S and dP) runs between
+  // the MFMAs of tile it: two accumulator sets alternate, so the VALU work
+  // and the stores overlap the matrix work instead of following it.
+  auto epi_part = [&](uint32_t mask, const f32x16& sa, const f32x16& da, uint32_t (&pw)[4][2],
+                      uint32_t (&dw)[4][2], auto gc) {
+    constexpr int g = decltype(gc)::value;
+    const bool valid = (mask >> r32) & 1u;
+    float pv[4], dv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * g + e;
+      const float p = valid ? fast_exp2(fmaf(sa[i], c2, -lz2[i])) : 0.0f;
+      pv[e] = p;
+      dv[e] = a.scale * p * (da[i] - dd[i]);
+    }
+    pw[g][0] = pack_bf16x2(pv[0], pv[1]);
+    pw[g][1] = pack_bf16x2(pv[2], pv[3]);
+    dw[g][0] = pack_bf16x2(dv[0], dv[1]);
+    dw[g][1] = pack_bf16x2(dv[2], dv[3]);
+  };
+  // lane (slot, half) holds heads 8g + 4*half + 0..3 of its slot for
+  // g = 0..3 (the C layout); one v_permlane32_swap per word and pair of
+  // groups (2pi, 2pi + 1) gives half 0 heads 16pi + 0..7 and half 1 heads
+  // 16pi + 8..15, stored as 16-byte runs through buffer descriptors of the
+  // row's P and dS. The stores of the first tile step (no previous tile) take
+  // an offset past the range and are dropped, so every step issues the same
+  // four stores.
+  const __amdgpu_buffer_rsrc_t rP = raw_buffer(wsP, (uint32_t)(a.Kw * HP * 2));
+  const __amdgpu_buffer_rsrc_t rD = raw_buffer(wsD, (uint32_t)(a.Kw * HP * 2));
+  auto epi_store = [&](int te, bool live, const uint32_t (&pw)[4][2], const uint32_t (&dw)[4][2],
+                       auto pc) {
+    constexpr int pi = decltype(pc)::value;
+    u32x4 po, dq4;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const auto sp = __builtin_amdgcn_permlane32_swap(pw[2 * pi][w], pw[2 * pi + 1][w], false, false);
+      const auto sd = __builtin_amdgcn_permlane32_swap(dw[2 * pi][w], dw[2 * pi + 1][w], false, false);
+      po[w] = sp[0];
+      po[2 + w] = sp[1];
+      dq4[w] = sd[0];
+      dq4[2 + w] = sd[1];
+    }
+    // 8 consecutive heads
+    const uint32_t off = live ? (uint32_t)pds_off(te * kBT + r32, h0 + 16 * pi + 8 * half, a.Kw) * 2u
+                              : 0x80000000u;
+    __builtin_amdgcn_raw_buffer_store_b128(po, rP, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(dq4, rD, (int)off, 0, 0);
+  };
+  uint32_t mask_prev = 0;
+  auto tile_step = [&](int it, f32x16& sacc, f32x16& dacc, const f32x16& sprev, const f32x16& dprev) {
     uint32_t mask_next = 0;
     const bool copy_next = it + 1 < n_tiles;  // uniform
+    const bool has_prev = it > 0;            // uniform
     CopySrc cs{};
     if (copy_next) {
-      const int32_t idv = valid_id(id_next);
+      // (the ids' row check happens here, at their first use, after the
+      // previous tile's barrier wait has covered their load)
+      const int32_t idv = (it + 1) * kBT + key_row < L ? valid_id(id_next) : -1;
       mask_next = (uint32_t)ballot(idv >= 0);
       cs = prep_copy(smem_base + ((it + 1) & 1) * STAGE, idv);
     }
-    // ids of tile it + 2 (all -1 past the last tile), loaded ahead of this
-    // tile's copies and stores so that the wait at the tile's end covers them
-    int32_t id_after = load_id((it + 2) * kBT, key_row);
+    // ids of tile it + 2 (clamped to the row, checked at their use), loaded
+    // ahead of this tile's copies and stores so that the wait at the tile's
+    // end covers them
+    const int32_t id_after = load_id_raw((it + 2) * kBT, key_row);
     // copies spread over the first two thirds of the S k-steps, so that
     // most have landed by the wait after the k-loop
     auto copies_at = [&](auto kc) {
@@ -310,7 +367,6 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
         });
     };
     const unsigned char* tile = smem + (it & 1) * STAGE;
-    f32x16 sacc, dacc;
     if (comp) {
       // fragment of k-step ks: row r32 (group kg, row kr), chunk 2*(ks%4) + half of
       // segment ks/4 at slot 8*kr + (chunk ^ f)
@@ -326,75 +382,55 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
       u32x4 bf[PF];
 #pragma unroll
       for (int i = 0; i < PF; ++i) bf[i] = kread(i);
+      uint32_t pw[4][2], dw[4][2];
       static_for<KS>([&](auto kc) {
         constexpr int ks = decltype(kc)::value;
         const u32x4 cur = bf[ks % PF];
         if constexpr (ks + PF < KS) bf[ks % PF] = kread(ks + PF);
         sacc = mfma32x32x16(qa[ks], cur, ks == 0 ? f32x16{} : sacc);
         if constexpr (ks == 0)
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(dacc) : "v"(ga[0]), "v"(cur));
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=a"(dacc) : "v"(ga[0]), "v"(cur));
         else if constexpr (ks < KV)
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(dacc) : "v"(ga[ks]), "v"(cur));
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(dacc) : "v"(ga[ks]), "v"(cur));
         copies_at(kc);
+        // the previous tile's P / dS: values at k-steps 2, 6, 10, 14, the
+        // stores at 26 and 30, after this tile's last copy
+        if constexpr (ks % 4 == 2 && ks / 4 < 4) {
+          constexpr int g = ks / 4;
+          epi_part(mask_prev, sprev, dprev, pw, dw, std::integral_constant<int, g>{});
+          // a use here, so that the values are not sunk towards the stores
+          asm volatile("" ::"v"(pw[g][0]), "v"(pw[g][1]), "v"(dw[g][0]), "v"(dw[g][1]));
+        }
+        if constexpr (ks == 26 || ks == 30)
+          epi_store(it - 1, has_prev, pw, dw, std::integral_constant<int, (ks - 26) / 4>{});
       });
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(dacc));
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(dacc));
     } else {
       static_for<KS>([&](auto kc) { copies_at(kc); });
     }
-    // the ids are taken here, ahead of the stores: a first use after them
-    // would wait for the stores as well
-    asm volatile("" : "+v"(id_after));
-    if (comp) {
-      const int slot = it * kBT + r32;
-      const bool valid = (mask_cur >> r32) & 1u;
-      // lane (slot, half) holds heads 8g + 4*half + 0..3 of its slot for
-      // g = 0..3 (the C layout); one v_permlane32_swap per word and pair of
-      // groups (2pi, 2pi + 1) gives half 0 heads 16pi + 0..7 and half 1
-      // heads 16pi + 8..15, stored as 16-byte runs
-      uint32_t pw[4][2], dw[4][2];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        float pv[4], dv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * g + e;
-          const float p = valid ? fast_exp2(fmaf(sacc[i], c2, -lz2[i])) : 0.0f;
-          pv[e] = p;
-          dv[e] = a.scale * p * (dacc[i] - dd[i]);
-        }
-        pw[g][0] = pack_bf16x2(pv[0], pv[1]);
-        pw[g][1] = pack_bf16x2(pv[2], pv[3]);
-        dw[g][0] = pack_bf16x2(dv[0], dv[1]);
-        dw[g][1] = pack_bf16x2(dv[2], dv[3]);
-      }
-#pragma unroll
-      for (int pi = 0; pi < 2; ++pi) {
-        u32x4 po, dq4;
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const auto sp = __builtin_amdgcn_permlane32_swap(pw[2 * pi][w], pw[2 * pi + 1][w], false, false);
-          const auto sd = __builtin_amdgcn_permlane32_swap(dw[2 * pi][w], dw[2 * pi + 1][w], false, false);
-          po[w] = sp[0];
-          po[2 + w] = sp[1];
-          dq4[w] = sd[0];
-          dq4[2 + w] = sd[1];
-        }
-        const int64_t off = pds_off(slot, h0 + 16 * pi + 8 * half, a.Kw);  // 8 consecutive heads
-        *reinterpret_cast<u32x4*>(wsP + off) = po;
-        *reinterpret_cast<u32x4*>(wsD + off) = dq4;
-      }
-    }
     id_next = id_after;
+    mask_prev = mask_cur;
     mask_cur = mask_next;
     if (copy_next) {  // uniform
-      // Tile it + 1 has landed in this wave's share. This tile's four P / dS
-      // stores were issued after its copies and the ids' load, so they may
-      // stay in flight: waiting for them too cost every tile a store round
-      // trip.
+      // Tile it + 1 has landed in this wave's share; the four P / dS stores,
+      // issued after its copies, may stay in flight.
       if (comp) wait_vmcnt_le<4>();  // uniform
       else wait_vmcnt0();
       __syncthreads();  // every wave's share has landed; tile it is consumed
     }
+  };
+  f32x16 s0{}, d0{}, s1{}, d1{};
+  for (int it = 0; it < n_tiles; it += 2) {
+    tile_step(it, s0, d0, s1, d1);
+    if (it + 1 < n_tiles) tile_step(it + 1, s1, d1, s0, d0);  // uniform
+  }
+  if (comp && n_tiles > 0) {  // the last tile's epilogue
+    const int te = n_tiles - 1;
+    const f32x16& sl = (te & 1) ? s1 : s0;
+    const f32x16& dl = (te & 1) ? d1 : d0;
+    uint32_t pw[4][2], dw[4][2];
+    static_for<4>([&](auto gc) { epi_part(mask_prev, sl, dl, pw, dw, gc); });
+    static_for<2>([&](auto pc) { epi_store(te, true, pw, dw, pc); });
   }
 }
 
