@@ -605,11 +605,14 @@ __global__ __launch_bounds__(NW * 128, NW <= 2 ? 2 : 1) void bwd_dq_ring_kernel(
 
 // ------------------------------------------------------------------ dkv --
 // One workgroup per (query row, 64-head chunk); NWD waves each own BPW
-// 32-dim blocks. C[s][d] on 32x32x16 with k = heads: A = dS^T / P^T
-// (16 heads of 32 slots contiguous in the workspace), B = q / dout of the chunk's
-// heads read transposed from LDS ([head][dim]). (The transposed product, with
-// runs of 4 dims per lane stored 8 bytes at a time, measured slower: its
-// stores coalesce less than these 2-byte stores of 32 consecutive dims.)
+// 32-dim blocks. C^T[d][s] on 32x32x16 with k = heads: A = q^T / dout^T of
+// the chunk's heads (dims x heads, read transposed once per row from the
+// staged [head][dim] rows into registers), B = dS^T / P^T (16 heads of 32
+// slots contiguous in the workspace). Lane (slot l%32, half) then holds runs
+// of 4 consecutive dims of its slot, written as 8-byte words into an LDS
+// tile of the 32 slot rows; after a barrier the waves store that tile as
+// whole rows, 16 bytes per lane on consecutive addresses. (Stored straight
+// from the MFMA layout, 2 bytes per lane, the row writes took twice as long.)
 template <int DQK, int NW, int NWD>
 __global__ __launch_bounds__(NWD * 64) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int HP = NW * 32;
@@ -618,10 +621,17 @@ __global__ __launch_bounds__(NWD * 64) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int NBLK = DQK / 32;
   constexpr int BPW = NBLK / NWD;
   static_assert(NBLK % NWD == 0, "dim blocks split evenly over waves");
-  __shared__ __attribute__((aligned(16))) uint16_t sq[HC * RQ];
-  __shared__ __attribute__((aligned(16))) uint16_t sg[HC * RG];
+  // C tile rows: DQK bf16 + 16 bytes, so that the 8-byte writes of 16 lanes
+  // (16 rows, one column) fall on distinct banks; two tiles alternate.
+  constexpr int RCB = DQK * 2 + 16;
+  constexpr int STAGE_B = HC * (RQ + RG) * 2, CT_B = 2 * kBT * RCB;
+  static_assert((RCB / 4) % 64 == 36 || (RCB / 4) % 64 == 4, "C tile row stride");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[STAGE_B > CT_B ? STAGE_B : CT_B];
+  uint16_t* const sq = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* const sg = sq + HC * RQ;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5, r32 = lane & 31;
+  const int lane = threadIdx.x & 63, half = lane >> 5, r32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // scalar
   const int64_t rc = blockIdx.x / (HP / HC);
   const int hc0 = (int)(blockIdx.x % (HP / HC)) * HC;
   const int64_t t = a.row0 + rc;
@@ -645,16 +655,37 @@ __global__ __launch_bounds__(NWD * 64) void bwd_dkv_kernel(BwdArgs a) {
   const int G = lane >> 4, li = lane & 15;
   const int rsel = 8 * (G >> 1) + (li >> 2);
   const int csel = 16 * (G & 1) + 4 * (li & 3);
-
-  // Per tile: wait for everything issued one tile earlier (this tile's A
-  // fragments, the stores of two tiles back), then issue the stores of the
-  // previous tile and the A loads of the next one, then this tile's MFMAs.
-  // A fragments alternate between two register sets, so no move waits on a
-  // load in flight.
   constexpr int NK = HC / 16;
+
+  // this wave's q and dout fragments for the whole row (dims 512.. have no
+  // dout), then the staging area is free for the C tiles
+  __syncthreads();  // q and dout staged
+  u32x4 qf[NK][BPW], gf[NK][BPW];
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk)
+#pragma unroll
+    for (int b = 0; b < BPW; ++b) {
+      const int col = (wave * BPW + b) * 32;
+      const uint16_t* qb = sq + (16 * kk + rsel) * RQ + col + csel;
+      const u32x2 q0 = lds_read_tr16(qb), q1 = lds_read_tr16(qb + 4 * RQ);
+      qf[kk][b] = u32x4{q0.x, q0.y, q1.x, q1.y};
+      if (col < 512) {
+        const uint16_t* gb = sg + (16 * kk + rsel) * RG + col + csel;
+        const u32x2 g0 = lds_read_tr16(gb), g1 = lds_read_tr16(gb + 4 * RG);
+        gf[kk][b] = u32x4{g0.x, g0.y, g1.x, g1.y};
+      } else {
+        gf[kk][b] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  __syncthreads();  // every wave holds its fragments: the LDS holds C tiles from here
+
+  // Per tile: wait for this tile's B fragments (loaded during the previous
+  // tile; its row stores, issued after them, may stay in flight), multiply,
+  // load the next tile's fragments into the same registers, write C^T into
+  // the tile's LDS rows; after the barrier store the tile's rows.
   const int ntiles = (L + kBT - 1) / kBT;
-  u32x4 adA[NK], apA[NK], adB[NK], apB[NK];
-  auto load_a = [&](int tl, u32x4* ad, u32x4* ap) {
+  u32x4 ad[NK], ap[NK];
+  auto load_b = [&](int tl, u32x4* ad, u32x4* ap) {
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
       const int64_t o = pds_off(tl * kBT + r32, hc0 + 16 * kk + 8 * half, a.Kw);
@@ -662,60 +693,45 @@ __global__ __launch_bounds__(NWD * 64) void bwd_dkv_kernel(BwdArgs a) {
       ap[kk] = load16(wsP + o);
     }
   };
-  // C: lane -> dim column, slot rows crow(i); the row of slot s of this head
-  // part goes to wsC[part][rc][s] (bf16). pend holds the previous tile's.
+  // the row of slot s of this head part goes to wsC[part][rc][s] (bf16)
   uint16_t* crow_base = a.wsC + ((int64_t)(hc0 / HC) * a.chunk_rows + rc) * a.Kw * DQK;
-  uint32_t pend[BPW][16];
-  int pend_tl = -1;
-  auto store_pending = [&]() {
-    if (pend_tl < 0) return;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int s = pend_tl * kBT + crow(i, half);
-#pragma unroll
-      for (int b = 0; b < BPW; ++b)
-        crow_base[(int64_t)s * DQK + (wave * BPW + b) * 32 + r32] = (uint16_t)pend[b][i];
-    }
-  };
-  auto body = [&](int tl, const u32x4* ad, const u32x4* ap, u32x4* nad, u32x4* nap) {
-    wait_vmcnt0();
-    store_pending();
-    if (tl + 1 < ntiles) load_a(tl + 1, nad, nap);
+  constexpr int CH = DQK / 8;                    // 16-byte chunks per row
+  constexpr int NST = kBT * CH / (NWD * 64);  // row stores per thread and tile
+  static_assert(kBT * CH % (NWD * 64) == 0, "every thread issues the same stores");
+  if (ntiles > 0) load_b(0, ad, ap);
+  for (int tl = 0; tl < ntiles; ++tl) {
+    if (tl > 0) wait_vmcnt_le<NST>();  // uniform
+    else wait_vmcnt0();
     f32x16 acc[BPW];
 #pragma unroll
     for (int b = 0; b < BPW; ++b) acc[b] = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < NK; ++kk) {   // 16-head k-steps
+    for (int kk = 0; kk < NK; ++kk)   // 16-head k-steps
 #pragma unroll
       for (int b = 0; b < BPW; ++b) {
-        const int col = (wave * BPW + b) * 32;
-        const uint16_t* qb = sq + (16 * kk + rsel) * RQ + col + csel;
-        const u32x2 q0 = lds_read_tr16(qb);
-        const u32x2 q1 = lds_read_tr16(qb + 4 * RQ);
-        acc[b] = mfma32x32x16(ad[kk], u32x4{q0.x, q0.y, q1.x, q1.y}, acc[b]);
-        if (col < 512) {
-          const uint16_t* gb = sg + (16 * kk + rsel) * RG + col + csel;
-          const u32x2 g0 = lds_read_tr16(gb);
-          const u32x2 g1 = lds_read_tr16(gb + 4 * RG);
-          acc[b] = mfma32x32x16(ap[kk], u32x4{g0.x, g0.y, g1.x, g1.y}, acc[b]);
-        }
+        acc[b] = mfma32x32x16(qf[kk][b], ad[kk], acc[b]);
+        if ((wave * BPW + b) * 32 < 512) acc[b] = mfma32x32x16(gf[kk][b], ap[kk], acc[b]);
       }
-    }
+    if (tl + 1 < ntiles) load_b(tl + 1, ad, ap);  // uniform
+    unsigned char* ct = smem + (tl & 1) * (kBT * RCB);
 #pragma unroll
     for (int b = 0; b < BPW; ++b)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) pend[b][i] = f32_to_bf16_bits(acc[b][i]);
-    pend_tl = tl;
-  };
-  __syncthreads();  // q and dout staged
-  if (ntiles > 0) load_a(0, adA, apA);
-  for (int tl = 0; tl < ntiles;) {
-    body(tl, adA, apA, adB, apB);
-    if (++tl >= ntiles) break;
-    body(tl, adB, apB, adA, apA);
-    ++tl;
+      for (int g = 0; g < 4; ++g) {
+        const int d = (wave * BPW + b) * 32 + 8 * g + 4 * half;  // dims d .. d+3 of slot r32
+        const u32x2 w = {pack_bf16x2(acc[b][4 * g], acc[b][4 * g + 1]),
+                         pack_bf16x2(acc[b][4 * g + 2], acc[b][4 * g + 3])};
+        *reinterpret_cast<u32x2*>(ct + r32 * RCB + 2 * d) = w;
+      }
+    __syncthreads();  // the tile's rows are in LDS; tile tl - 1's were stored
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      const int c = i * NWD * 64 + (int)threadIdx.x;
+      const int r = c / CH, ch = c - r * CH;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ct + r * RCB + 16 * ch);
+      *reinterpret_cast<u32x4*>(crow_base + (int64_t)(tl * kBT + r) * DQK + 8 * ch) = v;
+    }
   }
-  store_pending();
 }
 
 // ---------------------------------------------- sort of the slots by KV row --
