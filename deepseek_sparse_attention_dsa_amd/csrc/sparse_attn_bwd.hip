@@ -926,11 +926,16 @@ __global__ __launch_bounds__(256) void bwd_sort_scatter_kernel(BwdArgs a, SortPa
 }
 
 // dkv_ws[r] += the sum of the rows listed for KV row r (all head parts).
-// 256 threads: three rows at a time, 72 threads x 8 columns per row.
+// 256 threads: three rows at a time, 72 threads x 8 columns per row. The
+// list entries and rows are loaded U at a time with one head part (clamped
+// to the list, the extra ones not added) so that each thread keeps U loads
+// in flight; the sums run in list order, head parts in order within each
+// entry.
 template <int DQK>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
   constexpr int CPR = DQK / 8;  // 16-byte chunks per row
   constexpr int RPI = 256 / CPR;
+  constexpr int U = 8;
   __shared__ float s_acc[RPI][DQK];
   const int64_t r = blockIdx.x;
   const int32_t b = a.offs[r], e = a.offs[r + 1];
@@ -938,19 +943,37 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int ro = tid / CPR, ch = tid - ro * CPR;
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (ro < RPI) {
+  auto add = [&](const u32x4& v) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      acc[2 * k] += bf16_bits_to_f32(v[k] & 0xffffu);
+      acc[2 * k + 1] += bf16_bits_to_f32(v[k] >> 16);
+    }
+  };
+  if (ro < RPI && a.nparts == 1) {  // one head part: U entries at a time
+    for (int32_t p0 = b + ro; p0 < e; p0 += U * RPI) {
+      int64_t c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int32_t p = p0 + u * RPI;
+        c[u] = a.list[p < e ? p : e - 1];
+      }
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = load16(a.wsC + c[u] * DQK + 8 * ch);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (p0 + u * RPI < e) add(v[u]);
+    }
+  } else if (ro < RPI) {  // several head parts, in order within each entry
     const int64_t part_stride = a.chunk_rows * a.Kw;
     for (int32_t p = b + ro; p < e; p += RPI) {
       const int64_t c = a.list[p];
-      for (int part = 0; part < a.nparts; ++part) {
-        const u32x4 v = load16(a.wsC + (c + part * part_stride) * DQK + 8 * ch);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          acc[2 * k] += bf16_bits_to_f32(v[k] & 0xffffu);
-          acc[2 * k + 1] += bf16_bits_to_f32(v[k] >> 16);
-        }
-      }
+      for (int part = 0; part < a.nparts; ++part)
+        add(load16(a.wsC + (c + part * part_stride) * DQK + 8 * ch));
     }
+  }
+  if (ro < RPI) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) s_acc[ro][8 * ch + k] = acc[k];
   }
