@@ -744,17 +744,27 @@ __global__ __launch_bounds__(256) void bwd_count_kernel(BwdArgs a) {
   }
 }
 
-// offs = exclusive prefix sum of cnt (T_kv + 1 entries).
+// offs = exclusive prefix sum of cnt (T_kv + 1 entries). One workgroup; per
+// round each thread takes PT consecutive entries (its own running sum), the
+// threads' totals are scanned across the workgroup, and a carry links the
+// rounds.
 __global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
+  constexpr int PT = 16;
   __shared__ int32_t s_w[16];
   __shared__ int32_t s_carry;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) s_carry = 0;
   __syncthreads();
-  for (int64_t base = 0; base <= a.T_kv; base += 1024) {
-    const int64_t i = base + tid;
-    const int32_t v = i < a.T_kv ? a.cnt[i] : 0;
-    int32_t incl = v;
+  for (int64_t base = 0; base <= a.T_kv; base += 1024 * PT) {
+    const int64_t i0 = base + (int64_t)tid * PT;
+    int32_t v[PT];
+    int32_t tot = 0;
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+      v[k] = i0 + k < a.T_kv ? a.cnt[i0 + k] : 0;
+      tot += v[k];
+    }
+    int32_t incl = tot;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const int32_t o = __shfl_up(incl, d, 64);
@@ -764,7 +774,12 @@ __global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
     __syncthreads();
     int32_t before = s_carry;
     for (int w = 0; w < wave; ++w) before += s_w[w];
-    if (i <= a.T_kv) a.offs[i] = before + incl - v;
+    int32_t run = before + incl - tot;  // entries before this thread's first
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+      if (i0 + k <= a.T_kv) a.offs[i0 + k] = run;
+      run += v[k];
+    }
     __syncthreads();
     if (tid == 1023) s_carry = before + incl;
     __syncthreads();
