@@ -34,8 +34,9 @@
 //    part); bwd_tile_reduce_kernel: the parts summed in ascending order.
 //  * dkv otherwise (per-slot rows): bwd_dkv_kernel: per tile, dS^T . q +
 //    P^T . dout (the query's q and dout staged in LDS), each slot's row
-//    written once as bf16 (per 64-head part); bwd_count / bwd_scan: slots per
-//    KV row and the offsets of their lists; bwd_sort_{hist,scan,scatter}: a
+//    written once as bf16 (per 64-head part); the slots per KV row, counted
+//    by bwd_pds_kernel, and bwd_scan: the offsets of their lists;
+//    bwd_sort_{hist,scan,scatter}: a
 //    stable radix sort of the chunk's valid slots by KV row, giving each KV
 //    row the ascending list of the slot rows written for it;
 //    bwd_reduce_kernel: one workgroup per KV row sums its list (and parts) in
@@ -281,8 +282,13 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
 
   int32_t id_next = id_second;
   uint32_t mask_cur = 0;
+  // Per-slot dkv rows: the slots per KV row are counted here, as the ids are
+  // validated (one lane per slot, non-returning atomics issued before the
+  // tile's copies); with KV tiles nothing is counted.
+  const bool count = !a.tiles && wave == 0 && lane < 32;
   if (n_tiles > 0) {
     const int32_t id0 = valid_id(id_first);
+    if (count && id0 >= 0) atomicAdd(a.cnt + id0, 1);
     mask_cur = (uint32_t)ballot(id0 >= 0);
     const CopySrc cs0 = prep_copy(smem_base, id0);
     static_for<NCOPY>([&](auto jc) { copy_one(cs0, jc); });
@@ -347,6 +353,7 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
       // (the ids' row check happens here, at their first use, after the
       // previous tile's barrier wait has covered their load)
       const int32_t idv = (it + 1) * kBT + key_row < L ? valid_id(id_next) : -1;
+      if (count && idv >= 0) atomicAdd(a.cnt + idv, 1);
       mask_next = (uint32_t)ballot(idv >= 0);
       cs = prep_copy(smem_base + ((it + 1) & 1) * STAGE, idv);
     }
@@ -735,15 +742,6 @@ __global__ __launch_bounds__(NWD * 64) void bwd_dkv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------- sort of the slots by KV row --
-__global__ __launch_bounds__(256) void bwd_count_kernel(BwdArgs a) {
-  const int64_t t = a.row0 + blockIdx.x;
-  const int L = row_len(a, t);
-  for (int s = threadIdx.x; s < L; s += 256) {
-    const int32_t v = a.indices[t * a.ld_idx + s];
-    if (v >= 0 && v < a.T_kv) atomicAdd(&a.cnt[v], 1);
-  }
-}
-
 // offs = exclusive prefix sum of cnt (T_kv + 1 entries). One workgroup; per
 // round each thread takes PT consecutive entries (its own running sum), the
 // threads' totals are scanned across the workgroup, and a carry links the
@@ -1429,6 +1427,9 @@ hipError_t launch_bwd_nw(BwdArgs a, int64_t chunk, hipStream_t st) {
     a.row0 = r0;
     const int64_t n = a.T_q - r0 < chunk ? a.T_q - r0 : chunk;
     constexpr int NWC = NW == 3 ? 4 : NW;
+    if (!a.tiles && a.T_kv > 0)  // the P / dS pass counts the slots per KV row
+      hipLaunchKernelGGL(bwd_fill_kernel, dim3((unsigned)((a.T_kv + 255) / 256)), dim3(256), 0,
+                         st, reinterpret_cast<float*>(a.cnt), a.T_kv);
     if (buf)
       hipLaunchKernelGGL((bwd_pds_kernel<DQK, NW, NWC, true>), dim3((unsigned)n), dim3(NWC * 64), 0,
                          st, a);
@@ -1459,9 +1460,6 @@ hipError_t launch_bwd_nw(BwdArgs a, int64_t chunk, hipStream_t st) {
     hipLaunchKernelGGL((bwd_dkv_kernel<DQK, NW, NWD>), dim3((unsigned)(n * (HP / HC))),
                        dim3(NWD * 64), 0, st, a);
     if (a.T_kv > 0) {
-      hipLaunchKernelGGL(bwd_fill_kernel, dim3((unsigned)((a.T_kv + 255) / 256)), dim3(256), 0,
-                         st, reinterpret_cast<float*>(a.cnt), a.T_kv);
-      hipLaunchKernelGGL(bwd_count_kernel, dim3((unsigned)n), dim3(256), 0, st, a);
       hipLaunchKernelGGL(bwd_scan_kernel, dim3(1), dim3(1024), 0, st, a);
       // keys below T_kv: 8 bits a pass, the last pass writes the list
       const int bits = a.T_kv > 1 ? 32 - __builtin_clz((uint32_t)(a.T_kv - 1)) : 0;
