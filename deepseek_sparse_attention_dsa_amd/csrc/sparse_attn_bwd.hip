@@ -743,23 +743,31 @@ __global__ __launch_bounds__(NWD * 64) void bwd_dkv_kernel(BwdArgs a) {
 
 // ---------------------------------------------- sort of the slots by KV row --
 // offs = exclusive prefix sum of cnt (T_kv + 1 entries). One workgroup; per
-// round each thread takes PT consecutive entries (its own running sum), the
+// round of 1024 * PT entries the counts pass through LDS (coalesced loads
+// and stores), each thread sums a run of PT consecutive entries, the
 // threads' totals are scanned across the workgroup, and a carry links the
 // rounds.
 __global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
   constexpr int PT = 16;
+  constexpr int N = 1024 * PT;
+  __shared__ int32_t s_v[N + N / 32];  // entry i at i + i / 32 (spreads the runs over banks)
   __shared__ int32_t s_w[16];
   __shared__ int32_t s_carry;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto at = [](int i) { return i + (i >> 5); };
   if (tid == 0) s_carry = 0;
-  __syncthreads();
-  for (int64_t base = 0; base <= a.T_kv; base += 1024 * PT) {
-    const int64_t i0 = base + (int64_t)tid * PT;
+  for (int64_t base = 0; base <= a.T_kv; base += N) {
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+      const int i = k * 1024 + tid;
+      s_v[at(i)] = base + i < a.T_kv ? a.cnt[base + i] : 0;
+    }
+    __syncthreads();  // the round's counts are in LDS; the carry is set
     int32_t v[PT];
     int32_t tot = 0;
 #pragma unroll
     for (int k = 0; k < PT; ++k) {
-      v[k] = i0 + k < a.T_kv ? a.cnt[i0 + k] : 0;
+      v[k] = s_v[at(tid * PT + k)];
       tot += v[k];
     }
     int32_t incl = tot;
@@ -775,12 +783,17 @@ __global__ __launch_bounds__(1024) void bwd_scan_kernel(BwdArgs a) {
     int32_t run = before + incl - tot;  // entries before this thread's first
 #pragma unroll
     for (int k = 0; k < PT; ++k) {
-      if (i0 + k <= a.T_kv) a.offs[i0 + k] = run;
+      s_v[at(tid * PT + k)] = run;
       run += v[k];
     }
-    __syncthreads();
+    __syncthreads();  // the offsets are in LDS; every thread has read the carry
     if (tid == 1023) s_carry = before + incl;
-    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+      const int i = k * 1024 + tid;
+      if (base + i <= a.T_kv) a.offs[base + i] = s_v[at(i)];
+    }
+    __syncthreads();  // the round's offsets are stored before the next round's counts
   }
 }
 
