@@ -109,12 +109,22 @@ SMALL = [
     (200, 33, 512, 24, True, False, True),
     (400, 128, 576, 40, True, True, False),
     (270, 96, 512, 33, False, False, True),
+    (300, 16, 576, 32, True, False, True),   # one 32-head block: 32-head parts
+    (260, 24, 512, 24, False, True, True),
 ]
 
 
 def test_small_cases_cover_both_dkv_schemes():
     kinds = {_kv_tiles(T, kw) for T, _, _, kw, *_ in SMALL}
     assert kinds == {True, False}
+
+
+def test_small_per_slot_cases_cover_every_head_block_count():
+    """The per-slot dkv path at 1, 2, 3 and 4 blocks of 32 heads (head parts
+    of 32 or 64 heads, one to three of them), at both D_qk."""
+    blocks = {(-(-H // 32), D) for T, H, D, kw, *_ in SMALL if not _kv_tiles(T, kw)}
+    assert {b for b, _ in blocks} == {1, 2, 3, 4}
+    assert {D for _, D in blocks} == {512, 576}
 
 
 @pytest.mark.parametrize("T,H,D,kw,sink,stress,use_tl", SMALL)
