@@ -619,7 +619,7 @@ __global__ __launch_bounds__(NW * 128, NW <= 2 ? 2 : 1) void bwd_dq_ring_kernel(
 // of 4 consecutive dims of its slot, written as 8-byte words into an LDS
 // tile of the 32 slot rows; after a barrier the waves store that tile as
 // whole rows, 16 bytes per lane on consecutive addresses. (Stored straight
-// from the MFMA layout, 2 bytes per lane, the row writes took twice as long.)
+// from the MFMA layout, 2 bytes per lane, the kernel took 1.6 times as long.)
 template <int DQK, int NW, int NWD>
 __global__ __launch_bounds__(NWD * 64) void bwd_dkv_kernel(BwdArgs a) {
   constexpr int HP = NW * 32;
