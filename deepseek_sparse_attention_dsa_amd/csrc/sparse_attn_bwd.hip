@@ -736,7 +736,9 @@ __global__ __launch_bounds__(NWD * 64) void bwd_dkv_kernel(BwdArgs a) {
       const int c = i * NWD * 64 + (int)threadIdx.x;
       const int r = c / CH, ch = c - r * CH;
       const u32x4 v = *reinterpret_cast<const u32x4*>(ct + r * RCB + 16 * ch);
-      *reinterpret_cast<u32x4*>(crow_base + (int64_t)(tl * kBT + r) * DQK + 8 * ch) = v;
+      // streaming store: the row is read back once, by the reduce, long after
+      __builtin_nontemporal_store(
+          v, reinterpret_cast<u32x4*>(crow_base + (int64_t)(tl * kBT + r) * DQK + 8 * ch));
     }
   }
 }
@@ -986,7 +988,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
       }
       u32x4 v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = load16(a.wsC + c[u] * DQK + 8 * ch);
+      for (int u = 0; u < U; ++u)  // streaming loads: each row piece is read once
+        v[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(a.wsC + c[u] * DQK + 8 * ch));
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (p0 + u * RPI < e) add(v[u]);
