@@ -321,7 +321,9 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
   // 16pi + 8..15, stored as 16-byte runs through buffer descriptors of the
   // row's P and dS. The stores of the first tile step (no previous tile) take
   // an offset past the range and are dropped, so every step issues the same
-  // four stores.
+  // four stores. They are streaming (nontemporal: aux bit 1): P and dS are
+  // read again only by the later passes, and at long rows far exceed the
+  // caches.
   const __amdgpu_buffer_rsrc_t rP = raw_buffer(wsP, (uint32_t)(a.Kw * HP * 2));
   const __amdgpu_buffer_rsrc_t rD = raw_buffer(wsD, (uint32_t)(a.Kw * HP * 2));
   auto epi_store = [&](int te, bool live, const uint32_t (&pw)[4][2], const uint32_t (&dw)[4][2],
@@ -340,8 +342,8 @@ __global__ __launch_bounds__(NWC * 64, 1) void bwd_pds_kernel(BwdArgs a) {
     // 8 consecutive heads
     const uint32_t off = live ? (uint32_t)pds_off(te * kBT + r32, h0 + 16 * pi + 8 * half, a.Kw) * 2u
                               : 0x80000000u;
-    __builtin_amdgcn_raw_buffer_store_b128(po, rP, (int)off, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(dq4, rD, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(po, rP, (int)off, 0, 2);
+    __builtin_amdgcn_raw_buffer_store_b128(dq4, rD, (int)off, 0, 2);
   };
   uint32_t mask_prev = 0;
   auto tile_step = [&](int it, f32x16& sacc, f32x16& dacc, const f32x16& sprev, const f32x16& dprev) {
